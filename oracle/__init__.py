@@ -1,0 +1,143 @@
+"""fp64 CPU oracle of the gated delta rule forward.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the CPU
+baseline leg of ``bench.py`` are the only code allowed to import it. It shares
+no code with the HIP library in ``chunked_gated_delta_05_amd``; the two meet
+only in the seeded input generator, which holds none of the method's
+arithmetic.
+
+The C library ``gdn_oracle.c`` holds the arithmetic; this module loads it
+with ctypes and converts numpy arrays. ``twin.py`` is an independent numpy
+transcription used to cross-check it on tiny inputs; ``varlen.py`` defines the
+packed-sequence chunk metadata.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_build.LIB) or (
+                os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC)):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        lib.gdn_oracle_fwd.restype = ctypes.c_int
+        lib.gdn_oracle_fwd.argtypes = [
+            ctypes.c_int64, _i64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+            _f64p, ctypes.c_int64, _i64p, _f64p, _f64p, ctypes.c_int64, _f64p, ctypes.c_int]
+        lib.gdn_oracle_summary.restype = ctypes.c_int
+        lib.gdn_oracle_summary.argtypes = [
+            ctypes.c_int64, _i64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            _f32p, _f32p, _f32p, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int64, _i64p,
+            _f64p, _f64p, ctypes.c_int]
+        lib.gdn_oracle_merge.restype = ctypes.c_int
+        lib.gdn_oracle_merge.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_int64, _f64p, _f64p, _f64p, _f64p]
+        lib.gdn_oracle_max_threads.restype = ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+def _f32(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+def _ptr(a, t):
+    return None if a is None else a.ctypes.data_as(t)
+
+
+def max_threads() -> int:
+    return int(_lib().gdn_oracle_max_threads())
+
+
+def fwd(q, k, v, g, beta, offsets, scale, *, gate_per_key=False, use_exp2=False, S0=None,
+        heads=None, want_o=True, want_final=True, chunk_states=False, chunk=64, threads=0):
+    """Token-by-token forward in fp64.
+
+    q, k: [N, H, K]; v: [N, H, V] (N = flat token count); g: [N, H] (scalar
+    gate) or [N, H, K] (per-key gate); beta: [N, H]; offsets: unit token
+    offsets (length n_units + 1); S0: [n_units, H, K, V] or None (zeros);
+    heads: optional list of head indices to run (outputs are indexed by the
+    position in that list).
+
+    Returns a dict with ``o`` [N, n_sel, V], ``final`` [n_units, n_sel, K, V]
+    and ``chunk_states`` [n_chunks, n_sel, K, V] (the state entering each
+    ``chunk``-token block of every unit) as requested.
+    """
+    q, k, v, g, beta = _f32(q), _f32(k), _f32(v), _f32(g), _f32(beta)
+    N, H, K = k.shape
+    V = v.shape[2]
+    offs = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    n_units = len(offs) - 1
+    sel = None if heads is None else np.ascontiguousarray(np.asarray(heads, dtype=np.int64))
+    n_sel = H if sel is None else len(sel)
+    s0 = None if S0 is None else np.ascontiguousarray(np.asarray(S0, dtype=np.float64))
+    if s0 is not None and s0.shape != (n_units, H, K, V):
+        raise ValueError("S0 must be [n_units, H, K, V]")
+    o = np.zeros((N, n_sel, V)) if want_o else None
+    fin = np.zeros((n_units, n_sel, K, V)) if want_final else None
+    cs = None
+    if chunk_states:
+        n_chunks = int(sum((b - a + chunk - 1) // chunk for a, b in zip(offs[:-1], offs[1:])))
+        cs = np.zeros((n_chunks, n_sel, K, V))
+    rc = _lib().gdn_oracle_fwd(
+        n_units, _ptr(offs, _i64p), H, K, V, _ptr(q, _f32p), _ptr(k, _f32p), _ptr(v, _f32p),
+        _ptr(g, _f32p), _ptr(beta, _f32p), int(gate_per_key), int(use_exp2), float(scale),
+        _ptr(s0, _f64p), n_sel, _ptr(sel, _i64p), _ptr(o, _f64p), _ptr(fin, _f64p), int(chunk),
+        _ptr(cs, _f64p), int(threads))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return {"o": o, "final": fin, "chunk_states": cs}
+
+
+def summary(k, v, g, beta, offsets, *, gate_per_key=False, use_exp2=False, heads=None,
+            want_ext=True, want_M=True, threads=0):
+    """Per-unit segment summaries: S_ext [n_units, n_sel, K, V] (state reached
+    from zero) and M [n_units, n_sel, K, K] (the map applied to an entry
+    state), so that the state at the end of a unit is M @ S_entry + S_ext."""
+    k, v, g, beta = _f32(k), _f32(v), _f32(g), _f32(beta)
+    N, H, K = k.shape
+    V = v.shape[2]
+    offs = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    n_units = len(offs) - 1
+    sel = None if heads is None else np.ascontiguousarray(np.asarray(heads, dtype=np.int64))
+    n_sel = H if sel is None else len(sel)
+    ext = np.zeros((n_units, n_sel, K, V)) if want_ext else None
+    M = np.zeros((n_units, n_sel, K, K)) if want_M else None
+    rc = _lib().gdn_oracle_summary(
+        n_units, _ptr(offs, _i64p), H, K, V, _ptr(k, _f32p), _ptr(v, _f32p), _ptr(g, _f32p),
+        _ptr(beta, _f32p), int(gate_per_key), int(use_exp2), n_sel, _ptr(sel, _i64p),
+        _ptr(ext, _f64p), _ptr(M, _f64p), int(threads))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return {"S_ext": ext, "M": M}
+
+
+def merge(S_ext, M, S0=None):
+    """S_ext: [n_seg, n, K, V]; M: [n_seg, n, K, K]; S0: [n, K, V] or None.
+
+    Returns S_init [n_seg + 1, n, K, V]: the state entering every segment,
+    then the state at the end of the last one."""
+    ext = np.ascontiguousarray(np.asarray(S_ext, dtype=np.float64))
+    m = np.ascontiguousarray(np.asarray(M, dtype=np.float64))
+    n_seg, n, K, V = ext.shape
+    s0 = None if S0 is None else np.ascontiguousarray(np.asarray(S0, dtype=np.float64))
+    out = np.zeros((n_seg + 1, n, K, V))
+    rc = _lib().gdn_oracle_merge(n_seg, n, K, V, _ptr(ext, _f64p), _ptr(m, _f64p),
+                                 _ptr(s0, _f64p), _ptr(out, _f64p))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return out
