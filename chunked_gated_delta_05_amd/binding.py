@@ -1,0 +1,298 @@
+"""ctypes binding of libgdn (include/gdn.h): argument marshalling only.
+
+Every step of the forward runs in the HIP library; this module turns torch
+tensors into device pointers, allocates outputs and the workspace through
+torch (memory plumbing), passes torch's current HIP stream, and maps status
+codes to the exception types the pages' adapters use (ValueError for
+contract violations, NotImplementedError for unsupported features,
+RuntimeError for device failures). It fails loudly when the library has not
+been built: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_OK, GDN_ERR_INVALID, GDN_ERR_UNSUPPORTED, GDN_ERR_DEVICE, GDN_ERR_CAPACITY = range(5)
+LAYOUT_BSND, LAYOUT_TND = 0, 1
+DTYPE_F32, DTYPE_BF16 = 0, 1
+GATE_SCALAR, GATE_PER_KEY = 0, 1
+FLAG_REUSE_PREPARED, FLAG_PREPARE_ONLY = 1, 2
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+class GdnDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("layout", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("o_dtype", ctypes.c_int32),
+                ("gate_kind", ctypes.c_int32), ("use_exp2", ctypes.c_int32),
+                ("chunk_size", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("n_units", ctypes.c_int32), ("offsets_host", _i32p), ("offsets_dev", ctypes.c_void_p),
+                ("chunk_offsets_dev", ctypes.c_void_p), ("chunk_indices_dev", ctypes.c_void_p)]
+
+
+class GdnSlots(ctypes.Structure):
+    _fields_ = [("g_cumsum", ctypes.c_void_p), ("A", ctypes.c_void_p), ("h", ctypes.c_void_p)]
+
+
+_LIB = None
+
+
+def lib():
+    """The loaded libgdn.so; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libgdn.so is not built ({LIB_PATH}); run "
+                               "`python -m chunked_gated_delta_05_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)
+        L.gdn_varlen_meta.restype = ctypes.c_int
+        L.gdn_varlen_meta.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _i32p,
+                                      ctypes.c_int32, _i32p, _i32p]
+        L.gdn_chunk_fwd.restype = ctypes.c_int
+        L.gdn_chunk_fwd.argtypes = [ctypes.POINTER(GdnDesc), vp, vp, vp, vp, vp, vp, vp, vp,
+                                    ctypes.POINTER(GdnSlots), ctypes.c_int32, vp, sz, vp]
+        L.gdn_state_summary.restype = ctypes.c_int
+        L.gdn_state_summary.argtypes = [ctypes.POINTER(GdnDesc), vp, vp, vp, vp, vp, ctypes.c_int32,
+                                        vp, vp, vp, sz, vp]
+        L.gdn_state_merge.restype = ctypes.c_int
+        L.gdn_state_merge.argtypes = [ctypes.c_int32] * 5 + [vp, vp, vp, vp, vp, vp]
+        _LIB = L
+    return _LIB
+
+
+def check(status: int, what: str) -> None:
+    if status == GDN_OK:
+        return
+    msg = f"{what}: libgdn status {status}"
+    if status in (GDN_ERR_INVALID, GDN_ERR_CAPACITY):
+        raise ValueError(msg)
+    if status == GDN_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise RuntimeError(msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(dt):
+    if dt == torch.bfloat16:
+        return DTYPE_BF16
+    if dt == torch.float32:
+        return DTYPE_F32
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+# ------------------------------------------------------------------ metadata
+def gdn_varlen_meta(offsets, total_tokens: int, chunk_size: int = 64):
+    """Host chunk metadata: (chunk_indices int32 [n, 2], chunk_offsets int32
+    [len(offsets)]) as CPU tensors. Offsets must be ints (no bools), start at
+    0, end at total_tokens and strictly increase."""
+    offs = list(offsets.tolist() if isinstance(offsets, torch.Tensor) else offsets)
+    if any(isinstance(x, bool) or not isinstance(x, int) for x in offs):
+        raise ValueError("offsets must be integers")
+    if any(x < -2 ** 31 or x >= 2 ** 31 for x in offs):
+        raise ValueError("offsets must fit in int32")
+    n = len(offs)
+    arr = (ctypes.c_int32 * max(n, 1))(*offs)
+    cnt = ctypes.c_int32(0)
+    check(lib().gdn_varlen_meta(arr, n, int(total_tokens), int(chunk_size), None, 0, None,
+                                ctypes.byref(cnt)), "gdn_varlen_meta")
+    ci = torch.empty((max(cnt.value, 1), 2), dtype=torch.int32)
+    co = torch.empty((n,), dtype=torch.int32)
+    check(lib().gdn_varlen_meta(arr, n, int(total_tokens), int(chunk_size),
+                                ctypes.cast(ci.data_ptr(), _i32p), cnt.value,
+                                ctypes.cast(co.data_ptr(), _i32p), ctypes.byref(cnt)), "gdn_varlen_meta")
+    return ci[:cnt.value], co
+
+
+@dataclass
+class UnitMeta:
+    """Units of a call: host offsets (validated by the library) and their
+    device copies with the chunk metadata. Build once per offsets list."""
+    offsets: list
+    host: ctypes.Array
+    offsets_dev: torch.Tensor
+    chunk_offsets_dev: torch.Tensor
+    chunk_indices_dev: torch.Tensor
+    n_chunks: int
+
+
+def make_meta(offsets, total_tokens: int, device) -> UnitMeta:
+    offs = [int(x) for x in offsets]
+    ci, co = gdn_varlen_meta(offs, total_tokens)
+    dev = torch.device(device)
+    ci_dev = ci.to(dev) if ci.numel() else torch.zeros((1, 2), dtype=torch.int32, device=dev)
+    return UnitMeta(offs, (ctypes.c_int32 * len(offs))(*offs),
+                    torch.tensor(offs, dtype=torch.int32, device=dev), co.to(dev), ci_dev,
+                    int(co[-1]))
+
+
+def segment_offsets(B: int, T: int, seg) -> list:
+    """Flat unit offsets of a split: every row b cut at the in-row offsets seg."""
+    seg = [int(x) for x in seg]
+    return [b * T + s for b in range(B) for s in seg[:-1]] + [B * T]
+
+
+# ------------------------------------------------------------------ descriptor
+def _desc(q_like, H, dtype, o_dtype, per_key, use_exp2, scale, meta: UnitMeta | None):
+    d = GdnDesc()
+    if q_like.dim() == 4:
+        d.B, d.T = q_like.shape[0], q_like.shape[1]
+        d.layout = LAYOUT_BSND
+    elif q_like.dim() == 3:
+        d.B, d.T = 1, q_like.shape[0]
+        d.layout = LAYOUT_TND
+    else:
+        raise ValueError("GDN inputs must have shape [B,T,H,K] or [T,H,K]")
+    d.H, d.K = H, q_like.shape[-1]
+    d.V = d.K
+    d.dtype, d.o_dtype = _dtype_code(dtype), _dtype_code(o_dtype)
+    d.gate_kind = GATE_PER_KEY if per_key else GATE_SCALAR
+    d.use_exp2 = int(bool(use_exp2))
+    d.chunk_size = 64
+    d.scale = float(scale)
+    if meta is not None:
+        d.n_units = len(meta.offsets) - 1
+        d.offsets_host = ctypes.cast(meta.host, _i32p)
+        d.offsets_dev = meta.offsets_dev.data_ptr()
+        d.chunk_offsets_dev = meta.chunk_offsets_dev.data_ptr()
+        d.chunk_indices_dev = meta.chunk_indices_dev.data_ptr()
+    return d
+
+
+def _check_inputs(q, k, v, g, beta):
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if g is not None and g.dtype != torch.float32:
+        raise ValueError("g must be float32")
+
+
+def n_units_of(q_like, meta):
+    return q_like.shape[0] if meta is None else len(meta.offsets) - 1
+
+
+def workspace_bytes(desc: GdnDesc, fn="fwd") -> int:
+    nb = ctypes.c_size_t(0)
+    if fn == "fwd":
+        st = lib().gdn_chunk_fwd(ctypes.byref(desc), None, None, None, None, None, None, None, None,
+                                 None, 0, None, ctypes.byref(nb), None)
+    else:
+        st = lib().gdn_state_summary(ctypes.byref(desc), None, None, None, None, None, 0, None, None,
+                                     None, ctypes.byref(nb), None)
+    check(st, "workspace query")
+    return nb.value
+
+
+# ------------------------------------------------------------------ entry points
+def gdn_chunk_fwd(q, k, v, g, beta, scale=None, *, meta: UnitMeta | None = None, initial_state=None,
+                  output_final_state=False, use_exp2=False, o_dtype=torch.float32,
+                  want_g_cumsum=False, want_A=False, want_h=False, flags=0, workspace=None, out=None):
+    """Chunked gated delta rule forward through libgdn.
+
+    q, k [B,T,H,K] (BSND) or [T,H,K] (TND, needs meta); v like q; g fp32
+    [..,H] (scalar gate) or [..,H,K] (per-key gate); beta [..,H]. Returns
+    (o, final_state or None, extras dict)."""
+    _check_inputs(q, k, v, g, beta)
+    H = k.shape[-2]
+    per_key = g.dim() == k.dim()
+    if scale is None:
+        scale = k.shape[-1] ** -0.5
+    desc = _desc(k, H, k.dtype, o_dtype, per_key, use_exp2, scale, meta)
+    dev = k.device
+    nb = workspace_bytes(desc)
+    ws = workspace if workspace is not None else torch.empty(nb, dtype=torch.uint8, device=dev)
+    if ws.numel() < nb:
+        raise ValueError("workspace too small")
+    prep_only = bool(flags & FLAG_PREPARE_ONLY)
+    o = None
+    if not prep_only:
+        o = out if out is not None else torch.empty(v.shape, dtype=o_dtype, device=dev)
+    units = n_units_of(k, meta)
+    fin = torch.empty((units, H, k.shape[-1], v.shape[-1]), dtype=torch.float32, device=dev) \
+        if output_final_state and not prep_only else None
+    extras = {}
+    tokens = k.shape[0] * k.shape[1] if k.dim() == 4 else k.shape[0]
+    if want_g_cumsum:
+        extras["g_cumsum"] = torch.empty(g.shape, dtype=torch.float32, device=dev)
+    if want_A:
+        extras["A"] = torch.empty((tokens, H, 64), dtype=torch.float32, device=dev)
+    if want_h:
+        n_chunks = meta.n_chunks if meta is not None else k.shape[0] * ((k.shape[1] + 63) // 64)
+        extras["h"] = torch.empty((n_chunks, H, k.shape[-1], v.shape[-1]), dtype=torch.float32, device=dev)
+    slots = GdnSlots(_ptr(extras.get("g_cumsum")), _ptr(extras.get("A")), _ptr(extras.get("h")))
+    if initial_state is not None:
+        if initial_state.dtype != torch.float32 or not initial_state.is_contiguous():
+            raise ValueError("initial_state must be contiguous float32")
+        if tuple(initial_state.shape) != (units, H, k.shape[-1], v.shape[-1]):
+            raise ValueError("initial_state must be [units, H, K, V]")
+    nbytes = ctypes.c_size_t(ws.numel())
+    check(lib().gdn_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                              _ptr(initial_state), _ptr(o), _ptr(fin), ctypes.byref(slots), int(flags),
+                              _ptr(ws), ctypes.byref(nbytes), _stream(dev)), "gdn_chunk_fwd")
+    return o, fin, extras
+
+
+def gdn_state_summary(k, v, g, beta, *, meta: UnitMeta, mode=0, use_exp2=False, q=None,
+                      workspace=None):
+    """Per-unit summaries (S_ext [units,H,K,V], M [units,H,K,K]); pass q to
+    leave a per-key preparation that a reusing forward can use."""
+    _check_inputs(q, k, v, g, beta)
+    H = k.shape[-2]
+    per_key = g.dim() == k.dim()
+    desc = _desc(k, H, k.dtype, torch.float32, per_key, use_exp2, 1.0, meta)
+    dev = k.device
+    nb = workspace_bytes(desc)
+    ws = workspace if workspace is not None else torch.empty(nb, dtype=torch.uint8, device=dev)
+    units = n_units_of(k, meta)
+    K, V = k.shape[-1], v.shape[-1]
+    S_ext = torch.empty((units, H, K, V), dtype=torch.float32, device=dev) if mode != 2 else None
+    M = torch.empty((units, H, K, K), dtype=torch.float32, device=dev) if mode != 1 else None
+    nbytes = ctypes.c_size_t(ws.numel())
+    check(lib().gdn_state_summary(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                  int(mode), _ptr(S_ext), _ptr(M), _ptr(ws), ctypes.byref(nbytes),
+                                  _stream(dev)), "gdn_state_summary")
+    return S_ext, M, ws
+
+
+def gdn_state_merge(S_ext, M, S0=None, *, B: int, n_seg: int, want_final=True):
+    """S_ext [B*n_seg,H,K,V], M [B*n_seg,H,K,K] (units row-major) -> S_init
+    [B*n_seg,H,K,V] (the state entering every segment) and S_final [B,H,K,V]."""
+    H, K, V = S_ext.shape[1], S_ext.shape[2], S_ext.shape[3]
+    dev = S_ext.device
+    S_init = torch.empty_like(S_ext)
+    S_final = torch.empty((B, H, K, V), dtype=torch.float32, device=dev) if want_final else None
+    check(lib().gdn_state_merge(B, H, n_seg, K, V, _ptr(S_ext), _ptr(M), _ptr(S0), _ptr(S_init),
+                                _ptr(S_final), _stream(dev)), "gdn_state_merge")
+    return S_init, S_final
+
+
+def split_forward(q, k, v, g, beta, scale=None, *, seg, use_exp2=False, initial_state=None,
+                  o_dtype=torch.float32):
+    """Sequence split on one GPU: per-segment summaries, their merge, then the
+    correction pass (the forward of every segment from its true entry state,
+    reusing the preparation). seg: in-row segment offsets [0, ..., T].
+    Returns (o, S_final [B,H,K,V], S_init [B*n_seg,H,K,V])."""
+    B, T = k.shape[0], k.shape[1]
+    n_seg = len(seg) - 1
+    meta = make_meta(segment_offsets(B, T, seg), B * T, k.device)
+    S_ext, M, ws = gdn_state_summary(k, v, g, beta, meta=meta, mode=0, use_exp2=use_exp2, q=q)
+    S_init, S_final = gdn_state_merge(S_ext, M, initial_state, B=B, n_seg=n_seg)
+    o, _, _ = gdn_chunk_fwd(q, k, v, g, beta, scale, meta=meta, initial_state=S_init,
+                            use_exp2=use_exp2, o_dtype=o_dtype, flags=FLAG_REUSE_PREPARED,
+                            workspace=ws)
+    return o, S_final, S_init

@@ -1,0 +1,213 @@
+// Host side of libgdn: argument validation, workspace layout and launch
+// order for the C ABI declared in include/gdn.h. Every check runs before the
+// first HIP call, so a rejected call enqueues nothing and the checks can be
+// exercised without a GPU.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <vector>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+
+using gdn::BT;
+using gdn::DK;
+using gdn::DV;
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;   // sanity bound on any tensor
+
+// _packed_offsets rules (hyper-parallel Diff Coverage page): at least two
+// entries, first 0, last total, strictly increasing.
+bool offsets_ok(const int32_t* offs, int32_t n, int64_t total) {
+    if (offs == nullptr || n < 2) return false;
+    if (offs[0] != 0 || offs[n - 1] != total) return false;
+    for (int32_t i = 0; i + 1 < n; ++i)
+        if (offs[i] >= offs[i + 1]) return false;
+    return true;
+}
+
+int64_t count_chunks(const int32_t* offs, int32_t n, int32_t cs) {
+    int64_t c = 0;
+    for (int32_t i = 0; i + 1 < n; ++i) c += (int64_t(offs[i + 1]) - offs[i] + cs - 1) / cs;
+    return c;
+}
+
+gdn_status validate(const gdn_desc* d, gdn::Problem* p) {
+    if (d == nullptr) return GDN_ERR_INVALID;
+    if (d->chunk_size != 64) return GDN_ERR_INVALID;
+    if (d->K != DK || d->V != DV) return GDN_ERR_UNSUPPORTED;
+    if (d->B < 1 || d->T < 0 || d->H < 1) return GDN_ERR_INVALID;
+    if (d->layout != GDN_LAYOUT_BSND && d->layout != GDN_LAYOUT_TND) return GDN_ERR_INVALID;
+    if (d->dtype != GDN_DTYPE_F32 && d->dtype != GDN_DTYPE_BF16) return GDN_ERR_INVALID;
+    if (d->o_dtype != GDN_DTYPE_F32 && d->o_dtype != GDN_DTYPE_BF16) return GDN_ERR_INVALID;
+    if (d->gate_kind != GDN_GATE_SCALAR && d->gate_kind != GDN_GATE_PER_KEY) return GDN_ERR_INVALID;
+    if (d->use_exp2 != 0 && d->use_exp2 != 1) return GDN_ERR_INVALID;
+    if (!isfinite(d->scale)) return GDN_ERR_INVALID;
+    const int64_t total = int64_t(d->B) * d->T;
+    if (total * d->H * DK > kMaxElems) return GDN_ERR_INVALID;
+    gdn::UnitMap um;
+    memset(&um, 0, sizeof(um));
+    um.T = d->T;
+    um.total_tokens = total;
+    if (d->layout == GDN_LAYOUT_TND) {
+        // packed documents: physical batch one, offsets required
+        if (d->B != 1 || d->n_units < 1) return GDN_ERR_INVALID;
+    }
+    if (d->n_units < 0) return GDN_ERR_INVALID;
+    if (d->n_units == 0) {
+        um.dense = 1;
+        um.n_units = d->B;
+        um.nt_dense = (d->T + BT - 1) / BT;
+        const int64_t nc = int64_t(d->B) * um.nt_dense;
+        if (nc > INT32_MAX / 2) return GDN_ERR_INVALID;
+        um.n_chunks = (int32_t)nc;
+    } else {
+        if (!offsets_ok(d->offsets_host, d->n_units + 1, total)) return GDN_ERR_INVALID;
+        if (d->layout == GDN_LAYOUT_BSND) {
+            // segments of rows: every row start must be a unit boundary
+            int32_t j = 0;
+            for (int32_t b = 1; b < d->B; ++b) {
+                const int64_t rs = int64_t(b) * d->T;
+                while (j <= d->n_units && d->offsets_host[j] < rs) ++j;
+                if (j > d->n_units || d->offsets_host[j] != rs) return GDN_ERR_INVALID;
+            }
+        }
+        if (!d->offsets_dev || !d->chunk_offsets_dev || !d->chunk_indices_dev) return GDN_ERR_INVALID;
+        const int64_t nc = count_chunks(d->offsets_host, d->n_units + 1, BT);
+        if (nc > INT32_MAX / 2) return GDN_ERR_INVALID;
+        um.dense = 0;
+        um.n_units = d->n_units;
+        um.n_chunks = (int32_t)nc;
+        um.offsets = d->offsets_dev;
+        um.chunk_offsets = d->chunk_offsets_dev;
+        um.chunk_indices = d->chunk_indices_dev;
+    }
+    p->H = d->H;
+    p->dtype = d->dtype;
+    p->o_dtype = d->o_dtype;
+    p->per_key = d->gate_kind == GDN_GATE_PER_KEY;
+    p->use_exp2 = d->use_exp2;
+    p->scale = d->scale;
+    p->um = um;
+    return GDN_OK;
+}
+
+gdn_status size_workspace(const gdn::Problem& p, void* workspace, size_t* workspace_bytes,
+                          gdn::Workspace* ws, bool* query_only) {
+    if (workspace_bytes == nullptr) return GDN_ERR_INVALID;
+    const size_t need = gdn::workspace_bytes(p, nullptr, nullptr);
+    *query_only = workspace == nullptr;
+    if (workspace == nullptr) {
+        *workspace_bytes = need;
+        return GDN_OK;
+    }
+    if (*workspace_bytes < need) {
+        *workspace_bytes = need;
+        return GDN_ERR_CAPACITY;
+    }
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return GDN_ERR_INVALID;
+    gdn::workspace_bytes(p, ws, static_cast<char*>(workspace));
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" gdn_status gdn_varlen_meta(const int32_t* offsets, int32_t n_offsets, int32_t total_tokens,
+                                      int32_t chunk_size, int32_t* chunk_indices, int32_t cap_chunks,
+                                      int32_t* chunk_offsets, int32_t* n_chunks_out) {
+    if (chunk_size <= 0 || total_tokens < 1) return GDN_ERR_INVALID;
+    if (!offsets_ok(offsets, n_offsets, total_tokens)) return GDN_ERR_INVALID;
+    const int64_t nc = count_chunks(offsets, n_offsets, chunk_size);
+    if (nc > INT32_MAX) return GDN_ERR_INVALID;
+    if (n_chunks_out) *n_chunks_out = (int32_t)nc;
+    if (chunk_offsets) {
+        int64_t c = 0;
+        for (int32_t i = 0; i + 1 < n_offsets; ++i) {
+            chunk_offsets[i] = (int32_t)c;
+            c += (int64_t(offsets[i + 1]) - offsets[i] + chunk_size - 1) / chunk_size;
+        }
+        chunk_offsets[n_offsets - 1] = (int32_t)c;
+    }
+    if (chunk_indices) {
+        if (cap_chunks < nc) return GDN_ERR_CAPACITY;
+        int64_t c = 0;
+        for (int32_t i = 0; i + 1 < n_offsets; ++i) {
+            const int64_t m = (int64_t(offsets[i + 1]) - offsets[i] + chunk_size - 1) / chunk_size;
+            for (int64_t j = 0; j < m; ++j, ++c) {
+                chunk_indices[2 * c] = i;
+                chunk_indices[2 * c + 1] = (int32_t)j;
+            }
+        }
+    }
+    return GDN_OK;
+}
+
+extern "C" gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                                    const float* g, const void* beta, const float* initial_state,
+                                    void* o, float* final_state, const gdn_slots* slots, int32_t flags,
+                                    void* workspace, size_t* workspace_bytes, hipStream_t stream) {
+    gdn::Problem p;
+    gdn_status st = validate(desc, &p);
+    if (st != GDN_OK) return st;
+    if (flags & ~(GDN_FLAG_REUSE_PREPARED | GDN_FLAG_PREPARE_ONLY)) return GDN_ERR_INVALID;
+    const bool reuse = flags & GDN_FLAG_REUSE_PREPARED, prep_only = flags & GDN_FLAG_PREPARE_ONLY;
+    if (reuse && prep_only) return GDN_ERR_INVALID;
+    gdn::Workspace ws;
+    bool query = false;
+    st = size_workspace(p, workspace, workspace_bytes, &ws, &query);
+    if (st != GDN_OK || query) return st;
+    const bool tokens = p.um.total_tokens > 0;
+    if (tokens && (!k || !g || !beta)) return GDN_ERR_INVALID;
+    if (!prep_only && tokens && (!q || !v || !o)) return GDN_ERR_INVALID;
+    if (p.per_key && !reuse && tokens && !q) return GDN_ERR_INVALID;   // the per-key preparation gates q
+    float* gcs = slots ? slots->g_cumsum : nullptr;
+    float* A = slots ? slots->A : nullptr;
+    float* hs = slots ? slots->h : nullptr;
+    if (!reuse) {
+        if (gdn::launch_prep(p, ws, k, q, g, beta, gcs, A, stream) != hipSuccess) return GDN_ERR_DEVICE;
+    }
+    if (!prep_only) {
+        if (gdn::launch_state(p, ws, q, k, v, beta, initial_state, o, final_state, hs, 0, 0, 0, nullptr,
+                              nullptr, stream) != hipSuccess)
+            return GDN_ERR_DEVICE;
+    }
+    return GDN_OK;
+}
+
+extern "C" gdn_status gdn_state_summary(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                                        const float* g, const void* beta, int32_t mode, float* S_ext, float* M,
+                                        void* workspace, size_t* workspace_bytes, hipStream_t stream) {
+    gdn::Problem p;
+    gdn_status st = validate(desc, &p);
+    if (st != GDN_OK) return st;
+    if (mode < 0 || mode > 2) return GDN_ERR_INVALID;
+    const bool want_ext = mode != 2, want_M = mode != 1;
+    gdn::Workspace ws;
+    bool query = false;
+    st = size_workspace(p, workspace, workspace_bytes, &ws, &query);
+    if (st != GDN_OK || query) return st;
+    if ((want_ext && !S_ext) || (want_M && !M)) return GDN_ERR_INVALID;
+    const bool tokens = p.um.total_tokens > 0;
+    if (tokens && (!k || !v || !g || !beta)) return GDN_ERR_INVALID;
+    if (gdn::launch_prep(p, ws, k, q, g, beta, nullptr, nullptr, stream) != hipSuccess)
+        return GDN_ERR_DEVICE;
+    if (gdn::launch_state(p, ws, nullptr, k, v, beta, nullptr, nullptr, nullptr, nullptr, 1, want_ext,
+                          want_M, S_ext, M, stream) != hipSuccess)
+        return GDN_ERR_DEVICE;
+    return GDN_OK;
+}
+
+extern "C" gdn_status gdn_state_merge(int32_t B, int32_t H, int32_t n_seg, int32_t K, int32_t V,
+                                      const float* S_ext, const float* M, const float* S0, float* S_init,
+                                      float* S_final, hipStream_t stream) {
+    if (K != DK || V != DV) return GDN_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || n_seg < 0) return GDN_ERR_INVALID;
+    if (int64_t(B) * H * n_seg * DK * DK > kMaxElems) return GDN_ERR_INVALID;
+    if (n_seg > 0 && (!S_ext || !M || !S_init)) return GDN_ERR_INVALID;
+    if (gdn::launch_merge(B, H, n_seg, S_ext, M, S0, S_init, S_final, stream) != hipSuccess)
+        return GDN_ERR_DEVICE;
+    return GDN_OK;
+}

@@ -1,0 +1,68 @@
+// Internal interface between the host API (gdn_host.cpp) and the HIP kernels
+// (gdn_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace gdn {
+
+constexpr int BT = 64;    // tokens per chunk
+constexpr int DK = 128;   // key width
+constexpr int DV = 128;   // value width
+constexpr int BV = 32;    // value columns per state-pass workgroup
+
+// Where every chunk of every unit lives on the flat token axis.
+struct UnitMap {
+    int32_t n_units;             // number of units (B when dense)
+    int32_t dense;               // 1: unit b = tokens [b*T, (b+1)*T), no device metadata
+    int32_t T;                   // dense row length
+    int32_t n_chunks;            // total chunks over all units
+    int32_t nt_dense;            // chunks per dense row
+    int64_t total_tokens;
+    const int32_t* offsets;      // device [n_units + 1] (NULL when dense)
+    const int32_t* chunk_offsets;// device [n_units + 1]
+    const int32_t* chunk_indices;// device [n_chunks][2]
+};
+
+// Workspace regions, all device pointers inside the caller's workspace.
+struct Workspace {
+    float* Tm;       // [n_chunks][H][64][64]  (I + L)^{-1}
+    float* gam;      // [n_chunks][H][64]      chunk-local cumulative gate (scalar gate)
+    // per-key gate only
+    float* P;        // [n_chunks][H][64][64]  intra-chunk decayed q.k, lower incl. diagonal
+    void* qg;        // planes x [n_chunks][H][64][K]  q * b^G
+    void* kd;        // [n_chunks][H][64][K]            k * b^G (one plane)
+    void* kg;        // planes x [n_chunks][H][64][K]  k * b^{G_last - G}
+    float* gamL;     // [n_chunks][H][K]       G at the chunk's last valid token
+    int64_t plane;   // elements between the hi and lo planes of qg / kg
+};
+
+struct Problem {
+    int32_t H;
+    int32_t dtype;      // 0 fp32, 1 bf16
+    int32_t o_dtype;
+    int32_t per_key;
+    int32_t use_exp2;
+    float scale;
+    UnitMap um;
+};
+
+size_t workspace_bytes(const Problem& p, Workspace* ws, char* base);
+
+hipError_t launch_prep(const Problem& p, const Workspace& ws, const void* k, const void* q,
+                       const float* g, const void* beta, float* g_cumsum_slot, float* A_slot,
+                       hipStream_t s);
+
+// mode: 0 forward; 1 summary (S_ext and/or M)
+hipError_t launch_state(const Problem& p, const Workspace& ws, const void* q, const void* k,
+                        const void* v, const void* beta, const float* h0, void* o,
+                        float* hfinal, float* hslot, int summary, int want_ext, int want_M,
+                        float* S_ext, float* M, hipStream_t s);
+
+hipError_t launch_merge(int B, int H, int n_seg, const float* S_ext, const float* M,
+                        const float* S0, float* S_init, float* S_final, hipStream_t s);
+
+}  // namespace gdn

@@ -1,0 +1,210 @@
+/*
+ * gdn.h - C ABI of the chunkwise gated delta rule forward on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation (gated delta rule problem statement; chunked evaluation as in
+ * the chunk_gated_delta_rule_fwd adapter on the hyper-parallel "Diff
+ * Coverage" page, _AscendCGDN.forward): for every head of every unit (a batch
+ * row, a packed document, or a segment of a row) with state h in K x V,
+ *
+ *     h_t = (I - beta_t k_t k_t^T) Diag(b^{g_t}) h_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * h_t^T q_t
+ *
+ * where b = e (use_exp2 = 0) or 2 (use_exp2 = 1) and g_t is a scalar per
+ * (token, head) or, for a per-key gate, a K-vector (the KDA form of the
+ * state_summary.py coverage page, whose chunk recurrence decays the state
+ * before the delta update; for a scalar gate both orders coincide). The work
+ * is done in chunks of 64 tokens.
+ *
+ * Conventions (all taken from the pages' adapters):
+ *   - K = V = 128 and chunk_size = 64 are the supported shapes.
+ *   - Layout BSND: q, k [B,T,H,K], v [B,T,H,V], g [B,T,H] or [B,T,H,K],
+ *     beta [B,T,H]. Layout TND: the same with B = 1 and no batch axis, with
+ *     document offsets (cu_seqlens). Both are row-major and contiguous.
+ *   - g and beta are used as given: no sigmoid, no L2 norm, no gate
+ *     activation inside (normalisation happens before the core).
+ *   - scale multiplies the output; callers normally pass 1/sqrt(K).
+ *   - The state is K x V (key-major, "state_v_first = False").
+ *
+ * Memory: every pointer argument marked "device" is HIP device memory owned
+ * by the caller; inputs are never written. The library allocates nothing,
+ * never synchronises and keeps no global state: all work is enqueued on the
+ * given stream, in order. Scratch memory is the caller's workspace
+ * (query its size with workspace == NULL).
+ *
+ * Errors: every check runs on the host before the first HIP call, so a
+ * rejected call enqueues nothing. GDN_ERR_INVALID is a contract violation
+ * (the pages raise ValueError), GDN_ERR_UNSUPPORTED a shape or feature this
+ * build does not implement (NotImplementedError), GDN_ERR_DEVICE a HIP
+ * launch failure (RuntimeError), GDN_ERR_CAPACITY a too-small caller buffer.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_INVALID = 1,
+    GDN_ERR_UNSUPPORTED = 2,
+    GDN_ERR_DEVICE = 3,
+    GDN_ERR_CAPACITY = 4
+} gdn_status;
+
+enum { GDN_LAYOUT_BSND = 0, GDN_LAYOUT_TND = 1 };
+enum { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 };
+enum { GDN_GATE_SCALAR = 0, GDN_GATE_PER_KEY = 1 };
+
+/* gdn_chunk_fwd flags */
+enum {
+    GDN_FLAG_REUSE_PREPARED = 1, /* skip chunk preparation: the workspace already
+                                    holds it (from gdn_state_summary or a
+                                    GDN_FLAG_PREPARE_ONLY call with the same
+                                    descriptor and inputs) */
+    GDN_FLAG_PREPARE_ONLY = 2    /* run chunk preparation only */
+};
+
+/*
+ * Problem descriptor.
+ *
+ * Units are contiguous token ranges on the flat token axis (BSND [B,T,...]
+ * is viewed as [B*T,...]). With n_units = 0 the units are the B rows of T
+ * tokens. Otherwise offsets_host holds n_units + 1 strictly increasing token
+ * offsets from 0 to B*T (the _packed_offsets rules of the Diff Coverage
+ * page): for TND (B must be 1) they are the documents' cu_seqlens; for BSND
+ * they are segments, and every row start b*T must be one of them (a unit
+ * never crosses rows). The device arrays are the caller's device copies of
+ * the unit offsets and of the chunk metadata that gdn_varlen_meta computes
+ * for them; kernels read only these and clamp to the token range, so a
+ * mismatch gives wrong results, never out-of-range accesses.
+ */
+typedef struct {
+    int32_t B, T, H, K, V;      /* TND: B = 1 and T = total packed tokens */
+    int32_t layout;             /* GDN_LAYOUT_* */
+    int32_t dtype;              /* q, k, v, beta: GDN_DTYPE_*; g is always fp32 */
+    int32_t o_dtype;            /* output o: GDN_DTYPE_* (fp32 keeps the full
+                                   accuracy of the fp32 accumulation) */
+    int32_t gate_kind;          /* GDN_GATE_* */
+    int32_t use_exp2;           /* 0: decay e^g, 1: decay 2^g */
+    int32_t chunk_size;         /* must be 64 */
+    float scale;                /* output scale */
+    int32_t n_units;            /* 0: dense rows; else entries of offsets - 1 */
+    const int32_t* offsets_host;       /* host   [n_units + 1] */
+    const int32_t* offsets_dev;        /* device [n_units + 1] */
+    const int32_t* chunk_offsets_dev;  /* device [n_units + 1], from gdn_varlen_meta */
+    const int32_t* chunk_indices_dev;  /* device [n_chunks][2], from gdn_varlen_meta */
+} gdn_desc;
+
+/*
+ * Optional extra outputs of gdn_chunk_fwd (any pointer may be NULL; the
+ * struct pointer itself may be NULL). These are the saved-for-backward slots
+ * of the native forward on the Diff Coverage page (g_cumsum, A, h).
+ *   g_cumsum: device fp32, token-major like g ([tokens][H] or
+ *             [tokens][H][K]): the gate's inclusive cumulative sum inside
+ *             each 64-token chunk of each unit.
+ *   A:        device fp32 [tokens][H][64]: row i of the chunk's
+ *             T = (I + L)^{-1}, L_ij = beta_i (k_i . k_j) b^{G_i - G_j}
+ *             (per key: beta_i sum_d k_id k_jd b^{G_id - G_jd}) for j < i,
+ *             the WY inverse that turns the chunk into dense products.
+ *   h:        device fp32 [n_chunks][H][K][V]: the state entering every
+ *             chunk (chunks ordered by unit, then position in the unit).
+ */
+typedef struct {
+    float* g_cumsum;
+    float* A;
+    float* h;
+} gdn_slots;
+
+/*
+ * gdn_varlen_meta - chunk metadata of packed sequences (host only).
+ * _packed_metadata on the Diff Coverage page: every unit of length L
+ * contributes ceil(L / chunk_size) chunks, listed unit-major as
+ * (unit index, chunk index in the unit) int32 pairs.
+ *
+ *   offsets        host [n_offsets]: 0 = c_0 < c_1 < ... < c_N = total_tokens
+ *   chunk_indices  host [cap_chunks][2] or NULL (count only)
+ *   chunk_offsets  host [n_offsets] or NULL: first chunk of every unit, then
+ *                  the total chunk count
+ *   n_chunks_out   receives the chunk count (also on GDN_ERR_CAPACITY)
+ * Errors: GDN_ERR_INVALID for offsets that break the rules or chunk_size <= 0;
+ * GDN_ERR_CAPACITY when chunk_indices is given and cap_chunks is too small.
+ */
+gdn_status gdn_varlen_meta(const int32_t* offsets, int32_t n_offsets, int32_t total_tokens,
+                           int32_t chunk_size, int32_t* chunk_indices, int32_t cap_chunks,
+                           int32_t* chunk_offsets, int32_t* n_chunks_out);
+
+/*
+ * gdn_chunk_fwd - the chunked forward: gate cumulative sums, the A build and
+ * its 64 x 64 triangular inverse (chunk preparation), then the inter-chunk
+ * state pass fused with the output.
+ *
+ *   q, k           device [tokens][H][K] in desc->dtype
+ *   v              device [tokens][H][V] in desc->dtype
+ *   g              device fp32 [tokens][H] (scalar) or [tokens][H][K] (per key)
+ *   beta           device [tokens][H] in desc->dtype
+ *   initial_state  device fp32 [units][H][K][V] or NULL (zero state)
+ *   o              device [tokens][H][V] in desc->o_dtype
+ *   final_state    device fp32 [units][H][K][V] or NULL
+ *   slots          optional extra outputs (see gdn_slots) or NULL
+ *   flags          GDN_FLAG_* bits
+ *   workspace      device scratch of *workspace_bytes bytes, 256-byte
+ *                  aligned; NULL: only store the required size in
+ *                  *workspace_bytes and return GDN_OK
+ *   stream         HIP stream the work is enqueued on
+ * With GDN_FLAG_PREPARE_ONLY, q, v, o, initial_state and final_state are not
+ * used and may be NULL.
+ */
+gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                         const float* g, const void* beta, const float* initial_state, void* o,
+                         float* final_state, const gdn_slots* slots, int32_t flags,
+                         void* workspace, size_t* workspace_bytes, hipStream_t stream);
+
+/*
+ * gdn_state_summary - affine summary of every unit (kda_split_state_summary_kernel
+ * on the state_summary.py coverage page): running a unit from an entry state
+ * S gives the exit state M S + S_ext, with
+ *   S_ext  device fp32 [units][H][K][V]: the exit state from a zero entry
+ *   M      device fp32 [units][H][K][K]: the transfer map (I at an empty unit)
+ *   mode   0: both, 1: S_ext only (M may be NULL), 2: M only (S_ext may be NULL)
+ *   q      device [tokens][H][K] or NULL. The summaries do not read it; with a
+ *          per-key gate the chunk preparation that a later reusing forward
+ *          needs includes q * b^G and the decayed q.k products, which are
+ *          only prepared when q is given.
+ * Units are those of desc (normally the segments of a sequence split). The
+ * chunk preparation is left in the workspace, so a following gdn_chunk_fwd
+ * with the same descriptor, inputs and workspace may pass
+ * GDN_FLAG_REUSE_PREPARED (the correction pass of a split scan); with a
+ * per-key gate that requires q here.
+ */
+gdn_status gdn_state_summary(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                             const float* g, const void* beta, int32_t mode, float* S_ext, float* M,
+                             void* workspace, size_t* workspace_bytes, hipStream_t stream);
+
+/*
+ * gdn_state_merge - composes segment summaries in order (apply_kda_state_summary
+ * on the Diff Coverage page; the exclusive prefix of the Sana
+ * distributed_scan.py page):
+ *   S_init[b][0] = S0[b] (zero when S0 == NULL)
+ *   S_init[b][s+1] = M[b][s] S_init[b][s] + S_ext[b][s]   (fp32)
+ *   S_ext   device fp32 [B][n_seg][H][K][V]
+ *   M       device fp32 [B][n_seg][H][K][K]
+ *   S0      device fp32 [B][H][K][V] or NULL
+ *   S_init  device fp32 [B][n_seg][H][K][V]: the state entering every segment
+ *   S_final device fp32 [B][H][K][V] or NULL: the state after the last segment
+ */
+gdn_status gdn_state_merge(int32_t B, int32_t H, int32_t n_seg, int32_t K, int32_t V,
+                           const float* S_ext, const float* M, const float* S0, float* S_init,
+                           float* S_final, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

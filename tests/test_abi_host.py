@@ -1,0 +1,198 @@
+"""Host-side checks of libgdn (no GPU): exported symbols, the chunk metadata
+(bit-exact against the oracle's definition) and every validation error,
+which the library raises before any HIP call."""
+import ctypes
+import os
+import random
+import re
+
+import pytest
+
+from chunked_gated_delta_05_amd import binding as gb
+from oracle import varlen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    return sorted(set(re.findall(r"^gdn_status\s+(gdn_\w+)\s*\(", src, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert names == ["gdn_chunk_fwd", "gdn_state_merge", "gdn_state_summary", "gdn_varlen_meta"]
+    L = gb.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+# ------------------------------------------------------------------ varlen metadata
+@pytest.mark.parametrize("lens", [[1], [63], [64], [65], [1, 1, 1], [128, 1, 64, 65, 200], [4000] * 3 + [100]])
+def test_varlen_meta_matches_definition(lens):
+    offs = [0]
+    for x in lens:
+        offs.append(offs[-1] + x)
+    ci, co = gb.gdn_varlen_meta(offs, offs[-1])
+    assert [tuple(r) for r in ci.tolist()] == varlen.chunk_indices(offs)
+    assert co.tolist() == varlen.chunk_offsets(offs)
+
+
+def test_varlen_meta_random():
+    rnd = random.Random(11)
+    for _ in range(200):
+        lens = [rnd.randint(1, 500) for _ in range(rnd.randint(1, 30))]
+        offs = [0]
+        for x in lens:
+            offs.append(offs[-1] + x)
+        ci, co = gb.gdn_varlen_meta(offs, offs[-1])
+        assert [tuple(r) for r in ci.tolist()] == varlen.chunk_indices(offs)
+        assert co.tolist() == varlen.chunk_offsets(offs)
+
+
+@pytest.mark.parametrize("offs,total", [([0], 0), ([1, 5], 5), ([0, 5], 6), ([0, 5, 5, 9], 9),
+                                        ([0, 6, 5, 9], 9), ([0, 4.0, 9], 9), ([0, True, 9], 9)])
+def test_varlen_meta_rejects(offs, total):
+    assert not varlen.valid_offsets(offs, total)
+    with pytest.raises(ValueError):
+        gb.gdn_varlen_meta(offs, total)
+
+
+def test_varlen_meta_capacity():
+    offs = (ctypes.c_int32 * 3)(0, 100, 300)
+    ci = (ctypes.c_int32 * 4)()
+    n = ctypes.c_int32(0)
+    st = gb.lib().gdn_varlen_meta(offs, 3, 300, 64, ci, 2, None, ctypes.byref(n))
+    assert st == gb.GDN_ERR_CAPACITY and n.value == 6   # ceil(100/64) + ceil(200/64)
+
+
+# ------------------------------------------------------------------ validation
+def desc(**kw):
+    d = gb.GdnDesc()
+    d.B, d.T, d.H, d.K, d.V = 2, 200, 3, 128, 128
+    d.layout, d.dtype, d.o_dtype, d.gate_kind, d.use_exp2 = 0, 1, 0, 0, 0
+    d.chunk_size, d.scale, d.n_units = 64, 0.0883883, 0
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+FAKE = 1 << 20   # an aligned non-null "device" address; never dereferenced
+
+
+def fwd(d, *, ws=FAKE, nbytes=None, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o=FAKE, flags=0):
+    nb = ctypes.c_size_t(nbytes if nbytes is not None else (1 << 40))
+    return gb.lib().gdn_chunk_fwd(ctypes.byref(d), q, k, v, g, beta, None, o, None, None, flags, ws,
+                                  ctypes.byref(nb), None), nb.value
+
+
+def test_workspace_query_sizes():
+    st, nb = fwd(desc(), ws=None)
+    # T: 64x64 fp32 + gate cumsum 64 fp32 per chunk-head, each region 256-aligned
+    nch = 2 * 4 * 3
+    expect = ((nch * 64 * 64 * 4 + 255) // 256) * 256 + ((nch * 64 * 4 + 255) // 256) * 256
+    assert st == gb.GDN_OK and nb == expect
+    st, nb2 = fwd(desc(gate_kind=1), ws=None)
+    assert st == gb.GDN_OK and nb2 > nb
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"chunk_size": 32}, gb.GDN_ERR_INVALID),
+    ({"K": 64, "V": 64}, gb.GDN_ERR_UNSUPPORTED),
+    ({"V": 64}, gb.GDN_ERR_UNSUPPORTED),
+    ({"B": 0}, gb.GDN_ERR_INVALID),
+    ({"H": 0}, gb.GDN_ERR_INVALID),
+    ({"T": -1}, gb.GDN_ERR_INVALID),
+    ({"layout": 5}, gb.GDN_ERR_INVALID),
+    ({"dtype": 7}, gb.GDN_ERR_INVALID),
+    ({"o_dtype": 3}, gb.GDN_ERR_INVALID),
+    ({"gate_kind": 2}, gb.GDN_ERR_INVALID),
+    ({"use_exp2": 2}, gb.GDN_ERR_INVALID),
+    ({"scale": float("nan")}, gb.GDN_ERR_INVALID),
+    ({"layout": 1}, gb.GDN_ERR_INVALID),            # TND needs offsets and B = 1
+    ({"n_units": -1}, gb.GDN_ERR_INVALID),
+])
+def test_descriptor_errors(kw, code):
+    st, _ = fwd(desc(**kw))
+    assert st == code
+
+
+def _with_offsets(offs, **kw):
+    arr = (ctypes.c_int32 * len(offs))(*offs)
+    d = desc(n_units=len(offs) - 1, offsets_host=ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)),
+             offsets_dev=FAKE, chunk_offsets_dev=FAKE, chunk_indices_dev=FAKE, **kw)
+    return d, arr
+
+
+@pytest.mark.parametrize("offs,kw,code", [
+    ([0, 100, 200, 400], {}, gb.GDN_OK),                          # segments of rows 0 and 1
+    ([0, 100, 400], {}, gb.GDN_ERR_INVALID),                      # a unit crossing the row start 200
+    ([0, 150, 400], {}, gb.GDN_ERR_INVALID),
+    ([0, 100, 100, 400], {}, gb.GDN_ERR_INVALID),                 # empty unit
+    ([0, 300, 200, 400], {}, gb.GDN_ERR_INVALID),                 # decreasing
+    ([0, 100, 399], {}, gb.GDN_ERR_INVALID),                      # does not end at B*T
+    ([5, 100, 400], {}, gb.GDN_ERR_INVALID),                      # does not start at 0
+    ([0, 100, 200, 400], {"layout": 1}, gb.GDN_ERR_INVALID),      # TND with B = 2
+    ([0, 7, 200], {"layout": 1, "B": 1}, gb.GDN_OK),              # TND documents
+])
+def test_offset_errors(offs, kw, code):
+    d, arr = _with_offsets(offs, **kw)
+    st, _ = fwd(d, ws=None)
+    assert st == code
+
+
+def test_missing_device_metadata():
+    d, arr = _with_offsets([0, 7, 200], layout=1, B=1)
+    d.chunk_indices_dev = None
+    assert fwd(d, ws=None)[0] == gb.GDN_ERR_INVALID
+
+
+def test_workspace_errors():
+    st, need = fwd(desc(), ws=None)
+    assert st == gb.GDN_OK
+    st, nb = fwd(desc(), nbytes=need - 1)
+    assert st == gb.GDN_ERR_CAPACITY and nb == need
+    assert fwd(desc(), ws=FAKE + 128)[0] == gb.GDN_ERR_INVALID          # not 256-byte aligned
+    nb = ctypes.c_size_t(0)
+    assert gb.lib().gdn_chunk_fwd(ctypes.byref(desc()), None, None, None, None, None, None, None, None,
+                                  None, 0, None, None, None) == gb.GDN_ERR_INVALID   # no size pointer
+    assert gb.lib().gdn_chunk_fwd(None, None, None, None, None, None, None, None, None, None, 0, None,
+                                  ctypes.byref(nb), None) == gb.GDN_ERR_INVALID   # no descriptor
+
+
+@pytest.mark.parametrize("missing", ["q", "k", "v", "g", "beta", "o"])
+def test_missing_tensors(missing):
+    st, _ = fwd(desc(), **{missing: None})
+    assert st == gb.GDN_ERR_INVALID
+
+
+def test_flag_errors():
+    assert fwd(desc(), flags=3)[0] == gb.GDN_ERR_INVALID
+    assert fwd(desc(), flags=8)[0] == gb.GDN_ERR_INVALID
+
+
+def test_summary_and_merge_errors():
+    L = gb.lib()
+    nb = ctypes.c_size_t(1 << 40)
+    d, arr = _with_offsets([0, 100, 200, 300, 400])   # two segments per row
+    for mode in (-1, 3):
+        assert L.gdn_state_summary(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, mode, FAKE, FAKE, FAKE,
+                                   ctypes.byref(nb), None) == gb.GDN_ERR_INVALID
+    # mode 1 needs S_ext, mode 2 needs M
+    assert L.gdn_state_summary(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, 1, None, FAKE, FAKE,
+                               ctypes.byref(nb), None) == gb.GDN_ERR_INVALID
+    assert L.gdn_state_summary(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, 2, FAKE, None, FAKE,
+                               ctypes.byref(nb), None) == gb.GDN_ERR_INVALID
+    assert L.gdn_state_merge(2, 3, 4, 64, 64, FAKE, FAKE, None, FAKE, None, None) == gb.GDN_ERR_UNSUPPORTED
+    assert L.gdn_state_merge(2, 3, -1, 128, 128, FAKE, FAKE, None, FAKE, None, None) == gb.GDN_ERR_INVALID
+    assert L.gdn_state_merge(0, 3, 4, 128, 128, FAKE, FAKE, None, FAKE, None, None) == gb.GDN_ERR_INVALID
+    assert L.gdn_state_merge(2, 3, 4, 128, 128, None, FAKE, None, FAKE, None, None) == gb.GDN_ERR_INVALID
+
+
+def test_status_maps_to_page_exceptions():
+    with pytest.raises(ValueError):
+        gb.check(gb.GDN_ERR_INVALID, "x")
+    with pytest.raises(NotImplementedError):
+        gb.check(gb.GDN_ERR_UNSUPPORTED, "x")
+    with pytest.raises(RuntimeError):
+        gb.check(gb.GDN_ERR_DEVICE, "x")

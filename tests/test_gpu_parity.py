@@ -1,0 +1,320 @@
+"""Parity of the HIP forward (through the C ABI) with the fp64 oracle.
+
+Tolerances: max |x - oracle| <= tol * rms(oracle) with tol = 1e-4 for fp32
+inputs and 2e-2 for bf16 inputs (fp32 accumulation, fp32 output o). Exact
+cases (zero writes, basis-key tables) are compared bit for bit.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from chunked_gated_delta_05_amd import binding as gb
+from chunked_gated_delta_05_amd import workloads as W
+from tests.gpu_helpers import TOL, assert_close, flat_inputs, np32, rel_err, unit_offsets
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def small(B=1, T=200, H=3, dtype="bf16", per_key=False, use_exp2=False, gate_coef=0.1,
+          layout="BSND", n_docs=0, doc_len=(100, 4000), n_seg=0):
+    return W.Workload("small", B=B, T=T, H=H, dtype=dtype, layout=layout, gate_per_key=per_key,
+                      use_exp2=use_exp2, gate_coef=gate_coef, n_docs=n_docs, doc_len=doc_len,
+                      n_seg=n_seg)
+
+
+def to_dev(d):
+    out = dict(d)
+    for n in ("q", "k", "v", "g", "beta"):
+        out[n] = d[n].to(DEV)
+    return out
+
+
+def run_gpu(d, meta=None, **kw):
+    w = d["workload"]
+    if meta is None and d["offsets"] is not None and w.layout == "TND":
+        meta = gb.make_meta(d["offsets"], w.T, DEV)
+    o, fin, ex = gb.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], meta=meta,
+                                  use_exp2=w.use_exp2, **kw)
+    torch.cuda.synchronize()
+    return o, fin, ex
+
+
+def run_oracle(d, offsets=None, heads=None, S0=None, **kw):
+    q, k, v, g, beta = flat_inputs(d)
+    w = d["workload"]
+    return oracle.fwd(q, k, v, g, beta, offsets or unit_offsets(d), d["scale"],
+                      gate_per_key=w.gate_per_key, use_exp2=w.use_exp2, heads=heads, S0=S0, **kw)
+
+
+def flat_o(o, w):
+    return np32(o.reshape(-1, *o.shape[2:]) if w.layout == "BSND" else o)
+
+
+# ------------------------------------------------------------------ small shapes
+@pytest.mark.parametrize("B,T,H", [(1, 64, 1), (2, 200, 3), (1, 1, 2), (1, 130, 2), (3, 63, 1)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_dense_small(B, T, H, dtype):
+    print(f"dense B={B} T={T} H={H} {dtype}", flush=True)
+    d = to_dev(W.generate(small(B=B, T=T, H=H, dtype=dtype), 11 + T))
+    o, fin, ex = run_gpu(d, output_final_state=True, want_h=True, want_g_cumsum=True)
+    r = run_oracle(d, chunk_states=True)
+    w = d["workload"]
+    tol = TOL[dtype]
+    assert_close(flat_o(o, w), r["o"], tol, "o")
+    assert_close(np32(fin), r["final"], tol, "final state")
+    assert_close(np32(ex["h"]), r["chunk_states"], tol, "chunk entry states")
+    gc = np32(ex["g_cumsum"]).reshape(B, T, H)
+    ref = np.zeros((B, T, H))
+    gg = np32(d["g"]).astype(np.float64)
+    for c0 in range(0, T, 64):
+        ref[:, c0:c0 + 64] = np.cumsum(gg[:, c0:c0 + 64], axis=1)
+    np.testing.assert_allclose(gc, ref, rtol=1e-5, atol=1e-5)
+
+
+def test_tiny_fp32_workload():
+    d = to_dev(W.generate(W.WORKLOADS[0], 1000))
+    o, fin, _ = run_gpu(d, output_final_state=True)
+    r = run_oracle(d)
+    e = assert_close(flat_o(o, d["workload"]), r["o"], TOL["fp32"], "o")
+    assert_close(np32(fin), r["final"], TOL["fp32"], "final")
+    print(f"gdn_tiny_fp32 o err/rms {e:.2e}")
+
+
+def test_initial_state_and_resume():
+    d = to_dev(W.generate(small(B=2, T=256, H=2), 5))
+    S0 = torch.randn(2, 2, 128, 128, device=DEV) * 0.3
+    o, fin, _ = run_gpu(d, initial_state=S0, output_final_state=True)
+    r = run_oracle(d, S0=np32(S0).astype(np.float64))
+    assert_close(flat_o(o, d["workload"]), r["o"], TOL["bf16"], "o with S0")
+    assert_close(np32(fin), r["final"], TOL["bf16"], "final with S0")
+    # two calls over [0,128) and [128,256) with the state handed over
+    half = {n: d[n][:, :128].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    rest = {n: d[n][:, 128:].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    for x in (half, rest):
+        x.update(scale=d["scale"], offsets=None, workload=small(B=2, T=128, H=2))
+    o1, f1, _ = run_gpu(half, initial_state=S0, output_final_state=True)
+    o2, f2, _ = run_gpu(rest, initial_state=f1, output_final_state=True)
+    np.testing.assert_allclose(np32(torch.cat([o1, o2], 1)), np32(o), rtol=0, atol=1e-4 * float(o.abs().max()))
+    np.testing.assert_allclose(np32(f2), np32(fin), rtol=0, atol=1e-4 * float(fin.abs().max()))
+
+
+def test_prep_slots_inverse_residual():
+    # A slot: T = (I + L)^{-1}; check (I + L) T = I with L rebuilt in fp64
+    d = to_dev(W.generate(small(B=1, T=150, H=2), 21))
+    _, _, ex = run_gpu(d, want_A=True)
+    A = np32(ex["A"]).astype(np.float64)            # [T, H, 64]
+    k = np32(d["k"][0]).astype(np.float64)
+    beta = np32(d["beta"][0]).astype(np.float64)
+    g = np32(d["g"][0]).astype(np.float64)
+    for h in range(2):
+        for c0 in range(0, 150, 64):
+            n = min(64, 150 - c0)
+            G = np.cumsum(g[c0:c0 + n, h])
+            kk = k[c0:c0 + n, h]
+            L = np.tril(beta[c0:c0 + n, h, None] * (kk @ kk.T) * np.exp(G[:, None] - G[None, :]), -1)
+            Tm = A[c0:c0 + n, h, :n]
+            res = (np.eye(n) + L) @ Tm - np.eye(n)
+            assert np.abs(res).max() < 1e-5, np.abs(res).max()
+
+
+# ------------------------------------------------------------------ exact cases
+def test_beta_zero_gives_exact_zero():
+    d = to_dev(W.generate(small(B=2, T=190, H=2), 31))
+    d["beta"] = torch.zeros_like(d["beta"])
+    o, fin, _ = run_gpu(d, output_final_state=True)
+    assert torch.count_nonzero(o).item() == 0 and torch.count_nonzero(fin).item() == 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_basis_key_table_exact(dtype):
+    # g = 0, beta = 1, keys and queries are basis vectors, integer values,
+    # scale 2^-3: every intermediate is an exact small integer, so the GPU
+    # must match the table read-out bit for bit
+    rng = np.random.default_rng(3)
+    T, H = 300, 2
+    widx = rng.integers(0, 128, (T, H)); qidx = rng.integers(0, 128, (T, H))
+    widx[:, 1] = rng.integers(0, 6, T)                   # many rewrites of few keys
+    dt = W.torch_dtype(dtype)
+    eye = torch.eye(128)
+    k = eye[torch.from_numpy(widx)].to(dt)[None]
+    q = eye[torch.from_numpy(qidx)].to(dt)[None]
+    v = torch.from_numpy(rng.integers(-8, 9, (1, T, H, 128)).astype(np.float32)).to(dt)
+    d = {"q": q.to(DEV), "k": k.to(DEV), "v": v.to(DEV), "g": torch.zeros(1, T, H, device=DEV),
+         "beta": torch.ones(1, T, H, dtype=dt, device=DEV), "scale": 0.125, "offsets": None,
+         "workload": small(B=1, T=T, H=H, dtype=dtype)}
+    o, _, _ = run_gpu(d)
+    out = np32(o[0])
+    vv = np32(v[0])
+    for h in range(H):
+        table = np.zeros((128, 128), np.float32)
+        for t in range(T):
+            table[widx[t, h]] = vv[t, h]
+            assert np.array_equal(out[t, h], 0.125 * table[qidx[t, h]]), (t, h)
+
+
+def test_total_forgetting():
+    d = to_dev(W.generate(small(B=1, T=200, H=2), 41))
+    d["g"] = torch.full_like(d["g"], -1e4)
+    o, _, _ = run_gpu(d)
+    q, k, v, beta = (np32(d[n][0]).astype(np.float64) for n in ("q", "k", "v", "beta"))
+    ref = d["scale"] * (beta * np.einsum("thk,thk->th", q, k))[..., None] * v
+    assert_close(np32(o[0]), ref, 1e-3, "total forgetting")
+
+
+def test_orthonormal_keys_retrieve():
+    # g = 0, beta = 1, an orthonormal key set (fp32 inputs): querying a key
+    # written once returns its value
+    rng = np.random.default_rng(8)
+    Qm, _ = np.linalg.qr(rng.standard_normal((128, 128)))
+    T = 128
+    k = torch.from_numpy(np.ascontiguousarray(Qm.T.astype(np.float32)))[None, :, None, :].contiguous()
+    v = torch.from_numpy(rng.standard_normal((1, T, 1, 128)).astype(np.float32))
+    d = {"q": k.to(DEV), "k": k.to(DEV), "v": v.to(DEV), "g": torch.zeros(1, T, 1, device=DEV),
+         "beta": torch.ones(1, T, 1, device=DEV), "scale": 1.0, "offsets": None,
+         "workload": small(B=1, T=T, H=1, dtype="fp32")}
+    _, fin, _ = run_gpu(d, output_final_state=True)
+    S = np32(fin[0, 0]).astype(np.float64)
+    got = Qm.T @ S
+    np.testing.assert_allclose(got, np32(v[0, :, 0]), atol=1e-4)
+
+
+# ------------------------------------------------------------------ varlen
+def test_varlen_packed_matches_oracle_and_separate_runs():
+    lens = [1, 63, 64, 65, 200, 7, 128]
+    cu = W.cu_from_lengths(lens)
+    T = cu[-1]
+    base = W.generate(small(B=1, T=T, H=3), 51)
+    d = {n: base[n][0].contiguous().to(DEV) for n in ("q", "k", "v", "g", "beta")}
+    d.update(scale=base["scale"], offsets=cu, workload=small(B=1, T=T, H=3, layout="TND", n_docs=len(lens)))
+    o, fin, _ = run_gpu(d, output_final_state=True)
+    r = run_oracle(d)
+    assert_close(np32(o), r["o"], TOL["bf16"], "packed o")
+    assert_close(np32(fin), r["final"], TOL["bf16"], "packed final")
+    for i, (a, b) in enumerate(zip(cu, cu[1:])):
+        sep = {n: d[n][a:b][None].contiguous() for n in ("q", "k", "v", "g", "beta")}
+        sep.update(scale=d["scale"], offsets=None, workload=small(B=1, T=b - a, H=3))
+        o1, f1, _ = run_gpu(sep, output_final_state=True)
+        assert torch.equal(o1[0], o[a:b]), f"document {i} differs from its separate run"
+        assert torch.equal(f1[0], fin[i])
+
+
+# ------------------------------------------------------------------ per-key + split
+@pytest.mark.parametrize("seg", [[0, 128, 256], [0, 100, 190, 256], [0, 64, 65, 200, 256]])
+def test_split_equals_unsplit_slow_decay(seg):
+    # slow per-key decay keeps M far from zero, so a wrong M cannot hide
+    w = small(B=2, T=256, H=2, per_key=True, use_exp2=True, gate_coef=0.001)
+    d = to_dev(W.generate(w, 61 + len(seg)))
+    S0 = (torch.randn(2, 2, 128, 128, device=DEV) * 0.5).contiguous()
+    o_u, f_u, _ = run_gpu(d, initial_state=S0, output_final_state=True)
+    o_s, f_s, S_init = gb.split_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"],
+                                        seg=seg, use_exp2=True, initial_state=S0)
+    torch.cuda.synchronize()
+    r = run_oracle(d, S0=np32(S0).astype(np.float64))
+    assert_close(np32(o_u.reshape(-1, 2, 128)), r["o"], TOL["bf16"], "unsplit o")
+    assert_close(np32(o_s.reshape(-1, 2, 128)), r["o"], TOL["bf16"], "split o")
+    assert_close(np32(f_s), r["final"], TOL["bf16"], "split final")
+    assert_close(np32(f_u), r["final"], TOL["bf16"], "unsplit final")
+    # summaries and merged entry states against the oracle
+    q, k, v, g, beta = flat_inputs(d)
+    offs = gb.segment_offsets(2, 256, seg)
+    s = oracle.summary(k, v, g, beta, offs, gate_per_key=True, use_exp2=True)
+    meta = gb.make_meta(offs, 512, DEV)
+    S_ext, M, _ = gb.gdn_state_summary(d["k"], d["v"], d["g"], d["beta"], meta=meta, use_exp2=True)
+    torch.cuda.synchronize()
+    assert_close(np32(S_ext), s["S_ext"], TOL["bf16"], "S_ext")
+    assert_close(np32(M), s["M"], TOL["bf16"], "M")
+    n_seg = len(seg) - 1
+    ext = s["S_ext"].reshape(2, n_seg, 2, 128, 128).transpose(1, 0, 2, 3, 4).reshape(n_seg, 4, 128, 128)
+    MM = s["M"].reshape(2, n_seg, 2, 128, 128).transpose(1, 0, 2, 3, 4).reshape(n_seg, 4, 128, 128)
+    si = oracle.merge(ext, MM, np32(S0).reshape(4, 128, 128).astype(np.float64))
+    si_gpu = np32(S_init).reshape(2, n_seg, 2, 128, 128).transpose(1, 0, 2, 3, 4).reshape(n_seg, 4, 128, 128)
+    assert_close(si_gpu, si[:n_seg], TOL["bf16"], "S_init")
+    # the transposed transfer map would not reproduce the unsplit end state
+    wrong = oracle.merge(ext, np.swapaxes(MM, -1, -2), np32(S0).reshape(4, 128, 128).astype(np.float64))
+    assert rel_err(wrong[n_seg], r["final"].reshape(4, 128, 128)) > 0.05
+
+
+def test_merge_kernel_against_oracle():
+    B, H, n_seg = 2, 3, 4
+    g = torch.Generator().manual_seed(7)
+    S_ext = torch.randn(B * n_seg, H, 128, 128, generator=g).to(DEV)
+    M = (torch.randn(B * n_seg, H, 128, 128, generator=g) * 0.05).to(DEV)
+    S0 = torch.randn(B, H, 128, 128, generator=g).to(DEV)
+    S_init, S_final = gb.gdn_state_merge(S_ext, M, S0, B=B, n_seg=n_seg)
+    torch.cuda.synchronize()
+    ext = np32(S_ext).reshape(B, n_seg, H, 128, 128).transpose(1, 0, 2, 3, 4).reshape(n_seg, B * H, 128, 128)
+    MM = np32(M).reshape(B, n_seg, H, 128, 128).transpose(1, 0, 2, 3, 4).reshape(n_seg, B * H, 128, 128)
+    si = oracle.merge(ext, MM, np32(S0).reshape(B * H, 128, 128))
+    got = np32(S_init).reshape(B, n_seg, H, 128, 128).transpose(1, 0, 2, 3, 4).reshape(n_seg, B * H, 128, 128)
+    assert_close(got, si[:n_seg], 1e-5, "S_init")
+    assert_close(np32(S_final).reshape(B * H, 128, 128), si[n_seg], 1e-5, "S_final")
+
+
+def test_per_key_small_forward():
+    w = small(B=1, T=300, H=2, per_key=True, use_exp2=True, gate_coef=0.05)
+    d = to_dev(W.generate(w, 71))
+    o, fin, _ = run_gpu(d, output_final_state=True)
+    r = run_oracle(d)
+    assert_close(np32(o[0]), r["o"], TOL["bf16"], "per-key o")
+    assert_close(np32(fin), r["final"], TOL["bf16"], "per-key final")
+
+
+# ------------------------------------------------------------------ full-size workloads (sampled)
+def _sampled_check(d, o, heads, fin=None):
+    """Oracle on the selected heads only (heads are independent)."""
+    w = d["workload"]
+
+    def pick(x):
+        x = x.reshape(-1, *x.shape[2:]) if w.layout == "BSND" else x
+        return np32(x[:, heads].contiguous())
+
+    q, k, v, g, beta = (pick(d[n]) for n in ("q", "k", "v", "g", "beta"))
+    r = oracle.fwd(q, k, v, g, beta, unit_offsets(d), d["scale"], gate_per_key=w.gate_per_key,
+                   use_exp2=w.use_exp2, want_final=fin is not None)
+    e = assert_close(pick(o), r["o"], TOL[w.dtype], f"{w.name} o (heads {heads})")
+    if fin is not None:
+        assert_close(np32(fin[:, heads]), r["final"], TOL[w.dtype], f"{w.name} final")
+    return e
+
+
+def test_workload_dense_bf16_full():
+    w = W.WORKLOADS[1]
+    d = W.generate(w, 1001, device=DEV)
+    o, _, _ = run_gpu(d)
+    e = _sampled_check(d, o, heads=[0, 7, 15])
+    print(f"{w.name}: sampled o err/rms {e:.2e}")
+
+
+def test_workload_varlen_full():
+    w = W.WORKLOADS[2]
+    d = W.generate(w, 1002, device=DEV)
+    o, fin, _ = run_gpu(d, output_final_state=True)
+    e = _sampled_check(d, o, heads=[3, 30], fin=fin)
+    print(f"{w.name}: sampled o err/rms {e:.2e}")
+
+
+def test_workload_kda_split_full():
+    w = W.WORKLOADS[3]
+    d = W.generate(w, 1003, device=DEV)
+    o_s, f_s, _ = gb.split_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"],
+                                   seg=d["seg_offsets"], use_exp2=True)
+    o_u, f_u, _ = run_gpu(d, output_final_state=True)
+    torch.cuda.synchronize()
+    # split == unsplit on the GPU, and both against the oracle on sampled heads
+    assert_close(np32(o_s.reshape(-1, 8, 128)), np32(o_u.reshape(-1, 8, 128)), TOL["bf16"], "split vs unsplit")
+    d2 = dict(d)
+    d2["offsets"] = [0, w.T, 2 * w.T]
+    e = _sampled_check(d2, o_s, heads=[1, 6], fin=f_s)
+    print(f"{w.name}: sampled split o err/rms {e:.2e}")
+
+
+def test_workload_long_full():
+    w = W.WORKLOADS[4]
+    d = W.generate(w, 1004, device=DEV)
+    o, fin, _ = run_gpu(d, output_final_state=True)
+    e = _sampled_check(d, o, heads=[5], fin=fin)
+    print(f"{w.name}: sampled o err/rms {e:.2e}")
