@@ -1,0 +1,193 @@
+"""Benchmark of the chunked gated delta rule forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+A step is one full forward (chunk preparation + state pass with the fused
+output) over one batch of synthetic inputs already resident in HBM. W untimed
+steps, then K timed steps between device synchronisations; one JSON line on
+stdout. Per-kernel durations come from HIP events recorded on the launch
+stream between the two kernels of every timed step. The CPU baseline times
+the fp64 oracle on a bounded sample of the same workload (host threads).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "chunked GDN fwd tokens/s and TFLOP/s at H=16,K=V=128 (bf16); % MFMA roofline"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3
+FLOP_PER_TOKEN_HEAD = 139264   # 2 [3KV + (BT/2)(3K + 2V)], K = V = 128, BT = 64
+KERNEL_SRC = os.path.join(ROOT, "chunked_gated_delta_05_amd", "csrc", "gdn_kernels.hip")
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def byte_model(w, n_chunk_heads: int) -> dict:
+    """Algorithmic bytes per launch: what each kernel must read and write by
+    its contract (every byte once), summed over the chunk-heads it processes.
+    Scalar gate, per chunk-head of 64 tokens:
+      prep : k (64*128*es), g (64*4), beta (64*es)  ->  T (64*64*4), G (64*4)
+      state: q, k, v (3*64*128*es), T (64*64*4), G (64*4), beta (64*es) -> o (64*128*os)"""
+    es = 2 if w.dtype == "bf16" else 4
+    os_ = 4
+    prep = 64 * 128 * es + 64 * 4 + 64 * es + 64 * 64 * 4 + 64 * 4
+    state = 3 * 64 * 128 * es + 64 * 64 * 4 + 64 * 4 + 64 * es + 64 * 128 * os_
+    return {"prep": prep * n_chunk_heads, "state": state * n_chunk_heads,
+            "prep_per_chunk_head": prep, "state_per_chunk_head": state}
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when absent or taken on another version of the kernels."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except ValueError:
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(d, w, budget_s: float = 15.0) -> dict:
+    """The fp64 oracle on a bounded sample of (row, head) streams of the
+    workload, on this host's cores."""
+    import numpy as np
+
+    import oracle
+
+    threads = max(1, len(os.sched_getaffinity(0)))
+    pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+
+    def run(sel, nthr):
+        q, k, v, g, beta = (np.ascontiguousarray(
+            np.stack([d[n][b, :, h].float().cpu().numpy() for b, h in sel], axis=1))
+            for n in ("q", "k", "v", "g", "beta"))
+        t0 = time.perf_counter()
+        r = oracle.fwd(q, k, v, g, beta, [0, w.T], d["scale"], want_final=False, threads=nthr)
+        return time.perf_counter() - t0, r
+
+    t1, _ = run(pairs[:1], 1)                                  # one stream, one thread
+    n = int(min(len(pairs), max(1, budget_s * min(threads, len(pairs)) / max(t1, 1e-3))))
+    n = max(1, min(n, len(pairs)))
+    sel = pairs[:n]
+    used = min(threads, n)
+    t, r = run(sel, used)
+    token_heads = n * w.T
+    return {"value": token_heads / w.H / t, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"{n} of {len(pairs)} (row, head) streams of {w.name}, full length T={w.T}, "
+                      f"fp64 token recurrence, {t:.1f} s wall on {used} threads",
+            "seconds": t, "_result": r, "_sel": sel}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gdn_dense_bf16")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the forward shards by (unit, head) with no communication; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from chunked_gated_delta_05_amd import binding as gb
+    from chunked_gated_delta_05_amd import workloads as W
+
+    wl = {w.name: w for w in W.WORKLOADS}[args.workload]
+    if wl.gate_per_key or wl.n_seg or wl.layout != "BSND":
+        raise SystemExit("bench.py times the dense scalar-gate workloads (gdn_dense_bf16, gdn_long, gdn_tiny_fp32)")
+    dev = torch.device("cuda:0")
+    d = W.generate(wl, 1000 + [w.name for w in W.WORKLOADS].index(wl.name), device=dev)
+    q, k, v, g, beta = (d[n] for n in ("q", "k", "v", "g", "beta"))
+    o = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    fin = torch.empty((wl.B, wl.H, 128, 128), dtype=torch.float32, device=dev) if wl.final_state else None
+    nb = gb.workspace_bytes(gb._desc(k, wl.H, k.dtype, torch.float32, False, False, d["scale"], None))
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        gb.gdn_chunk_fwd(q, k, v, g, beta, d["scale"], flags=gb.FLAG_PREPARE_ONLY, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+        _, f, _ = gb.gdn_chunk_fwd(q, k, v, g, beta, d["scale"], flags=gb.FLAG_REUSE_PREPARED, workspace=ws,
+                                   out=o, output_final_state=wl.final_state, final_out=fin)
+        if ev is not None:
+            ev[2].record()
+        return f
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    state_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ms_step = wall * 1e3 / args.steps
+    tokens = wl.B * wl.T
+    n_chunk_heads = wl.B * ((wl.T + 63) // 64) * wl.H
+    bm = byte_model(wl, n_chunk_heads)
+    flops = FLOP_PER_TOKEN_HEAD * tokens * wl.H
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    dom = "state" if state_ms >= prep_ms else "prep"
+    dom_ms = state_ms if dom == "state" else prep_ms
+    achieved = bm[dom] / (dom_ms * 1e-3) / 1e9
+    kname = {"state": "state_kernel", "prep": "prep_kernel"}[dom]
+    traffic = load_traffic(kname, wl.name)
+    io_bytes = (3 * 128 * (2 if wl.dtype == "bf16" else 4) + 128 * 4 + 4 + (2 if wl.dtype == "bf16" else 4)) * tokens * wl.H
+    peak_mfma = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
+    out = {
+        "metric": METRIC, "value": tokens / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": wl.H, "K": 128, "V": 128, "chunk": 64,
+                   "layout": wl.layout, "gate": "scalar", "o_dtype": "fp32",
+                   "final_state": wl.final_state},
+        "tflops": tflops, "mfma_frac": tflops / peak_mfma,
+        "hbm_frac_io": io_bytes / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
+        "hbm_frac_design": (bm["prep"] + bm["state"]) / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
+        "kernel_ms": {"prep_kernel": prep_ms, "state_kernel": state_ms},
+        "roofline": {"kernel": kname, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": bm[dom]},
+    }
+    print(f"[bench] {wl.name}: {ms_step:.4f} ms/step, prep {prep_ms:.4f} ms, state {state_ms:.4f} ms, "
+          f"{tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    if not args.no_cpu:
+        import numpy as np
+
+        cb = cpu_baseline(d, wl)
+        r, sel = cb.pop("_result"), cb.pop("_sel")
+        got = np.stack([o[b, :, h].cpu().numpy() for b, h in sel], axis=1)
+        ref = r["o"]
+        out["parity_sample_err_over_rms"] = float(np.abs(got - ref).max() / np.sqrt((ref ** 2).mean()))
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

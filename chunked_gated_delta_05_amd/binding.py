@@ -201,7 +201,8 @@ def workspace_bytes(desc: GdnDesc, fn="fwd") -> int:
 # ------------------------------------------------------------------ entry points
 def gdn_chunk_fwd(q, k, v, g, beta, scale=None, *, meta: UnitMeta | None = None, initial_state=None,
                   output_final_state=False, use_exp2=False, o_dtype=torch.float32,
-                  want_g_cumsum=False, want_A=False, want_h=False, flags=0, workspace=None, out=None):
+                  want_g_cumsum=False, want_A=False, want_h=False, flags=0, workspace=None, out=None,
+                  final_out=None):
     """Chunked gated delta rule forward through libgdn.
 
     q, k [B,T,H,K] (BSND) or [T,H,K] (TND, needs meta); v like q; g fp32
@@ -223,8 +224,10 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale=None, *, meta: UnitMeta | None = None,
     if not prep_only:
         o = out if out is not None else torch.empty(v.shape, dtype=o_dtype, device=dev)
     units = n_units_of(k, meta)
-    fin = torch.empty((units, H, k.shape[-1], v.shape[-1]), dtype=torch.float32, device=dev) \
-        if output_final_state and not prep_only else None
+    fin = None
+    if output_final_state and not prep_only:
+        fin = final_out if final_out is not None else \
+            torch.empty((units, H, k.shape[-1], v.shape[-1]), dtype=torch.float32, device=dev)
     extras = {}
     tokens = k.shape[0] * k.shape[1] if k.dim() == 4 else k.shape[0]
     if want_g_cumsum:
