@@ -50,6 +50,10 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 __device__ __forceinline__ float bpow(float x, int use_exp2) { return use_exp2 ? exp2f(x) : expf(x); }
+// b^x with the hardware base-2 exponential (about 1 ulp; e^x = 2^(x log2 e))
+__device__ __forceinline__ float fpow(float x, int use_exp2) {
+    return __builtin_amdgcn_exp2f(use_exp2 ? x : x * 1.4426950408889634f);
+}
 
 // ------------------------------------------------------------------ policies
 // A fragment holds, for lane (G = lane / 16, n = lane % 16), the 8 elements
@@ -491,7 +495,8 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
     __shared__ float bet[2][BT];
     __shared__ float gl[2][PERKEY ? DK : 1];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, G = lane >> 4, n = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
     const int H = a.H;
     // blocks are dealt round-robin to the 8 XCDs: keep every column tile of a
     // (unit, head) pair on one XCD so that they share its L2
@@ -509,6 +514,7 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
     const In* vin = reinterpret_cast<const In*>(a.v);
     const In* bin = reinterpret_cast<const In*>(a.beta);
     const int nkw = w >= 2 ? 2 : 1;                  // 32-token steps that cover rows <= 16w+15
+    const int e2 = a.use_exp2;
 
     // ---- state tile: rows (keys) 32w + 16ks + 4G + r, columns vc0 + 16vs + n
     f32x4 h[2][2];
@@ -522,94 +528,99 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
                 h[ks][vs][r] = x;
             }
 
-    // ---- chunk loaders (rows past the chunk end load as zeros)
+    // ---- next-chunk prefetch. Loads stay raw in registers until the chunk is
+    // used one step later, so their latency overlaps a whole step; rows past
+    // the chunk end read a clamped (valid) row and are zeroed at use.
     constexpr int VPR = 16 / sizeof(In);
     constexpr int NKV = BT * DK / VPR / 256;          // 16-byte vectors per thread for a 64 x 128 tile
     auto chunk_len = [&](int c) { int l = ui.len - c * BT; return l < 0 ? 0 : (l > BT ? BT : l); };
-    auto load_k = [&](int c, f32x4* buf) {
+    struct Raw {
+        f32x4 k[NKV];    // k tile (per key: k*b^G), 16-byte vectors
+        float gb;        // thread < 64: G; 128..255: G_last per key
+        In bt;           // thread 64..127: beta
+        F q[4];          // scalar gate: q rows 16w+n
+        S qs[4];         // per-key gate: q*b^G rows 16w+n
+        f32x4 T[2][2];   // T rows 16w+n, columns 32kk + 8G .. +7
+        f32x4 Pw[2][2];  // per-key gate: P rows 16w+n
+        In v[2][4];      // v rows 16w+4G+r, columns vc0+16vs+n
+        f32x4 kg[PERKEY ? NP : 1][NKV];   // per-key gate: k*b^{G_last-G} tile planes
+        int len;
+    };
+    auto load_raw = [&](int c, Raw& x) {
         const int len = chunk_len(c);
-        const int64_t t0 = ui.start + (int64_t)c * BT;
-        const In* src = kin;
-        int64_t base = 0;
-        if (PERKEY) { src = reinterpret_cast<const In*>(a.ws.kd); base = ((int64_t)(ui.cbase + c) * H + head) * (BT * DK); }
-        for (int i = 0; i < NKV; ++i) {
-            const int idx = tid + 256 * i, r = idx / (DK / VPR), cv = (idx % (DK / VPR)) * VPR;
-            f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            if (PERKEY) buf[i] = *reinterpret_cast<const f32x4*>(src + base + r * DK + cv);
-            else buf[i] = r < len ? *reinterpret_cast<const f32x4*>(src + ((t0 + r) * H + head) * DK + cv) : z;
-        }
-    };
-    auto store_k = [&](const f32x4* buf, In* dst) {
-        for (int i = 0; i < NKV; ++i) {
-            const int idx = tid + 256 * i, r = idx / (DK / VPR), cv = (idx % (DK / VPR)) * VPR;
-            *reinterpret_cast<f32x4*>(dst + r * LDK + cv) = buf[i];
-        }
-    };
-    auto load_gb = [&](int c, float& x) {
-        const int len = chunk_len(c);
-        const int64_t t0 = ui.start + (int64_t)c * BT;
-        x = 0.0f;
-        if (tid < BT) { if (!PERKEY) x = a.ws.gam[((int64_t)(ui.cbase + c) * H + head) * BT + tid]; }
-        else if (tid < 2 * BT) { const int r = tid - BT; x = r < len ? P::f(bin[(t0 + r) * H + head]) : 0.0f; }
-        else if (PERKEY && tid < 2 * BT + DK) x = a.ws.gamL[((int64_t)(ui.cbase + c) * H + head) * DK + tid - 2 * BT];
-    };
-    auto store_gb = [&](float x, int b) {
-        if (tid < BT) gam[b][tid] = x;
-        else if (tid < 2 * BT) bet[b][tid - BT] = x;
-        else if (PERKEY && tid < 2 * BT + DK) gl[b][tid - 2 * BT] = x;
-    };
-    // per-wave register operands of a chunk
-    struct Ops {
-        F q[4];          // scalar gate: q rows 16w+n (exact)
-        S qs[4];         // per-key gate: q*b^G rows 16w+n (split)
-        F T[2];          // T rows 16w+n, columns 32kk + 8G..
-        S Pf[2];         // per-key gate: P rows 16w+n
-        float v[2][4];   // v rows 16w+4G+r, columns vc0+16vs+n
-    };
-    auto load_ops = [&](int c, Ops& op) {
-        const int len = chunk_len(c);
+        x.len = len;
+        const int last = len > 0 ? len - 1 : 0;
         const int64_t t0 = ui.start + (int64_t)c * BT;
         const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
+        for (int i = 0; i < NKV; ++i) {
+            const int idx = tid + 256 * i, r = idx / (DK / VPR), cv = (idx % (DK / VPR)) * VPR;
+            if (PERKEY) x.k[i] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const In*>(a.ws.kd) + ch * (BT * DK) + r * DK + cv);
+            else x.k[i] = *reinterpret_cast<const f32x4*>(kin + ((t0 + min(r, last)) * H + head) * DK + cv);
+        }
+        // every thread loads (no divergent branches around loads); publish keeps
+        // what its wave owns: wave 0 G, wave 1 beta, waves 2-3 G_last per key
+        x.gb = PERKEY ? a.ws.gamL[ch * DK + (tid & (DK - 1))] : a.ws.gam[ch * BT + lane];
+        x.bt = bin[(t0 + min(lane, last)) * H + head];
+        if (PERKEY) {
+            const In* src = reinterpret_cast<const In*>(a.ws.kg) + ch * (BT * DK);
+            for (int p = 0; p < NP; ++p)
+                for (int i = 0; i < NKV; ++i) {
+                    const int idx = tid + 256 * i, r = idx / (DK / VPR), cv = (idx % (DK / VPR)) * VPR;
+                    x.kg[p][i] = *reinterpret_cast<const f32x4*>(src + p * a.ws.plane + r * DK + cv);
+                }
+        }
         const int row = 16 * w + n;
         if (!SUMMARY) {
             if (!PERKEY) {
-                for (int kk = 0; kk < 4; ++kk)
-                    op.q[kk] = row < len ? P::ldF(qin + ((t0 + row) * H + head) * DK + 32 * kk + 8 * G) : P::zeroF();
+                const In* qr = qin + ((t0 + min(row, last)) * H + head) * DK + 8 * G;
+                for (int kk = 0; kk < 4; ++kk) x.q[kk] = P::ldF(qr + 32 * kk);
             } else {
-                const In* qg = reinterpret_cast<const In*>(a.ws.qg) + ch * (BT * DK);
-                for (int kk = 0; kk < 4; ++kk) op.qs[kk] = P::ldS(qg + row * DK + 32 * kk + 8 * G, a.ws.plane);
-                const float* Pw = a.ws.P + ch * (BT * BT);
-                for (int kk = 0; kk < 2; ++kk) {
-                    float x[8];
-                    for (int e = 0; e < 8; ++e) x[e] = Pw[row * BT + 32 * kk + 8 * G + e];
-                    op.Pf[kk] = P::splitS(x);
-                }
+                const In* qg = reinterpret_cast<const In*>(a.ws.qg) + ch * (BT * DK) + row * DK + 8 * G;
+                for (int kk = 0; kk < 4; ++kk) x.qs[kk] = P::ldS(qg + 32 * kk, a.ws.plane);
+                const float* Pr = a.ws.P + ch * (BT * BT) + row * BT + 8 * G;
+                for (int kk = 0; kk < 2; ++kk)
+                    if (kk < nkw) {
+                        x.Pw[kk][0] = *reinterpret_cast<const f32x4*>(Pr + 32 * kk);
+                        x.Pw[kk][1] = *reinterpret_cast<const f32x4*>(Pr + 32 * kk + 4);
+                    }
             }
         }
-        const float* Tw = a.ws.Tm + ch * (BT * BT);
-        for (int kk = 0; kk < 2; ++kk) {
-            float x[8];
-            for (int e = 0; e < 8; ++e) x[e] = kk < nkw ? Tw[row * BT + 32 * kk + 8 * G + e] : 0.0f;
-            op.T[kk] = P::roundF(x);
-        }
-        for (int vs = 0; vs < 2; ++vs)
+        const float* Tr = a.ws.Tm + ch * (BT * BT) + row * BT + 8 * G;
+        for (int kk = 0; kk < 2; ++kk)
+            if (kk < nkw) {
+                x.T[kk][0] = *reinterpret_cast<const f32x4*>(Tr + 32 * kk);
+                x.T[kk][1] = *reinterpret_cast<const f32x4*>(Tr + 32 * kk + 4);
+            }
+        if (!mcols)
             for (int r = 0; r < 4; ++r) {
-                const int i = 16 * w + 4 * G + r;
-                op.v[vs][r] = (!mcols && i < len) ? P::f(vin[((t0 + i) * H + head) * DV + vc0 + 16 * vs + n]) : 0.0f;
+                const In* vr = vin + ((t0 + min(16 * w + 4 * G + r, last)) * H + head) * DV + vc0 + n;
+                x.v[0][r] = vr[0];
+                x.v[1][r] = vr[16];
             }
+    };
+    // chunk data that the whole workgroup reads through LDS
+    auto publish = [&](const Raw& x, int b) {
+        for (int i = 0; i < NKV; ++i) {
+            const int idx = tid + 256 * i, r = idx / (DK / VPR), cv = (idx % (DK / VPR)) * VPR;
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            *reinterpret_cast<f32x4*>(&kt[b][r * LDK + cv]) = r < x.len ? x.k[i] : z;
+        }
+        if (w == 0) { if (!PERKEY) gam[b][lane] = x.gb; }
+        else if (w == 1) bet[b][lane] = lane < x.len ? P::f(x.bt) : 0.0f;
+        else if (PERKEY) gl[b][tid - 2 * BT] = x.gb;
+    };
+    auto t_frag = [&](const Raw& x, int kk) {
+        float f[8];
+        for (int e = 0; e < 4; ++e) { f[e] = x.T[kk][0][e]; f[e + 4] = x.T[kk][1][e]; }
+        return P::roundF(f);
     };
 
     // ---- prologue
     const int nch = ui.nch;
-    Ops cur, nxt;
-    f32x4 kbuf[NKV];
-    float gbv;
+    Raw cur, nxt;
     if (nch > 0) {
-        load_k(0, kbuf);
-        store_k(kbuf, kt[0]);
-        load_gb(0, gbv);
-        store_gb(gbv, 0);
-        load_ops(0, cur);
+        load_raw(0, cur);
+        publish(cur, 0);
     }
     if (!PERKEY && !SUMMARY) {
         // columns of the wave's P rows that are never computed stay zero
@@ -624,22 +635,18 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
 
     for (int c = 0; c < nch; ++c) {
         const int b = c & 1;
-        const int len = chunk_len(c);
+        const int len = cur.len;
         const int64_t t0 = ui.start + (int64_t)c * BT;
         const bool more = c + 1 < nch;
-        if (more) {
-            load_k(c + 1, kbuf);
-            load_gb(c + 1, gbv);
-            load_ops(c + 1, nxt);
-        }
+        if (more) load_raw(c + 1, nxt);
         if (PERKEY) {
-            // k*b^{G_last-G} for this chunk; read only after the next two barriers
-            const In* src = reinterpret_cast<const In*>(a.ws.kg) + ((int64_t)(ui.cbase + c) * H + head) * (BT * DK);
+            // k*b^{G_last-G} of this chunk (prefetched a step ago); the previous
+            // chunk's reads of kgt ended before the last barrier, and the reads of
+            // this one follow the next two
             for (int p = 0; p < NP; ++p)
                 for (int i = 0; i < NKV; ++i) {
                     const int idx = tid + 256 * i, r = idx / (DK / VPR), cv = (idx % (DK / VPR)) * VPR;
-                    *reinterpret_cast<f32x4*>(&kgt[p * BT * LDK + r * LDK + cv]) =
-                        *reinterpret_cast<const f32x4*>(src + p * a.ws.plane + r * DK + cv);
+                    *reinterpret_cast<f32x4*>(&kgt[p * BT * LDK + r * LDK + cv]) = cur.kg[p][i];
                 }
         }
         if (!SUMMARY && a.hslot) {
@@ -650,6 +657,18 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
                         a.hslot[(((int64_t)(ui.cbase + c) * H + head) * DK + key) * DV + col] = h[ks][vs][r];
                     }
         }
+        // per-row decay factors of this lane's accumulator rows i = 16w + 4G + r
+        float eG[4], eLG[4];
+        const float gL = PERKEY ? 0.0f : gam[b][len > 0 ? len - 1 : 0];
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * w + 4 * G + r;
+            eG[r] = PERKEY ? 1.0f : fpow(gam[b][i], e2);
+            eLG[r] = PERKEY ? 1.0f : fpow(gL - gam[b][i], e2);
+        }
+        const bool qrow = 16 * w + n < len;
+        F qa[4];
+        if (!SUMMARY && !PERKEY)
+            for (int kk = 0; kk < 4; ++kk) qa[kk] = qrow ? cur.q[kk] : P::zeroF();
 
         // ---- token side: K h and q h for rows 16w .. 16w+15
         const In* K = kt[b];
@@ -666,7 +685,7 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
                 if constexpr (NP == 2) hhi.v = hb.hi; else hhi = hb;
                 P::mFF(kh[vs], ka, hhi);
                 if (!SUMMARY) {
-                    if (!PERKEY) P::mFS(qh[vs], cur.q[kk], hb);
+                    if (!PERKEY) P::mFS(qh[vs], qa[kk], hb);
                     else P::mSS(qh[vs], cur.qs[kk], hb);
                 }
             }
@@ -676,29 +695,28 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
             float y[4];
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * w + 4 * G + r;
-                const float d = PERKEY ? 1.0f : bpow(gam[b][i], a.use_exp2);
-                y[r] = bet[b][i] * (cur.v[vs][r] - d * kh[vs][r]);
+                const float vv = (!mcols && i < len) ? P::f(cur.v[vs][r]) : 0.0f;
+                y[r] = bet[b][i] * (vv - eG[r] * kh[vs][r]);
             }
             P::st4(&YT[(16 * vs + n) * LDY + 16 * w + 4 * G], BV * LDY, y);
         }
         f32x4 oacc[2];
         if (!SUMMARY) {
             for (int vs = 0; vs < 2; ++vs)
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * w + 4 * G + r;
-                    oacc[vs][r] = PERKEY ? qh[vs][r] : bpow(gam[b][i], a.use_exp2) * qh[vs][r];
-                }
+                for (int r = 0; r < 4; ++r) oacc[vs][r] = eG[r] * qh[vs][r];
             if (!PERKEY) {
                 // P^T tiles (j block jt, i block w): rows j, columns i = 16w + n
-                for (int jt = 0; jt <= w; ++jt) {
+                const float gi = gam[b][16 * w + n];
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt) {
+                    if (jt > w) continue;
                     f32x4 pt = {0.f, 0.f, 0.f, 0.f};
                     for (int kk = 0; kk < 4; ++kk)
-                        P::mFF(pt, P::ldF(&K[(16 * jt + n) * LDK + 32 * kk + 8 * G]), cur.q[kk]);
+                        P::mFF(pt, P::ldF(&K[(16 * jt + n) * LDK + 32 * kk + 8 * G]), qa[kk]);
                     float x[4];
-                    const int i = 16 * w + n;
                     for (int r = 0; r < 4; ++r) {
                         const int j = 16 * jt + 4 * G + r;
-                        x[r] = j <= i ? pt[r] * bpow(gam[b][i] - gam[b][j], a.use_exp2) : 0.0f;
+                        x[r] = j <= 16 * w + n ? pt[r] * fpow(gi - gam[b][j], e2) : 0.0f;
                     }
                     P::st4(&PS[w * NP * 16 * LDY + n * LDY + 16 * jt + 4 * G], 16 * LDY, x);
                 }
@@ -708,18 +726,18 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
 
         // ---- v_new = T Y for rows 16w .. 16w+15
         f32x4 vn[2];
-        for (int vs = 0; vs < 2; ++vs) {
-            vn[vs] = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int kk = 0; kk < nkw; ++kk)
-                P::mFS(vn[vs], cur.T[kk], P::ldS(&YT[(16 * vs + n) * LDY + 32 * kk + 8 * G], BV * LDY));
+        for (int vs = 0; vs < 2; ++vs) vn[vs] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kk = 0; kk < 2; ++kk) {
+            if (kk >= nkw) continue;
+            const F ta = t_frag(cur, kk);
+            for (int vs = 0; vs < 2; ++vs)
+                P::mFS(vn[vs], ta, P::ldS(&YT[(16 * vs + n) * LDY + 32 * kk + 8 * G], BV * LDY));
         }
-        const float gL = PERKEY ? 0.0f : gam[b][len > 0 ? len - 1 : 0];
         for (int vs = 0; vs < 2; ++vs) {
             float x[4], xp[4];
             for (int r = 0; r < 4; ++r) {
-                const int i = 16 * w + 4 * G + r;
                 x[r] = vn[vs][r];
-                xp[r] = PERKEY ? x[r] : x[r] * bpow(gL - gam[b][i], a.use_exp2);
+                xp[r] = x[r] * eLG[r];
             }
             if (!SUMMARY) P::st4(&vnT[(16 * vs + n) * LDY + 16 * w + 4 * G], BV * LDY, x);
             P::st4(&vpT[(16 * vs + n) * LDY + 16 * w + 4 * G], BV * LDY, xp);
@@ -728,10 +746,16 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
 
         // ---- output rows 16w .. 16w+15
         if (!SUMMARY) {
-            for (int kk = 0; kk < nkw; ++kk) {
+            for (int kk = 0; kk < 2; ++kk) {
+                if (kk >= nkw) continue;
                 S pa;
-                if (!PERKEY) pa = P::ldS(&PS[w * NP * 16 * LDY + n * LDY + 32 * kk + 8 * G], 16 * LDY);
-                else pa = cur.Pf[kk];
+                if (!PERKEY) {
+                    pa = P::ldS(&PS[w * NP * 16 * LDY + n * LDY + 32 * kk + 8 * G], 16 * LDY);
+                } else {
+                    float f[8];
+                    for (int e = 0; e < 4; ++e) { f[e] = cur.Pw[kk][0][e]; f[e + 4] = cur.Pw[kk][1][e]; }
+                    pa = P::splitS(f);
+                }
                 for (int vs = 0; vs < 2; ++vs)
                     P::mSS(oacc[vs], pa, P::ldS(&vnT[(16 * vs + n) * LDY + 32 * kk + 8 * G], BV * LDY));
             }
@@ -752,10 +776,11 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
         for (int kk = 0; kk < 2; ++kk)
             for (int vs = 0; vs < 2; ++vs)
                 vb[kk][vs] = P::ldS(&vpT[(16 * vs + n) * LDY + 32 * kk + 8 * G], BV * LDY);
+        const float eL = PERKEY ? 1.0f : fpow(gL, e2);
         for (int ks = 0; ks < 2; ++ks) {
             float dec[4];
             for (int r = 0; r < 4; ++r)
-                dec[r] = PERKEY ? bpow(gl[b][32 * w + 16 * ks + 4 * G + r], a.use_exp2) : bpow(gL, a.use_exp2);
+                dec[r] = PERKEY ? fpow(gl[b][32 * w + 16 * ks + 4 * G + r], e2) : eL;
             for (int vs = 0; vs < 2; ++vs)
                 for (int r = 0; r < 4; ++r) h[ks][vs][r] *= dec[r];
             for (int kk = 0; kk < 2; ++kk) {
@@ -773,8 +798,7 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
             }
         }
         if (more) {
-            store_k(kbuf, kt[b ^ 1]);
-            store_gb(gbv, b ^ 1);
+            publish(nxt, b ^ 1);
             cur = nxt;
         }
         __syncthreads();
