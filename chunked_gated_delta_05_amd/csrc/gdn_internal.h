@@ -28,16 +28,17 @@ struct UnitMap {
 };
 
 // Workspace regions, all device pointers inside the caller's workspace.
+// Operand arrays hold fp16 for bf16 inputs and fp32 for fp32 inputs.
 struct Workspace {
-    float* Tm;       // [n_chunks][H][64][64]  (I + L)^{-1}
-    float* gam;      // [n_chunks][H][64]      chunk-local cumulative gate (scalar gate)
+    void* Tm;        // operands [n_chunks][H][64][64]  T = (I + L)^{-1}
+    void* P;         // operands [n_chunks][H][64][64]  decayed q.k, lower incl. diagonal
+    float* gam;      // [n_chunks][H][4][64]  scalar gate: G, b^G, b^{G_last-G}, b^{G_last}
     // per-key gate only
-    float* P;        // [n_chunks][H][64][64]  intra-chunk decayed q.k, lower incl. diagonal
-    void* qg;        // planes x [n_chunks][H][64][K]  q * b^G
-    void* kd;        // [n_chunks][H][64][K]            k * b^G (one plane)
-    void* kg;        // planes x [n_chunks][H][64][K]  k * b^{G_last - G}
-    float* gamL;     // [n_chunks][H][K]       G at the chunk's last valid token
-    int64_t plane;   // elements between the hi and lo planes of qg / kg
+    void* qg;        // operands [n_chunks][H][64][K]  q * b^G
+    void* kd;        // operands [n_chunks][H][64][K]  k * b^G
+    void* kg;        // operands [n_chunks][H][64][K]  k * b^{G_last - G}
+    float* gamL;     // [n_chunks][H][K]  G at the chunk's last valid token
+    int64_t plane;   // unused
 };
 
 struct Problem {

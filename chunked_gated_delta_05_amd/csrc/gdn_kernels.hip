@@ -22,17 +22,18 @@
 //   prep_kernel   one workgroup per (chunk, head): G, L on MFMA, the 64 x 64
 //                 triangular inverse in LDS, T to the workspace (per-key gate:
 //                 also P, q*b^G, k*b^G, k*b^{G_last-G}, G_last).
-//   state_kernel  one workgroup per (unit, head, 32-column value tile): walks
-//                 the unit's chunks with the 128 x 32 fp32 state tile in
-//                 registers, fused with the output; in summary mode it runs
-//                 the same recurrence on [S_ext | M] from [0 | I].
+//   state_kernel  one workgroup per (unit, head, column tile); every wave owns
+//                 all 128 state rows of 16 value columns, so the recurrence
+//                 needs no exchange between waves; the waves share the chunk
+//                 tiles (k, q, T, P) through LDS. In summary mode it runs the
+//                 same recurrence on [S_ext | M] from [0 | I].
 //   merge_kernel  S_init[s+1] = M_s S_init[s] + S_ext[s] in fp32.
 //
-// Precision: every MFMA takes bf16 operands with fp32 accumulation. Operands
-// that are not exact bf16 values (the state, the residual Y, v_new, P, and on
-// the per-key path the gated q and k) are split into hi + lo bf16 pairs and
-// multiplied as hi*hi + hi*lo + lo*hi, which keeps the o path at about 16
-// significant bits; the fp32 input path uses fp32 MFMA throughout.
+// Precision: bf16 inputs are converted to fp16 MFMA operands (exact for
+// normal-range values); products accumulate in fp32; the state, the cumulative
+// gates and the triangular solve stay fp32, and operands computed on the fly
+// (the state, the residual Y, v_new, P, T) are rounded to fp16 once. fp32
+// inputs use fp32 MFMA throughout.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -41,145 +42,124 @@
 namespace gdn {
 
 typedef __bf16 bf16;
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-__device__ __forceinline__ float bpow(float x, int use_exp2) { return use_exp2 ? exp2f(x) : expf(x); }
 // b^x with the hardware base-2 exponential (about 1 ulp; e^x = 2^(x log2 e))
 __device__ __forceinline__ float fpow(float x, int use_exp2) {
     return __builtin_amdgcn_exp2f(use_exp2 ? x : x * 1.4426950408889634f);
 }
 
+// orders this wave's LDS writes before its following LDS reads
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // ------------------------------------------------------------------ policies
 // A fragment holds, for lane (G = lane / 16, n = lane % 16), the 8 elements
 // X[n][8G .. 8G+7] of a 16 x 32 A tile or X[8G .. 8G+7][n] of a 32 x 16 B
-// tile: the operand layout of v_mfma_f32_16x16x32_bf16. The accumulator holds
-// C[4G + r][n], r = 0..3.
+// tile: the operand layout of v_mfma_f32_16x16x32_{f16,bf16}. The
+// accumulator holds C[4G + r][n], r = 0..3.
 
-struct PolicyBF16 {
+struct PolicyH {          // bf16 inputs, fp16 operands
     using In = bf16;
-    static constexpr int PLANES = 2;
-    struct F { bf16x8 v; };
-    struct S { bf16x8 hi, lo; };
-
-    __device__ static F ldF(const In* p) { F f; f.v = *reinterpret_cast<const bf16x8*>(p); return f; }
-    __device__ static F zeroF() { F f; for (int e = 0; e < 8; ++e) f.v[e] = (bf16)0.0f; return f; }
-    __device__ static F roundF(const float* x) {
+    using Op = f16;
+    static constexpr int LDQ = 136;   // 64 x 128 LDS tile rows: 272 bytes
+    struct F { f16x8 v; };
+    __device__ static F ld(const Op* p) { F f; f.v = *reinterpret_cast<const f16x8*>(p); return f; }
+    __device__ static F from(const float* x) {
         F f;
-        for (int e = 0; e < 8; ++e) f.v[e] = (bf16)x[e];
+        for (int e = 0; e < 8; ++e) f.v[e] = (f16)x[e];
         return f;
     }
-    __device__ static S splitS(const float* x) {
-        S s;
-        for (int e = 0; e < 8; ++e) {
-            bf16 h = (bf16)x[e];
-            s.hi[e] = h;
-            s.lo[e] = (bf16)(x[e] - (float)h);
-        }
-        return s;
+    __device__ static void st4(Op* p, const float* x) {
+        f16x4 h;
+        for (int e = 0; e < 4; ++e) h[e] = (f16)x[e];
+        *reinterpret_cast<f16x4*>(p) = h;
     }
-    __device__ static S zeroS() { S s; F z = zeroF(); s.hi = z.v; s.lo = z.v; return s; }
-    // four consecutive values into a hi/lo plane pair (ps = plane stride in elements)
-    __device__ static void st4(In* p, int ps, const float* x) {
-        bf16x4 h, l;
-        for (int e = 0; e < 4; ++e) {
-            h[e] = (bf16)x[e];
-            l[e] = (bf16)(x[e] - (float)h[e]);
-        }
-        *reinterpret_cast<bf16x4*>(p) = h;
-        *reinterpret_cast<bf16x4*>(p + ps) = l;
-    }
-    __device__ static S ldS(const In* p, int64_t ps) {
-        S s;
-        s.hi = *reinterpret_cast<const bf16x8*>(p);
-        s.lo = *reinterpret_cast<const bf16x8*>(p + ps);
-        return s;
-    }
-    __device__ static void mma(f32x4& c, const bf16x8& a, const bf16x8& b) {
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-    }
-    __device__ static void mFF(f32x4& c, const F& a, const F& b) { mma(c, a.v, b.v); }
-    __device__ static void mFS(f32x4& c, const F& a, const S& b) { mma(c, a.v, b.hi); mma(c, a.v, b.lo); }
-    __device__ static void mSF(f32x4& c, const S& a, const F& b) { mma(c, a.hi, b.v); mma(c, a.lo, b.v); }
-    __device__ static void mSS(f32x4& c, const S& a, const S& b) {
-        mma(c, a.hi, b.hi);
-        mma(c, a.hi, b.lo);
-        mma(c, a.lo, b.hi);
+    __device__ static void mma(f32x4& c, const F& a, const F& b) {
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, c, 0, 0, 0);
     }
     // Column fragment of an LDS tile: lane (G, n) gets tile[r0 + 8G + e][c0 + n].
     // ds_read_b64_tr_b16 hands component c of lane j's 4-element row to lane
     // 4(j%4)+c as element j/4, so lane j points at row r0 + 8G + j/4 (+4),
     // columns c0 + 4(j%4) .. +3.
-    __device__ static bf16x8 ldcol_raw(const In* tile, int ld, int r0, int c0, int lane) {
+    __device__ static F ldcol(const Op* tile, int ld, int r0, int c0, int lane) {
         const int G = lane >> 4, j = lane & 15;
-        const In* p = tile + (r0 + 8 * G + (j >> 2)) * ld + c0 + 4 * (j & 3);
+        const Op* p = tile + (r0 + 8 * G + (j >> 2)) * ld + c0 + 4 * (j & 3);
         s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, p));
         s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, p + 4 * ld));
-        bf16x4 x = __builtin_bit_cast(bf16x4, a), y = __builtin_bit_cast(bf16x4, b);
-        bf16x8 r;
-        for (int e = 0; e < 4; ++e) { r[e] = x[e]; r[e + 4] = y[e]; }
-        return r;
-    }
-    __device__ static F ldcolF(const In* tile, int ld, int r0, int c0, int lane) {
-        F f; f.v = ldcol_raw(tile, ld, r0, c0, lane); return f;
-    }
-    __device__ static S ldcolS(const In* tile, int ps, int ld, int r0, int c0, int lane) {
-        S s;
-        s.hi = ldcol_raw(tile, ld, r0, c0, lane);
-        s.lo = ldcol_raw(tile + ps, ld, r0, c0, lane);
-        return s;
+        f16x4 x = __builtin_bit_cast(f16x4, a), y = __builtin_bit_cast(f16x4, b);
+        F f;
+        for (int e = 0; e < 4; ++e) { f.v[e] = x[e]; f.v[e + 4] = y[e]; }
+        return f;
     }
     __device__ static float f(In x) { return (float)x; }
-    __device__ static In cvt(float x) { return (bf16)x; }
+    __device__ static Op cvt(float x) { return (f16)x; }
+    static constexpr int FV = 1;   // 16-byte vectors per 8-operand fragment
+    __device__ static F frag(const f32x4* v) { F f; f.v = __builtin_bit_cast(f16x8, v[0]); return f; }
+    // 16 bytes of inputs (8 bf16) -> the same 8 values as operands (16 bytes of
+    // fp16). bf16 -> fp32 is a shift; fp32 -> fp16 of a bf16 value in the fp16
+    // normal range is exact, so the truncating pack is exact too.
+    __device__ static f32x4 in2op(f32x4 raw) {
+        const u32x4 w = __builtin_bit_cast(u32x4, raw);
+        u32x4 o;
+        for (int i = 0; i < 4; ++i) {
+            const float lo = __builtin_bit_cast(float, w[i] << 16), hi = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+            o[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+        }
+        return __builtin_bit_cast(f32x4, o);
+    }
+    // 4 fp32 values -> 4 operands (8 bytes)
+    __device__ static void f32_to_op4(Op* p, f32x4 x) {
+        f16x4 h;
+        for (int e = 0; e < 4; ++e) h[e] = (f16)x[e];
+        *reinterpret_cast<f16x4*>(p) = h;
+    }
 };
 
-struct PolicyF32 {
+struct PolicyF {          // fp32 inputs and operands
     using In = float;
-    static constexpr int PLANES = 1;
+    using Op = float;
+    static constexpr int LDQ = 132;   // 64 x 128 LDS tile rows: 528 bytes
     struct F { float v[8]; };
-    using S = F;
-
-    __device__ static F ldF(const In* p) {
+    __device__ static F ld(const Op* p) {
         F f;
         f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
         for (int e = 0; e < 4; ++e) { f.v[e] = a[e]; f.v[e + 4] = b[e]; }
         return f;
     }
-    __device__ static F zeroF() { F f; for (int e = 0; e < 8; ++e) f.v[e] = 0.0f; return f; }
-    __device__ static F roundF(const float* x) { F f; for (int e = 0; e < 8; ++e) f.v[e] = x[e]; return f; }
-    __device__ static S splitS(const float* x) { return roundF(x); }
-    __device__ static S zeroS() { return zeroF(); }
-    __device__ static void st4(In* p, int, const float* x) {
+    __device__ static F from(const float* x) { F f; for (int e = 0; e < 8; ++e) f.v[e] = x[e]; return f; }
+    __device__ static void st4(Op* p, const float* x) {
         f32x4 a;
         for (int e = 0; e < 4; ++e) a[e] = x[e];
         *reinterpret_cast<f32x4*>(p) = a;
     }
-    __device__ static S ldS(const In* p, int64_t) { return ldF(p); }
     // the 32-deep product as eight 16x16x4 fp32 MFMAs: instruction e takes
     // element e of every lane, so together they cover k = 8G + e for all G, e
-    __device__ static void m8(f32x4& c, const F& a, const F& b) {
+    __device__ static void mma(f32x4& c, const F& a, const F& b) {
         for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], c, 0, 0, 0);
     }
-    __device__ static void mFF(f32x4& c, const F& a, const F& b) { m8(c, a, b); }
-    __device__ static void mFS(f32x4& c, const F& a, const S& b) { m8(c, a, b); }
-    __device__ static void mSF(f32x4& c, const S& a, const F& b) { m8(c, a, b); }
-    __device__ static void mSS(f32x4& c, const S& a, const S& b) { m8(c, a, b); }
-    __device__ static F ldcolF(const In* tile, int ld, int r0, int c0, int lane) {
+    __device__ static F ldcol(const Op* tile, int ld, int r0, int c0, int lane) {
         const int G = lane >> 4, n = lane & 15;
         F f;
         for (int e = 0; e < 8; ++e) f.v[e] = tile[(r0 + 8 * G + e) * ld + c0 + n];
         return f;
     }
-    __device__ static S ldcolS(const In* tile, int, int ld, int r0, int c0, int lane) {
-        return ldcolF(tile, ld, r0, c0, lane);
-    }
     __device__ static float f(In x) { return x; }
-    __device__ static In cvt(float x) { return x; }
+    __device__ static Op cvt(float x) { return x; }
+    static constexpr int FV = 2;   // 16-byte vectors per 8-operand fragment
+    __device__ static F frag(const f32x4* v) {
+        F f;
+        for (int e = 0; e < 4; ++e) { f.v[e] = v[0][e]; f.v[e + 4] = v[1][e]; }
+        return f;
+    }
+    __device__ static f32x4 in2op(f32x4 raw) { return raw; }
+    __device__ static void f32_to_op4(Op* p, f32x4 x) { *reinterpret_cast<f32x4*>(p) = x; }
 };
 
 // ------------------------------------------------------------------ units
@@ -226,7 +206,7 @@ __device__ __forceinline__ void chunk_of(const UnitMap& um, int ci, int& u, int&
 }
 
 // ------------------------------------------------------------------ prep
-constexpr int LDK = DK + 8;   // row stride of 64 x 128 LDS tiles (elements)
+constexpr int LD6 = BT + 8;   // row stride of 64-wide LDS operand tiles (elements)
 constexpr int LDL = BT + 1;   // row stride of 64 x 64 fp32 LDS matrices
 
 struct PrepArgs {
@@ -245,8 +225,10 @@ struct PrepArgs {
 template <class P, bool PERKEY>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     using In = typename P::In;
-    __shared__ __attribute__((aligned(16))) In kt[BT * LDK];
-    __shared__ __attribute__((aligned(16))) In qt[PERKEY ? BT * LDK : 8];
+    using Op = typename P::Op;
+    constexpr int LDQ = P::LDQ;
+    __shared__ __attribute__((aligned(16))) Op kt[BT * LDQ];
+    __shared__ __attribute__((aligned(16))) Op qt[BT * LDQ];
     __shared__ float Gs[PERKEY ? BT * (DK + 4) : BT];
     __shared__ float bet[BT];
     __shared__ float Ls[BT * LDL];
@@ -266,9 +248,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     const In* kin = reinterpret_cast<const In*>(a.k);
     const In* qin = reinterpret_cast<const In*>(a.q);
     const In* bin = reinterpret_cast<const In*>(a.beta);
-    const bool has_q = PERKEY && qin != nullptr;   // per key: prepare q * b^G and P as well
+    const bool has_q = qin != nullptr;   // P (and per key q * b^G) are prepared when q is given
 
-    // ---- tiles into LDS (rows past the chunk end are zero)
+    // ---- tiles into LDS as operands (rows past the chunk end are zero)
     constexpr int VPR = 16 / sizeof(In);             // elements per 16-byte vector
     constexpr int NV = BT * DK / VPR;                // vectors per tile
     for (int idx = tid; idx < NV; idx += 256) {
@@ -276,23 +258,29 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
         f32x4 kv = z, qv = z;
         if (r < len) {
-            kv = *reinterpret_cast<const f32x4*>(kin + ((t0 + r) * H + head) * DK + cv);
-            if (has_q) qv = *reinterpret_cast<const f32x4*>(qin + ((t0 + r) * H + head) * DK + cv);
+            kv = P::in2op(*reinterpret_cast<const f32x4*>(kin + ((t0 + r) * H + head) * DK + cv));
+            if (has_q) qv = P::in2op(*reinterpret_cast<const f32x4*>(qin + ((t0 + r) * H + head) * DK + cv));
         }
-        *reinterpret_cast<f32x4*>(&kt[r * LDK + cv]) = kv;
-        if (PERKEY) *reinterpret_cast<f32x4*>(&qt[r * LDK + cv]) = qv;
+        *reinterpret_cast<f32x4*>(&kt[r * LDQ + cv]) = kv;
+        *reinterpret_cast<f32x4*>(&qt[r * LDQ + cv]) = qv;
     }
     if (tid < BT) bet[tid] = tid < len ? P::f(bin[(t0 + tid) * H + head]) : 0.0f;
     if (!PERKEY) {
-        // inclusive scan of the scalar gate over the chunk, one wave
+        // inclusive scan of the scalar gate over the chunk, one wave; stores
+        // G, b^G, b^{G_last - G} and b^{G_last} for the state pass
         if (w == 0) {
             float x = lane < len ? a.g[(t0 + lane) * H + head] : 0.0f;
             for (int off = 1; off < 64; off <<= 1) {
                 float y = __shfl_up(x, off, 64);
                 if (lane >= off) x += y;
             }
+            const float xl = __shfl(x, len > 0 ? len - 1 : 0, 64);
             Gs[lane] = x;
-            a.ws.gam[ch * BT + lane] = x;
+            float* gw = a.ws.gam + ch * (4 * BT);
+            gw[lane] = x;
+            gw[BT + lane] = fpow(x, a.use_exp2);
+            gw[2 * BT + lane] = fpow(xl - x, a.use_exp2);
+            gw[3 * BT + lane] = fpow(xl, a.use_exp2);
             if (a.g_cumsum && lane < len) a.g_cumsum[(t0 + lane) * H + head] = x;
         }
     } else {
@@ -310,39 +298,35 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     __syncthreads();
 
     // ---- L = strictly lower (beta_i k_i.k_j b^{G_i-G_j}) on MFMA, 10 tiles over 4 waves
-    {
-        const int mid = len > 0 ? (len - 1) / 2 : 0;   // reference row of the per-key factorisation
-        for (int t = w; t < 10; t += 4) {
-            const int it = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
-            const int jt = t - (it * (it + 1)) / 2;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int kk = 0; kk < DK / 32; ++kk) {
-                const int col = 32 * kk + 8 * G;
-                if (!PERKEY) {
-                    typename P::F A = P::ldF(&kt[(16 * it + n) * LDK + col]);
-                    typename P::F B = P::ldF(&kt[(16 * jt + n) * LDK + col]);
-                    P::mFF(acc, A, B);
-                } else {
-                    float xa[8], xb[8];
-                    for (int e = 0; e < 8; ++e) {
-                        const float gr = Gs[mid * (DK + 4) + col + e];
-                        xa[e] = P::f(kt[(16 * it + n) * LDK + col + e]) *
-                                bpow(Gs[(16 * it + n) * (DK + 4) + col + e] - gr, a.use_exp2);
-                        xb[e] = P::f(kt[(16 * jt + n) * LDK + col + e]) *
-                                bpow(gr - Gs[(16 * jt + n) * (DK + 4) + col + e], a.use_exp2);
-                    }
-                    P::mSS(acc, P::splitS(xa), P::splitS(xb));
+    const int mid = len > 0 ? (len - 1) / 2 : 0;   // reference row of the per-key factorisation
+    for (int t = w; t < 10; t += 4) {
+        const int it = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+        const int jt = t - (it * (it + 1)) / 2;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int kk = 0; kk < DK / 32; ++kk) {
+            const int col = 32 * kk + 8 * G;
+            if (!PERKEY) {
+                P::mma(acc, P::ld(&kt[(16 * it + n) * LDQ + col]), P::ld(&kt[(16 * jt + n) * LDQ + col]));
+            } else {
+                float xa[8], xb[8];
+                for (int e = 0; e < 8; ++e) {
+                    const float gr = Gs[mid * (DK + 4) + col + e];
+                    xa[e] = (float)kt[(16 * it + n) * LDQ + col + e] *
+                            fpow(Gs[(16 * it + n) * (DK + 4) + col + e] - gr, a.use_exp2);
+                    xb[e] = (float)kt[(16 * jt + n) * LDQ + col + e] *
+                            fpow(gr - Gs[(16 * jt + n) * (DK + 4) + col + e], a.use_exp2);
                 }
+                P::mma(acc, P::from(xa), P::from(xb));
             }
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * it + 4 * G + r, j = 16 * jt + n;
-                float l = 0.0f;
-                if (j < i) {
-                    l = bet[i] * acc[r];
-                    if (!PERKEY) l *= bpow(Gs[i] - Gs[j], a.use_exp2);
-                }
-                Ls[i * LDL + j] = l;
+        }
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * it + 4 * G + r, j = 16 * jt + n;
+            float l = 0.0f;
+            if (j < i) {
+                l = bet[i] * acc[r];
+                if (!PERKEY) l *= fpow(Gs[i] - Gs[j], a.use_exp2);
             }
+            Ls[i * LDL + j] = l;
         }
     }
     __syncthreads();
@@ -393,69 +377,78 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         __syncthreads();
     }
 
-    // ---- T out (row-major 64 x 64 fp32), optional token-major A slot
-    float* Tw = a.ws.Tm + ch * (BT * BT);
+    // ---- T out as operands (row-major 64 x 64), optional token-major fp32 A slot
+    Op* Tw = reinterpret_cast<Op*>(a.ws.Tm) + ch * (BT * BT);
     for (int e = tid; e < BT * BT / 4; e += 256) {
         const int r = e / (BT / 4), c4 = (e % (BT / 4)) * 4;
         f32x4 x;
         for (int q2 = 0; q2 < 4; ++q2) x[q2] = Ts[r * LDL + c4 + q2];
-        *reinterpret_cast<f32x4*>(Tw + r * BT + c4) = x;
+        P::f32_to_op4(Tw + r * BT + c4, x);
         if (a.A && r < len) *reinterpret_cast<f32x4*>(a.A + ((t0 + r) * H + head) * BT + c4) = x;
     }
 
-    if (PERKEY) {
-        // P = q.k decayed, lower triangle with the diagonal; stored fp32 row-major
-        const int mid = len > 0 ? (len - 1) / 2 : 0;
-        float* Pw = a.ws.P + ch * (BT * BT);
-        for (int t = w; has_q && t < 16; t += 4) {
-            const int it = t >> 2, jt = t & 3;
+    // ---- P = tril_incl(q k^T decayed) as operands, computed as P^T tiles
+    // (rows j of block jt, columns i of block it); blocks above the diagonal
+    // are written as zeros
+    if (has_q) {
+        Op* Pw = reinterpret_cast<Op*>(a.ws.P) + ch * (BT * BT);
+        for (int t = w; t < 16; t += 4) {
+            const int jt = t >> 2, it = t & 3;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             if (jt <= it) {
                 for (int kk = 0; kk < DK / 32; ++kk) {
                     const int col = 32 * kk + 8 * G;
-                    float xa[8], xb[8];
-                    for (int e = 0; e < 8; ++e) {
-                        const float gr = Gs[mid * (DK + 4) + col + e];
-                        xa[e] = P::f(qt[(16 * it + n) * LDK + col + e]) *
-                                bpow(Gs[(16 * it + n) * (DK + 4) + col + e] - gr, a.use_exp2);
-                        xb[e] = P::f(kt[(16 * jt + n) * LDK + col + e]) *
-                                bpow(gr - Gs[(16 * jt + n) * (DK + 4) + col + e], a.use_exp2);
+                    if (!PERKEY) {
+                        P::mma(acc, P::ld(&kt[(16 * jt + n) * LDQ + col]), P::ld(&qt[(16 * it + n) * LDQ + col]));
+                    } else {
+                        float xa[8], xb[8];
+                        for (int e = 0; e < 8; ++e) {
+                            const float gr = Gs[mid * (DK + 4) + col + e];
+                            xa[e] = (float)kt[(16 * jt + n) * LDQ + col + e] *
+                                    fpow(gr - Gs[(16 * jt + n) * (DK + 4) + col + e], a.use_exp2);
+                            xb[e] = (float)qt[(16 * it + n) * LDQ + col + e] *
+                                    fpow(Gs[(16 * it + n) * (DK + 4) + col + e] - gr, a.use_exp2);
+                        }
+                        P::mma(acc, P::from(xa), P::from(xb));
                     }
-                    P::mSS(acc, P::splitS(xa), P::splitS(xb));
                 }
             }
+            const int i = 16 * it + n;
+            float x[4];
             for (int r = 0; r < 4; ++r) {
-                const int i = 16 * it + 4 * G + r, j = 16 * jt + n;
-                Pw[i * BT + j] = j <= i ? acc[r] : 0.0f;
+                const int j = 16 * jt + 4 * G + r;
+                float pv = j <= i ? acc[r] : 0.0f;
+                if (!PERKEY && j <= i) pv *= fpow(Gs[i] - Gs[j], a.use_exp2);
+                x[r] = pv;
             }
+            P::st4(Pw + i * BT + 16 * jt + 4 * G, x);
         }
-        // gated q and k tiles: q*b^G (split), k*b^G (one plane), k*b^{G_last-G} (split)
-        const int64_t plane = a.ws.plane;
-        In* qg = reinterpret_cast<In*>(a.ws.qg) + ch * (BT * DK);
-        In* kd = reinterpret_cast<In*>(a.ws.kd) + ch * (BT * DK);
-        In* kg = reinterpret_cast<In*>(a.ws.kg) + ch * (BT * DK);
+    }
+
+    if (PERKEY) {
+        // gated q and k tiles as operands: q*b^G, k*b^G, k*b^{G_last-G}
+        Op* qg = reinterpret_cast<Op*>(a.ws.qg) + ch * (BT * DK);
+        Op* kd = reinterpret_cast<Op*>(a.ws.kd) + ch * (BT * DK);
+        Op* kg = reinterpret_cast<Op*>(a.ws.kg) + ch * (BT * DK);
         const int last = len > 0 ? len - 1 : 0;
         for (int e4 = tid; e4 < BT * DK / 4; e4 += 256) {
             const int r = e4 / (DK / 4), c4 = (e4 % (DK / 4)) * 4;
             float xq[4], xd[4], xg[4];
             for (int e = 0; e < 4; ++e) {
                 const float gg = Gs[r * (DK + 4) + c4 + e];
-                const float kv = P::f(kt[r * LDK + c4 + e]);
-                xq[e] = P::f(qt[r * LDK + c4 + e]) * bpow(gg, a.use_exp2);
-                xd[e] = kv * bpow(gg, a.use_exp2);
-                xg[e] = kv * bpow(Gs[last * (DK + 4) + c4 + e] - gg, a.use_exp2);
+                const float kv = (float)kt[r * LDQ + c4 + e];
+                xq[e] = (float)qt[r * LDQ + c4 + e] * fpow(gg, a.use_exp2);
+                xd[e] = kv * fpow(gg, a.use_exp2);
+                xg[e] = kv * fpow(Gs[last * (DK + 4) + c4 + e] - gg, a.use_exp2);
             }
-            if (has_q) P::st4(qg + r * DK + c4, (int)plane, xq);
-            P::st4(kg + r * DK + c4, (int)plane, xg);
-            for (int e = 0; e < 4; ++e) kd[r * DK + c4 + e] = P::cvt(xd[e]);
+            if (has_q) P::st4(qg + r * DK + c4, xq);
+            P::st4(kd + r * DK + c4, xd);
+            P::st4(kg + r * DK + c4, xg);
         }
     }
 }
 
 // ------------------------------------------------------------------ state pass
-constexpr int LDH = DK + 8;   // hT rows (value column) of 128 keys
-constexpr int LDY = BT + 8;   // YT / vnT rows (value column) of 64 tokens
-
 struct StateArgs {
     UnitMap um;
     int H;
@@ -473,30 +466,42 @@ struct StateArgs {
     int use_exp2;
     int n_pairs;     // units * H
     int ntiles;      // column tiles per pair
-    int tile0;       // first column tile (summary mode: 0, or V / 32 for M only)
+    int tile0;       // first column tile (summary mode: 0, or the first M tile)
     float* S_ext;
     float* M;
 };
 
+// Work split of the 8 waves of a state-pass workgroup (one 32-column value
+// tile): wave w owns token rows 16*rg .. 16*rg+15 and state rows (keys)
+// 32*rg .. 32*rg+31 of row group rg, and the 16 value columns of column group
+// cg. Waves w and w+4 share a SIMD; pairing row group s with 3-s there
+// balances the triangular work (later rows of a chunk see more of it).
+constexpr int SW = 8;              // waves per state-pass workgroup
+constexpr int ST = 64 * SW;        // threads
+constexpr int LDY = BT + 8;        // rows (value columns) of the transposed 64-token LDS tiles
+
 template <class P, bool PERKEY, bool SUMMARY>
-__global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
+__global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
     using In = typename P::In;
+    using Op = typename P::Op;
     using F = typename P::F;
-    using S = typename P::S;
-    constexpr int NP = P::PLANES;
-    __shared__ __attribute__((aligned(16))) In kt[2][BT * LDK];                   // k (per key: k*b^G)
-    __shared__ __attribute__((aligned(16))) In kgt[PERKEY ? NP * BT * LDK : 8];  // per key: k*b^{G_last-G}
-    __shared__ __attribute__((aligned(16))) In hT[NP * BV * LDH];                // state, transposed
-    __shared__ __attribute__((aligned(16))) In YT[NP * BV * LDY];
-    __shared__ __attribute__((aligned(16))) In vnT[NP * BV * LDY];
-    __shared__ __attribute__((aligned(16))) In vpT[NP * BV * LDY];
-    __shared__ __attribute__((aligned(16))) In PS[(!PERKEY && !SUMMARY) ? 4 * NP * 16 * LDY : 8];
-    __shared__ float gam[2][BT];
-    __shared__ float bet[2][BT];
-    __shared__ float gl[2][PERKEY ? DK : 1];
+    constexpr int LDQ = P::LDQ;
+    constexpr int FV = P::FV;
+    constexpr bool OUT = !SUMMARY;
+    __shared__ __attribute__((aligned(16))) Op kt[2][BT * LDQ];                  // k (per key: k*b^G)
+    __shared__ __attribute__((aligned(16))) Op kgt[PERKEY ? BT * LDQ : 8];      // per key: k*b^{G_last-G}
+    __shared__ __attribute__((aligned(16))) Op hT[BV * LDQ];                    // state, transposed
+    __shared__ __attribute__((aligned(16))) Op YT[BV * LDY];
+    __shared__ __attribute__((aligned(16))) Op vnT[OUT ? BV * LDY : 8];
+    __shared__ __attribute__((aligned(16))) Op vpT[BV * LDY];
+    __shared__ __attribute__((aligned(16))) float gam[2][4 * BT];               // G, b^G, b^{G_L-G}, b^{G_L}
+    __shared__ __attribute__((aligned(16))) float bet[2][BT];
+    __shared__ __attribute__((aligned(16))) float gl[2][PERKEY ? DK : 4];
 
     const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);          // wave index, kept scalar
+    const int cg = wv >> 2;                                           // column group
+    const int rg = cg == 0 ? (wv & 3) : 3 - (wv & 3);                 // row group
     const int H = a.H;
     // blocks are dealt round-robin to the 8 XCDs: keep every column tile of a
     // (unit, head) pair on one XCD so that they share its L2
@@ -508,43 +513,49 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
     const UnitInfo ui = unit_info(a.um, u);
     const int c0 = tile * BV;                       // column of [S_ext | M] or of V
     const bool mcols = SUMMARY && c0 >= DV;         // transfer-map columns: v = 0, start at I
-    const int vc0 = mcols ? c0 - DV : c0;
+    const int col = (mcols ? c0 - DV : c0) + 16 * cg + n;   // this lane's state / output column
     const In* qin = reinterpret_cast<const In*>(a.q);
     const In* kin = reinterpret_cast<const In*>(a.k);
     const In* vin = reinterpret_cast<const In*>(a.v);
     const In* bin = reinterpret_cast<const In*>(a.beta);
-    const int nkw = w >= 2 ? 2 : 1;                  // 32-token steps that cover rows <= 16w+15
+    const int nkw = rg >= 2 ? 2 : 1;                // 32-token steps that cover rows <= 16rg+15
     const int e2 = a.use_exp2;
+    const uint32_t tokstride = (uint32_t)H * DK;    // elements between consecutive tokens (K = V)
 
-    // ---- state tile: rows (keys) 32w + 16ks + 4G + r, columns vc0 + 16vs + n
-    f32x4 h[2][2];
+    // ---- state tile: rows (keys) 32rg + 16ks + 4G + r, column col
+    f32x4 h[2];
     for (int ks = 0; ks < 2; ++ks)
-        for (int vs = 0; vs < 2; ++vs)
-            for (int r = 0; r < 4; ++r) {
-                const int key = 32 * w + 16 * ks + 4 * G + r, col = vc0 + 16 * vs + n;
-                float x = 0.0f;
-                if (mcols) x = key == col ? 1.0f : 0.0f;
-                else if (!SUMMARY && a.h0) x = a.h0[(((int64_t)u * H + head) * DK + key) * DV + col];
-                h[ks][vs][r] = x;
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int key = 32 * rg + 16 * ks + 4 * G + r;
+            float x = 0.0f;
+            if (mcols) x = key == col ? 1.0f : 0.0f;
+            else if (OUT && a.h0) x = a.h0[(((int64_t)u * H + head) * DK + key) * DV + col];
+            h[ks][r] = x;
+        }
 
-    // ---- next-chunk prefetch. Loads stay raw in registers until the chunk is
-    // used one step later, so their latency overlaps a whole step; rows past
-    // the chunk end read a clamped (valid) row and are zeroed at use.
+    // ---- next-chunk prefetch. Loads for chunk c+1 are issued at the start of
+    // step c and stay raw in registers until used, so their latency overlaps a
+    // whole step. Rows past the chunk end read a clamped (valid) row: their
+    // contributions vanish because beta is zero there and T is the identity
+    // on padded rows, and padded output rows are never stored.
     constexpr int VPR = 16 / sizeof(In);
-    constexpr int NKV = BT * DK / VPR / 256;          // 16-byte vectors per thread for a 64 x 128 tile
+    constexpr int NKV = BT * DK / VPR / ST;           // 16-byte vectors per thread of a 64 x 128 tile
+    constexpr int NGW = PERKEY ? DK : 4 * BT;         // gate words per chunk
     auto chunk_len = [&](int c) { int l = ui.len - c * BT; return l < 0 ? 0 : (l > BT ? BT : l); };
     struct Raw {
-        f32x4 k[NKV];    // k tile (per key: k*b^G), 16-byte vectors
-        float gb;        // thread < 64: G; 128..255: G_last per key
-        In bt;           // thread 64..127: beta
-        F q[4];          // scalar gate: q rows 16w+n
-        S qs[4];         // per-key gate: q*b^G rows 16w+n
-        f32x4 T[2][2];   // T rows 16w+n, columns 32kk + 8G .. +7
-        f32x4 Pw[2][2];  // per-key gate: P rows 16w+n
-        In v[2][4];      // v rows 16w+4G+r, columns vc0+16vs+n
-        f32x4 kg[PERKEY ? NP : 1][NKV];   // per-key gate: k*b^{G_last-G} tile planes
+        f32x4 k[NKV];                    // k tile vectors (per key: k*b^G operands)
+        f32x4 q[OUT ? 4 * FV : 1];       // q rows 16rg+n (per key: q*b^G operands)
+        f32x4 T[2 * FV];                 // T rows 16rg+n, columns 32kk+8G.. (operands)
+        f32x4 Pr[OUT ? 2 * FV : 1];      // P rows 16rg+n (operands)
+        float gb;                        // gate word tid (threads < NGW)
+        In bt;                           // beta
+        In v[4];                         // v rows 16rg+4G+r, column col
         int len;
+    };
+    auto tile_rc = [&](int i, int& r, int& cv) {
+        const int idx = tid + ST * i;
+        r = idx / (DK / VPR);
+        cv = (idx % (DK / VPR)) * VPR;
     };
     auto load_raw = [&](int c, Raw& x) {
         const int len = chunk_len(c);
@@ -552,67 +563,60 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
         const int last = len > 0 ? len - 1 : 0;
         const int64_t t0 = ui.start + (int64_t)c * BT;
         const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
-        for (int i = 0; i < NKV; ++i) {
-            const int idx = tid + 256 * i, r = idx / (DK / VPR), cv = (idx % (DK / VPR)) * VPR;
-            if (PERKEY) x.k[i] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const In*>(a.ws.kd) + ch * (BT * DK) + r * DK + cv);
-            else x.k[i] = *reinterpret_cast<const f32x4*>(kin + ((t0 + min(r, last)) * H + head) * DK + cv);
-        }
-        // every thread loads (no divergent branches around loads); publish keeps
-        // what its wave owns: wave 0 G, wave 1 beta, waves 2-3 G_last per key
-        x.gb = PERKEY ? a.ws.gamL[ch * DK + (tid & (DK - 1))] : a.ws.gam[ch * BT + lane];
-        x.bt = bin[(t0 + min(lane, last)) * H + head];
+        const int row = 16 * rg + n;
         if (PERKEY) {
-            const In* src = reinterpret_cast<const In*>(a.ws.kg) + ch * (BT * DK);
-            for (int p = 0; p < NP; ++p)
-                for (int i = 0; i < NKV; ++i) {
-                    const int idx = tid + 256 * i, r = idx / (DK / VPR), cv = (idx % (DK / VPR)) * VPR;
-                    x.kg[p][i] = *reinterpret_cast<const f32x4*>(src + p * a.ws.plane + r * DK + cv);
-                }
-        }
-        const int row = 16 * w + n;
-        if (!SUMMARY) {
-            if (!PERKEY) {
-                const In* qr = qin + ((t0 + min(row, last)) * H + head) * DK + 8 * G;
-                for (int kk = 0; kk < 4; ++kk) x.q[kk] = P::ldF(qr + 32 * kk);
-            } else {
-                const In* qg = reinterpret_cast<const In*>(a.ws.qg) + ch * (BT * DK) + row * DK + 8 * G;
-                for (int kk = 0; kk < 4; ++kk) x.qs[kk] = P::ldS(qg + 32 * kk, a.ws.plane);
-                const float* Pr = a.ws.P + ch * (BT * BT) + row * BT + 8 * G;
-                for (int kk = 0; kk < 2; ++kk)
-                    if (kk < nkw) {
-                        x.Pw[kk][0] = *reinterpret_cast<const f32x4*>(Pr + 32 * kk);
-                        x.Pw[kk][1] = *reinterpret_cast<const f32x4*>(Pr + 32 * kk + 4);
-                    }
+            const Op* kd = reinterpret_cast<const Op*>(a.ws.kd) + ch * (BT * DK);
+            for (int i = 0; i < NKV; ++i) {
+                int r, cv;
+                tile_rc(i, r, cv);
+                x.k[i] = *reinterpret_cast<const f32x4*>(kd + r * DK + cv);
             }
+            if (OUT) {
+                const Op* qg = reinterpret_cast<const Op*>(a.ws.qg) + ch * (BT * DK) + row * DK + 8 * G;
+                for (int kk = 0; kk < 4; ++kk)
+                    for (int f = 0; f < FV; ++f) x.q[FV * kk + f] = *reinterpret_cast<const f32x4*>(qg + 32 * kk + 4 * f);
+            }
+            x.gb = tid < NGW ? a.ws.gamL[ch * DK + tid] : 0.0f;
+        } else {
+            const In* kb = kin + (t0 * H + head) * DK;
+            for (int i = 0; i < NKV; ++i) {
+                int r, cv;
+                tile_rc(i, r, cv);
+                x.k[i] = *reinterpret_cast<const f32x4*>(kb + (uint32_t)min(r, last) * tokstride + cv);
+            }
+            if (OUT) {
+                const In* qb = qin + (t0 * H + head) * DK + (uint32_t)min(row, last) * tokstride + 8 * G;
+                for (int kk = 0; kk < 4; ++kk)
+                    for (int f = 0; f < FV; ++f) x.q[FV * kk + f] = *reinterpret_cast<const f32x4*>(qb + 32 * kk + 4 * f);
+            }
+            x.gb = tid < NGW ? a.ws.gam[ch * (4 * BT) + tid] : 0.0f;
         }
-        const float* Tr = a.ws.Tm + ch * (BT * BT) + row * BT + 8 * G;
+        const Op* Tr = reinterpret_cast<const Op*>(a.ws.Tm) + ch * (BT * BT) + row * BT + 8 * G;
+        const Op* Pw = reinterpret_cast<const Op*>(a.ws.P) + ch * (BT * BT) + row * BT + 8 * G;
         for (int kk = 0; kk < 2; ++kk)
-            if (kk < nkw) {
-                x.T[kk][0] = *reinterpret_cast<const f32x4*>(Tr + 32 * kk);
-                x.T[kk][1] = *reinterpret_cast<const f32x4*>(Tr + 32 * kk + 4);
-            }
-        if (!mcols)
-            for (int r = 0; r < 4; ++r) {
-                const In* vr = vin + ((t0 + min(16 * w + 4 * G + r, last)) * H + head) * DV + vc0 + n;
-                x.v[0][r] = vr[0];
-                x.v[1][r] = vr[16];
-            }
+            if (kk < nkw)
+                for (int f = 0; f < FV; ++f) {
+                    x.T[FV * kk + f] = *reinterpret_cast<const f32x4*>(Tr + 32 * kk + 4 * f);
+                    if (OUT) x.Pr[FV * kk + f] = *reinterpret_cast<const f32x4*>(Pw + 32 * kk + 4 * f);
+                }
+        x.bt = (bin + t0 * H + head)[(uint32_t)min(lane, last) * H];
+        if (!mcols) {
+            const In* vb = vin + (t0 * H + head) * DV;
+            for (int r = 0; r < 4; ++r) x.v[r] = vb[(uint32_t)min(16 * rg + 4 * G + r, last) * tokstride + col];
+        }
     };
-    // chunk data that the whole workgroup reads through LDS
+    // chunk data the whole workgroup reads through LDS
     auto publish = [&](const Raw& x, int b) {
         for (int i = 0; i < NKV; ++i) {
-            const int idx = tid + 256 * i, r = idx / (DK / VPR), cv = (idx % (DK / VPR)) * VPR;
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            *reinterpret_cast<f32x4*>(&kt[b][r * LDK + cv]) = r < x.len ? x.k[i] : z;
+            int r, cv;
+            tile_rc(i, r, cv);
+            *reinterpret_cast<f32x4*>(&kt[b][r * LDQ + cv]) = PERKEY ? x.k[i] : P::in2op(x.k[i]);
         }
-        if (w == 0) { if (!PERKEY) gam[b][lane] = x.gb; }
-        else if (w == 1) bet[b][lane] = lane < x.len ? P::f(x.bt) : 0.0f;
-        else if (PERKEY) gl[b][tid - 2 * BT] = x.gb;
-    };
-    auto t_frag = [&](const Raw& x, int kk) {
-        float f[8];
-        for (int e = 0; e < 4; ++e) { f[e] = x.T[kk][0][e]; f[e + 4] = x.T[kk][1][e]; }
-        return P::roundF(f);
+        if (tid < NGW) {
+            if (PERKEY) gl[b][tid] = x.gb;
+            else gam[b][tid] = x.gb;
+        }
+        if (tid < BT) bet[b][tid] = tid < x.len ? P::f(x.bt) : 0.0f;
     };
 
     // ---- prologue
@@ -622,179 +626,121 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
         load_raw(0, cur);
         publish(cur, 0);
     }
-    if (!PERKEY && !SUMMARY) {
-        // columns of the wave's P rows that are never computed stay zero
-        for (int e = lane; e < NP * 16 * LDY; e += 64) PS[w * NP * 16 * LDY + e] = P::cvt(0.0f);
+    for (int ks = 0; ks < 2; ++ks) {
+        float x[4] = {h[ks][0], h[ks][1], h[ks][2], h[ks][3]};
+        P::st4(&hT[(16 * cg + n) * LDQ + 32 * rg + 16 * ks + 4 * G], x);
     }
-    for (int ks = 0; ks < 2; ++ks)
-        for (int vs = 0; vs < 2; ++vs) {
-            float x[4] = {h[ks][vs][0], h[ks][vs][1], h[ks][vs][2], h[ks][vs][3]};
-            P::st4(&hT[(16 * vs + n) * LDH + 32 * w + 16 * ks + 4 * G], BV * LDH, x);
-        }
     __syncthreads();
 
     for (int c = 0; c < nch; ++c) {
         const int b = c & 1;
         const int len = cur.len;
         const int64_t t0 = ui.start + (int64_t)c * BT;
+        const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
         const bool more = c + 1 < nch;
         if (more) load_raw(c + 1, nxt);
+        f32x4 kgr[PERKEY ? NKV : 1];
         if (PERKEY) {
-            // k*b^{G_last-G} of this chunk (prefetched a step ago); the previous
-            // chunk's reads of kgt ended before the last barrier, and the reads of
-            // this one follow the next two
-            for (int p = 0; p < NP; ++p)
-                for (int i = 0; i < NKV; ++i) {
-                    const int idx = tid + 256 * i, r = idx / (DK / VPR), cv = (idx % (DK / VPR)) * VPR;
-                    *reinterpret_cast<f32x4*>(&kgt[p * BT * LDK + r * LDK + cv]) = cur.kg[p][i];
-                }
+            // k*b^{G_last-G} of this chunk, stored to LDS after the next barrier
+            const Op* kg = reinterpret_cast<const Op*>(a.ws.kg) + ch * (BT * DK);
+            for (int i = 0; i < NKV; ++i) {
+                int r, cv;
+                tile_rc(i, r, cv);
+                kgr[i] = *reinterpret_cast<const f32x4*>(kg + r * DK + cv);
+            }
         }
-        if (!SUMMARY && a.hslot) {
+        if (OUT && a.hslot) {
             for (int ks = 0; ks < 2; ++ks)
-                for (int vs = 0; vs < 2; ++vs)
-                    for (int r = 0; r < 4; ++r) {
-                        const int key = 32 * w + 16 * ks + 4 * G + r, col = vc0 + 16 * vs + n;
-                        a.hslot[(((int64_t)(ui.cbase + c) * H + head) * DK + key) * DV + col] = h[ks][vs][r];
-                    }
-        }
-        // per-row decay factors of this lane's accumulator rows i = 16w + 4G + r
-        float eG[4], eLG[4];
-        const float gL = PERKEY ? 0.0f : gam[b][len > 0 ? len - 1 : 0];
-        for (int r = 0; r < 4; ++r) {
-            const int i = 16 * w + 4 * G + r;
-            eG[r] = PERKEY ? 1.0f : fpow(gam[b][i], e2);
-            eLG[r] = PERKEY ? 1.0f : fpow(gL - gam[b][i], e2);
-        }
-        const bool qrow = 16 * w + n < len;
-        F qa[4];
-        if (!SUMMARY && !PERKEY)
-            for (int kk = 0; kk < 4; ++kk) qa[kk] = qrow ? cur.q[kk] : P::zeroF();
-
-        // ---- token side: K h and q h for rows 16w .. 16w+15
-        const In* K = kt[b];
-        f32x4 kh[2], qh[2];
-        for (int vs = 0; vs < 2; ++vs) {
-            kh[vs] = f32x4{0.f, 0.f, 0.f, 0.f};
-            qh[vs] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        for (int kk = 0; kk < 4; ++kk) {
-            const F ka = P::ldF(&K[(16 * w + n) * LDK + 32 * kk + 8 * G]);
-            for (int vs = 0; vs < 2; ++vs) {
-                const S hb = P::ldS(&hT[(16 * vs + n) * LDH + 32 * kk + 8 * G], BV * LDH);
-                F hhi;
-                if constexpr (NP == 2) hhi.v = hb.hi; else hhi = hb;
-                P::mFF(kh[vs], ka, hhi);
-                if (!SUMMARY) {
-                    if (!PERKEY) P::mFS(qh[vs], qa[kk], hb);
-                    else P::mSS(qh[vs], cur.qs[kk], hb);
+                for (int r = 0; r < 4; ++r) {
+                    const int key = 32 * rg + 16 * ks + 4 * G + r;
+                    a.hslot[((ch * DK) + key) * DV + col] = h[ks][r];
                 }
+        }
+        const float* gm = gam[b];
+        const f32x4 eG = PERKEY ? f32x4{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const f32x4*>(&gm[BT + 16 * rg + 4 * G]);
+        const f32x4 eLG = PERKEY ? f32x4{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const f32x4*>(&gm[2 * BT + 16 * rg + 4 * G]);
+
+        // ---- token side: K h and q h for rows 16rg .. 16rg+15, columns of cg
+        const Op* K = kt[b];
+        f32x4 kh = {0.f, 0.f, 0.f, 0.f}, qh = {0.f, 0.f, 0.f, 0.f};
+        for (int kk = 0; kk < 4; ++kk) {
+            const F hb = P::ld(&hT[(16 * cg + n) * LDQ + 32 * kk + 8 * G]);
+            P::mma(kh, P::ld(&K[(16 * rg + n) * LDQ + 32 * kk + 8 * G]), hb);
+            if (OUT) {
+                f32x4 qv[FV];
+                for (int f = 0; f < FV; ++f) qv[f] = PERKEY ? cur.q[FV * kk + f] : P::in2op(cur.q[FV * kk + f]);
+                P::mma(qh, P::frag(qv), hb);
             }
         }
         // Y = beta (v - b^G K h) (per key: K already carries b^G)
-        for (int vs = 0; vs < 2; ++vs) {
+        {
+            const f32x4 bt = *reinterpret_cast<const f32x4*>(&bet[b][16 * rg + 4 * G]);
             float y[4];
             for (int r = 0; r < 4; ++r) {
-                const int i = 16 * w + 4 * G + r;
-                const float vv = (!mcols && i < len) ? P::f(cur.v[vs][r]) : 0.0f;
-                y[r] = bet[b][i] * (vv - eG[r] * kh[vs][r]);
+                const float vv = mcols ? 0.0f : P::f(cur.v[r]);
+                y[r] = bt[r] * (vv - eG[r] * kh[r]);
             }
-            P::st4(&YT[(16 * vs + n) * LDY + 16 * w + 4 * G], BV * LDY, y);
+            P::st4(&YT[(16 * cg + n) * LDY + 16 * rg + 4 * G], y);
         }
-        f32x4 oacc[2];
-        if (!SUMMARY) {
-            for (int vs = 0; vs < 2; ++vs)
-                for (int r = 0; r < 4; ++r) oacc[vs][r] = eG[r] * qh[vs][r];
-            if (!PERKEY) {
-                // P^T tiles (j block jt, i block w): rows j, columns i = 16w + n
-                const float gi = gam[b][16 * w + n];
-#pragma unroll
-                for (int jt = 0; jt < 4; ++jt) {
-                    if (jt > w) continue;
-                    f32x4 pt = {0.f, 0.f, 0.f, 0.f};
-                    for (int kk = 0; kk < 4; ++kk)
-                        P::mFF(pt, P::ldF(&K[(16 * jt + n) * LDK + 32 * kk + 8 * G]), qa[kk]);
-                    float x[4];
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = 16 * jt + 4 * G + r;
-                        x[r] = j <= 16 * w + n ? pt[r] * fpow(gi - gam[b][j], e2) : 0.0f;
-                    }
-                    P::st4(&PS[w * NP * 16 * LDY + n * LDY + 16 * jt + 4 * G], 16 * LDY, x);
-                }
-            }
-        }
+        f32x4 oacc;
+        if (OUT)
+            for (int r = 0; r < 4; ++r) oacc[r] = eG[r] * qh[r];
         __syncthreads();
+        if (PERKEY)
+            for (int i = 0; i < NKV; ++i) {
+                int r, cv;
+                tile_rc(i, r, cv);
+                *reinterpret_cast<f32x4*>(&kgt[r * LDQ + cv]) = kgr[i];
+            }
 
-        // ---- v_new = T Y for rows 16w .. 16w+15
-        f32x4 vn[2];
-        for (int vs = 0; vs < 2; ++vs) vn[vs] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int kk = 0; kk < 2; ++kk) {
-            if (kk >= nkw) continue;
-            const F ta = t_frag(cur, kk);
-            for (int vs = 0; vs < 2; ++vs)
-                P::mFS(vn[vs], ta, P::ldS(&YT[(16 * vs + n) * LDY + 32 * kk + 8 * G], BV * LDY));
-        }
-        for (int vs = 0; vs < 2; ++vs) {
+        // ---- v_new = T Y for rows 16rg .. 16rg+15
+        f32x4 vn = {0.f, 0.f, 0.f, 0.f};
+        for (int kk = 0; kk < 2; ++kk)
+            if (kk < nkw) P::mma(vn, P::frag(&cur.T[FV * kk]), P::ld(&YT[(16 * cg + n) * LDY + 32 * kk + 8 * G]));
+        {
             float x[4], xp[4];
             for (int r = 0; r < 4; ++r) {
-                x[r] = vn[vs][r];
-                xp[r] = x[r] * eLG[r];
+                x[r] = vn[r];
+                xp[r] = vn[r] * eLG[r];
             }
-            if (!SUMMARY) P::st4(&vnT[(16 * vs + n) * LDY + 16 * w + 4 * G], BV * LDY, x);
-            P::st4(&vpT[(16 * vs + n) * LDY + 16 * w + 4 * G], BV * LDY, xp);
+            if (OUT) P::st4(&vnT[(16 * cg + n) * LDY + 16 * rg + 4 * G], x);
+            P::st4(&vpT[(16 * cg + n) * LDY + 16 * rg + 4 * G], xp);
         }
         __syncthreads();
 
-        // ---- output rows 16w .. 16w+15
-        if (!SUMMARY) {
-            for (int kk = 0; kk < 2; ++kk) {
-                if (kk >= nkw) continue;
-                S pa;
-                if (!PERKEY) {
-                    pa = P::ldS(&PS[w * NP * 16 * LDY + n * LDY + 32 * kk + 8 * G], 16 * LDY);
-                } else {
-                    float f[8];
-                    for (int e = 0; e < 4; ++e) { f[e] = cur.Pw[kk][0][e]; f[e + 4] = cur.Pw[kk][1][e]; }
-                    pa = P::splitS(f);
+        // ---- output rows 16rg .. 16rg+15
+        if (OUT) {
+            for (int kk = 0; kk < 2; ++kk)
+                if (kk < nkw) P::mma(oacc, P::frag(&cur.Pr[FV * kk]), P::ld(&vnT[(16 * cg + n) * LDY + 32 * kk + 8 * G]));
+            float* of = reinterpret_cast<float*>(a.o) + (t0 * H + head) * DV;
+            bf16* ob = reinterpret_cast<bf16*>(a.o) + (t0 * H + head) * DV;
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * rg + 4 * G + r;
+                if (i < len) {
+                    const float x = a.scale * oacc[r];
+                    const uint32_t off = (uint32_t)i * tokstride + col;
+                    if (a.o_bf16) ob[off] = (bf16)x;
+                    else of[off] = x;
                 }
-                for (int vs = 0; vs < 2; ++vs)
-                    P::mSS(oacc[vs], pa, P::ldS(&vnT[(16 * vs + n) * LDY + 32 * kk + 8 * G], BV * LDY));
             }
-            for (int vs = 0; vs < 2; ++vs)
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * w + 4 * G + r;
-                    if (i < len) {
-                        const int64_t oi = ((t0 + i) * H + head) * DV + vc0 + 16 * vs + n;
-                        const float x = a.scale * oacc[vs][r];
-                        if (a.o_bf16) reinterpret_cast<bf16*>(a.o)[oi] = (bf16)x;
-                        else reinterpret_cast<float*>(a.o)[oi] = x;
-                    }
-                }
         }
 
-        // ---- state: h = Diag(b^{G_last}) h + kg^T v_new' for keys 32w .. 32w+31
-        S vb[2][2];
-        for (int kk = 0; kk < 2; ++kk)
-            for (int vs = 0; vs < 2; ++vs)
-                vb[kk][vs] = P::ldS(&vpT[(16 * vs + n) * LDY + 32 * kk + 8 * G], BV * LDY);
-        const float eL = PERKEY ? 1.0f : fpow(gL, e2);
-        for (int ks = 0; ks < 2; ++ks) {
-            float dec[4];
-            for (int r = 0; r < 4; ++r)
-                dec[r] = PERKEY ? fpow(gl[b][32 * w + 16 * ks + 4 * G + r], e2) : eL;
-            for (int vs = 0; vs < 2; ++vs)
-                for (int r = 0; r < 4; ++r) h[ks][vs][r] *= dec[r];
-            for (int kk = 0; kk < 2; ++kk) {
-                if (!PERKEY) {
-                    const F ka = P::ldcolF(K, LDK, 32 * kk, 32 * w + 16 * ks, lane);
-                    for (int vs = 0; vs < 2; ++vs) P::mFS(h[ks][vs], ka, vb[kk][vs]);
+        // ---- state: h = Diag(b^{G_last}) h + kg^T v_new' for keys 32rg .. 32rg+31
+        {
+            F vb[2];
+            for (int kk = 0; kk < 2; ++kk) vb[kk] = P::ld(&vpT[(16 * cg + n) * LDY + 32 * kk + 8 * G]);
+            const Op* KG = PERKEY ? kgt : K;
+            for (int ks = 0; ks < 2; ++ks) {
+                if (PERKEY) {
+                    const f32x4 gv = *reinterpret_cast<const f32x4*>(&gl[b][32 * rg + 16 * ks + 4 * G]);
+                    for (int r = 0; r < 4; ++r) h[ks][r] *= fpow(gv[r], e2);
                 } else {
-                    const S ka = P::ldcolS(kgt, BT * LDK, LDK, 32 * kk, 32 * w + 16 * ks, lane);
-                    for (int vs = 0; vs < 2; ++vs) P::mSS(h[ks][vs], ka, vb[kk][vs]);
+                    const float eL = gm[3 * BT];
+                    for (int r = 0; r < 4; ++r) h[ks][r] *= eL;
                 }
-            }
-            for (int vs = 0; vs < 2; ++vs) {
-                float x[4] = {h[ks][vs][0], h[ks][vs][1], h[ks][vs][2], h[ks][vs][3]};
-                P::st4(&hT[(16 * vs + n) * LDH + 32 * w + 16 * ks + 4 * G], BV * LDH, x);
+                for (int kk = 0; kk < 2; ++kk) P::mma(h[ks], P::ldcol(KG, LDQ, 32 * kk, 32 * rg + 16 * ks, lane), vb[kk]);
+                float x[4] = {h[ks][0], h[ks][1], h[ks][2], h[ks][3]};
+                P::st4(&hT[(16 * cg + n) * LDQ + 32 * rg + 16 * ks + 4 * G], x);
             }
         }
         if (more) {
@@ -806,17 +752,16 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
 
     // ---- results
     for (int ks = 0; ks < 2; ++ks)
-        for (int vs = 0; vs < 2; ++vs)
-            for (int r = 0; r < 4; ++r) {
-                const int key = 32 * w + 16 * ks + 4 * G + r, col = vc0 + 16 * vs + n;
-                const int64_t uh = (int64_t)u * H + head;
-                if (SUMMARY) {
-                    if (mcols) { if (a.M) a.M[(uh * DK + key) * DK + col] = h[ks][vs][r]; }
-                    else if (a.S_ext) a.S_ext[(uh * DK + key) * DV + col] = h[ks][vs][r];
-                } else if (a.hfinal) {
-                    a.hfinal[(uh * DK + key) * DV + col] = h[ks][vs][r];
-                }
+        for (int r = 0; r < 4; ++r) {
+            const int key = 32 * rg + 16 * ks + 4 * G + r;
+            const int64_t uh = (int64_t)u * H + head;
+            if (SUMMARY) {
+                if (mcols) { if (a.M) a.M[(uh * DK + key) * DK + col] = h[ks][r]; }
+                else if (a.S_ext) a.S_ext[(uh * DK + key) * DV + col] = h[ks][r];
+            } else if (a.hfinal) {
+                a.hfinal[(uh * DK + key) * DV + col] = h[ks][r];
             }
+        }
 }
 
 // ------------------------------------------------------------------ merge
@@ -863,29 +808,28 @@ static int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
 size_t workspace_bytes(const Problem& p, Workspace* ws, char* base) {
     const int64_t nch = (int64_t)p.um.n_chunks * p.H;
-    const int64_t es = p.dtype == 1 ? 2 : 4;
-    const int planes = p.dtype == 1 ? 2 : 1;
+    const int64_t es = p.dtype == 1 ? 2 : 4;      // operand element size (fp16 or fp32)
     int64_t off = 0;
     auto take = [&](int64_t bytes) { int64_t o = off; off = align256(off + bytes); return o; };
-    const int64_t oT = take(nch * BT * BT * 4);
-    const int64_t og = take(nch * BT * 4);
-    int64_t oP = 0, oq = 0, od = 0, ok = 0, ol = 0;
+    const int64_t oT = take(nch * BT * BT * es);
+    const int64_t oP = take(nch * BT * BT * es);
+    const int64_t og = take(nch * 4 * BT * 4);
+    int64_t oq = 0, od = 0, ok = 0, ol = 0;
     if (p.per_key) {
-        oP = take(nch * BT * BT * 4);
-        oq = take(planes * nch * BT * DK * es);
+        oq = take(nch * BT * DK * es);
         od = take(nch * BT * DK * es);
-        ok = take(planes * nch * BT * DK * es);
+        ok = take(nch * BT * DK * es);
         ol = take(nch * DK * 4);
     }
     if (ws && base) {
-        ws->Tm = reinterpret_cast<float*>(base + oT);
+        ws->Tm = base + oT;
+        ws->P = base + oP;
         ws->gam = reinterpret_cast<float*>(base + og);
-        ws->P = p.per_key ? reinterpret_cast<float*>(base + oP) : nullptr;
         ws->qg = p.per_key ? base + oq : nullptr;
         ws->kd = p.per_key ? base + od : nullptr;
         ws->kg = p.per_key ? base + ok : nullptr;
         ws->gamL = p.per_key ? reinterpret_cast<float*>(base + ol) : nullptr;
-        ws->plane = nch * BT * DK;
+        ws->plane = 0;
     }
     return (size_t)(off > 0 ? off : 256);
 }
@@ -899,19 +843,29 @@ hipError_t launch_prep(const Problem& p, const Workspace& ws, const void* k, con
     a.ws = ws; a.g_cumsum = g_cumsum_slot; a.A = A_slot;
     dim3 grid(p.um.n_chunks, p.H), block(256);
     if (p.dtype == 1) {
-        if (p.per_key) hipLaunchKernelGGL((prep_kernel<PolicyBF16, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((prep_kernel<PolicyBF16, false>), grid, block, 0, s, a);
+        if (p.per_key) hipLaunchKernelGGL((prep_kernel<PolicyH, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((prep_kernel<PolicyH, false>), grid, block, 0, s, a);
     } else {
-        if (p.per_key) hipLaunchKernelGGL((prep_kernel<PolicyF32, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((prep_kernel<PolicyF32, false>), grid, block, 0, s, a);
+        if (p.per_key) hipLaunchKernelGGL((prep_kernel<PolicyF, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((prep_kernel<PolicyF, false>), grid, block, 0, s, a);
     }
     return hipGetLastError();
 }
 
 template <class P, bool PK>
-static void launch_state_t(bool summary, dim3 grid, hipStream_t s, const StateArgs& a) {
-    if (summary) hipLaunchKernelGGL((state_kernel<P, PK, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((state_kernel<P, PK, false>), grid, dim3(256), 0, s, a);
+static void launch_state_t(bool summary, StateArgs a, int want_ext, int want_M, hipStream_t s) {
+    if (summary) {
+        a.tile0 = want_ext ? 0 : DV / BV;
+        a.ntiles = (want_ext ? DV / BV : 0) + (want_M ? DK / BV : 0);
+    } else {
+        a.tile0 = 0;
+        a.ntiles = DV / BV;
+    }
+    if (a.n_pairs == 0 || a.ntiles == 0) return;
+    const int groups = (a.n_pairs + 7) / 8;
+    dim3 grid(8 * a.ntiles * groups), block(ST);
+    if (summary) hipLaunchKernelGGL((state_kernel<P, PK, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((state_kernel<P, PK, false>), grid, block, 0, s, a);
 }
 
 hipError_t launch_state(const Problem& p, const Workspace& ws, const void* q, const void* k,
@@ -924,22 +878,13 @@ hipError_t launch_state(const Problem& p, const Workspace& ws, const void* q, co
     a.scale = p.scale; a.use_exp2 = p.use_exp2;
     a.n_pairs = p.um.n_units * p.H;
     a.S_ext = S_ext; a.M = M;
-    if (summary) {
-        a.tile0 = want_ext ? 0 : DV / BV;
-        a.ntiles = (want_ext ? DV / BV : 0) + (want_M ? DK / BV : 0);
-    } else {
-        a.tile0 = 0;
-        a.ntiles = DV / BV;
-    }
-    if (a.n_pairs == 0 || a.ntiles == 0) return hipSuccess;
-    const int groups = (a.n_pairs + 7) / 8;
-    dim3 grid(8 * a.ntiles * groups);
+    a.ntiles = 0; a.tile0 = 0;
     if (p.dtype == 1) {
-        if (p.per_key) launch_state_t<PolicyBF16, true>(summary, grid, s, a);
-        else launch_state_t<PolicyBF16, false>(summary, grid, s, a);
+        if (p.per_key) launch_state_t<PolicyH, true>(summary, a, want_ext, want_M, s);
+        else launch_state_t<PolicyH, false>(summary, a, want_ext, want_M, s);
     } else {
-        if (p.per_key) launch_state_t<PolicyF32, true>(summary, grid, s, a);
-        else launch_state_t<PolicyF32, false>(summary, grid, s, a);
+        if (p.per_key) launch_state_t<PolicyF, true>(summary, a, want_ext, want_M, s);
+        else launch_state_t<PolicyF, false>(summary, a, want_ext, want_M, s);
     }
     return hipGetLastError();
 }

@@ -162,7 +162,9 @@ def test_total_forgetting():
     o, _, _ = run_gpu(d)
     q, k, v, beta = (np32(d[n][0]).astype(np.float64) for n in ("q", "k", "v", "beta"))
     ref = d["scale"] * (beta * np.einsum("thk,thk->th", q, k))[..., None] * v
-    assert_close(np32(o[0]), ref, 1e-3, "total forgetting")
+    # each o_t is one product P_tt * v_new_t of two fp16-rounded operands
+    # (2 * 2^-11 relative) and max|o|/rms(o) is about 8 here: about 8e-3 at most
+    assert_close(np32(o[0]), ref, 1e-2, "total forgetting")
 
 
 def test_orthonormal_keys_retrieve():
