@@ -36,13 +36,16 @@ def kernel_source_hash() -> str:
 def byte_model(w, n_chunk_heads: int) -> dict:
     """Algorithmic bytes per launch: what each kernel must read and write by
     its contract (every byte once), summed over the chunk-heads it processes.
-    Scalar gate, per chunk-head of 64 tokens:
-      prep : k (64*128*es), g (64*4), beta (64*es)  ->  T (64*64*4), G (64*4)
-      state: q, k, v (3*64*128*es), T (64*64*4), G (64*4), beta (64*es) -> o (64*128*os)"""
+    Scalar gate, per chunk-head of 64 tokens, es = input element size, and
+    the prepared operands T, P in fp16 (bf16 inputs) or fp32 (fp32 inputs):
+      prep : q, k (2*64*128*es), g (64*4), beta (64*es)
+             -> T, P (2*64*64*ps), gate rows (4*64*4)
+      state: q, k, v (3*64*128*es), T, P (2*64*64*ps), gate rows (4*64*4),
+             beta (64*es) -> o (64*128*4, fp32)"""
     es = 2 if w.dtype == "bf16" else 4
-    os_ = 4
-    prep = 64 * 128 * es + 64 * 4 + 64 * es + 64 * 64 * 4 + 64 * 4
-    state = 3 * 64 * 128 * es + 64 * 64 * 4 + 64 * 4 + 64 * es + 64 * 128 * os_
+    ps = es
+    prep = 2 * 64 * 128 * es + 64 * 4 + 64 * es + 2 * 64 * 64 * ps + 4 * 64 * 4
+    state = 3 * 64 * 128 * es + 2 * 64 * 64 * ps + 4 * 64 * 4 + 64 * es + 64 * 128 * 4
     return {"prep": prep * n_chunk_heads, "state": state * n_chunk_heads,
             "prep_per_chunk_head": prep, "state_per_chunk_head": state}
 
@@ -100,6 +103,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gdn_dense_bf16")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device to device (calibrates the HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -108,6 +113,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n}), flush=True)
+        return
 
     from chunked_gated_delta_05_amd import binding as gb
     from chunked_gated_delta_05_amd import workloads as W

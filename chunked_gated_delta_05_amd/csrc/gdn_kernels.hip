@@ -488,13 +488,23 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
     constexpr int LDQ = P::LDQ;
     constexpr int FV = P::FV;
     constexpr bool OUT = !SUMMARY;
+    // STAGE: the q, T and P tiles are published once per workgroup into LDS
+    // and the output leaves through an LDS tile as whole row segments. The
+    // fp32 operand variant (twice the bytes per tile) reads q, T and P rows
+    // into registers per wave and stores the output directly instead.
+    constexpr bool STAGE = sizeof(Op) == 2;
+    constexpr int LDO = BV + 4;                                                 // output staging rows (fp32)
     __shared__ __attribute__((aligned(16))) Op kt[2][BT * LDQ];                  // k (per key: k*b^G)
-    __shared__ __attribute__((aligned(16))) Op kgt[PERKEY ? BT * LDQ : 8];      // per key: k*b^{G_last-G}
-    __shared__ __attribute__((aligned(16))) Op hT[BV * LDQ];                    // state, transposed
+    __shared__ __attribute__((aligned(16))) Op qt[STAGE && OUT ? BT * LDQ : 8];  // q (per key: q*b^G)
+    __shared__ __attribute__((aligned(16))) Op Tt[STAGE ? BT * LD6 : 8];         // T
+    __shared__ __attribute__((aligned(16))) Op Pt[STAGE && OUT ? BT * LD6 : 8];  // P
+    __shared__ __attribute__((aligned(16))) Op kgt[PERKEY ? BT * LDQ : 8];       // per key: k*b^{G_last-G}
+    __shared__ __attribute__((aligned(16))) Op hT[BV * LDQ];                     // state, transposed
     __shared__ __attribute__((aligned(16))) Op YT[BV * LDY];
     __shared__ __attribute__((aligned(16))) Op vnT[OUT ? BV * LDY : 8];
     __shared__ __attribute__((aligned(16))) Op vpT[BV * LDY];
-    __shared__ __attribute__((aligned(16))) float gam[2][4 * BT];               // G, b^G, b^{G_L-G}, b^{G_L}
+    __shared__ __attribute__((aligned(16))) float ot[STAGE && OUT ? BT * LDO : 4];  // output staging
+    __shared__ __attribute__((aligned(16))) float gam[2][4 * BT];                // G, b^G, b^{G_L-G}, b^{G_L}
     __shared__ __attribute__((aligned(16))) float bet[2][BT];
     __shared__ __attribute__((aligned(16))) float gl[2][PERKEY ? DK : 4];
 
@@ -513,7 +523,8 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
     const UnitInfo ui = unit_info(a.um, u);
     const int c0 = tile * BV;                       // column of [S_ext | M] or of V
     const bool mcols = SUMMARY && c0 >= DV;         // transfer-map columns: v = 0, start at I
-    const int col = (mcols ? c0 - DV : c0) + 16 * cg + n;   // this lane's state / output column
+    const int vc0 = mcols ? c0 - DV : c0;           // first state / output column of the workgroup
+    const int col = vc0 + 16 * cg + n;              // this lane's state / output column
     const In* qin = reinterpret_cast<const In*>(a.q);
     const In* kin = reinterpret_cast<const In*>(a.k);
     const In* vin = reinterpret_cast<const In*>(a.v);
@@ -534,28 +545,40 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
         }
 
     // ---- next-chunk prefetch. Loads for chunk c+1 are issued at the start of
-    // step c and stay raw in registers until used, so their latency overlaps a
-    // whole step. Rows past the chunk end read a clamped (valid) row: their
-    // contributions vanish because beta is zero there and T is the identity
-    // on padded rows, and padded output rows are never stored.
+    // step c and stay raw in registers until published (k, q, T and the gates
+    // at the end of step c, P and the per-key gated k at the start of step
+    // c+1), so their latency overlaps a whole step. Every tile load is a
+    // contiguous 16 bytes per lane. Rows past the chunk end read a clamped
+    // (valid) row: their contributions vanish because beta is zero there and
+    // T is the identity on padded rows, and padded output rows are not stored.
     constexpr int VPR = 16 / sizeof(In);
     constexpr int NKV = BT * DK / VPR / ST;           // 16-byte vectors per thread of a 64 x 128 tile
+    constexpr int NTV = BT * BT * (int)sizeof(Op) / 16 / ST;   // ... of a 64 x 64 operand tile
     constexpr int NGW = PERKEY ? DK : 4 * BT;         // gate words per chunk
+    constexpr int RQ = STAGE ? NKV : 4 * FV;          // q registers: tile vectors or the wave's rows
+    constexpr int RT = STAGE ? NTV : 2 * FV;          // T / P registers: tile vectors or the wave's rows
     auto chunk_len = [&](int c) { int l = ui.len - c * BT; return l < 0 ? 0 : (l > BT ? BT : l); };
     struct Raw {
-        f32x4 k[NKV];                    // k tile vectors (per key: k*b^G operands)
-        f32x4 q[OUT ? 4 * FV : 1];       // q rows 16rg+n (per key: q*b^G operands)
-        f32x4 T[2 * FV];                 // T rows 16rg+n, columns 32kk+8G.. (operands)
-        f32x4 Pr[OUT ? 2 * FV : 1];      // P rows 16rg+n (operands)
+        f32x4 k[NKV];                    // k tile (per key: k*b^G operands)
+        f32x4 q[OUT ? RQ : 1];           // q (per key: q*b^G operands)
+        f32x4 T[RT];                     // T operands
+        f32x4 Pr[OUT ? RT : 1];          // P operands
+        f32x4 kg[PERKEY ? NKV : 1];      // per key: k*b^{G_last-G} operands
         float gb;                        // gate word tid (threads < NGW)
         In bt;                           // beta
         In v[4];                         // v rows 16rg+4G+r, column col
         int len;
     };
-    auto tile_rc = [&](int i, int& r, int& cv) {
+    auto tile_rc = [&](int i, int& r, int& cv) {     // 64 x 128 tile vector -> (row, column)
         const int idx = tid + ST * i;
         r = idx / (DK / VPR);
         cv = (idx % (DK / VPR)) * VPR;
+    };
+    auto tile64_rc = [&](int i, int& r, int& cv) {   // 64 x 64 operand tile vector -> (row, column)
+        constexpr int per_row = BT * (int)sizeof(Op) / 16;
+        const int idx = tid + ST * i;
+        r = idx / per_row;
+        cv = (idx % per_row) * (16 / (int)sizeof(Op));
     };
     auto load_raw = [&](int c, Raw& x) {
         const int len = chunk_len(c);
@@ -564,17 +587,16 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
         const int64_t t0 = ui.start + (int64_t)c * BT;
         const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
         const int row = 16 * rg + n;
+        const Op* Tw = reinterpret_cast<const Op*>(a.ws.Tm) + ch * (BT * BT);
+        const Op* Pw = reinterpret_cast<const Op*>(a.ws.P) + ch * (BT * BT);
         if (PERKEY) {
             const Op* kd = reinterpret_cast<const Op*>(a.ws.kd) + ch * (BT * DK);
+            const Op* kg = reinterpret_cast<const Op*>(a.ws.kg) + ch * (BT * DK);
             for (int i = 0; i < NKV; ++i) {
                 int r, cv;
                 tile_rc(i, r, cv);
                 x.k[i] = *reinterpret_cast<const f32x4*>(kd + r * DK + cv);
-            }
-            if (OUT) {
-                const Op* qg = reinterpret_cast<const Op*>(a.ws.qg) + ch * (BT * DK) + row * DK + 8 * G;
-                for (int kk = 0; kk < 4; ++kk)
-                    for (int f = 0; f < FV; ++f) x.q[FV * kk + f] = *reinterpret_cast<const f32x4*>(qg + 32 * kk + 4 * f);
+                x.kg[i] = *reinterpret_cast<const f32x4*>(kg + r * DK + cv);
             }
             x.gb = tid < NGW ? a.ws.gamL[ch * DK + tid] : 0.0f;
         } else {
@@ -584,39 +606,98 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
                 tile_rc(i, r, cv);
                 x.k[i] = *reinterpret_cast<const f32x4*>(kb + (uint32_t)min(r, last) * tokstride + cv);
             }
-            if (OUT) {
-                const In* qb = qin + (t0 * H + head) * DK + (uint32_t)min(row, last) * tokstride + 8 * G;
-                for (int kk = 0; kk < 4; ++kk)
-                    for (int f = 0; f < FV; ++f) x.q[FV * kk + f] = *reinterpret_cast<const f32x4*>(qb + 32 * kk + 4 * f);
-            }
             x.gb = tid < NGW ? a.ws.gam[ch * (4 * BT) + tid] : 0.0f;
         }
-        const Op* Tr = reinterpret_cast<const Op*>(a.ws.Tm) + ch * (BT * BT) + row * BT + 8 * G;
-        const Op* Pw = reinterpret_cast<const Op*>(a.ws.P) + ch * (BT * BT) + row * BT + 8 * G;
-        for (int kk = 0; kk < 2; ++kk)
-            if (kk < nkw)
-                for (int f = 0; f < FV; ++f) {
-                    x.T[FV * kk + f] = *reinterpret_cast<const f32x4*>(Tr + 32 * kk + 4 * f);
-                    if (OUT) x.Pr[FV * kk + f] = *reinterpret_cast<const f32x4*>(Pw + 32 * kk + 4 * f);
+        if (OUT) {
+            const Op* qg = reinterpret_cast<const Op*>(a.ws.qg) + ch * (BT * DK);
+            const In* qb = qin + (t0 * H + head) * DK;
+            if (STAGE) {
+                for (int i = 0; i < NKV; ++i) {
+                    int r, cv;
+                    tile_rc(i, r, cv);
+                    x.q[i] = PERKEY ? *reinterpret_cast<const f32x4*>(qg + r * DK + cv)
+                                    : *reinterpret_cast<const f32x4*>(qb + (uint32_t)min(r, last) * tokstride + cv);
                 }
+            } else {
+                for (int kk = 0; kk < 4; ++kk)
+                    for (int f = 0; f < FV; ++f)
+                        x.q[FV * kk + f] = PERKEY ? *reinterpret_cast<const f32x4*>(qg + row * DK + 32 * kk + 8 * G + 4 * f)
+                                                  : *reinterpret_cast<const f32x4*>(qb + (uint32_t)min(row, last) * tokstride +
+                                                                                     32 * kk + 8 * G + 4 * f);
+            }
+        }
+        if (STAGE) {
+            for (int i = 0; i < NTV; ++i) {
+                int r, cv;
+                tile64_rc(i, r, cv);
+                x.T[i] = *reinterpret_cast<const f32x4*>(Tw + r * BT + cv);
+                if (OUT) x.Pr[i] = *reinterpret_cast<const f32x4*>(Pw + r * BT + cv);
+            }
+        } else {
+            for (int kk = 0; kk < 2; ++kk)
+                if (kk < nkw)
+                    for (int f = 0; f < FV; ++f) {
+                        x.T[FV * kk + f] = *reinterpret_cast<const f32x4*>(Tw + row * BT + 32 * kk + 8 * G + 4 * f);
+                        if (OUT) x.Pr[FV * kk + f] = *reinterpret_cast<const f32x4*>(Pw + row * BT + 32 * kk + 8 * G + 4 * f);
+                    }
+        }
         x.bt = (bin + t0 * H + head)[(uint32_t)min(lane, last) * H];
         if (!mcols) {
             const In* vb = vin + (t0 * H + head) * DV;
             for (int r = 0; r < 4; ++r) x.v[r] = vb[(uint32_t)min(16 * rg + 4 * G + r, last) * tokstride + col];
         }
     };
-    // chunk data the whole workgroup reads through LDS
-    auto publish = [&](const Raw& x, int b) {
+    // k, q, T and the gates of a chunk (read from its step's start)
+    auto publish_main = [&](const Raw& x, int b) {
         for (int i = 0; i < NKV; ++i) {
             int r, cv;
             tile_rc(i, r, cv);
             *reinterpret_cast<f32x4*>(&kt[b][r * LDQ + cv]) = PERKEY ? x.k[i] : P::in2op(x.k[i]);
+            if (STAGE && OUT) *reinterpret_cast<f32x4*>(&qt[r * LDQ + cv]) = PERKEY ? x.q[i] : P::in2op(x.q[i]);
         }
+        if (STAGE)
+            for (int i = 0; i < NTV; ++i) {
+                int r, cv;
+                tile64_rc(i, r, cv);
+                *reinterpret_cast<f32x4*>(&Tt[r * LD6 + cv]) = x.T[i];
+            }
         if (tid < NGW) {
             if (PERKEY) gl[b][tid] = x.gb;
             else gam[b][tid] = x.gb;
         }
         if (tid < BT) bet[b][tid] = tid < x.len ? P::f(x.bt) : 0.0f;
+    };
+    // P and the per-key gated k of a chunk (read only after its step's first barrier)
+    auto publish_late = [&](const Raw& x) {
+        if (STAGE && OUT)
+            for (int i = 0; i < NTV; ++i) {
+                int r, cv;
+                tile64_rc(i, r, cv);
+                *reinterpret_cast<f32x4*>(&Pt[r * LD6 + cv]) = x.Pr[i];
+            }
+        if (PERKEY)
+            for (int i = 0; i < NKV; ++i) {
+                int r, cv;
+                tile_rc(i, r, cv);
+                *reinterpret_cast<f32x4*>(&kgt[r * LDQ + cv]) = x.kg[i];
+            }
+    };
+    // output rows of chunk c from the staging tile, 16 bytes per thread
+    auto flush_out = [&](int c, int len) {
+        const int64_t t0 = ui.start + (int64_t)c * BT;
+        constexpr int per_row = BV / 4;
+        const int r = tid / per_row, cc = (tid % per_row) * 4;
+        if (r < len) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(&ot[r * LDO + cc]);
+            const uint32_t off = (uint32_t)r * tokstride + vc0 + cc;
+            if (a.o_bf16) {
+                bf16* ob = reinterpret_cast<bf16*>(a.o) + (t0 * H + head) * DV;
+                for (int e = 0; e < 4; ++e) ob[off + e] = (bf16)x[e];
+            } else {
+                float* of = reinterpret_cast<float*>(a.o) + (t0 * H + head) * DV;
+                *reinterpret_cast<f32x4*>(of + off) = x;
+            }
+        }
     };
 
     // ---- prologue
@@ -624,7 +705,7 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
     Raw cur, nxt;
     if (nch > 0) {
         load_raw(0, cur);
-        publish(cur, 0);
+        publish_main(cur, 0);
     }
     for (int ks = 0; ks < 2; ++ks) {
         float x[4] = {h[ks][0], h[ks][1], h[ks][2], h[ks][3]};
@@ -638,17 +719,9 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
         const int64_t t0 = ui.start + (int64_t)c * BT;
         const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
         const bool more = c + 1 < nch;
+        if (STAGE && OUT && c > 0) flush_out(c - 1, chunk_len(c - 1));
+        publish_late(cur);
         if (more) load_raw(c + 1, nxt);
-        f32x4 kgr[PERKEY ? NKV : 1];
-        if (PERKEY) {
-            // k*b^{G_last-G} of this chunk, stored to LDS after the next barrier
-            const Op* kg = reinterpret_cast<const Op*>(a.ws.kg) + ch * (BT * DK);
-            for (int i = 0; i < NKV; ++i) {
-                int r, cv;
-                tile_rc(i, r, cv);
-                kgr[i] = *reinterpret_cast<const f32x4*>(kg + r * DK + cv);
-            }
-        }
         if (OUT && a.hslot) {
             for (int ks = 0; ks < 2; ++ks)
                 for (int r = 0; r < 4; ++r) {
@@ -667,9 +740,13 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
             const F hb = P::ld(&hT[(16 * cg + n) * LDQ + 32 * kk + 8 * G]);
             P::mma(kh, P::ld(&K[(16 * rg + n) * LDQ + 32 * kk + 8 * G]), hb);
             if (OUT) {
-                f32x4 qv[FV];
-                for (int f = 0; f < FV; ++f) qv[f] = PERKEY ? cur.q[FV * kk + f] : P::in2op(cur.q[FV * kk + f]);
-                P::mma(qh, P::frag(qv), hb);
+                if (STAGE) {
+                    P::mma(qh, P::ld(&qt[(16 * rg + n) * LDQ + 32 * kk + 8 * G]), hb);
+                } else {
+                    f32x4 qv[FV];
+                    for (int f = 0; f < FV; ++f) qv[f] = PERKEY ? cur.q[FV * kk + f] : P::in2op(cur.q[FV * kk + f]);
+                    P::mma(qh, P::frag(qv), hb);
+                }
             }
         }
         // Y = beta (v - b^G K h) (per key: K already carries b^G)
@@ -686,17 +763,14 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
         if (OUT)
             for (int r = 0; r < 4; ++r) oacc[r] = eG[r] * qh[r];
         __syncthreads();
-        if (PERKEY)
-            for (int i = 0; i < NKV; ++i) {
-                int r, cv;
-                tile_rc(i, r, cv);
-                *reinterpret_cast<f32x4*>(&kgt[r * LDQ + cv]) = kgr[i];
-            }
 
         // ---- v_new = T Y for rows 16rg .. 16rg+15
         f32x4 vn = {0.f, 0.f, 0.f, 0.f};
         for (int kk = 0; kk < 2; ++kk)
-            if (kk < nkw) P::mma(vn, P::frag(&cur.T[FV * kk]), P::ld(&YT[(16 * cg + n) * LDY + 32 * kk + 8 * G]));
+            if (kk < nkw) {
+                const F ta = STAGE ? P::ld(&Tt[(16 * rg + n) * LD6 + 32 * kk + 8 * G]) : P::frag(&cur.T[FV * kk]);
+                P::mma(vn, ta, P::ld(&YT[(16 * cg + n) * LDY + 32 * kk + 8 * G]));
+            }
         {
             float x[4], xp[4];
             for (int r = 0; r < 4; ++r) {
@@ -711,16 +785,23 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
         // ---- output rows 16rg .. 16rg+15
         if (OUT) {
             for (int kk = 0; kk < 2; ++kk)
-                if (kk < nkw) P::mma(oacc, P::frag(&cur.Pr[FV * kk]), P::ld(&vnT[(16 * cg + n) * LDY + 32 * kk + 8 * G]));
-            float* of = reinterpret_cast<float*>(a.o) + (t0 * H + head) * DV;
-            bf16* ob = reinterpret_cast<bf16*>(a.o) + (t0 * H + head) * DV;
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * rg + 4 * G + r;
-                if (i < len) {
-                    const float x = a.scale * oacc[r];
-                    const uint32_t off = (uint32_t)i * tokstride + col;
-                    if (a.o_bf16) ob[off] = (bf16)x;
-                    else of[off] = x;
+                if (kk < nkw) {
+                    const F pa = STAGE ? P::ld(&Pt[(16 * rg + n) * LD6 + 32 * kk + 8 * G]) : P::frag(&cur.Pr[FV * kk]);
+                    P::mma(oacc, pa, P::ld(&vnT[(16 * cg + n) * LDY + 32 * kk + 8 * G]));
+                }
+            if (STAGE) {
+                for (int r = 0; r < 4; ++r) ot[(16 * rg + 4 * G + r) * LDO + 16 * cg + n] = a.scale * oacc[r];
+            } else {
+                float* of = reinterpret_cast<float*>(a.o) + (t0 * H + head) * DV;
+                bf16* ob = reinterpret_cast<bf16*>(a.o) + (t0 * H + head) * DV;
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * rg + 4 * G + r;
+                    if (i < len) {
+                        const float x = a.scale * oacc[r];
+                        const uint32_t off = (uint32_t)i * tokstride + col;
+                        if (a.o_bf16) ob[off] = (bf16)x;
+                        else of[off] = x;
+                    }
                 }
             }
         }
@@ -744,11 +825,12 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
             }
         }
         if (more) {
-            publish(nxt, b ^ 1);
+            publish_main(nxt, b ^ 1);
             cur = nxt;
         }
         __syncthreads();
     }
+    if (STAGE && OUT && nch > 0) flush_out(nch - 1, chunk_len(nch - 1));
 
     // ---- results
     for (int ks = 0; ks < 2; ++ks)

@@ -88,9 +88,12 @@ def fwd(d, *, ws=FAKE, nbytes=None, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o
 
 def test_workspace_query_sizes():
     st, nb = fwd(desc(), ws=None)
-    # T: 64x64 fp32 + gate cumsum 64 fp32 per chunk-head, each region 256-aligned
+    # bf16 inputs: T and P as 64x64 fp16 operand tiles, plus four 64-entry fp32
+    # gate rows (G, b^G, b^{G_last-G}, b^{G_last}) per chunk-head; every region
+    # starts 256-aligned
     nch = 2 * 4 * 3
-    expect = ((nch * 64 * 64 * 4 + 255) // 256) * 256 + ((nch * 64 * 4 + 255) // 256) * 256
+    a256 = lambda x: ((x + 255) // 256) * 256
+    expect = 2 * a256(nch * 64 * 64 * 2) + a256(nch * 4 * 64 * 4)
     assert st == gb.GDN_OK and nb == expect
     st, nb2 = fwd(desc(gate_kind=1), ws=None)
     assert st == gb.GDN_OK and nb2 > nb
