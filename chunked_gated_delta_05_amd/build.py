@@ -36,6 +36,9 @@ def build(verbose: bool = False) -> str:
     hobj = os.path.join(BUILD, "gdn_host.o")
     _run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # MFMA accumulators in ordinary VGPRs: the state update scales them
+          # with VALU ops every chunk, which AGPR accumulators turn into copies
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           *warn, *inc, "-c", SOURCES[0], "-o", kobj], verbose)
     _run([HIPCC, "-O2", "-std=c++17", "-fPIC", "-D__HIP_PLATFORM_AMD__", *warn, *inc, "-I", "/opt/rocm/include",
           "-x", "c++", "-c", SOURCES[1], "-o", hobj], verbose)

@@ -51,6 +51,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
+// bits of a float. Taken through a by-value parameter: applied directly to a
+// vector element (v[i]), __builtin_bit_cast reads element 0 with this
+// compiler.
+__device__ __forceinline__ uint32_t f2u(float x) { return __builtin_bit_cast(uint32_t, x); }
+
 // b^x with the hardware base-2 exponential (about 1 ulp; e^x = 2^(x log2 e))
 __device__ __forceinline__ float fpow(float x, int use_exp2) {
     return __builtin_amdgcn_exp2f(use_exp2 ? x : x * 1.4426950408889634f);
@@ -193,6 +198,18 @@ __device__ __forceinline__ UnitInfo unit_info(const UnitMap& um, int u) {
     return r;
 }
 
+// the same fields, marked wave-uniform (they depend on the workgroup only) so
+// that values derived from them can live in scalar registers
+__device__ __forceinline__ UnitInfo uniform(UnitInfo r) {
+    const uint64_t s = (uint64_t)r.start;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)s), hi = __builtin_amdgcn_readfirstlane((uint32_t)(s >> 32));
+    r.start = (int64_t)(((uint64_t)hi << 32) | lo);
+    r.len = __builtin_amdgcn_readfirstlane(r.len);
+    r.nch = __builtin_amdgcn_readfirstlane(r.nch);
+    r.cbase = __builtin_amdgcn_readfirstlane(r.cbase);
+    return r;
+}
+
 // (unit, chunk in unit) of a flat chunk index
 __device__ __forceinline__ void chunk_of(const UnitMap& um, int ci, int& u, int& c) {
     if (um.dense) {
@@ -203,6 +220,29 @@ __device__ __forceinline__ void chunk_of(const UnitMap& um, int ci, int& u, int&
         c = um.chunk_indices[2 * ci + 1];
         if (u < 0 || u >= um.n_units) { u = -1; c = 0; }
     }
+}
+
+// ------------------------------------------------------------------ operand order
+// Order of the 64 x 128 k / q tiles (along keys) and of the 64 x 64 T and P
+// tiles (along tokens) in the fp16 state pass: within each 32-wide slice,
+// position 8g + 4h + c holds element 16h + 4g + c. A 16-byte fragment read
+// at position 32s + 8g then pairs, element for element, with accumulator
+// rows 4g + c of the 16-row tiles 2s (h = 0) and 2s + 1 (h = 1), so that
+// accumulators serve as MFMA B operands straight from registers: the order
+// of the terms inside one 32-deep contraction does not change the product.
+__device__ __forceinline__ int op_pos(int x) { return (x & ~31) | ((x & 12) << 1) | ((x & 16) >> 2) | (x & 3); }
+
+// 16-byte granule swizzles of LDS tiles that avoid bank conflicts for the
+// row-fragment reads and the transposed reads of the fp16 state pass:
+// rows of 128 operands (16 granules) and rows of 64 operands (8 granules)
+__device__ __forceinline__ int swz16(int r) { return ((r & 3) << 2) ^ ((r >> 2) & 3); }
+__device__ __forceinline__ int swz8(int r) { return r & 7; }
+
+// raw buffer resource over [base, base + bytes): accesses outside read as zero
+// and writes outside are dropped
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 // ------------------------------------------------------------------ prep
@@ -378,12 +418,14 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     }
 
     // ---- T out as operands (row-major 64 x 64), optional token-major fp32 A slot
+    // fp16 operands are stored in the state pass's operand order (op_pos)
+    constexpr bool PERM = sizeof(Op) == 2;
     Op* Tw = reinterpret_cast<Op*>(a.ws.Tm) + ch * (BT * BT);
     for (int e = tid; e < BT * BT / 4; e += 256) {
         const int r = e / (BT / 4), c4 = (e % (BT / 4)) * 4;
         f32x4 x;
         for (int q2 = 0; q2 < 4; ++q2) x[q2] = Ts[r * LDL + c4 + q2];
-        P::f32_to_op4(Tw + r * BT + c4, x);
+        P::f32_to_op4(Tw + r * BT + (PERM ? op_pos(c4) : c4), x);
         if (a.A && r < len) *reinterpret_cast<f32x4*>(a.A + ((t0 + r) * H + head) * BT + c4) = x;
     }
 
@@ -421,7 +463,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
                 if (!PERKEY && j <= i) pv *= fpow(Gs[i] - Gs[j], a.use_exp2);
                 x[r] = pv;
             }
-            P::st4(Pw + i * BT + 16 * jt + 4 * G, x);
+            P::st4(Pw + i * BT + (PERM ? op_pos(16 * jt + 4 * G) : 16 * jt + 4 * G), x);
         }
     }
 
@@ -846,6 +888,416 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
         }
 }
 
+// ------------------------------------------------------------------ state pass, fp16 operands
+// Workgroup of 4 waves for one (unit, head, 32-column tile). Waves 0 and 1
+// each own 16 value columns with all 64 token rows and all 128 keys, so the
+// recurrence needs no exchange between waves: the state, the residual Y and
+// v_new stay in registers and feed the MFMAs as B operands (operand order
+// above). Waves 2 and 3, on the other two SIMDs, stream the chunk tiles
+// (k and q converted to fp16, T, P, beta*v and the per-row gate factors)
+// into double-buffered LDS, issuing each chunk's loads two steps ahead of
+// its use. One barrier per chunk hands the buffers over.
+constexpr int HW = 4;              // waves per workgroup
+constexpr int HT = 64 * HW;        // threads
+constexpr int LVT = BT + 4;        // row stride (floats) of the transposed beta*v tile
+
+template <bool PERKEY, bool SUMMARY>
+__global__ __launch_bounds__(HT) void state_kernel_h(StateArgs a) {
+    using F = PolicyH::F;
+    constexpr bool OUT = !SUMMARY;
+    constexpr int NSET = PERKEY && OUT ? 1 : 2;        // register sets of chunk loads in flight
+    __shared__ __attribute__((aligned(16))) f16 kt[2][BT * DK];                          // k (per key: k*b^G)
+    __shared__ __attribute__((aligned(16))) f16 qt[OUT ? 2 : 1][OUT ? BT * DK : 8];      // q (per key: q*b^G)
+    __shared__ __attribute__((aligned(16))) f16 gt[PERKEY ? 2 : 1][PERKEY ? BT * DK : 8];// per key: k*b^{G_L-G}
+    __shared__ __attribute__((aligned(16))) f16 Tt[2][BT * BT];
+    __shared__ __attribute__((aligned(16))) f16 Pt[OUT ? 2 : 1][OUT ? BT * BT : 8];
+    __shared__ __attribute__((aligned(16))) float vbT[2][BV * LVT];                      // beta*v, [column][row]
+    __shared__ __attribute__((aligned(16))) float cf[2][4][BT];   // beta b^G, b^{G_L-G}, scale b^G, b^{G_L}
+    __shared__ __attribute__((aligned(16))) float gl[2][PERKEY ? DK : 4];                // per key: b^{G_L}
+
+    const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = a.H;
+    const int L = blockIdx.x, xcd = L & 7, slot = L >> 3;
+    const int tile = slot % a.ntiles + a.tile0;
+    const int pair = (slot / a.ntiles) * 8 + xcd;
+    if (pair >= a.n_pairs) return;
+    const int u = pair / H, head = pair - u * H;
+    const UnitInfo ui = uniform(unit_info(a.um, u));
+    const int c0 = tile * BV;
+    const bool mcols = SUMMARY && c0 >= DV;         // transfer-map columns: v = 0, start at I
+    const int vc0 = mcols ? c0 - DV : c0;
+    const int nch = ui.nch;
+    const uint32_t tokstride = (uint32_t)H * DK;
+    auto chunk_len = [&](int c) {
+        int l = ui.len - c * BT;
+        return __builtin_amdgcn_readfirstlane(l < 0 ? 0 : (l > BT ? BT : l));
+    };
+
+    if (wv < 2) {
+        // ======================= compute waves
+        const int col = vc0 + 16 * wv + n;
+        f32x4 h[8];                                  // keys 16 kt8 + 4G + r, column col
+        for (int kt8 = 0; kt8 < 8; ++kt8)
+            for (int r = 0; r < 4; ++r) {
+                const int key = 16 * kt8 + 4 * G + r;
+                float x = 0.0f;
+                if (mcols) x = key == col ? 1.0f : 0.0f;
+                else if (OUT && a.h0) x = a.h0[(((int64_t)u * H + head) * DK + key) * DV + col];
+                h[kt8][r] = x;
+            }
+        auto pack = [](const f32x4& x, const f32x4& y) {
+            F f;
+            for (int e = 0; e < 4; ++e) { f.v[e] = (f16)x[e]; f.v[e + 4] = (f16)y[e]; }
+            return f;
+        };
+        F hb[4];
+        for (int s2 = 0; s2 < 4; ++s2) hb[s2] = pack(h[2 * s2], h[2 * s2 + 1]);
+        // per-lane LDS byte offsets
+        int offA[4], offG[4];
+        for (int s2 = 0; s2 < 4; ++s2) {
+            offA[s2] = n * 256 + (((4 * s2 + G) ^ swz16(n)) << 4);            // row n, granule 4s+G
+            const int rt = 4 * G + (n >> 2);                                    // transposed read row
+            offG[s2] = rt * 256 + (((4 * s2 + (n & 3)) ^ swz16(rt)) << 4);
+        }
+        int offT[2];
+        for (int kk = 0; kk < 2; ++kk) offT[kk] = n * 128 + (((4 * kk + G) ^ swz8(n)) << 4);
+        const int offV = (16 * wv + n) * LVT + 4 * G;
+        uint32_t ooff[4];
+        for (int r = 0; r < 4; ++r) ooff[r] = (uint32_t)(4 * G + r) * tokstride + col;
+        auto ldA = [](const f16* t, int byte_off) {
+            F f;
+            f.v = *reinterpret_cast<const f16x8*>(reinterpret_cast<const char*>(t) + byte_off);
+            return f;
+        };
+        // k^T fragment (keys 16 kt8 + n, tokens 32 kk + 4G + e and 32 kk + 16 + 4G + e)
+        auto ldKT = [&](const f16* t, int kt8, int kk) {
+            const char* p = reinterpret_cast<const char*>(t) + offG[kt8 >> 1] + (kt8 & 1) * 8 + kk * 32 * 256;
+            s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, p));
+            s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, p + 16 * 256));
+            f16x4 fx = __builtin_bit_cast(f16x4, x), fy = __builtin_bit_cast(f16x4, y);
+            F f;
+            for (int e = 0; e < 4; ++e) { f.v[e] = fx[e]; f.v[e + 4] = fy[e]; }
+            return f;
+        };
+        __syncthreads();                              // chunk 0 published
+
+        // per-lane element offsets of the state slot rows (keys 4G + r)
+        uint32_t hoff[4];
+        for (int r = 0; r < 4; ++r) hoff[r] = (uint32_t)(4 * G + r) * DV + col;
+        for (int c = 0; c < nch; ++c) {
+            // an opaque copy of the chunk index keeps the compiler from turning
+            // every per-lane address into a loop-carried 64-bit pointer
+            const int cu = __builtin_amdgcn_readfirstlane(c);
+            const int b = cu & 1;
+            const int len = chunk_len(cu);
+            const int64_t t0 = ui.start + (int64_t)cu * BT;
+            const int64_t ch = (int64_t)(ui.cbase + cu) * H + head;
+            if (OUT && a.hslot) {
+                float* hs = a.hslot + ch * (DK * DV);
+                for (int kt8 = 0; kt8 < 8; ++kt8)
+                    for (int r = 0; r < 4; ++r) hs[16 * kt8 * DV + hoff[r]] = h[kt8][r];
+            }
+            const f16* K = kt[b];
+            const f16* Q = qt[OUT ? b : 0];
+            const f16* Tc = Tt[b];
+            const f16* Pc = Pt[OUT ? b : 0];
+            const f16* KG = PERKEY ? gt[PERKEY ? b : 0] : K;
+            // LDS reads are issued in the order they are consumed, a stage ahead
+            // of the MFMAs that use them; the scheduling fences keep the compiler
+            // from sinking them next to their uses, which would expose the LDS
+            // latency once per MFMA.
+            F fk[2][4], fq[2][4];
+            auto ldKQ = [&](int s2, F* k4, F* q4) {
+                for (int it = 0; it < 4; ++it) {
+                    k4[it] = ldA(K, offA[s2] + it * 16 * 256);
+                    if (OUT) q4[it] = ldA(Q, offA[s2] + it * 16 * 256);
+                }
+            };
+            auto mmaKQ = [&](int s2, const F* k4, const F* q4, f32x4* kh, f32x4* qh) {
+                for (int it = 0; it < 4; ++it) {
+                    PolicyH::mma(kh[it], k4[it], hb[s2]);
+                    if (OUT) PolicyH::mma(qh[it], q4[it], hb[s2]);
+                }
+            };
+            // ---- K h and q h, all 64 rows
+            f32x4 kh[4], qh[4];
+            for (int it = 0; it < 4; ++it) kh[it] = qh[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+            ldKQ(0, fk[0], fq[0]);
+            ldKQ(1, fk[1], fq[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mmaKQ(0, fk[0], fq[0], kh, qh);
+            __builtin_amdgcn_sched_barrier(0);
+            ldKQ(2, fk[0], fq[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            mmaKQ(1, fk[1], fq[1], kh, qh);
+            __builtin_amdgcn_sched_barrier(0);
+            ldKQ(3, fk[1], fq[1]);
+            // T fragments and the Y coefficients for the next phase
+            F ft[4][2];
+            for (int it = 0; it < 4; ++it) {
+                ft[it][0] = ldA(Tc, offT[0] + it * 16 * 128);
+                if (it >= 2) ft[it][1] = ldA(Tc, offT[1] + it * 16 * 128);
+            }
+            f32x4 cy[4], vv[4];
+            for (int it = 0; it < 4; ++it) {
+                cy[it] = *reinterpret_cast<const f32x4*>(&cf[b][0][16 * it + 4 * G]);
+                vv[it] = mcols ? f32x4{0.f, 0.f, 0.f, 0.f} : *reinterpret_cast<const f32x4*>(&vbT[b][offV + 16 * it]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            mmaKQ(2, fk[0], fq[0], kh, qh);
+            __builtin_amdgcn_sched_barrier(0);
+            mmaKQ(3, fk[1], fq[1], kh, qh);
+            __builtin_amdgcn_sched_barrier(0);
+            // first k^T fragments of the state update, P fragments, coefficients
+            F fg0[8], fg1[8];                         // token slices 0 and 1 of key tile kt8
+            for (int kt8 = 0; kt8 < 2; ++kt8) {
+                fg0[kt8] = ldKT(KG, kt8, 0);
+                fg1[kt8] = ldKT(KG, kt8, 1);
+            }
+            // ---- Y = beta v - beta b^G (K h)
+            f32x4 y[4];
+            for (int it = 0; it < 4; ++it)
+                for (int r = 0; r < 4; ++r) y[it][r] = vv[it][r] - cy[it][r] * kh[it][r];
+            const F yb0 = pack(y[0], y[1]), yb1 = pack(y[2], y[3]);
+            // ---- v_new = T Y (T lower triangular)
+            f32x4 vn[4];
+            for (int it = 0; it < 4; ++it) {
+                vn[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+                PolicyH::mma(vn[it], ft[it][0], yb0);
+                if (it >= 2) PolicyH::mma(vn[it], ft[it][1], yb1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            F fp[4][2];
+            f32x4 cp[4], co[4];
+            for (int it = 0; it < 4; ++it) {
+                if (OUT) {
+                    fp[it][0] = ldA(Pc, offT[0] + it * 16 * 128);
+                    if (it >= 2) fp[it][1] = ldA(Pc, offT[1] + it * 16 * 128);
+                    co[it] = *reinterpret_cast<const f32x4*>(&cf[b][2][16 * it + 4 * G]);
+                }
+                if (!PERKEY) cp[it] = *reinterpret_cast<const f32x4*>(&cf[b][1][16 * it + 4 * G]);
+            }
+            for (int kt8 = 2; kt8 < 4; ++kt8) {
+                fg0[kt8] = ldKT(KG, kt8, 0);
+                fg1[kt8] = ldKT(KG, kt8, 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 vp[4];
+            for (int it = 0; it < 4; ++it) {
+                if (PERKEY) vp[it] = vn[it];
+                else
+                    for (int r = 0; r < 4; ++r) vp[it][r] = vn[it][r] * cp[it][r];
+            }
+            const F vb0 = pack(vp[0], vp[1]), vb1 = pack(vp[2], vp[3]);
+            // ---- output: scale b^G (q h) + P (scale v_new)
+            if (OUT) {
+                f32x4 vs[4];
+                for (int it = 0; it < 4; ++it)
+                    for (int r = 0; r < 4; ++r) vs[it][r] = a.scale * vn[it][r];
+                const F nb0 = pack(vs[0], vs[1]), nb1 = pack(vs[2], vs[3]);
+                for (int it = 0; it < 4; ++it) {
+                    f32x4 o;
+                    for (int r = 0; r < 4; ++r) o[r] = co[it][r] * qh[it][r];
+                    PolicyH::mma(o, fp[it][0], nb0);
+                    if (it >= 2) PolicyH::mma(o, fp[it][1], nb1);
+                    // rows past the chunk end fall outside the buffer range: dropped
+                    const int64_t rb = ((t0 + 16 * it) * H + head) * DV;
+                    const uint32_t nrow = (uint32_t)max(len - 16 * it, 0);
+                    if (a.o_bf16) {
+                        const rsrc_t ro = make_rsrc(reinterpret_cast<bf16*>(a.o) + rb, nrow * tokstride * 2);
+                        for (int r = 0; r < 4; ++r)
+                            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (bf16)o[r]), ro, ooff[r] * 2, 0, 0);
+                    } else {
+                        const rsrc_t ro = make_rsrc(reinterpret_cast<float*>(a.o) + rb, nrow * tokstride * 4);
+                        for (int r = 0; r < 4; ++r)
+                            __builtin_amdgcn_raw_buffer_store_b32(f2u(o[r]), ro, ooff[r] * 4, 0, 0);
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- state: h = Diag(b^{G_last}) h + kg^T v_new', k^T fragments two tiles ahead
+            const float eL = PERKEY ? 1.0f : cf[b][3][0];
+            for (int kt8 = 0; kt8 < 8; ++kt8) {
+                if (kt8 + 4 < 8) {
+                    fg0[kt8 + 4] = ldKT(KG, kt8 + 4, 0);
+                    fg1[kt8 + 4] = ldKT(KG, kt8 + 4, 1);
+                }
+                if (PERKEY) {
+                    const f32x4 gv = *reinterpret_cast<const f32x4*>(&gl[b][16 * kt8 + 4 * G]);
+                    for (int r = 0; r < 4; ++r) h[kt8][r] *= gv[r];
+                } else {
+                    for (int r = 0; r < 4; ++r) h[kt8][r] *= eL;
+                }
+                PolicyH::mma(h[kt8], fg0[kt8], vb0);
+                PolicyH::mma(h[kt8], fg1[kt8], vb1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            for (int s2 = 0; s2 < 4; ++s2) hb[s2] = pack(h[2 * s2], h[2 * s2 + 1]);
+            __syncthreads();                          // chunk c consumed, chunk c+1 published
+        }
+        // ---- results
+        for (int kt8 = 0; kt8 < 8; ++kt8)
+            for (int r = 0; r < 4; ++r) {
+                const int key = 16 * kt8 + 4 * G + r;
+                const int64_t uh = (int64_t)u * H + head;
+                if (SUMMARY) {
+                    if (mcols) { if (a.M) a.M[(uh * DK + key) * DK + col] = h[kt8][r]; }
+                    else if (a.S_ext) a.S_ext[(uh * DK + key) * DV + col] = h[kt8][r];
+                } else if (a.hfinal) {
+                    a.hfinal[(uh * DK + key) * DV + col] = h[kt8][r];
+                }
+            }
+    } else {
+        // ======================= streaming waves
+        // Buffer loads with 32-bit lane offsets; rows past the chunk end fall
+        // outside the buffer range and read as zeros, which zeroes beta and v
+        // there (the padded rows then contribute nothing).
+        const int lt = tid - 128;
+        struct Raw {
+            u32x4 k[8];                   // 64 x 128 tile: row (lt >> 4) + 8i, elements 8 (lt & 15) ..
+            u32x4 q[OUT ? 8 : 1];
+            u32x4 g[PERKEY ? 8 : 1];
+            u32x4 T[4];                   // 64 x 64 tile: row (lt >> 3) + 16i, granule lt & 7
+            u32x4 P[OUT ? 4 : 1];
+            u32x4 v[2];                   // v row (lt >> 2) + 32i, columns vc0 + 8 (lt & 3) ..
+            uint16_t bv[2];               // beta of those rows
+            uint16_t bt;                  // beta of row lt
+            float w0, w1, w2;             // gate words of row lt (per key: G_last of key lt)
+        };
+        uint32_t okq[8], ov[2], obv[2];
+        for (int i = 0; i < 8; ++i)
+            okq[i] = ((lt >> 4) + 8 * i) * (PERKEY ? DK * 2 : tokstride * 2) + 16 * (lt & 15);
+        for (int i = 0; i < 2; ++i) {
+            ov[i] = ((lt >> 2) + 32 * i) * tokstride * 2 + 16 * (lt & 3);
+            obv[i] = ((lt >> 2) + 32 * i) * H * 2;
+        }
+        const uint32_t obt = lt * H * 2;
+        auto load = [&](int c_, Raw& x) {
+            const int c = __builtin_amdgcn_readfirstlane(c_);
+            const int len = chunk_len(c);
+            const int64_t t0 = ui.start + (int64_t)c * BT;
+            const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
+            const uint32_t tile_bytes = (uint32_t)len * tokstride * 2;
+            if (PERKEY) {
+                const rsrc_t rk = make_rsrc(reinterpret_cast<const f16*>(a.ws.kd) + ch * (BT * DK), BT * DK * 2);
+                const rsrc_t rq = make_rsrc(reinterpret_cast<const f16*>(a.ws.qg) + ch * (BT * DK), BT * DK * 2);
+                const rsrc_t rg = make_rsrc(reinterpret_cast<const f16*>(a.ws.kg) + ch * (BT * DK), BT * DK * 2);
+                for (int i = 0; i < 8; ++i) {
+                    x.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, okq[i], 0, 0);
+                    if (OUT) x.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, okq[i], 0, 0);
+                    x.g[i] = __builtin_amdgcn_raw_buffer_load_b128(rg, okq[i], 0, 0);
+                }
+                x.w0 = a.ws.gamL[ch * DK + lt];
+            } else {
+                const rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(a.k) + (t0 * H + head) * DK, tile_bytes);
+                const rsrc_t rq = make_rsrc(reinterpret_cast<const bf16*>(a.q) + (t0 * H + head) * DK, tile_bytes);
+                for (int i = 0; i < 8; ++i) {
+                    x.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, okq[i], 0, 0);
+                    if (OUT) x.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, okq[i], 0, 0);
+                }
+                const float* gw = a.ws.gam + ch * (4 * BT) + (lt & (BT - 1));
+                x.w0 = gw[BT];
+                x.w1 = gw[2 * BT];
+                x.w2 = gw[3 * BT];
+            }
+            const rsrc_t rT = make_rsrc(reinterpret_cast<const f16*>(a.ws.Tm) + ch * (BT * BT), BT * BT * 2);
+            const rsrc_t rP = make_rsrc(reinterpret_cast<const f16*>(a.ws.P) + ch * (BT * BT), BT * BT * 2);
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t off = ((lt >> 3) + 16 * i) * (BT * 2) + 16 * (lt & 7);
+                x.T[i] = __builtin_amdgcn_raw_buffer_load_b128(rT, off, 0, 0);
+                if (OUT) x.P[i] = __builtin_amdgcn_raw_buffer_load_b128(rP, off, 0, 0);
+            }
+            const rsrc_t rb = make_rsrc(reinterpret_cast<const bf16*>(a.beta) + t0 * H + head, (uint32_t)len * H * 2);
+            x.bt = __builtin_amdgcn_raw_buffer_load_b16(rb, obt, 0, 0);
+            if (!mcols) {
+                const rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(a.v) + (t0 * H + head) * DV + vc0, tile_bytes);
+                for (int i = 0; i < 2; ++i) {
+                    x.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, ov[i], 0, 0);
+                    x.bv[i] = __builtin_amdgcn_raw_buffer_load_b16(rb, obv[i], 0, 0);
+                }
+            }
+        };
+        auto bf = [](uint32_t w, bool hi) { return __builtin_bit_cast(float, hi ? (w & 0xffff0000u) : (w << 16)); };
+        auto publish = [&](int buf, const Raw& x) {
+            const int jv = lt & 15;
+            const int p0 = op_pos(8 * jv);            // elements 8jv..8jv+3 -> granule p0/8, half (p0/4)&1
+            const int g0 = p0 >> 3, hf = ((p0 >> 2) & 1) * 8;
+            for (int i = 0; i < 8; ++i) {
+                const int r = (lt >> 4) + 8 * i;
+                const int sw = swz16(r);
+                const int a0 = r * 256 + ((g0 ^ sw) << 4) + hf, a1 = r * 256 + (((g0 + 1) ^ sw) << 4) + hf;
+                const u32x4 kv = PERKEY ? x.k[i] : __builtin_bit_cast(u32x4, PolicyH::in2op(__builtin_bit_cast(f32x4, x.k[i])));
+                *reinterpret_cast<uint2*>(reinterpret_cast<char*>(kt[buf]) + a0) = uint2{kv[0], kv[1]};
+                *reinterpret_cast<uint2*>(reinterpret_cast<char*>(kt[buf]) + a1) = uint2{kv[2], kv[3]};
+                if (OUT) {
+                    const u32x4 qv = PERKEY ? x.q[i] : __builtin_bit_cast(u32x4, PolicyH::in2op(__builtin_bit_cast(f32x4, x.q[i])));
+                    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(qt[buf]) + a0) = uint2{qv[0], qv[1]};
+                    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(qt[buf]) + a1) = uint2{qv[2], qv[3]};
+                }
+                if (PERKEY) {
+                    const u32x4 gv = x.g[i];
+                    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(gt[PERKEY ? buf : 0]) + a0) = uint2{gv[0], gv[1]};
+                    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(gt[PERKEY ? buf : 0]) + a1) = uint2{gv[2], gv[3]};
+                }
+            }
+            for (int i = 0; i < 4; ++i) {
+                const int r = (lt >> 3) + 16 * i;
+                const int ad = r * 128 + (((lt & 7) ^ swz8(r)) << 4);
+                *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(Tt[buf]) + ad) = x.T[i];
+                if (OUT) *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(Pt[OUT ? buf : 0]) + ad) = x.P[i];
+            }
+            if (!mcols)
+                for (int i = 0; i < 2; ++i) {
+                    const int r = (lt >> 2) + 32 * i;
+                    const float bm = __builtin_bit_cast(float, (uint32_t)x.bv[i] << 16);
+                    float* dst = &vbT[buf][(8 * (lt & 3)) * LVT + r];
+                    for (int e = 0; e < 4; ++e) {
+                        dst[(2 * e) * LVT] = bm * bf(x.v[i][e], false);
+                        dst[(2 * e + 1) * LVT] = bm * bf(x.v[i][e], true);
+                    }
+                }
+            if (PERKEY) gl[buf][lt] = fpow(x.w0, a.use_exp2);
+            if (lt < BT) {
+                const float bm = __builtin_bit_cast(float, (uint32_t)x.bt << 16);
+                if (PERKEY) {
+                    cf[buf][0][lt] = bm;
+                    cf[buf][2][lt] = a.scale;
+                } else {
+                    cf[buf][0][lt] = bm * x.w0;
+                    cf[buf][1][lt] = x.w1;
+                    cf[buf][2][lt] = a.scale * x.w0;
+                    cf[buf][3][lt] = x.w2;
+                }
+            }
+        };
+        // Chunk c's loads go out NSET steps before it is published. Every step
+        // issues one load group (the last ones repeat the final chunk), so the
+        // number of loads in flight is the same on every path through the loop.
+        Raw R0, R1;
+        if (nch > 0) {
+            load(0, R0);
+            if (NSET == 2) load(min(1, nch - 1), R1);
+            publish(0, R0);
+            load(min(NSET, nch - 1), R0);
+        }
+        __syncthreads();
+        auto step = [&](int c, Raw& R) {               // R holds chunk c+1; refilled with c+1+NSET
+            if (c + 1 < nch) publish((c + 1) & 1, R);
+            load(min(c + 1 + NSET, nch - 1), R);
+            __syncthreads();
+        };
+        // both steps of a pair run unconditionally, so that the last loads
+        // before the back edge are always the same set's
+        int c = 0;
+        for (; c + 1 < nch; c += 2) {
+            step(c, NSET == 2 ? R1 : R0);
+            step(c + 1, R0);
+        }
+        if (c < nch) step(c, NSET == 2 ? R1 : R0);
+    }
+}
+
 // ------------------------------------------------------------------ merge
 constexpr int MC = 8;   // state columns per merge workgroup
 
@@ -950,6 +1402,22 @@ static void launch_state_t(bool summary, StateArgs a, int want_ext, int want_M, 
     else hipLaunchKernelGGL((state_kernel<P, PK, false>), grid, block, 0, s, a);
 }
 
+template <bool PK>
+static void launch_state_h(bool summary, StateArgs a, int want_ext, int want_M, hipStream_t s) {
+    if (summary) {
+        a.tile0 = want_ext ? 0 : DV / BV;
+        a.ntiles = (want_ext ? DV / BV : 0) + (want_M ? DK / BV : 0);
+    } else {
+        a.tile0 = 0;
+        a.ntiles = DV / BV;
+    }
+    if (a.n_pairs == 0 || a.ntiles == 0) return;
+    const int groups = (a.n_pairs + 7) / 8;
+    dim3 grid(8 * a.ntiles * groups), block(HT);
+    if (summary) hipLaunchKernelGGL((state_kernel_h<PK, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((state_kernel_h<PK, false>), grid, block, 0, s, a);
+}
+
 hipError_t launch_state(const Problem& p, const Workspace& ws, const void* q, const void* k,
                         const void* v, const void* beta, const float* h0, void* o, float* hfinal,
                         float* hslot, int summary, int want_ext, int want_M, float* S_ext,
@@ -962,8 +1430,8 @@ hipError_t launch_state(const Problem& p, const Workspace& ws, const void* q, co
     a.S_ext = S_ext; a.M = M;
     a.ntiles = 0; a.tile0 = 0;
     if (p.dtype == 1) {
-        if (p.per_key) launch_state_t<PolicyH, true>(summary, a, want_ext, want_M, s);
-        else launch_state_t<PolicyH, false>(summary, a, want_ext, want_M, s);
+        if (p.per_key) launch_state_h<true>(summary, a, want_ext, want_M, s);
+        else launch_state_h<false>(summary, a, want_ext, want_M, s);
     } else {
         if (p.per_key) launch_state_t<PolicyF, true>(summary, a, want_ext, want_M, s);
         else launch_state_t<PolicyF, false>(summary, a, want_ext, want_M, s);
