@@ -48,6 +48,7 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
@@ -63,6 +64,20 @@ __device__ __forceinline__ float fpow(float x, int use_exp2) {
 
 // orders this wave's LDS writes before its following LDS reads
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier for LDS hand-offs only: this wave's LDS accesses complete
+// before it, but outstanding global loads and stores stay in flight (the
+// fence of __syncthreads would wait for all of them). Data copied into LDS by
+// global-to-LDS loads is made ready by an explicit vector-memory wait first.
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8); issued through the builtin so that the compiler's own
+// wait insertion knows what has completed
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int waitcnt_lgkm0() { return 15 | (3 << 14) | (7 << 4); }
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
+    __builtin_amdgcn_s_barrier();
+}
 
 // ------------------------------------------------------------------ policies
 // A fragment holds, for lane (G = lane / 16, n = lane % 16), the 8 elements
@@ -232,11 +247,29 @@ __device__ __forceinline__ void chunk_of(const UnitMap& um, int ci, int& u, int&
 // of the terms inside one 32-deep contraction does not change the product.
 __device__ __forceinline__ int op_pos(int x) { return (x & ~31) | ((x & 12) << 1) | ((x & 16) >> 2) | (x & 3); }
 
-// 16-byte granule swizzles of LDS tiles that avoid bank conflicts for the
-// row-fragment reads and the transposed reads of the fp16 state pass:
-// rows of 128 operands (16 granules) and rows of 64 operands (8 granules)
-__device__ __forceinline__ int swz16(int r) { return ((r & 3) << 2) ^ ((r >> 2) & 3); }
+// 16-byte granule swizzles of the LDS tiles of the fp16 state pass. The LDS
+// has 32 four-byte banks: a 16-byte read is served 8 lanes at a time and an
+// 8-byte read 16 lanes at a time, so the granule index modulo 8 picks the
+// banks. Rows of 128 operands (16 granules): the low three bits of the
+// swizzle are a bijection on any 8 consecutive rows (row-fragment reads are
+// conflict free) and bit 2 alternates with the row, which spreads the
+// 4-row x 4-piece transposed reads over every bank pair (two-way, the least
+// possible for 8-byte pieces that all sit in the same granule half). Rows of
+// 64 operands (8 granules): row-fragment reads only.
+__device__ __forceinline__ int swz16(int r) {
+    return ((r & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 1) & 1) | (r & 8);
+}
 __device__ __forceinline__ int swz8(int r) { return r & 7; }
+
+// Per-chunk coefficient block of the fp16 state pass (CFB bytes, written by
+// the preparation): four 64-entry fp16 rows in lane order (entry 16G + 4it + r
+// belongs to token row 16it + 4G + r) - beta b^G, b^{G_L-G}, b^G, beta (per-key
+// gate: beta, 1, 1, beta) - then fp32 b^{G_L} (scalar gate) or b^{G_L} of
+// every key (per-key gate).
+constexpr int CFB = 1024;
+constexpr int CF_CY = 0, CF_CP = 64, CF_BG = 128, CF_BETA = 192;   // fp16 offsets
+constexpr int CF_EL = 128, CF_GL = 128;                              // fp32 offsets
+__device__ __forceinline__ int lane_order(int t) { return 16 * ((t >> 2) & 3) + 4 * (t >> 4) + (t & 3); }
 
 // raw buffer resource over [base, base + bytes): accesses outside read as zero
 // and writes outside are dropped
@@ -289,6 +322,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     const In* qin = reinterpret_cast<const In*>(a.q);
     const In* bin = reinterpret_cast<const In*>(a.beta);
     const bool has_q = qin != nullptr;   // P (and per key q * b^G) are prepared when q is given
+    // fp16 operands are stored in the state pass's operand order (op_pos)
+    constexpr bool PERM = sizeof(Op) == 2;
 
     // ---- tiles into LDS as operands (rows past the chunk end are zero)
     constexpr int VPR = 16 / sizeof(In);             // elements per 16-byte vector
@@ -305,6 +340,24 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         *reinterpret_cast<f32x4*>(&qt[r * LDQ + cv]) = qv;
     }
     if (tid < BT) bet[tid] = tid < len ? P::f(bin[(t0 + tid) * H + head]) : 0.0f;
+    if (PERM && !PERKEY) {
+        // k and q as fp16 operand tiles for the state pass. Operand granule g =
+        // 4s + j of a row holds elements 32s + 4j .. +3 and 32s + 16 + 4j .. +3.
+        __syncthreads();
+        Op* k16 = reinterpret_cast<Op*>(a.ws.kq16) + ch * (2 * BT * DK);
+        for (int idx = tid; idx < BT * DK / 8; idx += 256) {
+            const int r = idx >> 4, g = idx & 15;
+            const int e0 = 32 * (g >> 2) + 4 * (g & 3);
+            uint2 lo = *reinterpret_cast<const uint2*>(&kt[r * LDQ + e0]);
+            uint2 hi = *reinterpret_cast<const uint2*>(&kt[r * LDQ + e0 + 16]);
+            *reinterpret_cast<u32x4*>(k16 + r * DK + 8 * g) = u32x4{lo.x, lo.y, hi.x, hi.y};
+            if (has_q) {
+                lo = *reinterpret_cast<const uint2*>(&qt[r * LDQ + e0]);
+                hi = *reinterpret_cast<const uint2*>(&qt[r * LDQ + e0 + 16]);
+                *reinterpret_cast<u32x4*>(k16 + BT * DK + r * DK + 8 * g) = u32x4{lo.x, lo.y, hi.x, hi.y};
+            }
+        }
+    }
     if (!PERKEY) {
         // inclusive scan of the scalar gate over the chunk, one wave; stores
         // G, b^G, b^{G_last - G} and b^{G_last} for the state pass
@@ -317,11 +370,23 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
             const float xl = __shfl(x, len > 0 ? len - 1 : 0, 64);
             Gs[lane] = x;
             float* gw = a.ws.gam + ch * (4 * BT);
+            const float bG = fpow(x, a.use_exp2), bLG = fpow(xl - x, a.use_exp2), bL = fpow(xl, a.use_exp2);
             gw[lane] = x;
-            gw[BT + lane] = fpow(x, a.use_exp2);
-            gw[2 * BT + lane] = fpow(xl - x, a.use_exp2);
-            gw[3 * BT + lane] = fpow(xl, a.use_exp2);
+            gw[BT + lane] = bG;
+            gw[2 * BT + lane] = bLG;
+            gw[3 * BT + lane] = bL;
             if (a.g_cumsum && lane < len) a.g_cumsum[(t0 + lane) * H + head] = x;
+            if (PERM) {
+                // coefficient block of the fp16 state pass
+                const float bt = lane < len ? P::f(bin[(t0 + lane) * H + head]) : 0.0f;
+                f16* cf = reinterpret_cast<f16*>(a.ws.cfh) + ch * (CFB / 2);
+                const int lo = lane_order(lane);
+                cf[CF_CY + lo] = (f16)(bt * bG);
+                cf[CF_CP + lo] = (f16)bLG;
+                cf[CF_BG + lo] = (f16)bG;
+                cf[CF_BETA + lo] = (f16)bt;
+                if (lane == 0) reinterpret_cast<float*>(cf)[CF_EL] = bL;
+            }
         }
     } else {
         // per-key gate: running sum down each key column
@@ -333,6 +398,16 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
                 if (a.g_cumsum && r < len) a.g_cumsum[((t0 + r) * H + head) * DK + tid] = acc;
             }
             a.ws.gamL[ch * DK + tid] = acc;
+            if (PERM) reinterpret_cast<float*>(a.ws.cfh)[ch * (CFB / 4) + CF_GL + tid] = fpow(acc, a.use_exp2);
+        }
+        if (PERM && tid < BT) {
+            const float bt = tid < len ? P::f(bin[(t0 + tid) * H + head]) : 0.0f;
+            f16* cf = reinterpret_cast<f16*>(a.ws.cfh) + ch * (CFB / 2);
+            const int lo = lane_order(tid);
+            cf[CF_CY + lo] = (f16)bt;
+            cf[CF_CP + lo] = (f16)1.0f;
+            cf[CF_BG + lo] = (f16)1.0f;
+            cf[CF_BETA + lo] = (f16)bt;
         }
     }
     __syncthreads();
@@ -418,8 +493,6 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     }
 
     // ---- T out as operands (row-major 64 x 64), optional token-major fp32 A slot
-    // fp16 operands are stored in the state pass's operand order (op_pos)
-    constexpr bool PERM = sizeof(Op) == 2;
     Op* Tw = reinterpret_cast<Op*>(a.ws.Tm) + ch * (BT * BT);
     for (int e = tid; e < BT * BT / 4; e += 256) {
         const int r = e / (BT / 4), c4 = (e % (BT / 4)) * 4;
@@ -483,9 +556,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
                 xd[e] = kv * fpow(gg, a.use_exp2);
                 xg[e] = kv * fpow(Gs[last * (DK + 4) + c4 + e] - gg, a.use_exp2);
             }
-            if (has_q) P::st4(qg + r * DK + c4, xq);
-            P::st4(kd + r * DK + c4, xd);
-            P::st4(kg + r * DK + c4, xg);
+            const int cp = PERM ? op_pos(c4) : c4;
+            if (has_q) P::st4(qg + r * DK + cp, xq);
+            P::st4(kd + r * DK + cp, xd);
+            P::st4(kg + r * DK + cp, xg);
         }
     }
 }
@@ -899,21 +973,21 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
 // its use. One barrier per chunk hands the buffers over.
 constexpr int HW = 4;              // waves per workgroup
 constexpr int HT = 64 * HW;        // threads
-constexpr int LVT = BT + 4;        // row stride (floats) of the transposed beta*v tile
 
-template <bool PERKEY, bool SUMMARY>
+template <bool PERKEY, bool SUMMARY, bool OBF>
 __global__ __launch_bounds__(HT) void state_kernel_h(StateArgs a) {
     using F = PolicyH::F;
     constexpr bool OUT = !SUMMARY;
-    constexpr int NSET = PERKEY && OUT ? 1 : 2;        // register sets of chunk loads in flight
-    __shared__ __attribute__((aligned(16))) f16 kt[2][BT * DK];                          // k (per key: k*b^G)
-    __shared__ __attribute__((aligned(16))) f16 qt[OUT ? 2 : 1][OUT ? BT * DK : 8];      // q (per key: q*b^G)
-    __shared__ __attribute__((aligned(16))) f16 gt[PERKEY ? 2 : 1][PERKEY ? BT * DK : 8];// per key: k*b^{G_L-G}
-    __shared__ __attribute__((aligned(16))) f16 Tt[2][BT * BT];
-    __shared__ __attribute__((aligned(16))) f16 Pt[OUT ? 2 : 1][OUT ? BT * BT : 8];
-    __shared__ __attribute__((aligned(16))) float vbT[2][BV * LVT];                      // beta*v, [column][row]
-    __shared__ __attribute__((aligned(16))) float cf[2][4][BT];   // beta b^G, b^{G_L-G}, scale b^G, b^{G_L}
-    __shared__ __attribute__((aligned(16))) float gl[2][PERKEY ? DK : 4];                // per key: b^{G_L}
+    // Tile buffers: three where LDS allows (copies run two chunks ahead), two
+    // for the per-key forward (one chunk ahead).
+    constexpr int NB = PERKEY && OUT ? 2 : 3;
+    __shared__ __attribute__((aligned(16))) f16 kt[NB][BT * DK];                          // k (per key: k*b^G)
+    __shared__ __attribute__((aligned(16))) f16 qt[OUT ? NB : 1][OUT ? BT * DK : 8];      // q (per key: q*b^G)
+    __shared__ __attribute__((aligned(16))) f16 gt[PERKEY ? NB : 1][PERKEY ? BT * DK : 8];// per key: k*b^{G_L-G}
+    __shared__ __attribute__((aligned(16))) f16 Tt[NB][BT * BT];
+    __shared__ __attribute__((aligned(16))) f16 Pt[OUT ? NB : 1][OUT ? BT * BT : 8];
+    __shared__ __attribute__((aligned(16))) bf16 vt[NB][BT * BV];                         // v rows, 32 columns
+    __shared__ __attribute__((aligned(16))) uint32_t cb[NB][CFB / 4];                    // per-row coefficient block
 
     const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -962,9 +1036,8 @@ __global__ __launch_bounds__(HT) void state_kernel_h(StateArgs a) {
         }
         int offT[2];
         for (int kk = 0; kk < 2; ++kk) offT[kk] = n * 128 + (((4 * kk + G) ^ swz8(n)) << 4);
-        const int offV = (16 * wv + n) * LVT + 4 * G;
-        uint32_t ooff[4];
-        for (int r = 0; r < 4; ++r) ooff[r] = (uint32_t)(4 * G + r) * tokstride + col;
+        // v fragment (rows 16 it + 4G + e, column 16 wv + n) by a transposed read
+        const int offV = (4 * G + (n >> 2)) * (BV * 2) + 32 * wv + 8 * (n & 3);
         auto ldA = [](const f16* t, int byte_off) {
             F f;
             f.v = *reinterpret_cast<const f16x8*>(reinterpret_cast<const char*>(t) + byte_off);
@@ -980,16 +1053,18 @@ __global__ __launch_bounds__(HT) void state_kernel_h(StateArgs a) {
             for (int e = 0; e < 4; ++e) { f.v[e] = fx[e]; f.v[e + 4] = fy[e]; }
             return f;
         };
-        __syncthreads();                              // chunk 0 published
+        lds_barrier();                              // chunk 0 published
 
-        // per-lane element offsets of the state slot rows (keys 4G + r)
+        // per-lane element offsets of output rows 4G + r and of state slot rows (keys 4G + r)
+        uint32_t ooff[4];
+        for (int r = 0; r < 4; ++r) ooff[r] = (uint32_t)(4 * G + r) * tokstride + col;
         uint32_t hoff[4];
         for (int r = 0; r < 4; ++r) hoff[r] = (uint32_t)(4 * G + r) * DV + col;
         for (int c = 0; c < nch; ++c) {
             // an opaque copy of the chunk index keeps the compiler from turning
             // every per-lane address into a loop-carried 64-bit pointer
             const int cu = __builtin_amdgcn_readfirstlane(c);
-            const int b = cu & 1;
+            const int tb = NB == 2 ? cu & 1 : cu % NB;   // tile buffers
             const int len = chunk_len(cu);
             const int64_t t0 = ui.start + (int64_t)cu * BT;
             const int64_t ch = (int64_t)(ui.cbase + cu) * H + head;
@@ -998,143 +1073,173 @@ __global__ __launch_bounds__(HT) void state_kernel_h(StateArgs a) {
                 for (int kt8 = 0; kt8 < 8; ++kt8)
                     for (int r = 0; r < 4; ++r) hs[16 * kt8 * DV + hoff[r]] = h[kt8][r];
             }
-            const f16* K = kt[b];
-            const f16* Q = qt[OUT ? b : 0];
-            const f16* Tc = Tt[b];
-            const f16* Pc = Pt[OUT ? b : 0];
-            const f16* KG = PERKEY ? gt[PERKEY ? b : 0] : K;
-            // LDS reads are issued in the order they are consumed, a stage ahead
-            // of the MFMAs that use them; the scheduling fences keep the compiler
-            // from sinking them next to their uses, which would expose the LDS
-            // latency once per MFMA.
-            F fk[2][4], fq[2][4];
-            auto ldKQ = [&](int s2, F* k4, F* q4) {
-                for (int it = 0; it < 4; ++it) {
-                    k4[it] = ldA(K, offA[s2] + it * 16 * 256);
-                    if (OUT) q4[it] = ldA(Q, offA[s2] + it * 16 * 256);
+            const f16* K = kt[tb];
+            const f16* Q = qt[OUT ? tb : 0];
+            const f16* Tc = Tt[tb];
+            const f16* Pc = Pt[OUT ? tb : 0];
+            const f16* KG = PERKEY ? gt[PERKEY ? tb : 0] : K;
+            // The step runs as a pipeline over the four 16-row tiles: while the
+            // MFMAs of one row tile run, the VALU work of the previous one (Y,
+            // v_new scaling, the state decay) and the LDS reads of the next one
+            // are in flight. Scheduling fences keep the LDS reads of a stage
+            // ahead of the MFMAs that consume them.
+            F fa[2][4], fb[2][4];                      // k and q fragments of two row tiles
+            auto ldRow = [&](int it, F* k4, F* q4) {
+                for (int s2 = 0; s2 < 4; ++s2) {
+                    k4[s2] = ldA(K, offA[s2] + it * 16 * 256);
+                    if (OUT) q4[s2] = ldA(Q, offA[s2] + it * 16 * 256);
                 }
             };
-            auto mmaKQ = [&](int s2, const F* k4, const F* q4, f32x4* kh, f32x4* qh) {
-                for (int it = 0; it < 4; ++it) {
-                    PolicyH::mma(kh[it], k4[it], hb[s2]);
-                    if (OUT) PolicyH::mma(qh[it], q4[it], hb[s2]);
-                }
-            };
-            // ---- K h and q h, all 64 rows
             f32x4 kh[4], qh[4];
-            for (int it = 0; it < 4; ++it) kh[it] = qh[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-            ldKQ(0, fk[0], fq[0]);
-            ldKQ(1, fk[1], fq[1]);
-            __builtin_amdgcn_sched_barrier(0);
-            mmaKQ(0, fk[0], fq[0], kh, qh);
-            __builtin_amdgcn_sched_barrier(0);
-            ldKQ(2, fk[0], fq[0]);
-            __builtin_amdgcn_sched_barrier(0);
-            mmaKQ(1, fk[1], fq[1], kh, qh);
-            __builtin_amdgcn_sched_barrier(0);
-            ldKQ(3, fk[1], fq[1]);
-            // T fragments and the Y coefficients for the next phase
-            F ft[4][2];
-            for (int it = 0; it < 4; ++it) {
-                ft[it][0] = ldA(Tc, offT[0] + it * 16 * 128);
-                if (it >= 2) ft[it][1] = ldA(Tc, offT[1] + it * 16 * 128);
+            auto mmaRow = [&](int it, const F* k4, const F* q4) {
+                kh[it] = qh[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int s2 = 0; s2 < 4; ++s2) {
+                    PolicyH::mma(kh[it], k4[s2], hb[s2]);
+                    if (OUT) PolicyH::mma(qh[it], q4[s2], hb[s2]);
+                }
+            };
+            // the per-row data of the chunk, read first so that no later wait drains it
+            const f16* cbh = reinterpret_cast<const f16*>(cb[tb]);
+            f16x8 cyv[2], cpv[2], bgv[2], btv[2];
+            for (int h2 = 0; h2 < 2; ++h2) {
+                cyv[h2] = *reinterpret_cast<const f16x8*>(&cbh[CF_CY + 16 * G + 8 * h2]);
+                if (!PERKEY) cpv[h2] = *reinterpret_cast<const f16x8*>(&cbh[CF_CP + 16 * G + 8 * h2]);
+                if (OUT && !PERKEY) bgv[h2] = *reinterpret_cast<const f16x8*>(&cbh[CF_BG + 16 * G + 8 * h2]);
+                btv[h2] = *reinterpret_cast<const f16x8*>(&cbh[CF_BETA + 16 * G + 8 * h2]);
             }
-            f32x4 cy[4], vv[4];
-            for (int it = 0; it < 4; ++it) {
-                cy[it] = *reinterpret_cast<const f32x4*>(&cf[b][0][16 * it + 4 * G]);
-                vv[it] = mcols ? f32x4{0.f, 0.f, 0.f, 0.f} : *reinterpret_cast<const f32x4*>(&vbT[b][offV + 16 * it]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            mmaKQ(2, fk[0], fq[0], kh, qh);
-            __builtin_amdgcn_sched_barrier(0);
-            mmaKQ(3, fk[1], fq[1], kh, qh);
-            __builtin_amdgcn_sched_barrier(0);
-            // first k^T fragments of the state update, P fragments, coefficients
-            F fg0[8], fg1[8];                         // token slices 0 and 1 of key tile kt8
-            for (int kt8 = 0; kt8 < 2; ++kt8) {
-                fg0[kt8] = ldKT(KG, kt8, 0);
-                fg1[kt8] = ldKT(KG, kt8, 1);
-            }
-            // ---- Y = beta v - beta b^G (K h)
-            f32x4 y[4];
+            s16x4 vraw[4];
             for (int it = 0; it < 4; ++it)
-                for (int r = 0; r < 4; ++r) y[it][r] = vv[it][r] - cy[it][r] * kh[it][r];
-            const F yb0 = pack(y[0], y[1]), yb1 = pack(y[2], y[3]);
-            // ---- v_new = T Y (T lower triangular)
-            f32x4 vn[4];
-            for (int it = 0; it < 4; ++it) {
-                vn[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-                PolicyH::mma(vn[it], ft[it][0], yb0);
-                if (it >= 2) PolicyH::mma(vn[it], ft[it][1], yb1);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            F fp[4][2];
-            f32x4 cp[4], co[4];
-            for (int it = 0; it < 4; ++it) {
-                if (OUT) {
-                    fp[it][0] = ldA(Pc, offT[0] + it * 16 * 128);
-                    if (it >= 2) fp[it][1] = ldA(Pc, offT[1] + it * 16 * 128);
-                    co[it] = *reinterpret_cast<const f32x4*>(&cf[b][2][16 * it + 4 * G]);
-                }
-                if (!PERKEY) cp[it] = *reinterpret_cast<const f32x4*>(&cf[b][1][16 * it + 4 * G]);
-            }
-            for (int kt8 = 2; kt8 < 4; ++kt8) {
-                fg0[kt8] = ldKT(KG, kt8, 0);
-                fg1[kt8] = ldKT(KG, kt8, 1);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            f32x4 vp[4];
-            for (int it = 0; it < 4; ++it) {
-                if (PERKEY) vp[it] = vn[it];
-                else
-                    for (int r = 0; r < 4; ++r) vp[it][r] = vn[it][r] * cp[it][r];
-            }
-            const F vb0 = pack(vp[0], vp[1]), vb1 = pack(vp[2], vp[3]);
-            // ---- output: scale b^G (q h) + P (scale v_new)
-            if (OUT) {
-                f32x4 vs[4];
-                for (int it = 0; it < 4; ++it)
-                    for (int r = 0; r < 4; ++r) vs[it][r] = a.scale * vn[it][r];
-                const F nb0 = pack(vs[0], vs[1]), nb1 = pack(vs[2], vs[3]);
-                for (int it = 0; it < 4; ++it) {
-                    f32x4 o;
-                    for (int r = 0; r < 4; ++r) o[r] = co[it][r] * qh[it][r];
-                    PolicyH::mma(o, fp[it][0], nb0);
-                    if (it >= 2) PolicyH::mma(o, fp[it][1], nb1);
-                    // rows past the chunk end fall outside the buffer range: dropped
-                    const int64_t rb = ((t0 + 16 * it) * H + head) * DV;
-                    const uint32_t nrow = (uint32_t)max(len - 16 * it, 0);
-                    if (a.o_bf16) {
-                        const rsrc_t ro = make_rsrc(reinterpret_cast<bf16*>(a.o) + rb, nrow * tokstride * 2);
-                        for (int r = 0; r < 4; ++r)
-                            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (bf16)o[r]), ro, ooff[r] * 2, 0, 0);
-                    } else {
-                        const rsrc_t ro = make_rsrc(reinterpret_cast<float*>(a.o) + rb, nrow * tokstride * 4);
-                        for (int r = 0; r < 4; ++r)
-                            __builtin_amdgcn_raw_buffer_store_b32(f2u(o[r]), ro, ooff[r] * 4, 0, 0);
-                    }
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // ---- state: h = Diag(b^{G_last}) h + kg^T v_new', k^T fragments two tiles ahead
-            const float eL = PERKEY ? 1.0f : cf[b][3][0];
-            for (int kt8 = 0; kt8 < 8; ++kt8) {
-                if (kt8 + 4 < 8) {
-                    fg0[kt8 + 4] = ldKT(KG, kt8 + 4, 0);
-                    fg1[kt8 + 4] = ldKT(KG, kt8 + 4, 1);
-                }
+                vraw[it] = mcols ? s16x4{0, 0, 0, 0}
+                                 : __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                       LDS_PTR(s16x4, reinterpret_cast<const char*>(vt[tb]) + offV + it * 16 * BV * 2));
+            auto coef = [](const f16x8* v, int it, int r) { return (float)v[it >> 1][4 * (it & 1) + r]; };
+            const float* cbf = reinterpret_cast<const float*>(cb[tb]);
+            const float eL = PERKEY ? 1.0f : cbf[CF_EL];
+            auto decay = [&](int kt8) {
                 if (PERKEY) {
-                    const f32x4 gv = *reinterpret_cast<const f32x4*>(&gl[b][16 * kt8 + 4 * G]);
+                    const f32x4 gv = *reinterpret_cast<const f32x4*>(&cbf[CF_GL + 16 * kt8 + 4 * G]);
                     for (int r = 0; r < 4; ++r) h[kt8][r] *= gv[r];
                 } else {
                     for (int r = 0; r < 4; ++r) h[kt8][r] *= eL;
                 }
-                PolicyH::mma(h[kt8], fg0[kt8], vb0);
-                PolicyH::mma(h[kt8], fg1[kt8], vb1);
-                __builtin_amdgcn_sched_barrier(0);
+            };
+            f32x4 y[4];
+            auto mkY = [&](int it) {                   // Y = beta v - beta b^G (K h)
+                for (int r = 0; r < 4; ++r) {
+                    const float vv = __builtin_bit_cast(float, (uint32_t)(uint16_t)vraw[it][r] << 16);
+                    y[it][r] = __builtin_fmaf(coef(btv, it, r), vv, -coef(cyv, it, r) * kh[it][r]);
+                }
+            };
+            f32x4 vn[4], vp[4];
+            auto scaleVn = [&](int it) {               // v_new' = b^{G_L - G} v_new
+                if (PERKEY) {
+                    vp[it] = vn[it];
+                } else {
+                    for (int r = 0; r < 4; ++r) vp[it][r] = vn[it][r] * coef(cpv, it, r);
+                }
+            };
+            F ft[4][2], fp[4][2], fg0[8], fg1[8];
+            // output rows of tile it: scale (b^G (q h) + P v_new); rows past the
+            // chunk end fall outside the buffer range and are dropped
+            auto output = [&](int it, const F& nb0, const F& nb1) {
+                f32x4 o;
+                for (int r = 0; r < 4; ++r) o[r] = PERKEY ? qh[it][r] : coef(bgv, it, r) * qh[it][r];
+                PolicyH::mma(o, fp[it][0], nb0);
+                if (it >= 2) PolicyH::mma(o, fp[it][1], nb1);
+                const int64_t rb = ((t0 + 16 * it) * H + head) * DV;
+                const uint32_t nrow = (uint32_t)max(len - 16 * it, 0);
+                if (OBF) {
+                    const rsrc_t ro = make_rsrc(reinterpret_cast<bf16*>(a.o) + rb, nrow * tokstride * 2);
+                    for (int r = 0; r < 4; ++r)
+                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (bf16)(a.scale * o[r])), ro, ooff[r] * 2, 0, 0);
+                } else {
+                    const rsrc_t ro = make_rsrc(reinterpret_cast<float*>(a.o) + rb, nrow * tokstride * 4);
+                    for (int r = 0; r < 4; ++r) __builtin_amdgcn_raw_buffer_store_b32(f2u(a.scale * o[r]), ro, ooff[r] * 4, 0, 0);
+                }
+            };
+
+            // ---- stage 0: fragments of row tiles 0 and 1
+            ldRow(0, fa[0], fb[0]);
+            ldRow(1, fa[1], fb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- row tile 0
+            mmaRow(0, fa[0], fb[0]);
+            decay(0);
+            decay(1);
+            __builtin_amdgcn_sched_barrier(0);
+            ldRow(2, fa[0], fb[0]);
+            for (int it = 0; it < 2; ++it) ft[it][0] = ldA(Tc, offT[0] + it * 16 * 128);
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- row tile 1
+            mmaRow(1, fa[1], fb[1]);
+            mkY(0);
+            decay(2);
+            decay(3);
+            __builtin_amdgcn_sched_barrier(0);
+            ldRow(3, fa[1], fb[1]);
+            for (int it = 2; it < 4; ++it) {
+                ft[it][0] = ldA(Tc, offT[0] + it * 16 * 128);
+                ft[it][1] = ldA(Tc, offT[1] + it * 16 * 128);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- row tile 2; v_new of rows 0..31
+            mmaRow(2, fa[0], fb[0]);
+            mkY(1);
+            const F yb0 = pack(y[0], y[1]);
+            for (int it = 0; it < 2; ++it) {
+                vn[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+                PolicyH::mma(vn[it], ft[it][0], yb0);
+            }
+            decay(4);
+            decay(5);
+            __builtin_amdgcn_sched_barrier(0);
+            for (int kt8 = 0; kt8 < 8; ++kt8) fg0[kt8] = ldKT(KG, kt8, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- row tile 3; scaled v_new of rows 0..31
+            mmaRow(3, fa[1], fb[1]);
+            scaleVn(0);
+            scaleVn(1);
+            const F vb0 = pack(vp[0], vp[1]);
+            mkY(2);
+            decay(6);
+            decay(7);
+            __builtin_amdgcn_sched_barrier(0);
+            if (OUT)
+                for (int it = 0; it < 4; ++it) {
+                    fp[it][0] = ldA(Pc, offT[0] + it * 16 * 128);
+                    if (it >= 2) fp[it][1] = ldA(Pc, offT[1] + it * 16 * 128);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- v_new of rows 32..63; state update from the first 32 tokens
+            mkY(3);
+            const F yb1 = pack(y[2], y[3]);
+            for (int it = 2; it < 4; ++it) {
+                vn[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+                PolicyH::mma(vn[it], ft[it][0], yb0);
+                PolicyH::mma(vn[it], ft[it][1], yb1);
+            }
+            for (int kt8 = 0; kt8 < 8; ++kt8) PolicyH::mma(h[kt8], fg0[kt8], vb0);
+            F nb0;
+            if (OUT) {
+                nb0 = pack(vn[0], vn[1]);
+                output(0, nb0, nb0);
+                output(1, nb0, nb0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            for (int kt8 = 0; kt8 < 8; ++kt8) fg1[kt8] = ldKT(KG, kt8, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- state update from the last 32 tokens; remaining output rows
+            scaleVn(2);
+            scaleVn(3);
+            const F vb1 = pack(vp[2], vp[3]);
+            for (int kt8 = 0; kt8 < 8; ++kt8) PolicyH::mma(h[kt8], fg1[kt8], vb1);
+            if (OUT) {
+                const F nb1 = pack(vn[2], vn[3]);
+                output(2, nb0, nb1);
+                output(3, nb0, nb1);
             }
             for (int s2 = 0; s2 < 4; ++s2) hb[s2] = pack(h[2 * s2], h[2 * s2 + 1]);
-            __syncthreads();                          // chunk c consumed, chunk c+1 published
+            lds_barrier();                          // chunk c consumed, chunk c+1 published
         }
         // ---- results
         for (int kt8 = 0; kt8 < 8; ++kt8)
@@ -1150,151 +1255,93 @@ __global__ __launch_bounds__(HT) void state_kernel_h(StateArgs a) {
             }
     } else {
         // ======================= streaming waves
-        // Buffer loads with 32-bit lane offsets; rows past the chunk end fall
-        // outside the buffer range and read as zeros, which zeroes beta and v
-        // there (the padded rows then contribute nothing).
-        const int lt = tid - 128;
-        struct Raw {
-            u32x4 k[8];                   // 64 x 128 tile: row (lt >> 4) + 8i, elements 8 (lt & 15) ..
-            u32x4 q[OUT ? 8 : 1];
-            u32x4 g[PERKEY ? 8 : 1];
-            u32x4 T[4];                   // 64 x 64 tile: row (lt >> 3) + 16i, granule lt & 7
-            u32x4 P[OUT ? 4 : 1];
-            u32x4 v[2];                   // v row (lt >> 2) + 32i, columns vc0 + 8 (lt & 3) ..
-            uint16_t bv[2];               // beta of those rows
-            uint16_t bt;                  // beta of row lt
-            float w0, w1, w2;             // gate words of row lt (per key: G_last of key lt)
-        };
-        uint32_t okq[8], ov[2], obv[2];
-        for (int i = 0; i < 8; ++i)
-            okq[i] = ((lt >> 4) + 8 * i) * (PERKEY ? DK * 2 : tokstride * 2) + 16 * (lt & 15);
-        for (int i = 0; i < 2; ++i) {
-            ov[i] = ((lt >> 2) + 32 * i) * tokstride * 2 + 16 * (lt & 3);
-            obv[i] = ((lt >> 2) + 32 * i) * H * 2;
-        }
-        const uint32_t obt = lt * H * 2;
-        auto load = [&](int c_, Raw& x) {
+        // Waves 2 and 3 copy the next chunks' tiles into LDS by direct
+        // global-to-LDS loads (16 bytes per lane, lane i to base + 16 i; the
+        // source addresses apply the granule swizzles): the fp16 k and q tiles
+        // (per key: k*b^G, q*b^G, k*b^{G_L-G}), T, P, the v rows of the column
+        // tile (buffer loads: rows past the chunk end read as zero) and the
+        // per-row coefficient block. They issue no other vector memory
+        // operations, so the number of copies in flight is known exactly: with
+        // three buffers, each step waits for all but the copies just issued
+        // for the chunk after next.
+        typedef __attribute__((address_space(3))) void lds_void;
+        const bool s0 = wv == 2;
+        constexpr int D0 = 16 + (PERKEY && OUT ? 16 : 0) + 4 + (SUMMARY ? 0 : 8);   // wave 2: k (+kg), v, T (forward)
+        constexpr int D1 = (OUT ? 16 + 8 : 0) + (PERKEY && !OUT ? 16 : 0) + (SUMMARY ? 8 : 0) + 1;
+        auto dma = [&](int c_, int buf) {
             const int c = __builtin_amdgcn_readfirstlane(c_);
             const int len = chunk_len(c);
             const int64_t t0 = ui.start + (int64_t)c * BT;
             const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
-            const uint32_t tile_bytes = (uint32_t)len * tokstride * 2;
-            if (PERKEY) {
-                const rsrc_t rk = make_rsrc(reinterpret_cast<const f16*>(a.ws.kd) + ch * (BT * DK), BT * DK * 2);
-                const rsrc_t rq = make_rsrc(reinterpret_cast<const f16*>(a.ws.qg) + ch * (BT * DK), BT * DK * 2);
-                const rsrc_t rg = make_rsrc(reinterpret_cast<const f16*>(a.ws.kg) + ch * (BT * DK), BT * DK * 2);
-                for (int i = 0; i < 8; ++i) {
-                    x.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, okq[i], 0, 0);
-                    if (OUT) x.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, okq[i], 0, 0);
-                    x.g[i] = __builtin_amdgcn_raw_buffer_load_b128(rg, okq[i], 0, 0);
+            const f16* ks = PERKEY ? reinterpret_cast<const f16*>(a.ws.kd) + ch * (BT * DK)
+                                   : reinterpret_cast<const f16*>(a.ws.kq16) + ch * (2 * BT * DK);
+            const f16* qs = PERKEY ? reinterpret_cast<const f16*>(a.ws.qg) + ch * (BT * DK) : ks + BT * DK;
+            const f16* gs = reinterpret_cast<const f16*>(a.ws.kg) + ch * (BT * DK);
+            const f16* Ts = reinterpret_cast<const f16*>(a.ws.Tm) + ch * (BT * BT);
+            const f16* Ps = reinterpret_cast<const f16*>(a.ws.P) + ch * (BT * BT);
+            auto tile128 = [&](const f16* src, f16* dst) {       // 64 x 128: copy m covers rows 4m .. 4m+3
+                for (int m = 0; m < 16; ++m) {
+                    const int row = 4 * m + (lane >> 4);
+                    __builtin_amdgcn_global_load_lds(src + row * DK + 8 * ((lane & 15) ^ swz16(row)),
+                                                     (lds_void*)(dst + m * 512), 16, 0, 0);
                 }
-                x.w0 = a.ws.gamL[ch * DK + lt];
+            };
+            auto tile64 = [&](const f16* src, f16* dst) {        // 64 x 64: copy m covers rows 8m .. 8m+7
+                for (int m = 0; m < 8; ++m) {
+                    const int row = 8 * m + (lane >> 3);
+                    __builtin_amdgcn_global_load_lds(src + row * BT + 8 * ((lane & 7) ^ swz8(row)),
+                                                     (lds_void*)(dst + m * 512), 16, 0, 0);
+                }
+            };
+            if (s0) {
+                tile128(ks, kt[buf]);
+                if (PERKEY && OUT) tile128(gs, gt[PERKEY ? buf : 0]);
+                // v rows of the column tile: copy m covers rows 16m .. 16m+15, 4 lanes per row
+                const rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(a.v) + (t0 * H + head) * DV + vc0,
+                                            (uint32_t)len * tokstride * 2);
+                for (int m = 0; m < 4; ++m)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vt[buf] + m * 512), 16,
+                                                             (16 * m + (lane >> 2)) * tokstride * 2 + 16 * (lane & 3), 0, 0, 0);
+                if (OUT) tile64(Ts, Tt[buf]);
             } else {
-                const rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(a.k) + (t0 * H + head) * DK, tile_bytes);
-                const rsrc_t rq = make_rsrc(reinterpret_cast<const bf16*>(a.q) + (t0 * H + head) * DK, tile_bytes);
-                for (int i = 0; i < 8; ++i) {
-                    x.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, okq[i], 0, 0);
-                    if (OUT) x.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, okq[i], 0, 0);
-                }
-                const float* gw = a.ws.gam + ch * (4 * BT) + (lt & (BT - 1));
-                x.w0 = gw[BT];
-                x.w1 = gw[2 * BT];
-                x.w2 = gw[3 * BT];
-            }
-            const rsrc_t rT = make_rsrc(reinterpret_cast<const f16*>(a.ws.Tm) + ch * (BT * BT), BT * BT * 2);
-            const rsrc_t rP = make_rsrc(reinterpret_cast<const f16*>(a.ws.P) + ch * (BT * BT), BT * BT * 2);
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t off = ((lt >> 3) + 16 * i) * (BT * 2) + 16 * (lt & 7);
-                x.T[i] = __builtin_amdgcn_raw_buffer_load_b128(rT, off, 0, 0);
-                if (OUT) x.P[i] = __builtin_amdgcn_raw_buffer_load_b128(rP, off, 0, 0);
-            }
-            const rsrc_t rb = make_rsrc(reinterpret_cast<const bf16*>(a.beta) + t0 * H + head, (uint32_t)len * H * 2);
-            x.bt = __builtin_amdgcn_raw_buffer_load_b16(rb, obt, 0, 0);
-            if (!mcols) {
-                const rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(a.v) + (t0 * H + head) * DV + vc0, tile_bytes);
-                for (int i = 0; i < 2; ++i) {
-                    x.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, ov[i], 0, 0);
-                    x.bv[i] = __builtin_amdgcn_raw_buffer_load_b16(rb, obv[i], 0, 0);
-                }
-            }
-        };
-        auto bf = [](uint32_t w, bool hi) { return __builtin_bit_cast(float, hi ? (w & 0xffff0000u) : (w << 16)); };
-        auto publish = [&](int buf, const Raw& x) {
-            const int jv = lt & 15;
-            const int p0 = op_pos(8 * jv);            // elements 8jv..8jv+3 -> granule p0/8, half (p0/4)&1
-            const int g0 = p0 >> 3, hf = ((p0 >> 2) & 1) * 8;
-            for (int i = 0; i < 8; ++i) {
-                const int r = (lt >> 4) + 8 * i;
-                const int sw = swz16(r);
-                const int a0 = r * 256 + ((g0 ^ sw) << 4) + hf, a1 = r * 256 + (((g0 + 1) ^ sw) << 4) + hf;
-                const u32x4 kv = PERKEY ? x.k[i] : __builtin_bit_cast(u32x4, PolicyH::in2op(__builtin_bit_cast(f32x4, x.k[i])));
-                *reinterpret_cast<uint2*>(reinterpret_cast<char*>(kt[buf]) + a0) = uint2{kv[0], kv[1]};
-                *reinterpret_cast<uint2*>(reinterpret_cast<char*>(kt[buf]) + a1) = uint2{kv[2], kv[3]};
                 if (OUT) {
-                    const u32x4 qv = PERKEY ? x.q[i] : __builtin_bit_cast(u32x4, PolicyH::in2op(__builtin_bit_cast(f32x4, x.q[i])));
-                    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(qt[buf]) + a0) = uint2{qv[0], qv[1]};
-                    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(qt[buf]) + a1) = uint2{qv[2], qv[3]};
+                    tile128(qs, qt[OUT ? buf : 0]);
+                    tile64(Ps, Pt[OUT ? buf : 0]);
                 }
-                if (PERKEY) {
-                    const u32x4 gv = x.g[i];
-                    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(gt[PERKEY ? buf : 0]) + a0) = uint2{gv[0], gv[1]};
-                    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(gt[PERKEY ? buf : 0]) + a1) = uint2{gv[2], gv[3]};
-                }
-            }
-            for (int i = 0; i < 4; ++i) {
-                const int r = (lt >> 3) + 16 * i;
-                const int ad = r * 128 + (((lt & 7) ^ swz8(r)) << 4);
-                *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(Tt[buf]) + ad) = x.T[i];
-                if (OUT) *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(Pt[OUT ? buf : 0]) + ad) = x.P[i];
-            }
-            if (!mcols)
-                for (int i = 0; i < 2; ++i) {
-                    const int r = (lt >> 2) + 32 * i;
-                    const float bm = __builtin_bit_cast(float, (uint32_t)x.bv[i] << 16);
-                    float* dst = &vbT[buf][(8 * (lt & 3)) * LVT + r];
-                    for (int e = 0; e < 4; ++e) {
-                        dst[(2 * e) * LVT] = bm * bf(x.v[i][e], false);
-                        dst[(2 * e + 1) * LVT] = bm * bf(x.v[i][e], true);
-                    }
-                }
-            if (PERKEY) gl[buf][lt] = fpow(x.w0, a.use_exp2);
-            if (lt < BT) {
-                const float bm = __builtin_bit_cast(float, (uint32_t)x.bt << 16);
-                if (PERKEY) {
-                    cf[buf][0][lt] = bm;
-                    cf[buf][2][lt] = a.scale;
-                } else {
-                    cf[buf][0][lt] = bm * x.w0;
-                    cf[buf][1][lt] = x.w1;
-                    cf[buf][2][lt] = a.scale * x.w0;
-                    cf[buf][3][lt] = x.w2;
-                }
+                if (PERKEY && !OUT) tile128(gs, gt[PERKEY ? buf : 0]);
+                if (SUMMARY) tile64(Ts, Tt[buf]);
+                const uint32_t* cs = reinterpret_cast<const uint32_t*>(a.ws.cfh) + ch * (CFB / 4);
+                __builtin_amdgcn_global_load_lds(cs + 4 * lane, (lds_void*)cb[buf], 16, 0, 0);
             }
         };
-        // Chunk c's loads go out NSET steps before it is published. Every step
-        // issues one load group (the last ones repeat the final chunk), so the
-        // number of loads in flight is the same on every path through the loop.
-        Raw R0, R1;
+        auto wait_copies = [&](bool leave_next) {
+            // all but the copies of the chunk after next (issued last) have landed
+            asm volatile("" ::: "memory");
+            if (leave_next) {
+                if (s0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(D0));
+                else __builtin_amdgcn_s_waitcnt(waitcnt_vm(D1));
+            } else {
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            }
+            asm volatile("" ::: "memory");
+        };
         if (nch > 0) {
-            load(0, R0);
-            if (NSET == 2) load(min(1, nch - 1), R1);
-            publish(0, R0);
-            load(min(NSET, nch - 1), R0);
+            dma(0, 0);
+            if (NB == 3) {
+                asm volatile("" ::: "memory");
+                dma(min(1, nch - 1), 1);
+            }
+            wait_copies(NB == 3);
         }
-        __syncthreads();
-        auto step = [&](int c, Raw& R) {               // R holds chunk c+1; refilled with c+1+NSET
-            if (c + 1 < nch) publish((c + 1) & 1, R);
-            load(min(c + 1 + NSET, nch - 1), R);
-            __syncthreads();
-        };
-        // both steps of a pair run unconditionally, so that the last loads
-        // before the back edge are always the same set's
-        int c = 0;
-        for (; c + 1 < nch; c += 2) {
-            step(c, NSET == 2 ? R1 : R0);
-            step(c + 1, R0);
+        lds_barrier();
+        for (int c = 0; c < nch; ++c) {
+            // the chunk index is clamped, so every step issues the same copies;
+            // the target buffer was released by the chunk before this one
+            const int cn = min(c + NB - 1, nch - 1);
+            dma(cn, NB == 2 ? (c + 1) & 1 : (c + 2) % 3);
+            wait_copies(NB == 3);
+            lds_barrier();
         }
-        if (c < nch) step(c, NSET == 2 ? R1 : R0);
     }
 }
 
@@ -1348,13 +1395,16 @@ size_t workspace_bytes(const Problem& p, Workspace* ws, char* base) {
     const int64_t oT = take(nch * BT * BT * es);
     const int64_t oP = take(nch * BT * BT * es);
     const int64_t og = take(nch * 4 * BT * 4);
-    int64_t oq = 0, od = 0, ok = 0, ol = 0;
+    int64_t oq = 0, od = 0, ok = 0, ol = 0, o16 = 0;
     if (p.per_key) {
         oq = take(nch * BT * DK * es);
         od = take(nch * BT * DK * es);
         ok = take(nch * BT * DK * es);
         ol = take(nch * DK * 4);
+    } else if (p.dtype == 1) {
+        o16 = take(nch * 2 * BT * DK * 2);
     }
+    const int64_t ocf = p.dtype == 1 ? take(nch * CFB) : 0;
     if (ws && base) {
         ws->Tm = base + oT;
         ws->P = base + oP;
@@ -1363,7 +1413,8 @@ size_t workspace_bytes(const Problem& p, Workspace* ws, char* base) {
         ws->kd = p.per_key ? base + od : nullptr;
         ws->kg = p.per_key ? base + ok : nullptr;
         ws->gamL = p.per_key ? reinterpret_cast<float*>(base + ol) : nullptr;
-        ws->plane = 0;
+        ws->kq16 = (!p.per_key && p.dtype == 1) ? base + o16 : nullptr;
+        ws->cfh = p.dtype == 1 ? base + ocf : nullptr;
     }
     return (size_t)(off > 0 ? off : 256);
 }
@@ -1414,8 +1465,9 @@ static void launch_state_h(bool summary, StateArgs a, int want_ext, int want_M, 
     if (a.n_pairs == 0 || a.ntiles == 0) return;
     const int groups = (a.n_pairs + 7) / 8;
     dim3 grid(8 * a.ntiles * groups), block(HT);
-    if (summary) hipLaunchKernelGGL((state_kernel_h<PK, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((state_kernel_h<PK, false>), grid, block, 0, s, a);
+    if (summary) hipLaunchKernelGGL((state_kernel_h<PK, true, false>), grid, block, 0, s, a);
+    else if (a.o_bf16) hipLaunchKernelGGL((state_kernel_h<PK, false, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((state_kernel_h<PK, false, false>), grid, block, 0, s, a);
 }
 
 hipError_t launch_state(const Problem& p, const Workspace& ws, const void* q, const void* k,
