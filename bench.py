@@ -33,19 +33,21 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def byte_model(w, n_chunk_heads: int) -> dict:
+def byte_model(w, n_chunk_heads: int, o_bytes: int) -> dict:
     """Algorithmic bytes per launch: what each kernel must read and write by
     its contract (every byte once), summed over the chunk-heads it processes.
-    Scalar gate, per chunk-head of 64 tokens, es = input element size, and
-    the prepared operands T, P in fp16 (bf16 inputs) or fp32 (fp32 inputs):
+    Scalar gate, per chunk-head of 64 tokens, es = input element size, ps =
+    prepared operand size (fp16 for bf16 inputs, fp32 for fp32 inputs):
       prep : q, k (2*64*128*es), g (64*4), beta (64*es)
-             -> T, P (2*64*64*ps), gate rows (4*64*4)
-      state: q, k, v (3*64*128*es), T, P (2*64*64*ps), gate rows (4*64*4),
-             beta (64*es) -> o (64*128*4, fp32)"""
+             -> T, P (2*64*64*ps), per-row coefficients (1 KiB, bf16 inputs)
+                or gate rows (4*64*4, fp32 inputs)
+      state: q, k, v (3*64*128*es), T, P (2*64*64*ps), the coefficients
+             -> o (64*128*o_bytes)"""
     es = 2 if w.dtype == "bf16" else 4
     ps = es
-    prep = 2 * 64 * 128 * es + 64 * 4 + 64 * es + 2 * 64 * 64 * ps + 4 * 64 * 4
-    state = 3 * 64 * 128 * es + 2 * 64 * 64 * ps + 4 * 64 * 4 + 64 * es + 64 * 128 * 4
+    coef = 1024 if w.dtype == "bf16" else 4 * 64 * 4
+    prep = 2 * 64 * 128 * es + 64 * 4 + 64 * es + 2 * 64 * 64 * ps + coef
+    state = 3 * 64 * 128 * es + 2 * 64 * 64 * ps + coef + 64 * 128 * o_bytes
     return {"prep": prep * n_chunk_heads, "state": state * n_chunk_heads,
             "prep_per_chunk_head": prep, "state_per_chunk_head": state}
 
@@ -103,6 +105,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gdn_dense_bf16")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--o-dtype", choices=("input", "fp32"), default="input",
+                    help="output dtype: the input dtype (default) or fp32")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device to device (calibrates the HBM byte counters) and exit")
     args = ap.parse_args()
@@ -133,7 +137,8 @@ def main():
     dev = torch.device("cuda:0")
     d = W.generate(wl, 1000 + [w.name for w in W.WORKLOADS].index(wl.name), device=dev)
     q, k, v, g, beta = (d[n] for n in ("q", "k", "v", "g", "beta"))
-    o = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    o_dtype = torch.float32 if args.o_dtype == "fp32" else v.dtype
+    o = torch.empty(v.shape, dtype=o_dtype, device=dev)
     fin = torch.empty((wl.B, wl.H, 128, 128), dtype=torch.float32, device=dev) if wl.final_state else None
     nb = gb.workspace_bytes(gb._desc(k, wl.H, k.dtype, torch.float32, False, False, d["scale"], None))
     ws = torch.empty(nb, dtype=torch.uint8, device=dev)
@@ -145,7 +150,7 @@ def main():
         if ev is not None:
             ev[1].record()
         _, f, _ = gb.gdn_chunk_fwd(q, k, v, g, beta, d["scale"], flags=gb.FLAG_REUSE_PREPARED, workspace=ws,
-                                   out=o, output_final_state=wl.final_state, final_out=fin)
+                                   out=o, o_dtype=o_dtype, output_final_state=wl.final_state, final_out=fin)
         if ev is not None:
             ev[2].record()
         return f
@@ -165,7 +170,8 @@ def main():
     ms_step = wall * 1e3 / args.steps
     tokens = wl.B * wl.T
     n_chunk_heads = wl.B * ((wl.T + 63) // 64) * wl.H
-    bm = byte_model(wl, n_chunk_heads)
+    o_bytes = o.element_size()
+    bm = byte_model(wl, n_chunk_heads, o_bytes)
     flops = FLOP_PER_TOKEN_HEAD * tokens * wl.H
     tflops = flops / (ms_step * 1e-3) / 1e12
     dom = "state" if state_ms >= prep_ms else "prep"
@@ -173,14 +179,14 @@ def main():
     achieved = bm[dom] / (dom_ms * 1e-3) / 1e9
     kname = {"state": "state_kernel", "prep": "prep_kernel"}[dom]
     traffic = load_traffic(kname, wl.name)
-    io_bytes = (3 * 128 * (2 if wl.dtype == "bf16" else 4) + 128 * 4 + 4 + (2 if wl.dtype == "bf16" else 4)) * tokens * wl.H
+    io_bytes = (3 * 128 * (2 if wl.dtype == "bf16" else 4) + 128 * o_bytes + 4 + (2 if wl.dtype == "bf16" else 4)) * tokens * wl.H
     peak_mfma = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
     out = {
         "metric": METRIC, "value": tokens / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": wl.H, "K": 128, "V": 128, "chunk": 64,
-                   "layout": wl.layout, "gate": "scalar", "o_dtype": "fp32",
+                   "layout": wl.layout, "gate": "scalar", "o_dtype": str(o_dtype).replace("torch.", ""),
                    "final_state": wl.final_state},
         "tflops": tflops, "mfma_frac": tflops / peak_mfma,
         "hbm_frac_io": io_bytes / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
@@ -197,7 +203,7 @@ def main():
 
         cb = cpu_baseline(d, wl)
         r, sel = cb.pop("_result"), cb.pop("_sel")
-        got = np.stack([o[b, :, h].cpu().numpy() for b, h in sel], axis=1)
+        got = np.stack([o[b, :, h].float().cpu().numpy() for b, h in sel], axis=1)
         ref = r["o"]
         out["parity_sample_err_over_rms"] = float(np.abs(got - ref).max() / np.sqrt((ref ** 2).mean()))
         out["cpu_baseline"] = cb

@@ -29,19 +29,17 @@ struct UnitMap {
 
 // Workspace regions, all device pointers inside the caller's workspace.
 // Operand arrays hold fp16 for bf16 inputs and fp32 for fp32 inputs. With
-// fp16 operands the 64-wide (T, P) and K-wide (k, q and their gated forms)
+// fp16 operands the 64-wide (T, P) and K-wide (the gated k and q forms)
 // rows are stored in the state pass's operand order (op_pos in the kernels).
 struct Workspace {
     void* Tm;        // operands [n_chunks][H][64][64]  T = (I + L)^{-1}
     void* P;         // operands [n_chunks][H][64][64]  decayed q.k, lower incl. diagonal
-    float* gam;      // [n_chunks][H][4][64]  scalar gate: G, b^G, b^{G_last-G}, b^{G_last}
+    float* gam;      // fp32 scalar gate only: [n_chunks][H][4][64]  G, b^G, b^{G_last-G}, b^{G_last}
     // per-key gate only
     void* qg;        // operands [n_chunks][H][64][K]  q * b^G
     void* kd;        // operands [n_chunks][H][64][K]  k * b^G
     void* kg;        // operands [n_chunks][H][64][K]  k * b^{G_last - G}
     float* gamL;     // [n_chunks][H][K]  G at the chunk's last valid token
-    // scalar gate, bf16 inputs only
-    void* kq16;      // fp16 [n_chunks][H][2][64][K]  k and q tiles, rows past the chunk end zero
     // bf16 inputs only
     void* cfh;       // [n_chunks][H][1 KiB]  per-row coefficient block of the fp16 state pass
 };

@@ -340,24 +340,6 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         *reinterpret_cast<f32x4*>(&qt[r * LDQ + cv]) = qv;
     }
     if (tid < BT) bet[tid] = tid < len ? P::f(bin[(t0 + tid) * H + head]) : 0.0f;
-    if (PERM && !PERKEY) {
-        // k and q as fp16 operand tiles for the state pass. Operand granule g =
-        // 4s + j of a row holds elements 32s + 4j .. +3 and 32s + 16 + 4j .. +3.
-        __syncthreads();
-        Op* k16 = reinterpret_cast<Op*>(a.ws.kq16) + ch * (2 * BT * DK);
-        for (int idx = tid; idx < BT * DK / 8; idx += 256) {
-            const int r = idx >> 4, g = idx & 15;
-            const int e0 = 32 * (g >> 2) + 4 * (g & 3);
-            uint2 lo = *reinterpret_cast<const uint2*>(&kt[r * LDQ + e0]);
-            uint2 hi = *reinterpret_cast<const uint2*>(&kt[r * LDQ + e0 + 16]);
-            *reinterpret_cast<u32x4*>(k16 + r * DK + 8 * g) = u32x4{lo.x, lo.y, hi.x, hi.y};
-            if (has_q) {
-                lo = *reinterpret_cast<const uint2*>(&qt[r * LDQ + e0]);
-                hi = *reinterpret_cast<const uint2*>(&qt[r * LDQ + e0 + 16]);
-                *reinterpret_cast<u32x4*>(k16 + BT * DK + r * DK + 8 * g) = u32x4{lo.x, lo.y, hi.x, hi.y};
-            }
-        }
-    }
     if (!PERKEY) {
         // inclusive scan of the scalar gate over the chunk, one wave; stores
         // G, b^G, b^{G_last - G} and b^{G_last} for the state pass
@@ -376,17 +358,6 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
             gw[2 * BT + lane] = bLG;
             gw[3 * BT + lane] = bL;
             if (a.g_cumsum && lane < len) a.g_cumsum[(t0 + lane) * H + head] = x;
-            if (PERM) {
-                // coefficient block of the fp16 state pass
-                const float bt = lane < len ? P::f(bin[(t0 + lane) * H + head]) : 0.0f;
-                f16* cf = reinterpret_cast<f16*>(a.ws.cfh) + ch * (CFB / 2);
-                const int lo = lane_order(lane);
-                cf[CF_CY + lo] = (f16)(bt * bG);
-                cf[CF_CP + lo] = (f16)bLG;
-                cf[CF_BG + lo] = (f16)bG;
-                cf[CF_BETA + lo] = (f16)bt;
-                if (lane == 0) reinterpret_cast<float*>(cf)[CF_EL] = bL;
-            }
         }
     } else {
         // per-key gate: running sum down each key column
@@ -562,6 +533,224 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
             P::st4(kg + r * DK + cp, xg);
         }
     }
+}
+
+// ------------------------------------------------------------------ prep, fp16 scalar gate
+// One wave per (chunk, head) with every tile in registers. Fragment (b, kk)
+// of a 64 x 128 input tile: lane (G, n) holds elements 32kk + 8G .. +7 of row
+// 16b + n (the 16x16x32 fp16 MFMA operand layout). With k_K as A and k_I (or
+// q_I) as B the product over the 128 keys leaves lane (G, n) holding the
+// value for token i = 16I + n against token j = 16K + 4G + r: block (I, K) of
+// k k^T (of q k^T) in "row layout" R(X), lane holding X[n][4G .. 4G+3]. The
+// accumulator layout C(X) holds X[4G .. 4G+3][n]. With 16x16x4 fp32 MFMAs
+// contracting over k = 4G + s (s = 0..3)
+//     mm4(R(A), C(B)) = C(AB),   mm4(C(B), R(A)) = R(AB),
+// so the blockwise inverse of (I + L) chains on MFMA with no lane exchange:
+// diagonal 16 x 16 blocks T_II by forward substitution (lane = block, column;
+// rows through LDS), then T_IJ = -T_II sum_{J<=K<I} L_IK T_KJ by distance.
+// The state pass reads T and P (fp16, op_pos columns) and the coefficient
+// block from here; it converts k and q itself.
+__device__ __forceinline__ f32x4 mm4(f32x4 a, f32x4 b, f32x4 c) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], c, 0, 0, 0);
+    return c;
+}
+
+// 8 bf16 (16 bytes) -> the same 8 values as fp16 (exact in the fp16 normal range)
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 w) {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = __builtin_bit_cast(float, w[i] << 16), hi = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+        o[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+    }
+    return o;
+}
+
+// 4 fp32 -> 4 fp16, rounded to nearest
+__device__ __forceinline__ u32x2 f32x4_to_f16x4(f32x4 x) {
+    f16x4 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = (f16)x[e];
+    return __builtin_bit_cast(u32x2, h);
+}
+
+constexpr int PLS = 20;               // row stride (floats) of the 16 x 16 LDS blocks
+constexpr int PBL = 16 * PLS + 4;     // L blocks: successive blocks 4 banks apart
+constexpr int PBT = 16 * PLS + 16;    // T blocks: successive blocks 16 banks apart
+
+__global__ __launch_bounds__(64) void prep_kernel_h(PrepArgs a) {
+    __shared__ __attribute__((aligned(16))) float Ld[4 * PBL];
+    __shared__ __attribute__((aligned(16))) float Td[4 * PBT];
+    __shared__ __attribute__((aligned(16))) float Gs[BT];
+    __shared__ __attribute__((aligned(16))) float Bs[BT];
+
+    const int lane = threadIdx.x, G = lane >> 4, n = lane & 15;
+    const int ci = blockIdx.x, head = blockIdx.y, H = a.H;
+    int u, cc;
+    chunk_of(a.um, ci, u, cc);
+    u = __builtin_amdgcn_readfirstlane(u);
+    cc = __builtin_amdgcn_readfirstlane(cc);
+    if (u < 0) return;
+    const UnitInfo ui = uniform(unit_info(a.um, u));
+    const int64_t t0 = ui.start + (int64_t)cc * BT;
+    int len = ui.len - cc * BT;
+    len = len < 0 ? 0 : (len > BT ? BT : len);
+    const int64_t ch = (int64_t)ci * H + head;
+    const bool has_q = a.q != nullptr;
+
+    // ---- every load up front; buffer ranges end at the chunk's last token,
+    // so rows past it read as zero
+    const uint32_t rowb = (uint32_t)H * DK * 2;   // bytes between token rows of k and q
+    const int64_t e0 = t0 * H + head;             // element index of token t0 in the gate arrays
+    const uint32_t span16 = len > 0 ? (uint32_t)(len - 1) * rowb + DK * 2 : 0;
+    const rsrc_t rg = make_rsrc(a.g + e0, len > 0 ? ((uint32_t)(len - 1) * H + 1) * 4 : 0);
+    const rsrc_t rb = make_rsrc(reinterpret_cast<const bf16*>(a.beta) + e0, len > 0 ? ((uint32_t)(len - 1) * H + 1) * 2 : 0);
+    const rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(a.k) + e0 * DK, span16);
+    const rsrc_t rq = make_rsrc(has_q ? reinterpret_cast<const bf16*>(a.q) + e0 * DK : a.k, has_q ? span16 : 0);
+    const float gv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, lane * H * 4, 0, 0));
+    const uint32_t braw = __builtin_amdgcn_raw_buffer_load_b16(rb, lane * H * 2, 0, 0);
+    u32x4 kf[4][4], qf[4][4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            kf[b][kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, (16 * b + n) * rowb + (32 * kk + 8 * G) * 2, 0, 0);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            qf[b][kk] = __builtin_amdgcn_raw_buffer_load_b128(rq, (16 * b + n) * rowb + (32 * kk + 8 * G) * 2, 0, 0);
+
+    // ---- inclusive scan of the gate (lane = token; zero past the chunk end)
+    float x = gv;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    const float xl = __shfl(x, len > 0 ? len - 1 : 0, 64);
+    const float bt = __builtin_bit_cast(float, braw << 16);
+    Gs[lane] = x;
+    Bs[lane] = bt;
+    {
+        const float bG = fpow(x, a.use_exp2), bLG = fpow(xl - x, a.use_exp2);
+        f16* cf = reinterpret_cast<f16*>(a.ws.cfh) + ch * (CFB / 2);
+        const int lo = lane_order(lane);
+        cf[CF_CY + lo] = (f16)(bt * bG);
+        cf[CF_CP + lo] = (f16)bLG;
+        cf[CF_BG + lo] = (f16)bG;
+        cf[CF_BETA + lo] = (f16)bt;
+        if (lane == 0) reinterpret_cast<float*>(cf)[CF_EL] = fpow(xl, a.use_exp2);
+        if (a.g_cumsum && lane < len) a.g_cumsum[e0 + (int64_t)lane * H] = x;
+    }
+    float Gi[4], Bi[4];
+    f32x4 Gj[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        Gi[b] = Gs[16 * b + n];
+        Bi[b] = Bs[16 * b + n];
+        Gj[b] = *reinterpret_cast<const f32x4*>(&Gs[16 * b + 4 * G]);
+    }
+
+    // ---- k and q as fp16 operands
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            kf[b][kk] = bf16x8_to_f16x8(kf[b][kk]);
+            qf[b][kk] = bf16x8_to_f16x8(qf[b][kk]);
+        }
+
+    // ---- Gram and q k^T blocks (I, K), K <= I: decay, P out, L kept
+    f16* Pw = reinterpret_cast<f16*>(a.ws.P) + ch * (BT * BT);
+    f32x4 TL[4][4];   // R(L_IK), K < I
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+#pragma unroll
+        for (int K = 0; K < 4; ++K) {
+            f16* pdst = Pw + (16 * I + n) * BT + op_pos(16 * K + 4 * G);
+            if (K > I) {
+                if (has_q) *reinterpret_cast<u32x2*>(pdst) = u32x2{0u, 0u};
+                continue;
+            }
+            f32x4 gk = {0.f, 0.f, 0.f, 0.f}, gq = gk;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const f16x8 A = __builtin_bit_cast(f16x8, kf[K][kk]);
+                gk = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(f16x8, kf[I][kk]), gk, 0, 0, 0);
+                if (has_q) gq = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(f16x8, qf[I][kk]), gq, 0, 0, 0);
+            }
+            f32x4 pv, lv;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool le = K < I || 4 * G + r <= n, lt = K < I || 4 * G + r < n;
+                const float d = le ? fpow(Gi[I] - Gj[K][r], a.use_exp2) : 0.0f;
+                pv[r] = le ? gq[r] * d : 0.0f;
+                lv[r] = lt ? Bi[I] * gk[r] * d : 0.0f;
+            }
+            if (has_q) *reinterpret_cast<u32x2*>(pdst) = f32x4_to_f16x4(pv);
+            if (K < I) TL[I][K] = lv;
+            else *reinterpret_cast<f32x4*>(&Ld[I * PBL + n * PLS + 4 * G]) = lv;
+        }
+    }
+
+    // ---- diagonal blocks: lane (block G, column n) solves (I + L_GG) x = e_n
+    {
+        const float* Lb = Ld + G * PBL;
+        float xs[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float s = 0.0f;
+#pragma unroll
+            for (int m = 0; 4 * m < i; ++m) {
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lb + i * PLS + 4 * m);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * m + e < i) s += l4[e] * xs[4 * m + e];
+            }
+            xs[i] = i == n ? 1.0f : (i > n ? -s : 0.0f);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Td[G * PBT + i * PLS + n] = xs[i];
+    }
+    f32x4 TR[4], TC[3], nTR[4];   // R(T_II), C(T_JJ), R(-T_II)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        TR[b] = *reinterpret_cast<const f32x4*>(&Td[b * PBT + n * PLS + 4 * G]);
+        nTR[b] = -TR[b];
+        if (b < 3)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) TC[b][r] = Td[b * PBT + (4 * G + r) * PLS + n];
+    }
+
+    // ---- off-diagonal blocks by distance
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 S, R10, R21, R32, R20, R31, R30, C10, C21, C20;
+    S = mm4(TL[1][0], TC[0], z4);
+    R10 = mm4(S, nTR[1], z4); C10 = mm4(nTR[1], S, z4);
+    S = mm4(TL[2][1], TC[1], z4);
+    R21 = mm4(S, nTR[2], z4); C21 = mm4(nTR[2], S, z4);
+    S = mm4(TL[3][2], TC[2], z4);
+    R32 = mm4(S, nTR[3], z4);
+    S = mm4(TL[2][1], C10, mm4(TL[2][0], TC[0], z4));
+    R20 = mm4(S, nTR[2], z4); C20 = mm4(nTR[2], S, z4);
+    S = mm4(TL[3][2], C21, mm4(TL[3][1], TC[1], z4));
+    R31 = mm4(S, nTR[3], z4);
+    S = mm4(TL[3][2], C20, mm4(TL[3][1], C10, mm4(TL[3][0], TC[0], z4)));
+    R30 = mm4(S, nTR[3], z4);
+
+    // ---- T out: fp16 operands (op_pos columns), optional token-major fp32 A slot
+    f16* Tw = reinterpret_cast<f16*>(a.ws.Tm) + ch * (BT * BT);
+    const f32x4 TB[4][4] = {{TR[0], z4, z4, z4}, {R10, TR[1], z4, z4}, {R20, R21, TR[2], z4}, {R30, R31, R32, TR[3]}};
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            *reinterpret_cast<u32x2*>(Tw + (16 * I + n) * BT + op_pos(16 * J + 4 * G)) = f32x4_to_f16x4(TB[I][J]);
+            if (a.A && 16 * I + n < len)
+                *reinterpret_cast<f32x4*>(a.A + (e0 + (int64_t)(16 * I + n) * H) * BT + 16 * J + 4 * G) = TB[I][J];
+        }
 }
 
 // ------------------------------------------------------------------ state pass
@@ -968,8 +1157,8 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
 // recurrence needs no exchange between waves: the state, the residual Y and
 // v_new stay in registers and feed the MFMAs as B operands (operand order
 // above). Waves 2 and 3, on the other two SIMDs, stream the chunk tiles
-// (k and q converted to fp16, T, P, beta*v and the per-row gate factors)
-// into double-buffered LDS, issuing each chunk's loads two steps ahead of
+// (k and q as fp16 operands, T, P, the v rows and the per-row gate factors)
+// into triple-buffered LDS, issuing each chunk's loads two steps ahead of
 // its use. One barrier per chunk hands the buffers over.
 constexpr int HW = 4;              // waves per workgroup
 constexpr int HT = 64 * HW;        // threads
@@ -981,13 +1170,17 @@ __global__ __launch_bounds__(HT) void state_kernel_h(StateArgs a) {
     // Tile buffers: three where LDS allows (copies run two chunks ahead), two
     // for the per-key forward (one chunk ahead).
     constexpr int NB = PERKEY && OUT ? 2 : 3;
-    __shared__ __attribute__((aligned(16))) f16 kt[NB][BT * DK];                          // k (per key: k*b^G)
-    __shared__ __attribute__((aligned(16))) f16 qt[OUT ? NB : 1][OUT ? BT * DK : 8];      // q (per key: q*b^G)
+    // The scalar gate's k and q tiles are written during the step before
+    // their use, so two buffers suffice for them.
+    constexpr int NBK = PERKEY ? NB : 2;
+    __shared__ __attribute__((aligned(16))) f16 kt[NBK][BT * DK];                         // k (per key: k*b^G)
+    __shared__ __attribute__((aligned(16))) f16 qt[OUT ? NBK : 1][OUT ? BT * DK : 8];     // q (per key: q*b^G)
     __shared__ __attribute__((aligned(16))) f16 gt[PERKEY ? NB : 1][PERKEY ? BT * DK : 8];// per key: k*b^{G_L-G}
     __shared__ __attribute__((aligned(16))) f16 Tt[NB][BT * BT];
     __shared__ __attribute__((aligned(16))) f16 Pt[OUT ? NB : 1][OUT ? BT * BT : 8];
     __shared__ __attribute__((aligned(16))) bf16 vt[NB][BT * BV];                         // v rows, 32 columns
     __shared__ __attribute__((aligned(16))) uint32_t cb[NB][CFB / 4];                    // per-row coefficient block
+    __shared__ __attribute__((aligned(16))) uint32_t pf[PERKEY ? 1 : 64];                 // target of the L2 prefetch copies
 
     const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1073,8 +1266,9 @@ __global__ __launch_bounds__(HT) void state_kernel_h(StateArgs a) {
                 for (int kt8 = 0; kt8 < 8; ++kt8)
                     for (int r = 0; r < 4; ++r) hs[16 * kt8 * DV + hoff[r]] = h[kt8][r];
             }
-            const f16* K = kt[tb];
-            const f16* Q = qt[OUT ? tb : 0];
+            const int tk = PERKEY ? tb : (cu & 1);
+            const f16* K = kt[tk];
+            const f16* Q = qt[OUT ? tk : 0];
             const f16* Tc = Tt[tb];
             const f16* Pc = Pt[OUT ? tb : 0];
             const f16* KG = PERKEY ? gt[PERKEY ? tb : 0] : K;
@@ -1253,32 +1447,88 @@ __global__ __launch_bounds__(HT) void state_kernel_h(StateArgs a) {
                     a.hfinal[(uh * DK + key) * DV + col] = h[kt8][r];
                 }
             }
+    } else if (!PERKEY && wv == 3) {
+        // ======================= k / q wave (scalar gate)
+        // Loads the bf16 k and q rows of the chunk after next into registers
+        // (buffer loads: rows past the chunk end read as zero) and, one step
+        // later, writes them to the LDS tiles as fp16 operands in the op_pos
+        // order. Lane (row 8i + l/8, s = (l%8)/2, m = l%2) loads the 16-byte
+        // pieces at keys 32s + 8m and 32s + 16 + 8m, which make up operand
+        // granules 4s + 2m and 4s + 2m + 1. The wave issues no global-to-LDS
+        // copies, so its waits are the compiler's own.
+        const int rl = lane >> 3, s = (lane & 7) >> 1, m = lane & 1;
+        const uint32_t rowb = tokstride * 2;   // bytes between token rows (bf16)
+        constexpr int NT = OUT ? 2 : 1;        // k, and q when there is output
+        u32x4 raw[NT][16];
+        auto ldkq = [&](int c_) {
+            const int c = __builtin_amdgcn_readfirstlane(c_);
+            const int len = chunk_len(c);
+            const int64_t e0 = ((ui.start + (int64_t)c * BT) * H + head) * DK;
+            const uint32_t span = len > 0 ? (uint32_t)(len - 1) * rowb + DK * 2 : 0;
+            for (int t = 0; t < NT; ++t) {
+                const rsrc_t r = make_rsrc(reinterpret_cast<const bf16*>(t ? a.q : a.k) + e0, span);
+                for (int i = 0; i < 8; ++i)
+                    for (int p = 0; p < 2; ++p)
+                        raw[t][2 * i + p] = __builtin_amdgcn_raw_buffer_load_b128(
+                            r, (8 * i + rl) * rowb + (32 * s + 16 * p + 8 * m) * 2, 0, 0);
+            }
+        };
+        auto stkq = [&](int buf) {
+            for (int t = 0; t < NT; ++t) {
+                char* dst = reinterpret_cast<char*>(t ? qt[OUT ? buf : 0] : kt[buf]);
+                for (int i = 0; i < 8; ++i) {
+                    const int row = 8 * i + rl, g0 = 4 * s + 2 * m;
+                    const u32x4 A = bf16x8_to_f16x8(raw[t][2 * i]), B = bf16x8_to_f16x8(raw[t][2 * i + 1]);
+                    *reinterpret_cast<u32x4*>(dst + row * 256 + ((g0 ^ swz16(row)) << 4)) = u32x4{A[0], A[1], B[0], B[1]};
+                    *reinterpret_cast<u32x4*>(dst + row * 256 + (((g0 + 1) ^ swz16(row)) << 4)) = u32x4{A[2], A[3], B[2], B[3]};
+                }
+            }
+        };
+        if (nch > 0) {
+            ldkq(0);
+            stkq(0);
+            ldkq(min(1, nch - 1));
+        }
+        lds_barrier();
+        for (int c = 0; c < nch; ++c) {
+            // buffer (c+1) & 1 was released by chunk c-1; the rows of chunk
+            // c+2 were pulled into L2 a step earlier by the copy wave. The
+            // chunk index is clamped, so the last step rewrites the last
+            // chunk's tiles.
+            stkq((c + 1) & 1);
+            ldkq(min(c + 2, nch - 1));
+            lds_barrier();
+        }
     } else {
-        // ======================= streaming waves
-        // Waves 2 and 3 copy the next chunks' tiles into LDS by direct
-        // global-to-LDS loads (16 bytes per lane, lane i to base + 16 i; the
-        // source addresses apply the granule swizzles): the fp16 k and q tiles
-        // (per key: k*b^G, q*b^G, k*b^{G_L-G}), T, P, the v rows of the column
-        // tile (buffer loads: rows past the chunk end read as zero) and the
-        // per-row coefficient block. They issue no other vector memory
+        // ======================= copy waves
+        // Direct global-to-LDS loads (16 bytes per lane, lane i to base + 16 i;
+        // the source addresses apply the granule swizzles) of T, P, the v rows
+        // of the column tile (buffer loads: rows past the chunk end read as
+        // zero), the per-row coefficient block and, per key, the gated fp16
+        // k and q tiles (k*b^G, q*b^G, k*b^{G_L-G}). Scalar gate: wave 2 alone,
+        // which also touches every 64-byte piece of the k and q rows of the
+        // chunk after its copies (one dword each, into a scratch LDS word) so
+        // that the k / q wave finds them in L2; per key: waves 2 and 3. They
+        // issue no other vector memory
         // operations, so the number of copies in flight is known exactly: with
         // three buffers, each step waits for all but the copies just issued
         // for the chunk after next.
         typedef __attribute__((address_space(3))) void lds_void;
         const bool s0 = wv == 2;
-        constexpr int D0 = 16 + (PERKEY && OUT ? 16 : 0) + 4 + (SUMMARY ? 0 : 8);   // wave 2: k (+kg), v, T (forward)
+        constexpr int D0 = !PERKEY ? 4 + 8 + (OUT ? 8 : 0) + 1 + (OUT ? 8 : 4)
+                                   : 16 + (OUT ? 16 : 0) + 4 + (SUMMARY ? 0 : 8);
         constexpr int D1 = (OUT ? 16 + 8 : 0) + (PERKEY && !OUT ? 16 : 0) + (SUMMARY ? 8 : 0) + 1;
         auto dma = [&](int c_, int buf) {
             const int c = __builtin_amdgcn_readfirstlane(c_);
             const int len = chunk_len(c);
             const int64_t t0 = ui.start + (int64_t)c * BT;
             const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
-            const f16* ks = PERKEY ? reinterpret_cast<const f16*>(a.ws.kd) + ch * (BT * DK)
-                                   : reinterpret_cast<const f16*>(a.ws.kq16) + ch * (2 * BT * DK);
-            const f16* qs = PERKEY ? reinterpret_cast<const f16*>(a.ws.qg) + ch * (BT * DK) : ks + BT * DK;
+            const f16* ks = reinterpret_cast<const f16*>(a.ws.kd) + ch * (BT * DK);
+            const f16* qs = reinterpret_cast<const f16*>(a.ws.qg) + ch * (BT * DK);
             const f16* gs = reinterpret_cast<const f16*>(a.ws.kg) + ch * (BT * DK);
             const f16* Ts = reinterpret_cast<const f16*>(a.ws.Tm) + ch * (BT * BT);
             const f16* Ps = reinterpret_cast<const f16*>(a.ws.P) + ch * (BT * BT);
+            const uint32_t* cs = reinterpret_cast<const uint32_t*>(a.ws.cfh) + ch * (CFB / 4);
             auto tile128 = [&](const f16* src, f16* dst) {       // 64 x 128: copy m covers rows 4m .. 4m+3
                 for (int m = 0; m < 16; ++m) {
                     const int row = 4 * m + (lane >> 4);
@@ -1293,24 +1543,42 @@ __global__ __launch_bounds__(HT) void state_kernel_h(StateArgs a) {
                                                      (lds_void*)(dst + m * 512), 16, 0, 0);
                 }
             };
-            if (s0) {
-                tile128(ks, kt[buf]);
-                if (PERKEY && OUT) tile128(gs, gt[PERKEY ? buf : 0]);
-                // v rows of the column tile: copy m covers rows 16m .. 16m+15, 4 lanes per row
+            auto vrows = [&]() {   // copy m covers rows 16m .. 16m+15, 4 lanes per row
                 const rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(a.v) + (t0 * H + head) * DV + vc0,
                                             (uint32_t)len * tokstride * 2);
                 for (int m = 0; m < 4; ++m)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vt[buf] + m * 512), 16,
                                                              (16 * m + (lane >> 2)) * tokstride * 2 + 16 * (lane & 3), 0, 0, 0);
+            };
+            if (!PERKEY) {
+                vrows();
+                tile64(Ts, Tt[buf]);
+                if (OUT) tile64(Ps, Pt[OUT ? buf : 0]);
+                __builtin_amdgcn_global_load_lds(cs + 4 * lane, (lds_void*)cb[buf], 16, 0, 0);
+                // L2 prefetch of the k (and q) rows of chunk c + 1
+                const int cp = min(c + 1, nch - 1), lp = chunk_len(cp);
+                const int64_t e0 = ((ui.start + (int64_t)cp * BT) * H + head) * DK;
+                const uint32_t rowb = tokstride * 2;
+                const uint32_t span = lp > 0 ? (uint32_t)(lp - 1) * rowb + DK * 2 : 0;
+                for (int t = 0; t < (OUT ? 2 : 1); ++t) {
+                    const rsrc_t r = make_rsrc(reinterpret_cast<const bf16*>(t ? a.q : a.k) + e0, span);
+                    for (int i = 0; i < 4; ++i)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)pf, 4,
+                                                                 (16 * i + (lane >> 2)) * rowb + 64 * (lane & 3), 0, 0, 0);
+                }
+            } else if (s0) {
+                tile128(ks, kt[buf]);
+                if (OUT) tile128(gs, gt[PERKEY ? buf : 0]);
+                vrows();
                 if (OUT) tile64(Ts, Tt[buf]);
             } else {
                 if (OUT) {
                     tile128(qs, qt[OUT ? buf : 0]);
                     tile64(Ps, Pt[OUT ? buf : 0]);
+                } else {
+                    tile128(gs, gt[PERKEY ? buf : 0]);
+                    tile64(Ts, Tt[buf]);
                 }
-                if (PERKEY && !OUT) tile128(gs, gt[PERKEY ? buf : 0]);
-                if (SUMMARY) tile64(Ts, Tt[buf]);
-                const uint32_t* cs = reinterpret_cast<const uint32_t*>(a.ws.cfh) + ch * (CFB / 4);
                 __builtin_amdgcn_global_load_lds(cs + 4 * lane, (lds_void*)cb[buf], 16, 0, 0);
             }
         };
@@ -1394,26 +1662,23 @@ size_t workspace_bytes(const Problem& p, Workspace* ws, char* base) {
     auto take = [&](int64_t bytes) { int64_t o = off; off = align256(off + bytes); return o; };
     const int64_t oT = take(nch * BT * BT * es);
     const int64_t oP = take(nch * BT * BT * es);
-    const int64_t og = take(nch * 4 * BT * 4);
-    int64_t oq = 0, od = 0, ok = 0, ol = 0, o16 = 0;
+    const int64_t og = (p.dtype == 0 && !p.per_key) ? take(nch * 4 * BT * 4) : 0;
+    int64_t oq = 0, od = 0, ok = 0, ol = 0;
     if (p.per_key) {
         oq = take(nch * BT * DK * es);
         od = take(nch * BT * DK * es);
         ok = take(nch * BT * DK * es);
         ol = take(nch * DK * 4);
-    } else if (p.dtype == 1) {
-        o16 = take(nch * 2 * BT * DK * 2);
     }
     const int64_t ocf = p.dtype == 1 ? take(nch * CFB) : 0;
     if (ws && base) {
         ws->Tm = base + oT;
         ws->P = base + oP;
-        ws->gam = reinterpret_cast<float*>(base + og);
+        ws->gam = (p.dtype == 0 && !p.per_key) ? reinterpret_cast<float*>(base + og) : nullptr;
         ws->qg = p.per_key ? base + oq : nullptr;
         ws->kd = p.per_key ? base + od : nullptr;
         ws->kg = p.per_key ? base + ok : nullptr;
         ws->gamL = p.per_key ? reinterpret_cast<float*>(base + ol) : nullptr;
-        ws->kq16 = (!p.per_key && p.dtype == 1) ? base + o16 : nullptr;
         ws->cfh = p.dtype == 1 ? base + ocf : nullptr;
     }
     return (size_t)(off > 0 ? off : 256);
@@ -1429,7 +1694,7 @@ hipError_t launch_prep(const Problem& p, const Workspace& ws, const void* k, con
     dim3 grid(p.um.n_chunks, p.H), block(256);
     if (p.dtype == 1) {
         if (p.per_key) hipLaunchKernelGGL((prep_kernel<PolicyH, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((prep_kernel<PolicyH, false>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL(prep_kernel_h, grid, dim3(64), 0, s, a);
     } else {
         if (p.per_key) hipLaunchKernelGGL((prep_kernel<PolicyF, true>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((prep_kernel<PolicyF, false>), grid, block, 0, s, a);

@@ -88,14 +88,12 @@ def fwd(d, *, ws=FAKE, nbytes=None, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o
 
 def test_workspace_query_sizes():
     st, nb = fwd(desc(), ws=None)
-    # bf16 inputs, scalar gate: T and P as 64x64 fp16 operand tiles, four
-    # 64-entry fp32 gate rows (G, b^G, b^{G_last-G}, b^{G_last}), the k and q
-    # tiles as fp16 operands and a 1 KiB per-row coefficient block, per
-    # chunk-head; every region starts 256-aligned
+    # bf16 inputs, scalar gate: T and P as 64x64 fp16 operand tiles and a
+    # 1 KiB per-row coefficient block per chunk-head; every region starts
+    # 256-aligned
     nch = 2 * 4 * 3
     a256 = lambda x: ((x + 255) // 256) * 256
-    expect = (2 * a256(nch * 64 * 64 * 2) + a256(nch * 4 * 64 * 4) + a256(nch * 2 * 64 * 128 * 2)
-              + a256(nch * 1024))
+    expect = 2 * a256(nch * 64 * 64 * 2) + a256(nch * 1024)
     assert st == gb.GDN_OK and nb == expect
     st, nb2 = fwd(desc(gate_kind=1), ws=None)
     assert st == gb.GDN_OK and nb2 > nb
