@@ -105,8 +105,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gdn_dense_bf16")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--o-dtype", choices=("input", "fp32"), default="input",
-                    help="output dtype: the input dtype (default) or fp32")
+    ap.add_argument("--o-dtype", choices=("fp32", "input"), default="fp32",
+                    help="output dtype: fp32 (default; rounding o to bf16 alone exceeds the "
+                         "2e-2 rms parity bar at this workload) or the input dtype")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device to device (calibrates the HBM byte counters) and exit")
     args = ap.parse_args()

@@ -173,15 +173,15 @@ gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, con
  *   S_ext  device fp32 [units][H][K][V]: the exit state from a zero entry
  *   M      device fp32 [units][H][K][K]: the transfer map (I at an empty unit)
  *   mode   0: both, 1: S_ext only (M may be NULL), 2: M only (S_ext may be NULL)
- *   q      device [tokens][H][K] or NULL. The summaries do not read it; with a
- *          per-key gate the chunk preparation that a later reusing forward
- *          needs includes q * b^G and the decayed q.k products, which are
- *          only prepared when q is given.
+ *   q      device [tokens][H][K] or NULL. The summaries do not read it, but
+ *          the chunk preparation that a later reusing forward needs includes
+ *          the decayed q.k products (and, with a per-key gate, q * b^G),
+ *          which are only prepared when q is given.
  * Units are those of desc (normally the segments of a sequence split). The
  * chunk preparation is left in the workspace, so a following gdn_chunk_fwd
  * with the same descriptor, inputs and workspace may pass
- * GDN_FLAG_REUSE_PREPARED (the correction pass of a split scan); with a
- * per-key gate that requires q here.
+ * GDN_FLAG_REUSE_PREPARED (the correction pass of a split scan), provided
+ * q was given here.
  */
 gdn_status gdn_state_summary(const gdn_desc* desc, const void* q, const void* k, const void* v,
                              const float* g, const void* beta, int32_t mode, float* S_ext, float* M,
