@@ -42,6 +42,7 @@ struct Workspace {
     float* gamL;     // [n_chunks][H][K]  G at the chunk's last valid token
     // bf16 inputs only
     void* cfh;       // [n_chunks][H][1 KiB]  per-row coefficient block of the fp16 state pass
+                     // (fp32 rows for the scalar gate, fp16 rows + fp32 gates per key)
 };
 
 struct Problem {

@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -269,6 +271,11 @@ __device__ __forceinline__ int swz8(int r) { return r & 7; }
 constexpr int CFB = 1024;
 constexpr int CF_CY = 0, CF_CP = 64, CF_BG = 128, CF_BETA = 192;   // fp16 offsets
 constexpr int CF_EL = 128, CF_GL = 128;                              // fp32 offsets
+// The scalar gate's block (CFS bytes) holds the same four rows in fp32
+// (float offsets below, same lane order); b^{G_L} is the b^G entry of the
+// chunk's last valid token.
+constexpr int CFS = 1024;
+constexpr int CS_CY = 0, CS_CP = 64, CS_BG = 128, CS_BETA = 192;
 __device__ __forceinline__ int lane_order(int t) { return 16 * ((t >> 2) & 3) + 4 * (t >> 4) + (t & 3); }
 
 // raw buffer resource over [base, base + bytes): accesses outside read as zero
@@ -635,13 +642,12 @@ __global__ __launch_bounds__(64) void prep_kernel_h(PrepArgs a) {
     Bs[lane] = bt;
     {
         const float bG = fpow(x, a.use_exp2), bLG = fpow(xl - x, a.use_exp2);
-        f16* cf = reinterpret_cast<f16*>(a.ws.cfh) + ch * (CFB / 2);
+        float* cf = reinterpret_cast<float*>(a.ws.cfh) + ch * (CFS / 4);
         const int lo = lane_order(lane);
-        cf[CF_CY + lo] = (f16)(bt * bG);
-        cf[CF_CP + lo] = (f16)bLG;
-        cf[CF_BG + lo] = (f16)bG;
-        cf[CF_BETA + lo] = (f16)bt;
-        if (lane == 0) reinterpret_cast<float*>(cf)[CF_EL] = fpow(xl, a.use_exp2);
+        cf[CS_CY + lo] = bt * bG;
+        cf[CS_CP + lo] = bLG;
+        cf[CS_BG + lo] = bG;
+        cf[CS_BETA + lo] = bt;
         if (a.g_cumsum && lane < len) a.g_cumsum[e0 + (int64_t)lane * H] = x;
     }
     float Gi[4], Bi[4];
@@ -1613,6 +1619,330 @@ __global__ __launch_bounds__(HT) void state_kernel_h(StateArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ state pass, split keys (scalar gate)
+// Workgroup of 8 waves for one (unit, head, 32-column tile). Compute wave
+// w < 4 owns value columns 16 (w & 1) .. +15 and keys 64 (w >> 1) .. +63 of
+// the fp32 state, so the four compute waves run on all four SIMDs. At the
+// end of each step a wave publishes its keys' half of the fp16 state operand
+// in LDS; after the barrier its partner (w ^ 2) reads it, so both hold the
+// whole operand and form k.h for all 64 rows themselves (the products are
+// duplicated, the step needs no second barrier). Each wave then builds Y and
+// v_new = T Y for all rows, updates its own keys, and writes the output rows
+// of its half (rows 0..31 for the first key half, 32..63 for the second).
+// Waves 4..7 stream the tiles with ordinary buffer loads into registers and
+// write them to double-buffered LDS: the k rows and the q rows (converted to
+// fp16 operands in op_pos order), T and P, and the v rows of the column tile
+// with the coefficient block. Each holds two register sets, so the loads of
+// chunk c+2 are issued at the start of step c, a full step before they are
+// written out. Rows past the chunk end read as zero.
+constexpr int KSW = 8;
+constexpr int KST = 64 * KSW;
+
+template <bool SUMMARY, bool OBF>
+__global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
+    using F = PolicyH::F;
+    constexpr bool OUT = !SUMMARY;
+    __shared__ __attribute__((aligned(16))) f16 kt[2][BT * DK];
+    __shared__ __attribute__((aligned(16))) f16 qt[OUT ? 2 : 1][OUT ? BT * DK : 8];
+    __shared__ __attribute__((aligned(16))) f16 Tt[2][BT * BT];
+    __shared__ __attribute__((aligned(16))) f16 Pt[OUT ? 2 : 1][OUT ? BT * BT : 8];
+    __shared__ __attribute__((aligned(16))) bf16 vt[2][BT * BV];
+    __shared__ __attribute__((aligned(16))) float cb[2][CFS / 4];
+    __shared__ __attribute__((aligned(16))) f16x8 hx[2][4][2][64];   // [step parity][wave][slice][lane]
+
+    const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = a.H;
+    const int L = blockIdx.x, xcd = L & 7, slot = L >> 3;
+    const int tile = slot % a.ntiles + a.tile0;
+    const int pair = (slot / a.ntiles) * 8 + xcd;
+    if (pair >= a.n_pairs) return;
+    const int u = pair / H, head = pair - u * H;
+    const UnitInfo ui = uniform(unit_info(a.um, u));
+    const int c0 = tile * BV;
+    const bool mcols = SUMMARY && c0 >= DV;         // transfer-map columns: v = 0, start at I
+    const int vc0 = mcols ? c0 - DV : c0;
+    const int nch = ui.nch;
+    const uint32_t tokstride = (uint32_t)H * DK;
+    auto chunk_len = [&](int c) {
+        int l = ui.len - c * BT;
+        return __builtin_amdgcn_readfirstlane(l < 0 ? 0 : (l > BT ? BT : l));
+    };
+
+    // the compute body, instantiated per key half so that every register
+    // array index is a compile-time constant
+    auto compute = [&](auto kq_c) {
+        constexpr int kq = decltype(kq_c)::value;
+        const int cg = wv & 1, partner = wv ^ 2;
+        const int col = vc0 + 16 * cg + n;
+        const int64_t uh = (int64_t)u * H + head;
+        f32x4 h[4];                                  // keys 64 kq + 16 j + 4G + r, column col
+        for (int j = 0; j < 4; ++j)
+            for (int r = 0; r < 4; ++r) {
+                const int key = 64 * kq + 16 * j + 4 * G + r;
+                float x = 0.0f;
+                if (mcols) x = key == col ? 1.0f : 0.0f;
+                else if (OUT && a.h0) x = a.h0[(uh * DK + key) * DV + col];
+                h[j][r] = x;
+            }
+        auto pack = [](const f32x4& x, const f32x4& y) {
+            F f;
+            for (int e = 0; e < 4; ++e) { f.v[e] = (f16)x[e]; f.v[e + 4] = (f16)y[e]; }
+            return f;
+        };
+        F hb[4];                                     // operand slices 0..3 (2 kq, 2 kq + 1 are this wave's)
+        for (int j2 = 0; j2 < 2; ++j2) {
+            hb[2 * kq + j2] = pack(h[2 * j2], h[2 * j2 + 1]);
+            hx[0][wv][j2][lane] = hb[2 * kq + j2].v;
+        }
+        // per-lane LDS byte offsets
+        int offA[4], offG[2];
+        for (int s2 = 0; s2 < 4; ++s2) offA[s2] = n * 256 + (((4 * s2 + G) ^ swz16(n)) << 4);   // row n, granule 4 s2 + G
+        for (int j2 = 0; j2 < 2; ++j2) {
+            const int s2 = 2 * kq + j2, rt = 4 * G + (n >> 2);                  // transposed read row
+            offG[j2] = rt * 256 + (((4 * s2 + (n & 3)) ^ swz16(rt)) << 4);
+        }
+        int offT[2];
+        for (int kk = 0; kk < 2; ++kk) offT[kk] = n * 128 + (((4 * kk + G) ^ swz8(n)) << 4);
+        const int offV = (4 * G + (n >> 2)) * (BV * 2) + 32 * cg + 8 * (n & 3);
+        auto ldA = [](const f16* t, int byte_off) {
+            F f;
+            f.v = *reinterpret_cast<const f16x8*>(reinterpret_cast<const char*>(t) + byte_off);
+            return f;
+        };
+        // k^T fragment of key tile 4 kq + j (keys 16 j + n of the wave's half)
+        auto ldKT = [&](const f16* t, int j, int kk) {
+            const char* p = reinterpret_cast<const char*>(t) + offG[j >> 1] + (j & 1) * 8 + kk * 32 * 256;
+            s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, p));
+            s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, p + 16 * 256));
+            f16x4 fx = __builtin_bit_cast(f16x4, x), fy = __builtin_bit_cast(f16x4, y);
+            F f;
+            for (int e = 0; e < 4; ++e) { f.v[e] = fx[e]; f.v[e + 4] = fy[e]; }
+            return f;
+        };
+        uint32_t ooff[4];
+        for (int r = 0; r < 4; ++r) ooff[r] = (uint32_t)(4 * G + r) * tokstride + col;
+        uint32_t hoff[4];
+        for (int r = 0; r < 4; ++r) hoff[r] = (uint32_t)(64 * kq + 4 * G + r) * DV + col;
+        lds_barrier();                              // chunk 0 and the entry state published
+
+        for (int c = 0; c < nch; ++c) {
+            const int cu = __builtin_amdgcn_readfirstlane(c);
+            const int tb = cu & 1, tq = tb;
+            const int len = chunk_len(cu);
+            const int64_t t0 = ui.start + (int64_t)cu * BT;
+            const int64_t ch = (int64_t)(ui.cbase + cu) * H + head;
+            if (OUT && a.hslot) {
+                float* hs = a.hslot + ch * (DK * DV);
+                for (int j = 0; j < 4; ++j)
+                    for (int r = 0; r < 4; ++r) hs[16 * j * DV + hoff[r]] = h[j][r];
+            }
+            const f16* K = kt[tb];
+            const f16* Q = qt[OUT ? tq : 0];
+            const f16* Tc = Tt[tb];
+            const f16* Pc = Pt[OUT ? tb : 0];
+            // the partner's half of the state operand
+            for (int j2 = 0; j2 < 2; ++j2) hb[2 * (1 - kq) + j2].v = hx[tq][partner][j2][lane];
+            // per-row coefficients: lane G holds rows 16 it + 4G + r at [16G + 4it + r]
+            const float* cf = cb[tb];
+            f32x4 cy[4], cpf[4], bg[4], bt[4];
+            for (int it = 0; it < 4; ++it) {
+                cy[it] = *reinterpret_cast<const f32x4*>(&cf[CS_CY + 16 * G + 4 * it]);
+                cpf[it] = *reinterpret_cast<const f32x4*>(&cf[CS_CP + 16 * G + 4 * it]);
+                if (OUT) bg[it] = *reinterpret_cast<const f32x4*>(&cf[CS_BG + 16 * G + 4 * it]);
+                bt[it] = *reinterpret_cast<const f32x4*>(&cf[CS_BETA + 16 * G + 4 * it]);
+            }
+            const float eL = cf[CS_BG + lane_order(len > 0 ? len - 1 : 0)];
+            s16x4 vraw[4];
+            for (int it = 0; it < 4; ++it)
+                vraw[it] = mcols ? s16x4{0, 0, 0, 0}
+                                 : __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                       LDS_PTR(s16x4, reinterpret_cast<const char*>(vt[tb]) + offV + it * 16 * BV * 2));
+
+            // ---- k.h for all rows; Y = beta v - beta b^G (k h)
+            f32x4 y[4];
+            for (int it = 0; it < 4; ++it) {
+                f32x4 kh = {0.f, 0.f, 0.f, 0.f};
+                for (int s2 = 0; s2 < 4; ++s2) PolicyH::mma(kh, ldA(K, offA[s2] + it * 16 * 256), hb[s2]);
+                for (int r = 0; r < 4; ++r) {
+                    const float vv = __builtin_bit_cast(float, (uint32_t)(uint16_t)vraw[it][r] << 16);
+                    y[it][r] = __builtin_fmaf(bt[it][r], vv, -cy[it][r] * kh[r]);
+                }
+            }
+            // ---- v_new = T Y for all rows
+            const F yb0 = pack(y[0], y[1]), yb1 = pack(y[2], y[3]);
+            f32x4 vn[4];
+            for (int it = 0; it < 4; ++it) {
+                vn[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+                PolicyH::mma(vn[it], ldA(Tc, offT[0] + it * 16 * 128), yb0);
+                if (it >= 2) PolicyH::mma(vn[it], ldA(Tc, offT[1] + it * 16 * 128), yb1);
+            }
+            // ---- state of this wave's keys: h = b^{G_L} h + kg^T v_new'
+            f32x4 vp[4];
+            for (int it = 0; it < 4; ++it)
+                for (int r = 0; r < 4; ++r) vp[it][r] = vn[it][r] * cpf[it][r];
+            const F vb0 = pack(vp[0], vp[1]), vb1 = pack(vp[2], vp[3]);
+            for (int j = 0; j < 4; ++j) {
+                for (int r = 0; r < 4; ++r) h[j][r] *= eL;
+                PolicyH::mma(h[j], ldKT(K, j, 0), vb0);
+                PolicyH::mma(h[j], ldKT(K, j, 1), vb1);
+            }
+            // ---- output rows of this wave's half: scale (b^G (q h) + P v_new)
+            if (OUT) {
+                const F nb0 = pack(vn[0], vn[1]), nb1 = pack(vn[2], vn[3]);
+                for (int j = 0; j < 2; ++j) {
+                    const int it = 2 * kq + j;
+                    f32x4 qh = {0.f, 0.f, 0.f, 0.f};
+                    for (int s2 = 0; s2 < 4; ++s2) PolicyH::mma(qh, ldA(Q, offA[s2] + it * 16 * 256), hb[s2]);
+                    f32x4 o;
+                    for (int r = 0; r < 4; ++r) o[r] = bg[it][r] * qh[r];
+                    PolicyH::mma(o, ldA(Pc, offT[0] + it * 16 * 128), nb0);
+                    if (kq == 1) PolicyH::mma(o, ldA(Pc, offT[1] + it * 16 * 128), nb1);
+                    const int64_t rb = ((t0 + 16 * it) * H + head) * DV;
+                    const uint32_t nrow = (uint32_t)max(len - 16 * it, 0);
+                    if (OBF) {
+                        const rsrc_t ro = make_rsrc(reinterpret_cast<bf16*>(a.o) + rb, nrow * tokstride * 2);
+                        for (int r = 0; r < 4; ++r)
+                            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (bf16)(a.scale * o[r])), ro, ooff[r] * 2, 0, 0);
+                    } else {
+                        const rsrc_t ro = make_rsrc(reinterpret_cast<float*>(a.o) + rb, nrow * tokstride * 4);
+                        for (int r = 0; r < 4; ++r) __builtin_amdgcn_raw_buffer_store_b32(f2u(a.scale * o[r]), ro, ooff[r] * 4, 0, 0);
+                    }
+                }
+            }
+            // after the output (q h uses the entry state): publish this wave's half of the next state operand
+            for (int j2 = 0; j2 < 2; ++j2) {
+                hb[2 * kq + j2] = pack(h[2 * j2], h[2 * j2 + 1]);
+                hx[tq ^ 1][wv][j2][lane] = hb[2 * kq + j2].v;
+            }
+            lds_barrier();                          // chunk c consumed, chunk c+1 and the state operand published
+        }
+        // ---- results
+        for (int j = 0; j < 4; ++j)
+            for (int r = 0; r < 4; ++r) {
+                const int key = 64 * kq + 16 * j + 4 * G + r;
+                if (SUMMARY) {
+                    if (mcols) { if (a.M) a.M[(uh * DK + key) * DK + col] = h[j][r]; }
+                    else if (a.S_ext) a.S_ext[(uh * DK + key) * DV + col] = h[j][r];
+                } else if (a.hfinal) {
+                    a.hfinal[(uh * DK + key) * DV + col] = h[j][r];
+                }
+            }
+    };
+    if (wv < 4) {
+        // ======================= compute waves
+        if (wv >> 1) compute(std::integral_constant<int, 1>{});
+        else compute(std::integral_constant<int, 0>{});
+    } else {
+        // ======================= streaming waves
+        // instantiated per wave role so that every register index is static:
+        // role 0 the k rows, 1 the q rows, 2 T and P, 3 the v rows and the
+        // coefficient block
+        auto stream = [&](auto role_c) {
+            constexpr int role = decltype(role_c)::value;
+            constexpr bool XR = role <= 1 && (role == 0 || OUT);   // k / q rows
+            constexpr bool TP = role == 2;
+            constexpr bool VC = role == 3;
+            const uint32_t rowb = tokstride * 2;         // bytes between token rows of k, q, v (bf16)
+            // k / q rows: lane (row 8i + l/8, s = (l%8)/2, m = l%2) loads the
+            // 16-byte pieces at keys 32s + 8m and 32s + 16 + 8m, which make up
+            // operand granules 4s + 2m and 4s + 2m + 1
+            const int rl = lane >> 3, s = (lane & 7) >> 1, m = lane & 1;
+            struct Set { u32x4 x[16]; };                 // role 0/1: 16 pieces; 2: T (0..7), P (8..15); 3: v (0..3), coefficients (4)
+            auto load = [&](int c_, Set& d) {
+                const int c = __builtin_amdgcn_readfirstlane(c_);
+                const int len = chunk_len(c);
+                const int64_t t0 = ui.start + (int64_t)c * BT;
+                const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
+                if (XR) {
+                    const uint32_t span = len > 0 ? (uint32_t)(len - 1) * rowb + DK * 2 : 0;
+                    const rsrc_t rx = make_rsrc(reinterpret_cast<const bf16*>(role == 0 ? a.k : a.q) + (t0 * H + head) * DK, span);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+#pragma unroll
+                        for (int p = 0; p < 2; ++p)
+                            d.x[2 * i + p] = __builtin_amdgcn_raw_buffer_load_b128(rx, (8 * i + rl) * rowb + (32 * s + 16 * p + 8 * m) * 2, 0, 0);
+                }
+                if (TP) {
+#pragma unroll
+                    for (int tp = 0; tp < (OUT ? 2 : 1); ++tp) {
+                        const rsrc_t rt = make_rsrc(reinterpret_cast<const f16*>(tp ? a.ws.P : a.ws.Tm) + ch * (BT * BT), BT * BT * 2);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            d.x[8 * tp + i] = __builtin_amdgcn_raw_buffer_load_b128(rt, (8 * i + (lane >> 3)) * 128 + 16 * (lane & 7), 0, 0);
+                    }
+                }
+                if (VC) {
+                    // rows 16i + l/4, 16-byte piece l%4 of the tile's 32 columns
+                    const rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(a.v) + (t0 * H + head) * DV + vc0,
+                                                mcols ? 0u : (uint32_t)len * rowb);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        d.x[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (16 * i + (lane >> 2)) * rowb + 16 * (lane & 3), 0, 0);
+                    const rsrc_t rc = make_rsrc(reinterpret_cast<const char*>(a.ws.cfh) + ch * CFS, CFS);
+                    d.x[4] = __builtin_amdgcn_raw_buffer_load_b128(rc, 16 * lane, 0, 0);
+                }
+            };
+            auto store = [&](const Set& d, int buf) {
+                if (XR) {
+                    char* dx = reinterpret_cast<char*>(role == 0 ? kt[buf] : qt[OUT ? buf : 0]);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int row = 8 * i + rl, g0 = 4 * s + 2 * m;
+                        const u32x4 A = bf16x8_to_f16x8(d.x[2 * i]), B = bf16x8_to_f16x8(d.x[2 * i + 1]);
+                        *reinterpret_cast<u32x4*>(dx + row * 256 + ((g0 ^ swz16(row)) << 4)) = u32x4{A[0], A[1], B[0], B[1]};
+                        *reinterpret_cast<u32x4*>(dx + row * 256 + (((g0 + 1) ^ swz16(row)) << 4)) = u32x4{A[2], A[3], B[2], B[3]};
+                    }
+                }
+                if (TP) {
+#pragma unroll
+                    for (int tp = 0; tp < (OUT ? 2 : 1); ++tp) {
+                        char* dt = reinterpret_cast<char*>(tp ? Pt[OUT ? buf : 0] : Tt[buf]);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            const int row = 8 * i + (lane >> 3);
+                            *reinterpret_cast<u32x4*>(dt + row * 128 + (((lane & 7) ^ swz8(row)) << 4)) = d.x[8 * tp + i];
+                        }
+                    }
+                }
+                if (VC) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(vt[buf]) + i * 1024 + 16 * lane) = d.x[i];
+                    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(cb[buf]) + 16 * lane) = d.x[4];
+                }
+            };
+            // two register sets: even chunks in sa, odd chunks in sb
+            Set sa, sb;
+            if (nch > 0) {
+                load(0, sa);
+                load(min(1, nch - 1), sb);
+                store(sa, 0);
+            }
+            lds_barrier();
+            // Step c: the loads of chunk c + 2 into the set that held chunk
+            // c, then chunk c + 1 (loaded a step ago) into the LDS buffers
+            // that chunk c - 1 released. The loop is unrolled by two so that
+            // each set keeps its registers. Chunk indices are clamped, so the
+            // last steps repeat the last chunk.
+            for (int c = 0; c < nch; c += 2) {
+                load(min(c + 2, nch - 1), sa);
+                store(sb, 1);
+                lds_barrier();
+                if (c + 1 < nch) {
+                    load(min(c + 3, nch - 1), sb);
+                    store(sa, 0);
+                    lds_barrier();
+                }
+            }
+        };
+        if (wv == 4) stream(std::integral_constant<int, 0>{});
+        else if (wv == 5) stream(std::integral_constant<int, 1>{});
+        else if (wv == 6) stream(std::integral_constant<int, 2>{});
+        else stream(std::integral_constant<int, 3>{});
+    }
+}
+
 // ------------------------------------------------------------------ merge
 constexpr int MC = 8;   // state columns per merge workgroup
 
@@ -1670,7 +2000,7 @@ size_t workspace_bytes(const Problem& p, Workspace* ws, char* base) {
         ok = take(nch * BT * DK * es);
         ol = take(nch * DK * 4);
     }
-    const int64_t ocf = p.dtype == 1 ? take(nch * CFB) : 0;
+    const int64_t ocf = p.dtype == 1 ? take(nch * (p.per_key ? CFB : CFS)) : 0;
     if (ws && base) {
         ws->Tm = base + oT;
         ws->P = base + oP;
@@ -1729,10 +2059,16 @@ static void launch_state_h(bool summary, StateArgs a, int want_ext, int want_M, 
     }
     if (a.n_pairs == 0 || a.ntiles == 0) return;
     const int groups = (a.n_pairs + 7) / 8;
-    dim3 grid(8 * a.ntiles * groups), block(HT);
-    if (summary) hipLaunchKernelGGL((state_kernel_h<PK, true, false>), grid, block, 0, s, a);
-    else if (a.o_bf16) hipLaunchKernelGGL((state_kernel_h<PK, false, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((state_kernel_h<PK, false, false>), grid, block, 0, s, a);
+    dim3 grid(8 * a.ntiles * groups);
+    if (!PK) {
+        if (summary) hipLaunchKernelGGL((state_kernel_ks<true, false>), grid, dim3(KST), 0, s, a);
+        else if (a.o_bf16) hipLaunchKernelGGL((state_kernel_ks<false, true>), grid, dim3(KST), 0, s, a);
+        else hipLaunchKernelGGL((state_kernel_ks<false, false>), grid, dim3(KST), 0, s, a);
+        return;
+    }
+    if (summary) hipLaunchKernelGGL((state_kernel_h<true, true, false>), grid, dim3(HT), 0, s, a);
+    else if (a.o_bf16) hipLaunchKernelGGL((state_kernel_h<true, false, true>), grid, dim3(HT), 0, s, a);
+    else hipLaunchKernelGGL((state_kernel_h<true, false, false>), grid, dim3(HT), 0, s, a);
 }
 
 hipError_t launch_state(const Problem& p, const Workspace& ws, const void* q, const void* k,
