@@ -1630,11 +1630,12 @@ __global__ __launch_bounds__(HT) void state_kernel_h(StateArgs a) {
 // v_new = T Y for all rows, updates its own keys, and writes the output rows
 // of its half (rows 0..31 for the first key half, 32..63 for the second).
 // Waves 4..7 stream the tiles with ordinary buffer loads into registers and
-// write them to double-buffered LDS: the k rows and the q rows (converted to
-// fp16 operands in op_pos order), T and P, and the v rows of the column tile
-// with the coefficient block. Each holds two register sets, so the loads of
-// chunk c+2 are issued at the start of step c, a full step before they are
-// written out. Rows past the chunk end read as zero.
+// write them to double-buffered LDS, each a quarter of the token rows of
+// every tile: k and q (converted to fp16 operands in op_pos order), T, P and
+// the v rows of the column tile, plus the coefficient block. Each holds two
+// register sets, so the loads of chunk c+2 are issued at the start of step
+// c, a full step before they are written out. Rows past the chunk end read
+// as zero.
 constexpr int KSW = 8;
 constexpr int KST = 64 * KSW;
 
@@ -1835,82 +1836,74 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
         else compute(std::integral_constant<int, 0>{});
     } else {
         // ======================= streaming waves
-        // instantiated per wave role so that every register index is static:
-        // role 0 the k rows, 1 the q rows, 2 T and P, 3 the v rows and the
-        // coefficient block
+        // Streaming wave 4 + r takes token rows 16r .. 16r+15 of every tile
+        // (k and q rows, T, P, v), wave 4 also the coefficient block;
+        // instantiated per r so that every register index is static.
         auto stream = [&](auto role_c) {
             constexpr int role = decltype(role_c)::value;
-            constexpr bool XR = role <= 1 && (role == 0 || OUT);   // k / q rows
-            constexpr bool TP = role == 2;
-            constexpr bool VC = role == 3;
             const uint32_t rowb = tokstride * 2;         // bytes between token rows of k, q, v (bf16)
             // k / q rows: lane (row 8i + l/8, s = (l%8)/2, m = l%2) loads the
             // 16-byte pieces at keys 32s + 8m and 32s + 16 + 8m, which make up
-            // operand granules 4s + 2m and 4s + 2m + 1
+            // operand granules 4s + 2m and 4s + 2m + 1 (i = 2 role, 2 role + 1)
             const int rl = lane >> 3, s = (lane & 7) >> 1, m = lane & 1;
-            struct Set { u32x4 x[16]; };                 // role 0/1: 16 pieces; 2: T (0..7), P (8..15); 3: v (0..3), coefficients (4)
+            // [0..3] k, [4..7] q, [8..9] T, [10..11] P, [12] v, [13] coefficients
+            struct Set { u32x4 x[14]; };
             auto load = [&](int c_, Set& d) {
                 const int c = __builtin_amdgcn_readfirstlane(c_);
                 const int len = chunk_len(c);
                 const int64_t t0 = ui.start + (int64_t)c * BT;
                 const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
-                if (XR) {
-                    const uint32_t span = len > 0 ? (uint32_t)(len - 1) * rowb + DK * 2 : 0;
-                    const rsrc_t rx = make_rsrc(reinterpret_cast<const bf16*>(role == 0 ? a.k : a.q) + (t0 * H + head) * DK, span);
+                const uint32_t span = len > 0 ? (uint32_t)(len - 1) * rowb + DK * 2 : 0;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i)
+                for (int kq = 0; kq < (OUT ? 2 : 1); ++kq) {
+                    const rsrc_t rx = make_rsrc(reinterpret_cast<const bf16*>(kq ? a.q : a.k) + (t0 * H + head) * DK, span);
+#pragma unroll
+                    for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
                         for (int p = 0; p < 2; ++p)
-                            d.x[2 * i + p] = __builtin_amdgcn_raw_buffer_load_b128(rx, (8 * i + rl) * rowb + (32 * s + 16 * p + 8 * m) * 2, 0, 0);
+                            d.x[4 * kq + 2 * ii + p] = __builtin_amdgcn_raw_buffer_load_b128(
+                                rx, (8 * (2 * role + ii) + rl) * rowb + (32 * s + 16 * p + 8 * m) * 2, 0, 0);
                 }
-                if (TP) {
 #pragma unroll
-                    for (int tp = 0; tp < (OUT ? 2 : 1); ++tp) {
-                        const rsrc_t rt = make_rsrc(reinterpret_cast<const f16*>(tp ? a.ws.P : a.ws.Tm) + ch * (BT * BT), BT * BT * 2);
+                for (int tp = 0; tp < (OUT ? 2 : 1); ++tp) {
+                    const rsrc_t rt = make_rsrc(reinterpret_cast<const f16*>(tp ? a.ws.P : a.ws.Tm) + ch * (BT * BT), BT * BT * 2);
 #pragma unroll
-                        for (int i = 0; i < 8; ++i)
-                            d.x[8 * tp + i] = __builtin_amdgcn_raw_buffer_load_b128(rt, (8 * i + (lane >> 3)) * 128 + 16 * (lane & 7), 0, 0);
-                    }
+                    for (int ii = 0; ii < 2; ++ii)
+                        d.x[8 + 2 * tp + ii] = __builtin_amdgcn_raw_buffer_load_b128(
+                            rt, (8 * (2 * role + ii) + (lane >> 3)) * 128 + 16 * (lane & 7), 0, 0);
                 }
-                if (VC) {
-                    // rows 16i + l/4, 16-byte piece l%4 of the tile's 32 columns
-                    const rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(a.v) + (t0 * H + head) * DV + vc0,
-                                                mcols ? 0u : (uint32_t)len * rowb);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        d.x[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (16 * i + (lane >> 2)) * rowb + 16 * (lane & 3), 0, 0);
+                // v rows 16 role + l/4, 16-byte piece l%4 of the tile's 32 columns
+                const rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(a.v) + (t0 * H + head) * DV + vc0,
+                                            mcols ? 0u : (uint32_t)len * rowb);
+                d.x[12] = __builtin_amdgcn_raw_buffer_load_b128(rv, (16 * role + (lane >> 2)) * rowb + 16 * (lane & 3), 0, 0);
+                if (role == 0) {
                     const rsrc_t rc = make_rsrc(reinterpret_cast<const char*>(a.ws.cfh) + ch * CFS, CFS);
-                    d.x[4] = __builtin_amdgcn_raw_buffer_load_b128(rc, 16 * lane, 0, 0);
+                    d.x[13] = __builtin_amdgcn_raw_buffer_load_b128(rc, 16 * lane, 0, 0);
                 }
             };
             auto store = [&](const Set& d, int buf) {
-                if (XR) {
-                    char* dx = reinterpret_cast<char*>(role == 0 ? kt[buf] : qt[OUT ? buf : 0]);
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const int row = 8 * i + rl, g0 = 4 * s + 2 * m;
-                        const u32x4 A = bf16x8_to_f16x8(d.x[2 * i]), B = bf16x8_to_f16x8(d.x[2 * i + 1]);
+                for (int kq = 0; kq < (OUT ? 2 : 1); ++kq) {
+                    char* dx = reinterpret_cast<char*>(kq ? qt[OUT ? buf : 0] : kt[buf]);
+#pragma unroll
+                    for (int ii = 0; ii < 2; ++ii) {
+                        const int row = 8 * (2 * role + ii) + rl, g0 = 4 * s + 2 * m;
+                        const u32x4 A = bf16x8_to_f16x8(d.x[4 * kq + 2 * ii]), B = bf16x8_to_f16x8(d.x[4 * kq + 2 * ii + 1]);
                         *reinterpret_cast<u32x4*>(dx + row * 256 + ((g0 ^ swz16(row)) << 4)) = u32x4{A[0], A[1], B[0], B[1]};
                         *reinterpret_cast<u32x4*>(dx + row * 256 + (((g0 + 1) ^ swz16(row)) << 4)) = u32x4{A[2], A[3], B[2], B[3]};
                     }
                 }
-                if (TP) {
 #pragma unroll
-                    for (int tp = 0; tp < (OUT ? 2 : 1); ++tp) {
-                        char* dt = reinterpret_cast<char*>(tp ? Pt[OUT ? buf : 0] : Tt[buf]);
+                for (int tp = 0; tp < (OUT ? 2 : 1); ++tp) {
+                    char* dt = reinterpret_cast<char*>(tp ? Pt[OUT ? buf : 0] : Tt[buf]);
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            const int row = 8 * i + (lane >> 3);
-                            *reinterpret_cast<u32x4*>(dt + row * 128 + (((lane & 7) ^ swz8(row)) << 4)) = d.x[8 * tp + i];
-                        }
+                    for (int ii = 0; ii < 2; ++ii) {
+                        const int row = 8 * (2 * role + ii) + (lane >> 3);
+                        *reinterpret_cast<u32x4*>(dt + row * 128 + (((lane & 7) ^ swz8(row)) << 4)) = d.x[8 + 2 * tp + ii];
                     }
                 }
-                if (VC) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(vt[buf]) + i * 1024 + 16 * lane) = d.x[i];
-                    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(cb[buf]) + 16 * lane) = d.x[4];
-                }
+                *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(vt[buf]) + role * 1024 + 16 * lane) = d.x[12];
+                if (role == 0) *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(cb[buf]) + 16 * lane) = d.x[13];
             };
             // two register sets: even chunks in sa, odd chunks in sb
             Set sa, sb;
