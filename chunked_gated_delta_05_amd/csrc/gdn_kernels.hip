@@ -592,8 +592,10 @@ __global__ __launch_bounds__(64) void prep_kernel_h(PrepArgs a) {
     __shared__ __attribute__((aligned(16))) float Gs[BT];
     __shared__ __attribute__((aligned(16))) float Bs[BT];
 
+    // heads vary fastest across the grid, so that waves dispatched together
+    // read the same token rows (all heads of a row are contiguous)
     const int lane = threadIdx.x, G = lane >> 4, n = lane & 15;
-    const int ci = blockIdx.x, head = blockIdx.y, H = a.H;
+    const int H = a.H, ci = (int)(blockIdx.x / (uint32_t)H), head = (int)(blockIdx.x - (uint32_t)ci * H);
     int u, cc;
     chunk_of(a.um, ci, u, cc);
     u = __builtin_amdgcn_readfirstlane(u);
@@ -1760,34 +1762,42 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
                                  : __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                        LDS_PTR(s16x4, reinterpret_cast<const char*>(vt[tb]) + offV + it * 16 * BV * 2));
 
-            // ---- k.h for all rows; Y = beta v - beta b^G (k h)
-            f32x4 y[4];
-            for (int it = 0; it < 4; ++it) {
+            // The step runs as a pipeline over the two 32-row halves: T is
+            // lower triangular, so v_new of rows 0..31 needs Y of rows 0..31
+            // only, and the state update from the first 32 tokens can run
+            // while the k.h products of the second half complete.
+            auto khY = [&](int it, f32x4& y) {           // Y = beta v - beta b^G (k h), row tile it
                 f32x4 kh = {0.f, 0.f, 0.f, 0.f};
                 for (int s2 = 0; s2 < 4; ++s2) PolicyH::mma(kh, ldA(K, offA[s2] + it * 16 * 256), hb[s2]);
                 for (int r = 0; r < 4; ++r) {
                     const float vv = __builtin_bit_cast(float, (uint32_t)(uint16_t)vraw[it][r] << 16);
-                    y[it][r] = __builtin_fmaf(bt[it][r], vv, -cy[it][r] * kh[r]);
+                    y[r] = __builtin_fmaf(bt[it][r], vv, -cy[it][r] * kh[r]);
                 }
-            }
-            // ---- v_new = T Y for all rows
-            const F yb0 = pack(y[0], y[1]), yb1 = pack(y[2], y[3]);
-            f32x4 vn[4];
+            };
+            f32x4 y[4], vn[4], vp[4];
+            khY(0, y[0]);
+            khY(1, y[1]);
+            const F yb0 = pack(y[0], y[1]);
             for (int it = 0; it < 4; ++it) {
                 vn[it] = f32x4{0.f, 0.f, 0.f, 0.f};
                 PolicyH::mma(vn[it], ldA(Tc, offT[0] + it * 16 * 128), yb0);
-                if (it >= 2) PolicyH::mma(vn[it], ldA(Tc, offT[1] + it * 16 * 128), yb1);
             }
+            khY(2, y[2]);
+            khY(3, y[3]);
             // ---- state of this wave's keys: h = b^{G_L} h + kg^T v_new'
-            f32x4 vp[4];
-            for (int it = 0; it < 4; ++it)
+            for (int it = 0; it < 2; ++it)
                 for (int r = 0; r < 4; ++r) vp[it][r] = vn[it][r] * cpf[it][r];
-            const F vb0 = pack(vp[0], vp[1]), vb1 = pack(vp[2], vp[3]);
+            const F vb0 = pack(vp[0], vp[1]);
             for (int j = 0; j < 4; ++j) {
                 for (int r = 0; r < 4; ++r) h[j][r] *= eL;
                 PolicyH::mma(h[j], ldKT(K, j, 0), vb0);
-                PolicyH::mma(h[j], ldKT(K, j, 1), vb1);
             }
+            const F yb1 = pack(y[2], y[3]);
+            for (int it = 2; it < 4; ++it) PolicyH::mma(vn[it], ldA(Tc, offT[1] + it * 16 * 128), yb1);
+            for (int it = 2; it < 4; ++it)
+                for (int r = 0; r < 4; ++r) vp[it][r] = vn[it][r] * cpf[it][r];
+            const F vb1 = pack(vp[2], vp[3]);
+            for (int j = 0; j < 4; ++j) PolicyH::mma(h[j], ldKT(K, j, 1), vb1);
             // ---- output rows of this wave's half: scale (b^G (q h) + P v_new)
             if (OUT) {
                 const F nb0 = pack(vn[0], vn[1]), nb1 = pack(vn[2], vn[3]);
@@ -2017,7 +2027,7 @@ hipError_t launch_prep(const Problem& p, const Workspace& ws, const void* k, con
     dim3 grid(p.um.n_chunks, p.H), block(256);
     if (p.dtype == 1) {
         if (p.per_key) hipLaunchKernelGGL((prep_kernel<PolicyH, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL(prep_kernel_h, grid, dim3(64), 0, s, a);
+        else hipLaunchKernelGGL(prep_kernel_h, dim3(p.H * p.um.n_chunks), dim3(64), 0, s, a);
     } else {
         if (p.per_key) hipLaunchKernelGGL((prep_kernel<PolicyF, true>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((prep_kernel<PolicyF, false>), grid, block, 0, s, a);
