@@ -19,15 +19,22 @@
 // (residual first, then the decayed state plus the gated-key update).
 //
 // Kernels:
-//   prep_kernel   one workgroup per (chunk, head): G, L on MFMA, the 64 x 64
-//                 triangular inverse in LDS, T to the workspace (per-key gate:
-//                 also P, q*b^G, k*b^G, k*b^{G_last-G}, G_last).
-//   state_kernel  one workgroup per (unit, head, column tile); every wave owns
-//                 all 128 state rows of 16 value columns, so the recurrence
-//                 needs no exchange between waves; the waves share the chunk
-//                 tiles (k, q, T, P) through LDS. In summary mode it runs the
-//                 same recurrence on [S_ext | M] from [0 | I].
-//   merge_kernel  S_init[s+1] = M_s S_init[s] + S_ext[s] in fp32.
+//   prep_kernel_h    bf16, scalar gate: one wave per (chunk, head) with every
+//                    tile in registers: G, L and P on MFMA, the 64 x 64 inverse
+//                    (diagonal blocks by substitution, the rest on fp32 MFMA),
+//                    T, P and the per-row coefficients to the workspace.
+//   prep_kernel      fp32 inputs and per-key gates: one workgroup per (chunk,
+//                    head), the inverse in LDS (per-key gate: also q*b^G,
+//                    k*b^G, k*b^{G_last-G}, G_last).
+//   state_kernel_ks  bf16, scalar gate: one workgroup per (unit, head, 32
+//                    columns); four compute waves split the state by keys,
+//                    four streaming waves stage the chunk tiles.
+//   state_kernel_pk  bf16, per-key gate: two compute waves own all keys of 16
+//                    columns each; two waves copy the prepared tiles.
+//   state_kernel     fp32 inputs: eight waves, each owning 32 keys of 16
+//                    columns. In summary mode every state kernel runs the same
+//                    recurrence on [S_ext | M] from [0 | I].
+//   merge_kernel     S_init[s+1] = M_s S_init[s] + S_ext[s] in fp32.
 //
 // Precision: bf16 inputs are converted to fp16 MFMA operands (exact for
 // normal-range values); products accumulate in fp32; the state, the cumulative
@@ -63,9 +70,6 @@ __device__ __forceinline__ uint32_t f2u(float x) { return __builtin_bit_cast(uin
 __device__ __forceinline__ float fpow(float x, int use_exp2) {
     return __builtin_amdgcn_exp2f(use_exp2 ? x : x * 1.4426950408889634f);
 }
-
-// orders this wave's LDS writes before its following LDS reads
-__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Workgroup barrier for LDS hand-offs only: this wave's LDS accesses complete
 // before it, but outstanding global loads and stores stay in flight (the
@@ -263,14 +267,13 @@ __device__ __forceinline__ int swz16(int r) {
 }
 __device__ __forceinline__ int swz8(int r) { return r & 7; }
 
-// Per-chunk coefficient block of the fp16 state pass (CFB bytes, written by
-// the preparation): four 64-entry fp16 rows in lane order (entry 16G + 4it + r
-// belongs to token row 16it + 4G + r) - beta b^G, b^{G_L-G}, b^G, beta (per-key
-// gate: beta, 1, 1, beta) - then fp32 b^{G_L} (scalar gate) or b^{G_L} of
-// every key (per-key gate).
+// Per-chunk coefficient block of the per-key fp16 state pass (CFB bytes,
+// written by the preparation): four 64-entry fp16 rows in lane order (entry
+// 16G + 4it + r belongs to token row 16it + 4G + r) - beta, 1, 1, beta - then
+// the fp32 b^{G_L} of every key.
 constexpr int CFB = 1024;
 constexpr int CF_CY = 0, CF_CP = 64, CF_BG = 128, CF_BETA = 192;   // fp16 offsets
-constexpr int CF_EL = 128, CF_GL = 128;                              // fp32 offsets
+constexpr int CF_GL = 128;                                          // fp32 offset
 // The scalar gate's block (CFS bytes) holds the same four rows in fp32
 // (float offsets below, same lane order); b^{G_L} is the b^G entry of the
 // chunk's last valid token.
@@ -286,7 +289,6 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 }
 
 // ------------------------------------------------------------------ prep
-constexpr int LD6 = BT + 8;   // row stride of 64-wide LDS operand tiles (elements)
 constexpr int LDL = BT + 1;   // row stride of 64 x 64 fp32 LDS matrices
 
 struct PrepArgs {
@@ -801,22 +803,14 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
     constexpr int LDQ = P::LDQ;
     constexpr int FV = P::FV;
     constexpr bool OUT = !SUMMARY;
-    // STAGE: the q, T and P tiles are published once per workgroup into LDS
-    // and the output leaves through an LDS tile as whole row segments. The
-    // fp32 operand variant (twice the bytes per tile) reads q, T and P rows
-    // into registers per wave and stores the output directly instead.
-    constexpr bool STAGE = sizeof(Op) == 2;
-    constexpr int LDO = BV + 4;                                                 // output staging rows (fp32)
+    // Each wave reads its q, T and P rows into registers and stores its
+    // output rows directly; k and the per-key gated k are shared through LDS.
     __shared__ __attribute__((aligned(16))) Op kt[2][BT * LDQ];                  // k (per key: k*b^G)
-    __shared__ __attribute__((aligned(16))) Op qt[STAGE && OUT ? BT * LDQ : 8];  // q (per key: q*b^G)
-    __shared__ __attribute__((aligned(16))) Op Tt[STAGE ? BT * LD6 : 8];         // T
-    __shared__ __attribute__((aligned(16))) Op Pt[STAGE && OUT ? BT * LD6 : 8];  // P
     __shared__ __attribute__((aligned(16))) Op kgt[PERKEY ? BT * LDQ : 8];       // per key: k*b^{G_last-G}
     __shared__ __attribute__((aligned(16))) Op hT[BV * LDQ];                     // state, transposed
     __shared__ __attribute__((aligned(16))) Op YT[BV * LDY];
     __shared__ __attribute__((aligned(16))) Op vnT[OUT ? BV * LDY : 8];
     __shared__ __attribute__((aligned(16))) Op vpT[BV * LDY];
-    __shared__ __attribute__((aligned(16))) float ot[STAGE && OUT ? BT * LDO : 4];  // output staging
     __shared__ __attribute__((aligned(16))) float gam[2][4 * BT];                // G, b^G, b^{G_L-G}, b^{G_L}
     __shared__ __attribute__((aligned(16))) float bet[2][BT];
     __shared__ __attribute__((aligned(16))) float gl[2][PERKEY ? DK : 4];
@@ -866,10 +860,9 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
     // T is the identity on padded rows, and padded output rows are not stored.
     constexpr int VPR = 16 / sizeof(In);
     constexpr int NKV = BT * DK / VPR / ST;           // 16-byte vectors per thread of a 64 x 128 tile
-    constexpr int NTV = BT * BT * (int)sizeof(Op) / 16 / ST;   // ... of a 64 x 64 operand tile
     constexpr int NGW = PERKEY ? DK : 4 * BT;         // gate words per chunk
-    constexpr int RQ = STAGE ? NKV : 4 * FV;          // q registers: tile vectors or the wave's rows
-    constexpr int RT = STAGE ? NTV : 2 * FV;          // T / P registers: tile vectors or the wave's rows
+    constexpr int RQ = 4 * FV;                        // q registers: the wave's rows
+    constexpr int RT = 2 * FV;                        // T / P registers: the wave's rows
     auto chunk_len = [&](int c) { int l = ui.len - c * BT; return l < 0 ? 0 : (l > BT ? BT : l); };
     struct Raw {
         f32x4 k[NKV];                    // k tile (per key: k*b^G operands)
@@ -886,12 +879,6 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
         const int idx = tid + ST * i;
         r = idx / (DK / VPR);
         cv = (idx % (DK / VPR)) * VPR;
-    };
-    auto tile64_rc = [&](int i, int& r, int& cv) {   // 64 x 64 operand tile vector -> (row, column)
-        constexpr int per_row = BT * (int)sizeof(Op) / 16;
-        const int idx = tid + ST * i;
-        r = idx / per_row;
-        cv = (idx % per_row) * (16 / (int)sizeof(Op));
     };
     auto load_raw = [&](int c, Raw& x) {
         const int len = chunk_len(c);
@@ -924,36 +911,18 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
         if (OUT) {
             const Op* qg = reinterpret_cast<const Op*>(a.ws.qg) + ch * (BT * DK);
             const In* qb = qin + (t0 * H + head) * DK;
-            if (STAGE) {
-                for (int i = 0; i < NKV; ++i) {
-                    int r, cv;
-                    tile_rc(i, r, cv);
-                    x.q[i] = PERKEY ? *reinterpret_cast<const f32x4*>(qg + r * DK + cv)
-                                    : *reinterpret_cast<const f32x4*>(qb + (uint32_t)min(r, last) * tokstride + cv);
+            for (int kk = 0; kk < 4; ++kk)
+                for (int f = 0; f < FV; ++f)
+                    x.q[FV * kk + f] = PERKEY ? *reinterpret_cast<const f32x4*>(qg + row * DK + 32 * kk + 8 * G + 4 * f)
+                                              : *reinterpret_cast<const f32x4*>(qb + (uint32_t)min(row, last) * tokstride +
+                                                                                 32 * kk + 8 * G + 4 * f);
+        }
+        for (int kk = 0; kk < 2; ++kk)
+            if (kk < nkw)
+                for (int f = 0; f < FV; ++f) {
+                    x.T[FV * kk + f] = *reinterpret_cast<const f32x4*>(Tw + row * BT + 32 * kk + 8 * G + 4 * f);
+                    if (OUT) x.Pr[FV * kk + f] = *reinterpret_cast<const f32x4*>(Pw + row * BT + 32 * kk + 8 * G + 4 * f);
                 }
-            } else {
-                for (int kk = 0; kk < 4; ++kk)
-                    for (int f = 0; f < FV; ++f)
-                        x.q[FV * kk + f] = PERKEY ? *reinterpret_cast<const f32x4*>(qg + row * DK + 32 * kk + 8 * G + 4 * f)
-                                                  : *reinterpret_cast<const f32x4*>(qb + (uint32_t)min(row, last) * tokstride +
-                                                                                     32 * kk + 8 * G + 4 * f);
-            }
-        }
-        if (STAGE) {
-            for (int i = 0; i < NTV; ++i) {
-                int r, cv;
-                tile64_rc(i, r, cv);
-                x.T[i] = *reinterpret_cast<const f32x4*>(Tw + r * BT + cv);
-                if (OUT) x.Pr[i] = *reinterpret_cast<const f32x4*>(Pw + r * BT + cv);
-            }
-        } else {
-            for (int kk = 0; kk < 2; ++kk)
-                if (kk < nkw)
-                    for (int f = 0; f < FV; ++f) {
-                        x.T[FV * kk + f] = *reinterpret_cast<const f32x4*>(Tw + row * BT + 32 * kk + 8 * G + 4 * f);
-                        if (OUT) x.Pr[FV * kk + f] = *reinterpret_cast<const f32x4*>(Pw + row * BT + 32 * kk + 8 * G + 4 * f);
-                    }
-        }
         x.bt = (bin + t0 * H + head)[(uint32_t)min(lane, last) * H];
         if (!mcols) {
             const In* vb = vin + (t0 * H + head) * DV;
@@ -966,28 +935,15 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
             int r, cv;
             tile_rc(i, r, cv);
             *reinterpret_cast<f32x4*>(&kt[b][r * LDQ + cv]) = PERKEY ? x.k[i] : P::in2op(x.k[i]);
-            if (STAGE && OUT) *reinterpret_cast<f32x4*>(&qt[r * LDQ + cv]) = PERKEY ? x.q[i] : P::in2op(x.q[i]);
         }
-        if (STAGE)
-            for (int i = 0; i < NTV; ++i) {
-                int r, cv;
-                tile64_rc(i, r, cv);
-                *reinterpret_cast<f32x4*>(&Tt[r * LD6 + cv]) = x.T[i];
-            }
         if (tid < NGW) {
             if (PERKEY) gl[b][tid] = x.gb;
             else gam[b][tid] = x.gb;
         }
         if (tid < BT) bet[b][tid] = tid < x.len ? P::f(x.bt) : 0.0f;
     };
-    // P and the per-key gated k of a chunk (read only after its step's first barrier)
+    // the per-key gated k of a chunk (read only after its step's first barrier)
     auto publish_late = [&](const Raw& x) {
-        if (STAGE && OUT)
-            for (int i = 0; i < NTV; ++i) {
-                int r, cv;
-                tile64_rc(i, r, cv);
-                *reinterpret_cast<f32x4*>(&Pt[r * LD6 + cv]) = x.Pr[i];
-            }
         if (PERKEY)
             for (int i = 0; i < NKV; ++i) {
                 int r, cv;
@@ -995,24 +951,6 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
                 *reinterpret_cast<f32x4*>(&kgt[r * LDQ + cv]) = x.kg[i];
             }
     };
-    // output rows of chunk c from the staging tile, 16 bytes per thread
-    auto flush_out = [&](int c, int len) {
-        const int64_t t0 = ui.start + (int64_t)c * BT;
-        constexpr int per_row = BV / 4;
-        const int r = tid / per_row, cc = (tid % per_row) * 4;
-        if (r < len) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(&ot[r * LDO + cc]);
-            const uint32_t off = (uint32_t)r * tokstride + vc0 + cc;
-            if (a.o_bf16) {
-                bf16* ob = reinterpret_cast<bf16*>(a.o) + (t0 * H + head) * DV;
-                for (int e = 0; e < 4; ++e) ob[off + e] = (bf16)x[e];
-            } else {
-                float* of = reinterpret_cast<float*>(a.o) + (t0 * H + head) * DV;
-                *reinterpret_cast<f32x4*>(of + off) = x;
-            }
-        }
-    };
-
     // ---- prologue
     const int nch = ui.nch;
     Raw cur, nxt;
@@ -1032,7 +970,6 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
         const int64_t t0 = ui.start + (int64_t)c * BT;
         const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
         const bool more = c + 1 < nch;
-        if (STAGE && OUT && c > 0) flush_out(c - 1, chunk_len(c - 1));
         publish_late(cur);
         if (more) load_raw(c + 1, nxt);
         if (OUT && a.hslot) {
@@ -1053,13 +990,9 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
             const F hb = P::ld(&hT[(16 * cg + n) * LDQ + 32 * kk + 8 * G]);
             P::mma(kh, P::ld(&K[(16 * rg + n) * LDQ + 32 * kk + 8 * G]), hb);
             if (OUT) {
-                if (STAGE) {
-                    P::mma(qh, P::ld(&qt[(16 * rg + n) * LDQ + 32 * kk + 8 * G]), hb);
-                } else {
-                    f32x4 qv[FV];
-                    for (int f = 0; f < FV; ++f) qv[f] = PERKEY ? cur.q[FV * kk + f] : P::in2op(cur.q[FV * kk + f]);
-                    P::mma(qh, P::frag(qv), hb);
-                }
+                f32x4 qv[FV];
+                for (int f = 0; f < FV; ++f) qv[f] = PERKEY ? cur.q[FV * kk + f] : P::in2op(cur.q[FV * kk + f]);
+                P::mma(qh, P::frag(qv), hb);
             }
         }
         // Y = beta (v - b^G K h) (per key: K already carries b^G)
@@ -1081,7 +1014,7 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
         f32x4 vn = {0.f, 0.f, 0.f, 0.f};
         for (int kk = 0; kk < 2; ++kk)
             if (kk < nkw) {
-                const F ta = STAGE ? P::ld(&Tt[(16 * rg + n) * LD6 + 32 * kk + 8 * G]) : P::frag(&cur.T[FV * kk]);
+                const F ta = P::frag(&cur.T[FV * kk]);
                 P::mma(vn, ta, P::ld(&YT[(16 * cg + n) * LDY + 32 * kk + 8 * G]));
             }
         {
@@ -1099,22 +1032,17 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
         if (OUT) {
             for (int kk = 0; kk < 2; ++kk)
                 if (kk < nkw) {
-                    const F pa = STAGE ? P::ld(&Pt[(16 * rg + n) * LD6 + 32 * kk + 8 * G]) : P::frag(&cur.Pr[FV * kk]);
-                    P::mma(oacc, pa, P::ld(&vnT[(16 * cg + n) * LDY + 32 * kk + 8 * G]));
+                    P::mma(oacc, P::frag(&cur.Pr[FV * kk]), P::ld(&vnT[(16 * cg + n) * LDY + 32 * kk + 8 * G]));
                 }
-            if (STAGE) {
-                for (int r = 0; r < 4; ++r) ot[(16 * rg + 4 * G + r) * LDO + 16 * cg + n] = a.scale * oacc[r];
-            } else {
-                float* of = reinterpret_cast<float*>(a.o) + (t0 * H + head) * DV;
-                bf16* ob = reinterpret_cast<bf16*>(a.o) + (t0 * H + head) * DV;
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * rg + 4 * G + r;
-                    if (i < len) {
-                        const float x = a.scale * oacc[r];
-                        const uint32_t off = (uint32_t)i * tokstride + col;
-                        if (a.o_bf16) ob[off] = (bf16)x;
-                        else of[off] = x;
-                    }
+            float* of = reinterpret_cast<float*>(a.o) + (t0 * H + head) * DV;
+            bf16* ob = reinterpret_cast<bf16*>(a.o) + (t0 * H + head) * DV;
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * rg + 4 * G + r;
+                if (i < len) {
+                    const float x = a.scale * oacc[r];
+                    const uint32_t off = (uint32_t)i * tokstride + col;
+                    if (a.o_bf16) ob[off] = (bf16)x;
+                    else of[off] = x;
                 }
             }
         }
@@ -1143,7 +1071,6 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
         }
         __syncthreads();
     }
-    if (STAGE && OUT && nch > 0) flush_out(nch - 1, chunk_len(nch - 1));
 
     // ---- results
     for (int ks = 0; ks < 2; ++ks)
@@ -1159,36 +1086,32 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
         }
 }
 
-// ------------------------------------------------------------------ state pass, fp16 operands
+// ------------------------------------------------------------------ state pass, fp16 operands, per-key gate
 // Workgroup of 4 waves for one (unit, head, 32-column tile). Waves 0 and 1
 // each own 16 value columns with all 64 token rows and all 128 keys, so the
 // recurrence needs no exchange between waves: the state, the residual Y and
 // v_new stay in registers and feed the MFMAs as B operands (operand order
-// above). Waves 2 and 3, on the other two SIMDs, stream the chunk tiles
-// (k and q as fp16 operands, T, P, the v rows and the per-row gate factors)
-// into triple-buffered LDS, issuing each chunk's loads two steps ahead of
-// its use. One barrier per chunk hands the buffers over.
+// above). Waves 2 and 3, on the other two SIMDs, copy the prepared gated
+// tiles (k*b^G, q*b^G, k*b^{G_L-G}), T, P, the v rows and the per-row gate
+// factors into multi-buffered LDS ahead of their use. One barrier per chunk
+// hands the buffers over.
 constexpr int HW = 4;              // waves per workgroup
 constexpr int HT = 64 * HW;        // threads
 
-template <bool PERKEY, bool SUMMARY, bool OBF>
-__global__ __launch_bounds__(HT) void state_kernel_h(StateArgs a) {
+template <bool SUMMARY, bool OBF>
+__global__ __launch_bounds__(HT) void state_kernel_pk(StateArgs a) {
     using F = PolicyH::F;
     constexpr bool OUT = !SUMMARY;
     // Tile buffers: three where LDS allows (copies run two chunks ahead), two
-    // for the per-key forward (one chunk ahead).
-    constexpr int NB = PERKEY && OUT ? 2 : 3;
-    // The scalar gate's k and q tiles are written during the step before
-    // their use, so two buffers suffice for them.
-    constexpr int NBK = PERKEY ? NB : 2;
-    __shared__ __attribute__((aligned(16))) f16 kt[NBK][BT * DK];                         // k (per key: k*b^G)
-    __shared__ __attribute__((aligned(16))) f16 qt[OUT ? NBK : 1][OUT ? BT * DK : 8];     // q (per key: q*b^G)
-    __shared__ __attribute__((aligned(16))) f16 gt[PERKEY ? NB : 1][PERKEY ? BT * DK : 8];// per key: k*b^{G_L-G}
+    // for the forward (one chunk ahead).
+    constexpr int NB = OUT ? 2 : 3;
+    __shared__ __attribute__((aligned(16))) f16 kt[NB][BT * DK];                          // k*b^G
+    __shared__ __attribute__((aligned(16))) f16 qt[OUT ? NB : 1][OUT ? BT * DK : 8];      // q*b^G
+    __shared__ __attribute__((aligned(16))) f16 gt[NB][BT * DK];                          // k*b^{G_L-G}
     __shared__ __attribute__((aligned(16))) f16 Tt[NB][BT * BT];
     __shared__ __attribute__((aligned(16))) f16 Pt[OUT ? NB : 1][OUT ? BT * BT : 8];
     __shared__ __attribute__((aligned(16))) bf16 vt[NB][BT * BV];                         // v rows, 32 columns
     __shared__ __attribute__((aligned(16))) uint32_t cb[NB][CFB / 4];                    // per-row coefficient block
-    __shared__ __attribute__((aligned(16))) uint32_t pf[PERKEY ? 1 : 64];                 // target of the L2 prefetch copies
 
     const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1274,12 +1197,11 @@ __global__ __launch_bounds__(HT) void state_kernel_h(StateArgs a) {
                 for (int kt8 = 0; kt8 < 8; ++kt8)
                     for (int r = 0; r < 4; ++r) hs[16 * kt8 * DV + hoff[r]] = h[kt8][r];
             }
-            const int tk = PERKEY ? tb : (cu & 1);
-            const f16* K = kt[tk];
-            const f16* Q = qt[OUT ? tk : 0];
+            const f16* K = kt[tb];
+            const f16* Q = qt[OUT ? tb : 0];
             const f16* Tc = Tt[tb];
             const f16* Pc = Pt[OUT ? tb : 0];
-            const f16* KG = PERKEY ? gt[PERKEY ? tb : 0] : K;
+            const f16* KG = gt[tb];
             // The step runs as a pipeline over the four 16-row tiles: while the
             // MFMAs of one row tile run, the VALU work of the previous one (Y,
             // v_new scaling, the state decay) and the LDS reads of the next one
@@ -1302,11 +1224,9 @@ __global__ __launch_bounds__(HT) void state_kernel_h(StateArgs a) {
             };
             // the per-row data of the chunk, read first so that no later wait drains it
             const f16* cbh = reinterpret_cast<const f16*>(cb[tb]);
-            f16x8 cyv[2], cpv[2], bgv[2], btv[2];
+            f16x8 cyv[2], btv[2];
             for (int h2 = 0; h2 < 2; ++h2) {
                 cyv[h2] = *reinterpret_cast<const f16x8*>(&cbh[CF_CY + 16 * G + 8 * h2]);
-                if (!PERKEY) cpv[h2] = *reinterpret_cast<const f16x8*>(&cbh[CF_CP + 16 * G + 8 * h2]);
-                if (OUT && !PERKEY) bgv[h2] = *reinterpret_cast<const f16x8*>(&cbh[CF_BG + 16 * G + 8 * h2]);
                 btv[h2] = *reinterpret_cast<const f16x8*>(&cbh[CF_BETA + 16 * G + 8 * h2]);
             }
             s16x4 vraw[4];
@@ -1316,14 +1236,9 @@ __global__ __launch_bounds__(HT) void state_kernel_h(StateArgs a) {
                                        LDS_PTR(s16x4, reinterpret_cast<const char*>(vt[tb]) + offV + it * 16 * BV * 2));
             auto coef = [](const f16x8* v, int it, int r) { return (float)v[it >> 1][4 * (it & 1) + r]; };
             const float* cbf = reinterpret_cast<const float*>(cb[tb]);
-            const float eL = PERKEY ? 1.0f : cbf[CF_EL];
-            auto decay = [&](int kt8) {
-                if (PERKEY) {
-                    const f32x4 gv = *reinterpret_cast<const f32x4*>(&cbf[CF_GL + 16 * kt8 + 4 * G]);
-                    for (int r = 0; r < 4; ++r) h[kt8][r] *= gv[r];
-                } else {
-                    for (int r = 0; r < 4; ++r) h[kt8][r] *= eL;
-                }
+            auto decay = [&](int kt8) {                // h = Diag(b^{G_L}) h for keys 16 kt8 + 4G + r
+                const f32x4 gv = *reinterpret_cast<const f32x4*>(&cbf[CF_GL + 16 * kt8 + 4 * G]);
+                for (int r = 0; r < 4; ++r) h[kt8][r] *= gv[r];
             };
             f32x4 y[4];
             auto mkY = [&](int it) {                   // Y = beta v - beta b^G (K h)
@@ -1333,19 +1248,13 @@ __global__ __launch_bounds__(HT) void state_kernel_h(StateArgs a) {
                 }
             };
             f32x4 vn[4], vp[4];
-            auto scaleVn = [&](int it) {               // v_new' = b^{G_L - G} v_new
-                if (PERKEY) {
-                    vp[it] = vn[it];
-                } else {
-                    for (int r = 0; r < 4; ++r) vp[it][r] = vn[it][r] * coef(cpv, it, r);
-                }
-            };
+            auto scaleVn = [&](int it) { vp[it] = vn[it]; };   // the gated keys carry b^{G_L - G}
             F ft[4][2], fp[4][2], fg0[8], fg1[8];
             // output rows of tile it: scale (b^G (q h) + P v_new); rows past the
             // chunk end fall outside the buffer range and are dropped
             auto output = [&](int it, const F& nb0, const F& nb1) {
                 f32x4 o;
-                for (int r = 0; r < 4; ++r) o[r] = PERKEY ? qh[it][r] : coef(bgv, it, r) * qh[it][r];
+                for (int r = 0; r < 4; ++r) o[r] = qh[it][r];       // q*b^G is prepared
                 PolicyH::mma(o, fp[it][0], nb0);
                 if (it >= 2) PolicyH::mma(o, fp[it][1], nb1);
                 const int64_t rb = ((t0 + 16 * it) * H + head) * DV;
@@ -1455,77 +1364,20 @@ __global__ __launch_bounds__(HT) void state_kernel_h(StateArgs a) {
                     a.hfinal[(uh * DK + key) * DV + col] = h[kt8][r];
                 }
             }
-    } else if (!PERKEY && wv == 3) {
-        // ======================= k / q wave (scalar gate)
-        // Loads the bf16 k and q rows of the chunk after next into registers
-        // (buffer loads: rows past the chunk end read as zero) and, one step
-        // later, writes them to the LDS tiles as fp16 operands in the op_pos
-        // order. Lane (row 8i + l/8, s = (l%8)/2, m = l%2) loads the 16-byte
-        // pieces at keys 32s + 8m and 32s + 16 + 8m, which make up operand
-        // granules 4s + 2m and 4s + 2m + 1. The wave issues no global-to-LDS
-        // copies, so its waits are the compiler's own.
-        const int rl = lane >> 3, s = (lane & 7) >> 1, m = lane & 1;
-        const uint32_t rowb = tokstride * 2;   // bytes between token rows (bf16)
-        constexpr int NT = OUT ? 2 : 1;        // k, and q when there is output
-        u32x4 raw[NT][16];
-        auto ldkq = [&](int c_) {
-            const int c = __builtin_amdgcn_readfirstlane(c_);
-            const int len = chunk_len(c);
-            const int64_t e0 = ((ui.start + (int64_t)c * BT) * H + head) * DK;
-            const uint32_t span = len > 0 ? (uint32_t)(len - 1) * rowb + DK * 2 : 0;
-            for (int t = 0; t < NT; ++t) {
-                const rsrc_t r = make_rsrc(reinterpret_cast<const bf16*>(t ? a.q : a.k) + e0, span);
-                for (int i = 0; i < 8; ++i)
-                    for (int p = 0; p < 2; ++p)
-                        raw[t][2 * i + p] = __builtin_amdgcn_raw_buffer_load_b128(
-                            r, (8 * i + rl) * rowb + (32 * s + 16 * p + 8 * m) * 2, 0, 0);
-            }
-        };
-        auto stkq = [&](int buf) {
-            for (int t = 0; t < NT; ++t) {
-                char* dst = reinterpret_cast<char*>(t ? qt[OUT ? buf : 0] : kt[buf]);
-                for (int i = 0; i < 8; ++i) {
-                    const int row = 8 * i + rl, g0 = 4 * s + 2 * m;
-                    const u32x4 A = bf16x8_to_f16x8(raw[t][2 * i]), B = bf16x8_to_f16x8(raw[t][2 * i + 1]);
-                    *reinterpret_cast<u32x4*>(dst + row * 256 + ((g0 ^ swz16(row)) << 4)) = u32x4{A[0], A[1], B[0], B[1]};
-                    *reinterpret_cast<u32x4*>(dst + row * 256 + (((g0 + 1) ^ swz16(row)) << 4)) = u32x4{A[2], A[3], B[2], B[3]};
-                }
-            }
-        };
-        if (nch > 0) {
-            ldkq(0);
-            stkq(0);
-            ldkq(min(1, nch - 1));
-        }
-        lds_barrier();
-        for (int c = 0; c < nch; ++c) {
-            // buffer (c+1) & 1 was released by chunk c-1; the rows of chunk
-            // c+2 were pulled into L2 a step earlier by the copy wave. The
-            // chunk index is clamped, so the last step rewrites the last
-            // chunk's tiles.
-            stkq((c + 1) & 1);
-            ldkq(min(c + 2, nch - 1));
-            lds_barrier();
-        }
     } else {
         // ======================= copy waves
         // Direct global-to-LDS loads (16 bytes per lane, lane i to base + 16 i;
-        // the source addresses apply the granule swizzles) of T, P, the v rows
-        // of the column tile (buffer loads: rows past the chunk end read as
-        // zero), the per-row coefficient block and, per key, the gated fp16
-        // k and q tiles (k*b^G, q*b^G, k*b^{G_L-G}). Scalar gate: wave 2 alone,
-        // which also touches every 64-byte piece of the k and q rows of the
-        // chunk after its copies (one dword each, into a scratch LDS word) so
-        // that the k / q wave finds them in L2; per key: waves 2 and 3. They
-        // issue no other vector memory
-        // operations, so the number of copies in flight is known exactly: with
-        // three buffers, each step waits for all but the copies just issued
-        // for the chunk after next.
+        // the source addresses apply the granule swizzles) of the gated fp16
+        // k and q tiles (k*b^G, q*b^G, k*b^{G_L-G}), T, P, the v rows of the
+        // column tile (buffer loads: rows past the chunk end read as zero) and
+        // the per-row coefficient block. The waves issue no other vector
+        // memory operations, so the number of copies in flight is known
+        // exactly: each step waits for all but the copies just issued for the
+        // chunk ahead.
         typedef __attribute__((address_space(3))) void lds_void;
         const bool s0 = wv == 2;
-        constexpr int D0 = !PERKEY ? 4 + 8 + (OUT ? 8 : 0) + 1 + (OUT ? 8 : 4)
-                                   : 16 + (OUT ? 16 : 0) + 4 + (SUMMARY ? 0 : 8);
-        constexpr int D1 = (OUT ? 16 + 8 : 0) + (PERKEY && !OUT ? 16 : 0) + (SUMMARY ? 8 : 0) + 1;
+        constexpr int D0 = 16 + (OUT ? 16 : 0) + 4 + (SUMMARY ? 0 : 8);
+        constexpr int D1 = (OUT ? 16 + 8 : 0) + (!OUT ? 16 : 0) + (SUMMARY ? 8 : 0) + 1;
         auto dma = [&](int c_, int buf) {
             const int c = __builtin_amdgcn_readfirstlane(c_);
             const int len = chunk_len(c);
@@ -1558,25 +1410,9 @@ __global__ __launch_bounds__(HT) void state_kernel_h(StateArgs a) {
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vt[buf] + m * 512), 16,
                                                              (16 * m + (lane >> 2)) * tokstride * 2 + 16 * (lane & 3), 0, 0, 0);
             };
-            if (!PERKEY) {
-                vrows();
-                tile64(Ts, Tt[buf]);
-                if (OUT) tile64(Ps, Pt[OUT ? buf : 0]);
-                __builtin_amdgcn_global_load_lds(cs + 4 * lane, (lds_void*)cb[buf], 16, 0, 0);
-                // L2 prefetch of the k (and q) rows of chunk c + 1
-                const int cp = min(c + 1, nch - 1), lp = chunk_len(cp);
-                const int64_t e0 = ((ui.start + (int64_t)cp * BT) * H + head) * DK;
-                const uint32_t rowb = tokstride * 2;
-                const uint32_t span = lp > 0 ? (uint32_t)(lp - 1) * rowb + DK * 2 : 0;
-                for (int t = 0; t < (OUT ? 2 : 1); ++t) {
-                    const rsrc_t r = make_rsrc(reinterpret_cast<const bf16*>(t ? a.q : a.k) + e0, span);
-                    for (int i = 0; i < 4; ++i)
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)pf, 4,
-                                                                 (16 * i + (lane >> 2)) * rowb + 64 * (lane & 3), 0, 0, 0);
-                }
-            } else if (s0) {
+            if (s0) {
                 tile128(ks, kt[buf]);
-                if (OUT) tile128(gs, gt[PERKEY ? buf : 0]);
+                if (OUT) tile128(gs, gt[buf]);
                 vrows();
                 if (OUT) tile64(Ts, Tt[buf]);
             } else {
@@ -1584,7 +1420,7 @@ __global__ __launch_bounds__(HT) void state_kernel_h(StateArgs a) {
                     tile128(qs, qt[OUT ? buf : 0]);
                     tile64(Ps, Pt[OUT ? buf : 0]);
                 } else {
-                    tile128(gs, gt[PERKEY ? buf : 0]);
+                    tile128(gs, gt[buf]);
                     tile64(Ts, Tt[buf]);
                 }
                 __builtin_amdgcn_global_load_lds(cs + 4 * lane, (lds_void*)cb[buf], 16, 0, 0);
@@ -2069,9 +1905,9 @@ static void launch_state_h(bool summary, StateArgs a, int want_ext, int want_M, 
         else hipLaunchKernelGGL((state_kernel_ks<false, false>), grid, dim3(KST), 0, s, a);
         return;
     }
-    if (summary) hipLaunchKernelGGL((state_kernel_h<true, true, false>), grid, dim3(HT), 0, s, a);
-    else if (a.o_bf16) hipLaunchKernelGGL((state_kernel_h<true, false, true>), grid, dim3(HT), 0, s, a);
-    else hipLaunchKernelGGL((state_kernel_h<true, false, false>), grid, dim3(HT), 0, s, a);
+    if (summary) hipLaunchKernelGGL((state_kernel_pk<true, false>), grid, dim3(HT), 0, s, a);
+    else if (a.o_bf16) hipLaunchKernelGGL((state_kernel_pk<false, true>), grid, dim3(HT), 0, s, a);
+    else hipLaunchKernelGGL((state_kernel_pk<false, false>), grid, dim3(HT), 0, s, a);
 }
 
 hipError_t launch_state(const Problem& p, const Workspace& ws, const void* q, const void* k,
