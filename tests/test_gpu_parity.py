@@ -75,6 +75,23 @@ def test_dense_small(B, T, H, dtype):
     np.testing.assert_allclose(gc, ref, rtol=1e-5, atol=1e-5)
 
 
+@pytest.mark.parametrize("per_key", [False, True])
+def test_bf16_output_is_the_rounded_fp32_output(per_key):
+    # o_dtype = bf16 stores the same fp32 result rounded to nearest-even:
+    # within half a bf16 ulp of the fp32-output run (allowing one ulp for
+    # reassociation between the two instantiations)
+    print(f"bf16 output per_key={per_key}", flush=True)
+    d = to_dev(W.generate(small(B=2, T=200, H=3, per_key=per_key, use_exp2=per_key,
+                                gate_coef=0.05 if per_key else 0.1), 29))
+    o32, _, _ = run_gpu(d)
+    o16, _, _ = run_gpu(d, o_dtype=torch.bfloat16)
+    assert o16.dtype == torch.bfloat16
+    ref = np32(o32).astype(np.float64)
+    got = np32(o16).astype(np.float64)
+    ulp = np.abs(ref) * 2.0 ** -7 + 1e-30
+    assert np.all(np.abs(got - ref) <= ulp), float(np.max(np.abs(got - ref) / ulp))
+
+
 def test_tiny_fp32_workload():
     d = to_dev(W.generate(W.WORKLOADS[0], 1000))
     o, fin, _ = run_gpu(d, output_final_state=True)
