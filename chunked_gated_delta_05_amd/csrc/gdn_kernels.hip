@@ -287,6 +287,10 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// Cache policy of the output stores: non-temporal. A forward never reads o
+// back, and o written through the caches would push k, q, v, T and P (which
+// the next forward reads again) out of the last-level cache.
+constexpr int CP_NT = 2;
 
 // ------------------------------------------------------------------ prep
 constexpr int LDL = BT + 1;   // row stride of 64 x 64 fp32 LDS matrices
@@ -1262,10 +1266,10 @@ __global__ __launch_bounds__(HT) void state_kernel_pk(StateArgs a) {
                 if (OBF) {
                     const rsrc_t ro = make_rsrc(reinterpret_cast<bf16*>(a.o) + rb, nrow * tokstride * 2);
                     for (int r = 0; r < 4; ++r)
-                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (bf16)(a.scale * o[r])), ro, ooff[r] * 2, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (bf16)(a.scale * o[r])), ro, ooff[r] * 2, 0, CP_NT);
                 } else {
                     const rsrc_t ro = make_rsrc(reinterpret_cast<float*>(a.o) + rb, nrow * tokstride * 4);
-                    for (int r = 0; r < 4; ++r) __builtin_amdgcn_raw_buffer_store_b32(f2u(a.scale * o[r]), ro, ooff[r] * 4, 0, 0);
+                    for (int r = 0; r < 4; ++r) __builtin_amdgcn_raw_buffer_store_b32(f2u(a.scale * o[r]), ro, ooff[r] * 4, 0, CP_NT);
                 }
             };
 
@@ -1465,7 +1469,7 @@ __global__ __launch_bounds__(HT) void state_kernel_pk(StateArgs a) {
 // in LDS; after the barrier its partner (w ^ 2) reads it, so both hold the
 // whole operand and form k.h for all 64 rows themselves (the products are
 // duplicated, the step needs no second barrier). Each wave then builds Y and
-// v_new = T Y for all rows, updates its own keys, and writes the output rows
+// v_new = T Y for all rows, updates its own keys, and computes the output rows
 // of its half (rows 0..31 for the first key half, 32..63 for the second).
 // Waves 4..7 stream the tiles with ordinary buffer loads into registers and
 // write them to double-buffered LDS, each a quarter of the token rows of
@@ -1473,8 +1477,10 @@ __global__ __launch_bounds__(HT) void state_kernel_pk(StateArgs a) {
 // the v rows of the column tile, plus the coefficient block. Each holds two
 // register sets, so the loads of chunk c+2 are issued at the start of step
 // c, a full step before they are written out. Rows past the chunk end read
-// as zero.
+// as zero. The compute waves leave their output rows in an LDS tile; one
+// step later the streaming waves store them as whole 128-byte row segments.
 constexpr int KSW = 8;
+constexpr int OXP = BV + 4;        // row pitch (floats) of the output tile
 constexpr int KST = 64 * KSW;
 
 template <bool SUMMARY, bool OBF>
@@ -1488,6 +1494,7 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
     __shared__ __attribute__((aligned(16))) bf16 vt[2][BT * BV];
     __shared__ __attribute__((aligned(16))) float cb[2][CFS / 4];
     __shared__ __attribute__((aligned(16))) f16x8 hx[2][4][2][64];   // [step parity][wave][slice][lane]
+    __shared__ __attribute__((aligned(16))) float ox[OUT ? 2 : 1][OUT ? BT * OXP : 4];   // scaled output rows
 
     const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1559,8 +1566,6 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
             for (int e = 0; e < 4; ++e) { f.v[e] = fx[e]; f.v[e + 4] = fy[e]; }
             return f;
         };
-        uint32_t ooff[4];
-        for (int r = 0; r < 4; ++r) ooff[r] = (uint32_t)(4 * G + r) * tokstride + col;
         uint32_t hoff[4];
         for (int r = 0; r < 4; ++r) hoff[r] = (uint32_t)(64 * kq + 4 * G + r) * DV + col;
         lds_barrier();                              // chunk 0 and the entry state published
@@ -1645,16 +1650,7 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
                     for (int r = 0; r < 4; ++r) o[r] = bg[it][r] * qh[r];
                     PolicyH::mma(o, ldA(Pc, offT[0] + it * 16 * 128), nb0);
                     if (kq == 1) PolicyH::mma(o, ldA(Pc, offT[1] + it * 16 * 128), nb1);
-                    const int64_t rb = ((t0 + 16 * it) * H + head) * DV;
-                    const uint32_t nrow = (uint32_t)max(len - 16 * it, 0);
-                    if (OBF) {
-                        const rsrc_t ro = make_rsrc(reinterpret_cast<bf16*>(a.o) + rb, nrow * tokstride * 2);
-                        for (int r = 0; r < 4; ++r)
-                            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (bf16)(a.scale * o[r])), ro, ooff[r] * 2, 0, 0);
-                    } else {
-                        const rsrc_t ro = make_rsrc(reinterpret_cast<float*>(a.o) + rb, nrow * tokstride * 4);
-                        for (int r = 0; r < 4; ++r) __builtin_amdgcn_raw_buffer_store_b32(f2u(a.scale * o[r]), ro, ooff[r] * 4, 0, 0);
-                    }
+                    for (int r = 0; r < 4; ++r) ox[OUT ? tb : 0][(16 * it + 4 * G + r) * OXP + 16 * cg + n] = a.scale * o[r];
                 }
             }
             // after the output (q h uses the entry state): publish this wave's half of the next state operand
@@ -1751,6 +1747,30 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
                 *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(vt[buf]) + role * 1024 + 16 * lane) = d.x[12];
                 if (role == 0) *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(cb[buf]) + 16 * lane) = d.x[13];
             };
+            // output rows 16 role .. +15 of chunk co from the LDS tile: copy i
+            // covers rows 16 role + 8i .. +7, 8 lanes (16 bytes each) per row
+            auto store_out = [&](int co_) {
+                const int co = __builtin_amdgcn_readfirstlane(co_);
+                const int len = chunk_len(co);
+                const int64_t rb = ((ui.start + (int64_t)co * BT + 16 * role) * H + head) * DV + vc0;
+                const uint32_t nrow = (uint32_t)max(len - 16 * role, 0);
+                const float* src = ox[OUT ? (co & 1) : 0];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int rr = 8 * i + (lane >> 3), c4 = 4 * (lane & 7);
+                    const f32x4 x = *reinterpret_cast<const f32x4*>(&src[(16 * role + rr) * OXP + c4]);
+                    const uint32_t off = (uint32_t)rr * tokstride + c4;
+                    if (OBF) {
+                        const rsrc_t ro = make_rsrc(reinterpret_cast<bf16*>(a.o) + rb, nrow * tokstride * 2);
+                        const u32x2 w = {(uint32_t)__builtin_bit_cast(uint16_t, (bf16)x[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)x[1]) << 16),
+                                         (uint32_t)__builtin_bit_cast(uint16_t, (bf16)x[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)x[3]) << 16)};
+                        __builtin_amdgcn_raw_buffer_store_b64(w, ro, off * 2, 0, CP_NT);
+                    } else {
+                        const rsrc_t ro = make_rsrc(reinterpret_cast<float*>(a.o) + rb, nrow * tokstride * 4);
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), ro, off * 4, 0, CP_NT);
+                    }
+                }
+            };
             // two register sets: even chunks in sa, odd chunks in sb
             Set sa, sb;
             if (nch > 0) {
@@ -1760,20 +1780,24 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
             }
             lds_barrier();
             // Step c: the loads of chunk c + 2 into the set that held chunk
-            // c, then chunk c + 1 (loaded a step ago) into the LDS buffers
-            // that chunk c - 1 released. The loop is unrolled by two so that
-            // each set keeps its registers. Chunk indices are clamped, so the
-            // last steps repeat the last chunk.
+            // c, the output of chunk c - 1 (left in LDS during step c - 1),
+            // then chunk c + 1 (loaded a step ago) into the LDS buffers that
+            // chunk c - 1 released. The loop is unrolled by two so that each
+            // set keeps its registers. Chunk indices are clamped, so the last
+            // steps repeat the last chunk.
             for (int c = 0; c < nch; c += 2) {
                 load(min(c + 2, nch - 1), sa);
+                if (OUT && c > 0) store_out(c - 1);
                 store(sb, 1);
                 lds_barrier();
                 if (c + 1 < nch) {
                     load(min(c + 3, nch - 1), sb);
+                    if (OUT) store_out(c);
                     store(sa, 0);
                     lds_barrier();
                 }
             }
+            if (OUT && nch > 0) store_out(nch - 1);
         };
         if (wv == 4) stream(std::integral_constant<int, 0>{});
         else if (wv == 5) stream(std::integral_constant<int, 1>{});
