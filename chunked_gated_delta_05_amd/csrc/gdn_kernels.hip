@@ -65,6 +65,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // vector element (v[i]), __builtin_bit_cast reads element 0 with this
 // compiler.
 __device__ __forceinline__ uint32_t f2u(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float u2f(uint32_t x) { return __builtin_bit_cast(float, x); }
 
 // b^x with the hardware base-2 exponential (about 1 ulp; e^x = 2^(x log2 e))
 __device__ __forceinline__ float fpow(float x, int use_exp2) {
@@ -765,6 +766,248 @@ __global__ __launch_bounds__(64) void prep_kernel_h(PrepArgs a) {
             if (a.A && 16 * I + n < len)
                 *reinterpret_cast<f32x4*>(a.A + (e0 + (int64_t)(16 * I + n) * H) * BT + 16 * J + 4 * G) = TB[I][J];
         }
+}
+
+// ------------------------------------------------------------------ prep, fp16 per-key gate
+// One workgroup of four waves per (chunk, head). Wave w owns token rows
+// 16w .. 16w+15 and lane l the key pair 2l, 2l+1: every load of g, k and q is
+// a coalesced 512- or 256-byte row segment, and the per-key cumulative gate
+// is a scan in registers plus the column sums of the waves before. Every
+// gated form is computed once per element: the reference-row factors
+// k b^{G-G_m}, k b^{G_m-G}, q b^{G-G_m} (G_m the gate at the chunk's middle
+// row, which keeps every exponent within half the chunk's range) go to LDS as
+// fp16 operands of the L and P tiles, and the state pass's operands q b^G,
+// k b^G, k b^{G_L-G} go straight to the workspace. L and P are then plain
+// 16x16x32 MFMA tiles, and the inverse runs in LDS over the dead operand
+// tiles. 70.5 KiB of LDS: two workgroups per CU.
+constexpr int PKL = 136;   // row stride (fp16) of the 64 x 128 operand tiles: 272 bytes
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16x2(float x, float y) {
+    f16x2 h;
+    h[0] = (f16)x;
+    h[1] = (f16)y;
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+__global__ __launch_bounds__(256) void prep_kernel_pk(PrepArgs a) {
+    __shared__ __attribute__((aligned(16))) f16 ka[BT * PKL];   // k b^{G-G_m}; T (fp32 64 x 65) once L and P are done
+    __shared__ __attribute__((aligned(16))) f16 kb[BT * PKL];   // k b^{G_m-G}; then the partial products of the inverse
+    __shared__ __attribute__((aligned(16))) f16 qa[BT * PKL];   // q b^{G-G_m}
+    __shared__ __attribute__((aligned(16))) float Ls[BT * LDL];
+    __shared__ __attribute__((aligned(16))) float part[4][DK];  // column sums of g over each wave's rows
+    __shared__ __attribute__((aligned(16))) float gref[2][DK];  // G at the middle row and at the last valid row
+    __shared__ float bet[BT];
+    float* Ts = reinterpret_cast<float*>(ka);
+    float* Yb = reinterpret_cast<float*>(kb);
+
+    const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ci = blockIdx.x, head = blockIdx.y, H = a.H;
+    int u, cc;
+    chunk_of(a.um, ci, u, cc);
+    u = __builtin_amdgcn_readfirstlane(u);
+    cc = __builtin_amdgcn_readfirstlane(cc);
+    if (u < 0) return;
+    const UnitInfo ui = uniform(unit_info(a.um, u));
+    const int64_t t0 = ui.start + (int64_t)cc * BT;
+    int len = ui.len - cc * BT;
+    len = len < 0 ? 0 : (len > BT ? BT : len);
+    const int64_t ch = (int64_t)ci * H + head;
+    const int64_t e0 = t0 * H + head;              // token-head index of the chunk's first row
+    const bool has_q = a.q != nullptr;
+    const int mid = len > 0 ? (len - 1) / 2 : 0, last = len > 0 ? len - 1 : 0;
+
+    // ---- loads: buffer ranges end at the chunk's last token, so rows past it read as zero
+    const uint32_t rowk = (uint32_t)H * DK * 2, rowg = (uint32_t)H * DK * 4;
+    const rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(a.k) + e0 * DK, len > 0 ? (uint32_t)(len - 1) * rowk + DK * 2 : 0);
+    const rsrc_t rq = make_rsrc(has_q ? reinterpret_cast<const bf16*>(a.q) + e0 * DK : a.k,
+                                has_q && len > 0 ? (uint32_t)(len - 1) * rowk + DK * 2 : 0);
+    const rsrc_t rg = make_rsrc(a.g + e0 * DK, len > 0 ? (uint32_t)(len - 1) * rowg + DK * 4 : 0);
+    uint32_t kr[16], qr[16];
+    u32x2 gr[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const uint32_t row = 16 * w + r;
+        gr[r] = __builtin_amdgcn_raw_buffer_load_b64(rg, row * rowg + 8 * lane, 0, 0);
+        kr[r] = __builtin_amdgcn_raw_buffer_load_b32(rk, row * rowk + 4 * lane, 0, 0);
+        qr[r] = __builtin_amdgcn_raw_buffer_load_b32(rq, row * rowk + 4 * lane, 0, 0);
+    }
+    if (tid < BT) {
+        const float bt = tid < len ? (float)reinterpret_cast<const bf16*>(a.beta)[(t0 + tid) * H + head] : 0.0f;
+        bet[tid] = bt;
+        f16* cf = reinterpret_cast<f16*>(a.ws.cfh) + ch * (CFB / 2);
+        const int lo = lane_order(tid);
+        cf[CF_CY + lo] = (f16)bt;
+        cf[CF_CP + lo] = (f16)1.0f;
+        cf[CF_BG + lo] = (f16)1.0f;
+        cf[CF_BETA + lo] = (f16)bt;
+    }
+
+    // ---- cumulative gate down each key column
+    float gc[16][2];
+    {
+        float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            s0 += u2f(gr[r][0]);
+            s1 += u2f(gr[r][1]);
+            gc[r][0] = s0;
+            gc[r][1] = s1;
+        }
+        part[w][2 * lane] = s0;
+        part[w][2 * lane + 1] = s1;
+    }
+    __syncthreads();
+    {
+        float p0 = 0.0f, p1 = 0.0f;
+        for (int ww = 0; ww < w; ++ww) {
+            p0 += part[ww][2 * lane];
+            p1 += part[ww][2 * lane + 1];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            gc[r][0] += p0;
+            gc[r][1] += p1;
+            const int row = 16 * w + r;
+            if (row == mid) { gref[0][2 * lane] = gc[r][0]; gref[0][2 * lane + 1] = gc[r][1]; }
+            if (row == last) { gref[1][2 * lane] = gc[r][0]; gref[1][2 * lane + 1] = gc[r][1]; }
+            if (a.g_cumsum && row < len)
+                *reinterpret_cast<float2*>(a.g_cumsum + (e0 + (int64_t)row * H) * DK + 2 * lane) = float2{gc[r][0], gc[r][1]};
+        }
+    }
+    __syncthreads();
+    if (tid < DK) {
+        const float gl = gref[1][tid];
+        a.ws.gamL[ch * DK + tid] = gl;
+        reinterpret_cast<float*>(a.ws.cfh)[ch * (CFB / 4) + CF_GL + tid] = fpow(gl, a.use_exp2);
+    }
+
+    // ---- gated forms: reference-row operands to LDS, state-pass operands out
+    {
+        const float m0 = gref[0][2 * lane], m1 = gref[0][2 * lane + 1];
+        const float l0 = gref[1][2 * lane], l1 = gref[1][2 * lane + 1];
+        const int cp = op_pos(2 * lane);
+        uint32_t* qg = reinterpret_cast<uint32_t*>(reinterpret_cast<f16*>(a.ws.qg) + ch * (BT * DK) + cp);
+        uint32_t* kd = reinterpret_cast<uint32_t*>(reinterpret_cast<f16*>(a.ws.kd) + ch * (BT * DK) + cp);
+        uint32_t* kg = reinterpret_cast<uint32_t*>(reinterpret_cast<f16*>(a.ws.kg) + ch * (BT * DK) + cp);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = 16 * w + r;
+            const float k0 = __builtin_bit_cast(float, kr[r] << 16), k1 = __builtin_bit_cast(float, kr[r] & 0xffff0000u);
+            const float q0 = __builtin_bit_cast(float, qr[r] << 16), q1 = __builtin_bit_cast(float, qr[r] & 0xffff0000u);
+            const float x0 = gc[r][0], x1 = gc[r][1];
+            const float a0 = fpow(x0 - m0, a.use_exp2), a1 = fpow(x1 - m1, a.use_exp2);
+            const float b0 = fpow(m0 - x0, a.use_exp2), b1 = fpow(m1 - x1, a.use_exp2);
+            *reinterpret_cast<uint32_t*>(&ka[row * PKL + 2 * lane]) = pack_f16x2(k0 * a0, k1 * a1);
+            *reinterpret_cast<uint32_t*>(&kb[row * PKL + 2 * lane]) = pack_f16x2(k0 * b0, k1 * b1);
+            *reinterpret_cast<uint32_t*>(&qa[row * PKL + 2 * lane]) = pack_f16x2(q0 * a0, q1 * a1);
+            const float d0 = fpow(x0, a.use_exp2), d1 = fpow(x1, a.use_exp2);
+            const float c0 = fpow(l0 - x0, a.use_exp2), c1 = fpow(l1 - x1, a.use_exp2);
+            if (has_q) qg[row * (DK / 2)] = pack_f16x2(q0 * d0, q1 * d1);
+            kd[row * (DK / 2)] = pack_f16x2(k0 * d0, k1 * d1);
+            kg[row * (DK / 2)] = pack_f16x2(k0 * c0, k1 * c1);
+        }
+    }
+    __syncthreads();
+
+    // ---- L (strictly lower, 10 tiles) and P (lower incl. diagonal, 10 tiles)
+    // on MFMA, 20 tiles over 4 waves; the 6 zero tiles of P above the diagonal
+    f16* Pw = reinterpret_cast<f16*>(a.ws.P) + ch * (BT * BT);
+    for (int t = w; t < 26; t += 4) {
+        if (t >= 20) {
+            if (!has_q) continue;
+            const int z = t - 20;                                 // (it, jt) with it < jt
+            const int it = z < 3 ? 0 : (z < 5 ? 1 : 2);
+            const int jt = z < 3 ? z + 1 : (z < 5 ? z - 1 : 3);
+            *reinterpret_cast<u32x2*>(Pw + (16 * it + n) * BT + op_pos(16 * jt + 4 * G)) = u32x2{0u, 0u};
+            continue;
+        }
+        const bool isL = t < 10;
+        if (!isL && !has_q) continue;
+        const int tt = isL ? t : t - 10;
+        const int it = tt < 1 ? 0 : tt < 3 ? 1 : tt < 6 ? 2 : 3;
+        const int jt = tt - (it * (it + 1)) / 2;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) {
+            const int col = 32 * kk + 8 * G;
+            if (isL) PolicyH::mma(acc, PolicyH::ld(&ka[(16 * it + n) * PKL + col]), PolicyH::ld(&kb[(16 * jt + n) * PKL + col]));
+            else PolicyH::mma(acc, PolicyH::ld(&kb[(16 * jt + n) * PKL + col]), PolicyH::ld(&qa[(16 * it + n) * PKL + col]));
+        }
+        if (isL) {
+            // acc[r]: row i = 16 it + 4G + r against column j = 16 jt + n
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * it + 4 * G + r, j = 16 * jt + n;
+                Ls[i * LDL + j] = j < i ? bet[i] * acc[r] : 0.0f;
+            }
+        } else {
+            // acc[r]: row i = 16 it + n against column j = 16 jt + 4G + r
+            const int i = 16 * it + n;
+            float x[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[r] = 16 * jt + 4 * G + r <= i ? acc[r] : 0.0f;
+            PolicyH::st4(Pw + i * BT + op_pos(16 * jt + 4 * G), x);
+        }
+    }
+    __syncthreads();
+
+    // ---- T = (I + L)^{-1}: 16 x 16 diagonal blocks by substitution (wave 0,
+    // lane = block * 16 + column), then the off-diagonal blocks by distance
+    if (w == 0) {
+        const int bk = lane >> 4, c = lane & 15, o = 16 * bk;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float s = 0.0f;
+#pragma unroll
+            for (int j = 0; j < i; ++j) s += Ls[(o + i) * LDL + o + j] * x[j];
+            x[i] = i == c ? 1.0f : (i > c ? -s : 0.0f);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Ts[(o + i) * LDL + o + c] = x[i];
+    } else {
+        for (int e = tid - 64; e < 6 * 256; e += 192) {
+            const int blk = e >> 8, rr = (e >> 4) & 15, cc2 = e & 15;
+            const int I = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+            const int J = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+            Ts[(16 * I + rr) * LDL + 16 * J + cc2] = 0.0f;
+        }
+    }
+    __syncthreads();
+    for (int d = 1; d < 4; ++d) {
+        const int nb = 4 - d;
+        for (int e = tid; e < nb * 256; e += 256) {
+            const int bi = e >> 8, rr = (e >> 4) & 15, cc2 = e & 15;
+            const int I = d + bi, J = bi;
+            float s = 0.0f;
+            for (int K2 = J; K2 < I; ++K2)
+                for (int m = 0; m < 16; ++m)
+                    s += Ls[(16 * I + rr) * LDL + 16 * K2 + m] * Ts[(16 * K2 + m) * LDL + 16 * J + cc2];
+            Yb[(bi * 16 + rr) * 17 + cc2] = s;
+        }
+        __syncthreads();
+        for (int e = tid; e < nb * 256; e += 256) {
+            const int bi = e >> 8, rr = (e >> 4) & 15, cc2 = e & 15;
+            const int I = d + bi, J = bi;
+            float s = 0.0f;
+            for (int m = 0; m < 16; ++m) s += Ts[(16 * I + rr) * LDL + 16 * I + m] * Yb[(bi * 16 + m) * 17 + cc2];
+            Ts[(16 * I + rr) * LDL + 16 * J + cc2] = -s;
+        }
+        __syncthreads();
+    }
+
+    // ---- T out as fp16 operands (op_pos columns), optional token-major fp32 A slot
+    f16* Tw = reinterpret_cast<f16*>(a.ws.Tm) + ch * (BT * BT);
+    for (int e = tid; e < BT * BT / 4; e += 256) {
+        const int r = e / (BT / 4), c4 = (e % (BT / 4)) * 4;
+        f32x4 x;
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) x[q2] = Ts[r * LDL + c4 + q2];
+        PolicyH::f32_to_op4(Tw + r * BT + op_pos(c4), x);
+        if (a.A && r < len) *reinterpret_cast<f32x4*>(a.A + (e0 + (int64_t)r * H) * BT + c4) = x;
+    }
 }
 
 // ------------------------------------------------------------------ state pass
@@ -1886,7 +2129,7 @@ hipError_t launch_prep(const Problem& p, const Workspace& ws, const void* k, con
     a.ws = ws; a.g_cumsum = g_cumsum_slot; a.A = A_slot;
     dim3 grid(p.um.n_chunks, p.H), block(256);
     if (p.dtype == 1) {
-        if (p.per_key) hipLaunchKernelGGL((prep_kernel<PolicyH, true>), grid, block, 0, s, a);
+        if (p.per_key) hipLaunchKernelGGL(prep_kernel_pk, grid, block, 0, s, a);
         else hipLaunchKernelGGL(prep_kernel_h, dim3(p.H * p.um.n_chunks), dim3(64), 0, s, a);
     } else {
         if (p.per_key) hipLaunchKernelGGL((prep_kernel<PolicyF, true>), grid, block, 0, s, a);

@@ -138,6 +138,41 @@ def test_prep_slots_inverse_residual():
             assert np.abs(res).max() < 1e-5, np.abs(res).max()
 
 
+def test_prep_slots_per_key():
+    # per-key gate (log2 units): g_cumsum against the fp64 per-key prefix sum,
+    # (I + L) T = I with L_ij = beta_i sum_d k_id k_jd 2^{G_id - G_jd} rebuilt
+    # in fp64, and the chunk entry states against the oracle
+    T, H = 150, 2
+    print(f"per-key slots T={T} H={H}", flush=True)
+    d = to_dev(W.generate(small(B=1, T=T, H=H, per_key=True, use_exp2=True, gate_coef=0.05), 23))
+    _, _, ex = run_gpu(d, want_A=True, want_g_cumsum=True, want_h=True)
+    A = np32(ex["A"]).astype(np.float64)            # [T, H, 64]
+    gc = np32(ex["g_cumsum"]).astype(np.float64)[0]  # [T, H, K]
+    k = np32(d["k"][0]).astype(np.float64)
+    beta = np32(d["beta"][0]).astype(np.float64)
+    g = np32(d["g"][0]).astype(np.float64)
+    for h in range(H):
+        for c0 in range(0, T, 64):
+            n = min(64, T - c0)
+            G = np.cumsum(g[c0:c0 + n, h], axis=0)                     # [n, K]
+            np.testing.assert_allclose(gc[c0:c0 + n, h], G, rtol=1e-5, atol=1e-5)
+            kk = k[c0:c0 + n, h]
+            D = np.exp2(G[:, None, :] - G[None, :, :])                  # [i, j, K]
+            bt = beta[c0:c0 + n, h, None]
+            L = np.tril(bt * np.einsum("id,jd,ijd->ij", kk, kk, D), -1)
+            Tm = A[c0:c0 + n, h, :n]
+            res = (np.eye(n) + L) @ Tm - np.eye(n)
+            # the gated keys enter the L product as fp16 operands (two
+            # roundings of 2^-11 relative each), so |L_gpu - L| <= 2.01 2^-11
+            # L_abs elementwise and the residual (L - L_gpu) T is bounded by
+            # that times |T|
+            L_abs = np.tril(bt * np.einsum("id,jd,ijd->ij", np.abs(kk), np.abs(kk), D), -1)
+            bound = 2.01 * 2.0 ** -11 * (L_abs @ np.abs(Tm)) + 1e-5
+            assert (np.abs(res) <= bound).all(), float((np.abs(res) / bound).max())
+    r = run_oracle(d, chunk_states=True)
+    assert_close(np32(ex["h"]), r["chunk_states"], TOL["bf16"], "per-key chunk entry states")
+
+
 # ------------------------------------------------------------------ exact cases
 def test_beta_zero_gives_exact_zero():
     d = to_dev(W.generate(small(B=2, T=190, H=2), 31))
