@@ -2050,11 +2050,15 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
 }
 
 // ------------------------------------------------------------------ merge
-constexpr int MC = 8;   // state columns per merge workgroup
+constexpr int MC = 8;         // state columns per merge workgroup
+constexpr int MLD = DK + 4;   // LDS row stride of M (16-byte rows, conflict-free column reads)
 
+// One workgroup per (b, head, 8 state columns): S = M_s S + S_ext[s] over the
+// segments in order. M_s (64 KiB) arrives as 16-byte loads, and the next
+// segment's M and S_ext are in flight during the current product.
 __global__ __launch_bounds__(256) void merge_kernel(int H, int n_seg, const float* S_ext, const float* M,
                                                      const float* S0, float* S_init, float* S_final) {
-    __shared__ float Ms[DK * (DK + 1)];
+    __shared__ __attribute__((aligned(16))) float Ms[DK * MLD];
     __shared__ float Sc[DK * MC];
     const int tid = threadIdx.x, c = tid % MC, rbase = tid / MC;   // rows rbase + 32 i
     const int col0 = blockIdx.x * MC, bh = blockIdx.y, b = bh / H, head = bh % H;
@@ -2062,20 +2066,37 @@ __global__ __launch_bounds__(256) void merge_kernel(int H, int n_seg, const floa
         const int r = rbase + 32 * i;
         Sc[r * MC + c] = S0 ? S0[((int64_t)bh * DK + r) * DV + col0 + c] : 0.0f;
     }
+    f32x4 mr[16];
+    float er[4];
+    auto load = [&](int s) {
+        const int64_t us = ((int64_t)b * n_seg + s) * H + head;
+        const f32x4* src = reinterpret_cast<const f32x4*>(M + us * DK * DK);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mr[j] = src[tid + 256 * j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) er[i] = S_ext[(us * DK + rbase + 32 * i) * DV + col0 + c];
+    };
+    if (n_seg > 0) load(0);
     for (int s = 0; s < n_seg; ++s) {
         const int64_t us = ((int64_t)b * n_seg + s) * H + head;
-        __syncthreads();
+        __syncthreads();                          // the previous product has read Ms and written Sc
         for (int i = 0; i < 4; ++i) {
             const int r = rbase + 32 * i;
             S_init[(us * DK + r) * DV + col0 + c] = Sc[r * MC + c];
         }
-        for (int e = tid; e < DK * DK; e += 256) Ms[(e / DK) * (DK + 1) + e % DK] = M[us * DK * DK + e];
-        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int e = 4 * (tid + 256 * j);
+            *reinterpret_cast<f32x4*>(&Ms[(e / DK) * MLD + e % DK]) = mr[j];
+        }
         float acc[4];
-        for (int i = 0; i < 4; ++i) acc[i] = S_ext[(us * DK + rbase + 32 * i) * DV + col0 + c];
+        for (int i = 0; i < 4; ++i) acc[i] = er[i];
+        if (s + 1 < n_seg) load(s + 1);
+        __syncthreads();
         for (int m = 0; m < DK; ++m) {
             const float sv = Sc[m * MC + c];
-            for (int i = 0; i < 4; ++i) acc[i] += Ms[(rbase + 32 * i) * (DK + 1) + m] * sv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] += Ms[(rbase + 32 * i) * MLD + m] * sv;
         }
         __syncthreads();
         for (int i = 0; i < 4; ++i) Sc[(rbase + 32 * i) * MC + c] = acc[i];
