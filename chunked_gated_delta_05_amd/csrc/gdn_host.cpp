@@ -48,6 +48,7 @@ gdn_status validate(const gdn_desc* d, gdn::Problem* p) {
     if (!isfinite(d->scale)) return GDN_ERR_INVALID;
     const int64_t total = int64_t(d->B) * d->T;
     if (total * d->H * DK > kMaxElems) return GDN_ERR_INVALID;
+    p->reorder = 0;
     gdn::UnitMap um;
     memset(&um, 0, sizeof(um));
     um.T = d->T;
@@ -84,6 +85,13 @@ gdn_status validate(const gdn_desc* d, gdn::Problem* p) {
         um.offsets = d->offsets_dev;
         um.chunk_offsets = d->chunk_offsets_dev;
         um.chunk_indices = d->chunk_indices_dev;
+        // the state passes launch the units longest first unless they already
+        // come in non-increasing chunk count
+        for (int32_t u = 1; u < d->n_units && !p->reorder; ++u) {
+            const int64_t a = (int64_t(d->offsets_host[u]) - d->offsets_host[u - 1] + BT - 1) / BT;
+            const int64_t b = (int64_t(d->offsets_host[u + 1]) - d->offsets_host[u] + BT - 1) / BT;
+            p->reorder = b > a;
+        }
     }
     p->H = d->H;
     p->dtype = d->dtype;

@@ -43,6 +43,8 @@ struct Workspace {
     // bf16 inputs only
     void* cfh;       // [n_chunks][H][1 KiB]  per-row coefficient block of the fp16 state pass
                      // (fp32 rows for the scalar gate, fp16 rows + fp32 gates per key)
+    // packed units only
+    int32_t* order;  // [n_units]  units in state-pass launch order (most chunks first)
 };
 
 struct Problem {
@@ -53,6 +55,7 @@ struct Problem {
     int32_t use_exp2;
     float scale;
     UnitMap um;
+    int32_t reorder;    // packed units out of longest-first order: the state passes reorder them
 };
 
 size_t workspace_bytes(const Problem& p, Workspace* ws, char* base);

@@ -1031,6 +1031,7 @@ struct StateArgs {
     int tile0;       // first column tile (summary mode: 0, or the first M tile)
     float* S_ext;
     float* M;
+    const int32_t* order;   // units in launch order (longest first), or NULL: natural order
 };
 
 // Work split of the 8 waves of a state-pass workgroup (one 32-column value
@@ -1073,7 +1074,9 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
     const int tile = slot % a.ntiles + a.tile0;
     const int pair = (slot / a.ntiles) * 8 + xcd;
     if (pair >= a.n_pairs) return;
-    const int u = pair / H, head = pair - u * H;
+    const int pu = pair / H, head = pair - pu * H;
+    const int u = a.order ? a.order[pu] : pu;
+    if ((unsigned)u >= (unsigned)a.um.n_units) return;
     const UnitInfo ui = unit_info(a.um, u);
     const int c0 = tile * BV;                       // column of [S_ext | M] or of V
     const bool mcols = SUMMARY && c0 >= DV;         // transfer-map columns: v = 0, start at I
@@ -1367,7 +1370,9 @@ __global__ __launch_bounds__(HT) void state_kernel_pk(StateArgs a) {
     const int tile = slot % a.ntiles + a.tile0;
     const int pair = (slot / a.ntiles) * 8 + xcd;
     if (pair >= a.n_pairs) return;
-    const int u = pair / H, head = pair - u * H;
+    const int pu = pair / H, head = pair - pu * H;
+    const int u = a.order ? a.order[pu] : pu;
+    if ((unsigned)u >= (unsigned)a.um.n_units) return;
     const UnitInfo ui = uniform(unit_info(a.um, u));
     const int c0 = tile * BV;
     const bool mcols = SUMMARY && c0 >= DV;         // transfer-map columns: v = 0, start at I
@@ -1746,7 +1751,9 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
     const int tile = slot % a.ntiles + a.tile0;
     const int pair = (slot / a.ntiles) * 8 + xcd;
     if (pair >= a.n_pairs) return;
-    const int u = pair / H, head = pair - u * H;
+    const int pu = pair / H, head = pair - pu * H;
+    const int u = a.order ? a.order[pu] : pu;
+    if ((unsigned)u >= (unsigned)a.um.n_units) return;
     const UnitInfo ui = uniform(unit_info(a.um, u));
     const int c0 = tile * BV;
     const bool mcols = SUMMARY && c0 >= DV;         // transfer-map columns: v = 0, start at I
@@ -2109,6 +2116,36 @@ __global__ __launch_bounds__(256) void merge_kernel(int H, int n_seg, const floa
         }
 }
 
+// ------------------------------------------------------------------ unit order
+// Units of unequal length (packed documents, ragged segments) run their state
+// passes longest first: workgroups are dispatched in grid order, so a long
+// unit that starts last would stretch the tail of the pass. The rank of unit
+// u is the number of units with more chunks, or as many chunks and a smaller
+// index (a permutation); order[rank] = u.
+constexpr int ORD_T = 1024;
+constexpr int ORD_MAX = 2048;    // more units than this keep their natural order
+
+__global__ __launch_bounds__(ORD_T) void unit_order_kernel(UnitMap um, int32_t* order) {
+    __shared__ int32_t nch[ORD_T];
+    const int n = um.n_units, tid = threadIdx.x;
+    for (int u0 = 0; u0 < n; u0 += ORD_T) {
+        const int u = u0 + tid;
+        const int mine = u < n ? unit_info(um, u).nch : 0;
+        int rank = 0;
+        for (int v0 = 0; v0 < n; v0 += ORD_T) {
+            __syncthreads();
+            nch[tid] = v0 + tid < n ? unit_info(um, v0 + tid).nch : -1;
+            __syncthreads();
+            const int m = min(ORD_T, n - v0);
+            for (int j = 0; j < m; ++j) {
+                const int x = nch[j];
+                rank += (x > mine) || (x == mine && v0 + j < u);
+            }
+        }
+        if (u < n) order[rank] = u;
+    }
+}
+
 // ------------------------------------------------------------------ launchers
 static int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
@@ -2128,6 +2165,8 @@ size_t workspace_bytes(const Problem& p, Workspace* ws, char* base) {
         ol = take(nch * DK * 4);
     }
     const int64_t ocf = p.dtype == 1 ? take(nch * (p.per_key ? CFB : CFS)) : 0;
+    const bool ordered = p.reorder && !p.um.dense && p.um.n_units > 1 && p.um.n_units <= ORD_MAX;
+    const int64_t oor = ordered ? take((int64_t)p.um.n_units * 4) : 0;
     if (ws && base) {
         ws->Tm = base + oT;
         ws->P = base + oP;
@@ -2137,6 +2176,7 @@ size_t workspace_bytes(const Problem& p, Workspace* ws, char* base) {
         ws->kg = p.per_key ? base + ok : nullptr;
         ws->gamL = p.per_key ? reinterpret_cast<float*>(base + ol) : nullptr;
         ws->cfh = p.dtype == 1 ? base + ocf : nullptr;
+        ws->order = ordered ? reinterpret_cast<int32_t*>(base + oor) : nullptr;
     }
     return (size_t)(off > 0 ? off : 256);
 }
@@ -2209,6 +2249,11 @@ hipError_t launch_state(const Problem& p, const Workspace& ws, const void* q, co
     a.n_pairs = p.um.n_units * p.H;
     a.S_ext = S_ext; a.M = M;
     a.ntiles = 0; a.tile0 = 0;
+    a.order = nullptr;
+    if (ws.order && a.n_pairs > 0) {
+        hipLaunchKernelGGL(unit_order_kernel, dim3(1), dim3(ORD_T), 0, s, p.um, ws.order);
+        a.order = ws.order;
+    }
     if (p.dtype == 1) {
         if (p.per_key) launch_state_h<true>(summary, a, want_ext, want_M, s);
         else launch_state_h<false>(summary, a, want_ext, want_M, s);

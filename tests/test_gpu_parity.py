@@ -256,6 +256,28 @@ def test_varlen_packed_matches_oracle_and_separate_runs():
         assert torch.equal(f1[0], fin[i])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_varlen_increasing_lengths_with_entry_states(dtype):
+    # documents in increasing length: the state passes launch them in the
+    # reverse order, and every document's output, chunk states and final
+    # state must still land in its own place
+    lens = [3, 70, 129, 300]
+    cu = W.cu_from_lengths(lens)
+    T, H = cu[-1], 2
+    print(f"varlen increasing lengths {dtype}", flush=True)
+    base = W.generate(small(B=1, T=T, H=H, dtype=dtype), 53)
+    d = {n: base[n][0].contiguous().to(DEV) for n in ("q", "k", "v", "g", "beta")}
+    d.update(scale=base["scale"], offsets=cu,
+             workload=small(B=1, T=T, H=H, dtype=dtype, layout="TND", n_docs=len(lens)))
+    S0 = (torch.randn(len(lens), H, 128, 128, generator=torch.Generator().manual_seed(5)) * 0.3).to(DEV)
+    o, fin, ex = run_gpu(d, initial_state=S0, output_final_state=True, want_h=True)
+    r = run_oracle(d, S0=np32(S0).astype(np.float64), chunk_states=True)
+    tol = TOL[dtype]
+    assert_close(np32(o), r["o"], tol, "packed o")
+    assert_close(np32(fin), r["final"], tol, "packed final")
+    assert_close(np32(ex["h"]), r["chunk_states"], tol, "packed chunk entry states")
+
+
 # ------------------------------------------------------------------ per-key + split
 @pytest.mark.parametrize("seg", [[0, 128, 256], [0, 100, 190, 256], [0, 64, 65, 200, 256]])
 def test_split_equals_unsplit_slow_decay(seg):
