@@ -268,6 +268,18 @@ __device__ __forceinline__ int swz16(int r) {
 }
 __device__ __forceinline__ int swz8(int r) { return r & 7; }
 
+// k and q tiles of the scalar-gate state pass (rows of 16 granules): row r
+// keeps logical granule g at g ^ swzk(r), and every odd granule with its two
+// 8-byte halves swapped. swzk is a bijection on any 8 consecutive rows (the
+// 16-byte row-fragment reads stay conflict free), and on every aligned group
+// of 4 rows its bits 0 and 2 take all four values, so a transposed read -
+// 4 rows x 4 granules, 8 bytes each, half of them in the swapped halves -
+// meets all 32 banks once. A row-fragment read of granule 4s + G lands in
+// lanes of group G, so only odd groups see the swapped halves; the state
+// operand those reads pair with swaps the same halves on the same lanes,
+// which keeps every product's key pairing.
+__device__ __forceinline__ int swzk(int r) { return (r & 1) | ((r & 2) << 1) | ((r & 4) >> 1) | (r & 8); }
+
 // Per-chunk coefficient block of the per-key fp16 state pass (CFB bytes,
 // written by the preparation): four 64-entry fp16 rows in lane order (entry
 // 16G + 4it + r belongs to token row 16it + 4G + r) - beta, 1, 1, beta - then
@@ -1786,18 +1798,29 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
             for (int e = 0; e < 4; ++e) { f.v[e] = (f16)x[e]; f.v[e + 4] = (f16)y[e]; }
             return f;
         };
+        // the state operand, halves swapped on odd lane groups (the k and q tile layout)
+        const bool hswap = G & 1;
+        auto pack_state = [&](const f32x4& x, const f32x4& y) {
+            const F f = pack(x, y);
+            const u32x4 w = __builtin_bit_cast(u32x4, f.v);
+            const u32x4 sw = {w[2], w[3], w[0], w[1]};
+            F r;
+            r.v = __builtin_bit_cast(f16x8, hswap ? sw : w);
+            return r;
+        };
         F hb[4];                                     // operand slices 0..3 (2 kq, 2 kq + 1 are this wave's)
         for (int j2 = 0; j2 < 2; ++j2) {
-            hb[2 * kq + j2] = pack(h[2 * j2], h[2 * j2 + 1]);
+            hb[2 * kq + j2] = pack_state(h[2 * j2], h[2 * j2 + 1]);
             hx[0][wv][j2][lane] = hb[2 * kq + j2].v;
         }
         // per-lane LDS byte offsets
         int offA[4], offG[2];
-        for (int s2 = 0; s2 < 4; ++s2) offA[s2] = n * 256 + (((4 * s2 + G) ^ swz16(n)) << 4);   // row n, granule 4 s2 + G
+        for (int s2 = 0; s2 < 4; ++s2) offA[s2] = n * 256 + (((4 * s2 + G) ^ swzk(n)) << 4);   // row n, granule 4 s2 + G
         for (int j2 = 0; j2 < 2; ++j2) {
             const int s2 = 2 * kq + j2, rt = 4 * G + (n >> 2);                  // transposed read row
-            offG[j2] = rt * 256 + (((4 * s2 + (n & 3)) ^ swz16(rt)) << 4);
+            offG[j2] = rt * 256 + (((4 * s2 + (n & 3)) ^ swzk(rt)) << 4);
         }
+        const int hlo = (n & 1) * 8;                 // byte offset of logical half 0 in granule 4 s2 + (n & 3)
         int offT[2];
         for (int kk = 0; kk < 2; ++kk) offT[kk] = n * 128 + (((4 * kk + G) ^ swz8(n)) << 4);
         const int offV = (4 * G + (n >> 2)) * (BV * 2) + 32 * cg + 8 * (n & 3);
@@ -1808,7 +1831,7 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
         };
         // k^T fragment of key tile 4 kq + j (keys 16 j + n of the wave's half)
         auto ldKT = [&](const f16* t, int j, int kk) {
-            const char* p = reinterpret_cast<const char*>(t) + offG[j >> 1] + (j & 1) * 8 + kk * 32 * 256;
+            const char* p = reinterpret_cast<const char*>(t) + offG[j >> 1] + ((j & 1) * 8 ^ hlo) + kk * 32 * 256;
             s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, p));
             s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, p + 16 * 256));
             f16x4 fx = __builtin_bit_cast(f16x4, x), fy = __builtin_bit_cast(f16x4, y);
@@ -1905,7 +1928,7 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
             }
             // after the output (q h uses the entry state): publish this wave's half of the next state operand
             for (int j2 = 0; j2 < 2; ++j2) {
-                hb[2 * kq + j2] = pack(h[2 * j2], h[2 * j2 + 1]);
+                hb[2 * kq + j2] = pack_state(h[2 * j2], h[2 * j2 + 1]);
                 hx[tq ^ 1][wv][j2][lane] = hb[2 * kq + j2].v;
             }
             lds_barrier();                          // chunk c consumed, chunk c+1 and the state operand published
@@ -1981,8 +2004,8 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
                     for (int ii = 0; ii < 2; ++ii) {
                         const int row = 8 * (2 * role + ii) + rl, g0 = 4 * s + 2 * m;
                         const u32x4 A = bf16x8_to_f16x8(d.x[4 * kq + 2 * ii]), B = bf16x8_to_f16x8(d.x[4 * kq + 2 * ii + 1]);
-                        *reinterpret_cast<u32x4*>(dx + row * 256 + ((g0 ^ swz16(row)) << 4)) = u32x4{A[0], A[1], B[0], B[1]};
-                        *reinterpret_cast<u32x4*>(dx + row * 256 + (((g0 + 1) ^ swz16(row)) << 4)) = u32x4{A[2], A[3], B[2], B[3]};
+                        *reinterpret_cast<u32x4*>(dx + row * 256 + ((g0 ^ swzk(row)) << 4)) = u32x4{A[0], A[1], B[0], B[1]};
+                        *reinterpret_cast<u32x4*>(dx + row * 256 + (((g0 + 1) ^ swzk(row)) << 4)) = u32x4{B[2], B[3], A[2], A[3]};
                     }
                 }
 #pragma unroll
