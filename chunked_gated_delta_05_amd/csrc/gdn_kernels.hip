@@ -287,11 +287,12 @@ __device__ __forceinline__ int swzk(int r) { return (r & 1) | ((r & 2) << 1) | (
 constexpr int CFB = 1024;
 constexpr int CF_CY = 0, CF_CP = 64, CF_BG = 128, CF_BETA = 192;   // fp16 offsets
 constexpr int CF_GL = 128;                                          // fp32 offset
-// The scalar gate's block (CFS bytes) holds the same four rows in fp32
-// (float offsets below, same lane order); b^{G_L} is the b^G entry of the
-// chunk's last valid token.
+// The scalar gate's block (CFS bytes) holds three fp32 rows in the same lane
+// order - b^{G_L - G}, b^G, beta - at the float offsets below (the first 64
+// floats are not used); b^{G_L} is the b^G entry of the chunk's last valid
+// token.
 constexpr int CFS = 1024;
-constexpr int CS_CY = 0, CS_CP = 64, CS_BG = 128, CS_BETA = 192;
+constexpr int CS_CP = 64, CS_BG = 128, CS_BETA = 192;
 __device__ __forceinline__ int lane_order(int t) { return 16 * ((t >> 2) & 3) + 4 * (t >> 4) + (t & 3); }
 
 // raw buffer resource over [base, base + bytes): accesses outside read as zero
@@ -665,7 +666,6 @@ __global__ __launch_bounds__(64) void prep_kernel_h(PrepArgs a) {
         const float bG = fpow(x, a.use_exp2), bLG = fpow(xl - x, a.use_exp2);
         float* cf = reinterpret_cast<float*>(a.ws.cfh) + ch * (CFS / 4);
         const int lo = lane_order(lane);
-        cf[CS_CY + lo] = bt * bG;
         cf[CS_CP + lo] = bLG;
         cf[CS_BG + lo] = bG;
         cf[CS_BETA + lo] = bt;
@@ -698,7 +698,8 @@ __global__ __launch_bounds__(64) void prep_kernel_h(PrepArgs a) {
         for (int K = 0; K < 4; ++K) {
             f16* pdst = Pw + (16 * I + n) * BT + op_pos(16 * K + 4 * G);
             if (K > I) {
-                if (has_q) *reinterpret_cast<u32x2*>(pdst) = u32x2{0u, 0u};
+                // zero blocks; rows 0..31 of the state pass read columns 0..31 only
+                if (has_q && (I >= 2 || K < 2)) *reinterpret_cast<u32x2*>(pdst) = u32x2{0u, 0u};
                 continue;
             }
             f32x4 gk = {0.f, 0.f, 0.f, 0.f}, gq = gk;
@@ -774,7 +775,8 @@ __global__ __launch_bounds__(64) void prep_kernel_h(PrepArgs a) {
     for (int I = 0; I < 4; ++I)
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
-            *reinterpret_cast<u32x2*>(Tw + (16 * I + n) * BT + op_pos(16 * J + 4 * G)) = f32x4_to_f16x4(TB[I][J]);
+            if (I >= 2 || J < 2)   // rows 0..31 of the state pass read columns 0..31 only
+                *reinterpret_cast<u32x2*>(Tw + (16 * I + n) * BT + op_pos(16 * J + 4 * G)) = f32x4_to_f16x4(TB[I][J]);
             if (a.A && 16 * I + n < len)
                 *reinterpret_cast<f32x4*>(a.A + (e0 + (int64_t)(16 * I + n) * H) * BT + 16 * J + 4 * G) = TB[I][J];
         }
@@ -1862,11 +1864,10 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
             for (int j2 = 0; j2 < 2; ++j2) hb[2 * (1 - kq) + j2].v = hx[tq][partner][j2][lane];
             // per-row coefficients: lane G holds rows 16 it + 4G + r at [16G + 4it + r]
             const float* cf = cb[tb];
-            f32x4 cy[4], cpf[4], bg[4], bt[4];
+            f32x4 cpf[4], bg[4], bt[4];
             for (int it = 0; it < 4; ++it) {
-                cy[it] = *reinterpret_cast<const f32x4*>(&cf[CS_CY + 16 * G + 4 * it]);
                 cpf[it] = *reinterpret_cast<const f32x4*>(&cf[CS_CP + 16 * G + 4 * it]);
-                if (OUT) bg[it] = *reinterpret_cast<const f32x4*>(&cf[CS_BG + 16 * G + 4 * it]);
+                bg[it] = *reinterpret_cast<const f32x4*>(&cf[CS_BG + 16 * G + 4 * it]);
                 bt[it] = *reinterpret_cast<const f32x4*>(&cf[CS_BETA + 16 * G + 4 * it]);
             }
             const float eL = cf[CS_BG + lane_order(len > 0 ? len - 1 : 0)];
@@ -1880,12 +1881,12 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
             // lower triangular, so v_new of rows 0..31 needs Y of rows 0..31
             // only, and the state update from the first 32 tokens can run
             // while the k.h products of the second half complete.
-            auto khY = [&](int it, f32x4& y) {           // Y = beta v - beta b^G (k h), row tile it
+            auto khY = [&](int it, f32x4& y) {           // Y = beta (v - b^G (k h)), row tile it
                 f32x4 kh = {0.f, 0.f, 0.f, 0.f};
                 for (int s2 = 0; s2 < 4; ++s2) PolicyH::mma(kh, ldA(K, offA[s2] + it * 16 * 256), hb[s2]);
                 for (int r = 0; r < 4; ++r) {
                     const float vv = __builtin_bit_cast(float, (uint32_t)(uint16_t)vraw[it][r] << 16);
-                    y[r] = __builtin_fmaf(bt[it][r], vv, -cy[it][r] * kh[r]);
+                    y[r] = bt[it][r] * __builtin_fmaf(-bg[it][r], kh[r], vv);
                 }
             };
             f32x4 y[4], vn[4], vp[4];
@@ -1983,9 +1984,13 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
                 for (int tp = 0; tp < (OUT ? 2 : 1); ++tp) {
                     const rsrc_t rt = make_rsrc(reinterpret_cast<const f16*>(tp ? a.ws.P : a.ws.Tm) + ch * (BT * BT), BT * BT * 2);
 #pragma unroll
-                    for (int ii = 0; ii < 2; ++ii)
+                    for (int ii = 0; ii < 2; ++ii) {
+                        // rows 0..31 use operand positions 0..31 only: the pieces
+                        // at 32..63 (zero blocks, never written) are out of range
+                        const uint32_t off = (8 * (2 * role + ii) + (lane >> 3)) * 128 + 16 * (lane & 7);
                         d.x[8 + 2 * tp + ii] = __builtin_amdgcn_raw_buffer_load_b128(
-                            rt, (8 * (2 * role + ii) + (lane >> 3)) * 128 + 16 * (lane & 7), 0, 0);
+                            rt, role < 2 && (lane & 7) >= 4 ? 0x40000000u : off, 0, 0);
+                    }
                 }
                 // v rows 16 role + l/4, 16-byte piece l%4 of the tile's 32 columns
                 const rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(a.v) + (t0 * H + head) * DV + vc0,
