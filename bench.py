@@ -53,18 +53,21 @@ def kernel_source_hash() -> str:
 def byte_model(w, n_chunk_heads: int, o_bytes: int) -> dict:
     """Algorithmic bytes per launch: what each kernel must read and write by
     its contract (every byte once), summed over the chunk-heads it processes.
-    Scalar gate, per chunk-head of 64 tokens, es = input element size, ps =
-    prepared operand size (fp16 for bf16 inputs, fp32 for fp32 inputs):
-      prep : q, k (2*64*128*es), g (64*4), beta (64*es)
-             -> T, P (2*64*64*ps), per-row coefficients (1 KiB, bf16 inputs)
-                or gate rows (4*64*4, fp32 inputs)
-      state: q, k, v (3*64*128*es), T, P (2*64*64*ps), the coefficients
-             -> o (64*128*o_bytes)"""
+    Scalar gate, per chunk-head of 64 tokens, es = input element size:
+      bf16 inputs (fp16 operands):
+        prep : q, k (2*64*128*2), g (64*4), beta (64*2)
+               -> T, P (2 * 3072 * 2: the 64 x 64 tiles less the four zero
+                  16 x 16 blocks that token rows 0..31 never use), the
+                  per-row coefficient rows (3*64*4)
+        state: q, k, v (3*64*128*2), T, P (2 * 3072 * 2), the coefficient rows
+               -> o (64*128*o_bytes)
+      fp32 inputs (fp32 operands): the same with es = 4, whole T and P tiles
+        (2*64*64*4) and four gate rows (4*64*4)"""
     es = 2 if w.dtype == "bf16" else 4
-    ps = es
-    coef = 1024 if w.dtype == "bf16" else 4 * 64 * 4
-    prep = 2 * 64 * 128 * es + 64 * 4 + 64 * es + 2 * 64 * 64 * ps + coef
-    state = 3 * 64 * 128 * es + 2 * 64 * 64 * ps + coef + 64 * 128 * o_bytes
+    tp = 2 * 3072 * 2 if w.dtype == "bf16" else 2 * 64 * 64 * 4
+    coef = 3 * 64 * 4 if w.dtype == "bf16" else 4 * 64 * 4
+    prep = 2 * 64 * 128 * es + 64 * 4 + 64 * es + tp + coef
+    state = 3 * 64 * 128 * es + tp + coef + 64 * 128 * o_bytes
     return {"prep": prep * n_chunk_heads, "state": state * n_chunk_heads,
             "prep_per_chunk_head": prep, "state_per_chunk_head": state}
 

@@ -793,7 +793,8 @@ __global__ __launch_bounds__(64) void prep_kernel_h(PrepArgs a) {
 // fp16 operands of the L and P tiles, and the state pass's operands q b^G,
 // k b^G, k b^{G_L-G} go straight to the workspace. L and P are then plain
 // 16x16x32 MFMA tiles, and the inverse runs in LDS over the dead operand
-// tiles. 70.5 KiB of LDS: two workgroups per CU.
+// tiles. 70.5 KiB of LDS: two workgroups per CU. The phases hand data over
+// through LDS only, so their barriers leave the workspace stores in flight.
 constexpr int PKL = 136;   // row stride (fp16) of the 64 x 128 operand tiles: 272 bytes
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -872,7 +873,7 @@ __global__ __launch_bounds__(256) void prep_kernel_pk(PrepArgs a) {
         part[w][2 * lane] = s0;
         part[w][2 * lane + 1] = s1;
     }
-    __syncthreads();
+    lds_barrier();
     {
         float p0 = 0.0f, p1 = 0.0f;
         for (int ww = 0; ww < w; ++ww) {
@@ -890,7 +891,7 @@ __global__ __launch_bounds__(256) void prep_kernel_pk(PrepArgs a) {
                 *reinterpret_cast<float2*>(a.g_cumsum + (e0 + (int64_t)row * H) * DK + 2 * lane) = float2{gc[r][0], gc[r][1]};
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < DK) {
         const float gl = gref[1][tid];
         a.ws.gamL[ch * DK + tid] = gl;
@@ -923,7 +924,7 @@ __global__ __launch_bounds__(256) void prep_kernel_pk(PrepArgs a) {
             kg[row * (DK / 2)] = pack_f16x2(k0 * c0, k1 * c1);
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- L (strictly lower, 10 tiles) and P (lower incl. diagonal, 10 tiles)
     // on MFMA, 20 tiles over 4 waves; the 6 zero tiles of P above the diagonal
@@ -965,7 +966,7 @@ __global__ __launch_bounds__(256) void prep_kernel_pk(PrepArgs a) {
             PolicyH::st4(Pw + i * BT + op_pos(16 * jt + 4 * G), x);
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- T = (I + L)^{-1}: 16 x 16 diagonal blocks by substitution (wave 0,
     // lane = block * 16 + column), then the off-diagonal blocks by distance
@@ -989,7 +990,7 @@ __global__ __launch_bounds__(256) void prep_kernel_pk(PrepArgs a) {
             Ts[(16 * I + rr) * LDL + 16 * J + cc2] = 0.0f;
         }
     }
-    __syncthreads();
+    lds_barrier();
     for (int d = 1; d < 4; ++d) {
         const int nb = 4 - d;
         for (int e = tid; e < nb * 256; e += 256) {
@@ -1001,7 +1002,7 @@ __global__ __launch_bounds__(256) void prep_kernel_pk(PrepArgs a) {
                     s += Ls[(16 * I + rr) * LDL + 16 * K2 + m] * Ts[(16 * K2 + m) * LDL + 16 * J + cc2];
             Yb[(bi * 16 + rr) * 17 + cc2] = s;
         }
-        __syncthreads();
+        lds_barrier();
         for (int e = tid; e < nb * 256; e += 256) {
             const int bi = e >> 8, rr = (e >> 4) & 15, cc2 = e & 15;
             const int I = d + bi, J = bi;
@@ -1009,7 +1010,7 @@ __global__ __launch_bounds__(256) void prep_kernel_pk(PrepArgs a) {
             for (int m = 0; m < 16; ++m) s += Ts[(16 * I + rr) * LDL + 16 * I + m] * Yb[(bi * 16 + m) * 17 + cc2];
             Ts[(16 * I + rr) * LDL + 16 * J + cc2] = -s;
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     // ---- T out as fp16 operands (op_pos columns), optional token-major fp32 A slot
@@ -1998,7 +1999,8 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
                 d.x[12] = __builtin_amdgcn_raw_buffer_load_b128(rv, (16 * role + (lane >> 2)) * rowb + 16 * (lane & 3), 0, 0);
                 if (role == 0) {
                     const rsrc_t rc = make_rsrc(reinterpret_cast<const char*>(a.ws.cfh) + ch * CFS, CFS);
-                    d.x[13] = __builtin_amdgcn_raw_buffer_load_b128(rc, 16 * lane, 0, 0);
+                    // the block's first 64 floats are not used
+                    d.x[13] = __builtin_amdgcn_raw_buffer_load_b128(rc, lane < 16 ? 0x40000000u : 16u * lane, 0, 0);
                 }
             };
             auto store = [&](const Set& d, int buf) {

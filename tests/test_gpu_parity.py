@@ -174,6 +174,20 @@ def test_prep_slots_per_key():
 
 
 # ------------------------------------------------------------------ exact cases
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_empty_sequence_returns_entry_state(dtype):
+    # T = 0: no chunk to prepare, the state passes take zero steps, and the
+    # final state is the entry state (or zero)
+    print(f"empty sequence {dtype}", flush=True)
+    d = to_dev(W.generate(small(B=2, T=0, H=3, dtype=dtype), 17))
+    S0 = torch.randn(2, 3, 128, 128, generator=torch.Generator().manual_seed(9)).to(DEV)
+    o, fin, _ = run_gpu(d, initial_state=S0, output_final_state=True)
+    assert o.numel() == 0
+    assert torch.equal(fin, S0)
+    _, fin0, _ = run_gpu(d, output_final_state=True)
+    assert torch.count_nonzero(fin0).item() == 0
+
+
 def test_beta_zero_gives_exact_zero():
     d = to_dev(W.generate(small(B=2, T=190, H=2), 31))
     d["beta"] = torch.zeros_like(d["beta"])
