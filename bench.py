@@ -2,6 +2,11 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle S] [--workload NAME] [--no-cpu]
 
+The default workload is gdn_dense_bf16 (B=4, T=4096, H=16, bf16); --workload
+also takes gdn_tiny_fp32, gdn_varlen_tnd (packed documents), kda_split (per-key
+gate; the step is the sequence split: summaries, merge, correction) and
+gdn_long.
+
 A step is one full forward (chunk preparation + state pass with the fused
 output), one gdn_chunk_fwd call, over one batch of synthetic inputs already
 resident in HBM. Untimed steps for --settle seconds (the clocks ramp up over
@@ -50,26 +55,26 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def byte_model(w, n_chunk_heads: int, o_bytes: int) -> dict:
-    """Algorithmic bytes per launch: what each kernel must read and write by
-    its contract (every byte once), summed over the chunk-heads it processes.
-    Scalar gate, per chunk-head of 64 tokens, es = input element size:
+def byte_model(w, token_heads: int, chunk_heads: int, o_bytes: int) -> dict:
+    """Algorithmic bytes per launch of the scalar-gate kernels: what each
+    kernel must read and write by its contract (every byte once). Per
+    token-head (es = input element size) and per chunk-head (a chunk of up to
+    64 tokens of one head):
       bf16 inputs (fp16 operands):
-        prep : q, k (2*64*128*2), g (64*4), beta (64*2)
-               -> T, P (2 * 3072 * 2: the 64 x 64 tiles less the four zero
-                  16 x 16 blocks that token rows 0..31 never use), the
-                  per-row coefficient rows (3*64*4)
-        state: q, k, v (3*64*128*2), T, P (2 * 3072 * 2), the coefficient rows
-               -> o (64*128*o_bytes)
+        prep : q, k (2*128*2), g (4), beta (2) per token-head;
+               T, P (2 * 3072 * 2: the 64 x 64 tiles less the four zero
+               16 x 16 blocks that token rows 0..31 never use) and three
+               per-row coefficient rows (3*64*4) per chunk-head
+        state: q, k, v (3*128*2), o (128*o_bytes) per token-head; T, P and
+               the coefficient rows per chunk-head
       fp32 inputs (fp32 operands): the same with es = 4, whole T and P tiles
         (2*64*64*4) and four gate rows (4*64*4)"""
     es = 2 if w.dtype == "bf16" else 4
     tp = 2 * 3072 * 2 if w.dtype == "bf16" else 2 * 64 * 64 * 4
     coef = 3 * 64 * 4 if w.dtype == "bf16" else 4 * 64 * 4
-    prep = 2 * 64 * 128 * es + 64 * 4 + 64 * es + tp + coef
-    state = 3 * 64 * 128 * es + tp + coef + 64 * 128 * o_bytes
-    return {"prep": prep * n_chunk_heads, "state": state * n_chunk_heads,
-            "prep_per_chunk_head": prep, "state_per_chunk_head": state}
+    prep = token_heads * (2 * 128 * es + 4 + es) + chunk_heads * (tp + coef)
+    state = token_heads * (3 * 128 * es + 128 * o_bytes) + chunk_heads * (tp + coef)
+    return {"prep": prep, "state": state}
 
 
 def load_traffic(kernel: str, workload: str):
@@ -87,35 +92,59 @@ def load_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(d, w, budget_s: float = 15.0) -> dict:
-    """The fp64 oracle on a bounded sample of (row, head) streams of the
-    workload, on this host's cores."""
+def cpu_baseline(d, w, offsets, budget_s: float = 15.0) -> dict:
+    """The fp64 oracle on a bounded sample of the workload's (unit, head)
+    streams, on this host's cores: whole streams, in (unit, head) order, as
+    many as fit the budget (estimated from one stream's first tokens on one
+    thread). Every selected stream becomes one single-head unit of a packed
+    oracle input."""
     import numpy as np
 
     import oracle
 
     threads = max(1, len(os.sched_getaffinity(0)))
-    pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+    flat = {n: W_flat(d[n], w.layout) for n in ("q", "k", "v", "g", "beta")}
+    units = list(zip(offsets[:-1], offsets[1:]))
+    streams = [(a, b, h) for (a, b) in units for h in range(w.H)]
 
-    def run(sel, nthr):
-        q, k, v, g, beta = (np.ascontiguousarray(
-            np.stack([d[n][b, :, h].float().cpu().numpy() for b, h in sel], axis=1))
-            for n in ("q", "k", "v", "g", "beta"))
+    def pack(sel, limit=None):
+        cut = [(a, b if limit is None else min(b, a + limit), h) for a, b, h in sel]
+        arrs = {n: np.ascontiguousarray(np.concatenate(
+            [flat[n][a:b, h:h + 1].float().cpu().numpy() for a, b, h in cut], axis=0))
+            for n in flat}
+        offs = [0]
+        for a, b, _ in cut:
+            offs.append(offs[-1] + (b - a))
+        return arrs, offs
+
+    def run(sel, nthr, limit=None):
+        x, offs = pack(sel, limit)
         t0 = time.perf_counter()
-        r = oracle.fwd(q, k, v, g, beta, [0, w.T], d["scale"], want_final=False, threads=nthr)
-        return time.perf_counter() - t0, r
+        r = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], offs, d["scale"],
+                       gate_per_key=w.gate_per_key, use_exp2=w.use_exp2, want_final=False,
+                       threads=nthr)
+        return time.perf_counter() - t0, r, offs[-1]
 
-    t1, _ = run(pairs[:1], 1)                                  # one stream, one thread
-    n = int(min(len(pairs), max(1, budget_s * min(threads, len(pairs)) / max(t1, 1e-3))))
-    n = max(1, min(n, len(pairs)))
-    sel = pairs[:n]
-    used = min(threads, n)
-    t, r = run(sel, used)
-    token_heads = n * w.T
+    probe = min(2048, streams[0][1] - streams[0][0])
+    t1, _, n1 = run(streams[:1], 1, probe)                 # seconds per token, one thread
+    per_tok = t1 / max(n1, 1)
+    sel, tok = [], 0
+    for st in streams:
+        L = st[1] - st[0]
+        if sel and per_tok * (tok + L) / min(threads, len(sel) + 1) > budget_s:
+            break
+        sel.append(st)
+        tok += L
+    used = min(threads, len(sel))
+    t, r, token_heads = run(sel, used)
     return {"value": token_heads / w.H / t, "unit": "tokens/s", "cores": used, "kind": "oracle",
-            "sample": f"{n} of {len(pairs)} (row, head) streams of {w.name}, full length T={w.T}, "
-                      f"fp64 token recurrence, {t:.1f} s wall on {used} threads",
+            "sample": f"{len(sel)} of {len(streams)} (unit, head) streams of {w.name}, whole streams "
+                      f"({token_heads} token-heads), fp64 token recurrence, {t:.1f} s wall on {used} threads",
             "seconds": t, "_result": r, "_sel": sel}
+
+
+def W_flat(x, layout):
+    return x.reshape(-1, *x.shape[2:]) if layout == "BSND" else x
 
 
 def main():
@@ -125,7 +154,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--settle", type=float, default=1.0,
                     help="seconds of untimed steps before the warmup steps, so that the clocks settle")
-    ap.add_argument("--workload", default="gdn_dense_bf16")
+    ap.add_argument("--workload", default="gdn_dense_bf16",
+                    help="gdn_dense_bf16 (default), gdn_tiny_fp32, gdn_varlen_tnd, kda_split, gdn_long")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--o-dtype", choices=("fp32", "input"), default="fp32",
                     help="output dtype: fp32 (default; rounding o to bf16 alone exceeds the "
@@ -157,37 +187,68 @@ def main():
     from chunked_gated_delta_05_amd import binding as gb
     from chunked_gated_delta_05_amd import workloads as W
 
-    wl = {w.name: w for w in W.WORKLOADS}[args.workload]
-    if wl.gate_per_key or wl.n_seg or wl.layout != "BSND":
-        raise SystemExit("bench.py times the dense scalar-gate workloads (gdn_dense_bf16, gdn_long, gdn_tiny_fp32)")
+    names = [w.name for w in W.WORKLOADS]
+    if args.workload not in names:
+        raise SystemExit(f"unknown workload {args.workload}; one of {names}")
+    wl = W.WORKLOADS[names.index(args.workload)]
     dev = torch.device("cuda:0")
-    d = W.generate(wl, 1000 + [w.name for w in W.WORKLOADS].index(wl.name), device=dev)
+    d = W.generate(wl, 1000 + names.index(wl.name), device=dev)
     q, k, v, g, beta = (d[n] for n in ("q", "k", "v", "g", "beta"))
+    H, split = wl.H, bool(wl.n_seg)
     o_dtype = torch.float32 if args.o_dtype == "fp32" else v.dtype
     o = torch.empty(v.shape, dtype=o_dtype, device=dev)
-    fin = torch.empty((wl.B, wl.H, 128, 128), dtype=torch.float32, device=dev) if wl.final_state else None
-    nb = gb.workspace_bytes(gb._desc(k, wl.H, k.dtype, torch.float32, False, False, d["scale"], None))
+    tokens = wl.B * wl.T
+    # units of the whole forward (rows or packed documents); the oracle and the
+    # byte model count chunks per unit
+    offsets = list(d["offsets"]) if wl.layout == "TND" else [b * wl.T for b in range(wl.B + 1)]
+    chunks = sum((b - a + 63) // 64 for a, b in zip(offsets[:-1], offsets[1:]))
+    meta = gb.make_meta(d["offsets"], wl.T, dev) if wl.layout == "TND" else None
+    if split:
+        seg = d["seg_offsets"]
+        meta = gb.make_meta(gb.segment_offsets(wl.B, wl.T, seg), tokens, dev)
+        n_units = wl.B * wl.n_seg
+        S_ext = torch.empty((n_units, H, 128, 128), dtype=torch.float32, device=dev)
+        M = torch.empty((n_units, H, 128, 128), dtype=torch.float32, device=dev)
+        S_init = torch.empty_like(S_ext)
+        S_fin = torch.empty((wl.B, H, 128, 128), dtype=torch.float32, device=dev)
+    n_units = len(offsets) - 1 if not split else wl.B * wl.n_seg
+    fin = torch.empty((n_units, H, 128, 128), dtype=torch.float32, device=dev) if wl.final_state else None
+    nb = gb.workspace_bytes(gb._desc(k, H, k.dtype, o_dtype, wl.gate_per_key, wl.use_exp2, d["scale"], meta))
     ws = torch.empty(nb, dtype=torch.uint8, device=dev)
 
-    def fwd():
-        # the whole forward in one call, as a caller runs it
-        gb.gdn_chunk_fwd(q, k, v, g, beta, d["scale"], workspace=ws, out=o, o_dtype=o_dtype,
-                         output_final_state=wl.final_state, final_out=fin)
+    # unsplit forward: the arguments marshalled once, so that a step costs the
+    # host one C call and the GPU never waits for the host
+    call = None if split else gb.FwdCall(q, k, v, g, beta, d["scale"], out=o, workspace=ws, meta=meta,
+                                         final_out=fin, use_exp2=wl.use_exp2)
 
-    def step(ev=None, ev_end=None):
-        # the same forward as its two stages, for the per-kernel events:
-        # ev[0] before the prep kernel, ev[1] between the two kernels, ev_end
-        # after the state kernel (in the timed loop, the next step's ev[0])
-        if ev is not None:
-            ev[0].record()
-        gb.gdn_chunk_fwd(q, k, v, g, beta, d["scale"], flags=gb.FLAG_PREPARE_ONLY, workspace=ws)
-        if ev is not None:
-            ev[1].record()
-        _, f, _ = gb.gdn_chunk_fwd(q, k, v, g, beta, d["scale"], flags=gb.FLAG_REUSE_PREPARED, workspace=ws,
-                                   out=o, o_dtype=o_dtype, output_final_state=wl.final_state, final_out=fin)
-        if ev_end is not None:
-            ev_end.record()
-        return f
+    def fwd(ev=None):
+        # the whole forward as a caller runs it; ev: events between its launches
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        if not split:
+            call(0)
+            rec(1)
+            return
+        # sequence split: summaries from the zero state, their merge, then the
+        # forward of every segment from its true entry state (the correction)
+        gb.gdn_state_summary(k, v, g, beta, meta=meta, mode=0, use_exp2=wl.use_exp2, q=q, workspace=ws,
+                             S_ext=S_ext, M=M)
+        rec(1)
+        gb.gdn_state_merge(S_ext, M, None, B=wl.B, n_seg=wl.n_seg, S_init=S_init, S_final=S_fin)
+        rec(2)
+        gb.gdn_chunk_fwd(q, k, v, g, beta, d["scale"], meta=meta, initial_state=S_init, use_exp2=wl.use_exp2,
+                         o_dtype=o_dtype, flags=gb.FLAG_REUSE_PREPARED, workspace=ws, out=o)
+        rec(3)
+
+    def stages(ev=None):
+        # the unsplit forward as its two stages, for the per-kernel events:
+        # ev[0] before the preparation, ev[1] between the two kernels; the
+        # state pass ends at the next step's ev[0]
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        call(gb.FLAG_PREPARE_ONLY)
+        rec(1)
+        call(gb.FLAG_REUSE_PREPARED)
 
     # untimed steps until the clocks have settled (the first ~10-20 ms of
     # back-to-back work run at lower clocks), then the W warmup steps
@@ -195,7 +256,7 @@ def main():
     t_settle = time.perf_counter()
     while time.perf_counter() - t_settle < args.settle:
         for _ in range(20):
-            step()
+            fwd()
         torch.cuda.synchronize()
     for _ in range(args.warmup):
         fwd()
@@ -205,20 +266,33 @@ def main():
         fwd()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # second pass: the two stages with events, for the per-kernel split
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    ev_last = torch.cuda.Event(enable_timing=True)
+    ms_step = wall * 1e3 / args.steps
+
+    # second pass with HIP events on the launch stream: the per-kernel split.
+    # Unsplit: the two stages; split: summary (with the preparation), merge,
+    # correction. Every boundary is recorded once: a step's end is the next
+    # step's start event (each record costs the stream a few microseconds).
+    n_ev = 4 if split else 2
+    run = fwd if split else stages
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    last = torch.cuda.Event(enable_timing=True)
     for _ in range(args.warmup):
-        step()
+        run()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i], ev_last if i == args.steps - 1 else None)
+        run(evs[i])
+    last.record()
     torch.cuda.synchronize()
     wall_ev = time.perf_counter() - t1
-    ends = [evs[i + 1][0] for i in range(args.steps - 1)] + [ev_last]
-    prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    state_ms = sum(e[1].elapsed_time(x) for e, x in zip(evs, ends)) / args.steps
+    ends = [evs[i + 1][0] for i in range(args.steps - 1)] + [last]
+    seg_ms = []
+    for j in range(n_ev):
+        nxt = (lambda i: evs[i][j + 1]) if j + 1 < n_ev else (lambda i: ends[i])
+        seg_ms.append(sum(evs[i][j].elapsed_time(nxt(i)) for i in range(args.steps)) / args.steps)
+    names_ms = (["summary_with_prep", "merge", "correction"] if split else ["prep_kernel", "state_kernel"])
+    kernel_ms = dict(zip(names_ms, seg_ms[:len(names_ms)]))
+
     cold = None
     if args.cold_steps > 0:
         # each step after a 512 MiB write (outside the events) that pushes the
@@ -227,56 +301,65 @@ def main():
         cts = []
         for i in range(args.cold_steps):
             flush.fill_(i & 255)
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            step(ev, ev[2])
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev + 1)]
+            run(ev)
+            ev[-1].record()
             torch.cuda.synchronize()
-            cts.append((ev[0].elapsed_time(ev[2]), ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])))
+            cts.append([ev[0].elapsed_time(ev[-1])] + [ev[j].elapsed_time(ev[j + 1]) for j in range(n_ev)])
         del flush
         cts.sort()
         med = cts[len(cts) // 2]
-        cold = {"ms_per_step": med[0], "tokens_per_s": wl.B * wl.T / (med[0] * 1e-3),
-                "prep_ms": med[1], "state_ms": med[2], "steps": args.cold_steps,
+        cold = {"ms_per_step": med[0], "tokens_per_s": tokens / (med[0] * 1e-3), "steps": args.cold_steps,
                 "note": "median of steps timed one by one after a 512 MiB write evicting the cache"}
-    ms_step = wall * 1e3 / args.steps
-    tokens = wl.B * wl.T
-    n_chunk_heads = wl.B * ((wl.T + 63) // 64) * wl.H
-    o_bytes = o.element_size()
-    bm = byte_model(wl, n_chunk_heads, o_bytes)
-    flops = FLOP_PER_TOKEN_HEAD * tokens * wl.H
+        cold.update({f"{n}_ms": x for n, x in zip(names_ms, med[1:])})
+
+    token_heads = tokens * H
+    chunk_heads = chunks * H
+    flops = FLOP_PER_TOKEN_HEAD * token_heads
     tflops = flops / (ms_step * 1e-3) / 1e12
-    dom = "state" if state_ms >= prep_ms else "prep"
-    dom_ms = state_ms if dom == "state" else prep_ms
-    achieved = bm[dom] / (dom_ms * 1e-3) / 1e9
-    kname = {"state": "state_kernel", "prep": "prep_kernel"}[dom]
-    traffic = load_traffic(kname, wl.name)
-    io_bytes = (3 * 128 * (2 if wl.dtype == "bf16" else 4) + 128 * o_bytes + 4 + (2 if wl.dtype == "bf16" else 4)) * tokens * wl.H
+    io_bytes = (3 * 128 * (2 if wl.dtype == "bf16" else 4) + 128 * o.element_size()
+                + 4 * (128 if wl.gate_per_key else 1) + (2 if wl.dtype == "bf16" else 4)) * token_heads
     peak_mfma = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
     out = {
         "metric": METRIC, "value": tokens / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "settle_s": args.settle, "ms_per_step": ms_step, "higher_is_better": True,
-        "ms_per_step_event_pass": wall_ev * 1e3 / args.steps,
+        "steps": args.steps, "warmup": args.warmup, "settle_s": args.settle, "ms_per_step": ms_step,
+        "higher_is_better": True, "ms_per_step_event_pass": wall_ev * 1e3 / args.steps,
         "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
-        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": wl.H, "K": 128, "V": 128, "chunk": 64,
-                   "layout": wl.layout, "gate": "scalar", "o_dtype": str(o_dtype).replace("torch.", ""),
-                   "final_state": wl.final_state},
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": H, "K": 128, "V": 128, "chunk": 64,
+                   "layout": wl.layout, "gate": "per_key" if wl.gate_per_key else "scalar",
+                   "decay_base": 2 if wl.use_exp2 else "e", "o_dtype": str(o_dtype).replace("torch.", ""),
+                   "final_state": wl.final_state,
+                   **({"documents": len(offsets) - 1} if wl.layout == "TND" else {}),
+                   **({"segments_per_row": wl.n_seg, "path": "summary + merge + correction"} if split else {})},
         "tflops": tflops, "mfma_frac": tflops / peak_mfma,
         "hbm_frac_io": io_bytes / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
-        "hbm_frac_design": (bm["prep"] + bm["state"]) / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
-        "kernel_ms": {"prep_kernel": prep_ms, "state_kernel": state_ms},
+        "kernel_ms": kernel_ms,
         "cold": cold,
-        "roofline": {"kernel": kname, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": bm[dom]},
     }
-    print(f"[bench] {wl.name}: {ms_step:.4f} ms/step, prep {prep_ms:.4f} ms, state {state_ms:.4f} ms, "
-          f"{tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    if not wl.gate_per_key:
+        bm = byte_model(wl, token_heads, chunk_heads, o.element_size())
+        prep_ms, state_ms = kernel_ms["prep_kernel"], kernel_ms["state_kernel"]
+        dom = "state" if state_ms >= prep_ms else "prep"
+        dom_ms = state_ms if dom == "state" else prep_ms
+        achieved = bm[dom] / (dom_ms * 1e-3) / 1e9
+        kname = {"state": "state_kernel", "prep": "prep_kernel"}[dom]
+        out["hbm_frac_design"] = (bm["prep"] + bm["state"]) / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9)
+        out["roofline"] = {"kernel": kname, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                           "traffic": load_traffic(kname, wl.name), "algorithmic_bytes_per_launch": bm[dom]}
+    else:
+        out["roofline"] = None   # per-key split path: per-kernel figures are in the kernel traces
+    print(f"[bench] {wl.name}: {ms_step:.4f} ms/step, "
+          + ", ".join(f"{n} {x:.4f} ms" for n, x in kernel_ms.items()) + f", {tflops:.1f} TFLOP/s",
+          file=sys.stderr, flush=True)
     if not args.no_cpu:
         import numpy as np
 
-        cb = cpu_baseline(d, wl)
+        cb = cpu_baseline(d, wl, offsets)
         r, sel = cb.pop("_result"), cb.pop("_sel")
-        got = np.stack([o[b, :, h].float().cpu().numpy() for b, h in sel], axis=1)
-        ref = r["o"]
+        of = W_flat(o, wl.layout)
+        got = np.concatenate([of[a:b, h].float().cpu().numpy() for a, b, h in sel], axis=0)
+        ref = r["o"][:, 0]
         out["parity_sample_err_over_rms"] = float(np.abs(got - ref).max() / np.sqrt((ref ** 2).mean()))
         out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)

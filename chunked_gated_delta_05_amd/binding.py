@@ -250,10 +250,47 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale=None, *, meta: UnitMeta | None = None,
     return o, fin, extras
 
 
+class FwdCall:
+    """gdn_chunk_fwd with its arguments marshalled once, for repeated calls
+    on the same tensors (timing loops, serving steps): call(flags) issues the
+    C call with the stored descriptor, pointers, workspace and stream. The
+    tensors must stay alive and in place while the object is used."""
+
+    def __init__(self, q, k, v, g, beta, scale=None, *, out, workspace, meta: UnitMeta | None = None,
+                 initial_state=None, final_out=None, use_exp2=False):
+        _check_inputs(q, k, v, g, beta)
+        H = k.shape[-2]
+        per_key = g.dim() == k.dim()
+        if scale is None:
+            scale = k.shape[-1] ** -0.5
+        self._keep = (q, k, v, g, beta, out, workspace, meta, initial_state, final_out)
+        self._desc = _desc(k, H, k.dtype, out.dtype, per_key, use_exp2, scale, meta)
+        nb = workspace_bytes(self._desc)
+        if workspace.numel() < nb:
+            raise ValueError("workspace too small")
+        if tuple(out.shape) != tuple(v.shape):
+            raise ValueError("out must have v's shape")
+        units = n_units_of(k, meta)
+        for t, shp in ((initial_state, (units, H, k.shape[-1], v.shape[-1])),
+                       (final_out, (units, H, k.shape[-1], v.shape[-1]))):
+            if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != shp):
+                raise ValueError(f"states must be contiguous float32 {shp}")
+        self._slots = GdnSlots(None, None, None)
+        self._nbytes = ctypes.c_size_t(workspace.numel())
+        self._args = [ctypes.byref(self._desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                      _ptr(initial_state), _ptr(out), _ptr(final_out), ctypes.byref(self._slots)]
+        self._tail = [_ptr(workspace), ctypes.byref(self._nbytes), _stream(k.device)]
+        self._fn = lib().gdn_chunk_fwd
+
+    def __call__(self, flags: int = 0) -> None:
+        check(self._fn(*self._args, int(flags), *self._tail), "gdn_chunk_fwd")
+
+
 def gdn_state_summary(k, v, g, beta, *, meta: UnitMeta, mode=0, use_exp2=False, q=None,
-                      workspace=None):
-    """Per-unit summaries (S_ext [units,H,K,V], M [units,H,K,K]); pass q to
-    leave a per-key preparation that a reusing forward can use."""
+                      workspace=None, S_ext=None, M=None):
+    """Per-unit summaries (S_ext [units,H,K,V], M [units,H,K,K]; given
+    buffers are written in place); pass q to leave a per-key preparation
+    that a reusing forward can use."""
     _check_inputs(q, k, v, g, beta)
     H = k.shape[-2]
     per_key = g.dim() == k.dim()
@@ -263,8 +300,13 @@ def gdn_state_summary(k, v, g, beta, *, meta: UnitMeta, mode=0, use_exp2=False, 
     ws = workspace if workspace is not None else torch.empty(nb, dtype=torch.uint8, device=dev)
     units = n_units_of(k, meta)
     K, V = k.shape[-1], v.shape[-1]
-    S_ext = torch.empty((units, H, K, V), dtype=torch.float32, device=dev) if mode != 2 else None
-    M = torch.empty((units, H, K, K), dtype=torch.float32, device=dev) if mode != 1 else None
+    if mode != 2 and S_ext is None:
+        S_ext = torch.empty((units, H, K, V), dtype=torch.float32, device=dev)
+    if mode != 1 and M is None:
+        M = torch.empty((units, H, K, K), dtype=torch.float32, device=dev)
+    for t, shp in ((S_ext if mode != 2 else None, (units, H, K, V)), (M if mode != 1 else None, (units, H, K, K))):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != shp):
+            raise ValueError(f"summary buffers must be contiguous float32 {shp}")
     nbytes = ctypes.c_size_t(ws.numel())
     check(lib().gdn_state_summary(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                   int(mode), _ptr(S_ext), _ptr(M), _ptr(ws), ctypes.byref(nbytes),
@@ -272,13 +314,22 @@ def gdn_state_summary(k, v, g, beta, *, meta: UnitMeta, mode=0, use_exp2=False, 
     return S_ext, M, ws
 
 
-def gdn_state_merge(S_ext, M, S0=None, *, B: int, n_seg: int, want_final=True):
+def gdn_state_merge(S_ext, M, S0=None, *, B: int, n_seg: int, want_final=True, S_init=None,
+                    S_final=None):
     """S_ext [B*n_seg,H,K,V], M [B*n_seg,H,K,K] (units row-major) -> S_init
-    [B*n_seg,H,K,V] (the state entering every segment) and S_final [B,H,K,V]."""
+    [B*n_seg,H,K,V] (the state entering every segment) and S_final [B,H,K,V]
+    (given buffers are written in place)."""
     H, K, V = S_ext.shape[1], S_ext.shape[2], S_ext.shape[3]
     dev = S_ext.device
-    S_init = torch.empty_like(S_ext)
-    S_final = torch.empty((B, H, K, V), dtype=torch.float32, device=dev) if want_final else None
+    if S_init is None:
+        S_init = torch.empty_like(S_ext)
+    if want_final and S_final is None:
+        S_final = torch.empty((B, H, K, V), dtype=torch.float32, device=dev)
+    if not want_final:
+        S_final = None
+    for t, shp in ((S_init, tuple(S_ext.shape)), (S_final, (B, H, K, V))):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != shp):
+            raise ValueError(f"merge outputs must be contiguous float32 {shp}")
     check(lib().gdn_state_merge(B, H, n_seg, K, V, _ptr(S_ext), _ptr(M), _ptr(S0), _ptr(S_init),
                                 _ptr(S_final), _stream(dev)), "gdn_state_merge")
     return S_init, S_final

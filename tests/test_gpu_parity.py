@@ -174,6 +174,39 @@ def test_prep_slots_per_key():
 
 
 # ------------------------------------------------------------------ exact cases
+@pytest.mark.parametrize("layout", ["BSND", "TND"])
+def test_marshalled_call_matches_forward(layout):
+    # FwdCall (arguments marshalled once) and its two stages (prepare only,
+    # then reuse) give the forward's output and final state bit for bit
+    print(f"marshalled call {layout}", flush=True)
+    if layout == "BSND":
+        d = to_dev(W.generate(small(B=2, T=200, H=3), 41))
+        meta = None
+    else:
+        cu = W.cu_from_lengths([30, 200, 64, 9])
+        base = W.generate(small(B=1, T=cu[-1], H=3), 43)
+        d = {n: base[n][0].contiguous().to(DEV) for n in ("q", "k", "v", "g", "beta")}
+        d.update(scale=base["scale"], offsets=cu,
+                 workload=small(B=1, T=cu[-1], H=3, layout="TND", n_docs=4))
+        meta = gb.make_meta(cu, cu[-1], DEV)
+    o_ref, fin_ref, _ = run_gpu(d, meta=meta, output_final_state=True)
+    ws = torch.empty(gb.workspace_bytes(gb._desc(d["k"], 3, d["k"].dtype, torch.float32, False, False,
+                                                 d["scale"], meta)), dtype=torch.uint8, device=DEV)
+    o = torch.empty_like(o_ref)
+    fin = torch.empty_like(fin_ref)
+    call = gb.FwdCall(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], out=o, workspace=ws,
+                      meta=meta, final_out=fin)
+    call(0)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(fin, fin_ref)
+    o.zero_()
+    fin.zero_()
+    call(gb.FLAG_PREPARE_ONLY)
+    call(gb.FLAG_REUSE_PREPARED)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(fin, fin_ref)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_empty_sequence_returns_entry_state(dtype):
     # T = 0: no chunk to prepare, the state passes take zero steps, and the
