@@ -63,15 +63,16 @@ def byte_model(w, token_heads: int, chunk_heads: int, o_bytes: int) -> dict:
       bf16 inputs (fp16 operands):
         prep : q, k (2*128*2), g (4), beta (2) per token-head;
                T, P (2 * 3072 * 2: the 64 x 64 tiles less the four zero
-               16 x 16 blocks that token rows 0..31 never use) and three
-               per-row coefficient rows (3*64*4) per chunk-head
+               16 x 16 blocks that token rows 0..31 never use; beta is
+               folded into T) and two per-row coefficient rows (2*64*4) per
+               chunk-head
         state: q, k, v (3*128*2), o (128*o_bytes) per token-head; T, P and
                the coefficient rows per chunk-head
       fp32 inputs (fp32 operands): the same with es = 4, whole T and P tiles
         (2*64*64*4) and four gate rows (4*64*4)"""
     es = 2 if w.dtype == "bf16" else 4
     tp = 2 * 3072 * 2 if w.dtype == "bf16" else 2 * 64 * 64 * 4
-    coef = 3 * 64 * 4 if w.dtype == "bf16" else 4 * 64 * 4
+    coef = 2 * 64 * 4 if w.dtype == "bf16" else 4 * 64 * 4
     prep = token_heads * (2 * 128 * es + 4 + es) + chunk_heads * (tp + coef)
     state = token_heads * (3 * 128 * es + 128 * o_bytes) + chunk_heads * (tp + coef)
     return {"prep": prep, "state": state}

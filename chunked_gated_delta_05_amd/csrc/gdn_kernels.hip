@@ -287,12 +287,12 @@ __device__ __forceinline__ int swzk(int r) { return (r & 1) | ((r & 2) << 1) | (
 constexpr int CFB = 1024;
 constexpr int CF_CY = 0, CF_CP = 64, CF_BG = 128, CF_BETA = 192;   // fp16 offsets
 constexpr int CF_GL = 128;                                          // fp32 offset
-// The scalar gate's block (CFS bytes) holds three fp32 rows in the same lane
-// order - b^{G_L - G}, b^G, beta - at the float offsets below (the first 64
-// floats are not used); b^{G_L} is the b^G entry of the chunk's last valid
-// token.
+// The scalar gate's block (CFS bytes) holds two fp32 rows in the same lane
+// order - b^{G_L - G} and b^G - at the float offsets below (floats 0..63 and
+// 192..255 are not used; beta is folded into T); b^{G_L} is the b^G entry of
+// the chunk's last valid token.
 constexpr int CFS = 1024;
-constexpr int CS_CP = 64, CS_BG = 128, CS_BETA = 192;
+constexpr int CS_CP = 64, CS_BG = 128;
 __device__ __forceinline__ int lane_order(int t) { return 16 * ((t >> 2) & 3) + 4 * (t >> 4) + (t & 3); }
 
 // raw buffer resource over [base, base + bytes): accesses outside read as zero
@@ -668,7 +668,6 @@ __global__ __launch_bounds__(64) void prep_kernel_h(PrepArgs a) {
         const int lo = lane_order(lane);
         cf[CS_CP + lo] = bLG;
         cf[CS_BG + lo] = bG;
-        cf[CS_BETA + lo] = bt;
         if (a.g_cumsum && lane < len) a.g_cumsum[e0 + (int64_t)lane * H] = x;
     }
     float Gi[4], Bi[4];
@@ -768,7 +767,9 @@ __global__ __launch_bounds__(64) void prep_kernel_h(PrepArgs a) {
     S = mm4(TL[3][2], C20, mm4(TL[3][1], C10, mm4(TL[3][0], TC[0], z4)));
     R30 = mm4(S, nTR[3], z4);
 
-    // ---- T out: fp16 operands (op_pos columns), optional token-major fp32 A slot
+    // ---- T out: T diag(beta) as fp16 operands (op_pos columns) for the state
+    // pass, which then needs no beta; the optional token-major fp32 A slot
+    // holds T itself
     f16* Tw = reinterpret_cast<f16*>(a.ws.Tm) + ch * (BT * BT);
     const f32x4 TB[4][4] = {{TR[0], z4, z4, z4}, {R10, TR[1], z4, z4}, {R20, R21, TR[2], z4}, {R30, R31, R32, TR[3]}};
 #pragma unroll
@@ -776,7 +777,8 @@ __global__ __launch_bounds__(64) void prep_kernel_h(PrepArgs a) {
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
             if (I >= 2 || J < 2)   // rows 0..31 of the state pass read columns 0..31 only
-                *reinterpret_cast<u32x2*>(Tw + (16 * I + n) * BT + op_pos(16 * J + 4 * G)) = f32x4_to_f16x4(TB[I][J]);
+                *reinterpret_cast<u32x2*>(Tw + (16 * I + n) * BT + op_pos(16 * J + 4 * G)) =
+                    f32x4_to_f16x4(TB[I][J] * *reinterpret_cast<const f32x4*>(&Bs[16 * J + 4 * G]));
             if (a.A && 16 * I + n < len)
                 *reinterpret_cast<f32x4*>(a.A + (e0 + (int64_t)(16 * I + n) * H) * BT + 16 * J + 4 * G) = TB[I][J];
         }
@@ -1865,11 +1867,10 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
             for (int j2 = 0; j2 < 2; ++j2) hb[2 * (1 - kq) + j2].v = hx[tq][partner][j2][lane];
             // per-row coefficients: lane G holds rows 16 it + 4G + r at [16G + 4it + r]
             const float* cf = cb[tb];
-            f32x4 cpf[4], bg[4], bt[4];
+            f32x4 cpf[4], bg[4];
             for (int it = 0; it < 4; ++it) {
                 cpf[it] = *reinterpret_cast<const f32x4*>(&cf[CS_CP + 16 * G + 4 * it]);
                 bg[it] = *reinterpret_cast<const f32x4*>(&cf[CS_BG + 16 * G + 4 * it]);
-                bt[it] = *reinterpret_cast<const f32x4*>(&cf[CS_BETA + 16 * G + 4 * it]);
             }
             const float eL = cf[CS_BG + lane_order(len > 0 ? len - 1 : 0)];
             s16x4 vraw[4];
@@ -1882,12 +1883,12 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
             // lower triangular, so v_new of rows 0..31 needs Y of rows 0..31
             // only, and the state update from the first 32 tokens can run
             // while the k.h products of the second half complete.
-            auto khY = [&](int it, f32x4& y) {           // Y = beta (v - b^G (k h)), row tile it
+            auto khY = [&](int it, f32x4& y) {           // Y = v - b^G (k h), row tile it (beta is in T)
                 f32x4 kh = {0.f, 0.f, 0.f, 0.f};
                 for (int s2 = 0; s2 < 4; ++s2) PolicyH::mma(kh, ldA(K, offA[s2] + it * 16 * 256), hb[s2]);
                 for (int r = 0; r < 4; ++r) {
                     const float vv = __builtin_bit_cast(float, (uint32_t)(uint16_t)vraw[it][r] << 16);
-                    y[r] = bt[it][r] * __builtin_fmaf(-bg[it][r], kh[r], vv);
+                    y[r] = __builtin_fmaf(-bg[it][r], kh[r], vv);
                 }
             };
             f32x4 y[4], vn[4], vp[4];
@@ -1999,8 +2000,8 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
                 d.x[12] = __builtin_amdgcn_raw_buffer_load_b128(rv, (16 * role + (lane >> 2)) * rowb + 16 * (lane & 3), 0, 0);
                 if (role == 0) {
                     const rsrc_t rc = make_rsrc(reinterpret_cast<const char*>(a.ws.cfh) + ch * CFS, CFS);
-                    // the block's first 64 floats are not used
-                    d.x[13] = __builtin_amdgcn_raw_buffer_load_b128(rc, lane < 16 ? 0x40000000u : 16u * lane, 0, 0);
+                    // only floats 64..191 of the block are used
+                    d.x[13] = __builtin_amdgcn_raw_buffer_load_b128(rc, lane < 16 || lane >= 48 ? 0x40000000u : 16u * lane, 0, 0);
                 }
             };
             auto store = [&](const Set& d, int buf) {
