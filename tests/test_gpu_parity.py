@@ -386,6 +386,47 @@ def test_per_key_small_forward():
     assert_close(np32(fin), r["final"], TOL["bf16"], "per-key final")
 
 
+@pytest.mark.parametrize("use_exp2", [False, True])
+def test_per_key_fp32_with_entry_state(use_exp2):
+    # fp32 inputs with a per-key gate (the fp32 preparation and state pass),
+    # both decay bases, a random entry state and a ragged tail
+    print(f"per-key fp32 exp2={use_exp2}", flush=True)
+    w = small(B=2, T=170, H=2, dtype="fp32", per_key=True, use_exp2=use_exp2, gate_coef=0.05)
+    d = to_dev(W.generate(w, 73))
+    S0 = (torch.randn(2, 2, 128, 128, generator=torch.Generator().manual_seed(4)) * 0.3).to(DEV)
+    o, fin, ex = run_gpu(d, initial_state=S0, output_final_state=True, want_h=True)
+    r = run_oracle(d, S0=np32(S0).astype(np.float64), chunk_states=True)
+    assert_close(flat_o(o, w), r["o"], TOL["fp32"], "per-key fp32 o")
+    assert_close(np32(fin), r["final"], TOL["fp32"], "per-key fp32 final")
+    assert_close(np32(ex["h"]), r["chunk_states"], TOL["fp32"], "per-key fp32 chunk states")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_per_key_packed_documents(dtype):
+    # packed documents with a per-key gate: state reset per document, partial
+    # chunks, against the oracle and against the separate runs (bitwise)
+    lens = [40, 130, 1, 97]
+    cu = W.cu_from_lengths(lens)
+    T, H = cu[-1], 2
+    print(f"per-key packed {dtype}", flush=True)
+    base = W.generate(small(B=1, T=T, H=H, dtype=dtype, per_key=True, use_exp2=True, gate_coef=0.05), 79)
+    d = {n: base[n][0].contiguous().to(DEV) for n in ("q", "k", "v", "g", "beta")}
+    d.update(scale=base["scale"], offsets=cu,
+             workload=small(B=1, T=T, H=H, dtype=dtype, per_key=True, use_exp2=True, gate_coef=0.05,
+                            layout="TND", n_docs=len(lens)))
+    o, fin, _ = run_gpu(d, output_final_state=True)
+    r = run_oracle(d)
+    assert_close(np32(o), r["o"], TOL[dtype], "per-key packed o")
+    assert_close(np32(fin), r["final"], TOL[dtype], "per-key packed final")
+    for i, (a, b) in enumerate(zip(cu, cu[1:])):
+        sep = {n: d[n][a:b][None].contiguous() for n in ("q", "k", "v", "g", "beta")}
+        sep.update(scale=d["scale"], offsets=None,
+                   workload=small(B=1, T=b - a, H=H, dtype=dtype, per_key=True, use_exp2=True))
+        o1, f1, _ = run_gpu(sep, output_final_state=True)
+        assert torch.equal(o1[0], o[a:b]), f"document {i} differs from its separate run"
+        assert torch.equal(f1[0], fin[i])
+
+
 # ------------------------------------------------------------------ full-size workloads (sampled)
 def _sampled_check(d, o, heads, fin=None):
     """Oracle on the selected heads only (heads are independent)."""
