@@ -22,10 +22,14 @@
 //   prep_kernel_h    bf16, scalar gate: one wave per (chunk, head) with every
 //                    tile in registers: G, L and P on MFMA, the 64 x 64 inverse
 //                    (diagonal blocks by substitution, the rest on fp32 MFMA),
-//                    T, P and the per-row coefficients to the workspace.
-//   prep_kernel      fp32 inputs and per-key gates: one workgroup per (chunk,
-//                    head), the inverse in LDS (per-key gate: also q*b^G,
-//                    k*b^G, k*b^{G_last-G}, G_last).
+//                    T diag(beta), P and the per-row coefficients to the
+//                    workspace.
+//   prep_kernel_pk   bf16, per-key gate: four waves per (chunk, head); the
+//                    gated operands computed once per element, L and P on
+//                    MFMA, the inverse in LDS.
+//   prep_kernel      fp32 inputs (scalar and per-key gates): one workgroup per
+//                    (chunk, head), the inverse in LDS (per-key gate: also
+//                    q*b^G, k*b^G, k*b^{G_last-G}, G_last).
 //   state_kernel_ks  bf16, scalar gate: one workgroup per (unit, head, 32
 //                    columns); four compute waves split the state by keys,
 //                    four streaming waves stage the chunk tiles.
@@ -35,6 +39,11 @@
 //                    columns. In summary mode every state kernel runs the same
 //                    recurrence on [S_ext | M] from [0 | I].
 //   merge_kernel     S_init[s+1] = M_s S_init[s] + S_ext[s] in fp32.
+//   unit_order_kernel  packed units ranked by chunk count, so that the state
+//                    passes launch the longest units first.
+//
+// The bf16 scalar-gate preparation writes T diag(beta) (the A slot keeps T),
+// so the state pass needs no beta.
 //
 // Precision: bf16 inputs are converted to fp16 MFMA operands (exact for
 // normal-range values); products accumulate in fp32; the state, the cumulative
@@ -349,8 +358,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     const In* qin = reinterpret_cast<const In*>(a.q);
     const In* bin = reinterpret_cast<const In*>(a.beta);
     const bool has_q = qin != nullptr;   // P (and per key q * b^G) are prepared when q is given
-    // fp16 operands are stored in the state pass's operand order (op_pos)
-    constexpr bool PERM = sizeof(Op) == 2;
+    // the fp32 path: operands stay in natural order (the fp16 paths have kernels of their own)
+    static_assert(sizeof(Op) == 4, "prep_kernel serves fp32 operands");
 
     // ---- tiles into LDS as operands (rows past the chunk end are zero)
     constexpr int VPR = 16 / sizeof(In);             // elements per 16-byte vector
@@ -396,16 +405,6 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
                 if (a.g_cumsum && r < len) a.g_cumsum[((t0 + r) * H + head) * DK + tid] = acc;
             }
             a.ws.gamL[ch * DK + tid] = acc;
-            if (PERM) reinterpret_cast<float*>(a.ws.cfh)[ch * (CFB / 4) + CF_GL + tid] = fpow(acc, a.use_exp2);
-        }
-        if (PERM && tid < BT) {
-            const float bt = tid < len ? P::f(bin[(t0 + tid) * H + head]) : 0.0f;
-            f16* cf = reinterpret_cast<f16*>(a.ws.cfh) + ch * (CFB / 2);
-            const int lo = lane_order(tid);
-            cf[CF_CY + lo] = (f16)bt;
-            cf[CF_CP + lo] = (f16)1.0f;
-            cf[CF_BG + lo] = (f16)1.0f;
-            cf[CF_BETA + lo] = (f16)bt;
         }
     }
     __syncthreads();
@@ -496,7 +495,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         const int r = e / (BT / 4), c4 = (e % (BT / 4)) * 4;
         f32x4 x;
         for (int q2 = 0; q2 < 4; ++q2) x[q2] = Ts[r * LDL + c4 + q2];
-        P::f32_to_op4(Tw + r * BT + (PERM ? op_pos(c4) : c4), x);
+        P::f32_to_op4(Tw + r * BT + c4, x);
         if (a.A && r < len) *reinterpret_cast<f32x4*>(a.A + ((t0 + r) * H + head) * BT + c4) = x;
     }
 
@@ -534,7 +533,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
                 if (!PERKEY && j <= i) pv *= fpow(Gs[i] - Gs[j], a.use_exp2);
                 x[r] = pv;
             }
-            P::st4(Pw + i * BT + (PERM ? op_pos(16 * jt + 4 * G) : 16 * jt + 4 * G), x);
+            P::st4(Pw + i * BT + 16 * jt + 4 * G, x);
         }
     }
 
@@ -554,7 +553,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
                 xd[e] = kv * fpow(gg, a.use_exp2);
                 xg[e] = kv * fpow(Gs[last * (DK + 4) + c4 + e] - gg, a.use_exp2);
             }
-            const int cp = PERM ? op_pos(c4) : c4;
+            const int cp = c4;
             if (has_q) P::st4(qg + r * DK + cp, xq);
             P::st4(kd + r * DK + cp, xd);
             P::st4(kg + r * DK + cp, xg);
