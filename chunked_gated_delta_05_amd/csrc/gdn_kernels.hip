@@ -30,11 +30,10 @@
 //   prep_kernel      fp32 inputs (scalar and per-key gates): one workgroup per
 //                    (chunk, head), the inverse in LDS (per-key gate: also
 //                    q*b^G, k*b^G, k*b^{G_last-G}, G_last).
-//   state_kernel_ks  bf16, scalar gate: one workgroup per (unit, head, 32
-//                    columns); four compute waves split the state by keys,
-//                    four streaming waves stage the chunk tiles.
-//   state_kernel_pk  bf16, per-key gate: two compute waves own all keys of 16
-//                    columns each; two waves copy the prepared tiles.
+//   state_kernel_ks  bf16, scalar and per-key gates: one workgroup per (unit,
+//                    head, 32 columns); four compute waves split the state by
+//                    keys, four streaming waves stage the chunk tiles (per key:
+//                    the prepared gated k, q and k b^{G_L - G} tiles).
 //   state_kernel     fp32 inputs: eight waves, each owning 32 keys of 16
 //                    columns. In summary mode every state kernel runs the same
 //                    recurrence on [S_ext | M] from [0 | I].
@@ -83,12 +82,10 @@ __device__ __forceinline__ float fpow(float x, int use_exp2) {
 
 // Workgroup barrier for LDS hand-offs only: this wave's LDS accesses complete
 // before it, but outstanding global loads and stores stay in flight (the
-// fence of __syncthreads would wait for all of them). Data copied into LDS by
-// global-to-LDS loads is made ready by an explicit vector-memory wait first.
-// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
-// 6:4, lgkmcnt 11:8); issued through the builtin so that the compiler's own
-// wait insertion knows what has completed
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// fence of __syncthreads would wait for all of them).
+// The s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt 6:4, lgkmcnt 11:8) waits for LDS only; it is issued through the
+// builtin so that the compiler's own wait insertion knows what has completed.
 constexpr int waitcnt_lgkm0() { return 15 | (3 << 14) | (7 << 4); }
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
@@ -101,17 +98,10 @@ __device__ __forceinline__ void lds_barrier() {
 // tile: the operand layout of v_mfma_f32_16x16x32_{f16,bf16}. The
 // accumulator holds C[4G + r][n], r = 0..3.
 
-struct PolicyH {          // bf16 inputs, fp16 operands
-    using In = bf16;
+struct PolicyH {          // fp16 operands (bf16 inputs)
     using Op = f16;
-    static constexpr int LDQ = 136;   // 64 x 128 LDS tile rows: 272 bytes
     struct F { f16x8 v; };
     __device__ static F ld(const Op* p) { F f; f.v = *reinterpret_cast<const f16x8*>(p); return f; }
-    __device__ static F from(const float* x) {
-        F f;
-        for (int e = 0; e < 8; ++e) f.v[e] = (f16)x[e];
-        return f;
-    }
     __device__ static void st4(Op* p, const float* x) {
         f16x4 h;
         for (int e = 0; e < 4; ++e) h[e] = (f16)x[e];
@@ -119,36 +109,6 @@ struct PolicyH {          // bf16 inputs, fp16 operands
     }
     __device__ static void mma(f32x4& c, const F& a, const F& b) {
         c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, c, 0, 0, 0);
-    }
-    // Column fragment of an LDS tile: lane (G, n) gets tile[r0 + 8G + e][c0 + n].
-    // ds_read_b64_tr_b16 hands component c of lane j's 4-element row to lane
-    // 4(j%4)+c as element j/4, so lane j points at row r0 + 8G + j/4 (+4),
-    // columns c0 + 4(j%4) .. +3.
-    __device__ static F ldcol(const Op* tile, int ld, int r0, int c0, int lane) {
-        const int G = lane >> 4, j = lane & 15;
-        const Op* p = tile + (r0 + 8 * G + (j >> 2)) * ld + c0 + 4 * (j & 3);
-        s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, p));
-        s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, p + 4 * ld));
-        f16x4 x = __builtin_bit_cast(f16x4, a), y = __builtin_bit_cast(f16x4, b);
-        F f;
-        for (int e = 0; e < 4; ++e) { f.v[e] = x[e]; f.v[e + 4] = y[e]; }
-        return f;
-    }
-    __device__ static float f(In x) { return (float)x; }
-    __device__ static Op cvt(float x) { return (f16)x; }
-    static constexpr int FV = 1;   // 16-byte vectors per 8-operand fragment
-    __device__ static F frag(const f32x4* v) { F f; f.v = __builtin_bit_cast(f16x8, v[0]); return f; }
-    // 16 bytes of inputs (8 bf16) -> the same 8 values as operands (16 bytes of
-    // fp16). bf16 -> fp32 is a shift; fp32 -> fp16 of a bf16 value in the fp16
-    // normal range is exact, so the truncating pack is exact too.
-    __device__ static f32x4 in2op(f32x4 raw) {
-        const u32x4 w = __builtin_bit_cast(u32x4, raw);
-        u32x4 o;
-        for (int i = 0; i < 4; ++i) {
-            const float lo = __builtin_bit_cast(float, w[i] << 16), hi = __builtin_bit_cast(float, w[i] & 0xffff0000u);
-            o[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-        }
-        return __builtin_bit_cast(f32x4, o);
     }
     // 4 fp32 values -> 4 operands (8 bytes)
     __device__ static void f32_to_op4(Op* p, f32x4 x) {
@@ -263,18 +223,10 @@ __device__ __forceinline__ void chunk_of(const UnitMap& um, int ci, int& u, int&
 // of the terms inside one 32-deep contraction does not change the product.
 __device__ __forceinline__ int op_pos(int x) { return (x & ~31) | ((x & 12) << 1) | ((x & 16) >> 2) | (x & 3); }
 
-// 16-byte granule swizzles of the LDS tiles of the fp16 state pass. The LDS
-// has 32 four-byte banks: a 16-byte read is served 8 lanes at a time and an
-// 8-byte read 16 lanes at a time, so the granule index modulo 8 picks the
-// banks. Rows of 128 operands (16 granules): the low three bits of the
-// swizzle are a bijection on any 8 consecutive rows (row-fragment reads are
-// conflict free) and bit 2 alternates with the row, which spreads the
-// 4-row x 4-piece transposed reads over every bank pair (two-way, the least
-// possible for 8-byte pieces that all sit in the same granule half). Rows of
-// 64 operands (8 granules): row-fragment reads only.
-__device__ __forceinline__ int swz16(int r) {
-    return ((r & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 1) & 1) | (r & 8);
-}
+// 16-byte granule swizzle of the 64-operand rows (8 granules) of the T and P
+// tiles in LDS. The LDS has 32 four-byte banks: a 16-byte read is served 8
+// lanes at a time, so the granule index modulo 8 picks the banks, and the
+// row-fragment reads of 8 consecutive rows are conflict free.
 __device__ __forceinline__ int swz8(int r) { return r & 7; }
 
 // k and q tiles of the scalar-gate state pass (rows of 16 granules): row r
@@ -1352,380 +1304,7 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
         }
 }
 
-// ------------------------------------------------------------------ state pass, fp16 operands, per-key gate
-// Workgroup of 4 waves for one (unit, head, 32-column tile). Waves 0 and 1
-// each own 16 value columns with all 64 token rows and all 128 keys, so the
-// recurrence needs no exchange between waves: the state, the residual Y and
-// v_new stay in registers and feed the MFMAs as B operands (operand order
-// above). Waves 2 and 3, on the other two SIMDs, copy the prepared gated
-// tiles (k*b^G, q*b^G, k*b^{G_L-G}), T, P, the v rows and the per-row gate
-// factors into multi-buffered LDS ahead of their use. One barrier per chunk
-// hands the buffers over.
-constexpr int HW = 4;              // waves per workgroup
-constexpr int HT = 64 * HW;        // threads
-
-template <bool SUMMARY, bool OBF>
-__global__ __launch_bounds__(HT) void state_kernel_pk(StateArgs a) {
-    using F = PolicyH::F;
-    constexpr bool OUT = !SUMMARY;
-    // Tile buffers: three where LDS allows (copies run two chunks ahead), two
-    // for the forward (one chunk ahead).
-    constexpr int NB = OUT ? 2 : 3;
-    __shared__ __attribute__((aligned(16))) f16 kt[NB][BT * DK];                          // k*b^G
-    __shared__ __attribute__((aligned(16))) f16 qt[OUT ? NB : 1][OUT ? BT * DK : 8];      // q*b^G
-    __shared__ __attribute__((aligned(16))) f16 gt[NB][BT * DK];                          // k*b^{G_L-G}
-    __shared__ __attribute__((aligned(16))) f16 Tt[NB][BT * BT];
-    __shared__ __attribute__((aligned(16))) f16 Pt[OUT ? NB : 1][OUT ? BT * BT : 8];
-    __shared__ __attribute__((aligned(16))) bf16 vt[NB][BT * BV];                         // v rows, 32 columns
-    __shared__ __attribute__((aligned(16))) uint32_t cb[NB][CFB / 4];                    // per-row coefficient block
-
-    const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int H = a.H;
-    const int L = blockIdx.x, xcd = L & 7, slot = L >> 3;
-    const int tile = slot % a.ntiles + a.tile0;
-    const int pair = (slot / a.ntiles) * 8 + xcd;
-    if (pair >= a.n_pairs) return;
-    const int pu = pair / H, head = pair - pu * H;
-    const int u = a.order ? a.order[pu] : pu;
-    if ((unsigned)u >= (unsigned)a.um.n_units) return;
-    const UnitInfo ui = uniform(unit_info(a.um, u));
-    const int c0 = tile * BV;
-    const bool mcols = SUMMARY && c0 >= DV;         // transfer-map columns: v = 0, start at I
-    const int vc0 = mcols ? c0 - DV : c0;
-    const int nch = ui.nch;
-    const uint32_t tokstride = (uint32_t)H * DK;
-    auto chunk_len = [&](int c) {
-        int l = ui.len - c * BT;
-        return __builtin_amdgcn_readfirstlane(l < 0 ? 0 : (l > BT ? BT : l));
-    };
-
-    if (wv < 2) {
-        // ======================= compute waves
-        const int col = vc0 + 16 * wv + n;
-        f32x4 h[8];                                  // keys 16 kt8 + 4G + r, column col
-        for (int kt8 = 0; kt8 < 8; ++kt8)
-            for (int r = 0; r < 4; ++r) {
-                const int key = 16 * kt8 + 4 * G + r;
-                float x = 0.0f;
-                if (mcols) x = key == col ? 1.0f : 0.0f;
-                else if (OUT && a.h0) x = a.h0[(((int64_t)u * H + head) * DK + key) * DV + col];
-                h[kt8][r] = x;
-            }
-        auto pack = [](const f32x4& x, const f32x4& y) {
-            F f;
-            for (int e = 0; e < 4; ++e) { f.v[e] = (f16)x[e]; f.v[e + 4] = (f16)y[e]; }
-            return f;
-        };
-        F hb[4];
-        for (int s2 = 0; s2 < 4; ++s2) hb[s2] = pack(h[2 * s2], h[2 * s2 + 1]);
-        // per-lane LDS byte offsets
-        int offA[4], offG[4];
-        for (int s2 = 0; s2 < 4; ++s2) {
-            offA[s2] = n * 256 + (((4 * s2 + G) ^ swz16(n)) << 4);            // row n, granule 4s+G
-            const int rt = 4 * G + (n >> 2);                                    // transposed read row
-            offG[s2] = rt * 256 + (((4 * s2 + (n & 3)) ^ swz16(rt)) << 4);
-        }
-        int offT[2];
-        for (int kk = 0; kk < 2; ++kk) offT[kk] = n * 128 + (((4 * kk + G) ^ swz8(n)) << 4);
-        // v fragment (rows 16 it + 4G + e, column 16 wv + n) by a transposed read
-        const int offV = (4 * G + (n >> 2)) * (BV * 2) + 32 * wv + 8 * (n & 3);
-        auto ldA = [](const f16* t, int byte_off) {
-            F f;
-            f.v = *reinterpret_cast<const f16x8*>(reinterpret_cast<const char*>(t) + byte_off);
-            return f;
-        };
-        // k^T fragment (keys 16 kt8 + n, tokens 32 kk + 4G + e and 32 kk + 16 + 4G + e)
-        auto ldKT = [&](const f16* t, int kt8, int kk) {
-            const char* p = reinterpret_cast<const char*>(t) + offG[kt8 >> 1] + (kt8 & 1) * 8 + kk * 32 * 256;
-            s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, p));
-            s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, p + 16 * 256));
-            f16x4 fx = __builtin_bit_cast(f16x4, x), fy = __builtin_bit_cast(f16x4, y);
-            F f;
-            for (int e = 0; e < 4; ++e) { f.v[e] = fx[e]; f.v[e + 4] = fy[e]; }
-            return f;
-        };
-        lds_barrier();                              // chunk 0 published
-
-        // per-lane element offsets of output rows 4G + r and of state slot rows (keys 4G + r)
-        uint32_t ooff[4];
-        for (int r = 0; r < 4; ++r) ooff[r] = (uint32_t)(4 * G + r) * tokstride + col;
-        uint32_t hoff[4];
-        for (int r = 0; r < 4; ++r) hoff[r] = (uint32_t)(4 * G + r) * DV + col;
-        for (int c = 0; c < nch; ++c) {
-            // an opaque copy of the chunk index keeps the compiler from turning
-            // every per-lane address into a loop-carried 64-bit pointer
-            const int cu = __builtin_amdgcn_readfirstlane(c);
-            const int tb = NB == 2 ? cu & 1 : cu % NB;   // tile buffers
-            const int len = chunk_len(cu);
-            const int64_t t0 = ui.start + (int64_t)cu * BT;
-            const int64_t ch = (int64_t)(ui.cbase + cu) * H + head;
-            if (OUT && a.hslot) {
-                float* hs = a.hslot + ch * (DK * DV);
-                for (int kt8 = 0; kt8 < 8; ++kt8)
-                    for (int r = 0; r < 4; ++r) hs[16 * kt8 * DV + hoff[r]] = h[kt8][r];
-            }
-            const f16* K = kt[tb];
-            const f16* Q = qt[OUT ? tb : 0];
-            const f16* Tc = Tt[tb];
-            const f16* Pc = Pt[OUT ? tb : 0];
-            const f16* KG = gt[tb];
-            // The step runs as a pipeline over the four 16-row tiles: while the
-            // MFMAs of one row tile run, the VALU work of the previous one (Y,
-            // v_new scaling, the state decay) and the LDS reads of the next one
-            // are in flight. Scheduling fences keep the LDS reads of a stage
-            // ahead of the MFMAs that consume them.
-            F fa[2][4], fb[2][4];                      // k and q fragments of two row tiles
-            auto ldRow = [&](int it, F* k4, F* q4) {
-                for (int s2 = 0; s2 < 4; ++s2) {
-                    k4[s2] = ldA(K, offA[s2] + it * 16 * 256);
-                    if (OUT) q4[s2] = ldA(Q, offA[s2] + it * 16 * 256);
-                }
-            };
-            f32x4 kh[4], qh[4];
-            auto mmaRow = [&](int it, const F* k4, const F* q4) {
-                kh[it] = qh[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-                for (int s2 = 0; s2 < 4; ++s2) {
-                    PolicyH::mma(kh[it], k4[s2], hb[s2]);
-                    if (OUT) PolicyH::mma(qh[it], q4[s2], hb[s2]);
-                }
-            };
-            // the per-row data of the chunk, read first so that no later wait drains it
-            const f16* cbh = reinterpret_cast<const f16*>(cb[tb]);
-            f16x8 cyv[2], btv[2];
-            for (int h2 = 0; h2 < 2; ++h2) {
-                cyv[h2] = *reinterpret_cast<const f16x8*>(&cbh[CF_CY + 16 * G + 8 * h2]);
-                btv[h2] = *reinterpret_cast<const f16x8*>(&cbh[CF_BETA + 16 * G + 8 * h2]);
-            }
-            s16x4 vraw[4];
-            for (int it = 0; it < 4; ++it)
-                vraw[it] = mcols ? s16x4{0, 0, 0, 0}
-                                 : __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                       LDS_PTR(s16x4, reinterpret_cast<const char*>(vt[tb]) + offV + it * 16 * BV * 2));
-            auto coef = [](const f16x8* v, int it, int r) { return (float)v[it >> 1][4 * (it & 1) + r]; };
-            const float* cbf = reinterpret_cast<const float*>(cb[tb]);
-            auto decay = [&](int kt8) {                // h = Diag(b^{G_L}) h for keys 16 kt8 + 4G + r
-                const f32x4 gv = *reinterpret_cast<const f32x4*>(&cbf[CF_GL + 16 * kt8 + 4 * G]);
-                for (int r = 0; r < 4; ++r) h[kt8][r] *= gv[r];
-            };
-            f32x4 y[4];
-            auto mkY = [&](int it) {                   // Y = beta v - beta b^G (K h)
-                for (int r = 0; r < 4; ++r) {
-                    const float vv = __builtin_bit_cast(float, (uint32_t)(uint16_t)vraw[it][r] << 16);
-                    y[it][r] = __builtin_fmaf(coef(btv, it, r), vv, -coef(cyv, it, r) * kh[it][r]);
-                }
-            };
-            f32x4 vn[4], vp[4];
-            auto scaleVn = [&](int it) { vp[it] = vn[it]; };   // the gated keys carry b^{G_L - G}
-            F ft[4][2], fp[4][2], fg0[8], fg1[8];
-            // output rows of tile it: scale (b^G (q h) + P v_new); rows past the
-            // chunk end fall outside the buffer range and are dropped
-            auto output = [&](int it, const F& nb0, const F& nb1) {
-                f32x4 o;
-                for (int r = 0; r < 4; ++r) o[r] = qh[it][r];       // q*b^G is prepared
-                PolicyH::mma(o, fp[it][0], nb0);
-                if (it >= 2) PolicyH::mma(o, fp[it][1], nb1);
-                const int64_t rb = ((t0 + 16 * it) * H + head) * DV;
-                const uint32_t nrow = (uint32_t)max(len - 16 * it, 0);
-                if (OBF) {
-                    const rsrc_t ro = make_rsrc(reinterpret_cast<bf16*>(a.o) + rb, nrow * tokstride * 2);
-                    for (int r = 0; r < 4; ++r)
-                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (bf16)(a.scale * o[r])), ro, ooff[r] * 2, 0, CP_NT);
-                } else {
-                    const rsrc_t ro = make_rsrc(reinterpret_cast<float*>(a.o) + rb, nrow * tokstride * 4);
-                    for (int r = 0; r < 4; ++r) __builtin_amdgcn_raw_buffer_store_b32(f2u(a.scale * o[r]), ro, ooff[r] * 4, 0, CP_NT);
-                }
-            };
-
-            // ---- stage 0: fragments of row tiles 0 and 1
-            ldRow(0, fa[0], fb[0]);
-            ldRow(1, fa[1], fb[1]);
-            __builtin_amdgcn_sched_barrier(0);
-            // ---- row tile 0
-            mmaRow(0, fa[0], fb[0]);
-            decay(0);
-            decay(1);
-            __builtin_amdgcn_sched_barrier(0);
-            ldRow(2, fa[0], fb[0]);
-            for (int it = 0; it < 2; ++it) ft[it][0] = ldA(Tc, offT[0] + it * 16 * 128);
-            __builtin_amdgcn_sched_barrier(0);
-            // ---- row tile 1
-            mmaRow(1, fa[1], fb[1]);
-            mkY(0);
-            decay(2);
-            decay(3);
-            __builtin_amdgcn_sched_barrier(0);
-            ldRow(3, fa[1], fb[1]);
-            for (int it = 2; it < 4; ++it) {
-                ft[it][0] = ldA(Tc, offT[0] + it * 16 * 128);
-                ft[it][1] = ldA(Tc, offT[1] + it * 16 * 128);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // ---- row tile 2; v_new of rows 0..31
-            mmaRow(2, fa[0], fb[0]);
-            mkY(1);
-            const F yb0 = pack(y[0], y[1]);
-            for (int it = 0; it < 2; ++it) {
-                vn[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-                PolicyH::mma(vn[it], ft[it][0], yb0);
-            }
-            decay(4);
-            decay(5);
-            __builtin_amdgcn_sched_barrier(0);
-            for (int kt8 = 0; kt8 < 8; ++kt8) fg0[kt8] = ldKT(KG, kt8, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            // ---- row tile 3; scaled v_new of rows 0..31
-            mmaRow(3, fa[1], fb[1]);
-            scaleVn(0);
-            scaleVn(1);
-            const F vb0 = pack(vp[0], vp[1]);
-            mkY(2);
-            decay(6);
-            decay(7);
-            __builtin_amdgcn_sched_barrier(0);
-            if (OUT)
-                for (int it = 0; it < 4; ++it) {
-                    fp[it][0] = ldA(Pc, offT[0] + it * 16 * 128);
-                    if (it >= 2) fp[it][1] = ldA(Pc, offT[1] + it * 16 * 128);
-                }
-            __builtin_amdgcn_sched_barrier(0);
-            // ---- v_new of rows 32..63; state update from the first 32 tokens
-            mkY(3);
-            const F yb1 = pack(y[2], y[3]);
-            for (int it = 2; it < 4; ++it) {
-                vn[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-                PolicyH::mma(vn[it], ft[it][0], yb0);
-                PolicyH::mma(vn[it], ft[it][1], yb1);
-            }
-            for (int kt8 = 0; kt8 < 8; ++kt8) PolicyH::mma(h[kt8], fg0[kt8], vb0);
-            F nb0;
-            if (OUT) {
-                nb0 = pack(vn[0], vn[1]);
-                output(0, nb0, nb0);
-                output(1, nb0, nb0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            for (int kt8 = 0; kt8 < 8; ++kt8) fg1[kt8] = ldKT(KG, kt8, 1);
-            __builtin_amdgcn_sched_barrier(0);
-            // ---- state update from the last 32 tokens; remaining output rows
-            scaleVn(2);
-            scaleVn(3);
-            const F vb1 = pack(vp[2], vp[3]);
-            for (int kt8 = 0; kt8 < 8; ++kt8) PolicyH::mma(h[kt8], fg1[kt8], vb1);
-            if (OUT) {
-                const F nb1 = pack(vn[2], vn[3]);
-                output(2, nb0, nb1);
-                output(3, nb0, nb1);
-            }
-            for (int s2 = 0; s2 < 4; ++s2) hb[s2] = pack(h[2 * s2], h[2 * s2 + 1]);
-            lds_barrier();                          // chunk c consumed, chunk c+1 published
-        }
-        // ---- results
-        for (int kt8 = 0; kt8 < 8; ++kt8)
-            for (int r = 0; r < 4; ++r) {
-                const int key = 16 * kt8 + 4 * G + r;
-                const int64_t uh = (int64_t)u * H + head;
-                if (SUMMARY) {
-                    if (mcols) { if (a.M) a.M[(uh * DK + key) * DK + col] = h[kt8][r]; }
-                    else if (a.S_ext) a.S_ext[(uh * DK + key) * DV + col] = h[kt8][r];
-                } else if (a.hfinal) {
-                    a.hfinal[(uh * DK + key) * DV + col] = h[kt8][r];
-                }
-            }
-    } else {
-        // ======================= copy waves
-        // Direct global-to-LDS loads (16 bytes per lane, lane i to base + 16 i;
-        // the source addresses apply the granule swizzles) of the gated fp16
-        // k and q tiles (k*b^G, q*b^G, k*b^{G_L-G}), T, P, the v rows of the
-        // column tile (buffer loads: rows past the chunk end read as zero) and
-        // the per-row coefficient block. The waves issue no other vector
-        // memory operations, so the number of copies in flight is known
-        // exactly: each step waits for all but the copies just issued for the
-        // chunk ahead.
-        typedef __attribute__((address_space(3))) void lds_void;
-        const bool s0 = wv == 2;
-        constexpr int D0 = 16 + (OUT ? 16 : 0) + 4 + (SUMMARY ? 0 : 8);
-        constexpr int D1 = (OUT ? 16 + 8 : 0) + (!OUT ? 16 : 0) + (SUMMARY ? 8 : 0) + 1;
-        auto dma = [&](int c_, int buf) {
-            const int c = __builtin_amdgcn_readfirstlane(c_);
-            const int len = chunk_len(c);
-            const int64_t t0 = ui.start + (int64_t)c * BT;
-            const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
-            const f16* ks = reinterpret_cast<const f16*>(a.ws.kd) + ch * (BT * DK);
-            const f16* qs = reinterpret_cast<const f16*>(a.ws.qg) + ch * (BT * DK);
-            const f16* gs = reinterpret_cast<const f16*>(a.ws.kg) + ch * (BT * DK);
-            const f16* Ts = reinterpret_cast<const f16*>(a.ws.Tm) + ch * (BT * BT);
-            const f16* Ps = reinterpret_cast<const f16*>(a.ws.P) + ch * (BT * BT);
-            const uint32_t* cs = reinterpret_cast<const uint32_t*>(a.ws.cfh) + ch * (CFB / 4);
-            auto tile128 = [&](const f16* src, f16* dst) {       // 64 x 128: copy m covers rows 4m .. 4m+3
-                for (int m = 0; m < 16; ++m) {
-                    const int row = 4 * m + (lane >> 4);
-                    __builtin_amdgcn_global_load_lds(src + row * DK + 8 * ((lane & 15) ^ swz16(row)),
-                                                     (lds_void*)(dst + m * 512), 16, 0, 0);
-                }
-            };
-            auto tile64 = [&](const f16* src, f16* dst) {        // 64 x 64: copy m covers rows 8m .. 8m+7
-                for (int m = 0; m < 8; ++m) {
-                    const int row = 8 * m + (lane >> 3);
-                    __builtin_amdgcn_global_load_lds(src + row * BT + 8 * ((lane & 7) ^ swz8(row)),
-                                                     (lds_void*)(dst + m * 512), 16, 0, 0);
-                }
-            };
-            auto vrows = [&]() {   // copy m covers rows 16m .. 16m+15, 4 lanes per row
-                const rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(a.v) + (t0 * H + head) * DV + vc0,
-                                            (uint32_t)len * tokstride * 2);
-                for (int m = 0; m < 4; ++m)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vt[buf] + m * 512), 16,
-                                                             (16 * m + (lane >> 2)) * tokstride * 2 + 16 * (lane & 3), 0, 0, 0);
-            };
-            if (s0) {
-                tile128(ks, kt[buf]);
-                if (OUT) tile128(gs, gt[buf]);
-                vrows();
-                if (OUT) tile64(Ts, Tt[buf]);
-            } else {
-                if (OUT) {
-                    tile128(qs, qt[OUT ? buf : 0]);
-                    tile64(Ps, Pt[OUT ? buf : 0]);
-                } else {
-                    tile128(gs, gt[buf]);
-                    tile64(Ts, Tt[buf]);
-                }
-                __builtin_amdgcn_global_load_lds(cs + 4 * lane, (lds_void*)cb[buf], 16, 0, 0);
-            }
-        };
-        auto wait_copies = [&](bool leave_next) {
-            // all but the copies of the chunk after next (issued last) have landed
-            asm volatile("" ::: "memory");
-            if (leave_next) {
-                if (s0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(D0));
-                else __builtin_amdgcn_s_waitcnt(waitcnt_vm(D1));
-            } else {
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-            }
-            asm volatile("" ::: "memory");
-        };
-        if (nch > 0) {
-            dma(0, 0);
-            if (NB == 3) {
-                asm volatile("" ::: "memory");
-                dma(min(1, nch - 1), 1);
-            }
-            wait_copies(NB == 3);
-        }
-        lds_barrier();
-        for (int c = 0; c < nch; ++c) {
-            // the chunk index is clamped, so every step issues the same copies;
-            // the target buffer was released by the chunk before this one
-            const int cn = min(c + NB - 1, nch - 1);
-            dma(cn, NB == 2 ? (c + 1) & 1 : (c + 2) % 3);
-            wait_copies(NB == 3);
-            lds_barrier();
-        }
-    }
-}
-
-// ------------------------------------------------------------------ state pass, split keys (scalar gate)
+// ------------------------------------------------------------------ state pass, split keys (bf16)
 // Workgroup of 8 waves for one (unit, head, 32-column tile). Compute wave
 // w < 4 owns value columns 16 (w & 1) .. +15 and keys 64 (w >> 1) .. +63 of
 // the fp32 state, so the four compute waves run on all four SIMDs. At the
@@ -1743,22 +1322,29 @@ __global__ __launch_bounds__(HT) void state_kernel_pk(StateArgs a) {
 // c, a full step before they are written out. Rows past the chunk end read
 // as zero. The compute waves leave their output rows in an LDS tile; one
 // step later the streaming waves store them as whole 128-byte row segments.
+// Per-key gate (PK): the streaming waves copy the prepared k b^G, q b^G and
+// k b^{G_L - G} tiles (already fp16 in op_pos order) into the same layout;
+// k.h uses k b^G, the update uses k b^{G_L - G} and decays each key by its
+// own b^{G_L}, the output uses q b^G. The third tile leaves no room for the
+// output staging, so the compute waves store their output rows themselves.
 constexpr int KSW = 8;
 constexpr int OXP = BV + 4;        // row pitch (floats) of the output tile
 constexpr int KST = 64 * KSW;
 
-template <bool SUMMARY, bool OBF>
+template <bool SUMMARY, bool OBF, bool PK>
 __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
     using F = PolicyH::F;
     constexpr bool OUT = !SUMMARY;
-    __shared__ __attribute__((aligned(16))) f16 kt[2][BT * DK];
-    __shared__ __attribute__((aligned(16))) f16 qt[OUT ? 2 : 1][OUT ? BT * DK : 8];
+    constexpr bool OXS = OUT && !PK;    // output rows staged in LDS (scalar gate)
+    __shared__ __attribute__((aligned(16))) f16 kt[2][BT * DK];                   // k, or per key k b^G
+    __shared__ __attribute__((aligned(16))) f16 qt[OUT ? 2 : 1][OUT ? BT * DK : 8];   // q, or q b^G
+    __shared__ __attribute__((aligned(16))) f16 gt[PK ? 2 : 1][PK ? BT * DK : 8];     // per key: k b^{G_L - G}
     __shared__ __attribute__((aligned(16))) f16 Tt[2][BT * BT];
     __shared__ __attribute__((aligned(16))) f16 Pt[OUT ? 2 : 1][OUT ? BT * BT : 8];
     __shared__ __attribute__((aligned(16))) bf16 vt[2][BT * BV];
     __shared__ __attribute__((aligned(16))) float cb[2][CFS / 4];
     __shared__ __attribute__((aligned(16))) f16x8 hx[2][4][2][64];   // [step parity][wave][slice][lane]
-    __shared__ __attribute__((aligned(16))) float ox[OUT ? 2 : 1][OUT ? BT * OXP : 4];   // scaled output rows
+    __shared__ __attribute__((aligned(16))) float ox[OXS ? 2 : 1][OXS ? BT * OXP : 4];   // scaled output rows
 
     const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1859,6 +1445,7 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
                     for (int r = 0; r < 4; ++r) hs[16 * j * DV + hoff[r]] = h[j][r];
             }
             const f16* K = kt[tb];
+            const f16* KG = PK ? gt[tb] : kt[tb];    // keys of the state update
             const f16* Q = qt[OUT ? tq : 0];
             const f16* Tc = Tt[tb];
             const f16* Pc = Pt[OUT ? tb : 0];
@@ -1866,12 +1453,24 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
             for (int j2 = 0; j2 < 2; ++j2) hb[2 * (1 - kq) + j2].v = hx[tq][partner][j2][lane];
             // per-row coefficients: lane G holds rows 16 it + 4G + r at [16G + 4it + r]
             const float* cf = cb[tb];
-            f32x4 cpf[4], bg[4];
-            for (int it = 0; it < 4; ++it) {
-                cpf[it] = *reinterpret_cast<const f32x4*>(&cf[CS_CP + 16 * G + 4 * it]);
-                bg[it] = *reinterpret_cast<const f32x4*>(&cf[CS_BG + 16 * G + 4 * it]);
+            // scalar gate: b^{G_L - G}, b^G per row, b^{G_L}; per key: beta per
+            // row (fp16) and b^{G_L} of this wave's keys
+            f32x4 cpf[4], bg[4], gl[4];
+            float eL = 1.0f;
+            if (!PK) {
+                for (int it = 0; it < 4; ++it) {
+                    cpf[it] = *reinterpret_cast<const f32x4*>(&cf[CS_CP + 16 * G + 4 * it]);
+                    bg[it] = *reinterpret_cast<const f32x4*>(&cf[CS_BG + 16 * G + 4 * it]);
+                }
+                eL = cf[CS_BG + lane_order(len > 0 ? len - 1 : 0)];
+            } else {
+                const f16* cbh = reinterpret_cast<const f16*>(cf);
+                for (int it = 0; it < 4; ++it) {
+                    const f16x4 b4 = *reinterpret_cast<const f16x4*>(&cbh[CF_BETA + 16 * G + 4 * it]);
+                    for (int r = 0; r < 4; ++r) bg[it][r] = (float)b4[r];
+                }
+                for (int j = 0; j < 4; ++j) gl[j] = *reinterpret_cast<const f32x4*>(&cf[CF_GL + 64 * kq + 16 * j + 4 * G]);
             }
-            const float eL = cf[CS_BG + lane_order(len > 0 ? len - 1 : 0)];
             s16x4 vraw[4];
             for (int it = 0; it < 4; ++it)
                 vraw[it] = mcols ? s16x4{0, 0, 0, 0}
@@ -1887,7 +1486,7 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
                 for (int s2 = 0; s2 < 4; ++s2) PolicyH::mma(kh, ldA(K, offA[s2] + it * 16 * 256), hb[s2]);
                 for (int r = 0; r < 4; ++r) {
                     const float vv = __builtin_bit_cast(float, (uint32_t)(uint16_t)vraw[it][r] << 16);
-                    y[r] = __builtin_fmaf(-bg[it][r], kh[r], vv);
+                    y[r] = PK ? bg[it][r] * (vv - kh[r]) : __builtin_fmaf(-bg[it][r], kh[r], vv);
                 }
             };
             f32x4 y[4], vn[4], vp[4];
@@ -1902,18 +1501,18 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
             khY(3, y[3]);
             // ---- state of this wave's keys: h = b^{G_L} h + kg^T v_new'
             for (int it = 0; it < 2; ++it)
-                for (int r = 0; r < 4; ++r) vp[it][r] = vn[it][r] * cpf[it][r];
+                for (int r = 0; r < 4; ++r) vp[it][r] = PK ? vn[it][r] : vn[it][r] * cpf[it][r];
             const F vb0 = pack(vp[0], vp[1]);
             for (int j = 0; j < 4; ++j) {
-                for (int r = 0; r < 4; ++r) h[j][r] *= eL;
-                PolicyH::mma(h[j], ldKT(K, j, 0), vb0);
+                for (int r = 0; r < 4; ++r) h[j][r] *= PK ? gl[j][r] : eL;
+                PolicyH::mma(h[j], ldKT(KG, j, 0), vb0);
             }
             const F yb1 = pack(y[2], y[3]);
             for (int it = 2; it < 4; ++it) PolicyH::mma(vn[it], ldA(Tc, offT[1] + it * 16 * 128), yb1);
             for (int it = 2; it < 4; ++it)
-                for (int r = 0; r < 4; ++r) vp[it][r] = vn[it][r] * cpf[it][r];
+                for (int r = 0; r < 4; ++r) vp[it][r] = PK ? vn[it][r] : vn[it][r] * cpf[it][r];
             const F vb1 = pack(vp[2], vp[3]);
-            for (int j = 0; j < 4; ++j) PolicyH::mma(h[j], ldKT(K, j, 1), vb1);
+            for (int j = 0; j < 4; ++j) PolicyH::mma(h[j], ldKT(KG, j, 1), vb1);
             // ---- output rows of this wave's half: scale (b^G (q h) + P v_new)
             if (OUT) {
                 const F nb0 = pack(vn[0], vn[1]), nb1 = pack(vn[2], vn[3]);
@@ -1922,10 +1521,27 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
                     f32x4 qh = {0.f, 0.f, 0.f, 0.f};
                     for (int s2 = 0; s2 < 4; ++s2) PolicyH::mma(qh, ldA(Q, offA[s2] + it * 16 * 256), hb[s2]);
                     f32x4 o;
-                    for (int r = 0; r < 4; ++r) o[r] = bg[it][r] * qh[r];
+                    for (int r = 0; r < 4; ++r) o[r] = PK ? qh[r] : bg[it][r] * qh[r];   // per key: q b^G is prepared
                     PolicyH::mma(o, ldA(Pc, offT[0] + it * 16 * 128), nb0);
                     if (kq == 1) PolicyH::mma(o, ldA(Pc, offT[1] + it * 16 * 128), nb1);
-                    for (int r = 0; r < 4; ++r) ox[OUT ? tb : 0][(16 * it + 4 * G + r) * OXP + 16 * cg + n] = a.scale * o[r];
+                    if (OXS) {
+                        for (int r = 0; r < 4; ++r) ox[OXS ? tb : 0][(16 * it + 4 * G + r) * OXP + 16 * cg + n] = a.scale * o[r];
+                    } else {
+                        // per key: stored from here, non-temporal; rows past the
+                        // chunk end fall outside the buffer range and are dropped
+                        const int64_t rb = ((t0 + 16 * it) * H + head) * DV + vc0 + 16 * cg;   // wave-uniform
+                        const uint32_t nrow = (uint32_t)max(len - 16 * it, 0);
+                        for (int r = 0; r < 4; ++r) {
+                            const uint32_t off = (uint32_t)(4 * G + r) * tokstride + n;
+                            if (OBF) {
+                                const rsrc_t ro = make_rsrc(reinterpret_cast<bf16*>(a.o) + rb, nrow * tokstride * 2);
+                                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (bf16)(a.scale * o[r])), ro, off * 2, 0, CP_NT);
+                            } else {
+                                const rsrc_t ro = make_rsrc(reinterpret_cast<float*>(a.o) + rb, nrow * tokstride * 4);
+                                __builtin_amdgcn_raw_buffer_store_b32(f2u(a.scale * o[r]), ro, off * 4, 0, CP_NT);
+                            }
+                        }
+                    }
                 }
             }
             // after the output (q h uses the entry state): publish this wave's half of the next state operand
@@ -1963,23 +1579,42 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
             // 16-byte pieces at keys 32s + 8m and 32s + 16 + 8m, which make up
             // operand granules 4s + 2m and 4s + 2m + 1 (i = 2 role, 2 role + 1)
             const int rl = lane >> 3, s = (lane & 7) >> 1, m = lane & 1;
-            // [0..3] k, [4..7] q, [8..9] T, [10..11] P, [12] v, [13] coefficients
-            struct Set { u32x4 x[14]; };
+            // [0..3] k, [4..7] q, [8..9] T, [10..11] P, [12] v, [13] coefficients,
+            // per key [14..17] k b^{G_L - G}
+            struct Set { u32x4 x[PK ? 18 : 14]; };
             auto load = [&](int c_, Set& d) {
                 const int c = __builtin_amdgcn_readfirstlane(c_);
                 const int len = chunk_len(c);
                 const int64_t t0 = ui.start + (int64_t)c * BT;
                 const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
                 const uint32_t span = len > 0 ? (uint32_t)(len - 1) * rowb + DK * 2 : 0;
+                if (!PK) {
 #pragma unroll
-                for (int kq = 0; kq < (OUT ? 2 : 1); ++kq) {
-                    const rsrc_t rx = make_rsrc(reinterpret_cast<const bf16*>(kq ? a.q : a.k) + (t0 * H + head) * DK, span);
+                    for (int kq = 0; kq < (OUT ? 2 : 1); ++kq) {
+                        const rsrc_t rx = make_rsrc(reinterpret_cast<const bf16*>(kq ? a.q : a.k) + (t0 * H + head) * DK, span);
 #pragma unroll
-                    for (int ii = 0; ii < 2; ++ii)
+                        for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-                        for (int p = 0; p < 2; ++p)
-                            d.x[4 * kq + 2 * ii + p] = __builtin_amdgcn_raw_buffer_load_b128(
-                                rx, (8 * (2 * role + ii) + rl) * rowb + (32 * s + 16 * p + 8 * m) * 2, 0, 0);
+                            for (int p = 0; p < 2; ++p)
+                                d.x[4 * kq + 2 * ii + p] = __builtin_amdgcn_raw_buffer_load_b128(
+                                    rx, (8 * (2 * role + ii) + rl) * rowb + (32 * s + 16 * p + 8 * m) * 2, 0, 0);
+                    }
+                } else {
+                    // the prepared gated tiles (fp16, op_pos order, 256-byte rows):
+                    // lane (row 8i + l/8) takes granules 2 (l%8) and 2 (l%8) + 1
+#pragma unroll
+                    for (int t3 = 0; t3 < 3; ++t3) {
+                        if (t3 == 1 && !OUT) continue;
+                        const void* src = t3 == 0 ? a.ws.kd : (t3 == 1 ? a.ws.qg : a.ws.kg);
+                        const rsrc_t rx = make_rsrc(reinterpret_cast<const f16*>(src) + ch * (BT * DK), BT * DK * 2);
+                        const int xb = t3 == 0 ? 0 : (t3 == 1 ? 4 : 14);
+#pragma unroll
+                        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                            for (int p = 0; p < 2; ++p)
+                                d.x[xb + 2 * ii + p] = __builtin_amdgcn_raw_buffer_load_b128(
+                                    rx, (8 * (2 * role + ii) + rl) * 256 + 16 * (2 * (lane & 7) + p), 0, 0);
+                    }
                 }
 #pragma unroll
                 for (int tp = 0; tp < (OUT ? 2 : 1); ++tp) {
@@ -1999,13 +1634,33 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
                 d.x[12] = __builtin_amdgcn_raw_buffer_load_b128(rv, (16 * role + (lane >> 2)) * rowb + 16 * (lane & 3), 0, 0);
                 if (role == 0) {
                     const rsrc_t rc = make_rsrc(reinterpret_cast<const char*>(a.ws.cfh) + ch * CFS, CFS);
-                    // only floats 64..191 of the block are used
-                    d.x[13] = __builtin_amdgcn_raw_buffer_load_b128(rc, lane < 16 || lane >= 48 ? 0x40000000u : 16u * lane, 0, 0);
+                    // used: scalar gate floats 64..191; per key the beta row
+                    // (bytes 384..511) and the fp32 b^{G_L} (bytes 512..1023)
+                    const bool used = PK ? lane >= 24 : (lane >= 16 && lane < 48);
+                    d.x[13] = __builtin_amdgcn_raw_buffer_load_b128(rc, used ? 16u * lane : 0x40000000u, 0, 0);
                 }
             };
             auto store = [&](const Set& d, int buf) {
+                if (PK) {
+                    // granule g of row r at g ^ swzk(r), odd granules with swapped halves
 #pragma unroll
-                for (int kq = 0; kq < (OUT ? 2 : 1); ++kq) {
+                    for (int t3 = 0; t3 < 3; ++t3) {
+                        if (t3 == 1 && !OUT) continue;
+                        char* dx = reinterpret_cast<char*>(t3 == 0 ? kt[buf] : (t3 == 1 ? qt[OUT ? buf : 0] : gt[PK ? buf : 0]));
+                        const int xb = t3 == 0 ? 0 : (t3 == 1 ? 4 : 14);
+#pragma unroll
+                        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                            for (int p = 0; p < 2; ++p) {
+                                const int row = 8 * (2 * role + ii) + rl, g = 2 * (lane & 7) + p;
+                                const u32x4 w = d.x[xb + 2 * ii + p];
+                                *reinterpret_cast<u32x4*>(dx + row * 256 + ((g ^ swzk(row)) << 4)) =
+                                    p ? u32x4{w[2], w[3], w[0], w[1]} : w;
+                            }
+                    }
+                }
+#pragma unroll
+                for (int kq = 0; kq < (OUT && !PK ? 2 : (PK ? 0 : 1)); ++kq) {
                     char* dx = reinterpret_cast<char*>(kq ? qt[OUT ? buf : 0] : kt[buf]);
 #pragma unroll
                     for (int ii = 0; ii < 2; ++ii) {
@@ -2034,7 +1689,7 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
                 const int len = chunk_len(co);
                 const int64_t rb = ((ui.start + (int64_t)co * BT + 16 * role) * H + head) * DV + vc0;
                 const uint32_t nrow = (uint32_t)max(len - 16 * role, 0);
-                const float* src = ox[OUT ? (co & 1) : 0];
+                const float* src = ox[OXS ? (co & 1) : 0];
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     const int rr = 8 * i + (lane >> 3), c4 = 4 * (lane & 7);
@@ -2067,17 +1722,17 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
             // steps repeat the last chunk.
             for (int c = 0; c < nch; c += 2) {
                 load(min(c + 2, nch - 1), sa);
-                if (OUT && c > 0) store_out(c - 1);
+                if (OXS && c > 0) store_out(c - 1);
                 store(sb, 1);
                 lds_barrier();
                 if (c + 1 < nch) {
                     load(min(c + 3, nch - 1), sb);
-                    if (OUT) store_out(c);
+                    if (OXS) store_out(c);
                     store(sa, 0);
                     lds_barrier();
                 }
             }
-            if (OUT && nch > 0) store_out(nch - 1);
+            if (OXS && nch > 0) store_out(nch - 1);
         };
         if (wv == 4) stream(std::integral_constant<int, 0>{});
         else if (wv == 5) stream(std::integral_constant<int, 1>{});
@@ -2257,15 +1912,9 @@ static void launch_state_h(bool summary, StateArgs a, int want_ext, int want_M, 
     if (a.n_pairs == 0 || a.ntiles == 0) return;
     const int groups = (a.n_pairs + 7) / 8;
     dim3 grid(8 * a.ntiles * groups);
-    if (!PK) {
-        if (summary) hipLaunchKernelGGL((state_kernel_ks<true, false>), grid, dim3(KST), 0, s, a);
-        else if (a.o_bf16) hipLaunchKernelGGL((state_kernel_ks<false, true>), grid, dim3(KST), 0, s, a);
-        else hipLaunchKernelGGL((state_kernel_ks<false, false>), grid, dim3(KST), 0, s, a);
-        return;
-    }
-    if (summary) hipLaunchKernelGGL((state_kernel_pk<true, false>), grid, dim3(HT), 0, s, a);
-    else if (a.o_bf16) hipLaunchKernelGGL((state_kernel_pk<false, true>), grid, dim3(HT), 0, s, a);
-    else hipLaunchKernelGGL((state_kernel_pk<false, false>), grid, dim3(HT), 0, s, a);
+    if (summary) hipLaunchKernelGGL((state_kernel_ks<true, false, PK>), grid, dim3(KST), 0, s, a);
+    else if (a.o_bf16) hipLaunchKernelGGL((state_kernel_ks<false, true, PK>), grid, dim3(KST), 0, s, a);
+    else hipLaunchKernelGGL((state_kernel_ks<false, false, PK>), grid, dim3(KST), 0, s, a);
 }
 
 hipError_t launch_state(const Problem& p, const Workspace& ws, const void* q, const void* k,
