@@ -746,8 +746,11 @@ __global__ __launch_bounds__(64) void prep_kernel_h(PrepArgs a) {
 // fp16 operands of the L and P tiles, and the state pass's operands q b^G,
 // k b^G, k b^{G_L-G} go straight to the workspace. L and P are then plain
 // 16x16x32 MFMA tiles, and the inverse runs in LDS over the dead operand
-// tiles. 70.5 KiB of LDS: two workgroups per CU. The phases hand data over
-// through LDS only, so their barriers leave the workspace stores in flight.
+// tiles. q b^{G-G_m} waits in registers and takes over the first operand
+// tile once L is done, and the gate's column sums and reference rows live in
+// the L buffer before L: 50.5 KiB of LDS, three workgroups per CU. The phases
+// hand data over through LDS only, so their barriers leave the workspace
+// stores in flight.
 constexpr int PKL = 136;   // row stride (fp16) of the 64 x 128 operand tiles: 272 bytes
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -759,13 +762,16 @@ __device__ __forceinline__ uint32_t pack_f16x2(float x, float y) {
 }
 
 __global__ __launch_bounds__(256) void prep_kernel_pk(PrepArgs a) {
-    __shared__ __attribute__((aligned(16))) f16 ka[BT * PKL];   // k b^{G-G_m}; T (fp32 64 x 65) once L and P are done
-    __shared__ __attribute__((aligned(16))) f16 kb[BT * PKL];   // k b^{G_m-G}; then the partial products of the inverse
-    __shared__ __attribute__((aligned(16))) f16 qa[BT * PKL];   // q b^{G-G_m}
+    // ka: k b^{G-G_m} for L, then q b^{G-G_m} for P, then T (fp32 64 x 65);
+    // kb: k b^{G_m-G}, then the partial products of the inverse; Ls: the
+    // gate's column sums and reference rows until L is written
+    __shared__ __attribute__((aligned(16))) f16 ka[BT * PKL];
+    __shared__ __attribute__((aligned(16))) f16 kb[BT * PKL];
     __shared__ __attribute__((aligned(16))) float Ls[BT * LDL];
-    __shared__ __attribute__((aligned(16))) float part[4][DK];  // column sums of g over each wave's rows
-    __shared__ __attribute__((aligned(16))) float gref[2][DK];  // G at the middle row and at the last valid row
     __shared__ float bet[BT];
+    float (*part)[DK] = reinterpret_cast<float (*)[DK]>(Ls);            // [4][DK] column sums of g per wave
+    float (*gref)[DK] = reinterpret_cast<float (*)[DK]>(Ls + 4 * DK);   // [2][DK] G at the middle / last valid row
+    f16* qa = ka;
     float* Ts = reinterpret_cast<float*>(ka);
     float* Yb = reinterpret_cast<float*>(kb);
 
@@ -851,7 +857,9 @@ __global__ __launch_bounds__(256) void prep_kernel_pk(PrepArgs a) {
         reinterpret_cast<float*>(a.ws.cfh)[ch * (CFB / 4) + CF_GL + tid] = fpow(gl, a.use_exp2);
     }
 
-    // ---- gated forms: reference-row operands to LDS, state-pass operands out
+    // ---- gated forms: reference-row operands to LDS (q b^{G-G_m} waits in
+    // registers until L is done), state-pass operands out
+    uint32_t qpk[16];
     {
         const float m0 = gref[0][2 * lane], m1 = gref[0][2 * lane + 1];
         const float l0 = gref[1][2 * lane], l1 = gref[1][2 * lane + 1];
@@ -869,7 +877,7 @@ __global__ __launch_bounds__(256) void prep_kernel_pk(PrepArgs a) {
             const float b0 = fpow(m0 - x0, a.use_exp2), b1 = fpow(m1 - x1, a.use_exp2);
             *reinterpret_cast<uint32_t*>(&ka[row * PKL + 2 * lane]) = pack_f16x2(k0 * a0, k1 * a1);
             *reinterpret_cast<uint32_t*>(&kb[row * PKL + 2 * lane]) = pack_f16x2(k0 * b0, k1 * b1);
-            *reinterpret_cast<uint32_t*>(&qa[row * PKL + 2 * lane]) = pack_f16x2(q0 * a0, q1 * a1);
+            qpk[r] = pack_f16x2(q0 * a0, q1 * a1);
             const float d0 = fpow(x0, a.use_exp2), d1 = fpow(x1, a.use_exp2);
             const float c0 = fpow(l0 - x0, a.use_exp2), c1 = fpow(l1 - x1, a.use_exp2);
             if (has_q) qg[row * (DK / 2)] = pack_f16x2(q0 * d0, q1 * d1);
@@ -879,38 +887,51 @@ __global__ __launch_bounds__(256) void prep_kernel_pk(PrepArgs a) {
     }
     lds_barrier();
 
-    // ---- L (strictly lower, 10 tiles) and P (lower incl. diagonal, 10 tiles)
-    // on MFMA, 20 tiles over 4 waves; the 6 zero tiles of P above the diagonal
-    f16* Pw = reinterpret_cast<f16*>(a.ws.P) + ch * (BT * BT);
-    for (int t = w; t < 26; t += 4) {
-        if (t >= 20) {
-            if (!has_q) continue;
-            const int z = t - 20;                                 // (it, jt) with it < jt
-            const int it = z < 3 ? 0 : (z < 5 ? 1 : 2);
-            const int jt = z < 3 ? z + 1 : (z < 5 ? z - 1 : 3);
-            *reinterpret_cast<u32x2*>(Pw + (16 * it + n) * BT + op_pos(16 * jt + 4 * G)) = u32x2{0u, 0u};
-            continue;
-        }
-        const bool isL = t < 10;
-        if (!isL && !has_q) continue;
-        const int tt = isL ? t : t - 10;
-        const int it = tt < 1 ? 0 : tt < 3 ? 1 : tt < 6 ? 2 : 3;
-        const int jt = tt - (it * (it + 1)) / 2;
+    // ---- L (strictly lower, 10 tiles over 4 waves) on MFMA
+    for (int t = w; t < 10; t += 4) {
+        const int it = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+        const int jt = t - (it * (it + 1)) / 2;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < DK / 32; ++kk) {
             const int col = 32 * kk + 8 * G;
-            if (isL) PolicyH::mma(acc, PolicyH::ld(&ka[(16 * it + n) * PKL + col]), PolicyH::ld(&kb[(16 * jt + n) * PKL + col]));
-            else PolicyH::mma(acc, PolicyH::ld(&kb[(16 * jt + n) * PKL + col]), PolicyH::ld(&qa[(16 * it + n) * PKL + col]));
+            PolicyH::mma(acc, PolicyH::ld(&ka[(16 * it + n) * PKL + col]), PolicyH::ld(&kb[(16 * jt + n) * PKL + col]));
         }
-        if (isL) {
-            // acc[r]: row i = 16 it + 4G + r against column j = 16 jt + n
+        // acc[r]: row i = 16 it + 4G + r against column j = 16 jt + n
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * it + 4 * G + r, j = 16 * jt + n;
-                Ls[i * LDL + j] = j < i ? bet[i] * acc[r] : 0.0f;
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * it + 4 * G + r, j = 16 * jt + n;
+            Ls[i * LDL + j] = j < i ? bet[i] * acc[r] : 0.0f;
+        }
+    }
+    lds_barrier();
+    // q b^{G-G_m} over k b^{G-G_m}, which L no longer needs
+    if (has_q) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) *reinterpret_cast<uint32_t*>(&qa[(16 * w + r) * PKL + 2 * lane]) = qpk[r];
+    }
+    lds_barrier();
+
+    // ---- P (lower incl. diagonal, 10 tiles) on MFMA, and the 6 zero tiles
+    // above the diagonal, over 4 waves
+    f16* Pw = reinterpret_cast<f16*>(a.ws.P) + ch * (BT * BT);
+    if (has_q) {
+        for (int t = w; t < 16; t += 4) {
+            if (t >= 10) {
+                const int z = t - 10;                                 // (it, jt) with it < jt
+                const int it = z < 3 ? 0 : (z < 5 ? 1 : 2);
+                const int jt = z < 3 ? z + 1 : (z < 5 ? z - 1 : 3);
+                *reinterpret_cast<u32x2*>(Pw + (16 * it + n) * BT + op_pos(16 * jt + 4 * G)) = u32x2{0u, 0u};
+                continue;
             }
-        } else {
+            const int it = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+            const int jt = t - (it * (it + 1)) / 2;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) {
+                const int col = 32 * kk + 8 * G;
+                PolicyH::mma(acc, PolicyH::ld(&kb[(16 * jt + n) * PKL + col]), PolicyH::ld(&qa[(16 * it + n) * PKL + col]));
+            }
             // acc[r]: row i = 16 it + n against column j = 16 jt + 4G + r
             const int i = 16 * it + n;
             float x[4];
