@@ -159,7 +159,10 @@ gdn_status gdn_varlen_meta(const int32_t* offsets, int32_t n_offsets, int32_t to
  *                  *workspace_bytes and return GDN_OK
  *   stream         HIP stream the work is enqueued on
  * With GDN_FLAG_PREPARE_ONLY, q, v, o, initial_state and final_state are not
- * used and may be NULL.
+ * used and may be NULL. The workspace holds the chunk preparation in a layout
+ * internal to this library (valid for GDN_FLAG_REUSE_PREPARED with the same
+ * descriptor and inputs). Packed units may be processed in any order (the
+ * state pass starts the longest first); results do not depend on it.
  */
 gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, const void* v,
                          const float* g, const void* beta, const float* initial_state, void* o,
