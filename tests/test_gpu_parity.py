@@ -303,6 +303,24 @@ def test_varlen_packed_matches_oracle_and_separate_runs():
         assert torch.equal(f1[0], fin[i])
 
 
+@pytest.mark.parametrize("n_docs", [1500, 2500])
+def test_varlen_many_documents(n_docs):
+    # many short documents: 1500 are ranked longest first over two tiles of
+    # the ordering kernel; above 2048 the units keep their natural order
+    rng = np.random.default_rng(n_docs)
+    lens = [int(x) for x in rng.integers(1, 41, n_docs)]
+    cu = W.cu_from_lengths(lens)
+    T, H = cu[-1], 1
+    print(f"varlen {n_docs} documents, {T} tokens", flush=True)
+    base = W.generate(small(B=1, T=T, H=H), 59)
+    d = {n: base[n][0].contiguous().to(DEV) for n in ("q", "k", "v", "g", "beta")}
+    d.update(scale=base["scale"], offsets=cu, workload=small(B=1, T=T, H=H, layout="TND", n_docs=n_docs))
+    o, fin, _ = run_gpu(d, output_final_state=True)
+    r = run_oracle(d)
+    assert_close(np32(o), r["o"], TOL["bf16"], "many documents o")
+    assert_close(np32(fin), r["final"], TOL["bf16"], "many documents final")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_varlen_increasing_lengths_with_entry_states(dtype):
     # documents in increasing length: the state passes launch them in the
