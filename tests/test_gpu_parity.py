@@ -75,6 +75,32 @@ def test_dense_small(B, T, H, dtype):
     np.testing.assert_allclose(gc, ref, rtol=1e-5, atol=1e-5)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_scalar_gate_base2(dtype):
+    # scalar gate in log2 units (decay 2^g), ragged tail, entry and final states
+    print(f"scalar gate base 2 {dtype}", flush=True)
+    w = small(B=2, T=150, H=3, dtype=dtype, use_exp2=True, gate_coef=0.05)
+    d = to_dev(W.generate(w, 83))
+    S0 = (torch.randn(2, 3, 128, 128, generator=torch.Generator().manual_seed(6)) * 0.3).to(DEV)
+    o, fin, ex = run_gpu(d, initial_state=S0, output_final_state=True, want_h=True)
+    r = run_oracle(d, S0=np32(S0).astype(np.float64), chunk_states=True)
+    tol = TOL[dtype]
+    assert_close(flat_o(o, w), r["o"], tol, "base-2 o")
+    assert_close(np32(fin), r["final"], tol, "base-2 final")
+    assert_close(np32(ex["h"]), r["chunk_states"], tol, "base-2 chunk states")
+
+
+def test_many_heads():
+    # 40 heads: head strides of 10 KiB per token row in q, k, v and o
+    print("many heads", flush=True)
+    w = small(B=1, T=130, H=40)
+    d = to_dev(W.generate(w, 89))
+    o, fin, _ = run_gpu(d, output_final_state=True)
+    r = run_oracle(d)
+    assert_close(flat_o(o, w), r["o"], TOL["bf16"], "40-head o")
+    assert_close(np32(fin), r["final"], TOL["bf16"], "40-head final")
+
+
 @pytest.mark.parametrize("per_key", [False, True])
 def test_bf16_output_is_the_rounded_fp32_output(per_key):
     # o_dtype = bf16 stores the same fp32 result rounded to nearest-even:
