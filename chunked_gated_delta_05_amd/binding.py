@@ -174,12 +174,53 @@ def _desc(q_like, H, dtype, o_dtype, per_key, use_exp2, scale, meta: UnitMeta | 
     return d
 
 
-def _check_inputs(q, k, v, g, beta):
-    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
-        if t is not None and not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    if g is not None and g.dtype != torch.float32:
-        raise ValueError("g must be float32")
+def _check_tensor(name, t, dtype, shape, device):
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _check_inputs(q, k, v, g, beta, meta=None, device_check=True):
+    """Every input against k's dtype, layout and device, before any C call:
+    the C ABI takes bare pointers and cannot check buffer sizes, so this is
+    the guard against reading past a buffer. q and v may be None where the
+    call does not read them. Returns (H, per_key)."""
+    if k is None or k.dim() not in (3, 4):
+        raise ValueError("GDN inputs must have shape [B,T,H,K] or [T,H,K]")
+    if k.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"unsupported dtype {k.dtype}")
+    lead, H, K = tuple(k.shape[:-2]), k.shape[-2], k.shape[-1]
+    _check_tensor("k", k, k.dtype, k.shape, None)
+    if q is not None:
+        _check_tensor("q", q, k.dtype, k.shape, None)
+    if v is not None:
+        _check_tensor("v", v, k.dtype, (*lead, H, v.shape[-1] if v.dim() == k.dim() else -1), None)
+    if g is None or g.dim() not in (k.dim() - 1, k.dim()):
+        raise ValueError("g must be [..., H] (scalar gate) or [..., H, K] (per-key gate)")
+    per_key = g.dim() == k.dim()
+    _check_tensor("g", g, torch.float32, (*lead, H, K) if per_key else (*lead, H), None)
+    _check_tensor("beta", beta, k.dtype, (*lead, H), None)
+    if device_check:
+        _require_gpu(q, k, v, g, beta, meta)
+    return H, per_key
+
+
+def _require_gpu(q, k, v, g, beta, meta):
+    dev = k.device
+    if dev.type != "cuda":
+        raise ValueError(f"inputs must be GPU tensors, got {dev}")
+    for name, t in (("q", q), ("v", v), ("g", g), ("beta", beta)):
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} must be on {dev}, got {t.device}")
+    if meta is not None:
+        for t in (meta.offsets_dev, meta.chunk_offsets_dev, meta.chunk_indices_dev):
+            if t.device != dev:
+                raise ValueError(f"unit metadata must be on {dev}, got {t.device}")
 
 
 def n_units_of(q_like, meta):
@@ -198,6 +239,51 @@ def workspace_bytes(desc: GdnDesc, fn="fwd") -> int:
     return nb.value
 
 
+# ------------------------------------------------------------------ argument checks
+def _state_shape(k, v, meta):
+    return (n_units_of(k, meta), k.shape[-2], k.shape[-1], v.shape[-1])
+
+
+def _fwd_args(q, k, v, g, beta, scale, meta, initial_state, o_dtype, out, final_out, want_final,
+              use_exp2, flags, extras_wanted=()):
+    """Checked arguments of one forward call: (desc, o, final, slots, extras)."""
+    prep_only = bool(flags & FLAG_PREPARE_ONLY)
+    H, per_key = _check_inputs(q, k, None if prep_only else v, g, beta, meta, device_check=False)
+    if not prep_only and (q is None or v is None):
+        raise ValueError("q and v are required unless only preparing")
+    if per_key and q is None and not flags & FLAG_REUSE_PREPARED:
+        raise ValueError("the per-key preparation needs q")
+    if o_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"unsupported output dtype {o_dtype}")
+    if scale is None:
+        scale = k.shape[-1] ** -0.5
+    desc = _desc(k, H, k.dtype, o_dtype, per_key, use_exp2, scale, meta)
+    dev = k.device
+    vv = v if v is not None else k
+    sshape = _state_shape(k, vv, meta)
+    o = fin = None
+    if not prep_only:
+        o = out if out is not None else torch.empty(v.shape, dtype=o_dtype, device=dev)
+        _check_tensor("out", o, o_dtype, v.shape, dev)
+        if want_final or final_out is not None:
+            fin = final_out if final_out is not None else torch.empty(sshape, dtype=torch.float32, device=dev)
+            _check_tensor("final_out", fin, torch.float32, sshape, dev)
+    if initial_state is not None:
+        _check_tensor("initial_state", initial_state, torch.float32, sshape, dev)
+    extras = {}
+    tokens = k.shape[0] * k.shape[1] if k.dim() == 4 else k.shape[0]
+    if "g_cumsum" in extras_wanted:
+        extras["g_cumsum"] = torch.empty(g.shape, dtype=torch.float32, device=dev)
+    if "A" in extras_wanted:
+        extras["A"] = torch.empty((tokens, H, 64), dtype=torch.float32, device=dev)
+    if "h" in extras_wanted:
+        n_chunks = meta.n_chunks if meta is not None else k.shape[0] * ((k.shape[1] + 63) // 64)
+        extras["h"] = torch.empty((n_chunks, H, k.shape[-1], vv.shape[-1]), dtype=torch.float32, device=dev)
+    _require_gpu(q, k, None if prep_only else v, g, beta, meta)
+    slots = GdnSlots(_ptr(extras.get("g_cumsum")), _ptr(extras.get("A")), _ptr(extras.get("h")))
+    return desc, o, fin, slots, extras
+
+
 # ------------------------------------------------------------------ entry points
 def gdn_chunk_fwd(q, k, v, g, beta, scale=None, *, meta: UnitMeta | None = None, initial_state=None,
                   output_final_state=False, use_exp2=False, o_dtype=torch.float32,
@@ -206,43 +292,18 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale=None, *, meta: UnitMeta | None = None,
     """Chunked gated delta rule forward through libgdn.
 
     q, k [B,T,H,K] (BSND) or [T,H,K] (TND, needs meta); v like q; g fp32
-    [..,H] (scalar gate) or [..,H,K] (per-key gate); beta [..,H]. Returns
-    (o, final_state or None, extras dict)."""
-    _check_inputs(q, k, v, g, beta)
-    H = k.shape[-2]
-    per_key = g.dim() == k.dim()
-    if scale is None:
-        scale = k.shape[-1] ** -0.5
-    desc = _desc(k, H, k.dtype, o_dtype, per_key, use_exp2, scale, meta)
+    [..,H] (scalar gate) or [..,H,K] (per-key gate); beta [..,H]. Given
+    out / final_out buffers are written in place (out: o_dtype, v's shape;
+    final_out: fp32 [units,H,K,V]). Returns (o, final_state or None,
+    extras dict)."""
+    wanted = [n for n, f in (("g_cumsum", want_g_cumsum), ("A", want_A), ("h", want_h)) if f]
+    desc, o, fin, slots, extras = _fwd_args(q, k, v, g, beta, scale, meta, initial_state, o_dtype, out,
+                                            final_out, output_final_state, use_exp2, flags, wanted)
     dev = k.device
     nb = workspace_bytes(desc)
     ws = workspace if workspace is not None else torch.empty(nb, dtype=torch.uint8, device=dev)
-    if ws.numel() < nb:
-        raise ValueError("workspace too small")
-    prep_only = bool(flags & FLAG_PREPARE_ONLY)
-    o = None
-    if not prep_only:
-        o = out if out is not None else torch.empty(v.shape, dtype=o_dtype, device=dev)
-    units = n_units_of(k, meta)
-    fin = None
-    if output_final_state and not prep_only:
-        fin = final_out if final_out is not None else \
-            torch.empty((units, H, k.shape[-1], v.shape[-1]), dtype=torch.float32, device=dev)
-    extras = {}
-    tokens = k.shape[0] * k.shape[1] if k.dim() == 4 else k.shape[0]
-    if want_g_cumsum:
-        extras["g_cumsum"] = torch.empty(g.shape, dtype=torch.float32, device=dev)
-    if want_A:
-        extras["A"] = torch.empty((tokens, H, 64), dtype=torch.float32, device=dev)
-    if want_h:
-        n_chunks = meta.n_chunks if meta is not None else k.shape[0] * ((k.shape[1] + 63) // 64)
-        extras["h"] = torch.empty((n_chunks, H, k.shape[-1], v.shape[-1]), dtype=torch.float32, device=dev)
-    slots = GdnSlots(_ptr(extras.get("g_cumsum")), _ptr(extras.get("A")), _ptr(extras.get("h")))
-    if initial_state is not None:
-        if initial_state.dtype != torch.float32 or not initial_state.is_contiguous():
-            raise ValueError("initial_state must be contiguous float32")
-        if tuple(initial_state.shape) != (units, H, k.shape[-1], v.shape[-1]):
-            raise ValueError("initial_state must be [units, H, K, V]")
+    if ws.dtype != torch.uint8 or ws.device != dev or ws.numel() < nb:
+        raise ValueError(f"workspace must be a uint8 tensor of at least {nb} bytes on {dev}")
     nbytes = ctypes.c_size_t(ws.numel())
     check(lib().gdn_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                               _ptr(initial_state), _ptr(o), _ptr(fin), ctypes.byref(slots), int(flags),
@@ -258,27 +319,15 @@ class FwdCall:
 
     def __init__(self, q, k, v, g, beta, scale=None, *, out, workspace, meta: UnitMeta | None = None,
                  initial_state=None, final_out=None, use_exp2=False):
-        _check_inputs(q, k, v, g, beta)
-        H = k.shape[-2]
-        per_key = g.dim() == k.dim()
-        if scale is None:
-            scale = k.shape[-1] ** -0.5
-        self._keep = (q, k, v, g, beta, out, workspace, meta, initial_state, final_out)
-        self._desc = _desc(k, H, k.dtype, out.dtype, per_key, use_exp2, scale, meta)
+        self._desc, o, fin, self._slots, _ = _fwd_args(q, k, v, g, beta, scale, meta, initial_state, out.dtype,
+                                                       out, final_out, False, use_exp2, 0)
         nb = workspace_bytes(self._desc)
-        if workspace.numel() < nb:
-            raise ValueError("workspace too small")
-        if tuple(out.shape) != tuple(v.shape):
-            raise ValueError("out must have v's shape")
-        units = n_units_of(k, meta)
-        for t, shp in ((initial_state, (units, H, k.shape[-1], v.shape[-1])),
-                       (final_out, (units, H, k.shape[-1], v.shape[-1]))):
-            if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != shp):
-                raise ValueError(f"states must be contiguous float32 {shp}")
-        self._slots = GdnSlots(None, None, None)
+        if workspace.dtype != torch.uint8 or workspace.device != k.device or workspace.numel() < nb:
+            raise ValueError(f"workspace must be a uint8 tensor of at least {nb} bytes on {k.device}")
+        self._keep = (q, k, v, g, beta, out, workspace, meta, initial_state, final_out)
         self._nbytes = ctypes.c_size_t(workspace.numel())
         self._args = [ctypes.byref(self._desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                      _ptr(initial_state), _ptr(out), _ptr(final_out), ctypes.byref(self._slots)]
+                      _ptr(initial_state), _ptr(o), _ptr(fin), ctypes.byref(self._slots)]
         self._tail = [_ptr(workspace), ctypes.byref(self._nbytes), _stream(k.device)]
         self._fn = lib().gdn_chunk_fwd
 
@@ -291,26 +340,31 @@ def gdn_state_summary(k, v, g, beta, *, meta: UnitMeta, mode=0, use_exp2=False, 
     """Per-unit summaries (S_ext [units,H,K,V], M [units,H,K,K]; given
     buffers are written in place); pass q to leave a per-key preparation
     that a reusing forward can use."""
-    _check_inputs(q, k, v, g, beta)
-    H = k.shape[-2]
-    per_key = g.dim() == k.dim()
+    if mode not in (0, 1, 2):
+        raise ValueError("mode must be 0 (both), 1 (S_ext) or 2 (M)")
+    if v is None:
+        raise ValueError("v is required")
+    H, per_key = _check_inputs(q, k, v, g, beta, meta)
     desc = _desc(k, H, k.dtype, torch.float32, per_key, use_exp2, 1.0, meta)
     dev = k.device
     nb = workspace_bytes(desc)
     ws = workspace if workspace is not None else torch.empty(nb, dtype=torch.uint8, device=dev)
+    if ws.dtype != torch.uint8 or ws.device != dev or ws.numel() < nb:
+        raise ValueError(f"workspace must be a uint8 tensor of at least {nb} bytes on {dev}")
     units = n_units_of(k, meta)
     K, V = k.shape[-1], v.shape[-1]
     if mode != 2 and S_ext is None:
         S_ext = torch.empty((units, H, K, V), dtype=torch.float32, device=dev)
     if mode != 1 and M is None:
         M = torch.empty((units, H, K, K), dtype=torch.float32, device=dev)
-    for t, shp in ((S_ext if mode != 2 else None, (units, H, K, V)), (M if mode != 1 else None, (units, H, K, K))):
-        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != shp):
-            raise ValueError(f"summary buffers must be contiguous float32 {shp}")
+    if mode != 2:
+        _check_tensor("S_ext", S_ext, torch.float32, (units, H, K, V), dev)
+    if mode != 1:
+        _check_tensor("M", M, torch.float32, (units, H, K, K), dev)
     nbytes = ctypes.c_size_t(ws.numel())
     check(lib().gdn_state_summary(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                  int(mode), _ptr(S_ext), _ptr(M), _ptr(ws), ctypes.byref(nbytes),
-                                  _stream(dev)), "gdn_state_summary")
+                                  int(mode), _ptr(S_ext if mode != 2 else None), _ptr(M if mode != 1 else None),
+                                  _ptr(ws), ctypes.byref(nbytes), _stream(dev)), "gdn_state_summary")
     return S_ext, M, ws
 
 
@@ -319,17 +373,25 @@ def gdn_state_merge(S_ext, M, S0=None, *, B: int, n_seg: int, want_final=True, S
     """S_ext [B*n_seg,H,K,V], M [B*n_seg,H,K,K] (units row-major) -> S_init
     [B*n_seg,H,K,V] (the state entering every segment) and S_final [B,H,K,V]
     (given buffers are written in place)."""
+    if S_ext.dim() != 4:
+        raise ValueError("S_ext must be [B*n_seg, H, K, V]")
     H, K, V = S_ext.shape[1], S_ext.shape[2], S_ext.shape[3]
     dev = S_ext.device
+    if dev.type != "cuda":
+        raise ValueError(f"summaries must be GPU tensors, got {dev}")
+    _check_tensor("S_ext", S_ext, torch.float32, (B * n_seg, H, K, V), dev)
+    _check_tensor("M", M, torch.float32, (B * n_seg, H, K, K), dev)
+    if S0 is not None:
+        _check_tensor("S0", S0, torch.float32, (B, H, K, V), dev)
     if S_init is None:
         S_init = torch.empty_like(S_ext)
     if want_final and S_final is None:
         S_final = torch.empty((B, H, K, V), dtype=torch.float32, device=dev)
     if not want_final:
         S_final = None
-    for t, shp in ((S_init, tuple(S_ext.shape)), (S_final, (B, H, K, V))):
-        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != shp):
-            raise ValueError(f"merge outputs must be contiguous float32 {shp}")
+    _check_tensor("S_init", S_init, torch.float32, tuple(S_ext.shape), dev)
+    if S_final is not None:
+        _check_tensor("S_final", S_final, torch.float32, (B, H, K, V), dev)
     check(lib().gdn_state_merge(B, H, n_seg, K, V, _ptr(S_ext), _ptr(M), _ptr(S0), _ptr(S_init),
                                 _ptr(S_final), _stream(dev)), "gdn_state_merge")
     return S_init, S_final

@@ -153,6 +153,23 @@ extern "C" gdn_status gdn_varlen_meta(const int32_t* offsets, int32_t n_offsets,
     return GDN_OK;
 }
 
+// Every check of gdn_chunk_fwd that does not involve the workspace.
+gdn_status gdn::fwd_preflight(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                              const float* g, const void* beta, const void* o, int32_t flags,
+                              gdn::Problem* p, size_t* workspace_need) {
+    gdn_status st = validate(desc, p);
+    if (st != GDN_OK) return st;
+    if (flags & ~(GDN_FLAG_REUSE_PREPARED | GDN_FLAG_PREPARE_ONLY)) return GDN_ERR_INVALID;
+    const bool reuse = flags & GDN_FLAG_REUSE_PREPARED, prep_only = flags & GDN_FLAG_PREPARE_ONLY;
+    if (reuse && prep_only) return GDN_ERR_INVALID;
+    const bool tokens = p->um.total_tokens > 0;
+    if (tokens && (!k || !g || !beta)) return GDN_ERR_INVALID;
+    if (!prep_only && tokens && (!q || !v || !o)) return GDN_ERR_INVALID;
+    if (p->per_key && !reuse && tokens && !q) return GDN_ERR_INVALID;   // the per-key preparation gates q
+    if (workspace_need) *workspace_need = gdn::workspace_bytes(*p, nullptr, nullptr);
+    return GDN_OK;
+}
+
 extern "C" gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, const void* v,
                                     const float* g, const void* beta, const float* initial_state,
                                     void* o, float* final_state, const gdn_slots* slots, int32_t flags,
@@ -160,17 +177,13 @@ extern "C" gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const v
     gdn::Problem p;
     gdn_status st = validate(desc, &p);
     if (st != GDN_OK) return st;
-    if (flags & ~(GDN_FLAG_REUSE_PREPARED | GDN_FLAG_PREPARE_ONLY)) return GDN_ERR_INVALID;
-    const bool reuse = flags & GDN_FLAG_REUSE_PREPARED, prep_only = flags & GDN_FLAG_PREPARE_ONLY;
-    if (reuse && prep_only) return GDN_ERR_INVALID;
     gdn::Workspace ws;
     bool query = false;
     st = size_workspace(p, workspace, workspace_bytes, &ws, &query);
     if (st != GDN_OK || query) return st;
-    const bool tokens = p.um.total_tokens > 0;
-    if (tokens && (!k || !g || !beta)) return GDN_ERR_INVALID;
-    if (!prep_only && tokens && (!q || !v || !o)) return GDN_ERR_INVALID;
-    if (p.per_key && !reuse && tokens && !q) return GDN_ERR_INVALID;   // the per-key preparation gates q
+    st = gdn::fwd_preflight(desc, q, k, v, g, beta, o, flags, &p, nullptr);
+    if (st != GDN_OK) return st;
+    const bool reuse = flags & GDN_FLAG_REUSE_PREPARED, prep_only = flags & GDN_FLAG_PREPARE_ONLY;
     float* gcs = slots ? slots->g_cumsum : nullptr;
     float* A = slots ? slots->A : nullptr;
     float* hs = slots ? slots->h : nullptr;

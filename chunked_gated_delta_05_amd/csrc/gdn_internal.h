@@ -7,6 +7,8 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include "gdn.h"
+
 namespace gdn {
 
 constexpr int BT = 64;    // tokens per chunk
@@ -72,5 +74,11 @@ hipError_t launch_state(const Problem& p, const Workspace& ws, const void* q, co
 
 hipError_t launch_merge(int B, int H, int n_seg, const float* S_ext, const float* M,
                         const float* S0, float* S_init, float* S_final, hipStream_t s);
+
+// Host-only checks of a gdn_chunk_fwd call (descriptor, flags, pointers), and
+// the workspace it needs; no HIP call.
+gdn_status fwd_preflight(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                         const float* g, const void* beta, const void* o, int32_t flags, Problem* p,
+                         size_t* workspace_need);
 
 }  // namespace gdn
