@@ -65,6 +65,9 @@ def lib():
                                         vp, vp, vp, sz, vp]
         L.gdn_state_merge.restype = ctypes.c_int
         L.gdn_state_merge.argtypes = [ctypes.c_int32] * 5 + [vp, vp, vp, vp, vp, vp]
+        L.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
+        L.gdn_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(GdnDesc), vp, vp, vp, vp, vp, vp, vp, vp,
+                                            ctypes.POINTER(GdnSlots), ctypes.c_int32, vp]
         _LIB = L
     return _LIB
 
@@ -309,6 +312,19 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale=None, *, meta: UnitMeta | None = None,
                               _ptr(initial_state), _ptr(o), _ptr(fin), ctypes.byref(slots), int(flags),
                               _ptr(ws), ctypes.byref(nbytes), _stream(dev)), "gdn_chunk_fwd")
     return o, fin, extras
+
+
+def gdn_chunk_fwd_noalloc(q, k, v, g, beta, scale=None, *, out, final_out=None, meta: UnitMeta | None = None,
+                          initial_state=None, use_exp2=False, flags=0):
+    """gdn_chunk_fwd_noalloc: the forward with the library's own per-GPU
+    scratch instead of a workspace; the caller passes every output buffer
+    (out, and final_out when the final state is wanted)."""
+    desc, o, fin, slots, _ = _fwd_args(q, k, v, g, beta, scale, meta, initial_state, out.dtype, out,
+                                       final_out, False, use_exp2, flags)
+    check(lib().gdn_chunk_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      _ptr(initial_state), _ptr(o), _ptr(fin), ctypes.byref(slots), int(flags),
+                                      _stream(k.device)), "gdn_chunk_fwd_noalloc")
+    return o, fin
 
 
 class FwdCall:

@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = [os.path.join(CSRC, "gdn_kernels.hip"), os.path.join(CSRC, "gdn_host.cpp")]
+SOURCES = [os.path.join(CSRC, "gdn_kernels.hip"), os.path.join(CSRC, "gdn_host.cpp"),
+           os.path.join(CSRC, "gdn_noalloc.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
@@ -34,6 +35,7 @@ def build(verbose: bool = False) -> str:
     warn = ["-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
     kobj = os.path.join(BUILD, "gdn_kernels.o")
     hobj = os.path.join(BUILD, "gdn_host.o")
+    nobj = os.path.join(BUILD, "gdn_noalloc.o")
     _run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           # MFMA accumulators in ordinary VGPRs: the state update scales them
@@ -42,7 +44,10 @@ def build(verbose: bool = False) -> str:
           *warn, *inc, "-c", SOURCES[0], "-o", kobj], verbose)
     _run([HIPCC, "-O2", "-std=c++17", "-fPIC", "-D__HIP_PLATFORM_AMD__", *warn, *inc, "-I", "/opt/rocm/include",
           "-x", "c++", "-c", SOURCES[1], "-o", hobj], verbose)
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", kobj, hobj, "-o", LIB + ".tmp"], verbose)
+    _run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          *warn, *inc, "-c", SOURCES[2], "-o", nobj], verbose)
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", kobj, hobj, nobj, "-o", LIB + ".tmp"], verbose)
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

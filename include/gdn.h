@@ -206,6 +206,32 @@ gdn_status gdn_state_merge(int32_t B, int32_t H, int32_t n_seg, int32_t K, int32
                            const float* S_ext, const float* M, const float* S0, float* S_init,
                            float* S_final, hipStream_t stream);
 
+/*
+ * gdn_chunk_fwd_noalloc - gdn_chunk_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same arguments, results and errors as gdn_chunk_fwd
+ * without the workspace pair: the workspace is the library's own scratch
+ * array of GDN_NOALLOC_SCRATCH_BYTES, one copy per GPU, taken the first time
+ * the entry point runs on that GPU and held until the process ends. The call
+ * allocates nothing. The caller still passes every input and output.
+ *
+ *   GDN_ERR_CAPACITY  the problem needs more workspace than the scratch holds
+ *                     (about 17 KiB per (chunk, head) with bf16 inputs and a
+ *                     scalar gate); use gdn_chunk_fwd with a workspace
+ *   GDN_ERR_INVALID   as gdn_chunk_fwd, or stream is not on the current device
+ *
+ * Every call on one GPU shares that GPU's scratch, which keeps the last call's
+ * contents: GDN_FLAG_REUSE_PREPARED reuses the preparation of the previous
+ * call on the same GPU (same descriptor and inputs). Calls that overlap on
+ * one GPU (other streams, other host threads) race on the scratch and must be
+ * serialised by the caller. Nothing in the scratch needs to start at zero.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+gdn_status gdn_chunk_fwd_noalloc(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                                 const float* g, const void* beta, const float* initial_state, void* o,
+                                 float* final_state, const gdn_slots* slots, int32_t flags,
+                                 hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert names == ["gdn_chunk_fwd", "gdn_state_merge", "gdn_state_summary", "gdn_varlen_meta"]
+    assert names == ["gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_state_merge", "gdn_state_summary",
+                     "gdn_varlen_meta"]
     L = gb.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -199,3 +200,21 @@ def test_status_maps_to_page_exceptions():
         gb.check(gb.GDN_ERR_UNSUPPORTED, "x")
     with pytest.raises(RuntimeError):
         gb.check(gb.GDN_ERR_DEVICE, "x")
+
+
+# ------------------------------------------------------------------ allocation-free forward
+def noalloc(d, *, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o=FAKE, flags=0):
+    return gb.lib().gdn_chunk_fwd_noalloc(ctypes.byref(d), q, k, v, g, beta, None, o, None, None, flags, None)
+
+
+def test_noalloc_rejects_before_any_hip_call():
+    # sizing and every validation run on the host first, so these statuses
+    # come back without a GPU
+    big = desc(B=1, T=8192, H=64)        # 128 chunks x 64 heads x 17 KiB = 136 MiB > 128 MiB
+    st, need = fwd(big, ws=None)
+    assert st == gb.GDN_OK and need > 128 << 20
+    assert noalloc(big) == gb.GDN_ERR_CAPACITY
+    assert noalloc(desc(chunk_size=32)) == gb.GDN_ERR_INVALID
+    assert noalloc(desc(K=64, V=64)) == gb.GDN_ERR_UNSUPPORTED
+    assert noalloc(desc(), q=None) == gb.GDN_ERR_INVALID
+    assert noalloc(desc(), flags=3) == gb.GDN_ERR_INVALID
