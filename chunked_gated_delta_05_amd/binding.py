@@ -381,7 +381,7 @@ def gdn_state_summary(k, v, g, beta, *, meta: UnitMeta, mode=0, use_exp2=False, 
     check(lib().gdn_state_summary(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                   int(mode), _ptr(S_ext if mode != 2 else None), _ptr(M if mode != 1 else None),
                                   _ptr(ws), ctypes.byref(nbytes), _stream(dev)), "gdn_state_summary")
-    return S_ext, M, ws
+    return (S_ext if mode != 2 else None), (M if mode != 1 else None), ws
 
 
 def gdn_state_merge(S_ext, M, S0=None, *, B: int, n_seg: int, want_final=True, S_init=None,

@@ -361,26 +361,43 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     }
     __syncthreads();
 
-    // ---- L = strictly lower (beta_i k_i.k_j b^{G_i-G_j}) on MFMA, 10 tiles over 4 waves
-    const int mid = len > 0 ? (len - 1) / 2 : 0;   // reference row of the per-key factorisation
+    // ---- L = strictly lower (beta_i k_i.k_j b^{G_i-G_j}) on MFMA, 10 tiles over 4 waves.
+    // Per key, an off-diagonal tile (I > J) factors the decay about the last
+    // row of block J, so that both factors are at most 1 for any g <= 0; a
+    // diagonal tile takes the exponent differences directly.
+    auto direct = [&](const In* xi, int i, int j) {          // sum_d x_id k_jd b^{G_id - G_jd}
+        float s = 0.0f;
+        for (int d = 0; d < DK; ++d)
+            s += (float)xi[i * LDQ + d] * (float)kt[j * LDQ + d] *
+                 fpow(Gs[i * (DK + 4) + d] - Gs[j * (DK + 4) + d], a.use_exp2);
+        return s;
+    };
     for (int t = w; t < 10; t += 4) {
         const int it = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
         const int jt = t - (it * (it + 1)) / 2;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int kk = 0; kk < DK / 32; ++kk) {
-            const int col = 32 * kk + 8 * G;
-            if (!PERKEY) {
-                P::mma(acc, P::ld(&kt[(16 * it + n) * LDQ + col]), P::ld(&kt[(16 * jt + n) * LDQ + col]));
-            } else {
-                float xa[8], xb[8];
-                for (int e = 0; e < 8; ++e) {
-                    const float gr = Gs[mid * (DK + 4) + col + e];
-                    xa[e] = (float)kt[(16 * it + n) * LDQ + col + e] *
-                            fpow(Gs[(16 * it + n) * (DK + 4) + col + e] - gr, a.use_exp2);
-                    xb[e] = (float)kt[(16 * jt + n) * LDQ + col + e] *
-                            fpow(gr - Gs[(16 * jt + n) * (DK + 4) + col + e], a.use_exp2);
+        if (PERKEY && it == jt) {
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * it + 4 * G + r, j = 16 * jt + n;
+                acc[r] = j < i ? direct(kt, i, j) : 0.0f;
+            }
+        } else {
+            for (int kk = 0; kk < DK / 32; ++kk) {
+                const int col = 32 * kk + 8 * G;
+                if (!PERKEY) {
+                    P::mma(acc, P::ld(&kt[(16 * it + n) * LDQ + col]), P::ld(&kt[(16 * jt + n) * LDQ + col]));
+                } else {
+                    const int ref = 16 * jt + 15;
+                    float xa[8], xb[8];
+                    for (int e = 0; e < 8; ++e) {
+                        const float gr = Gs[ref * (DK + 4) + col + e];
+                        xa[e] = (float)kt[(16 * it + n) * LDQ + col + e] *
+                                fpow(Gs[(16 * it + n) * (DK + 4) + col + e] - gr, a.use_exp2);
+                        xb[e] = (float)kt[(16 * jt + n) * LDQ + col + e] *
+                                fpow(gr - Gs[(16 * jt + n) * (DK + 4) + col + e], a.use_exp2);
+                    }
+                    P::mma(acc, P::from(xa), P::from(xb));
                 }
-                P::mma(acc, P::from(xa), P::from(xb));
             }
         }
         for (int r = 0; r < 4; ++r) {
@@ -459,15 +476,21 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         for (int t = w; t < 16; t += 4) {
             const int jt = t >> 2, it = t & 3;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (jt <= it) {
+            if (PERKEY && jt == it) {
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * it + n, j = 16 * jt + 4 * G + r;
+                    acc[r] = j <= i ? direct(qt, i, j) : 0.0f;
+                }
+            } else if (jt <= it) {
                 for (int kk = 0; kk < DK / 32; ++kk) {
                     const int col = 32 * kk + 8 * G;
                     if (!PERKEY) {
                         P::mma(acc, P::ld(&kt[(16 * jt + n) * LDQ + col]), P::ld(&qt[(16 * it + n) * LDQ + col]));
                     } else {
+                        const int ref = 16 * jt + 15;
                         float xa[8], xb[8];
                         for (int e = 0; e < 8; ++e) {
-                            const float gr = Gs[mid * (DK + 4) + col + e];
+                            const float gr = Gs[ref * (DK + 4) + col + e];
                             xa[e] = (float)kt[(16 * jt + n) * LDQ + col + e] *
                                     fpow(gr - Gs[(16 * jt + n) * (DK + 4) + col + e], a.use_exp2);
                             xb[e] = (float)qt[(16 * it + n) * LDQ + col + e] *
@@ -737,21 +760,33 @@ __global__ __launch_bounds__(64) void prep_kernel_h(PrepArgs a) {
 
 // ------------------------------------------------------------------ prep, fp16 per-key gate
 // One workgroup of four waves per (chunk, head). Wave w owns token rows
-// 16w .. 16w+15 and lane l the key pair 2l, 2l+1: every load of g, k and q is
-// a coalesced 512- or 256-byte row segment, and the per-key cumulative gate
-// is a scan in registers plus the column sums of the waves before. Every
-// gated form is computed once per element: the reference-row factors
-// k b^{G-G_m}, k b^{G_m-G}, q b^{G-G_m} (G_m the gate at the chunk's middle
-// row, which keeps every exponent within half the chunk's range) go to LDS as
-// fp16 operands of the L and P tiles, and the state pass's operands q b^G,
-// k b^G, k b^{G_L-G} go straight to the workspace. L and P are then plain
-// 16x16x32 MFMA tiles, and the inverse runs in LDS over the dead operand
-// tiles. q b^{G-G_m} waits in registers and takes over the first operand
-// tile once L is done, and the gate's column sums and reference rows live in
-// the L buffer before L: 50.5 KiB of LDS, three workgroups per CU. The phases
-// hand data over through LDS only, so their barriers leave the workspace
-// stores in flight.
-constexpr int PKL = 136;   // row stride (fp16) of the 64 x 128 operand tiles: 272 bytes
+// 16w .. 16w+15 (row block w) and lane l the key pair 2l, 2l+1: every load of
+// g, k and q is a coalesced 512- or 256-byte row segment, and the per-key
+// cumulative gate is a scan in registers plus the column sums of the waves
+// before.
+//
+// The decays of L and P, b^{G_id - G_jd} (j <= i), are factored so that no
+// fp16 operand can overflow for any gate g <= 0. With rho_J the gate at the
+// last row of block J (rho_{-1} = 0):
+//   A side (rows i of block I):  k_i b^{G_i - rho_{I-1}},  q_i b^{G_i - rho_{I-1}}   (<= 1)
+//   B side (rows j of block J):  k_j b^{rho_J - G_j}                              (<= 1)
+// and tile (I, J) multiplies the B fragment by the per-key factor
+// f(I, J) = b^{rho_{I-1} - rho_J}: at most 1 for J < I, and b^{R_I} for the
+// diagonal tile, R_I being the block's own gate range. The diagonal tile takes
+// this form only when R_I <= PK_DIAG_LOG2 (log2 units) for every key, so that
+// the B operand stays within 2^PK_DIAG_LOG2 |k|; otherwise the wave owning
+// the block computes its diagonal L and P tiles from direct exponent
+// differences in fp32 (VALU), exact for any g <= 0. The state pass's operands
+// q b^G, k b^G and k b^{G_L - G} are the A and B forms times per-key factors
+// <= 1, so each element costs two exponentials.
+//
+// L and P are then 16x16x32 MFMA tiles, the inverse runs in LDS over the dead
+// operand tiles, and q's A form waits in registers and takes over the first
+// operand tile once L is done: 53 KiB of LDS, three workgroups per CU. The
+// phases hand data over through LDS only, so their barriers leave the
+// workspace stores in flight.
+constexpr int PKL = 136;              // row stride (fp16) of the 64 x 128 operand tiles: 272 bytes
+constexpr float PK_DIAG_LOG2 = 8.0f;  // largest in-block gate range (log2) of a factored diagonal tile
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_f16x2(float x, float y) {
@@ -761,16 +796,60 @@ __device__ __forceinline__ uint32_t pack_f16x2(float x, float y) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
+// The tiles (I, J), J <= I, of L and P computed by each wave (its own
+// diagonal block first):
+//   w0: (0,0) (1,0) (3,2)   w1: (1,1) (2,0)   w2: (2,2) (3,0)   w3: (3,3) (2,1) (3,1)
+// and the zero tiles of P (I < J, numbered 0..5) it writes: w0 0, w1 1-2,
+// w2 3-4, w3 5.
+constexpr int PK_NT[4] = {3, 2, 2, 3};
+constexpr int PK_TI[4][3] = {{0, 1, 3}, {1, 2, 0}, {2, 3, 0}, {3, 2, 3}};
+constexpr int PK_TJ[4][3] = {{0, 0, 2}, {1, 0, 0}, {2, 0, 0}, {3, 1, 1}};
+constexpr int PK_Z0[4] = {0, 1, 3, 5}, PK_NZ[4] = {1, 2, 2, 1};
+constexpr int pk_tri(int I, int J) { return I * (I + 1) / 2 + J; }
+
+// Sum over the 64 lanes of 32 per-lane values by recursive halving: at each
+// step a lane keeps half of its values and adds the other half received from
+// its partner (lanes 32 apart, then 16, 8, 4, 2), so that lanes 2m and 2m+1
+// end with the total of value m. The two upper exchanges swap whole 32- and
+// 16-lane halves (v_permlane32_swap, v_permlane16_swap); the lower ones move
+// one value per lane (row_ror:8, swizzle SWAP 4, quad_perm); the swizzle
+// builtin moves ints, so the floats cross it as their bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return u2f(__builtin_amdgcn_update_dpp(0u, f2u(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float lane_sum32(float (&v)[32], int lane) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const auto r = __builtin_amdgcn_permlane32_swap(f2u(v[m]), f2u(v[16 + m]), false, false);
+        v[m] = u2f(r[0]) + u2f(r[1]);
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const auto r = __builtin_amdgcn_permlane16_swap(f2u(v[m]), f2u(v[8 + m]), false, false);
+        v[m] = u2f(r[0]) + u2f(r[1]);
+    }
+    const bool up8 = lane & 8, up4 = lane & 4, up2 = lane & 2;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        v[m] = (up8 ? v[4 + m] : v[m]) + dpp_f<0x128>(up8 ? v[m] : v[4 + m]);
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+        v[m] = (up4 ? v[2 + m] : v[m]) + u2f(__builtin_amdgcn_ds_swizzle((int)f2u(up4 ? v[m] : v[2 + m]), 0x101f));
+    v[0] = (up2 ? v[1] : v[0]) + dpp_f<0x4e>(up2 ? v[0] : v[1]);
+    return v[0] + dpp_f<0xb1>(v[0]);
+}
+
 __global__ __launch_bounds__(256) void prep_kernel_pk(PrepArgs a) {
-    // ka: k b^{G-G_m} for L, then q b^{G-G_m} for P, then T (fp32 64 x 65);
-    // kb: k b^{G_m-G}, then the partial products of the inverse; Ls: the
-    // gate's column sums and reference rows until L is written
+    // ka: the A form of k for L, then that of q for P, then T (fp32 64 x 65);
+    // kb: the B form of k, then the partial products of the inverse; Ls: the
+    // gate's column sums until L is written; ft: the per-key factors f(I, J)
     __shared__ __attribute__((aligned(16))) f16 ka[BT * PKL];
     __shared__ __attribute__((aligned(16))) f16 kb[BT * PKL];
     __shared__ __attribute__((aligned(16))) float Ls[BT * LDL];
+    __shared__ __attribute__((aligned(16))) f16 ft[10 * DK];
     __shared__ float bet[BT];
     float (*part)[DK] = reinterpret_cast<float (*)[DK]>(Ls);            // [4][DK] column sums of g per wave
-    float (*gref)[DK] = reinterpret_cast<float (*)[DK]>(Ls + 4 * DK);   // [2][DK] G at the middle / last valid row
     f16* qa = ka;
     float* Ts = reinterpret_cast<float*>(ka);
     float* Yb = reinterpret_cast<float*>(kb);
@@ -790,9 +869,10 @@ __global__ __launch_bounds__(256) void prep_kernel_pk(PrepArgs a) {
     const int64_t ch = (int64_t)ci * H + head;
     const int64_t e0 = t0 * H + head;              // token-head index of the chunk's first row
     const bool has_q = a.q != nullptr;
-    const int mid = len > 0 ? (len - 1) / 2 : 0, last = len > 0 ? len - 1 : 0;
+    const float l2b = a.use_exp2 ? 1.0f : 1.4426950408889634f;   // log2 of the decay base
 
-    // ---- loads: buffer ranges end at the chunk's last token, so rows past it read as zero
+    // ---- loads: buffer ranges end at the chunk's last token, so rows past it
+    // read as zero (and the cumulative gate stays flat there)
     const uint32_t rowk = (uint32_t)H * DK * 2, rowg = (uint32_t)H * DK * 4;
     const rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(a.k) + e0 * DK, len > 0 ? (uint32_t)(len - 1) * rowk + DK * 2 : 0);
     const rsrc_t rq = make_rsrc(has_q ? reinterpret_cast<const bf16*>(a.q) + e0 * DK : a.k,
@@ -833,36 +913,77 @@ __global__ __launch_bounds__(256) void prep_kernel_pk(PrepArgs a) {
         part[w][2 * lane + 1] = s1;
     }
     lds_barrier();
-    {
-        float p0 = 0.0f, p1 = 0.0f;
-        for (int ww = 0; ww < w; ++ww) {
-            p0 += part[ww][2 * lane];
-            p1 += part[ww][2 * lane + 1];
-        }
+    // rho_{w-1} (the sum of the blocks before), rho_w and G_L of this lane's keys
+    float p0 = 0.0f, p1 = 0.0f, t0s = 0.0f, t1s = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            gc[r][0] += p0;
-            gc[r][1] += p1;
-            const int row = 16 * w + r;
-            if (row == mid) { gref[0][2 * lane] = gc[r][0]; gref[0][2 * lane + 1] = gc[r][1]; }
-            if (row == last) { gref[1][2 * lane] = gc[r][0]; gref[1][2 * lane + 1] = gc[r][1]; }
-            if (a.g_cumsum && row < len)
-                *reinterpret_cast<float2*>(a.g_cumsum + (e0 + (int64_t)row * H) * DK + 2 * lane) = float2{gc[r][0], gc[r][1]};
-        }
+    for (int ww = 0; ww < 4; ++ww) {
+        const float x0 = part[ww][2 * lane], x1 = part[ww][2 * lane + 1];
+        if (ww < w) { p0 += x0; p1 += x1; }
+        t0s += x0;
+        t1s += x1;
     }
-    lds_barrier();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        gc[r][0] += p0;
+        gc[r][1] += p1;
+        const int row = 16 * w + r;
+        if (a.g_cumsum && row < len)
+            *reinterpret_cast<float2*>(a.g_cumsum + (e0 + (int64_t)row * H) * DK + 2 * lane) = float2{gc[r][0], gc[r][1]};
+    }
+    const float r0 = gc[15][0], r1 = gc[15][1];     // rho_w
     if (tid < DK) {
-        const float gl = gref[1][tid];
+        float gl = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) gl += part[ww][tid];
         a.ws.gamL[ch * DK + tid] = gl;
         reinterpret_cast<float*>(a.ws.cfh)[ch * (CFB / 4) + CF_GL + tid] = fpow(gl, a.use_exp2);
     }
+    // per-key factors f(I, J) = b^{rho_{I-1} - rho_J} of the 10 tiles J <= I
+    for (int e = tid; e < 10 * DK; e += 256) {
+        const int tri = e / DK, d = e % DK;
+        const int I = tri < 1 ? 0 : tri < 3 ? 1 : tri < 6 ? 2 : 3, J = tri - I * (I + 1) / 2;
+        float rI = 0.0f, rJ = 0.0f;
+        for (int ww = 0; ww < 4; ++ww) {
+            const float x = part[ww][d];
+            if (ww < I) rI += x;
+            if (ww <= J) rJ += x;
+        }
+        // diagonal factors beyond the factored range are never used
+        ft[e] = (f16)fpow(fminf(rI - rJ, PK_DIAG_LOG2 / l2b), a.use_exp2);
+    }
 
-    // ---- gated forms: reference-row operands to LDS (q b^{G-G_m} waits in
-    // registers until L is done), state-pass operands out
+    // the diagonal tile's factored form needs the block's gate range within PK_DIAG_LOG2
+    float rng = fmaxf(p0 - r0, p1 - r1) * l2b;
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) rng = fmaxf(rng, __shfl_xor(rng, s, 64));
+    const bool diag_direct = __builtin_amdgcn_readfirstlane(rng > PK_DIAG_LOG2 ? 1 : 0);
+    // Direct diagonal tile: lanes 2m, 2m+1 end with value m of every row i
+    // of the block, L_ij (m = j < 16; before beta) or P_ij (m = 16 + j)
+    float dres[16];
+    if (diag_direct) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float v[32];
+#pragma unroll
+            for (int m = 0; m < 32; ++m) v[m] = 0.0f;
+            const float ki0 = __builtin_bit_cast(float, kr[i] << 16), ki1 = __builtin_bit_cast(float, kr[i] & 0xffff0000u);
+            const float qi0 = __builtin_bit_cast(float, qr[i] << 16), qi1 = __builtin_bit_cast(float, qr[i] & 0xffff0000u);
+#pragma unroll
+            for (int j = 0; j <= i; ++j) {
+                const float kj0 = __builtin_bit_cast(float, kr[j] << 16) * fpow(gc[i][0] - gc[j][0], a.use_exp2);
+                const float kj1 = __builtin_bit_cast(float, kr[j] & 0xffff0000u) * fpow(gc[i][1] - gc[j][1], a.use_exp2);
+                if (j < i) v[j] = ki0 * kj0 + ki1 * kj1;
+                v[16 + j] = qi0 * kj0 + qi1 * kj1;
+            }
+            dres[i] = lane_sum32(v, lane);
+        }
+    }
+    // ---- A and B forms to LDS (q's A form waits in registers until L is
+    // done), the state pass's operands out
     uint32_t qpk[16];
     {
-        const float m0 = gref[0][2 * lane], m1 = gref[0][2 * lane + 1];
-        const float l0 = gref[1][2 * lane], l1 = gref[1][2 * lane + 1];
+        const float cA0 = fpow(p0, a.use_exp2), cA1 = fpow(p1, a.use_exp2);                // b^{rho_{w-1}}
+        const float cB0 = fpow(t0s - r0, a.use_exp2), cB1 = fpow(t1s - r1, a.use_exp2);    // b^{G_L - rho_w}
         const int cp = op_pos(2 * lane);
         uint32_t* qg = reinterpret_cast<uint32_t*>(reinterpret_cast<f16*>(a.ws.qg) + ch * (BT * DK) + cp);
         uint32_t* kd = reinterpret_cast<uint32_t*>(reinterpret_cast<f16*>(a.ws.kd) + ch * (BT * DK) + cp);
@@ -872,74 +993,109 @@ __global__ __launch_bounds__(256) void prep_kernel_pk(PrepArgs a) {
             const int row = 16 * w + r;
             const float k0 = __builtin_bit_cast(float, kr[r] << 16), k1 = __builtin_bit_cast(float, kr[r] & 0xffff0000u);
             const float q0 = __builtin_bit_cast(float, qr[r] << 16), q1 = __builtin_bit_cast(float, qr[r] & 0xffff0000u);
-            const float x0 = gc[r][0], x1 = gc[r][1];
-            const float a0 = fpow(x0 - m0, a.use_exp2), a1 = fpow(x1 - m1, a.use_exp2);
-            const float b0 = fpow(m0 - x0, a.use_exp2), b1 = fpow(m1 - x1, a.use_exp2);
-            *reinterpret_cast<uint32_t*>(&ka[row * PKL + 2 * lane]) = pack_f16x2(k0 * a0, k1 * a1);
-            *reinterpret_cast<uint32_t*>(&kb[row * PKL + 2 * lane]) = pack_f16x2(k0 * b0, k1 * b1);
-            qpk[r] = pack_f16x2(q0 * a0, q1 * a1);
-            const float d0 = fpow(x0, a.use_exp2), d1 = fpow(x1, a.use_exp2);
-            const float c0 = fpow(l0 - x0, a.use_exp2), c1 = fpow(l1 - x1, a.use_exp2);
-            if (has_q) qg[row * (DK / 2)] = pack_f16x2(q0 * d0, q1 * d1);
-            kd[row * (DK / 2)] = pack_f16x2(k0 * d0, k1 * d1);
-            kg[row * (DK / 2)] = pack_f16x2(k0 * c0, k1 * c1);
+            const float eA0 = fpow(gc[r][0] - p0, a.use_exp2), eA1 = fpow(gc[r][1] - p1, a.use_exp2);
+            const float eB0 = fpow(r0 - gc[r][0], a.use_exp2), eB1 = fpow(r1 - gc[r][1], a.use_exp2);
+            const float ka0 = k0 * eA0, ka1 = k1 * eA1, qa0 = q0 * eA0, qa1 = q1 * eA1;
+            const float kb0 = k0 * eB0, kb1 = k1 * eB1;
+            *reinterpret_cast<uint32_t*>(&ka[row * PKL + 2 * lane]) = pack_f16x2(ka0, ka1);
+            *reinterpret_cast<uint32_t*>(&kb[row * PKL + 2 * lane]) = pack_f16x2(kb0, kb1);
+            qpk[r] = pack_f16x2(qa0, qa1);
+            if (has_q) qg[row * (DK / 2)] = pack_f16x2(qa0 * cA0, qa1 * cA1);
+            kd[row * (DK / 2)] = pack_f16x2(ka0 * cA0, ka1 * cA1);
+            kg[row * (DK / 2)] = pack_f16x2(kb0 * cB0, kb1 * cB1);
         }
     }
     lds_barrier();
 
-    // ---- L (strictly lower, 10 tiles over 4 waves) on MFMA
-    for (int t = w; t < 10; t += 4) {
-        const int it = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
-        const int jt = t - (it * (it + 1)) / 2;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) {
-            const int col = 32 * kk + 8 * G;
-            PolicyH::mma(acc, PolicyH::ld(&ka[(16 * it + n) * PKL + col]), PolicyH::ld(&kb[(16 * jt + n) * PKL + col]));
-        }
-        // acc[r]: row i = 16 it + 4G + r against column j = 16 jt + n
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = 16 * it + 4 * G + r, j = 16 * jt + n;
-            Ls[i * LDL + j] = j < i ? bet[i] * acc[r] : 0.0f;
-        }
-    }
-    lds_barrier();
-    // q b^{G-G_m} over k b^{G-G_m}, which L no longer needs
-    if (has_q) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) *reinterpret_cast<uint32_t*>(&qa[(16 * w + r) * PKL + 2 * lane]) = qpk[r];
-    }
-    lds_barrier();
-
-    // ---- P (lower incl. diagonal, 10 tiles) on MFMA, and the 6 zero tiles
-    // above the diagonal, over 4 waves
+    // ---- L (strictly lower) and P (lower incl. diagonal) on MFMA, with the
+    // tile coordinates of each wave fixed at compile time: tile (I, J) pairs
+    // the A forms of rows I with the B form of rows J scaled by f(I, J) (no
+    // scaling for J = I - 1, where f = 1)
     f16* Pw = reinterpret_cast<f16*>(a.ws.P) + ch * (BT * BT);
-    if (has_q) {
-        for (int t = w; t < 16; t += 4) {
-            if (t >= 10) {
-                const int z = t - 10;                                 // (it, jt) with it < jt
-                const int it = z < 3 ? 0 : (z < 5 ? 1 : 2);
-                const int jt = z < 3 ? z + 1 : (z < 5 ? z - 1 : 3);
-                *reinterpret_cast<u32x2*>(Pw + (16 * it + n) * BT + op_pos(16 * jt + 4 * G)) = u32x2{0u, 0u};
-                continue;
+    auto tiles = [&](auto w_c) {
+        constexpr int WV = decltype(w_c)::value;
+        auto bfrag = [&](auto I_c, auto J_c, int kk) {
+            constexpr int I = decltype(I_c)::value, J = decltype(J_c)::value;
+            const int col = 32 * kk + 8 * G;
+            PolicyH::F r;
+            r.v = *reinterpret_cast<const f16x8*>(&kb[(16 * J + n) * PKL + col]);
+            if (J != I - 1) r.v = r.v * *reinterpret_cast<const f16x8*>(&ft[pk_tri(I, J) * DK + col]);
+            return r;
+        };
+        // L
+        auto ltile = [&](auto s_c) {
+            constexpr int S = decltype(s_c)::value;
+            constexpr int I = PK_TI[WV][S], J = PK_TJ[WV][S];
+            if (I == J && diag_direct) {
+                const int m = lane >> 1, j = m & 15;
+                if (!(lane & 1) && m < 16)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        Ls[(16 * I + i) * LDL + 16 * I + j] = j < i ? bet[16 * I + i] * dres[i] : 0.0f;
+                return;
             }
-            const int it = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
-            const int jt = t - (it * (it + 1)) / 2;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) {
-                const int col = 32 * kk + 8 * G;
-                PolicyH::mma(acc, PolicyH::ld(&kb[(16 * jt + n) * PKL + col]), PolicyH::ld(&qa[(16 * it + n) * PKL + col]));
+            for (int kk = 0; kk < DK / 32; ++kk)
+                PolicyH::mma(acc, PolicyH::ld(&ka[(16 * I + n) * PKL + 32 * kk + 8 * G]),
+                             bfrag(std::integral_constant<int, I>{}, std::integral_constant<int, J>{}, kk));
+            // acc[r]: row i = 16 I + 4G + r against column j = 16 J + n
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int il = 4 * G + r, i = 16 * I + il;
+                float x = bet[i] * acc[r];
+                if (I == J) x = n < il ? x : 0.0f;
+                Ls[i * LDL + 16 * J + n] = x;
             }
-            // acc[r]: row i = 16 it + n against column j = 16 jt + 4G + r
-            const int i = 16 * it + n;
+        };
+        ltile(std::integral_constant<int, 0>{});
+        ltile(std::integral_constant<int, 1>{});
+        if constexpr (PK_NT[WV] > 2) ltile(std::integral_constant<int, 2>{});
+        lds_barrier();
+        // q's A form over k's, which L no longer needs
+        if (has_q) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) *reinterpret_cast<uint32_t*>(&qa[(16 * WV + r) * PKL + 2 * lane]) = qpk[r];
+        }
+        lds_barrier();
+        if (!has_q) return;
+        // P, and the zero tiles above the diagonal
+#pragma unroll
+        for (int z = PK_Z0[WV]; z < PK_Z0[WV] + PK_NZ[WV]; ++z) {             // (it, jt) with it < jt
+            const int it = z < 3 ? 0 : (z < 5 ? 1 : 2);
+            const int jt = z < 3 ? z + 1 : (z < 5 ? z - 1 : 3);
+            *reinterpret_cast<u32x2*>(Pw + (16 * it + n) * BT + op_pos(16 * jt + 4 * G)) = u32x2{0u, 0u};
+        }
+        auto ptile = [&](auto s_c) {
+            constexpr int S = decltype(s_c)::value;
+            constexpr int I = PK_TI[WV][S], J = PK_TJ[WV][S];
+            if (I == J && diag_direct) {
+                const int m = lane >> 1, j = m & 15;
+                if (!(lane & 1) && m >= 16)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        Pw[(16 * I + i) * BT + op_pos(16 * I + j)] = (f16)(j <= i ? dres[i] : 0.0f);
+                return;
+            }
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk)
+                PolicyH::mma(acc, bfrag(std::integral_constant<int, I>{}, std::integral_constant<int, J>{}, kk),
+                             PolicyH::ld(&qa[(16 * I + n) * PKL + 32 * kk + 8 * G]));
+            // acc[r]: row i = 16 I + n against column j = 16 J + 4G + r
             float x[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) x[r] = 16 * jt + 4 * G + r <= i ? acc[r] : 0.0f;
-            PolicyH::st4(Pw + i * BT + op_pos(16 * jt + 4 * G), x);
-        }
-    }
+            for (int r = 0; r < 4; ++r) x[r] = (I > J || 4 * G + r <= n) ? acc[r] : 0.0f;
+            PolicyH::st4(Pw + (16 * I + n) * BT + op_pos(16 * J + 4 * G), x);
+        };
+        ptile(std::integral_constant<int, 0>{});
+        ptile(std::integral_constant<int, 1>{});
+        if constexpr (PK_NT[WV] > 2) ptile(std::integral_constant<int, 2>{});
+    };
+    if (w == 0) tiles(std::integral_constant<int, 0>{});
+    else if (w == 1) tiles(std::integral_constant<int, 1>{});
+    else if (w == 2) tiles(std::integral_constant<int, 2>{});
+    else tiles(std::integral_constant<int, 3>{});
     lds_barrier();
 
     // ---- T = (I + L)^{-1}: 16 x 16 diagonal blocks by substitution (wave 0,

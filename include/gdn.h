@@ -23,6 +23,18 @@
  *     document offsets (cu_seqlens). Both are row-major and contiguous.
  *   - g and beta are used as given: no sigmoid, no L2 norm, no gate
  *     activation inside (normalisation happens before the core).
+ *   - Gates are log-decays: every g must be <= 0 (each decay b^g in (0, 1]),
+ *     scalar or per key, of any magnitude down to total forgetting (g = -1e4
+ *     and below give b^g = 0 exactly). Products of decays are formed from
+ *     differences of cumulative gates or as factors of at most 1, never as
+ *     quotients, so no intermediate overflows. g > 0 is outside the contract.
+ *   - Numeric range with bf16 inputs: the kernels multiply fp16 operands
+ *     (bf16 values are exact in fp16's normal range) with fp32 accumulation,
+ *     and round the state, the residual and v_new to fp16 once per chunk.
+ *     Every |component| of q, k must stay below 2^8, and |v|, the state and
+ *     v_new below fp16's 65504; beyond that, values saturate to infinity.
+ *     With unit-norm q, k (the pages' convention) and |v| up to 2^11 the
+ *     results meet the bf16 parity bar. fp32 inputs use fp32 operands.
  *   - scale multiplies the output; callers normally pass 1/sqrt(K).
  *   - The state is K x V (key-major, "state_v_first = False").
  *

@@ -526,3 +526,156 @@ def test_workload_long_full():
     o, fin, _ = run_gpu(d, output_final_state=True)
     e = _sampled_check(d, o, heads=[5], fin=fin)
     print(f"{w.name}: sampled o err/rms {e:.2e}")
+
+
+# ------------------------------------------------------------------ strong per-key gates
+def _no_nan(*ts):
+    for t in ts:
+        assert torch.isfinite(t).all(), "non-finite values in the output"
+
+
+@pytest.mark.parametrize("coef", [0.6, 1.0, 4.0])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_per_key_strong_gates(coef, dtype):
+    # g = -coef softplus(N(0,1)) per key in log2 units: up to tens of log2
+    # units of decay inside one 16-token block, which the factored fp16
+    # operands of the L and P tiles must survive (and the direct diagonal
+    # tiles take over from); ragged tail, entry state, chunk states
+    print(f"per-key strong gate coef={coef} {dtype}", flush=True)
+    w = small(B=2, T=200, H=2, dtype=dtype, per_key=True, use_exp2=True, gate_coef=coef)
+    d = to_dev(W.generate(w, 131 + int(10 * coef)))
+    S0 = (torch.randn(2, 2, 128, 128, generator=torch.Generator().manual_seed(13)) * 0.3).to(DEV)
+    o, fin, ex = run_gpu(d, initial_state=S0, output_final_state=True, want_h=True)
+    _no_nan(o, fin, ex["h"])
+    r = run_oracle(d, S0=np32(S0).astype(np.float64), chunk_states=True)
+    tol = TOL[dtype]
+    assert_close(flat_o(o, w), r["o"], tol, "strong-gate o")
+    assert_close(np32(fin), r["final"], tol, "strong-gate final")
+    assert_close(np32(ex["h"]), r["chunk_states"], tol, "strong-gate chunk states")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_per_key_total_forgetting(dtype):
+    # g = -1e4 on every key: each token sees only its own write, so
+    # o_t = scale beta_t (q_t . k_t) v_t, and the final state is
+    # beta_T k_T v_T^T of the last token
+    print(f"per-key total forgetting {dtype}", flush=True)
+    T, H = 200, 2
+    d = to_dev(W.generate(small(B=1, T=T, H=H, dtype=dtype, per_key=True, use_exp2=True), 43))
+    d["g"] = torch.full_like(d["g"], -1e4)
+    o, fin, _ = run_gpu(d, output_final_state=True)
+    _no_nan(o, fin)
+    q, k, v, beta = (np32(d[n][0]).astype(np.float64) for n in ("q", "k", "v", "beta"))
+    ref = d["scale"] * (beta * np.einsum("thk,thk->th", q, k))[..., None] * v
+    fref = beta[-1][:, None, None] * np.einsum("hk,hv->hkv", k[-1], v[-1])
+    # bf16: one product P_tt v_new_t of two fp16-rounded operands per token
+    # (2 * 2^-11 relative; max|o|/rms(o) is about 8): 1e-2
+    tol = 1e-2 if dtype == "bf16" else TOL["fp32"]
+    assert_close(np32(o[0]), ref, tol, "per-key total forgetting o")
+    assert_close(np32(fin[0]), fref, tol, "per-key total forgetting final")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_split_strong_per_key_gates(dtype):
+    # summary -> merge -> correction with strong per-key gates (coef 1, log2):
+    # the transfer maps are tiny but must be finite, and split == oracle
+    print(f"split with strong per-key gates {dtype}", flush=True)
+    w = small(B=2, T=256, H=2, dtype=dtype, per_key=True, use_exp2=True, gate_coef=1.0)
+    d = to_dev(W.generate(w, 149))
+    seg = [0, 64, 150, 256]
+    S0 = (torch.randn(2, 2, 128, 128, generator=torch.Generator().manual_seed(3)) * 0.5).to(DEV)
+    o_s, f_s, S_init = gb.split_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], seg=seg,
+                                        use_exp2=True, initial_state=S0)
+    torch.cuda.synchronize()
+    _no_nan(o_s, f_s, S_init)
+    r = run_oracle(d, S0=np32(S0).astype(np.float64))
+    assert_close(flat_o(o_s, w), r["o"], TOL[dtype], "split o")
+    assert_close(np32(f_s), r["final"], TOL[dtype], "split final")
+
+
+# ------------------------------------------------------------------ every summary path
+def _split_case(per_key, dtype, seed):
+    # slow decay keeps the transfer map far from zero, so a wrong M cannot hide
+    if per_key:
+        w = small(B=2, T=256, H=2, dtype=dtype, per_key=True, use_exp2=True, gate_coef=0.001)
+    else:
+        w = small(B=2, T=256, H=2, dtype=dtype, gate_coef=0.002)
+    return w, to_dev(W.generate(w, seed))
+
+
+@pytest.mark.parametrize("seg", [[0, 128, 256], [0, 100, 190, 256], [0, 64, 65, 200, 256]])
+@pytest.mark.parametrize("per_key,dtype", [(False, "bf16"), (False, "fp32"), (True, "fp32")])
+def test_split_equals_unsplit_every_path(seg, per_key, dtype):
+    # the summary kernels not covered by the bf16 per-key case above: the
+    # scalar-gate summary (bf16 and fp32) and the fp32 per-key summary;
+    # non-symmetric entry state, aligned and unaligned cuts
+    print(f"split path per_key={per_key} {dtype} seg={seg}", flush=True)
+    w, d = _split_case(per_key, dtype, 167 + len(seg))
+    tol = TOL[dtype]
+    S0 = (torch.randn(2, 2, 128, 128, generator=torch.Generator().manual_seed(19)) * 0.5).to(DEV)
+    ue2 = w.use_exp2
+    o_s, f_s, S_init = gb.split_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], seg=seg,
+                                        use_exp2=ue2, initial_state=S0)
+    torch.cuda.synchronize()
+    r = run_oracle(d, S0=np32(S0).astype(np.float64))
+    assert_close(flat_o(o_s, w), r["o"], tol, "split o")
+    assert_close(np32(f_s), r["final"], tol, "split final")
+    q, k, v, g, beta = flat_inputs(d)
+    offs = gb.segment_offsets(2, 256, seg)
+    s = oracle.summary(k, v, g, beta, offs, gate_per_key=per_key, use_exp2=ue2)
+    meta = gb.make_meta(offs, 512, DEV)
+    S_ext, M, _ = gb.gdn_state_summary(d["k"], d["v"], d["g"], d["beta"], meta=meta, use_exp2=ue2)
+    torch.cuda.synchronize()
+    assert_close(np32(S_ext), s["S_ext"], tol, "S_ext")
+    assert_close(np32(M), s["M"], tol, "M")
+    n_seg = len(seg) - 1
+    ext = s["S_ext"].reshape(2, n_seg, 2, 128, 128).transpose(1, 0, 2, 3, 4).reshape(n_seg, 4, 128, 128)
+    MM = s["M"].reshape(2, n_seg, 2, 128, 128).transpose(1, 0, 2, 3, 4).reshape(n_seg, 4, 128, 128)
+    si = oracle.merge(ext, MM, np32(S0).reshape(4, 128, 128).astype(np.float64))
+    si_gpu = np32(S_init).reshape(2, n_seg, 2, 128, 128).transpose(1, 0, 2, 3, 4).reshape(n_seg, 4, 128, 128)
+    assert_close(si_gpu, si[:n_seg], tol, "S_init")
+    # a transposed transfer map does not reproduce the unsplit end state
+    wrong = oracle.merge(ext, np.swapaxes(MM, -1, -2), np32(S0).reshape(4, 128, 128).astype(np.float64))
+    assert rel_err(wrong[n_seg], r["final"].reshape(4, 128, 128)) > 0.05
+
+
+@pytest.mark.parametrize("per_key,dtype", [(False, "bf16"), (True, "bf16"), (False, "fp32"), (True, "fp32")])
+def test_summary_modes(per_key, dtype):
+    # mode 1 (S_ext only) and mode 2 (M only) each equal their half of mode 0
+    # bit for bit (the same column tiles of the same recurrence), and match
+    # the oracle
+    print(f"summary modes per_key={per_key} {dtype}", flush=True)
+    w, d = _split_case(per_key, dtype, 181)
+    offs = gb.segment_offsets(2, 256, [0, 100, 256])
+    meta = gb.make_meta(offs, 512, DEV)
+    kw = dict(meta=meta, use_exp2=w.use_exp2)
+    e0, m0, _ = gb.gdn_state_summary(d["k"], d["v"], d["g"], d["beta"], mode=0, **kw)
+    e1, m1, _ = gb.gdn_state_summary(d["k"], d["v"], d["g"], d["beta"], mode=1, **kw)
+    e2, m2, _ = gb.gdn_state_summary(d["k"], d["v"], d["g"], d["beta"], mode=2, **kw)
+    torch.cuda.synchronize()
+    assert m1 is None and e2 is None
+    assert torch.equal(e1, e0), "mode 1 S_ext differs from mode 0"
+    assert torch.equal(m2, m0), "mode 2 M differs from mode 0"
+    q, k, v, g, beta = flat_inputs(d)
+    s = oracle.summary(k, v, g, beta, offs, gate_per_key=per_key, use_exp2=w.use_exp2)
+    assert_close(np32(e1), s["S_ext"], TOL[dtype], "mode 1 S_ext")
+    assert_close(np32(m2), s["M"], TOL[dtype], "mode 2 M")
+
+
+@pytest.mark.parametrize("per_key", [False, True])
+def test_values_near_the_fp16_operand_range(per_key):
+    # bf16 inputs become fp16 operands, and the state, the residual and v_new
+    # are rounded to fp16 every chunk: with v scaled by 2^11 (|v| up to about
+    # 1e4, the state and v_new alike) every operand stays inside fp16's range
+    # and the relative error is that of unit-scale inputs
+    print(f"values near the fp16 range per_key={per_key}", flush=True)
+    w = small(B=1, T=300, H=2, per_key=per_key, use_exp2=per_key, gate_coef=0.05 if per_key else 0.1)
+    d = to_dev(W.generate(w, 191))
+    d["v"] = (d["v"].float() * 2048.0).to(torch.bfloat16)
+    S0 = (torch.randn(1, 2, 128, 128, generator=torch.Generator().manual_seed(2)) * 2048.0).to(DEV)
+    o, fin, _ = run_gpu(d, initial_state=S0, output_final_state=True)
+    _no_nan(o, fin)
+    assert float(d["v"].float().abs().max()) > 8000.0
+    r = run_oracle(d, S0=np32(S0).astype(np.float64))
+    assert_close(flat_o(o, w), r["o"], TOL["bf16"], "scaled o")
+    assert_close(np32(fin), r["final"], TOL["bf16"], "scaled final")
