@@ -121,7 +121,44 @@ gdn_status size_workspace(const gdn::Problem& p, void* workspace, size_t* worksp
     return GDN_OK;
 }
 
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
 }  // namespace
+
+// Workspace layout: regions 256-byte aligned, one slot per (chunk, head) in
+// chunk-major order. With ws and base given, also sets the region pointers.
+size_t gdn::workspace_bytes(const gdn::Problem& p, gdn::Workspace* ws, char* base) {
+    const int64_t nch = (int64_t)p.um.n_chunks * p.H;
+    const int64_t es = p.dtype == 1 ? 2 : 4;      // operand element size (fp16 or fp32)
+    int64_t off = 0;
+    auto take = [&](int64_t bytes) { int64_t o = off; off = align256(off + bytes); return o; };
+    const int64_t oT = take(nch * BT * BT * es);
+    const int64_t oP = take(nch * BT * BT * es);
+    const int64_t og = (p.dtype == 0 && !p.per_key) ? take(nch * 4 * BT * 4) : 0;
+    int64_t oq = 0, od = 0, ok = 0, ol = 0;
+    if (p.per_key) {
+        oq = take(nch * BT * DK * es);
+        od = take(nch * BT * DK * es);
+        ok = take(nch * BT * DK * es);
+        ol = take(nch * DK * 4);
+    }
+    const int64_t ocf = p.dtype == 1 ? take(nch * (p.per_key ? CFB : CFS)) : 0;
+    const bool ordered = p.reorder && !p.um.dense && p.um.n_units > 1 && p.um.n_units <= ORD_MAX;
+    const int64_t oor = ordered ? take((int64_t)p.um.n_units * 4) : 0;
+    if (ws && base) {
+        ws->Tm = base + oT;
+        ws->P = base + oP;
+        ws->gam = (p.dtype == 0 && !p.per_key) ? reinterpret_cast<float*>(base + og) : nullptr;
+        ws->qg = p.per_key ? base + oq : nullptr;
+        ws->kd = p.per_key ? base + od : nullptr;
+        ws->kg = p.per_key ? base + ok : nullptr;
+        ws->gamL = p.per_key ? reinterpret_cast<float*>(base + ol) : nullptr;
+        ws->cfh = p.dtype == 1 ? base + ocf : nullptr;
+        ws->order = ordered ? reinterpret_cast<int32_t*>(base + oor) : nullptr;
+    }
+    return (size_t)(off > 0 ? off : 256);
+}
+
 
 extern "C" gdn_status gdn_varlen_meta(const int32_t* offsets, int32_t n_offsets, int32_t total_tokens,
                                       int32_t chunk_size, int32_t* chunk_indices, int32_t cap_chunks,

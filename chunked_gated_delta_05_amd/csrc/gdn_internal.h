@@ -15,6 +15,9 @@ constexpr int BT = 64;    // tokens per chunk
 constexpr int DK = 128;   // key width
 constexpr int DV = 128;   // value width
 constexpr int BV = 32;    // value columns per state-pass workgroup
+constexpr int CFB = 1024; // per-(chunk, head) coefficient block of the per-key fp16 state pass (bytes)
+constexpr int CFS = 1024; // the same block of the scalar-gate fp16 state pass (bytes)
+constexpr int ORD_MAX = 2048;  // packed units beyond this count keep their natural launch order
 
 // Where every chunk of every unit lives on the flat token axis.
 struct UnitMap {

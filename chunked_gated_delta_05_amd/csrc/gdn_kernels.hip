@@ -245,14 +245,12 @@ __device__ __forceinline__ int swzk(int r) { return (r & 1) | ((r & 2) << 1) | (
 // written by the preparation): four 64-entry fp16 rows in lane order (entry
 // 16G + 4it + r belongs to token row 16it + 4G + r) - beta, 1, 1, beta - then
 // the fp32 b^{G_L} of every key.
-constexpr int CFB = 1024;
 constexpr int CF_CY = 0, CF_CP = 64, CF_BG = 128, CF_BETA = 192;   // fp16 offsets
 constexpr int CF_GL = 128;                                          // fp32 offset
 // The scalar gate's block (CFS bytes) holds two fp32 rows in the same lane
 // order - b^{G_L - G} and b^G - at the float offsets below (floats 0..63 and
 // 192..255 are not used; beta is folded into T); b^{G_L} is the b^G entry of
 // the chunk's last valid token.
-constexpr int CFS = 1024;
 constexpr int CS_CP = 64, CS_BG = 128;
 __device__ __forceinline__ int lane_order(int t) { return 16 * ((t >> 2) & 3) + 4 * (t >> 4) + (t & 3); }
 
@@ -1985,7 +1983,6 @@ __global__ __launch_bounds__(256) void merge_kernel(int H, int n_seg, const floa
 // u is the number of units with more chunks, or as many chunks and a smaller
 // index (a permutation); order[rank] = u.
 constexpr int ORD_T = 1024;
-constexpr int ORD_MAX = 2048;    // more units than this keep their natural order
 
 __global__ __launch_bounds__(ORD_T) void unit_order_kernel(UnitMap um, int32_t* order) {
     __shared__ int32_t nch[ORD_T];
@@ -2009,40 +2006,6 @@ __global__ __launch_bounds__(ORD_T) void unit_order_kernel(UnitMap um, int32_t* 
 }
 
 // ------------------------------------------------------------------ launchers
-static int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
-
-size_t workspace_bytes(const Problem& p, Workspace* ws, char* base) {
-    const int64_t nch = (int64_t)p.um.n_chunks * p.H;
-    const int64_t es = p.dtype == 1 ? 2 : 4;      // operand element size (fp16 or fp32)
-    int64_t off = 0;
-    auto take = [&](int64_t bytes) { int64_t o = off; off = align256(off + bytes); return o; };
-    const int64_t oT = take(nch * BT * BT * es);
-    const int64_t oP = take(nch * BT * BT * es);
-    const int64_t og = (p.dtype == 0 && !p.per_key) ? take(nch * 4 * BT * 4) : 0;
-    int64_t oq = 0, od = 0, ok = 0, ol = 0;
-    if (p.per_key) {
-        oq = take(nch * BT * DK * es);
-        od = take(nch * BT * DK * es);
-        ok = take(nch * BT * DK * es);
-        ol = take(nch * DK * 4);
-    }
-    const int64_t ocf = p.dtype == 1 ? take(nch * (p.per_key ? CFB : CFS)) : 0;
-    const bool ordered = p.reorder && !p.um.dense && p.um.n_units > 1 && p.um.n_units <= ORD_MAX;
-    const int64_t oor = ordered ? take((int64_t)p.um.n_units * 4) : 0;
-    if (ws && base) {
-        ws->Tm = base + oT;
-        ws->P = base + oP;
-        ws->gam = (p.dtype == 0 && !p.per_key) ? reinterpret_cast<float*>(base + og) : nullptr;
-        ws->qg = p.per_key ? base + oq : nullptr;
-        ws->kd = p.per_key ? base + od : nullptr;
-        ws->kg = p.per_key ? base + ok : nullptr;
-        ws->gamL = p.per_key ? reinterpret_cast<float*>(base + ol) : nullptr;
-        ws->cfh = p.dtype == 1 ? base + ocf : nullptr;
-        ws->order = ordered ? reinterpret_cast<int32_t*>(base + oor) : nullptr;
-    }
-    return (size_t)(off > 0 ? off : 256);
-}
-
 hipError_t launch_prep(const Problem& p, const Workspace& ws, const void* k, const void* q,
                        const float* g, const void* beta, float* g_cumsum_slot, float* A_slot,
                        hipStream_t s) {

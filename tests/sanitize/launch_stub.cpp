@@ -1,0 +1,74 @@
+// Launch stubs for the host-only sanitizer build of libgdn's C ABI
+// (gdn_host.cpp under AddressSanitizer and UndefinedBehaviorSanitizer, no
+// GPU). Instead of launching kernels they check what the host code hands
+// them: every workspace region lies inside the caller's workspace, and the
+// unit map is consistent with the descriptor. Any violation aborts.
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "gdn_internal.h"
+
+namespace {
+const char* g_lo = nullptr;
+const char* g_hi = nullptr;
+
+void fail(const char* what) {
+    fprintf(stderr, "launch stub: %s\n", what);
+    abort();
+}
+
+void region(const void* p, int64_t bytes, const char* what) {
+    if (p == nullptr) return;
+    const char* c = static_cast<const char*>(p);
+    if (g_lo == nullptr || c < g_lo || bytes < 0 || c + bytes > g_hi) fail(what);
+    if (reinterpret_cast<uintptr_t>(c) % 256 != 0) fail(what);
+}
+
+void check_problem(const gdn::Problem& p, const gdn::Workspace& ws) {
+    const int64_t nch = int64_t(p.um.n_chunks) * p.H;
+    const int64_t es = p.dtype == 1 ? 2 : 4;
+    if (p.H < 1 || p.um.n_units < 0 || p.um.n_chunks < 0) fail("problem");
+    region(ws.Tm, nch * 64 * 64 * es, "T region");
+    region(ws.P, nch * 64 * 64 * es, "P region");
+    region(ws.gam, nch * 4 * 64 * 4, "gate rows");
+    region(ws.qg, nch * 64 * 128 * es, "q b^G region");
+    region(ws.kd, nch * 64 * 128 * es, "k b^G region");
+    region(ws.kg, nch * 64 * 128 * es, "k b^(G_L - G) region");
+    region(ws.gamL, nch * 128 * 4, "G_L region");
+    region(ws.cfh, nch * 1024, "coefficient blocks");
+    region(ws.order, int64_t(p.um.n_units) * 4, "unit order");
+    if (p.um.dense && int64_t(p.um.n_chunks) != int64_t(p.um.n_units) * p.um.nt_dense) fail("dense chunk count");
+}
+}  // namespace
+
+void stub_set_workspace(const void* base, size_t bytes) {
+    g_lo = static_cast<const char*>(base);
+    g_hi = g_lo + bytes;
+}
+
+namespace gdn {
+
+hipError_t launch_prep(const Problem& p, const Workspace& ws, const void* k, const void*, const float* g,
+                       const void* beta, float*, float*, hipStream_t) {
+    check_problem(p, ws);
+    if (p.um.total_tokens > 0 && (!k || !g || !beta)) fail("prep inputs");
+    return hipSuccess;
+}
+
+hipError_t launch_state(const Problem& p, const Workspace& ws, const void*, const void* k, const void*,
+                        const void*, const float*, void*, float*, float*, int summary, int want_ext, int want_M,
+                        float* S_ext, float* M, hipStream_t) {
+    check_problem(p, ws);
+    if (p.um.total_tokens > 0 && !k) fail("state inputs");
+    if (summary && ((want_ext && !S_ext) || (want_M && !M))) fail("summary outputs");
+    return hipSuccess;
+}
+
+hipError_t launch_merge(int B, int H, int n_seg, const float* S_ext, const float* M, const float*, float* S_init,
+                        float*, hipStream_t) {
+    if (B < 1 || H < 1 || n_seg < 0) fail("merge sizes");
+    if (n_seg > 0 && (!S_ext || !M || !S_init)) fail("merge buffers");
+    return hipSuccess;
+}
+
+}  // namespace gdn
