@@ -46,6 +46,11 @@ def _lib():
         lib.gdn_oracle_merge.restype = ctypes.c_int
         lib.gdn_oracle_merge.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                          ctypes.c_int64, _f64p, _f64p, _f64p, _f64p]
+        lib.gdn_oracle_bwd.restype = ctypes.c_int
+        lib.gdn_oracle_bwd.argtypes = [
+            ctypes.c_int64, _i64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+            _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, ctypes.c_int]
         lib.gdn_oracle_max_threads.restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -138,6 +143,40 @@ def merge(S_ext, M, S0=None):
     out = np.zeros((n_seg + 1, n, K, V))
     rc = _lib().gdn_oracle_merge(n_seg, n, K, V, _ptr(ext, _f64p), _ptr(m, _f64p),
                                  _ptr(s0, _f64p), _ptr(out, _f64p))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return out
+
+
+def bwd(q, k, v, g, beta, offsets, scale, dout, *, gate_per_key=False, use_exp2=False, S0=None,
+        dht=None, threads=0):
+    """Backward of ``fwd`` in fp64 (reverse mode of the token recurrence).
+
+    dout: [N, H, V] (dL/do); dht: [n_units, H, K, V] (dL/dh_final) or None.
+    Returns a dict of fp64 arrays: dq, dk [N, H, K], dv [N, H, V], dbeta
+    [N, H], dg [N, H] (scalar gate) or [N, H, K] (per key) and dS0
+    [n_units, H, K, V] (dL/dS0)."""
+    q, k, v, g, beta = _f32(q), _f32(k), _f32(v), _f32(g), _f32(beta)
+    N, H, K = k.shape
+    V = v.shape[2]
+    offs = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    n_units = len(offs) - 1
+    f64 = lambda a: None if a is None else np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    s0, do, dh = f64(S0), f64(dout), f64(dht)
+    if do.shape != (N, H, V):
+        raise ValueError("dout must be [N, H, V]")
+    for a, shp in ((s0, (n_units, H, K, V)), (dh, (n_units, H, K, V))):
+        if a is not None and a.shape != shp:
+            raise ValueError("states must be [n_units, H, K, V]")
+    out = {"dq": np.zeros((N, H, K)), "dk": np.zeros((N, H, K)), "dv": np.zeros((N, H, V)),
+           "dbeta": np.zeros((N, H)), "dg": np.zeros((N, H, K) if gate_per_key else (N, H)),
+           "dS0": np.zeros((n_units, H, K, V))}
+    rc = _lib().gdn_oracle_bwd(
+        n_units, _ptr(offs, _i64p), H, K, V, _ptr(q, _f32p), _ptr(k, _f32p), _ptr(v, _f32p),
+        _ptr(g, _f32p), _ptr(beta, _f32p), int(gate_per_key), int(use_exp2), float(scale),
+        _ptr(s0, _f64p), _ptr(do, _f64p), _ptr(dh, _f64p), _ptr(out["dq"], _f64p), _ptr(out["dk"], _f64p),
+        _ptr(out["dv"], _f64p), _ptr(out["dg"], _f64p), _ptr(out["dbeta"], _f64p), _ptr(out["dS0"], _f64p),
+        int(threads))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return out

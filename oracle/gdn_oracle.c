@@ -32,6 +32,23 @@
  *   M     = the product of the per-token maps (I - beta k k^T) Diag(d),
  *           i.e. the same update with v = 0 applied to X = I (K x K).
  *
+ * Backward (reverse mode of the same token recurrence; the backward slots of
+ * the native GDN op on the hyper-parallel Diff Coverage page,
+ * _AscendCGDN.backward: dq, dk, dv, dbeta and the raw-gate gradient dg),
+ * given do_t = dL/do_t and dL/dh_final, with h~ = Diag(d) h_{t-1} the
+ * decayed state and u = v_t - h~^T k_t, token by token from the last:
+ *
+ *   dh    += scale q_t do_t^T          dq_t = scale h_t do_t
+ *   dv_t   = beta_t dh^T k_t           dbeta_t = k_t^T dh u
+ *   dk_t   = beta_t dh u - h~ dv_t     dh~ = dh - k_t dv_t^T
+ *   dg_t   = ln(b) sum_j dh~[i][j] h~[i][j]   (summed over i for a scalar gate)
+ *   dh     = Diag(d) dh~
+ *
+ * and dL/dS0 is dh after the unit's first token. The states h_{t-1}, h_t
+ * are recomputed chunk by chunk (64 tokens) from the state stored at each
+ * chunk start, with the forward's own operations, so they are the forward's
+ * values.
+ *
  * All arithmetic is fp64.  Inputs are fp32 arrays (exact copies of the
  * rounded bf16 or fp32 inputs).  Layout: the token axis is flat (a
  * [B,T,H,D] tensor is viewed as [B*T, H, D]); units are given by token
@@ -223,6 +240,137 @@ int gdn_oracle_merge(int64_t n_seg, int64_t n, int64_t K, int64_t V, const doubl
                 }
         }
     return 0;
+}
+
+/*
+ * Backward of gdn_oracle_fwd (see the header). dout [N][H][V] and dht
+ * [n_units][H][K][V] (NULL: zero) are fp64; outputs dq, dk [N][H][K], dv
+ * [N][H][V], dbeta [N][H], dg [N][H] (scalar gate) or [N][H][K] (per key)
+ * and dS0 [n_units][H][K][V] (may be NULL) are fp64, for every head.
+ */
+int gdn_oracle_bwd(int64_t n_units, const int64_t* offsets, int64_t H, int64_t K, int64_t V,
+                   const float* q, const float* k, const float* v, const float* g, const float* beta,
+                   int gate_per_key, int use_exp2, double scale, const double* S0, const double* dout,
+                   const double* dht, double* dq, double* dk, double* dv, double* dg, double* dbeta,
+                   double* dS0, int n_threads) {
+    if (check_offsets(n_units, offsets) != 0 || H <= 0 || K <= 0 || V <= 0) return -1;
+    if (!dout || !dq || !dk || !dv || !dg || !dbeta) return -1;
+    const int64_t C = 64;                       /* tokens per recomputed chunk */
+    const double lnb = use_exp2 ? log(2.0) : 1.0;
+    const int64_t KV = K * V;
+    int64_t n_tasks = n_units * H;
+    int bad = 0;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+#endif
+    for (int64_t task = 0; task < n_tasks; ++task) {
+        const int64_t u = task / H, hd = task % H;
+        const int64_t t0 = offsets[u], t1 = offsets[u + 1], n = t1 - t0;
+        const int64_t nc = (n + C - 1) / C;
+        double* ck = (double*)malloc(sizeof(double) * (size_t)((nc > 0 ? nc : 1) * KV));   /* chunk-start states */
+        double* st = (double*)malloc(sizeof(double) * (size_t)((C + 1) * KV));            /* states in a chunk */
+        double* dh = (double*)malloc(sizeof(double) * (size_t)KV);
+        double* ht = (double*)malloc(sizeof(double) * (size_t)KV);                        /* h~ */
+        double* d = (double*)malloc(sizeof(double) * (size_t)K);
+        double* p = (double*)malloc(sizeof(double) * (size_t)V);
+        double* uu = (double*)malloc(sizeof(double) * (size_t)V);
+        double* dvt = (double*)malloc(sizeof(double) * (size_t)V);
+        double* tmp = (double*)malloc(sizeof(double) * (size_t)K);
+        if (!ck || !st || !dh || !ht || !d || !p || !uu || !dvt || !tmp) {
+            free(ck); free(st); free(dh); free(ht); free(d); free(p); free(uu); free(dvt); free(tmp);
+            bad |= 1;
+            continue;
+        }
+        /* forward, keeping the state at every chunk start */
+        double* h = st;
+        if (S0) memcpy(h, S0 + (u * H + hd) * KV, sizeof(double) * (size_t)KV);
+        else memset(h, 0, sizeof(double) * (size_t)KV);
+        for (int64_t t = t0; t < t1; ++t) {
+            if ((t - t0) % C == 0) memcpy(ck + ((t - t0) / C) * KV, h, sizeof(double) * (size_t)KV);
+            gate_vector(d, g, t, H, hd, K, gate_per_key, use_exp2);
+            token_step(h, K, V, k + (t * H + hd) * K, v + (t * H + hd) * V, (double)beta[t * H + hd], d, p);
+        }
+        /* reverse */
+        if (dht) memcpy(dh, dht + (u * H + hd) * KV, sizeof(double) * (size_t)KV);
+        else memset(dh, 0, sizeof(double) * (size_t)KV);
+        for (int64_t c = nc - 1; c >= 0; --c) {
+            const int64_t a = t0 + c * C, b = (a + C < t1) ? a + C : t1;
+            /* st[i] = state after token a + i - 1 (st[0] = chunk-start state) */
+            memcpy(st, ck + c * KV, sizeof(double) * (size_t)KV);
+            for (int64_t t = a; t < b; ++t) {
+                double* nx = st + (t - a + 1) * KV;
+                memcpy(nx, st + (t - a) * KV, sizeof(double) * (size_t)KV);
+                gate_vector(d, g, t, H, hd, K, gate_per_key, use_exp2);
+                token_step(nx, K, V, k + (t * H + hd) * K, v + (t * H + hd) * V, (double)beta[t * H + hd], d, p);
+            }
+            for (int64_t t = b - 1; t >= a; --t) {
+                const double* hprev = st + (t - a) * KV;
+                const double* hcur = st + (t - a + 1) * KV;
+                const float* qt = q + (t * H + hd) * K;
+                const float* kt = k + (t * H + hd) * K;
+                const float* vt = v + (t * H + hd) * V;
+                const double* dot = dout + (t * H + hd) * V;
+                const double bt = (double)beta[t * H + hd];
+                /* output: dh += scale q do^T, dq = scale h_t do */
+                for (int64_t i = 0; i < K; ++i) {
+                    double acc = 0.0;
+                    for (int64_t j = 0; j < V; ++j) {
+                        dh[i * V + j] += scale * (double)qt[i] * dot[j];
+                        acc += hcur[i * V + j] * dot[j];
+                    }
+                    dq[(t * H + hd) * K + i] = scale * acc;
+                }
+                /* the decayed state and the residual */
+                gate_vector(d, g, t, H, hd, K, gate_per_key, use_exp2);
+                for (int64_t i = 0; i < K; ++i)
+                    for (int64_t j = 0; j < V; ++j) ht[i * V + j] = d[i] * hprev[i * V + j];
+                for (int64_t j = 0; j < V; ++j) {
+                    double acc = 0.0;
+                    for (int64_t i = 0; i < K; ++i) acc += ht[i * V + j] * (double)kt[i];
+                    uu[j] = (double)vt[j] - acc;
+                }
+                /* dv = beta dh^T k; dbeta = k^T dh u; dk = beta dh u - h~ dv */
+                double db = 0.0;
+                for (int64_t j = 0; j < V; ++j) {
+                    double acc = 0.0;
+                    for (int64_t i = 0; i < K; ++i) acc += dh[i * V + j] * (double)kt[i];
+                    dvt[j] = bt * acc;
+                    db += acc * uu[j];
+                }
+                dbeta[t * H + hd] = db;
+                for (int64_t j = 0; j < V; ++j) dv[(t * H + hd) * V + j] = dvt[j];
+                for (int64_t i = 0; i < K; ++i) {
+                    double a1 = 0.0, a2 = 0.0;
+                    for (int64_t j = 0; j < V; ++j) {
+                        a1 += dh[i * V + j] * uu[j];
+                        a2 += ht[i * V + j] * dvt[j];
+                    }
+                    dk[(t * H + hd) * K + i] = bt * a1 - a2;
+                }
+                /* dh~ = dh - k dv^T, the gate gradient, then dh = Diag(d) dh~ */
+                for (int64_t i = 0; i < K; ++i) {
+                    double acc = 0.0;
+                    for (int64_t j = 0; j < V; ++j) {
+                        const double x = dh[i * V + j] - (double)kt[i] * dvt[j];
+                        acc += x * ht[i * V + j];
+                        dh[i * V + j] = d[i] * x;
+                    }
+                    tmp[i] = lnb * acc;
+                }
+                if (gate_per_key) {
+                    for (int64_t i = 0; i < K; ++i) dg[(t * H + hd) * K + i] = tmp[i];
+                } else {
+                    double s = 0.0;
+                    for (int64_t i = 0; i < K; ++i) s += tmp[i];
+                    dg[t * H + hd] = s;
+                }
+            }
+        }
+        if (dS0) memcpy(dS0 + (u * H + hd) * KV, dh, sizeof(double) * (size_t)KV);
+        free(ck); free(st); free(dh); free(ht); free(d); free(p); free(uu); free(dvt); free(tmp);
+    }
+    return bad ? -1 : 0;
 }
 
 int gdn_oracle_max_threads(void) {

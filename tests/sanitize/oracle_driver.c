@@ -17,6 +17,10 @@ int gdn_oracle_summary(int64_t n_units, const int64_t* offsets, int64_t H, int64
                        int64_t n_sel, const int64_t* heads_sel, double* S_ext, double* M, int n_threads);
 int gdn_oracle_merge(int64_t n_seg, int64_t n, int64_t K, int64_t V, const double* S_ext, const double* M,
                      const double* S0, double* S_init);
+int gdn_oracle_bwd(int64_t n_units, const int64_t* offsets, int64_t H, int64_t K, int64_t V, const float* q,
+                   const float* k, const float* v, const float* g, const float* beta, int gate_per_key, int use_exp2,
+                   double scale, const double* S0, const double* dout, const double* dht, double* dq, double* dk,
+                   double* dv, double* dg, double* dbeta, double* dS0, int n_threads);
 
 static uint64_t state = 88172645463325252ull;
 static double urand(void) {
@@ -57,6 +61,20 @@ int main(void) {
         bad |= gdn_oracle_summary(n_units, offs, H, K, V, k, v, g, beta, pk, it & 2, H, NULL, ext, M, 2) != 0;
         double* si = malloc(sizeof(double) * (size_t)((n_units + 1) * H * K * V));
         if (K == V) bad |= gdn_oracle_merge(n_units, H, K, V, ext, M, S0, si) != 0;
+        /* backward, with dL/dh_final on even iterations */
+        double* dout = malloc(sizeof(double) * (size_t)(N * H * V + 1));
+        for (int64_t i = 0; i < N * H * V; ++i) dout[i] = urand() - 0.5;
+        double* dq = malloc(sizeof(double) * (size_t)(N * H * K + 1));
+        double* dk = malloc(sizeof(double) * (size_t)(N * H * K + 1));
+        double* dv = malloc(sizeof(double) * (size_t)(N * H * V + 1));
+        double* dgr = malloc(sizeof(double) * (size_t)(N * H * (pk ? K : 1) + 1));
+        double* dbt = malloc(sizeof(double) * (size_t)(N * H + 1));
+        double* dS0 = malloc(sizeof(double) * (size_t)(n_units * H * K * V));
+        bad |= gdn_oracle_bwd(n_units, offs, H, K, V, q, k, v, g, beta, pk, it & 2, 0.5, S0, dout,
+                              (it & 4) ? NULL : S0, dq, dk, dv, dgr, dbt, (it & 8) ? NULL : dS0, 2) != 0;
+        bad |= gdn_oracle_bwd(n_units, offs, H, K, V, q, k, v, g, beta, pk, 0, 0.5, NULL, NULL, NULL, dq, dk, dv,
+                              dgr, dbt, NULL, 1) == 0;
+        free(dout); free(dq); free(dk); free(dv); free(dgr); free(dbt); free(dS0);
         /* rejected arguments */
         int64_t broken[3] = {0, 5, 3};
         bad |= gdn_oracle_fwd(2, broken, H, K, V, q, k, v, g, beta, pk, 0, 1.0, NULL, H, NULL, NULL, NULL, 0, NULL,
