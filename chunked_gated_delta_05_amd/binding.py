@@ -65,6 +65,8 @@ def lib():
                                         vp, vp, vp, sz, vp]
         L.gdn_state_merge.restype = ctypes.c_int
         L.gdn_state_merge.argtypes = [ctypes.c_int32] * 5 + [vp, vp, vp, vp, vp, vp]
+        L.gdn_chunk_bwd.restype = ctypes.c_int
+        L.gdn_chunk_bwd.argtypes = [ctypes.POINTER(GdnDesc)] + [vp] * 14 + [vp, sz, vp]
         L.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
         L.gdn_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(GdnDesc), vp, vp, vp, vp, vp, vp, vp, vp,
                                             ctypes.POINTER(GdnSlots), ctypes.c_int32, vp]
@@ -411,6 +413,77 @@ def gdn_state_merge(S_ext, M, S0=None, *, B: int, n_seg: int, want_final=True, S
     check(lib().gdn_state_merge(B, H, n_seg, K, V, _ptr(S_ext), _ptr(M), _ptr(S0), _ptr(S_init),
                                 _ptr(S_final), _stream(dev)), "gdn_state_merge")
     return S_init, S_final
+
+
+def gdn_chunk_bwd(q, k, v, g, beta, h, dout, scale=None, *, meta: UnitMeta | None = None, dht=None,
+                  use_exp2=False, want_dh0=True, workspace=None):
+    """Gradients of the chunked forward (scalar gate) through libgdn.
+
+    h: the forward's entry states (gdn_chunk_fwd(..., want_h=True) extras
+    "h", fp32 [n_chunks, H, K, V]); dout: dL/do in the input dtype, v's
+    shape; dht: dL/d(final state) fp32 [units, H, K, V] or None. Returns a
+    dict of fp32 tensors dq, dk, dv, dg, dbeta and dh0 (dL/d initial state,
+    when wanted)."""
+    H, per_key = _check_inputs(q, k, v, g, beta, meta, device_check=False)
+    if per_key:
+        raise NotImplementedError("the backward supports the scalar gate")
+    if scale is None:
+        scale = k.shape[-1] ** -0.5
+    desc = _desc(k, H, k.dtype, k.dtype, False, use_exp2, scale, meta)
+    dev = k.device
+    units = n_units_of(k, meta)
+    K, V = k.shape[-1], v.shape[-1]
+    n_chunks = meta.n_chunks if meta is not None else k.shape[0] * ((k.shape[1] + 63) // 64)
+    _check_tensor("h", h, torch.float32, (n_chunks, H, K, V), dev)
+    _check_tensor("dout", dout, k.dtype, v.shape, dev)
+    if dht is not None:
+        _check_tensor("dht", dht, torch.float32, (units, H, K, V), dev)
+    _require_gpu(q, k, v, g, beta, meta)
+    out = {"dq": torch.empty(q.shape, dtype=torch.float32, device=dev),
+           "dk": torch.empty(k.shape, dtype=torch.float32, device=dev),
+           "dv": torch.empty(v.shape, dtype=torch.float32, device=dev),
+           "dg": torch.empty(g.shape, dtype=torch.float32, device=dev),
+           "dbeta": torch.empty(beta.shape, dtype=torch.float32, device=dev)}
+    if want_dh0:
+        out["dh0"] = torch.empty((units, H, K, V), dtype=torch.float32, device=dev)
+    nb = ctypes.c_size_t(0)
+    check(lib().gdn_chunk_bwd(ctypes.byref(desc), *([None] * 14), None, ctypes.byref(nb), None), "workspace query")
+    ws = workspace if workspace is not None else torch.empty(nb.value, dtype=torch.uint8, device=dev)
+    if ws.dtype != torch.uint8 or ws.device != dev or ws.numel() < nb.value:
+        raise ValueError(f"workspace must be a uint8 tensor of at least {nb.value} bytes on {dev}")
+    nbytes = ctypes.c_size_t(ws.numel())
+    check(lib().gdn_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h),
+                              _ptr(dout), _ptr(dht), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                              _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out.get("dh0")), _ptr(ws),
+                              ctypes.byref(nbytes), _stream(dev)), "gdn_chunk_bwd")
+    return out
+
+
+class GatedDeltaRule(torch.autograd.Function):
+    """The chunked forward and its backward as one autograd op (the shape of
+    the pages' _AscendCGDN adapter): forward keeps the chunk entry states,
+    backward returns dq, dk, dv, dg, dbeta (and dL/d initial_state). Inputs
+    in the library's layouts; gradients come back in the inputs' dtypes."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, g, beta, initial_state=None, scale=None, meta=None, use_exp2=False):
+        o, fin, ex = gdn_chunk_fwd(q, k, v, g, beta, scale, meta=meta, initial_state=initial_state,
+                                   output_final_state=True, use_exp2=use_exp2, o_dtype=torch.float32, want_h=True)
+        ctx.save_for_backward(q, k, v, g, beta, ex["h"])
+        ctx.scale, ctx.meta, ctx.use_exp2 = scale, meta, use_exp2
+        ctx.has_s0 = initial_state is not None
+        ctx.mark_non_differentiable(fin)
+        return o, fin
+
+    @staticmethod
+    def backward(ctx, do, dfin):
+        q, k, v, g, beta, h = ctx.saved_tensors
+        r = gdn_chunk_bwd(q, k, v, g, beta, h, do.to(k.dtype).contiguous(), ctx.scale, meta=ctx.meta,
+                          dht=None if dfin is None else dfin.float().contiguous(), use_exp2=ctx.use_exp2,
+                          want_dh0=ctx.has_s0)
+        cast = lambda x, t: x.to(t.dtype)
+        return (cast(r["dq"], q), cast(r["dk"], k), cast(r["dv"], v), r["dg"], cast(r["dbeta"], beta),
+                r.get("dh0"), None, None, None)
 
 
 def split_forward(q, k, v, g, beta, scale=None, *, seg, use_exp2=False, initial_state=None,

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn.so")
 SOURCES = [os.path.join(CSRC, "gdn_kernels.hip"), os.path.join(CSRC, "gdn_host.cpp"),
-           os.path.join(CSRC, "gdn_noalloc.hip")]
+           os.path.join(CSRC, "gdn_noalloc.hip"), os.path.join(CSRC, "gdn_bwd.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
@@ -36,6 +36,7 @@ def build(verbose: bool = False) -> str:
     kobj = os.path.join(BUILD, "gdn_kernels.o")
     hobj = os.path.join(BUILD, "gdn_host.o")
     nobj = os.path.join(BUILD, "gdn_noalloc.o")
+    bobj = os.path.join(BUILD, "gdn_bwd.o")
     _run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           # MFMA accumulators in ordinary VGPRs: the state update scales them
@@ -47,7 +48,10 @@ def build(verbose: bool = False) -> str:
     _run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           *warn, *inc, "-c", SOURCES[2], "-o", nobj], verbose)
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", kobj, hobj, nobj, "-o", LIB + ".tmp"], verbose)
+    _run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          *warn, *inc, "-c", SOURCES[3], "-o", bobj], verbose)
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", kobj, hobj, nobj, bobj, "-o", LIB + ".tmp"], verbose)
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

@@ -1,0 +1,523 @@
+// HIP kernels of the chunked gated delta rule backward (scalar gate) for
+// gfx950.
+//
+// The forward of one chunk (n <= 64 tokens, entry state h in K x V, G the
+// chunk-local inclusive cumulative gate, b the decay base, gamma = b^{G_L}):
+//   Kd = diag(b^G) K, Qd = diag(b^G) Q, Kg = diag(b^{G_L - G}) K
+//   L  = strict_tril(diag(beta) (K K^T o D)),  D_ij = b^{G_i - G_j}
+//   T  = (I + L)^{-1},  Tb = T diag(beta)
+//   Y  = V - Kd h,  v_new = Tb Y
+//   O  = scale (Qd h + P v_new),  P = tril(Q K^T o D)
+//   h' = gamma h + Kg^T v_new
+// Given dO and dh' = dL/dh', reverse mode gives
+//   dvn = scale P^T dO + Kg dh'          Z = Tb^T dvn
+//   dh  = gamma dh' + scale Qd^T dO - Kd^T Z          (the reverse state pass)
+//   dV  = Z,  dKd = -Z h^T,  dQd = scale dO h^T,  dKg = v_new dh'^T
+//   dP  = scale dO v_new^T,  dTb = dvn Y^T,  dT = dTb diag(beta)
+//   dL  = -T^T dT T^T (strictly lower),  dbeta_j += sum_i dTb_ij T_ij,
+//   dbeta_i += sum_j dL_ij (k_i.k_j) D_ij
+// then dk, dq and the cumulative-gate gradient dG from the D factors, Kd, Qd,
+// Kg and gamma, and dg as the reverse cumulative sum of dG inside the chunk.
+// These are the stages of the staged backward on the hyper-parallel Diff
+// Coverage page (_AscendCKDAStages.backward: prepare, the reverse state pass
+// chunk_gated_delta_rule_bwd_dhu, finalize) and the reverse chunk loop of
+// kda_state_grad_ext_kernel on the state_summary.py page (the state gradient
+// decays by b^{G_L}, then gains Q^T dO scale - W^T (value gradient)).
+//
+// Kernels (fp32 operands on the fp32 16x16x4 MFMA, LDS tiles):
+//   bwd_dh_kernel    one workgroup per (unit, head, 32 value columns): the
+//                    reverse state pass; stores dh' and dvn of every chunk
+//                    and dL/dS0.
+//   bwd_grad_kernel  one workgroup per (chunk, head): recomputes Y and v_new
+//                    from the stored entry state, accumulates the products
+//                    over the value columns in 16-column tiles, then forms
+//                    dq, dk, dv, dbeta and dg.
+// The chunk preparation (T, P and the gate rows, fp32) comes from the
+// forward's fp32-operand preparation kernel.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int BKL = DK + 4;     // row stride (floats) of the 64 x 128 k and q tiles
+constexpr int BTL = BT + 1;     // row stride of the 64 x 64 T, P and scratch tiles
+
+struct BwdArgs {
+    UnitMap um;
+    int H;
+    int use_exp2;
+    float scale;
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* beta;
+    const void* dout;
+    const float* h;        // [n_chunks][H][K][V] entry state of every chunk
+    const float* dht;      // [units][H][K][V] or NULL
+    float* dq;
+    float* dk;
+    float* dv;
+    float* dg;
+    float* dbeta;
+    float* dh0;            // [units][H][K][V] or NULL
+    Workspace ws;          // fp32 preparation: T, P, gate rows
+    float* dH;             // [n_chunks][H][K][V]  dL/dh at every chunk's exit
+    float* dVN;            // [n_chunks][H][64][V] dvn of every chunk
+    int n_pairs;
+};
+
+template <class In>
+__device__ __forceinline__ float ldf(const In* p, int64_t i) { return (float)p[i]; }
+
+// acc += A B on the fp32 16x16x4 MFMA over k in [0, KLEN): lane (G, n)
+// supplies A[n][k0 + G] = fa(n, k0 + G) and B[k0 + G][n] = fb(k0 + G, n) and
+// holds D[4G + r][n]
+template <int KLEN, class FA, class FB>
+__device__ __forceinline__ void mmf(f32x4& acc, FA fa, FB fb, int G, int n) {
+#pragma unroll 8
+    for (int k0 = 0; k0 < KLEN; k0 += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa(n, k0 + G), fb(k0 + G, n), acc, 0, 0, 0);
+}
+
+// 16 bytes of inputs -> fp32 (4 fp32 or 8 bf16 values)
+template <class In> struct Vec16;
+template <> struct Vec16<float> {
+    static constexpr int N = 4;
+    __device__ static void cvt(u32x4 w, float* x) { for (int i = 0; i < 4; ++i) x[i] = u2f(w[i]); }
+};
+template <> struct Vec16<bf16> {
+    static constexpr int N = 8;
+    __device__ static void cvt(u32x4 w, float* x) {
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = u2f(w[i] << 16);
+            x[2 * i + 1] = u2f(w[i] & 0xffff0000u);
+        }
+    }
+};
+
+// ROWS x NCOLS elements (row r at src + r * stride, rows at or past `valid`
+// read as zero) into an fp32 LDS tile with row stride ld: 16-byte loads, all
+// issued before any store so that their latencies overlap
+template <class In, int ROWS, int NCOLS>
+__device__ __forceinline__ void load_tile(const In* src, int64_t stride, int valid, float* dst, int ld, int tid) {
+    constexpr int VPR = Vec16<In>::N, PER_ROW = NCOLS / VPR, NV = ROWS * PER_ROW;
+    constexpr int PT = (NV + 255) / 256;
+    u32x4 w[PT];
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+        const int e = tid + 256 * i, r = e / PER_ROW, c = (e - r * PER_ROW) * VPR;
+        w[i] = u32x4{0u, 0u, 0u, 0u};
+        if (e < NV && r < valid) w[i] = *reinterpret_cast<const u32x4*>(src + r * stride + c);
+    }
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+        const int e = tid + 256 * i, r = e / PER_ROW, c = (e - r * PER_ROW) * VPR;
+        if (e < NV) {
+            float x[VPR];
+            Vec16<In>::cvt(w[i], x);
+            for (int j = 0; j < VPR; ++j) dst[r * ld + c + j] = x[j];
+        }
+    }
+}
+
+// the chunk's k and q tiles, T (or T diag(beta)), P, the gate rows and beta
+template <class In, bool TB>
+__device__ void load_chunk(const BwdArgs& a, int64_t t0, int64_t ch, int head, int len, float* Ks, float* Qs,
+                           float* Ts, float* Ps, float* gm, float* bt, int tid) {
+    const int64_t rs = (int64_t)a.H * DK;
+    load_tile<In, BT, DK>(reinterpret_cast<const In*>(a.k) + (t0 * a.H + head) * DK, rs, len, Ks, BKL, tid);
+    load_tile<In, BT, DK>(reinterpret_cast<const In*>(a.q) + (t0 * a.H + head) * DK, rs, len, Qs, BKL, tid);
+    load_tile<float, BT, BT>(reinterpret_cast<const float*>(a.ws.Tm) + ch * (BT * BT), BT, BT, Ts, BTL, tid);
+    load_tile<float, BT, BT>(reinterpret_cast<const float*>(a.ws.P) + ch * (BT * BT), BT, BT, Ps, BTL, tid);
+    if (tid < BT) bt[tid] = tid < len ? ldf(reinterpret_cast<const In*>(a.beta), (t0 + tid) * a.H + head) : 0.0f;
+    gm[tid] = a.ws.gam[ch * (4 * BT) + tid];
+    __syncthreads();
+    if (TB)
+        for (int e = tid; e < BT * BT; e += 256) Ts[(e >> 6) * BTL + (e & 63)] *= bt[e & 63];
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ reverse state pass
+// One workgroup of four waves per (unit, head, 32 value columns); wave w
+// holds dL/dh for keys 32w .. 32w+31 of the 32 columns (four 16 x 16 tiles).
+// Chunks run from the last: store dh', then dvn = Kg dh' + scale P^T dO (wave
+// w: token rows 16w .. +15), Z = Tb^T dvn, and dh = gamma dh' + scale Qd^T dO
+// - Kd^T Z.
+template <class In>
+__global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
+    __shared__ __attribute__((aligned(16))) float Ks[BT * BKL];
+    __shared__ __attribute__((aligned(16))) float Qs[BT * BKL];
+    __shared__ __attribute__((aligned(16))) float Ts[BT * BTL];     // T diag(beta)
+    __shared__ __attribute__((aligned(16))) float Ps[BT * BTL];
+    __shared__ __attribute__((aligned(16))) float gm[4 * BT];       // G, b^G, b^{G_L - G}, b^{G_L}
+    __shared__ float bt[BT];
+    __shared__ __attribute__((aligned(16))) float dOs[BT * 33];     // dO, 32 columns
+    __shared__ __attribute__((aligned(16))) float dhS[DK * 33];     // dh' [key][column]
+    __shared__ __attribute__((aligned(16))) float dvS[BT * 33];     // dvn
+    __shared__ __attribute__((aligned(16))) float Zs[BT * 33];      // b^G Z
+
+    const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = a.H;
+    const int tile = blockIdx.x & 3, pair = blockIdx.x >> 2;
+    if (pair >= a.n_pairs) return;
+    const int u = pair / H, head = pair - u * H;
+    const UnitInfo ui = uniform(unit_info(a.um, u));
+    const int c0 = tile * 32;
+    const int64_t uh = (int64_t)u * H + head;
+    const In* dout = reinterpret_cast<const In*>(a.dout);
+
+    // dL/dh at the unit's end: keys 32w + 16kt + 4G + r, column c0 + 16ct + n
+    f32x4 dh[2][2];
+    for (int kt = 0; kt < 2; ++kt)
+        for (int ct = 0; ct < 2; ++ct)
+            for (int r = 0; r < 4; ++r) {
+                const int key = 32 * w + 16 * kt + 4 * G + r, col = 16 * ct + n;
+                const float x = a.dht ? a.dht[(uh * DK + key) * DV + c0 + col] : 0.0f;
+                dh[kt][ct][r] = x;
+                dhS[key * 33 + col] = x;
+            }
+
+    for (int c = ui.nch - 1; c >= 0; --c) {
+        int len = ui.len - c * BT;
+        len = len > BT ? BT : len;
+        const int64_t t0 = ui.start + (int64_t)c * BT;
+        const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
+        __syncthreads();                               // the previous chunk's tiles are consumed
+        load_chunk<In, true>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, gm, bt, tid);
+        load_tile<In, BT, 32>(dout + (t0 * H + head) * DV + c0, (int64_t)H * DV, len, dOs, 33, tid);
+        // dh' of this chunk to the workspace
+        for (int kt = 0; kt < 2; ++kt)
+            for (int ct = 0; ct < 2; ++ct)
+                for (int r = 0; r < 4; ++r) {
+                    const int key = 32 * w + 16 * kt + 4 * G + r;
+                    a.dH[(ch * DK + key) * DV + c0 + 16 * ct + n] = dh[kt][ct][r];
+                }
+        __syncthreads();
+        // dvn = b^{G_L - G} (K dh') + scale P^T dO, token rows 16w .. +15
+        for (int ct = 0; ct < 2; ++ct) {
+            f32x4 kh = {0.f, 0.f, 0.f, 0.f}, pd = {0.f, 0.f, 0.f, 0.f};
+            mmf<DK>(kh, [&](int m, int k) { return Ks[(16 * w + m) * BKL + k]; },
+                    [&](int k, int nn) { return dhS[k * 33 + 16 * ct + nn]; }, G, n);
+            mmf<BT>(pd, [&](int m, int k) { return Ps[k * BTL + 16 * w + m]; },
+                    [&](int k, int nn) { return dOs[k * 33 + 16 * ct + nn]; }, G, n);
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * w + 4 * G + r;
+                const float x = gm[2 * BT + row] * kh[r] + a.scale * pd[r];
+                dvS[row * 33 + 16 * ct + n] = x;
+                a.dVN[(ch * BT + row) * DV + c0 + 16 * ct + n] = x;
+            }
+        }
+        __syncthreads();
+        // Z = Tb^T dvn, kept as b^G Z
+        for (int ct = 0; ct < 2; ++ct) {
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            mmf<BT>(z, [&](int m, int k) { return Ts[k * BTL + 16 * w + m]; },
+                    [&](int k, int nn) { return dvS[k * 33 + 16 * ct + nn]; }, G, n);
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * w + 4 * G + r;
+                Zs[row * 33 + 16 * ct + n] = gm[BT + row] * z[r];
+            }
+        }
+        __syncthreads();
+        // dh = b^{G_L} dh' + Q^T (scale b^G dO) - K^T (b^G Z), keys 32w .. +31
+        const float gam = gm[3 * BT];
+        for (int kt = 0; kt < 2; ++kt)
+            for (int ct = 0; ct < 2; ++ct) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acz = {0.f, 0.f, 0.f, 0.f};
+                const int key0 = 32 * w + 16 * kt;
+                mmf<BT>(acc, [&](int m, int k) { return Qs[k * BKL + key0 + m]; },
+                        [&](int k, int nn) { return a.scale * gm[BT + k] * dOs[k * 33 + 16 * ct + nn]; }, G, n);
+                mmf<BT>(acz, [&](int m, int k) { return Ks[k * BKL + key0 + m]; },
+                        [&](int k, int nn) { return Zs[k * 33 + 16 * ct + nn]; }, G, n);
+                for (int r = 0; r < 4; ++r) {
+                    const float x = gam * dh[kt][ct][r] + acc[r] - acz[r];
+                    dh[kt][ct][r] = x;
+                    dhS[(key0 + 4 * G + r) * 33 + 16 * ct + n] = x;
+                }
+            }
+    }
+    if (a.dh0)
+        for (int kt = 0; kt < 2; ++kt)
+            for (int ct = 0; ct < 2; ++ct)
+                for (int r = 0; r < 4; ++r) {
+                    const int key = 32 * w + 16 * kt + 4 * G + r;
+                    a.dh0[(uh * DK + key) * DV + c0 + 16 * ct + n] = dh[kt][ct][r];
+                }
+}
+
+// ------------------------------------------------------------------ per-chunk gradients
+// One workgroup of four waves per (chunk, head); wave w owns token rows
+// 16w .. 16w+15 of every row-indexed product. The value columns are visited
+// in 16-column tiles: each recomputes Y = V - Kd h and v_new = Tb Y, writes
+// dV = Z = Tb^T dvn, and accumulates over its columns dP, dTb (64 x 64) and
+// dQd, dKg, dKd (64 x 128) in registers. The finish turns dTb into dL through
+// T, and assembles dq, dk, dbeta and the gate gradients.
+constexpr int VT = 16;          // value columns per tile
+constexpr int VTL = VT + 1;
+
+template <class In>
+__global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
+    __shared__ __attribute__((aligned(16))) float Ks[BT * BKL];
+    __shared__ __attribute__((aligned(16))) float Qs[BT * BKL];
+    __shared__ __attribute__((aligned(16))) float Ts[BT * BTL];     // T
+    __shared__ __attribute__((aligned(16))) float Ps[BT * BTL];
+    __shared__ __attribute__((aligned(16))) float gm[4 * BT];
+    __shared__ float bt[BT];
+    // value-tile buffers, reused as two 64 x 64 scratch tiles by the finish
+    __shared__ __attribute__((aligned(16))) float tb[2 * DK * VTL + 6 * BT * VTL];
+    __shared__ float rowG[BT], colP[4][BT], dbT[BT], red[8];
+    float* Hs = tb;                      // h      [key][col]
+    float* DHs = Hs + DK * VTL;          // dh'    [key][col]
+    float* Vs = DHs + DK * VTL;          // v      [row][col]
+    float* DOs = Vs + BT * VTL;          // dO
+    float* DVs = DOs + BT * VTL;         // dvn
+    float* Ys = DVs + BT * VTL;          // Y
+    float* VNs = Ys + BT * VTL;          // v_new
+    float* Zs = VNs + BT * VTL;          // Z
+    float* X1 = tb;                      // finish: 64 x 64 scratch
+    float* X2 = tb + BT * BTL;
+    static_assert(2 * BT * BTL <= 2 * DK * VTL + 6 * BT * VTL, "scratch tiles fit the value-tile buffers");
+
+    const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ci = blockIdx.x, head = blockIdx.y, H = a.H;
+    int u, cc;
+    chunk_of(a.um, ci, u, cc);
+    if (u < 0) return;
+    const UnitInfo ui = unit_info(a.um, u);
+    const int64_t t0 = ui.start + (int64_t)cc * BT;
+    int len = ui.len - cc * BT;
+    len = len < 0 ? 0 : (len > BT ? BT : len);
+    const int64_t ch = (int64_t)ci * H + head;
+    const float lnb = a.use_exp2 ? 0.6931471805599453f : 1.0f;
+    const In* vin = reinterpret_cast<const In*>(a.v);
+    const In* dout = reinterpret_cast<const In*>(a.dout);
+
+    load_chunk<In, false>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, gm, bt, tid);
+    if (tid < BT) rowG[tid] = 0.0f;
+    const int row0 = 16 * w;
+    auto bG = [&](int row) { return gm[BT + row]; };
+    auto Tb = [&](int i, int j) { return Ts[i * BTL + j] * bt[j]; };   // T diag(beta)
+
+    f32x4 aP[4], aT[4], aQ[8], aKg[8], aKd[8];
+    for (int j = 0; j < 4; ++j) { aP[j] = f32x4{0.f, 0.f, 0.f, 0.f}; aT[j] = aP[j]; }
+    for (int j = 0; j < 8; ++j) { aQ[j] = f32x4{0.f, 0.f, 0.f, 0.f}; aKg[j] = aQ[j]; aKd[j] = aQ[j]; }
+    float hdh = 0.0f;     // this thread's share of sum(h o dh')
+
+    for (int vt = 0; vt < DV / VT; ++vt) {
+        const int vc0 = vt * VT;
+        __syncthreads();                           // the previous tile's buffers are consumed
+        load_tile<float, DK, VT>(a.h + ch * DK * DV + vc0, DV, DK, Hs, VTL, tid);
+        load_tile<float, DK, VT>(a.dH + ch * DK * DV + vc0, DV, DK, DHs, VTL, tid);
+        load_tile<In, BT, VT>(vin + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, Vs, VTL, tid);
+        load_tile<In, BT, VT>(dout + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, DOs, VTL, tid);
+        load_tile<float, BT, VT>(a.dVN + ch * BT * DV + vc0, DV, BT, DVs, VTL, tid);
+        __syncthreads();
+        for (int e = tid; e < DK * VT; e += 256) {
+            const int key = e / VT, cl = e - key * VT;
+            hdh += Hs[key * VTL + cl] * DHs[key * VTL + cl];
+        }
+        // Y = V - b^G (K h), rows of this wave
+        {
+            f32x4 kh = {0.f, 0.f, 0.f, 0.f};
+            mmf<DK>(kh, [&](int m, int k) { return Ks[(row0 + m) * BKL + k]; },
+                    [&](int k, int nn) { return Hs[k * VTL + nn]; }, G, n);
+            for (int r = 0; r < 4; ++r) {
+                const int row = row0 + 4 * G + r;
+                Ys[row * VTL + n] = Vs[row * VTL + n] - bG(row) * kh[r];
+            }
+        }
+        __syncthreads();
+        // v_new = Tb Y and Z = Tb^T dvn = dV, rows of this wave
+        {
+            f32x4 vn = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
+            mmf<BT>(vn, [&](int m, int k) { return Tb(row0 + m, k); }, [&](int k, int nn) { return Ys[k * VTL + nn]; },
+                    G, n);
+            mmf<BT>(z, [&](int m, int k) { return Tb(k, row0 + m); }, [&](int k, int nn) { return DVs[k * VTL + nn]; },
+                    G, n);
+            for (int r = 0; r < 4; ++r) {
+                const int row = row0 + 4 * G + r;
+                VNs[row * VTL + n] = vn[r];
+                Zs[row * VTL + n] = z[r];
+                if (row < len) a.dv[((t0 + row) * H + head) * DV + vc0 + n] = z[r];
+            }
+        }
+        __syncthreads();
+        // accumulate over this tile's columns
+        for (int j = 0; j < 4; ++j) {
+            mmf<VT>(aP[j], [&](int m, int k) { return a.scale * DOs[(row0 + m) * VTL + k]; },
+                    [&](int k, int nn) { return VNs[(16 * j + nn) * VTL + k]; }, G, n);
+            mmf<VT>(aT[j], [&](int m, int k) { return DVs[(row0 + m) * VTL + k]; },
+                    [&](int k, int nn) { return Ys[(16 * j + nn) * VTL + k]; }, G, n);
+        }
+        for (int j = 0; j < 8; ++j) {
+            mmf<VT>(aQ[j], [&](int m, int k) { return a.scale * DOs[(row0 + m) * VTL + k]; },
+                    [&](int k, int nn) { return Hs[(16 * j + nn) * VTL + k]; }, G, n);
+            mmf<VT>(aKg[j], [&](int m, int k) { return VNs[(row0 + m) * VTL + k]; },
+                    [&](int k, int nn) { return DHs[(16 * j + nn) * VTL + k]; }, G, n);
+            mmf<VT>(aKd[j], [&](int m, int k) { return -Zs[(row0 + m) * VTL + k]; },
+                    [&](int k, int nn) { return Hs[(16 * j + nn) * VTL + k]; }, G, n);
+        }
+    }
+    __syncthreads();
+
+    // ---- finish. dTb (lower incl. diagonal) to X1, dP (lower incl.) to X2
+    for (int j = 0; j < 4; ++j)
+        for (int r = 0; r < 4; ++r) {
+            const int i = row0 + 4 * G + r, jj = 16 * j + n;
+            X1[i * BTL + jj] = jj <= i ? aT[j][r] : 0.0f;
+            X2[i * BTL + jj] = jj <= i ? aP[j][r] : 0.0f;
+        }
+    __syncthreads();
+    // dbeta from Tb = T diag(beta): column sums of dTb o T
+    if (tid < BT) {
+        float s = 0.0f;
+        for (int i = tid; i < BT; ++i) s += X1[i * BTL + tid] * Ts[i * BTL + tid];
+        dbT[tid] = s;
+    }
+    // M1 = dT T^T with dT = dTb diag(beta), rows of this wave
+    f32x4 m1[4];
+    for (int j = 0; j < 4; ++j) {
+        m1[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        mmf<BT>(m1[j], [&](int m, int k) { return X1[(row0 + m) * BTL + k] * bt[k]; },
+                [&](int k, int nn) { return Ts[(16 * j + nn) * BTL + k]; }, G, n);
+    }
+    __syncthreads();
+    for (int j = 0; j < 4; ++j)
+        for (int r = 0; r < 4; ++r) X1[(row0 + 4 * G + r) * BTL + 16 * j + n] = m1[j][r];
+    __syncthreads();
+    // dL = -T^T M1 (strictly lower), and G = (K K^T) o D, rows of this wave
+    f32x4 dl[4], kk[4];
+    for (int j = 0; j < 4; ++j) {
+        dl[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        kk[j] = dl[j];
+        mmf<BT>(dl[j], [&](int m, int k) { return Ts[k * BTL + row0 + m]; },
+                [&](int k, int nn) { return X1[k * BTL + 16 * j + nn]; }, G, n);
+        mmf<DK>(kk[j], [&](int m, int k) { return Ks[(row0 + m) * BKL + k]; },
+                [&](int k, int nn) { return Ks[(16 * j + nn) * BKL + k]; }, G, n);
+    }
+    __syncthreads();
+    // element terms of L and P: dbeta_i += sum_j dL_ij G_ij, dG = beta_i dL,
+    // the G_i / G_j parts of the gate gradient, and dG o D, dP o D in place
+    float rb[4] = {0.f, 0.f, 0.f, 0.f}, rg[4] = {0.f, 0.f, 0.f, 0.f}, cg[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j)
+        for (int r = 0; r < 4; ++r) {
+            const int i = row0 + 4 * G + r, jj = 16 * j + n;
+            const float d = jj <= i ? fpow(gm[i] - gm[jj], a.use_exp2) : 0.0f;
+            const float lij = jj < i ? -dl[j][r] : 0.0f;              // dL
+            const float gij = kk[j][r] * d;                           // (k_i . k_j) D_ij
+            const float dgg = bt[i] * lij;                            // dG
+            const float pij = Ps[i * BTL + jj], dpij = X2[i * BTL + jj];
+            rb[r] += lij * gij;
+            const float t = lnb * (dgg * gij + dpij * pij);
+            rg[r] += t;
+            cg[j] -= t;
+            X1[i * BTL + jj] = dgg * d;
+            X2[i * BTL + jj] = dpij * d;
+        }
+    // column sums over this wave's rows (lanes 16 apart), one partial per
+    // wave, added in a fixed order below: no float atomics, so the result
+    // is the same on every run
+    for (int j = 0; j < 4; ++j) {
+        cg[j] += __shfl_xor(cg[j], 16, 64);
+        cg[j] += __shfl_xor(cg[j], 32, 64);
+    }
+    if (G == 0)
+        for (int j = 0; j < 4; ++j) colP[w][16 * j + n] = cg[j];
+    // row sums over the 16 lanes of each group
+    for (int r = 0; r < 4; ++r)
+        for (int s = 1; s < 16; s <<= 1) {
+            rb[r] += __shfl_xor(rb[r], s, 16);
+            rg[r] += __shfl_xor(rg[r], s, 16);
+        }
+    if (n == 0)
+        for (int r = 0; r < 4; ++r) {
+            atomicAdd(&rowG[row0 + 4 * G + r], rg[r]);
+            atomicAdd(&dbT[row0 + 4 * G + r], rb[r]);
+        }
+    __syncthreads();
+    // dq, dk, rows of this wave: the products with dG o D and dP o D, then
+    // b^G dQd, b^G dKd + b^{G_L - G} dKg, and their gate terms
+    float rq[4] = {0.f, 0.f, 0.f, 0.f}, rkg = 0.0f;
+    for (int j = 0; j < 8; ++j) {
+        f32x4 q1 = {0.f, 0.f, 0.f, 0.f}, k1 = q1;
+        mmf<BT>(q1, [&](int m, int k) { return X2[(row0 + m) * BTL + k]; },
+                [&](int k, int nn) { return Ks[k * BKL + 16 * j + nn]; }, G, n);
+        mmf<BT>(k1, [&](int m, int k) { return X1[(row0 + m) * BTL + k]; },
+                [&](int k, int nn) { return Ks[k * BKL + 16 * j + nn]; }, G, n);
+        mmf<BT>(k1, [&](int m, int k) { return X1[k * BTL + row0 + m]; },
+                [&](int k, int nn) { return Ks[k * BKL + 16 * j + nn]; }, G, n);
+        mmf<BT>(k1, [&](int m, int k) { return X2[k * BTL + row0 + m]; },
+                [&](int k, int nn) { return Qs[k * BKL + 16 * j + nn]; }, G, n);
+        for (int r = 0; r < 4; ++r) {
+            const int i = row0 + 4 * G + r, d = 16 * j + n;
+            const float bg = gm[BT + i], blg = gm[2 * BT + i];
+            const float qv = Qs[i * BKL + d], kv = Ks[i * BKL + d];
+            const float dqv = q1[r] + bg * aQ[j][r];
+            const float dkv = k1[r] + bg * aKd[j][r] + blg * aKg[j][r];
+            rq[r] += lnb * (aQ[j][r] * bg * qv + aKd[j][r] * bg * kv - aKg[j][r] * blg * kv);
+            rkg += lnb * aKg[j][r] * blg * kv;
+            if (i < len) {
+                a.dq[((t0 + i) * H + head) * DK + d] = dqv;
+                a.dk[((t0 + i) * H + head) * DK + d] = dkv;
+            }
+        }
+    }
+    for (int r = 0; r < 4; ++r)
+        for (int s = 1; s < 16; s <<= 1) rq[r] += __shfl_xor(rq[r], s, 16);
+    if (n == 0)
+        for (int r = 0; r < 4; ++r) atomicAdd(&rowG[row0 + 4 * G + r], rq[r]);
+    // G_L: lnb (gamma sum(h o dh') + sum_i sum_d dKg Kg), summed over the workgroup
+    float tl = lnb * gm[3 * BT] * hdh + rkg;
+    for (int s = 1; s < 64; s <<= 1) tl += __shfl_xor(tl, s, 64);
+    if (lane == 0) red[w] = tl;
+    __syncthreads();
+    // dg: reverse cumulative sum over the chunk's rows of the gate gradient,
+    // with G_L's entering at the last valid row
+    if (w == 0) {
+        const float gl = red[0] + red[1] + red[2] + red[3];
+        const float colG = ((colP[0][lane] + colP[1][lane]) + colP[2][lane]) + colP[3][lane];
+        float x = lane < len ? rowG[lane] + colG + (lane == len - 1 ? gl : 0.0f) : 0.0f;
+        for (int s = 1; s < 64; s <<= 1) {
+            const float y = __shfl_down(x, s, 64);
+            if (lane + s < 64) x += y;
+        }
+        if (lane < len) {
+            a.dg[(t0 + lane) * H + head] = x;
+            a.dbeta[(t0 + lane) * H + head] = dbT[lane];
+        }
+    }
+}
+
+// ------------------------------------------------------------------ launcher
+hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* dVN, const void* q, const void* k,
+                      const void* v, const float* g, const void* beta, const float* h, const void* dout,
+                      const float* dht, float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0,
+                      hipStream_t s) {
+    if (launch_prep_f32(p, ws, k, q, g, beta, s) != hipSuccess) return hipGetLastError();
+    BwdArgs a;
+    a.um = p.um; a.H = p.H; a.use_exp2 = p.use_exp2; a.scale = p.scale;
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.dout = dout; a.h = h; a.dht = dht;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
+    a.ws = ws; a.dH = dH; a.dVN = dVN;
+    a.n_pairs = p.um.n_units * p.H;
+    if (a.n_pairs > 0) {
+        if (p.dtype == 1) hipLaunchKernelGGL(bwd_dh_kernel<bf16>, dim3(4 * a.n_pairs), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(bwd_dh_kernel<float>, dim3(4 * a.n_pairs), dim3(256), 0, s, a);
+    }
+    if (p.um.n_chunks > 0) {
+        dim3 grid(p.um.n_chunks, p.H);
+        if (p.dtype == 1) hipLaunchKernelGGL(bwd_grad_kernel<bf16>, grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(bwd_grad_kernel<float>, grid, dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -258,6 +258,56 @@ extern "C" gdn_status gdn_state_summary(const gdn_desc* desc, const void* q, con
     return GDN_OK;
 }
 
+// Workspace of the backward: the fp32-operand preparation (T, P and the gate
+// rows of every chunk-head), then dL/dh at every chunk's exit and dvn of
+// every chunk, fp32.
+static size_t bwd_workspace(const gdn::Problem& p, gdn::Workspace* ws, float** dH, float** dVN, char* base) {
+    gdn::Problem pf = p;
+    pf.dtype = 0;
+    pf.reorder = 0;
+    const int64_t prep = (int64_t)gdn::workspace_bytes(pf, ws, base);
+    const int64_t nch = (int64_t)p.um.n_chunks * p.H;
+    const int64_t o1 = align256(prep), o2 = align256(o1 + nch * DK * DV * 4);
+    const int64_t end = align256(o2 + nch * BT * DV * 4);
+    if (base) {
+        *dH = reinterpret_cast<float*>(base + o1);
+        *dVN = reinterpret_cast<float*>(base + o2);
+    }
+    return (size_t)end;
+}
+
+extern "C" gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                                    const float* g, const void* beta, const float* h, const void* dout,
+                                    const float* dht, float* dq, float* dk, float* dv, float* dg,
+                                    float* dbeta, float* dh0, void* workspace, size_t* workspace_bytes,
+                                    hipStream_t stream) {
+    gdn::Problem p;
+    gdn_status st = validate(desc, &p);
+    if (st != GDN_OK) return st;
+    if (p.per_key) return GDN_ERR_UNSUPPORTED;
+    if (workspace_bytes == nullptr) return GDN_ERR_INVALID;
+    const size_t need = bwd_workspace(p, nullptr, nullptr, nullptr, nullptr);
+    if (workspace == nullptr) {
+        *workspace_bytes = need;
+        return GDN_OK;
+    }
+    if (*workspace_bytes < need) {
+        *workspace_bytes = need;
+        return GDN_ERR_CAPACITY;
+    }
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return GDN_ERR_INVALID;
+    const bool tokens = p.um.total_tokens > 0;
+    if (tokens && (!q || !k || !v || !g || !beta || !h || !dout || !dq || !dk || !dv || !dg || !dbeta))
+        return GDN_ERR_INVALID;
+    gdn::Workspace ws;
+    float *dH = nullptr, *dVN = nullptr;
+    bwd_workspace(p, &ws, &dH, &dVN, static_cast<char*>(workspace));
+    if (gdn::launch_bwd(p, ws, dH, dVN, q, k, v, g, beta, h, dout, dht, dq, dk, dv, dg, dbeta, dh0, stream) !=
+        hipSuccess)
+        return GDN_ERR_DEVICE;
+    return GDN_OK;
+}
+
 extern "C" gdn_status gdn_state_merge(int32_t B, int32_t H, int32_t n_seg, int32_t K, int32_t V,
                                       const float* S_ext, const float* M, const float* S0, float* S_init,
                                       float* S_final, hipStream_t stream) {

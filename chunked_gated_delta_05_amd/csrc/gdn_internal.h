@@ -78,6 +78,16 @@ hipError_t launch_state(const Problem& p, const Workspace& ws, const void* q, co
 hipError_t launch_merge(int B, int H, int n_seg, const float* S_ext, const float* M,
                         const float* S0, float* S_init, float* S_final, hipStream_t s);
 
+// The fp32-operand chunk preparation (T, P, gate rows) for bf16 or fp32 inputs.
+hipError_t launch_prep_f32(const Problem& p, const Workspace& ws, const void* k, const void* q,
+                           const float* g, const void* beta, hipStream_t s);
+
+// The backward: fp32 preparation, reverse state pass, per-chunk gradients.
+hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* dVN, const void* q,
+                      const void* k, const void* v, const float* g, const void* beta, const float* h,
+                      const void* dout, const float* dht, float* dq, float* dk, float* dv, float* dg,
+                      float* dbeta, float* dh0, hipStream_t s);
+
 // Host-only checks of a gdn_chunk_fwd call (descriptor, flags, pointers), and
 // the workspace it needs; no HIP call.
 gdn_status fwd_preflight(const gdn_desc* desc, const void* q, const void* k, const void* v,

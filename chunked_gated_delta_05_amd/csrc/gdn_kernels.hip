@@ -55,42 +55,9 @@
 #include <type_traits>
 
 #include "gdn_internal.h"
+#include "gdn_device.h"
 
 namespace gdn {
-
-typedef __bf16 bf16;
-typedef _Float16 f16;
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
-
-// bits of a float. Taken through a by-value parameter: applied directly to a
-// vector element (v[i]), __builtin_bit_cast reads element 0 with this
-// compiler.
-__device__ __forceinline__ uint32_t f2u(float x) { return __builtin_bit_cast(uint32_t, x); }
-__device__ __forceinline__ float u2f(uint32_t x) { return __builtin_bit_cast(float, x); }
-
-// b^x with the hardware base-2 exponential (about 1 ulp; e^x = 2^(x log2 e))
-__device__ __forceinline__ float fpow(float x, int use_exp2) {
-    return __builtin_amdgcn_exp2f(use_exp2 ? x : x * 1.4426950408889634f);
-}
-
-// Workgroup barrier for LDS hand-offs only: this wave's LDS accesses complete
-// before it, but outstanding global loads and stores stay in flight (the
-// fence of __syncthreads would wait for all of them).
-// The s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
-// expcnt 6:4, lgkmcnt 11:8) waits for LDS only; it is issued through the
-// builtin so that the compiler's own wait insertion knows what has completed.
-constexpr int waitcnt_lgkm0() { return 15 | (3 << 14) | (7 << 4); }
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
-    __builtin_amdgcn_s_barrier();
-}
 
 // ------------------------------------------------------------------ policies
 // A fragment holds, for lane (G = lane / 16, n = lane % 16), the 8 elements
@@ -156,62 +123,28 @@ struct PolicyF {          // fp32 inputs and operands
     }
     __device__ static f32x4 in2op(f32x4 raw) { return raw; }
     __device__ static void f32_to_op4(Op* p, f32x4 x) { *reinterpret_cast<f32x4*>(p) = x; }
+    // one 16-byte vector of inputs (4 values) -> fp32
+    static constexpr int VPR = 4;
+    __device__ static void load16(const In* p, float* x) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(p);
+        for (int e = 0; e < 4; ++e) x[e] = v[e];
+    }
 };
 
-// ------------------------------------------------------------------ units
-struct UnitInfo {
-    int64_t start;   // first token on the flat axis
-    int32_t len;     // tokens
-    int32_t nch;     // chunks
-    int32_t cbase;   // index of the unit's first chunk
+// bf16 inputs with fp32 operands (the backward's preparation): bf16 widens to
+// fp32 exactly
+struct PolicyFB : PolicyF {
+    using In = bf16;
+    static constexpr int VPR = 8;
+    __device__ static float f(In x) { return (float)x; }
+    __device__ static void load16(const In* p, float* x) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+            x[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+        }
+    }
 };
-
-__device__ __forceinline__ UnitInfo unit_info(const UnitMap& um, int u) {
-    UnitInfo r;
-    if (um.dense) {
-        r.start = (int64_t)u * um.T;
-        r.len = um.T;
-        r.nch = um.nt_dense;
-        r.cbase = u * um.nt_dense;
-        return r;
-    }
-    int64_t a = um.offsets[u], b = um.offsets[u + 1];
-    a = a < 0 ? 0 : (a > um.total_tokens ? um.total_tokens : a);
-    b = b < a ? a : (b > um.total_tokens ? um.total_tokens : b);
-    r.start = a;
-    r.len = (int32_t)(b - a);
-    r.nch = (r.len + BT - 1) / BT;
-    int cb = um.chunk_offsets[u];
-    if (cb < 0) cb = 0;
-    if (cb > um.n_chunks) cb = um.n_chunks;
-    if (cb + r.nch > um.n_chunks) r.nch = um.n_chunks - cb;
-    r.cbase = cb;
-    return r;
-}
-
-// the same fields, marked wave-uniform (they depend on the workgroup only) so
-// that values derived from them can live in scalar registers
-__device__ __forceinline__ UnitInfo uniform(UnitInfo r) {
-    const uint64_t s = (uint64_t)r.start;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)s), hi = __builtin_amdgcn_readfirstlane((uint32_t)(s >> 32));
-    r.start = (int64_t)(((uint64_t)hi << 32) | lo);
-    r.len = __builtin_amdgcn_readfirstlane(r.len);
-    r.nch = __builtin_amdgcn_readfirstlane(r.nch);
-    r.cbase = __builtin_amdgcn_readfirstlane(r.cbase);
-    return r;
-}
-
-// (unit, chunk in unit) of a flat chunk index
-__device__ __forceinline__ void chunk_of(const UnitMap& um, int ci, int& u, int& c) {
-    if (um.dense) {
-        u = ci / um.nt_dense;
-        c = ci - u * um.nt_dense;
-    } else {
-        u = um.chunk_indices[2 * ci];
-        c = um.chunk_indices[2 * ci + 1];
-        if (u < 0 || u >= um.n_units) { u = -1; c = 0; }
-    }
-}
 
 // ------------------------------------------------------------------ operand order
 // Order of the 64 x 128 k / q tiles (along keys) and of the 64 x 64 T and P
@@ -254,16 +187,6 @@ constexpr int CF_GL = 128;                                          // fp32 offs
 constexpr int CS_CP = 64, CS_BG = 128;
 __device__ __forceinline__ int lane_order(int t) { return 16 * ((t >> 2) & 3) + 4 * (t >> 4) + (t & 3); }
 
-// raw buffer resource over [base, base + bytes): accesses outside read as zero
-// and writes outside are dropped
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-// Cache policy of the output stores: non-temporal. A forward never reads o
-// back, and o written through the caches would push k, q, v, T and P (which
-// the next forward reads again) out of the last-level cache.
-constexpr int CP_NT = 2;
 
 // ------------------------------------------------------------------ prep
 constexpr int LDL = BT + 1;   // row stride of 64 x 64 fp32 LDS matrices
@@ -312,18 +235,20 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     static_assert(sizeof(Op) == 4, "prep_kernel serves fp32 operands");
 
     // ---- tiles into LDS as operands (rows past the chunk end are zero)
-    constexpr int VPR = 16 / sizeof(In);             // elements per 16-byte vector
+    constexpr int VPR = P::VPR;                      // elements per 16-byte vector
     constexpr int NV = BT * DK / VPR;                // vectors per tile
     for (int idx = tid; idx < NV; idx += 256) {
         const int r = idx / (DK / VPR), cv = (idx % (DK / VPR)) * VPR;
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        f32x4 kv = z, qv = z;
+        float kv[VPR], qv[VPR];
+        for (int e = 0; e < VPR; ++e) { kv[e] = 0.0f; qv[e] = 0.0f; }
         if (r < len) {
-            kv = P::in2op(*reinterpret_cast<const f32x4*>(kin + ((t0 + r) * H + head) * DK + cv));
-            if (has_q) qv = P::in2op(*reinterpret_cast<const f32x4*>(qin + ((t0 + r) * H + head) * DK + cv));
+            P::load16(kin + ((t0 + r) * H + head) * DK + cv, kv);
+            if (has_q) P::load16(qin + ((t0 + r) * H + head) * DK + cv, qv);
         }
-        *reinterpret_cast<f32x4*>(&kt[r * LDQ + cv]) = kv;
-        *reinterpret_cast<f32x4*>(&qt[r * LDQ + cv]) = qv;
+        for (int e = 0; e < VPR; e += 4) {
+            *reinterpret_cast<f32x4*>(&kt[r * LDQ + cv + e]) = f32x4{kv[e], kv[e + 1], kv[e + 2], kv[e + 3]};
+            *reinterpret_cast<f32x4*>(&qt[r * LDQ + cv + e]) = f32x4{qv[e], qv[e + 1], qv[e + 2], qv[e + 3]};
+        }
     }
     if (tid < BT) bet[tid] = tid < len ? P::f(bin[(t0 + tid) * H + head]) : 0.0f;
     if (!PERKEY) {
@@ -363,7 +288,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     // Per key, an off-diagonal tile (I > J) factors the decay about the last
     // row of block J, so that both factors are at most 1 for any g <= 0; a
     // diagonal tile takes the exponent differences directly.
-    auto direct = [&](const In* xi, int i, int j) {          // sum_d x_id k_jd b^{G_id - G_jd}
+    auto direct = [&](const Op* xi, int i, int j) {          // sum_d x_id k_jd b^{G_id - G_jd}
         float s = 0.0f;
         for (int d = 0; d < DK; ++d)
             s += (float)xi[i * LDQ + d] * (float)kt[j * LDQ + d] *
@@ -2021,6 +1946,20 @@ hipError_t launch_prep(const Problem& p, const Workspace& ws, const void* k, con
         if (p.per_key) hipLaunchKernelGGL((prep_kernel<PolicyF, true>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((prep_kernel<PolicyF, false>), grid, block, 0, s, a);
     }
+    return hipGetLastError();
+}
+
+// The fp32-operand preparation (T, P and the gate rows in fp32, natural
+// order) for either input dtype: what the backward reads.
+hipError_t launch_prep_f32(const Problem& p, const Workspace& ws, const void* k, const void* q, const float* g,
+                           const void* beta, hipStream_t s) {
+    if (p.um.n_chunks == 0) return hipSuccess;
+    PrepArgs a;
+    a.um = p.um; a.H = p.H; a.k = k; a.q = q; a.g = g; a.beta = beta; a.use_exp2 = p.use_exp2;
+    a.ws = ws; a.g_cumsum = nullptr; a.A = nullptr;
+    dim3 grid(p.um.n_chunks, p.H), block(256);
+    if (p.dtype == 1) hipLaunchKernelGGL((prep_kernel<PolicyFB, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((prep_kernel<PolicyF, false>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 

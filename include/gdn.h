@@ -219,6 +219,34 @@ gdn_status gdn_state_merge(int32_t B, int32_t H, int32_t n_seg, int32_t K, int32
                            float* S_final, hipStream_t stream);
 
 /*
+ * gdn_chunk_bwd - gradients of the chunked forward (scalar gate): the
+ * backward slots of the native GDN op on the Diff Coverage page
+ * (_AscendCGDN.backward: dq, dk, dv, dbeta and the raw-gate gradient dg), by
+ * the staged chunk backward of the same page (_AscendCKDAStages.backward:
+ * preparation, the reverse state pass chunk_gated_delta_rule_bwd_dhu,
+ * finalisation), for L with dL/do = dout and dL/dh_final = dht.
+ *
+ *   q, k, v, g, beta  device, the forward's inputs (desc as for gdn_chunk_fwd)
+ *   h                 device fp32 [n_chunks][H][K][V]: the state entering every
+ *                     chunk, as gdn_chunk_fwd's h slot returns it for the same
+ *                     descriptor, inputs and initial state
+ *   dout              device [tokens][H][V] in desc->dtype
+ *   dht               device fp32 [units][H][K][V] or NULL (zero)
+ *   dq, dk            device fp32 [tokens][H][K]
+ *   dv                device fp32 [tokens][H][V]
+ *   dg, dbeta         device fp32 [tokens][H]
+ *   dh0               device fp32 [units][H][K][V] (dL/d initial_state) or NULL
+ *   workspace         as for gdn_chunk_fwd (query its size with NULL); about
+ *                     129 KiB per (chunk, head)
+ * A per-key gate returns GDN_ERR_UNSUPPORTED. Gradients are fp32 whatever the
+ * input dtype; every product runs on fp32 operands.
+ */
+gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                         const void* beta, const float* h, const void* dout, const float* dht, float* dq,
+                         float* dk, float* dv, float* dg, float* dbeta, float* dh0, void* workspace,
+                         size_t* workspace_bytes, hipStream_t stream);
+
+/*
  * gdn_chunk_fwd_noalloc - gdn_chunk_fwd for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc). Same arguments, results and errors as gdn_chunk_fwd

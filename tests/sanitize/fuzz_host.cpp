@@ -121,6 +121,24 @@ void fuzz_fwd() {
                             uni(0, 5) ? (float*)FAKE : nullptr, ws, &nb, nullptr));
     stub_set_workspace(nullptr, 0);
     free(ws);
+    // the backward, with its own (larger) workspace
+    size_t bneed = 0;
+    void* p15[15];
+    for (int i = 0; i < 15; ++i) p15[i] = uni(0, 19) ? FAKE : nullptr;
+    s = gdn_chunk_bwd(&d, p15[0], p15[1], p15[2], (const float*)p15[3], p15[4], (const float*)p15[5], p15[6],
+                      (const float*)p15[7], (float*)p15[8], (float*)p15[9], (float*)p15[10], (float*)p15[11],
+                      (float*)p15[12], (float*)p15[13], nullptr, &bneed, nullptr);
+    tally(s);
+    if (s != GDN_OK || bneed > (size_t(128) << 20)) return;
+    const size_t bhave = uni(0, 4) ? bneed : bneed - 256;
+    void* bws = aligned_alloc(256, (bhave + 255) / 256 * 256 + 256);
+    stub_set_workspace(bws, bhave);
+    size_t bnb = bhave;
+    tally(gdn_chunk_bwd(&d, p15[0], p15[1], p15[2], (const float*)p15[3], p15[4], (const float*)p15[5], p15[6],
+                        (const float*)p15[7], (float*)p15[8], (float*)p15[9], (float*)p15[10], (float*)p15[11],
+                        (float*)p15[12], (float*)p15[13], bws, &bnb, nullptr));
+    stub_set_workspace(nullptr, 0);
+    free(bws);
 }
 
 void fuzz_merge() {

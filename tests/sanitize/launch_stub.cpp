@@ -71,4 +71,27 @@ hipError_t launch_merge(int B, int H, int n_seg, const float* S_ext, const float
     return hipSuccess;
 }
 
+hipError_t launch_prep_f32(const Problem& p, const Workspace& ws, const void* k, const void*, const float* g,
+                           const void* beta, hipStream_t) {
+    check_problem(p, ws);
+    if (p.um.total_tokens > 0 && (!k || !g || !beta)) fail("fp32 prep inputs");
+    return hipSuccess;
+}
+
+hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* dVN, const void* q, const void* k,
+                      const void* v, const float* g, const void* beta, const float* h, const void* dout,
+                      const float*, float* dq, float* dk, float* dv, float* dg, float* dbeta, float*, hipStream_t) {
+    gdn::Problem pf = p;
+    pf.dtype = 0;                  // the backward's preparation has fp32 operands
+    check_problem(pf, ws);
+    const int64_t nch = int64_t(p.um.n_chunks) * p.H;
+    region(dH, nch * 128 * 128 * 4, "dH region");
+    region(dVN, nch * 64 * 128 * 4, "dvn region");
+    if (static_cast<const char*>(static_cast<void*>(dVN)) < static_cast<const char*>(static_cast<void*>(dH)) + nch * 128 * 128 * 4)
+        fail("dH and dvn overlap");
+    if (p.um.total_tokens > 0 && (!q || !k || !v || !g || !beta || !h || !dout || !dq || !dk || !dv || !dg || !dbeta))
+        fail("backward pointers");
+    return hipSuccess;
+}
+
 }  // namespace gdn

@@ -21,8 +21,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert names == ["gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_state_merge", "gdn_state_summary",
-                     "gdn_varlen_meta"]
+    assert names == ["gdn_chunk_bwd", "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_state_merge",
+                     "gdn_state_summary", "gdn_varlen_meta"]
     L = gb.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -218,3 +218,32 @@ def test_noalloc_rejects_before_any_hip_call():
     assert noalloc(desc(K=64, V=64)) == gb.GDN_ERR_UNSUPPORTED
     assert noalloc(desc(), q=None) == gb.GDN_ERR_INVALID
     assert noalloc(desc(), flags=3) == gb.GDN_ERR_INVALID
+
+
+# ------------------------------------------------------------------ backward
+def bwd(d, *, ws=FAKE, nbytes=None, ptrs=None):
+    # q, k, v, g, beta, h, dout, dht, dq, dk, dv, dg, dbeta, dh0
+    p = [FAKE] * 14 if ptrs is None else ptrs
+    nb = ctypes.c_size_t(nbytes if nbytes is not None else (1 << 40))
+    return gb.lib().gdn_chunk_bwd(ctypes.byref(d), *p, ws, ctypes.byref(nb), None), nb.value
+
+
+def test_backward_host_checks():
+    st, need = bwd(desc(), ws=None)
+    # fp32 preparation (T, P, gate rows), dL/dh at each chunk exit and dvn,
+    # every region 256-byte aligned
+    nch = 2 * 4 * 3
+    a256 = lambda x: ((x + 255) // 256) * 256
+    prep = 2 * a256(nch * 64 * 64 * 4) + a256(nch * 4 * 64 * 4)
+    assert st == gb.GDN_OK and need == a256(prep + nch * 128 * 128 * 4) + a256(nch * 64 * 128 * 4)
+    assert bwd(desc(gate_kind=1), ws=None)[0] == gb.GDN_ERR_UNSUPPORTED
+    assert bwd(desc(chunk_size=32), ws=None)[0] == gb.GDN_ERR_INVALID
+    assert bwd(desc(), nbytes=need - 1)[0] == gb.GDN_ERR_CAPACITY
+    assert bwd(desc(), ws=FAKE + 128)[0] == gb.GDN_ERR_INVALID
+    for i in range(14):
+        p = [FAKE] * 14
+        p[i] = None
+        want = gb.GDN_OK if i in (7, 13) else gb.GDN_ERR_INVALID    # dht and dh0 may be NULL
+        if want == gb.GDN_OK:
+            continue                                                  # would launch: GPU only
+        assert bwd(desc(), ptrs=p)[0] == want, i

@@ -1,0 +1,167 @@
+"""Parity of the HIP backward (gdn_chunk_bwd, through the C ABI) with the fp64
+backward oracle. Tolerances as for the forward, per gradient: max |x - ref|
+<= tol * rms(ref), tol = 1e-4 (fp32 inputs) or 2e-2 (bf16 inputs); dL/do is
+drawn in fp32 and rounded to the input dtype, and the oracle sees the same
+rounded values."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from chunked_gated_delta_05_amd import binding as gb
+from chunked_gated_delta_05_amd import workloads as W
+from tests.gpu_helpers import TOL, assert_close, flat_inputs, np32, unit_offsets
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+NAMES = ("dq", "dk", "dv", "dg", "dbeta")
+
+
+def small(B=1, T=200, H=3, dtype="bf16", use_exp2=False, gate_coef=0.1, layout="BSND", n_docs=0):
+    return W.Workload("small", B=B, T=T, H=H, dtype=dtype, layout=layout, use_exp2=use_exp2,
+                      gate_coef=gate_coef, n_docs=n_docs)
+
+
+def packed(lens, H, dtype, seed):
+    cu = W.cu_from_lengths(lens)
+    base = W.generate(small(B=1, T=cu[-1], H=H, dtype=dtype), seed)
+    d = {n: base[n][0].contiguous().to(DEV) for n in ("q", "k", "v", "g", "beta")}
+    d.update(scale=base["scale"], offsets=cu,
+             workload=small(B=1, T=cu[-1], H=H, dtype=dtype, layout="TND", n_docs=len(lens)))
+    return d
+
+
+def run_both(d, seed, S0=False, dht=False, heads=None):
+    """GPU forward (entry states) + backward, and the oracle's backward on the
+    same rounded inputs (restricted to `heads` when given)."""
+    w = d["workload"]
+    dev = {n: d[n] if d[n].is_cuda else d[n].to(DEV) for n in ("q", "k", "v", "g", "beta")}
+    meta = gb.make_meta(d["offsets"], w.T, DEV) if w.layout == "TND" else None
+    offs = unit_offsets(d)
+    units = len(offs) - 1
+    gen = torch.Generator().manual_seed(seed)
+    s0 = (torch.randn(units, w.H, 128, 128, generator=gen) * 0.3).to(DEV) if S0 else None
+    dh = (torch.randn(units, w.H, 128, 128, generator=gen) * 0.3).to(DEV) if dht else None
+    do = torch.randn(dev["v"].shape, generator=gen).to(dev["v"].dtype).to(DEV)
+    _, _, ex = gb.gdn_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], d["scale"], meta=meta,
+                                initial_state=s0, use_exp2=w.use_exp2, want_h=True)
+    got = gb.gdn_chunk_bwd(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], ex["h"], do, d["scale"], meta=meta,
+                           dht=dh, use_exp2=w.use_exp2)
+    torch.cuda.synchronize()
+    q, k, v, g, beta = flat_inputs(d)
+    flat = (lambda x: x.reshape(-1, *x.shape[2:])) if w.layout == "BSND" else (lambda x: x)
+    dof = np32(flat(do))
+    sel = slice(None) if heads is None else heads
+    pick = lambda x: np.ascontiguousarray(x[:, sel])
+    ref = oracle.bwd(pick(q), pick(k), pick(v), pick(g), pick(beta), offs, d["scale"], pick(dof),
+                     use_exp2=w.use_exp2, S0=None if s0 is None else np32(s0)[:, sel].astype(np.float64),
+                     dht=None if dh is None else np32(dh)[:, sel].astype(np.float64))
+    out = {n: pick(np32(flat(got[n]))) for n in NAMES}
+    out["dh0"] = np32(got["dh0"])[:, sel]
+    return out, ref
+
+
+def check_all(out, ref, tol, what):
+    errs = {}
+    for n in NAMES + ("dh0",):
+        ref_n = ref["dS0"] if n == "dh0" else ref[n]
+        errs[n] = assert_close(out[n], ref_n, tol, f"{what} {n}")
+    return errs
+
+
+@pytest.mark.parametrize("B,T,H", [(1, 64, 1), (2, 200, 3), (1, 1, 2), (1, 130, 2), (3, 63, 1)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_backward_small(B, T, H, dtype):
+    print(f"backward B={B} T={T} H={H} {dtype}", flush=True)
+    d = W.generate(small(B=B, T=T, H=H, dtype=dtype), 211 + T)
+    out, ref = run_both(d, 5 + T, S0=True, dht=True)
+    check_all(out, ref, TOL[dtype], "small")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_backward_base2_gate(dtype):
+    print(f"backward base-2 gate {dtype}", flush=True)
+    d = W.generate(small(B=2, T=150, H=2, dtype=dtype, use_exp2=True, gate_coef=0.05), 223)
+    out, ref = run_both(d, 7, S0=True, dht=True)
+    check_all(out, ref, TOL[dtype], "base 2")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_backward_packed_documents(dtype):
+    # packed documents with ragged chunks, an entry state and dL/dh_final per document
+    print(f"backward packed {dtype}", flush=True)
+    d = packed([1, 63, 64, 65, 200, 7, 128], 3, dtype, 227)
+    out, ref = run_both(d, 9, S0=True, dht=True)
+    check_all(out, ref, TOL[dtype], "packed")
+
+
+def test_backward_beta_zero_is_exactly_zero():
+    # beta = 0 and no entry state keep h = 0: dq, dk, dv and dg are exactly
+    # zero on the GPU as in the oracle; dbeta matches the oracle
+    print("backward beta = 0", flush=True)
+    d = W.generate(small(B=1, T=150, H=2), 229)
+    d["beta"] = torch.zeros_like(d["beta"])
+    out, ref = run_both(d, 11)
+    for n in ("dq", "dk", "dv", "dg"):
+        assert np.count_nonzero(out[n]) == 0, n
+    assert_close(out["dbeta"], ref["dbeta"], TOL["bf16"], "dbeta")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_backward_total_forgetting(dtype):
+    print(f"backward total forgetting {dtype}", flush=True)
+    d = W.generate(small(B=1, T=140, H=2, dtype=dtype), 233)
+    d["g"] = torch.full_like(d["g"], -1e4)
+    out, ref = run_both(d, 13, dht=True)
+    for n in NAMES:
+        assert np.isfinite(out[n]).all(), n
+    check_all({n: out[n] for n in ("dq", "dk", "dv", "dbeta", "dh0")} | {"dg": ref["dg"]}, ref, TOL[dtype],
+              "total forgetting")
+    assert np.abs(out["dg"]).max() <= 1e-6 * max(1.0, np.abs(out["dq"]).max())
+
+
+def test_backward_tiny_fp32_workload():
+    w = W.WORKLOADS[0]
+    d = W.generate(w, 1000)
+    out, ref = run_both(d, 15, dht=True)
+    errs = check_all(out, ref, TOL["fp32"], w.name)
+    print(f"{w.name} backward: " + ", ".join(f"{n} {e:.1e}" for n, e in errs.items()))
+
+
+def test_backward_dense_bf16_workload_sampled_heads():
+    w = W.WORKLOADS[1]
+    d = W.generate(w, 1001, device=DEV)
+    out, ref = run_both(d, 17, heads=[0, 9])
+    errs = check_all(out, ref, TOL["bf16"], w.name)
+    print(f"{w.name} backward (heads 0, 9): " + ", ".join(f"{n} {e:.1e}" for n, e in errs.items()))
+
+
+def test_autograd_op_matches_the_abi():
+    # GatedDeltaRule: forward output and final state as gdn_chunk_fwd, and its
+    # backward (dL/do and dL/d final) returns gdn_chunk_bwd's gradients
+    d = W.generate(small(B=2, T=130, H=2, dtype="fp32"), 239)
+    x = {n: d[n].to(DEV).requires_grad_(n != "g" or True) for n in ("q", "k", "v", "g", "beta")}
+    s0 = (torch.randn(2, 2, 128, 128) * 0.3).to(DEV).requires_grad_(True)
+    o, fin = gb.GatedDeltaRule.apply(x["q"], x["k"], x["v"], x["g"], x["beta"], s0, d["scale"])
+    do = torch.randn_like(o)
+    (o * do).sum().backward()
+    _, _, ex = gb.gdn_chunk_fwd(*(x[n].detach() for n in ("q", "k", "v", "g", "beta")), d["scale"],
+                                initial_state=s0.detach(), want_h=True)
+    r = gb.gdn_chunk_bwd(*(x[n].detach() for n in ("q", "k", "v", "g", "beta")), ex["h"], do, d["scale"])
+    torch.cuda.synchronize()
+    for n, t in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dg", "g"), ("dbeta", "beta")):
+        assert torch.equal(x[t].grad, r[n]), n
+    assert torch.equal(s0.grad, r["dh0"])
+
+
+def test_backward_is_deterministic():
+    # no float atomics in any reduction: two calls give the same bits
+    d = W.generate(small(B=2, T=300, H=3), 241)
+    x = {n: d[n].to(DEV) for n in ("q", "k", "v", "g", "beta")}
+    _, _, ex = gb.gdn_chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], d["scale"], want_h=True)
+    do = torch.randn(x["v"].shape, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16).to(DEV)
+    r1 = gb.gdn_chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], ex["h"], do, d["scale"])
+    r2 = gb.gdn_chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], ex["h"], do, d["scale"])
+    torch.cuda.synchronize()
+    for n in r1:
+        assert torch.equal(r1[n], r2[n]), n
