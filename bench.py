@@ -216,14 +216,12 @@ def main():
     offsets = list(d["offsets"]) if wl.layout == "TND" else [b * wl.T for b in range(wl.B + 1)]
     chunks = sum((b - a + 63) // 64 for a, b in zip(offsets[:-1], offsets[1:]))
     meta = gb.make_meta(d["offsets"], wl.T, dev) if wl.layout == "TND" else None
+    plan = None
     if split:
         seg = d["seg_offsets"]
         meta = gb.make_meta(gb.segment_offsets(wl.B, wl.T, seg), tokens, dev)
-        n_units = wl.B * wl.n_seg
-        S_ext = torch.empty((n_units, H, 128, 128), dtype=torch.float32, device=dev)
-        M = torch.empty((n_units, H, 128, 128), dtype=torch.float32, device=dev)
-        S_init = torch.empty_like(S_ext)
-        S_fin = torch.empty((wl.B, H, 128, 128), dtype=torch.float32, device=dev)
+        plan = gb.split_plan_rows(q, k, v, g, beta, d["scale"], seg=seg, use_exp2=wl.use_exp2, o_dtype=o_dtype)
+        o = plan.o
     n_units = len(offsets) - 1 if not split else wl.B * wl.n_seg
     fin = torch.empty((n_units, H, 128, 128), dtype=torch.float32, device=dev) if wl.final_state else None
     nb = gb.workspace_bytes(gb._desc(k, H, k.dtype, o_dtype, wl.gate_per_key, wl.use_exp2, d["scale"], meta))
@@ -242,16 +240,11 @@ def main():
             call(0)
             rec(1)
             return
-        # sequence split: summaries from the zero state, their merge, then the
-        # forward of every segment from its true entry state (the correction)
-        gb.gdn_state_summary(k, v, g, beta, meta=meta, mode=0, use_exp2=wl.use_exp2, q=q, workspace=ws,
-                             S_ext=S_ext, M=M)
-        rec(1)
-        gb.gdn_state_merge(S_ext, M, None, B=wl.B, n_seg=wl.n_seg, S_init=S_init, S_final=S_fin)
-        rec(2)
-        gb.gdn_chunk_fwd(q, k, v, g, beta, d["scale"], meta=meta, initial_state=S_init, use_exp2=wl.use_exp2,
-                         o_dtype=o_dtype, flags=gb.FLAG_REUSE_PREPARED, workspace=ws, out=o)
-        rec(3)
+        # sequence split: the summaries that something consumes (none for a
+        # row's last segment, S_ext only for its first), the merge, then the
+        # forward of every segment from its true entry state (the correction),
+        # which also gives the final states
+        plan(q, k, v, g, beta, rec=lambda i: rec(i + 1))
 
     def stages(ev=None):
         # the unsplit forward as its two stages, for the per-kernel events:

@@ -62,7 +62,12 @@ def lib():
                                     ctypes.POINTER(GdnSlots), ctypes.c_int32, vp, sz, vp]
         L.gdn_state_summary.restype = ctypes.c_int
         L.gdn_state_summary.argtypes = [ctypes.POINTER(GdnDesc), vp, vp, vp, vp, vp, ctypes.c_int32,
-                                        vp, vp, vp, sz, vp]
+                                        ctypes.c_int32, vp, ctypes.c_int32, vp, vp, vp, sz, vp]
+        L.gdn_split_meta.restype = ctypes.c_int
+        L.gdn_split_meta.argtypes = [_i32p, ctypes.c_int32, _i32p, ctypes.c_int32, ctypes.c_int32, _i32p,
+                                     _i32p, _i32p, ctypes.c_int32, _i32p]
+        L.gdn_state_merge_pieces.restype = ctypes.c_int
+        L.gdn_state_merge_pieces.argtypes = [ctypes.c_int32] * 5 + [vp, vp, vp, vp, vp, vp]
         L.gdn_state_merge.restype = ctypes.c_int
         L.gdn_state_merge.argtypes = [ctypes.c_int32] * 5 + [vp, vp, vp, vp, vp, vp]
         L.gdn_chunk_bwd.restype = ctypes.c_int
@@ -238,8 +243,8 @@ def workspace_bytes(desc: GdnDesc, fn="fwd") -> int:
         st = lib().gdn_chunk_fwd(ctypes.byref(desc), None, None, None, None, None, None, None, None,
                                  None, 0, None, ctypes.byref(nb), None)
     else:
-        st = lib().gdn_state_summary(ctypes.byref(desc), None, None, None, None, None, 0, None, None,
-                                     None, ctypes.byref(nb), None)
+        st = lib().gdn_state_summary(ctypes.byref(desc), None, None, None, None, None, 0, 0, None, -1,
+                                     None, None, None, ctypes.byref(nb), None)
     check(st, "workspace query")
     return nb.value
 
@@ -354,12 +359,16 @@ class FwdCall:
 
 
 def gdn_state_summary(k, v, g, beta, *, meta: UnitMeta, mode=0, use_exp2=False, q=None,
-                      workspace=None, S_ext=None, M=None):
+                      workspace=None, S_ext=None, M=None, flags=0, units=None):
     """Per-unit summaries (S_ext [units,H,K,V], M [units,H,K,K]; given
     buffers are written in place); pass q to leave a per-key preparation
-    that a reusing forward can use."""
+    that a reusing forward can use. units: None (all) or a device int32
+    tensor of the unit indices to summarise (the other slots are left
+    as they are); flags: 0 or FLAG_REUSE_PREPARED."""
     if mode not in (0, 1, 2):
         raise ValueError("mode must be 0 (both), 1 (S_ext) or 2 (M)")
+    if flags not in (0, FLAG_REUSE_PREPARED):
+        raise ValueError("flags must be 0 or FLAG_REUSE_PREPARED")
     if v is None:
         raise ValueError("v is required")
     H, per_key = _check_inputs(q, k, v, g, beta, meta)
@@ -369,19 +378,29 @@ def gdn_state_summary(k, v, g, beta, *, meta: UnitMeta, mode=0, use_exp2=False, 
     ws = workspace if workspace is not None else torch.empty(nb, dtype=torch.uint8, device=dev)
     if ws.dtype != torch.uint8 or ws.device != dev or ws.numel() < nb:
         raise ValueError(f"workspace must be a uint8 tensor of at least {nb} bytes on {dev}")
-    units = n_units_of(k, meta)
+    if flags and workspace is None:
+        raise ValueError("FLAG_REUSE_PREPARED needs the workspace of the preparing call")
+    n_units = n_units_of(k, meta)
+    n_sel = -1
+    if units is not None:
+        if units.dtype != torch.int32 or units.dim() != 1 or units.device != dev or not units.is_contiguous():
+            raise ValueError(f"units must be a contiguous 1-D int32 tensor on {dev}")
+        n_sel = units.numel()
+        if n_sel > n_units:
+            raise ValueError(f"{n_sel} units selected out of {n_units}")
     K, V = k.shape[-1], v.shape[-1]
     if mode != 2 and S_ext is None:
-        S_ext = torch.empty((units, H, K, V), dtype=torch.float32, device=dev)
+        S_ext = torch.empty((n_units, H, K, V), dtype=torch.float32, device=dev)
     if mode != 1 and M is None:
-        M = torch.empty((units, H, K, K), dtype=torch.float32, device=dev)
+        M = torch.empty((n_units, H, K, K), dtype=torch.float32, device=dev)
     if mode != 2:
-        _check_tensor("S_ext", S_ext, torch.float32, (units, H, K, V), dev)
+        _check_tensor("S_ext", S_ext, torch.float32, (n_units, H, K, V), dev)
     if mode != 1:
-        _check_tensor("M", M, torch.float32, (units, H, K, K), dev)
+        _check_tensor("M", M, torch.float32, (n_units, H, K, K), dev)
     nbytes = ctypes.c_size_t(ws.numel())
     check(lib().gdn_state_summary(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                  int(mode), _ptr(S_ext if mode != 2 else None), _ptr(M if mode != 1 else None),
+                                  int(mode), int(flags), _ptr(units) if n_sel > 0 else None, n_sel,
+                                  _ptr(S_ext if mode != 2 else None), _ptr(M if mode != 1 else None),
                                   _ptr(ws), ctypes.byref(nbytes), _stream(dev)), "gdn_state_summary")
     return (S_ext if mode != 2 else None), (M if mode != 1 else None), ws
 
@@ -486,18 +505,179 @@ class GatedDeltaRule(torch.autograd.Function):
                 r.get("dh0"), None, None, None)
 
 
-def split_forward(q, k, v, g, beta, scale=None, *, seg, use_exp2=False, initial_state=None,
-                  o_dtype=torch.float32):
-    """Sequence split on one GPU: per-segment summaries, their merge, then the
-    correction pass (the forward of every segment from its true entry state,
-    reusing the preparation). seg: in-row segment offsets [0, ..., T].
-    Returns (o, S_final [B,H,K,V], S_init [B*n_seg,H,K,V])."""
+def gdn_split_meta(doc_offsets, seg_offsets):
+    """Pieces of packed documents cut at segment offsets (host): returns
+    (piece_offsets, piece_doc, piece_seg) as lists. Both offset lists follow
+    the _packed_offsets rules and end at the same token count."""
+    docs, segs = [int(x) for x in doc_offsets], [int(x) for x in seg_offsets]
+    if not docs or not segs:
+        raise ValueError("offsets must not be empty")
+    da = (ctypes.c_int32 * len(docs))(*docs)
+    sa = (ctypes.c_int32 * len(segs))(*segs)
+    n = ctypes.c_int32(0)
+    check(lib().gdn_split_meta(da, len(docs), sa, len(segs), docs[-1], None, None, None, 0, ctypes.byref(n)),
+          "gdn_split_meta")
+    po = (ctypes.c_int32 * (n.value + 1))()
+    pd = (ctypes.c_int32 * max(n.value, 1))()
+    ps = (ctypes.c_int32 * max(n.value, 1))()
+    check(lib().gdn_split_meta(da, len(docs), sa, len(segs), docs[-1], po, pd, ps, n.value, ctypes.byref(n)),
+          "gdn_split_meta")
+    return list(po), list(pd)[:n.value], list(ps)[:n.value]
+
+
+def gdn_state_merge_pieces(S_ext, M, piece_doc, *, n_docs: int, S0_docs=None, S_in=None):
+    """Entry states S_in [n_pieces,H,K,V] of the pieces of a split packed
+    sequence. piece_doc: device int32 [n_pieces] (non-decreasing); S_ext /
+    M: summaries over the pieces (M may be None when no continuing piece
+    enters from a nonzero state); S0_docs: [n_docs,H,K,V] or None."""
+    if S_ext is None or S_ext.dim() != 4:
+        raise ValueError("S_ext must be [n_pieces, H, K, V]")
+    n_pieces, H, K, V = S_ext.shape
+    dev = S_ext.device
+    if dev.type != "cuda":
+        raise ValueError(f"summaries must be GPU tensors, got {dev}")
+    _check_tensor("S_ext", S_ext, torch.float32, (n_pieces, H, K, V), dev)
+    if M is not None:
+        _check_tensor("M", M, torch.float32, (n_pieces, H, K, K), dev)
+    _check_tensor("piece_doc", piece_doc, torch.int32, (n_pieces,), dev)
+    if S0_docs is not None:
+        _check_tensor("S0_docs", S0_docs, torch.float32, (n_docs, H, K, V), dev)
+    if S_in is None:
+        S_in = torch.empty_like(S_ext)
+    _check_tensor("S_in", S_in, torch.float32, (n_pieces, H, K, V), dev)
+    if M is None:
+        # legal only if no continuing piece enters from a nonzero state
+        doc = piece_doc.tolist()
+        for p in range(1, n_pieces):
+            if doc[p] == doc[p - 1] and (p >= 2 and doc[p - 2] == doc[p - 1] or S0_docs is not None):
+                raise ValueError("M is needed: a continuing piece enters from a nonzero state")
+        M = S_ext   # never read; any valid device pointer
+    check(lib().gdn_state_merge_pieces(n_pieces, int(n_docs), H, K, V, _ptr(piece_doc), _ptr(S_ext), _ptr(M),
+                                       _ptr(S0_docs), _ptr(S_in), _stream(dev)), "gdn_state_merge_pieces")
+    return S_in
+
+
+class SplitPlan:
+    """A sequence split on one GPU, planned once and run per call: the units
+    are pieces (segments of rows, or pieces of packed documents cut at
+    segment offsets), piece_doc names the row or document of each, and a
+    piece continues the previous one when both share it.
+
+    A call runs (1) the summaries that something consumes, those of the
+    pieces followed by a piece of the same document: the last piece of a
+    document needs none, its exit state comes from the correction
+    (needs_summary on the Diff Coverage page); (2) the piece merge; (3) the
+    correction forward of every piece from its true entry state, reusing the
+    preparation of (1), with the final states of all pieces. Buffers are
+    allocated once; the results of the last call are in o, S_in and the
+    final states (final_of_docs picks each document's).
+
+    ext_only_launch: a piece that starts its document from zero needs only
+    S_ext, not M (half the summary columns); with it set (the default) those
+    pieces are summarised in a launch of their own in mode 1, else every
+    consumed summary is computed in full in one launch (one launch fewer,
+    more work)."""
+
+    def __init__(self, q, k, v, g, beta, scale, *, pieces, piece_doc, use_exp2=False, with_s0=False,
+                 o_dtype=torch.float32, ext_only_launch=True):
+        H, per_key = _check_inputs(q, k, v, g, beta)
+        dev = k.device
+        self.shape = (tuple(k.shape), tuple(v.shape), tuple(g.shape), k.dtype)
+        self.scale, self.use_exp2, self.o_dtype, self.with_s0 = scale, use_exp2, o_dtype, with_s0
+        self.meta = make_meta(pieces, pieces[-1], dev)
+        pdoc = [int(x) for x in piece_doc]
+        n = len(pdoc)
+        if n != len(pieces) - 1 or any(b < a for a, b in zip(pdoc, pdoc[1:])):
+            raise ValueError("piece_doc must give a non-decreasing document per piece")
+        self.n_docs = pdoc[-1] + 1
+        cont = [p for p in range(n - 1) if pdoc[p + 1] == pdoc[p]]
+        starts = {p for p in cont if p == 0 or pdoc[p - 1] != pdoc[p]}
+        ext_only = sorted(starts) if ext_only_launch and not with_s0 else []
+        both = [p for p in cont if p not in ext_only]
+        self.sel = [(1, torch.tensor(ext_only, dtype=torch.int32).to(dev)),
+                    (0, torch.tensor(both, dtype=torch.int32).to(dev))]
+        K, V = k.shape[-1], v.shape[-1]
+        self.S_ext = torch.empty((n, H, K, V), dtype=torch.float32, device=dev)
+        self.M = torch.empty((n, H, K, K), dtype=torch.float32, device=dev) if both else None
+        self.S_in = torch.empty_like(self.S_ext)
+        self.final = torch.empty_like(self.S_ext)
+        self.o = torch.empty(v.shape, dtype=o_dtype, device=dev)
+        self.piece_doc = torch.tensor(pdoc, dtype=torch.int32).to(dev)
+        self.last = torch.tensor([p for p in range(n) if p == n - 1 or pdoc[p + 1] != pdoc[p]],
+                                 dtype=torch.long).to(dev)
+        desc = _desc(k, H, k.dtype, o_dtype, per_key, use_exp2, scale, self.meta)
+        self.ws = torch.empty(workspace_bytes(desc), dtype=torch.uint8, device=dev)
+
+    def __call__(self, q, k, v, g, beta, initial_state=None, rec=None):
+        """rec(i), when given, is called after stage i (0 summaries, 1 merge,
+        2 correction) to let the caller record events between them."""
+        if (tuple(k.shape), tuple(v.shape), tuple(g.shape), k.dtype) != self.shape:
+            raise ValueError("inputs differ from the planned shapes")
+        if (initial_state is not None) != self.with_s0:
+            raise ValueError("the plan was made " + ("with" if self.with_s0 else "without") + " entry states")
+        flags = 0
+        for mode, units in self.sel:
+            if units.numel() == 0 and flags:
+                continue
+            gdn_state_summary(k, v, g, beta, meta=self.meta, mode=mode, use_exp2=self.use_exp2, q=q,
+                              workspace=self.ws, S_ext=self.S_ext, M=self.M if mode == 0 else None,
+                              flags=flags, units=units)
+            flags = FLAG_REUSE_PREPARED
+        if rec:
+            rec(0)
+        # without a map buffer no continuing piece enters from a nonzero
+        # state (the plan asked for none), so the merge reads no map: S_ext
+        # (the same shape, as K = V) stands in for the pointer
+        gdn_state_merge_pieces(self.S_ext, self.M if self.M is not None else self.S_ext, self.piece_doc,
+                               n_docs=self.n_docs, S0_docs=initial_state, S_in=self.S_in)
+        if rec:
+            rec(1)
+        gdn_chunk_fwd(q, k, v, g, beta, self.scale, meta=self.meta, initial_state=self.S_in,
+                      use_exp2=self.use_exp2, o_dtype=self.o_dtype, flags=FLAG_REUSE_PREPARED,
+                      workspace=self.ws, out=self.o, final_out=self.final)
+        if rec:
+            rec(2)
+        return self.o
+
+    def final_of_docs(self):
+        return self.final.index_select(0, self.last)
+
+
+def split_forward_packed(q, k, v, g, beta, scale=None, *, doc_offsets, seg_offsets, use_exp2=False,
+                         initial_state=None, o_dtype=torch.float32, ext_only_launch=True):
+    """Packed documents (TND, q/k/v [T,H,K]) split into segments on one GPU
+    (SplitPlan over the pieces of gdn_split_meta). initial_state:
+    [n_docs,H,K,V] or None. Returns (o, final state of every document
+    [n_docs,H,K,V], S_in [n_pieces,H,K,V])."""
+    if k.dim() != 3:
+        raise ValueError("packed input must be [T, H, K]")
+    pieces, pdoc, _ = gdn_split_meta(doc_offsets, seg_offsets)
+    plan = SplitPlan(q, k, v, g, beta, scale, pieces=pieces, piece_doc=pdoc, use_exp2=use_exp2,
+                     with_s0=initial_state is not None, o_dtype=o_dtype, ext_only_launch=ext_only_launch)
+    o = plan(q, k, v, g, beta, initial_state)
+    return o, plan.final_of_docs(), plan.S_in
+
+
+def split_plan_rows(q, k, v, g, beta, scale=None, *, seg, use_exp2=False, with_s0=False,
+                    o_dtype=torch.float32, ext_only_launch=True):
+    """SplitPlan of BSND rows, each cut at the in-row offsets seg."""
     B, T = k.shape[0], k.shape[1]
     n_seg = len(seg) - 1
-    meta = make_meta(segment_offsets(B, T, seg), B * T, k.device)
-    S_ext, M, ws = gdn_state_summary(k, v, g, beta, meta=meta, mode=0, use_exp2=use_exp2, q=q)
-    S_init, S_final = gdn_state_merge(S_ext, M, initial_state, B=B, n_seg=n_seg)
-    o, _, _ = gdn_chunk_fwd(q, k, v, g, beta, scale, meta=meta, initial_state=S_init,
-                            use_exp2=use_exp2, o_dtype=o_dtype, flags=FLAG_REUSE_PREPARED,
-                            workspace=ws)
-    return o, S_final, S_init
+    return SplitPlan(q, k, v, g, beta, scale, pieces=segment_offsets(B, T, seg),
+                     piece_doc=[b for b in range(B) for _ in range(n_seg)], use_exp2=use_exp2,
+                     with_s0=with_s0, o_dtype=o_dtype, ext_only_launch=ext_only_launch)
+
+
+def split_forward(q, k, v, g, beta, scale=None, *, seg, use_exp2=False, initial_state=None,
+                  o_dtype=torch.float32, ext_only_launch=True):
+    """Sequence split of BSND rows on one GPU: the summaries that something
+    consumes, their merge, then the correction pass (the forward of every
+    segment from its true entry state, reusing the preparation). seg: in-row
+    segment offsets [0, ..., T]. Returns (o, S_final [B,H,K,V], S_init
+    [B*n_seg,H,K,V])."""
+    plan = split_plan_rows(q, k, v, g, beta, scale, seg=seg, use_exp2=use_exp2,
+                           with_s0=initial_state is not None, o_dtype=o_dtype, ext_only_launch=ext_only_launch)
+    o = plan(q, k, v, g, beta, initial_state)
+    return o, plan.final_of_docs(), plan.S_in
+
+

@@ -229,19 +229,23 @@ extern "C" gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const v
     }
     if (!prep_only) {
         if (gdn::launch_state(p, ws, q, k, v, beta, initial_state, o, final_state, hs, 0, 0, 0, nullptr,
-                              nullptr, stream) != hipSuccess)
+                              nullptr, nullptr, 0, stream) != hipSuccess)
             return GDN_ERR_DEVICE;
     }
     return GDN_OK;
 }
 
 extern "C" gdn_status gdn_state_summary(const gdn_desc* desc, const void* q, const void* k, const void* v,
-                                        const float* g, const void* beta, int32_t mode, float* S_ext, float* M,
+                                        const float* g, const void* beta, int32_t mode, int32_t flags,
+                                        const int32_t* units_dev, int32_t n_sel, float* S_ext, float* M,
                                         void* workspace, size_t* workspace_bytes, hipStream_t stream) {
     gdn::Problem p;
     gdn_status st = validate(desc, &p);
     if (st != GDN_OK) return st;
     if (mode < 0 || mode > 2) return GDN_ERR_INVALID;
+    if (flags & ~GDN_FLAG_REUSE_PREPARED) return GDN_ERR_INVALID;
+    const bool all = n_sel < 0;
+    if (n_sel > p.um.n_units || (n_sel > 0 && !units_dev)) return GDN_ERR_INVALID;
     const bool want_ext = mode != 2, want_M = mode != 1;
     gdn::Workspace ws;
     bool query = false;
@@ -250,10 +254,53 @@ extern "C" gdn_status gdn_state_summary(const gdn_desc* desc, const void* q, con
     if ((want_ext && !S_ext) || (want_M && !M)) return GDN_ERR_INVALID;
     const bool tokens = p.um.total_tokens > 0;
     if (tokens && (!k || !v || !g || !beta)) return GDN_ERR_INVALID;
-    if (gdn::launch_prep(p, ws, k, q, g, beta, nullptr, nullptr, stream) != hipSuccess)
+    if (!(flags & GDN_FLAG_REUSE_PREPARED) &&
+        gdn::launch_prep(p, ws, k, q, g, beta, nullptr, nullptr, stream) != hipSuccess)
         return GDN_ERR_DEVICE;
+    if (n_sel == 0) return GDN_OK;
     if (gdn::launch_state(p, ws, nullptr, k, v, beta, nullptr, nullptr, nullptr, nullptr, 1, want_ext,
-                          want_M, S_ext, M, stream) != hipSuccess)
+                          want_M, S_ext, M, all ? nullptr : units_dev, n_sel, stream) != hipSuccess)
+        return GDN_ERR_DEVICE;
+    return GDN_OK;
+}
+
+extern "C" gdn_status gdn_split_meta(const int32_t* doc_offsets, int32_t n_doc_offsets, const int32_t* seg_offsets,
+                                     int32_t n_seg_offsets, int32_t total_tokens, int32_t* piece_offsets,
+                                     int32_t* piece_doc, int32_t* piece_seg, int32_t cap_pieces,
+                                     int32_t* n_pieces_out) {
+    if (total_tokens < 1) return GDN_ERR_INVALID;
+    if (!offsets_ok(doc_offsets, n_doc_offsets, total_tokens)) return GDN_ERR_INVALID;
+    if (!offsets_ok(seg_offsets, n_seg_offsets, total_tokens)) return GDN_ERR_INVALID;
+    // the pieces are the gaps of the merged, de-duplicated cut lists
+    int32_t i = 1, j = 1, n = 0, d = 0, sgi = 0, start = 0;
+    while (i < n_doc_offsets || j < n_seg_offsets) {
+        const int32_t a = i < n_doc_offsets ? doc_offsets[i] : INT32_MAX;
+        const int32_t b = j < n_seg_offsets ? seg_offsets[j] : INT32_MAX;
+        const int32_t end = a < b ? a : b;
+        if (piece_offsets && n < cap_pieces) {
+            piece_offsets[n] = start;
+            piece_offsets[n + 1] = end;
+            if (piece_doc) piece_doc[n] = d;
+            if (piece_seg) piece_seg[n] = sgi;
+        }
+        ++n;
+        if (a == end) { ++i; ++d; }
+        if (b == end) { ++j; ++sgi; }
+        start = end;
+    }
+    if (n_pieces_out) *n_pieces_out = n;
+    if (piece_offsets && cap_pieces < n) return GDN_ERR_CAPACITY;
+    return GDN_OK;
+}
+
+extern "C" gdn_status gdn_state_merge_pieces(int32_t n_pieces, int32_t n_docs, int32_t H, int32_t K, int32_t V,
+                                             const int32_t* piece_doc_dev, const float* S_ext, const float* M,
+                                             const float* S0_docs, float* S_in, hipStream_t stream) {
+    if (K != DK || V != DV) return GDN_ERR_UNSUPPORTED;
+    if (n_pieces < 0 || n_docs < 1 || H < 1 || n_docs > (1 << 26) || H > 65535) return GDN_ERR_INVALID;
+    if (int64_t(n_pieces) * H * DK * DK > kMaxElems) return GDN_ERR_INVALID;
+    if (n_pieces > 0 && (!piece_doc_dev || !S_ext || !M || !S_in)) return GDN_ERR_INVALID;
+    if (gdn::launch_merge_pieces(n_pieces, n_docs, H, piece_doc_dev, S_ext, M, S0_docs, S_in, stream) != hipSuccess)
         return GDN_ERR_DEVICE;
     return GDN_OK;
 }

@@ -69,11 +69,15 @@ hipError_t launch_prep(const Problem& p, const Workspace& ws, const void* k, con
                        const float* g, const void* beta, float* g_cumsum_slot, float* A_slot,
                        hipStream_t s);
 
-// mode: 0 forward; 1 summary (S_ext and/or M)
+// mode: 0 forward; 1 summary (S_ext and/or M), of the units in units_sel
+// (device, n_sel entries) when given, else of all
 hipError_t launch_state(const Problem& p, const Workspace& ws, const void* q, const void* k,
                         const void* v, const void* beta, const float* h0, void* o,
                         float* hfinal, float* hslot, int summary, int want_ext, int want_M,
-                        float* S_ext, float* M, hipStream_t s);
+                        float* S_ext, float* M, const int32_t* units_sel, int n_sel, hipStream_t s);
+
+hipError_t launch_merge_pieces(int n_pieces, int n_docs, int H, const int32_t* piece_doc, const float* S_ext,
+                               const float* M, const float* S0, float* S_in, hipStream_t s);
 
 hipError_t launch_merge(int B, int H, int n_seg, const float* S_ext, const float* M,
                         const float* S0, float* S_init, float* S_final, hipStream_t s);

@@ -1901,6 +1901,90 @@ __global__ __launch_bounds__(256) void merge_kernel(int H, int n_seg, const floa
         }
 }
 
+// Pieces of a sequence split over packed documents, in token order: piece p
+// enters with its document's initial state (zero when S0 is NULL) when it
+// starts the document, else with the exit state of piece p - 1,
+// M_{p-1} S_in[p-1] + S_ext[p-1]. Documents are independent: one workgroup
+// per (8 state columns, head, document) walks that document's pieces, found
+// by binary search in the non-decreasing piece_doc. While the entry state is
+// known to be zero (the document's first piece without S0) the map is not
+// read, so its summary may be skipped; the next map and S_ext are in flight
+// during the current product.
+__global__ __launch_bounds__(256) void merge_pieces_kernel(int H, int n_pieces, const int32_t* piece_doc,
+                                                            const float* S_ext, const float* M, const float* S0,
+                                                            float* S_in) {
+    __shared__ __attribute__((aligned(16))) float Ms[DK * MLD];
+    __shared__ float Sc[DK * MC];
+    const int tid = threadIdx.x, c = tid % MC, rbase = tid / MC;   // rows rbase + 32 i
+    const int col0 = (blockIdx.x % (DV / MC)) * MC, doc = blockIdx.x / (DV / MC), head = blockIdx.y;
+    auto lower = [&](int d) {   // first piece whose document is >= d
+        int lo = 0, hi = n_pieces;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (__builtin_amdgcn_readfirstlane(piece_doc[mid]) < d) lo = mid + 1;
+            else hi = mid;
+        }
+        return lo;
+    };
+    const int p0 = lower(doc), p1 = lower(doc + 1);
+    if (p0 >= p1) return;
+    for (int i = 0; i < 4; ++i) {
+        const int r = rbase + 32 * i;
+        Sc[r * MC + c] = S0 ? S0[(((int64_t)doc * H + head) * DK + r) * DV + col0 + c] : 0.0f;
+    }
+    f32x4 mr[16];
+    float er[4];
+    auto load = [&](int p, bool with_map) {   // summary of piece p
+        const int64_t ph = (int64_t)p * H + head;
+        if (with_map) {
+            const f32x4* src = reinterpret_cast<const f32x4*>(M + ph * DK * DK);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) mr[j] = src[tid + 256 * j];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) er[i] = S_ext[(ph * DK + rbase + 32 * i) * DV + col0 + c];
+    };
+    // the first piece's map is read only when the document has an entry state
+    const bool map0 = S0 != nullptr;
+    if (p0 + 1 < p1) load(p0, map0);
+    for (int p = p0; p < p1; ++p) {
+        __syncthreads();                          // the previous product has read Ms and written Sc
+        for (int i = 0; i < 4; ++i) {
+            const int r = rbase + 32 * i;
+            S_in[(((int64_t)p * H + head) * DK + r) * DV + col0 + c] = Sc[r * MC + c];
+        }
+        if (p + 1 >= p1) break;
+        const bool with_map = p > p0 || map0;
+        if (with_map) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int e = 4 * (tid + 256 * j);
+                *reinterpret_cast<f32x4*>(&Ms[(e / DK) * MLD + e % DK]) = mr[j];
+            }
+        }
+        float acc[4];
+        for (int i = 0; i < 4; ++i) acc[i] = er[i];
+        if (p + 2 < p1) load(p + 1, true);
+        __syncthreads();
+        if (with_map)
+            for (int m = 0; m < DK; ++m) {
+                const float sv = Sc[m * MC + c];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] += Ms[(rbase + 32 * i) * MLD + m] * sv;
+            }
+        __syncthreads();
+        for (int i = 0; i < 4; ++i) Sc[(rbase + 32 * i) * MC + c] = acc[i];
+    }
+}
+
+hipError_t launch_merge_pieces(int n_pieces, int n_docs, int H, const int32_t* piece_doc, const float* S_ext,
+                               const float* M, const float* S0, float* S_in, hipStream_t s) {
+    if (n_pieces == 0 || H == 0) return hipSuccess;
+    dim3 grid((DV / MC) * n_docs, H);
+    hipLaunchKernelGGL(merge_pieces_kernel, grid, dim3(256), 0, s, H, n_pieces, piece_doc, S_ext, M, S0, S_in);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ unit order
 // Units of unequal length (packed documents, ragged segments) run their state
 // passes longest first: workgroups are dispatched in grid order, so a long
@@ -1999,7 +2083,7 @@ static void launch_state_h(bool summary, StateArgs a, int want_ext, int want_M, 
 hipError_t launch_state(const Problem& p, const Workspace& ws, const void* q, const void* k,
                         const void* v, const void* beta, const float* h0, void* o, float* hfinal,
                         float* hslot, int summary, int want_ext, int want_M, float* S_ext,
-                        float* M, hipStream_t s) {
+                        float* M, const int32_t* units_sel, int n_sel, hipStream_t s) {
     StateArgs a;
     a.um = p.um; a.H = p.H; a.q = q; a.k = k; a.v = v; a.beta = beta; a.ws = ws;
     a.h0 = h0; a.o = o; a.o_bf16 = p.o_dtype == 1; a.hfinal = hfinal; a.hslot = hslot;
@@ -2008,7 +2092,11 @@ hipError_t launch_state(const Problem& p, const Workspace& ws, const void* q, co
     a.S_ext = S_ext; a.M = M;
     a.ntiles = 0; a.tile0 = 0;
     a.order = nullptr;
-    if (ws.order && a.n_pairs > 0) {
+    if (units_sel) {
+        // only the selected units, in the caller's order
+        a.order = units_sel;
+        a.n_pairs = n_sel * p.H;
+    } else if (ws.order && a.n_pairs > 0) {
         hipLaunchKernelGGL(unit_order_kernel, dim3(1), dim3(ORD_T), 0, s, p.um, ws.order);
         a.order = ws.order;
     }

@@ -192,15 +192,78 @@ gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, con
  *          the chunk preparation that a later reusing forward needs includes
  *          the decayed q.k products (and, with a per-key gate, q * b^G),
  *          which are only prepared when q is given.
- * Units are those of desc (normally the segments of a sequence split). The
- * chunk preparation is left in the workspace, so a following gdn_chunk_fwd
- * with the same descriptor, inputs and workspace may pass
- * GDN_FLAG_REUSE_PREPARED (the correction pass of a split scan), provided
- * q was given here.
+ *   flags  0, or GDN_FLAG_REUSE_PREPARED: the workspace already holds the
+ *          chunk preparation of this descriptor and these inputs
+ *   units_dev, n_sel
+ *          n_sel < 0: summarise every unit (units_dev is ignored). Else
+ *          units_dev is a device int32 list of n_sel <= n_units unit indices
+ *          to summarise (it may be NULL when n_sel = 0, which runs only the
+ *          preparation): a summary that nothing consumes (the last
+ *          segment's, a piece that ends its document) need not be computed,
+ *          as needs_summary on the Diff Coverage page advises. The
+ *          results of unit u still land in slot u of S_ext / M; the slots of
+ *          unlisted units are left untouched. Indices outside [0, n_units)
+ *          are skipped by the kernel.
+ * Units are those of desc (normally the segments of a sequence split, or
+ * the pieces from gdn_split_meta). The chunk preparation is left in the
+ * workspace, so a following gdn_chunk_fwd with the same descriptor, inputs
+ * and workspace may pass GDN_FLAG_REUSE_PREPARED (the correction pass of a
+ * split scan), provided q was given here.
  */
 gdn_status gdn_state_summary(const gdn_desc* desc, const void* q, const void* k, const void* v,
-                             const float* g, const void* beta, int32_t mode, float* S_ext, float* M,
+                             const float* g, const void* beta, int32_t mode, int32_t flags,
+                             const int32_t* units_dev, int32_t n_sel, float* S_ext, float* M,
                              void* workspace, size_t* workspace_bytes, hipStream_t stream);
+
+/*
+ * gdn_split_meta - pieces of packed documents cut into segments (host only;
+ * the packed context-parallel plan of the Diff Coverage page, whose ranks
+ * hold a head window, whole documents and a tail window). The pieces are the
+ * token ranges between consecutive cuts of the union of both offset lists;
+ * a piece continues the previous one exactly when both lie in one document.
+ *   doc_offsets    host [n_doc_offsets]: cu_seqlens of the documents
+ *   seg_offsets    host [n_seg_offsets]: segment cuts (e.g. equal shares)
+ *                  both follow the _packed_offsets rules, ending at
+ *                  total_tokens
+ *   piece_offsets  host [cap_pieces + 1] or NULL (count only)
+ *   piece_doc      host [cap_pieces] or NULL: document of each piece
+ *   piece_seg      host [cap_pieces] or NULL: segment of each piece
+ *   n_pieces_out   receives the piece count (also on GDN_ERR_CAPACITY)
+ * GDN_ERR_INVALID for bad offsets, GDN_ERR_CAPACITY when piece_offsets is
+ * given and cap_pieces is too small.
+ */
+gdn_status gdn_split_meta(const int32_t* doc_offsets, int32_t n_doc_offsets, const int32_t* seg_offsets,
+                          int32_t n_seg_offsets, int32_t total_tokens, int32_t* piece_offsets,
+                          int32_t* piece_doc, int32_t* piece_seg, int32_t cap_pieces,
+                          int32_t* n_pieces_out);
+
+/*
+ * gdn_state_merge_pieces - entry states of the pieces of a split packed
+ * sequence (first_state / last_state of the Diff Coverage page's
+ * PackedSequenceInfo, in one ordered pass), in fp32:
+ *   S_in[p] = S0_docs[doc(p)] (zero when S0_docs == NULL)  if p starts its document
+ *   S_in[p] = M[p-1] S_in[p-1] + S_ext[p-1]                 otherwise
+ *   piece_doc_dev  device int32 [n_pieces], non-decreasing document indices
+ *                  (gdn_split_meta's piece_doc, copied to the device)
+ *   S_ext, M       device fp32 [n_pieces][H][K][V] / [n_pieces][H][K][K]:
+ *                  gdn_state_summary over the pieces. Only the slots of pieces
+ *                  followed by a piece of the same document are read, and M
+ *                  not even there when the piece enters from zero (it starts
+ *                  its document and S0_docs is NULL): such pieces need only
+ *                  S_ext (summary mode 1)
+ *   S0_docs        device fp32 [n_docs][H][K][V] or NULL
+ *   S_in           device fp32 [n_pieces][H][K][V]
+ * A following gdn_chunk_fwd over the pieces with initial_state = S_in gives
+ * the unsplit output, and each document's final state is the final state of
+ * its last piece. Documents are merged independently (one workgroup per
+ * document, head and 8 state columns); a piece whose document index lies
+ * outside [0, n_docs) gets no S_in written, and a piece_doc that is not
+ * non-decreasing gives wrong states, never out-of-range accesses.
+ * n_docs <= 2^26, H <= 65535.
+ */
+gdn_status gdn_state_merge_pieces(int32_t n_pieces, int32_t n_docs, int32_t H, int32_t K, int32_t V,
+                                  const int32_t* piece_doc_dev, const float* S_ext, const float* M,
+                                  const float* S0_docs, float* S_in, hipStream_t stream);
 
 /*
  * gdn_state_merge - composes segment summaries in order (apply_kda_state_summary

@@ -148,6 +148,28 @@ def merge(S_ext, M, S0=None):
     return out
 
 
+def merge_pieces(S_ext, M, piece_doc, S0_docs=None):
+    """Entry state of every piece of a split packed sequence, in fp64.
+
+    S_ext: [n_pieces, n, K, V]; M: [n_pieces, n, K, K]; piece_doc: document of
+    each piece (non-decreasing); S0_docs: [n_docs, n, K, V] or None.
+    Follows first_state / last_state of PackedSequenceInfo on the Diff
+    Coverage page: a piece that starts its document enters with that
+    document's initial state (zero without one); a piece that continues its
+    document enters with the previous piece's exit state, M S_in + S_ext, the
+    affine summary rule of the state_summary.py page."""
+    ext = np.asarray(S_ext, dtype=np.float64)
+    m = np.asarray(M, dtype=np.float64)
+    n_pieces, n, K, V = ext.shape
+    out = np.zeros((n_pieces, n, K, V))
+    for p in range(n_pieces):
+        if p > 0 and piece_doc[p] == piece_doc[p - 1]:
+            out[p] = m[p - 1] @ out[p - 1] + ext[p - 1]
+        elif S0_docs is not None:
+            out[p] = np.asarray(S0_docs, dtype=np.float64)[piece_doc[p]]
+    return out
+
+
 def bwd(q, k, v, g, beta, offsets, scale, dout, *, gate_per_key=False, use_exp2=False, S0=None,
         dht=None, threads=0):
     """Backward of ``fwd`` in fp64 (reverse mode of the token recurrence).

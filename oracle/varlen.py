@@ -42,3 +42,26 @@ def chunk_offsets(offsets, chunk_size: int = 64) -> list[int]:
     for start, end in zip(offsets, offsets[1:]):
         out.append(out[-1] + (end - start + chunk_size - 1) // chunk_size)
     return out
+
+
+def split_pieces(doc_offsets, seg_offsets):
+    """Pieces of packed documents cut into segments.
+
+    The packed context-parallel plan on the Diff Coverage page gives every
+    rank's share of the token axis a head window (the end of a document begun
+    on an earlier rank), whole documents, and a tail window (the start of a
+    document that goes on to a later rank). Over the whole axis this is the
+    list of token ranges between consecutive cuts, where the cuts are all
+    document boundaries and all segment boundaries. Returns
+    ``(piece_offsets, piece_doc, piece_seg)``; a piece continues its
+    predecessor exactly when both have the same document."""
+    total = doc_offsets[-1]
+    if not valid_offsets(doc_offsets, total) or not valid_offsets(seg_offsets, total):
+        raise ValueError("bad offsets")
+    cuts = sorted(set(doc_offsets) | set(seg_offsets))
+    docs, segs = [], []
+    for start in cuts[:-1]:
+        # the document / segment holding the piece's first token
+        docs.append(max(i for i, o in enumerate(doc_offsets[:-1]) if o <= start))
+        segs.append(max(i for i, o in enumerate(seg_offsets[:-1]) if o <= start))
+    return cuts, docs, segs

@@ -1,5 +1,6 @@
-// Host-side fuzz of libgdn's C ABI (gdn_varlen_meta, gdn_chunk_fwd,
-// gdn_state_summary, gdn_state_merge) under AddressSanitizer and
+// Host-side fuzz of libgdn's C ABI (gdn_varlen_meta, gdn_split_meta,
+// gdn_chunk_fwd, gdn_state_summary, gdn_state_merge, gdn_state_merge_pieces,
+// gdn_chunk_bwd) under AddressSanitizer and
 // UndefinedBehaviorSanitizer: random descriptors, unit offsets (valid and
 // broken), flags, modes, capacities and workspace sizes. Input pointers are
 // fake non-null addresses that nothing may dereference; output arrays of the
@@ -117,7 +118,9 @@ void fuzz_fwd() {
                         uni(0, 9) ? ws : static_cast<char*>(ws) + 64, &nb, nullptr));
     nb = have;
     const int mode = pick({0, 1, 2, 3});
-    tally(gdn_state_summary(&d, q, FAKE, FAKE, (const float*)FAKE, FAKE, mode, (float*)FAKE,
+    const int n_sel = pick({-1, -1, 0, 1, 3, 40});
+    tally(gdn_state_summary(&d, q, FAKE, FAKE, (const float*)FAKE, FAKE, mode, pick({0, 0, 1, 2}),
+                            uni(0, 5) ? static_cast<const int32_t*>(FAKE) : nullptr, n_sel, (float*)FAKE,
                             uni(0, 5) ? (float*)FAKE : nullptr, ws, &nb, nullptr));
     stub_set_workspace(nullptr, 0);
     free(ws);
@@ -141,7 +144,31 @@ void fuzz_fwd() {
     free(bws);
 }
 
+// pieces of random documents cut by random segments; the pieces written must
+// tile the token range, and a too-small capacity must write nothing past it
+void fuzz_split_meta() {
+    const int total = uni(1, 3000);
+    std::vector<int32_t> docs = offsets(total, uni(1, 20)), segs = offsets(total, uni(1, 9));
+    int32_t n = -1;
+    const gdn_status s0 = gdn_split_meta(docs.data(), (int32_t)docs.size(), segs.data(), (int32_t)segs.size(), total,
+                                         nullptr, nullptr, nullptr, 0, &n);
+    tally(s0);
+    if (s0 != GDN_OK) return;
+    const int cap = uni(0, 2) ? n : uni(0, n);
+    std::vector<int32_t> po((size_t)cap + 1), pd((size_t)std::max(cap, 1)), ps((size_t)std::max(cap, 1));
+    const gdn_status s1 = gdn_split_meta(docs.data(), (int32_t)docs.size(), segs.data(), (int32_t)segs.size(), total,
+                                         po.data(), pd.data(), ps.data(), cap, &n);
+    tally(s1);
+    if (s1 != GDN_OK) return;
+    if (po[0] != 0 || po[n] != total) exit(4);
+    for (int i = 0; i < n; ++i)
+        if (po[i] >= po[i + 1] || (i && (pd[i] < pd[i - 1] || ps[i] < ps[i - 1]))) exit(4);
+}
+
 void fuzz_merge() {
+    tally(gdn_state_merge_pieces(pick({0, 1, 9, -1}), pick({1, 3, 0}), pick({1, 8, 0}), pick({128, 64}), 128,
+                                 static_cast<const int32_t*>(uni(0, 5) ? FAKE : nullptr), (const float*)FAKE,
+                                 (const float*)FAKE, nullptr, (float*)FAKE, nullptr));
     tally(gdn_state_merge(pick({1, 2, 0}), pick({1, 8, 0}), pick({0, 1, 8, -1}), pick({128, 64}), 128,
                           (const float*)FAKE, uni(0, 5) ? (const float*)FAKE : nullptr, nullptr, (float*)FAKE,
                           nullptr, nullptr));
@@ -153,6 +180,7 @@ int main() {
         fuzz_meta();
         fuzz_fwd();
         fuzz_merge();
+        fuzz_split_meta();
     }
     printf("statuses: ok %ld invalid %ld unsupported %ld device %ld capacity %ld\n", counts[0], counts[1],
            counts[2], counts[3], counts[4]);

@@ -57,10 +57,18 @@ hipError_t launch_prep(const Problem& p, const Workspace& ws, const void* k, con
 
 hipError_t launch_state(const Problem& p, const Workspace& ws, const void*, const void* k, const void*,
                         const void*, const float*, void*, float*, float*, int summary, int want_ext, int want_M,
-                        float* S_ext, float* M, hipStream_t) {
+                        float* S_ext, float* M, const int32_t* units_sel, int n_sel, hipStream_t) {
     check_problem(p, ws);
     if (p.um.total_tokens > 0 && !k) fail("state inputs");
     if (summary && ((want_ext && !S_ext) || (want_M && !M))) fail("summary outputs");
+    if (units_sel && (!summary || n_sel < 1 || n_sel > p.um.n_units)) fail("unit selection");
+    return hipSuccess;
+}
+
+hipError_t launch_merge_pieces(int n_pieces, int n_docs, int H, const int32_t* piece_doc, const float* S_ext,
+                               const float* M, const float*, float* S_in, hipStream_t) {
+    if (n_pieces < 0 || n_docs < 1 || H < 1) fail("piece merge sizes");
+    if (n_pieces > 0 && (!piece_doc || !S_ext || !M || !S_in)) fail("piece merge buffers");
     return hipSuccess;
 }
 

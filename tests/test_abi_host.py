@@ -21,8 +21,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert names == ["gdn_chunk_bwd", "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_state_merge",
-                     "gdn_state_summary", "gdn_varlen_meta"]
+    assert names == ["gdn_chunk_bwd", "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_split_meta",
+                     "gdn_state_merge", "gdn_state_merge_pieces", "gdn_state_summary", "gdn_varlen_meta"]
     L = gb.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -179,18 +179,72 @@ def test_summary_and_merge_errors():
     L = gb.lib()
     nb = ctypes.c_size_t(1 << 40)
     d, arr = _with_offsets([0, 100, 200, 300, 400])   # two segments per row
+    def summ(mode=0, flags=0, units=None, n_sel=-1, ext=FAKE, m=FAKE):
+        return L.gdn_state_summary(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, mode, flags, units, n_sel,
+                                   ext, m, FAKE, ctypes.byref(nb), None)
     for mode in (-1, 3):
-        assert L.gdn_state_summary(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, mode, FAKE, FAKE, FAKE,
-                                   ctypes.byref(nb), None) == gb.GDN_ERR_INVALID
+        assert summ(mode=mode) == gb.GDN_ERR_INVALID
     # mode 1 needs S_ext, mode 2 needs M
-    assert L.gdn_state_summary(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, 1, None, FAKE, FAKE,
-                               ctypes.byref(nb), None) == gb.GDN_ERR_INVALID
-    assert L.gdn_state_summary(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, 2, FAKE, None, FAKE,
-                               ctypes.byref(nb), None) == gb.GDN_ERR_INVALID
+    assert summ(mode=1, ext=None) == gb.GDN_ERR_INVALID
+    assert summ(mode=2, m=None) == gb.GDN_ERR_INVALID
+    # flags other than REUSE_PREPARED; more units selected than exist; a
+    # selection without its list
+    for fl in (2, 3, 8):
+        assert summ(flags=fl) == gb.GDN_ERR_INVALID
+    assert summ(units=FAKE, n_sel=5) == gb.GDN_ERR_INVALID     # 4 units
+    assert summ(units=None, n_sel=2) == gb.GDN_ERR_INVALID
     assert L.gdn_state_merge(2, 3, 4, 64, 64, FAKE, FAKE, None, FAKE, None, None) == gb.GDN_ERR_UNSUPPORTED
     assert L.gdn_state_merge(2, 3, -1, 128, 128, FAKE, FAKE, None, FAKE, None, None) == gb.GDN_ERR_INVALID
     assert L.gdn_state_merge(0, 3, 4, 128, 128, FAKE, FAKE, None, FAKE, None, None) == gb.GDN_ERR_INVALID
     assert L.gdn_state_merge(2, 3, 4, 128, 128, None, FAKE, None, FAKE, None, None) == gb.GDN_ERR_INVALID
+
+
+def test_merge_pieces_errors():
+    L = gb.lib()
+    doc = ctypes.c_void_p(1 << 40)
+    assert L.gdn_state_merge_pieces(3, 2, 4, 64, 128, doc, FAKE, FAKE, None, FAKE, None) == gb.GDN_ERR_UNSUPPORTED
+    assert L.gdn_state_merge_pieces(-1, 2, 4, 128, 128, doc, FAKE, FAKE, None, FAKE, None) == gb.GDN_ERR_INVALID
+    assert L.gdn_state_merge_pieces(3, 0, 4, 128, 128, doc, FAKE, FAKE, None, FAKE, None) == gb.GDN_ERR_INVALID
+    assert L.gdn_state_merge_pieces(3, 2, 0, 128, 128, doc, FAKE, FAKE, None, FAKE, None) == gb.GDN_ERR_INVALID
+    for i in range(4):
+        ptrs = [doc, FAKE, FAKE, FAKE]
+        ptrs[i] = None
+        assert L.gdn_state_merge_pieces(3, 2, 4, 128, 128, ptrs[0], ptrs[1], ptrs[2], None, ptrs[3],
+                                        None) == gb.GDN_ERR_INVALID
+    # no pieces: nothing to launch
+    assert L.gdn_state_merge_pieces(0, 1, 4, 128, 128, None, None, None, None, None, None) == gb.GDN_OK
+
+
+# ------------------------------------------------------------------ split pieces
+def _random_offsets(rnd, total, n):
+    cuts = sorted(rnd.sample(range(1, total), min(n - 1, total - 1))) if total > 1 else []
+    return [0] + cuts + [total]
+
+
+def test_split_meta_matches_definition():
+    rnd = random.Random(23)
+    for _ in range(300):
+        total = rnd.randint(1, 2000)
+        docs = _random_offsets(rnd, total, rnd.randint(1, 25))
+        segs = _random_offsets(rnd, total, rnd.randint(1, 9))
+        po, pd, ps = gb.gdn_split_meta(docs, segs)
+        assert (po, pd, ps) == tuple(list(x) for x in varlen.split_pieces(docs, segs))
+
+
+def test_split_meta_rejects_and_capacity():
+    L = gb.lib()
+    with pytest.raises(ValueError):
+        gb.gdn_split_meta([0, 5, 9], [0, 4, 8])          # segments end before the tokens
+    with pytest.raises(ValueError):
+        gb.gdn_split_meta([0, 5, 5, 9], [0, 9])          # empty document
+    docs = (ctypes.c_int32 * 3)(0, 100, 300)
+    segs = (ctypes.c_int32 * 3)(0, 150, 300)
+    po = (ctypes.c_int32 * 3)()
+    n = ctypes.c_int32(0)
+    st = L.gdn_split_meta(docs, 3, segs, 3, 300, po, None, None, 2, ctypes.byref(n))
+    assert st == gb.GDN_ERR_CAPACITY and n.value == 3   # [0,100), [100,150), [150,300)
+    st = L.gdn_split_meta(docs, 3, segs, 3, 300, None, None, None, 0, ctypes.byref(n))
+    assert st == gb.GDN_OK and n.value == 3
 
 
 def test_status_maps_to_page_exceptions():

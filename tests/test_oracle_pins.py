@@ -297,3 +297,36 @@ def test_oracle_rejects_bad_offsets():
     q, k, v, g, beta = _rand(24, 10, 1, 4, 3)
     with pytest.raises(ValueError):
         oracle.fwd(q, k, v, g, beta, [0, 6, 5, 10], 1.0)
+
+
+@pytest.mark.parametrize("per_key,with_s0", [(False, False), (True, True), (False, True)])
+def test_piece_merge_equals_prefix_states(per_key, with_s0):
+    # every piece of a split packed sequence enters with the state that the
+    # plain recurrence reaches at the piece's first token from its document's
+    # start (first_state / last_state of the Diff Coverage page's packed plan)
+    from oracle import varlen
+    N, H, K, V = 40, 2, 5, 4
+    q, k, v, g, beta = _rand(31, N, H, K, V, per_key=per_key, gscale=0.05)
+    docs, segs = [0, 7, 26, 40], [0, 10, 13, 20, 33, 40]
+    pieces, pdoc, _ = varlen.split_pieces(docs, segs)
+    S0 = np.random.default_rng(32).standard_normal((len(docs) - 1, H, K, V)) if with_s0 else None
+    summ = oracle.summary(k, v, g, beta, pieces, gate_per_key=per_key)
+    S_in = oracle.merge_pieces(summ["S_ext"], summ["M"], pdoc, S0)
+    for p, start in enumerate(pieces[:-1]):
+        d = pdoc[p]
+        if start == docs[d]:
+            want = np.zeros((H, K, V)) if S0 is None else S0[d]
+        else:
+            want = oracle.fwd(q[docs[d]:start], k[docs[d]:start], v[docs[d]:start], g[docs[d]:start],
+                              beta[docs[d]:start], [0, start - docs[d]], 1.0, gate_per_key=per_key,
+                              S0=None if S0 is None else S0[d][None])["final"][0]
+        np.testing.assert_allclose(S_in[p], want, atol=1e-12)
+    # the correction forward over the pieces reproduces the packed forward
+    whole = oracle.fwd(q, k, v, g, beta, docs, 0.7, gate_per_key=per_key, S0=S0)
+    corr = oracle.fwd(q, k, v, g, beta, pieces, 0.7, gate_per_key=per_key, S0=S_in)
+    np.testing.assert_allclose(corr["o"], whole["o"], atol=1e-12)
+    last = [p for p in range(len(pdoc)) if p == len(pdoc) - 1 or pdoc[p + 1] != pdoc[p]]
+    np.testing.assert_allclose(corr["final"][last], whole["final"], atol=1e-12)
+    # carrying a state across a document boundary is wrong
+    wrong = oracle.merge_pieces(summ["S_ext"], summ["M"], [0] * len(pdoc), S0 if S0 is None else S0[:1])
+    assert np.abs(wrong - S_in).max() > 1e-3

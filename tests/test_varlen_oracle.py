@@ -51,3 +51,36 @@ def test_offset_rules():
     assert not varlen.valid_offsets([0, 6, 5, 9], 9)   # decreasing
     assert not varlen.valid_offsets([0, True, 9], 9)   # bools are not offsets
     assert not varlen.valid_offsets([0, 4.0, 9], 9)    # floats are not offsets
+
+
+def brute_pieces(docs, segs):
+    """Label every token with (document, segment) and keep the runs."""
+    offs, pdoc, pseg = [], [], []
+    total = docs[-1]
+    for t in range(total):
+        lab = (sum(1 for o in docs[1:] if o <= t), sum(1 for o in segs[1:] if o <= t))
+        if not pdoc or (pdoc[-1], pseg[-1]) != lab:
+            offs.append(t)
+            pdoc.append(lab[0])
+            pseg.append(lab[1])
+    return offs + [total], pdoc, pseg
+
+
+@pytest.mark.parametrize("docs,segs", [([0, 10], [0, 10]), ([0, 10], [0, 3, 7, 10]), ([0, 3, 7, 10], [0, 10]),
+                                       ([0, 4, 10], [0, 4, 10]), ([0, 5, 10], [0, 4, 6, 10]),
+                                       ([0, 1, 2, 3], [0, 2, 3])])
+def test_split_pieces_small(docs, segs):
+    assert varlen.split_pieces(docs, segs) == brute_pieces(docs, segs)
+
+
+def test_split_pieces_random():
+    rnd = random.Random(9)
+    for _ in range(200):
+        total = rnd.randint(1, 400)
+        cut = lambda n: [0] + sorted(rnd.sample(range(1, total), min(n, total - 1))) + [total]
+        docs, segs = cut(rnd.randint(0, 12)), cut(rnd.randint(0, 6))
+        po, pd, ps = varlen.split_pieces(docs, segs)
+        assert (po, pd, ps) == brute_pieces(docs, segs)
+        # a piece continues its predecessor exactly when it does not start a document
+        for p in range(1, len(pd)):
+            assert (pd[p] == pd[p - 1]) == (po[p] not in docs)
