@@ -37,12 +37,13 @@ def _lib():
         lib.gdn_oracle_fwd.argtypes = [
             ctypes.c_int64, _i64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_double,
-            _f64p, ctypes.c_int64, _i64p, _f64p, _f64p, ctypes.c_int64, _f64p, ctypes.c_int]
+            _f64p, ctypes.c_int64, _i64p, _f64p, _f64p, ctypes.c_int64, _f64p,
+            ctypes.c_int, ctypes.c_int, ctypes.c_double, _f64p, ctypes.c_int]
         lib.gdn_oracle_summary.restype = ctypes.c_int
         lib.gdn_oracle_summary.argtypes = [
             ctypes.c_int64, _i64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             _f32p, _f32p, _f32p, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int64, _i64p,
-            _f64p, _f64p, ctypes.c_int]
+            _f64p, _f64p, ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int]
         lib.gdn_oracle_merge.restype = ctypes.c_int
         lib.gdn_oracle_merge.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                          ctypes.c_int64, _f64p, _f64p, _f64p, _f64p]
@@ -68,8 +69,12 @@ def max_threads() -> int:
     return int(_lib().gdn_oracle_max_threads())
 
 
+L2NORM_EPS = 1e-6   # the epsilon of the native prepare (Diff Coverage page)
+
+
 def fwd(q, k, v, g, beta, offsets, scale, *, gate_per_key=False, use_exp2=False, S0=None,
-        heads=None, want_o=True, want_final=True, chunk_states=False, chunk=64, threads=0):
+        heads=None, want_o=True, want_final=True, chunk_states=False, chunk=64, qk_l2norm=False,
+        beta_sigmoid=False, eps=L2NORM_EPS, want_v_new=False, threads=0):
     """Token-by-token forward in fp64.
 
     q, k: [N, H, K]; v: [N, H, V] (N = flat token count); g: [N, H] (scalar
@@ -78,9 +83,14 @@ def fwd(q, k, v, g, beta, offsets, scale, *, gate_per_key=False, use_exp2=False,
     heads: optional list of head indices to run (outputs are indexed by the
     position in that list).
 
-    Returns a dict with ``o`` [N, n_sel, V], ``final`` [n_units, n_sel, K, V]
-    and ``chunk_states`` [n_chunks, n_sel, K, V] (the state entering each
-    ``chunk``-token block of every unit) as requested.
+    qk_l2norm / beta_sigmoid: the in-kernel input transforms (q and k
+    L2-normalised with ``eps`` inside the square root, beta through a
+    sigmoid) applied before the recurrence.
+
+    Returns a dict with ``o`` [N, n_sel, V], ``final`` [n_units, n_sel, K, V],
+    ``chunk_states`` [n_chunks, n_sel, K, V] (the state entering each
+    ``chunk``-token block of every unit) and ``v_new`` [N, n_sel, V] (the
+    value each token writes, beta_t (v_t - h~^T k_t)) as requested.
     """
     q, k, v, g, beta = _f32(q), _f32(k), _f32(v), _f32(g), _f32(beta)
     N, H, K = k.shape
@@ -98,18 +108,19 @@ def fwd(q, k, v, g, beta, offsets, scale, *, gate_per_key=False, use_exp2=False,
     if chunk_states:
         n_chunks = int(sum((b - a + chunk - 1) // chunk for a, b in zip(offs[:-1], offs[1:])))
         cs = np.zeros((n_chunks, n_sel, K, V))
+    vn = np.zeros((N, n_sel, V)) if want_v_new else None
     rc = _lib().gdn_oracle_fwd(
         n_units, _ptr(offs, _i64p), H, K, V, _ptr(q, _f32p), _ptr(k, _f32p), _ptr(v, _f32p),
         _ptr(g, _f32p), _ptr(beta, _f32p), int(gate_per_key), int(use_exp2), float(scale),
         _ptr(s0, _f64p), n_sel, _ptr(sel, _i64p), _ptr(o, _f64p), _ptr(fin, _f64p), int(chunk),
-        _ptr(cs, _f64p), int(threads))
+        _ptr(cs, _f64p), int(qk_l2norm), int(beta_sigmoid), float(eps), _ptr(vn, _f64p), int(threads))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
-    return {"o": o, "final": fin, "chunk_states": cs}
+    return {"o": o, "final": fin, "chunk_states": cs, "v_new": vn}
 
 
 def summary(k, v, g, beta, offsets, *, gate_per_key=False, use_exp2=False, heads=None,
-            want_ext=True, want_M=True, threads=0):
+            want_ext=True, want_M=True, qk_l2norm=False, beta_sigmoid=False, eps=L2NORM_EPS, threads=0):
     """Per-unit segment summaries: S_ext [n_units, n_sel, K, V] (state reached
     from zero) and M [n_units, n_sel, K, K] (the map applied to an entry
     state), so that the state at the end of a unit is M @ S_entry + S_ext."""
@@ -125,7 +136,7 @@ def summary(k, v, g, beta, offsets, *, gate_per_key=False, use_exp2=False, heads
     rc = _lib().gdn_oracle_summary(
         n_units, _ptr(offs, _i64p), H, K, V, _ptr(k, _f32p), _ptr(v, _f32p), _ptr(g, _f32p),
         _ptr(beta, _f32p), int(gate_per_key), int(use_exp2), n_sel, _ptr(sel, _i64p),
-        _ptr(ext, _f64p), _ptr(M, _f64p), int(threads))
+        _ptr(ext, _f64p), _ptr(M, _f64p), int(qk_l2norm), int(beta_sigmoid), float(eps), int(threads))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return {"S_ext": ext, "M": M}
@@ -146,6 +157,19 @@ def merge(S_ext, M, S0=None):
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return out
+
+
+def input_transforms(q, k, beta, eps=L2NORM_EPS):
+    """The transformed inputs and their slots, in fp64: q_hat = q r_q and
+    k_hat = k r_k with r = 1 / sqrt(sum x^2 + eps) per (token, head), and
+    beta_eff = 1 / (1 + e^{-beta}) (use_qk_l2norm_in_kernel and
+    use_beta_sigmoid_in_kernel of the native prepare, Diff Coverage page)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    rq = 1.0 / np.sqrt((q * q).sum(-1) + eps)
+    rk = 1.0 / np.sqrt((k * k).sum(-1) + eps)
+    be = 1.0 / (1.0 + np.exp(-np.asarray(beta, dtype=np.float64)))
+    return {"q_hat": q * rq[..., None], "k_hat": k * rk[..., None], "q_rstd": rq, "k_rstd": rk, "beta_eff": be}
 
 
 def merge_pieces(S_ext, M, piece_doc, S0_docs=None):

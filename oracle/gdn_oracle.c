@@ -49,6 +49,16 @@
  * chunk start, with the forward's own operations, so they are the forward's
  * values.
  *
+ * Input transforms (the in-kernel options of the native prepare on the Diff
+ * Coverage page, use_qk_l2norm_in_kernel and use_beta_sigmoid_in_kernel,
+ * whose slots q_hat, k_hat, q_rstd, k_rstd and beta_eff the ten-slot result
+ * names): with qk_l2norm, q_t and k_t are replaced by x * r with
+ * r = 1 / sqrt(sum_i x_i^2 + eps) before anything else; with beta_sigmoid,
+ * beta_t by 1 / (1 + e^{-beta_t}).  The forward can also return
+ * v_new_t = beta_t (v_t - p) (p as above), the value the token writes: the
+ * chunk form's v_new = u - w h (chunk_fwd_h on the same page returns it),
+ * which unrolled over a chunk is exactly this per-token quantity.
+ *
  * All arithmetic is fp64.  Inputs are fp32 arrays (exact copies of the
  * rounded bf16 or fp32 inputs).  Layout: the token axis is flat (a
  * [B,T,H,D] tensor is viewed as [B*T, H, D]); units are given by token
@@ -74,8 +84,24 @@ static int check_offsets(int64_t n_units, const int64_t* offsets) {
     return 0;
 }
 
+/* x as fp64, L2-normalised when l2norm is set; returns the reciprocal norm
+ * used (1 without normalisation). */
+static double load_vec(double* dst, const float* src, int64_t K, int l2norm, double eps) {
+    double ss = 0.0;
+    for (int64_t i = 0; i < K; ++i) {
+        dst[i] = (double)src[i];
+        ss += dst[i] * dst[i];
+    }
+    const double r = l2norm ? 1.0 / sqrt(ss + eps) : 1.0;
+    if (l2norm)
+        for (int64_t i = 0; i < K; ++i) dst[i] *= r;
+    return r;
+}
+
+static double beta_of(float b, int sigmoid) { return sigmoid ? 1.0 / (1.0 + exp(-(double)b)) : (double)b; }
+
 /* One token of the recurrence applied to the K x V state h (row i = key i). */
-static void token_step(double* h, int64_t K, int64_t V, const float* kt, const float* vt,
+static void token_step(double* h, int64_t K, int64_t V, const double* kt, const float* vt,
                        double beta, const double* d /* [K] decay per key row */, double* p) {
     for (int64_t i = 0; i < K; ++i) {
         double di = d[i];
@@ -84,12 +110,12 @@ static void token_step(double* h, int64_t K, int64_t V, const float* kt, const f
     }
     for (int64_t j = 0; j < V; ++j) p[j] = 0.0;
     for (int64_t i = 0; i < K; ++i) {
-        double ki = (double)kt[i];
+        double ki = kt[i];
         const double* hi = h + i * V;
         for (int64_t j = 0; j < V; ++j) p[j] += hi[j] * ki;
     }
     for (int64_t i = 0; i < K; ++i) {
-        double bk = beta * (double)kt[i];
+        double bk = beta * kt[i];
         double* hi = h + i * V;
         for (int64_t j = 0; j < V; ++j) hi[j] += bk * ((double)vt[j] - p[j]);
     }
@@ -110,7 +136,8 @@ int gdn_oracle_fwd(int64_t n_units, const int64_t* offsets, int64_t H, int64_t K
                    const float* q, const float* k, const float* v, const float* g, const float* beta,
                    int gate_per_key, int use_exp2, double scale, const double* S0, int64_t n_sel,
                    const int64_t* heads_sel, double* o, double* S_final, int64_t chunk,
-                   double* chunk_states, int n_threads) {
+                   double* chunk_states, int qk_l2norm, int beta_sigmoid, double eps, double* v_new,
+                   int n_threads) {
     if (check_offsets(n_units, offsets) != 0 || H <= 0 || K <= 0 || V <= 0) return -1;
     if (n_sel <= 0 || n_sel > H) return -1;
     if (chunk_states != NULL && chunk <= 0) return -1;
@@ -135,7 +162,9 @@ int gdn_oracle_fwd(int64_t n_units, const int64_t* offsets, int64_t H, int64_t K
         double* h = (double*)malloc(sizeof(double) * (size_t)(K * V));
         double* p = (double*)malloc(sizeof(double) * (size_t)V);
         double* d = (double*)malloc(sizeof(double) * (size_t)K);
-        if (!h || !p || !d) { free(h); free(p); free(d); bad |= 1; continue; }
+        double* kx = (double*)malloc(sizeof(double) * (size_t)K);
+        double* qx = (double*)malloc(sizeof(double) * (size_t)K);
+        if (!h || !p || !d || !kx || !qx) { free(h); free(p); free(d); free(kx); free(qx); bad |= 1; continue; }
         if (S0) memcpy(h, S0 + (u * H + hd) * K * V, sizeof(double) * (size_t)(K * V));
         else memset(h, 0, sizeof(double) * (size_t)(K * V));
         int64_t t0 = offsets[u], t1 = offsets[u + 1];
@@ -145,14 +174,20 @@ int gdn_oracle_fwd(int64_t n_units, const int64_t* offsets, int64_t H, int64_t K
                 memcpy(chunk_states + ((chunk_base[u] + local / chunk) * n_sel + s) * K * V, h,
                        sizeof(double) * (size_t)(K * V));
             gate_vector(d, g, t, H, hd, K, gate_per_key, use_exp2);
-            token_step(h, K, V, k + (t * H + hd) * K, v + (t * H + hd) * V,
-                       (double)beta[t * H + hd], d, p);
+            load_vec(kx, k + (t * H + hd) * K, K, qk_l2norm, eps);
+            const double bt = beta_of(beta[t * H + hd], beta_sigmoid);
+            const float* vt = v + (t * H + hd) * V;
+            token_step(h, K, V, kx, vt, bt, d, p);
+            if (v_new) {
+                double* nt = v_new + (t * n_sel + s) * V;
+                for (int64_t j = 0; j < V; ++j) nt[j] = bt * ((double)vt[j] - p[j]);
+            }
             if (o) {
-                const float* qt = q + (t * H + hd) * K;
+                load_vec(qx, q + (t * H + hd) * K, K, qk_l2norm, eps);
                 double* ot = o + (t * n_sel + s) * V;
                 for (int64_t j = 0; j < V; ++j) ot[j] = 0.0;
                 for (int64_t i = 0; i < K; ++i) {
-                    double qi = (double)qt[i];
+                    double qi = qx[i];
                     const double* hi = h + i * V;
                     for (int64_t j = 0; j < V; ++j) ot[j] += hi[j] * qi;
                 }
@@ -160,7 +195,7 @@ int gdn_oracle_fwd(int64_t n_units, const int64_t* offsets, int64_t H, int64_t K
             }
         }
         if (S_final) memcpy(S_final + (u * n_sel + s) * K * V, h, sizeof(double) * (size_t)(K * V));
-        free(h); free(p); free(d);
+        free(h); free(p); free(d); free(kx); free(qx);
     }
     free(chunk_base);
     return bad ? -1 : 0;
@@ -174,7 +209,8 @@ int gdn_oracle_fwd(int64_t n_units, const int64_t* offsets, int64_t H, int64_t K
 int gdn_oracle_summary(int64_t n_units, const int64_t* offsets, int64_t H, int64_t K, int64_t V,
                        const float* k, const float* v, const float* g, const float* beta,
                        int gate_per_key, int use_exp2, int64_t n_sel, const int64_t* heads_sel,
-                       double* S_ext, double* M, int n_threads) {
+                       double* S_ext, double* M, int qk_l2norm, int beta_sigmoid, double eps,
+                       int n_threads) {
     if (check_offsets(n_units, offsets) != 0 || H <= 0 || K <= 0 || V <= 0) return -1;
     if (n_sel <= 0 || n_sel > H) return -1;
     int64_t n_tasks = n_units * n_sel;
@@ -192,20 +228,21 @@ int gdn_oracle_summary(int64_t n_units, const int64_t* offsets, int64_t H, int64
         double* p = (double*)malloc(sizeof(double) * (size_t)(V > K ? V : K));
         double* d = (double*)malloc(sizeof(double) * (size_t)K);
         float* zero_v = (float*)calloc((size_t)K, sizeof(float));
-        if (!h || !x || !p || !d || !zero_v) {
-            free(h); free(x); free(p); free(d); free(zero_v); bad |= 1; continue;
+        double* kx = (double*)malloc(sizeof(double) * (size_t)K);
+        if (!h || !x || !p || !d || !zero_v || !kx) {
+            free(h); free(x); free(p); free(d); free(zero_v); free(kx); bad |= 1; continue;
         }
         for (int64_t i = 0; i < K; ++i) x[i * K + i] = 1.0;
         for (int64_t t = offsets[u]; t < offsets[u + 1]; ++t) {
             gate_vector(d, g, t, H, hd, K, gate_per_key, use_exp2);
-            double b = (double)beta[t * H + hd];
-            const float* kt = k + (t * H + hd) * K;
-            if (S_ext) token_step(h, K, V, kt, v + (t * H + hd) * V, b, d, p);
-            if (M) token_step(x, K, K, kt, zero_v, b, d, p);
+            double b = beta_of(beta[t * H + hd], beta_sigmoid);
+            load_vec(kx, k + (t * H + hd) * K, K, qk_l2norm, eps);
+            if (S_ext) token_step(h, K, V, kx, v + (t * H + hd) * V, b, d, p);
+            if (M) token_step(x, K, K, kx, zero_v, b, d, p);
         }
         if (S_ext) memcpy(S_ext + (u * n_sel + s) * K * V, h, sizeof(double) * (size_t)(K * V));
         if (M) memcpy(M + (u * n_sel + s) * K * K, x, sizeof(double) * (size_t)(K * K));
-        free(h); free(x); free(p); free(d); free(zero_v);
+        free(h); free(x); free(p); free(d); free(zero_v); free(kx);
     }
     return bad ? -1 : 0;
 }
@@ -277,8 +314,9 @@ int gdn_oracle_bwd(int64_t n_units, const int64_t* offsets, int64_t H, int64_t K
         double* uu = (double*)malloc(sizeof(double) * (size_t)V);
         double* dvt = (double*)malloc(sizeof(double) * (size_t)V);
         double* tmp = (double*)malloc(sizeof(double) * (size_t)K);
-        if (!ck || !st || !dh || !ht || !d || !p || !uu || !dvt || !tmp) {
-            free(ck); free(st); free(dh); free(ht); free(d); free(p); free(uu); free(dvt); free(tmp);
+        double* kx = (double*)malloc(sizeof(double) * (size_t)K);
+        if (!ck || !st || !dh || !ht || !d || !p || !uu || !dvt || !tmp || !kx) {
+            free(ck); free(st); free(dh); free(ht); free(d); free(p); free(uu); free(dvt); free(tmp); free(kx);
             bad |= 1;
             continue;
         }
@@ -289,7 +327,8 @@ int gdn_oracle_bwd(int64_t n_units, const int64_t* offsets, int64_t H, int64_t K
         for (int64_t t = t0; t < t1; ++t) {
             if ((t - t0) % C == 0) memcpy(ck + ((t - t0) / C) * KV, h, sizeof(double) * (size_t)KV);
             gate_vector(d, g, t, H, hd, K, gate_per_key, use_exp2);
-            token_step(h, K, V, k + (t * H + hd) * K, v + (t * H + hd) * V, (double)beta[t * H + hd], d, p);
+            load_vec(kx, k + (t * H + hd) * K, K, 0, 0.0);
+            token_step(h, K, V, kx, v + (t * H + hd) * V, (double)beta[t * H + hd], d, p);
         }
         /* reverse */
         if (dht) memcpy(dh, dht + (u * H + hd) * KV, sizeof(double) * (size_t)KV);
@@ -302,7 +341,8 @@ int gdn_oracle_bwd(int64_t n_units, const int64_t* offsets, int64_t H, int64_t K
                 double* nx = st + (t - a + 1) * KV;
                 memcpy(nx, st + (t - a) * KV, sizeof(double) * (size_t)KV);
                 gate_vector(d, g, t, H, hd, K, gate_per_key, use_exp2);
-                token_step(nx, K, V, k + (t * H + hd) * K, v + (t * H + hd) * V, (double)beta[t * H + hd], d, p);
+                load_vec(kx, k + (t * H + hd) * K, K, 0, 0.0);
+                token_step(nx, K, V, kx, v + (t * H + hd) * V, (double)beta[t * H + hd], d, p);
             }
             for (int64_t t = b - 1; t >= a; --t) {
                 const double* hprev = st + (t - a) * KV;
@@ -368,7 +408,7 @@ int gdn_oracle_bwd(int64_t n_units, const int64_t* offsets, int64_t H, int64_t K
             }
         }
         if (dS0) memcpy(dS0 + (u * H + hd) * KV, dh, sizeof(double) * (size_t)KV);
-        free(ck); free(st); free(dh); free(ht); free(d); free(p); free(uu); free(dvt); free(tmp);
+        free(ck); free(st); free(dh); free(ht); free(d); free(p); free(uu); free(dvt); free(tmp); free(kx);
     }
     return bad ? -1 : 0;
 }

@@ -1,6 +1,7 @@
 /* The fp64 oracle (oracle/gdn_oracle.c) under AddressSanitizer and
  * UndefinedBehaviorSanitizer: small random problems through every entry
- * point (forward with chunk states and a head selection, summaries, merge),
+ * point (forward with chunk states, a head selection, the input transforms
+ * and v_new, summaries, merge, backward),
  * ragged and empty units, and the invalid arguments it must reject. Every
  * output array is exactly as large as its declared shape. */
 #include <math.h>
@@ -11,10 +12,12 @@
 int gdn_oracle_fwd(int64_t n_units, const int64_t* offsets, int64_t H, int64_t K, int64_t V, const float* q,
                    const float* k, const float* v, const float* g, const float* beta, int gate_per_key,
                    int use_exp2, double scale, const double* S0, int64_t n_sel, const int64_t* heads_sel,
-                   double* o, double* S_final, int64_t chunk, double* chunk_states, int n_threads);
+                   double* o, double* S_final, int64_t chunk, double* chunk_states, int qk_l2norm,
+                   int beta_sigmoid, double eps, double* v_new, int n_threads);
 int gdn_oracle_summary(int64_t n_units, const int64_t* offsets, int64_t H, int64_t K, int64_t V, const float* k,
                        const float* v, const float* g, const float* beta, int gate_per_key, int use_exp2,
-                       int64_t n_sel, const int64_t* heads_sel, double* S_ext, double* M, int n_threads);
+                       int64_t n_sel, const int64_t* heads_sel, double* S_ext, double* M, int qk_l2norm,
+                       int beta_sigmoid, double eps, int n_threads);
 int gdn_oracle_merge(int64_t n_seg, int64_t n, int64_t K, int64_t V, const double* S_ext, const double* M,
                      const double* S0, double* S_init);
 int gdn_oracle_bwd(int64_t n_units, const int64_t* offsets, int64_t H, int64_t K, int64_t V, const float* q,
@@ -54,11 +57,14 @@ int main(void) {
         double* cs = malloc(sizeof(double) * (size_t)(n_chunks * n_sel * K * V + 1));
         double* S0 = malloc(sizeof(double) * (size_t)(n_units * H * K * V));
         for (int64_t i = 0; i < n_units * H * K * V; ++i) S0[i] = urand() - 0.5;
+        double* vn = malloc(sizeof(double) * (size_t)(N * n_sel * V + 1));
         bad |= gdn_oracle_fwd(n_units, offs, H, K, V, q, k, v, g, beta, pk, it & 2, 0.5, S0, n_sel, sel, o, fin,
-                              chunk, cs, 2) != 0;
+                              chunk, cs, it & 4, it & 8, 1e-6, (it & 16) ? NULL : vn, 2) != 0;
+        free(vn);
         double* ext = malloc(sizeof(double) * (size_t)(n_units * H * K * V));
         double* M = malloc(sizeof(double) * (size_t)(n_units * H * K * K));
-        bad |= gdn_oracle_summary(n_units, offs, H, K, V, k, v, g, beta, pk, it & 2, H, NULL, ext, M, 2) != 0;
+        bad |= gdn_oracle_summary(n_units, offs, H, K, V, k, v, g, beta, pk, it & 2, H, NULL, ext, M, it & 4, it & 8,
+                                  1e-6, 2) != 0;
         double* si = malloc(sizeof(double) * (size_t)((n_units + 1) * H * K * V));
         if (K == V) bad |= gdn_oracle_merge(n_units, H, K, V, ext, M, S0, si) != 0;
         /* backward, with dL/dh_final on even iterations */
@@ -78,11 +84,12 @@ int main(void) {
         /* rejected arguments */
         int64_t broken[3] = {0, 5, 3};
         bad |= gdn_oracle_fwd(2, broken, H, K, V, q, k, v, g, beta, pk, 0, 1.0, NULL, H, NULL, NULL, NULL, 0, NULL,
-                              1) == 0;
+                              0, 0, 0.0, NULL, 1) == 0;
         const int64_t wrong_head[1] = {H};
         bad |= gdn_oracle_fwd(n_units, offs, H, K, V, q, k, v, g, beta, pk, 0, 1.0, NULL, 1, wrong_head, o, NULL,
-                              0, NULL, 1) == 0;
-        bad |= gdn_oracle_summary(n_units, offs, H, K, V, k, v, g, beta, pk, 0, H + 1, NULL, ext, M, 1) == 0;
+                              0, NULL, 0, 0, 0.0, NULL, 1) == 0;
+        bad |= gdn_oracle_summary(n_units, offs, H, K, V, k, v, g, beta, pk, 0, H + 1, NULL, ext, M, 0, 0, 0.0,
+                                  1) == 0;
         bad |= gdn_oracle_merge(-1, H, K, V, ext, M, NULL, si) == 0;
         free(q); free(k); free(v); free(beta); free(g); free(o); free(fin); free(cs); free(S0);
         free(ext); free(M); free(si);

@@ -330,3 +330,86 @@ def test_piece_merge_equals_prefix_states(per_key, with_s0):
     # carrying a state across a document boundary is wrong
     wrong = oracle.merge_pieces(summ["S_ext"], summ["M"], [0] * len(pdoc), S0 if S0 is None else S0[:1])
     assert np.abs(wrong - S_in).max() > 1e-3
+
+
+# ---------------------------------------------------------------- v_new and the input transforms
+@pytest.mark.parametrize("per_key", [False, True])
+def test_v_new_rebuilds_the_chunk_state(per_key):
+    # the chunk form h_L = Diag(b^{G_L}) h_0 + sum_j (k_j * b^{G_L - G_j}) v_new_j^T
+    # (the state update of kda_split_state_summary_kernel on the state_summary.py
+    # page) must hold with the oracle's per-token v_new, for any chunk length
+    N, H, K, V = 23, 1, 5, 4
+    q, k, v, g, beta = _rand(41, N, H, K, V, per_key=per_key, gscale=0.3)
+    S0 = np.random.default_rng(42).standard_normal((1, H, K, V))
+    r = oracle.fwd(q, k, v, g, beta, [0, N], 1.0, gate_per_key=per_key, S0=S0, want_v_new=True)
+    gg = g.astype(np.float64)[:, 0]
+    G = np.cumsum(gg, axis=0)
+    GL = G[-1]
+    dec = lambda x: np.exp(x)
+    h = (dec(GL)[:, None] if per_key else dec(GL)) * S0[0, 0]
+    for j in range(N):
+        kj = k[j, 0].astype(np.float64) * (dec(GL - G[j]) if per_key else dec(GL - G[j]))
+        h = h + np.outer(kj, r["v_new"][j, 0])
+    np.testing.assert_allclose(h, r["final"][0, 0], atol=1e-12)
+    # first token from a zero state writes beta_0 v_0; beta = 0 writes nothing
+    z = oracle.fwd(q, k, v, g, beta, [0, N], 1.0, gate_per_key=per_key, want_v_new=True)
+    np.testing.assert_allclose(z["v_new"][0, 0], float(beta[0, 0]) * v[0, 0].astype(np.float64), rtol=1e-14)
+    b0 = oracle.fwd(q, k, v, g, np.zeros_like(beta), [0, N], 1.0, gate_per_key=per_key, want_v_new=True)
+    assert np.all(b0["v_new"] == 0.0)
+
+
+def test_qk_l2norm_is_scale_invariant():
+    # the normalised forward does not see the scale of q and k; the raw one does
+    N, H, K, V = 17, 2, 6, 3
+    q, k, v, g, beta = _rand(43, N, H, K, V)
+    rq = np.random.default_rng(44)
+    # rows of different norms, all large enough that the epsilon (1e-6 under
+    # the square root) moves nothing by more than about 1e-7
+    q = (q * rq.uniform(2.0, 5.0, (N, H, 1))).astype(np.float32)
+    k = (k * rq.uniform(2.0, 5.0, (N, H, 1))).astype(np.float32)
+    a = oracle.fwd(q, k, v, g, beta, [0, 9, N], 0.7, qk_l2norm=True, want_v_new=True)
+    b = oracle.fwd(3 * q, 2 * k, v, g, beta, [0, 9, N], 0.7, qk_l2norm=True, want_v_new=True)
+    for key in ("o", "final", "v_new"):
+        np.testing.assert_allclose(b[key], a[key], rtol=2e-6, atol=1e-7)
+    raw = oracle.fwd(3 * q, 2 * k, v, g, beta, [0, 9, N], 0.7)
+    assert np.abs(raw["o"] - a["o"]).max() > 1e-2
+    # unit-norm inputs are left as they are (up to the epsilon in the norm)
+    u = oracle.input_transforms(q, k, beta)
+    qn, kn = u["q_hat"].astype(np.float32), u["k_hat"].astype(np.float32)
+    c = oracle.fwd(qn, kn, v, g, beta, [0, 9, N], 0.7, qk_l2norm=True)
+    d = oracle.fwd(qn, kn, v, g, beta, [0, 9, N], 0.7)
+    np.testing.assert_allclose(c["o"], d["o"], rtol=1e-5, atol=1e-6)
+    # what the slots hold: unit rows, and r = 1 / |x| up to the epsilon
+    np.testing.assert_allclose(np.linalg.norm(u["q_hat"], axis=-1), 1.0, atol=1e-6)
+    np.testing.assert_allclose(u["k_rstd"] * np.linalg.norm(k.astype(np.float64), axis=-1), 1.0, atol=1e-6)
+
+
+def test_beta_sigmoid_closed_forms():
+    N, H, K, V = 12, 1, 4, 4
+    q, k, v, g, beta = _rand(45, N, H, K, V)
+    zero = np.zeros_like(beta)
+    half = np.full_like(beta, 0.5)
+    a = oracle.fwd(q, k, v, g, zero, [0, N], 1.0, beta_sigmoid=True)
+    b = oracle.fwd(q, k, v, g, half, [0, N], 1.0)
+    assert np.array_equal(a["o"], b["o"]) and np.array_equal(a["final"], b["final"])   # sigmoid(0) = 1/2
+    c = oracle.fwd(q, k, v, g, np.full_like(beta, -60.0), [0, N], 1.0, beta_sigmoid=True)
+    d = oracle.fwd(q, k, v, g, zero, [0, N], 1.0)
+    np.testing.assert_allclose(c["o"], d["o"], atol=1e-20)                                  # sigmoid(-60) ~ 1e-26
+    x = np.linspace(-5, 5, 11)
+    t = oracle.input_transforms(np.ones((11, 1, 2)), np.ones((11, 1, 2)), x)["beta_eff"]
+    np.testing.assert_allclose(t + t[::-1], 1.0, atol=1e-15)                                 # sigmoid(x) + sigmoid(-x) = 1
+
+
+@pytest.mark.parametrize("per_key", [False, True])
+def test_split_identity_with_transforms(per_key):
+    # S_end = M S_entry + S_ext holds for the transformed inputs too
+    N, H, K, V = 20, 1, 5, 4
+    q, k, v, g, beta = _rand(47, N, H, K, V, per_key=per_key, gscale=0.05)
+    k = (k * 2.5).astype(np.float32)
+    beta = (beta * 4 - 2).astype(np.float32)        # raw logits
+    S0 = np.random.default_rng(48).standard_normal((1, H, K, V))
+    kw = dict(gate_per_key=per_key, qk_l2norm=True, beta_sigmoid=True)
+    full = oracle.fwd(q, k, v, g, beta, [0, N], 1.0, S0=S0, **kw)["final"][0]
+    summ = oracle.summary(k, v, g, beta, [0, 7, N], **kw)
+    S_init = oracle.merge(summ["S_ext"], summ["M"], S0[0])
+    np.testing.assert_allclose(S_init[2], full, atol=1e-12)
