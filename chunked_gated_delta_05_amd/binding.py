@@ -23,7 +23,8 @@ GDN_OK, GDN_ERR_INVALID, GDN_ERR_UNSUPPORTED, GDN_ERR_DEVICE, GDN_ERR_CAPACITY =
 LAYOUT_BSND, LAYOUT_TND = 0, 1
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_SCALAR, GATE_PER_KEY = 0, 1
-FLAG_REUSE_PREPARED, FLAG_PREPARE_ONLY = 1, 2
+FLAG_REUSE_PREPARED, FLAG_PREPARE_ONLY, FLAG_QK_L2NORM, FLAG_BETA_SIGMOID = 1, 2, 4, 8
+_TRANSFORMS = FLAG_QK_L2NORM | FLAG_BETA_SIGMOID
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 
@@ -39,7 +40,12 @@ class GdnDesc(ctypes.Structure):
 
 
 class GdnSlots(ctypes.Structure):
-    _fields_ = [("g_cumsum", ctypes.c_void_p), ("A", ctypes.c_void_p), ("h", ctypes.c_void_p)]
+    _fields_ = [("g_cumsum", ctypes.c_void_p), ("A", ctypes.c_void_p), ("h", ctypes.c_void_p),
+                ("v_new", ctypes.c_void_p), ("q_hat", ctypes.c_void_p), ("k_hat", ctypes.c_void_p),
+                ("q_rstd", ctypes.c_void_p), ("k_rstd", ctypes.c_void_p), ("beta_eff", ctypes.c_void_p)]
+
+
+SLOT_NAMES = ("g_cumsum", "A", "h", "v_new", "q_hat", "k_hat", "q_rstd", "k_rstd", "beta_eff")
 
 
 _LIB = None
@@ -282,6 +288,11 @@ def _fwd_args(q, k, v, g, beta, scale, meta, initial_state, o_dtype, out, final_
         _check_tensor("initial_state", initial_state, torch.float32, sshape, dev)
     extras = {}
     tokens = k.shape[0] * k.shape[1] if k.dim() == 4 else k.shape[0]
+    lead = tuple(k.shape[:-2])
+    if any(n not in SLOT_NAMES for n in extras_wanted):
+        raise ValueError(f"unknown slots {extras_wanted}; known: {SLOT_NAMES}")
+    if any(n in extras_wanted for n in ("q_hat", "q_rstd")) and q is None:
+        raise ValueError("q_hat and q_rstd need q")
     if "g_cumsum" in extras_wanted:
         extras["g_cumsum"] = torch.empty(g.shape, dtype=torch.float32, device=dev)
     if "A" in extras_wanted:
@@ -289,8 +300,18 @@ def _fwd_args(q, k, v, g, beta, scale, meta, initial_state, o_dtype, out, final_
     if "h" in extras_wanted:
         n_chunks = meta.n_chunks if meta is not None else k.shape[0] * ((k.shape[1] + 63) // 64)
         extras["h"] = torch.empty((n_chunks, H, k.shape[-1], vv.shape[-1]), dtype=torch.float32, device=dev)
+    if "v_new" in extras_wanted:
+        extras["v_new"] = torch.empty(vv.shape, dtype=torch.float32, device=dev)
+    for n in ("q_hat", "k_hat"):
+        if n in extras_wanted:
+            extras[n] = torch.empty(k.shape, dtype=k.dtype, device=dev)
+    for n in ("q_rstd", "k_rstd"):
+        if n in extras_wanted:
+            extras[n] = torch.empty((*lead, H), dtype=torch.float32, device=dev)
+    if "beta_eff" in extras_wanted:
+        extras["beta_eff"] = torch.empty(beta.shape, dtype=beta.dtype, device=dev)
     _require_gpu(q, k, None if prep_only else v, g, beta, meta)
-    slots = GdnSlots(_ptr(extras.get("g_cumsum")), _ptr(extras.get("A")), _ptr(extras.get("h")))
+    slots = GdnSlots(*[_ptr(extras.get(n)) for n in SLOT_NAMES])
     return desc, o, fin, slots, extras
 
 
@@ -298,15 +319,18 @@ def _fwd_args(q, k, v, g, beta, scale, meta, initial_state, o_dtype, out, final_
 def gdn_chunk_fwd(q, k, v, g, beta, scale=None, *, meta: UnitMeta | None = None, initial_state=None,
                   output_final_state=False, use_exp2=False, o_dtype=torch.float32,
                   want_g_cumsum=False, want_A=False, want_h=False, flags=0, workspace=None, out=None,
-                  final_out=None):
+                  final_out=None, qk_l2norm=False, beta_sigmoid=False, slots=()):
     """Chunked gated delta rule forward through libgdn.
 
     q, k [B,T,H,K] (BSND) or [T,H,K] (TND, needs meta); v like q; g fp32
     [..,H] (scalar gate) or [..,H,K] (per-key gate); beta [..,H]. Given
     out / final_out buffers are written in place (out: o_dtype, v's shape;
-    final_out: fp32 [units,H,K,V]). Returns (o, final_state or None,
-    extras dict)."""
-    wanted = [n for n, f in (("g_cumsum", want_g_cumsum), ("A", want_A), ("h", want_h)) if f]
+    final_out: fp32 [units,H,K,V]). qk_l2norm / beta_sigmoid: the in-kernel
+    input transforms (FLAG_QK_L2NORM, FLAG_BETA_SIGMOID). slots: names from
+    SLOT_NAMES to return (want_* are the older spellings of three of them).
+    Returns (o, final_state or None, extras dict)."""
+    wanted = [n for n, f in (("g_cumsum", want_g_cumsum), ("A", want_A), ("h", want_h)) if f] + list(slots)
+    flags = int(flags) | (FLAG_QK_L2NORM if qk_l2norm else 0) | (FLAG_BETA_SIGMOID if beta_sigmoid else 0)
     desc, o, fin, slots, extras = _fwd_args(q, k, v, g, beta, scale, meta, initial_state, o_dtype, out,
                                             final_out, output_final_state, use_exp2, flags, wanted)
     dev = k.device
@@ -341,9 +365,12 @@ class FwdCall:
     tensors must stay alive and in place while the object is used."""
 
     def __init__(self, q, k, v, g, beta, scale=None, *, out, workspace, meta: UnitMeta | None = None,
-                 initial_state=None, final_out=None, use_exp2=False):
+                 initial_state=None, final_out=None, use_exp2=False, transforms=0):
         self._desc, o, fin, self._slots, _ = _fwd_args(q, k, v, g, beta, scale, meta, initial_state, out.dtype,
                                                        out, final_out, False, use_exp2, 0)
+        if transforms & ~_TRANSFORMS:
+            raise ValueError("transforms takes FLAG_QK_L2NORM and FLAG_BETA_SIGMOID only")
+        self._xf = int(transforms)
         nb = workspace_bytes(self._desc)
         if workspace.dtype != torch.uint8 or workspace.device != k.device or workspace.numel() < nb:
             raise ValueError(f"workspace must be a uint8 tensor of at least {nb} bytes on {k.device}")
@@ -355,11 +382,12 @@ class FwdCall:
         self._fn = lib().gdn_chunk_fwd
 
     def __call__(self, flags: int = 0) -> None:
-        check(self._fn(*self._args, int(flags), *self._tail), "gdn_chunk_fwd")
+        check(self._fn(*self._args, int(flags) | self._xf, *self._tail), "gdn_chunk_fwd")
 
 
 def gdn_state_summary(k, v, g, beta, *, meta: UnitMeta, mode=0, use_exp2=False, q=None,
-                      workspace=None, S_ext=None, M=None, flags=0, units=None):
+                      workspace=None, S_ext=None, M=None, flags=0, units=None, qk_l2norm=False,
+                      beta_sigmoid=False):
     """Per-unit summaries (S_ext [units,H,K,V], M [units,H,K,K]; given
     buffers are written in place); pass q to leave a per-key preparation
     that a reusing forward can use. units: None (all) or a device int32
@@ -367,8 +395,9 @@ def gdn_state_summary(k, v, g, beta, *, meta: UnitMeta, mode=0, use_exp2=False, 
     as they are); flags: 0 or FLAG_REUSE_PREPARED."""
     if mode not in (0, 1, 2):
         raise ValueError("mode must be 0 (both), 1 (S_ext) or 2 (M)")
-    if flags not in (0, FLAG_REUSE_PREPARED):
-        raise ValueError("flags must be 0 or FLAG_REUSE_PREPARED")
+    if flags & ~(FLAG_REUSE_PREPARED | _TRANSFORMS):
+        raise ValueError("flags take FLAG_REUSE_PREPARED and the transform flags only")
+    flags = int(flags) | (FLAG_QK_L2NORM if qk_l2norm else 0) | (FLAG_BETA_SIGMOID if beta_sigmoid else 0)
     if v is None:
         raise ValueError("v is required")
     H, per_key = _check_inputs(q, k, v, g, beta, meta)
@@ -378,7 +407,7 @@ def gdn_state_summary(k, v, g, beta, *, meta: UnitMeta, mode=0, use_exp2=False, 
     ws = workspace if workspace is not None else torch.empty(nb, dtype=torch.uint8, device=dev)
     if ws.dtype != torch.uint8 or ws.device != dev or ws.numel() < nb:
         raise ValueError(f"workspace must be a uint8 tensor of at least {nb} bytes on {dev}")
-    if flags and workspace is None:
+    if flags & FLAG_REUSE_PREPARED and workspace is None:
         raise ValueError("FLAG_REUSE_PREPARED needs the workspace of the preparing call")
     n_units = n_units_of(k, meta)
     n_sel = -1

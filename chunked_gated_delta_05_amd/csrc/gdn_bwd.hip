@@ -135,7 +135,7 @@ __device__ void load_chunk(const BwdArgs& a, int64_t t0, int64_t ch, int head, i
     load_tile<float, BT, BT>(reinterpret_cast<const float*>(a.ws.Tm) + ch * (BT * BT), BT, BT, Ts, BTL, tid);
     load_tile<float, BT, BT>(reinterpret_cast<const float*>(a.ws.P) + ch * (BT * BT), BT, BT, Ps, BTL, tid);
     if (tid < BT) bt[tid] = tid < len ? ldf(reinterpret_cast<const In*>(a.beta), (t0 + tid) * a.H + head) : 0.0f;
-    gm[tid] = a.ws.gam[ch * (4 * BT) + tid];
+    gm[tid] = a.ws.gam[ch * (GAMR * BT) + tid];   // rows 0..3 (the backward has no q / k normalisation)
     __syncthreads();
     if (TB)
         for (int e = tid; e < BT * BT; e += 256) Ts[(e >> 6) * BTL + (e & 63)] *= bt[e & 63];

@@ -32,6 +32,13 @@ __device__ __forceinline__ float fpow(float x, int use_exp2) {
     return __builtin_amdgcn_exp2f(use_exp2 ? x : x * 1.4426950408889634f);
 }
 
+// The input transforms: beta through a sigmoid, and the reciprocal L2 norm
+// of a q / k row from its sum of squares (epsilon 1e-6 under the root).
+__device__ __forceinline__ float sigmoid_f(float x) {
+    return 1.0f / (1.0f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+}
+__device__ __forceinline__ float rnorm_f(float sumsq) { return 1.0f / __builtin_sqrtf(sumsq + 1e-6f); }
+
 // Workgroup barrier for LDS hand-offs only: this wave's LDS accesses complete
 // before it, but outstanding global loads and stores stay in flight (the
 // fence of __syncthreads would wait for all of them).

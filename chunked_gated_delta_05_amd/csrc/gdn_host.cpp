@@ -49,6 +49,8 @@ gdn_status validate(const gdn_desc* d, gdn::Problem* p) {
     const int64_t total = int64_t(d->B) * d->T;
     if (total * d->H * DK > kMaxElems) return GDN_ERR_INVALID;
     p->reorder = 0;
+    p->qk_norm = 0;
+    p->beta_sig = 0;
     gdn::UnitMap um;
     memset(&um, 0, sizeof(um));
     um.T = d->T;
@@ -134,7 +136,7 @@ size_t gdn::workspace_bytes(const gdn::Problem& p, gdn::Workspace* ws, char* bas
     auto take = [&](int64_t bytes) { int64_t o = off; off = align256(off + bytes); return o; };
     const int64_t oT = take(nch * BT * BT * es);
     const int64_t oP = take(nch * BT * BT * es);
-    const int64_t og = (p.dtype == 0 && !p.per_key) ? take(nch * 4 * BT * 4) : 0;
+    const int64_t og = (p.dtype == 0 && !p.per_key) ? take(nch * GAMR * BT * 4) : 0;
     int64_t oq = 0, od = 0, ok = 0, ol = 0;
     if (p.per_key) {
         oq = take(nch * BT * DK * es);
@@ -196,9 +198,12 @@ gdn_status gdn::fwd_preflight(const gdn_desc* desc, const void* q, const void* k
                               gdn::Problem* p, size_t* workspace_need) {
     gdn_status st = validate(desc, p);
     if (st != GDN_OK) return st;
-    if (flags & ~(GDN_FLAG_REUSE_PREPARED | GDN_FLAG_PREPARE_ONLY)) return GDN_ERR_INVALID;
+    if (flags & ~(GDN_FLAG_REUSE_PREPARED | GDN_FLAG_PREPARE_ONLY | GDN_FLAG_QK_L2NORM | GDN_FLAG_BETA_SIGMOID))
+        return GDN_ERR_INVALID;
     const bool reuse = flags & GDN_FLAG_REUSE_PREPARED, prep_only = flags & GDN_FLAG_PREPARE_ONLY;
     if (reuse && prep_only) return GDN_ERR_INVALID;
+    p->qk_norm = (flags & GDN_FLAG_QK_L2NORM) != 0;
+    p->beta_sig = (flags & GDN_FLAG_BETA_SIGMOID) != 0;
     const bool tokens = p->um.total_tokens > 0;
     if (tokens && (!k || !g || !beta)) return GDN_ERR_INVALID;
     if (!prep_only && tokens && (!q || !v || !o)) return GDN_ERR_INVALID;
@@ -221,15 +226,25 @@ extern "C" gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const v
     st = gdn::fwd_preflight(desc, q, k, v, g, beta, o, flags, &p, nullptr);
     if (st != GDN_OK) return st;
     const bool reuse = flags & GDN_FLAG_REUSE_PREPARED, prep_only = flags & GDN_FLAG_PREPARE_ONLY;
-    float* gcs = slots ? slots->g_cumsum : nullptr;
-    float* A = slots ? slots->A : nullptr;
-    float* hs = slots ? slots->h : nullptr;
+    gdn::PrepSlots ps = {};
+    if (slots) {
+        ps.g_cumsum = slots->g_cumsum;
+        ps.A = slots->A;
+        ps.q_hat = slots->q_hat;
+        ps.k_hat = slots->k_hat;
+        ps.q_rstd = slots->q_rstd;
+        ps.k_rstd = slots->k_rstd;
+        ps.beta_eff = slots->beta_eff;
+    }
+    // q_hat and q_rstd come from q, which a preparation without q does not read
+    if (!q && (ps.q_hat || ps.q_rstd)) return GDN_ERR_INVALID;
     if (!reuse) {
-        if (gdn::launch_prep(p, ws, k, q, g, beta, gcs, A, stream) != hipSuccess) return GDN_ERR_DEVICE;
+        if (gdn::launch_prep(p, ws, k, q, g, beta, ps, stream) != hipSuccess) return GDN_ERR_DEVICE;
     }
     if (!prep_only) {
-        if (gdn::launch_state(p, ws, q, k, v, beta, initial_state, o, final_state, hs, 0, 0, 0, nullptr,
-                              nullptr, nullptr, 0, stream) != hipSuccess)
+        if (gdn::launch_state(p, ws, q, k, v, beta, initial_state, o, final_state, slots ? slots->h : nullptr,
+                              slots ? slots->v_new : nullptr, 0, 0, 0, nullptr, nullptr, nullptr, 0,
+                              stream) != hipSuccess)
             return GDN_ERR_DEVICE;
     }
     return GDN_OK;
@@ -243,7 +258,9 @@ extern "C" gdn_status gdn_state_summary(const gdn_desc* desc, const void* q, con
     gdn_status st = validate(desc, &p);
     if (st != GDN_OK) return st;
     if (mode < 0 || mode > 2) return GDN_ERR_INVALID;
-    if (flags & ~GDN_FLAG_REUSE_PREPARED) return GDN_ERR_INVALID;
+    if (flags & ~(GDN_FLAG_REUSE_PREPARED | GDN_FLAG_QK_L2NORM | GDN_FLAG_BETA_SIGMOID)) return GDN_ERR_INVALID;
+    p.qk_norm = (flags & GDN_FLAG_QK_L2NORM) != 0;
+    p.beta_sig = (flags & GDN_FLAG_BETA_SIGMOID) != 0;
     const bool all = n_sel < 0;
     if (n_sel > p.um.n_units || (n_sel > 0 && !units_dev)) return GDN_ERR_INVALID;
     const bool want_ext = mode != 2, want_M = mode != 1;
@@ -255,10 +272,10 @@ extern "C" gdn_status gdn_state_summary(const gdn_desc* desc, const void* q, con
     const bool tokens = p.um.total_tokens > 0;
     if (tokens && (!k || !v || !g || !beta)) return GDN_ERR_INVALID;
     if (!(flags & GDN_FLAG_REUSE_PREPARED) &&
-        gdn::launch_prep(p, ws, k, q, g, beta, nullptr, nullptr, stream) != hipSuccess)
+        gdn::launch_prep(p, ws, k, q, g, beta, gdn::PrepSlots{}, stream) != hipSuccess)
         return GDN_ERR_DEVICE;
     if (n_sel == 0) return GDN_OK;
-    if (gdn::launch_state(p, ws, nullptr, k, v, beta, nullptr, nullptr, nullptr, nullptr, 1, want_ext,
+    if (gdn::launch_state(p, ws, nullptr, k, v, beta, nullptr, nullptr, nullptr, nullptr, nullptr, 1, want_ext,
                           want_M, S_ext, M, all ? nullptr : units_dev, n_sel, stream) != hipSuccess)
         return GDN_ERR_DEVICE;
     return GDN_OK;

@@ -17,6 +17,7 @@ constexpr int DV = 128;   // value width
 constexpr int BV = 32;    // value columns per state-pass workgroup
 constexpr int CFB = 1024; // per-(chunk, head) coefficient block of the per-key fp16 state pass (bytes)
 constexpr int CFS = 1024; // the same block of the scalar-gate fp16 state pass (bytes)
+constexpr int GAMR = 5;       // fp32 scalar-gate rows per (chunk, head) in Workspace::gam
 constexpr int ORD_MAX = 2048;  // packed units beyond this count keep their natural launch order
 
 // Where every chunk of every unit lives on the flat token axis.
@@ -39,7 +40,8 @@ struct UnitMap {
 struct Workspace {
     void* Tm;        // operands [n_chunks][H][64][64]  T = (I + L)^{-1}
     void* P;         // operands [n_chunks][H][64][64]  decayed q.k, lower incl. diagonal
-    float* gam;      // fp32 scalar gate only: [n_chunks][H][4][64]  G, b^G, b^{G_last-G}, b^{G_last}
+    float* gam;      // fp32 scalar gate only: [n_chunks][H][5][64]  G, b^G r_k, b^{G_last-G} r_k,
+                     // b^{G_last}, b^G r_q (r: the reciprocal q / k norms, 1 without normalisation)
     // per-key gate only
     void* qg;        // operands [n_chunks][H][64][K]  q * b^G
     void* kd;        // operands [n_chunks][H][64][K]  k * b^G
@@ -61,19 +63,31 @@ struct Problem {
     float scale;
     UnitMap um;
     int32_t reorder;    // packed units out of longest-first order: the state passes reorder them
+    int32_t qk_norm;    // q and k L2-normalised in the kernels
+    int32_t beta_sig;   // beta through a sigmoid in the kernels
+};
+
+// Optional per-token outputs of the chunk preparation (NULL: not written).
+struct PrepSlots {
+    float* g_cumsum;
+    float* A;
+    void* q_hat;        // input dtype [tokens][H][K]
+    void* k_hat;
+    float* q_rstd;      // [tokens][H]
+    float* k_rstd;
+    void* beta_eff;     // input dtype [tokens][H]
 };
 
 size_t workspace_bytes(const Problem& p, Workspace* ws, char* base);
 
 hipError_t launch_prep(const Problem& p, const Workspace& ws, const void* k, const void* q,
-                       const float* g, const void* beta, float* g_cumsum_slot, float* A_slot,
-                       hipStream_t s);
+                       const float* g, const void* beta, const PrepSlots& slots, hipStream_t s);
 
 // mode: 0 forward; 1 summary (S_ext and/or M), of the units in units_sel
 // (device, n_sel entries) when given, else of all
 hipError_t launch_state(const Problem& p, const Workspace& ws, const void* q, const void* k,
                         const void* v, const void* beta, const float* h0, void* o,
-                        float* hfinal, float* hslot, int summary, int want_ext, int want_M,
+                        float* hfinal, float* hslot, float* vnew_slot, int summary, int want_ext, int want_M,
                         float* S_ext, float* M, const int32_t* units_sel, int n_sel, hipStream_t s);
 
 hipError_t launch_merge_pieces(int n_pieces, int n_docs, int H, const int32_t* piece_doc, const float* S_ext,

@@ -180,11 +180,12 @@ __device__ __forceinline__ int swzk(int r) { return (r & 1) | ((r & 2) << 1) | (
 // the fp32 b^{G_L} of every key.
 constexpr int CF_CY = 0, CF_CP = 64, CF_BG = 128, CF_BETA = 192;   // fp16 offsets
 constexpr int CF_GL = 128;                                          // fp32 offset
-// The scalar gate's block (CFS bytes) holds two fp32 rows in the same lane
-// order - b^{G_L - G} and b^G - at the float offsets below (floats 0..63 and
-// 192..255 are not used; beta is folded into T); b^{G_L} is the b^G entry of
-// the chunk's last valid token.
-constexpr int CS_CP = 64, CS_BG = 128;
+// The scalar gate's block (CFS bytes) holds, at the float offsets below,
+// b^{G_L} (one float) and three fp32 rows in the same lane order:
+// b^{G_L - G} r_k (the update), b^G r_k (k.h) and b^G r_q (q.h), r being the
+// reciprocal q / k norm of the row (1 without normalisation); beta is folded
+// into T. Floats 1..63 are not used.
+constexpr int CS_EL = 0, CS_CP = 64, CS_BG = 128, CS_BQ = 192;
 __device__ __forceinline__ int lane_order(int t) { return 16 * ((t >> 2) & 3) + 4 * (t >> 4) + (t & 3); }
 
 
@@ -202,6 +203,13 @@ struct PrepArgs {
     Workspace ws;
     float* g_cumsum;     // optional slot, token-major
     float* A;            // optional slot, token-major [tokens][H][64]
+    int qk_norm;         // q and k L2-normalised (rows scaled by r = 1 / |x|)
+    int beta_sig;        // beta through a sigmoid
+    void* q_hat;         // optional slots: the transformed inputs (input dtype) and r
+    void* k_hat;
+    float* q_rstd;
+    float* k_rstd;
+    void* beta_eff;
 };
 
 template <class P, bool PERKEY>
@@ -216,6 +224,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     __shared__ float Ls[BT * LDL];
     __shared__ float Ts[BT * LDL];
     __shared__ float Yb[3 * 16 * 17];
+    __shared__ float Rn[2 * BT];          // reciprocal norms of the k rows, then the q rows
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, G = lane >> 4, n = lane & 15;
     const int ci = blockIdx.x, head = blockIdx.y, H = a.H;
@@ -250,7 +259,42 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
             *reinterpret_cast<f32x4*>(&qt[r * LDQ + cv + e]) = f32x4{qv[e], qv[e + 1], qv[e + 2], qv[e + 3]};
         }
     }
-    if (tid < BT) bet[tid] = tid < len ? P::f(bin[(t0 + tid) * H + head]) : 0.0f;
+    // ---- input transforms: k and q rows normalised in place (r = 1 / |x|),
+    // beta through a sigmoid; optional slots of the transformed inputs
+    __syncthreads();
+    if (tid < 2 * BT) {
+        const int r = tid & (BT - 1);
+        const Op* t = tid < BT ? kt : qt;
+        float ss = 0.0f;
+        if (a.qk_norm && r < len)
+            for (int d = 0; d < DK; ++d) ss += (float)t[r * LDQ + d] * (float)t[r * LDQ + d];
+        Rn[tid] = a.qk_norm && r < len ? rnorm_f(ss) : 1.0f;
+    }
+    __syncthreads();
+    if (a.qk_norm || a.k_hat || a.q_hat) {
+        for (int e = tid; e < BT * DK; e += 256) {
+            const int r = e / DK, d = e % DK;
+            const float xk = (float)kt[r * LDQ + d] * Rn[r], xq = (float)qt[r * LDQ + d] * Rn[BT + r];
+            if (a.qk_norm) {
+                kt[r * LDQ + d] = (Op)xk;
+                qt[r * LDQ + d] = (Op)xq;
+            }
+            if (r < len) {
+                if (a.k_hat) reinterpret_cast<In*>(a.k_hat)[((t0 + r) * H + head) * DK + d] = (In)xk;
+                if (has_q && a.q_hat) reinterpret_cast<In*>(a.q_hat)[((t0 + r) * H + head) * DK + d] = (In)xq;
+            }
+        }
+    }
+    if (tid < len) {
+        if (a.k_rstd) a.k_rstd[(t0 + tid) * H + head] = Rn[tid];
+        if (has_q && a.q_rstd) a.q_rstd[(t0 + tid) * H + head] = Rn[BT + tid];
+    }
+    if (tid < BT) {
+        float bt = tid < len ? P::f(bin[(t0 + tid) * H + head]) : 0.0f;
+        if (a.beta_sig && tid < len) bt = sigmoid_f(bt);
+        if (a.beta_eff && tid < len) reinterpret_cast<In*>(a.beta_eff)[(t0 + tid) * H + head] = (In)bt;
+        bet[tid] = bt;
+    }
     if (!PERKEY) {
         // inclusive scan of the scalar gate over the chunk, one wave; stores
         // G, b^G, b^{G_last - G} and b^{G_last} for the state pass
@@ -262,12 +306,13 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
             }
             const float xl = __shfl(x, len > 0 ? len - 1 : 0, 64);
             Gs[lane] = x;
-            float* gw = a.ws.gam + ch * (4 * BT);
+            float* gw = a.ws.gam + ch * (GAMR * BT);
             const float bG = fpow(x, a.use_exp2), bLG = fpow(xl - x, a.use_exp2), bL = fpow(xl, a.use_exp2);
             gw[lane] = x;
-            gw[BT + lane] = bG;
-            gw[2 * BT + lane] = bLG;
+            gw[BT + lane] = bG * Rn[lane];
+            gw[2 * BT + lane] = bLG * Rn[lane];
             gw[3 * BT + lane] = bL;
+            gw[4 * BT + lane] = bG * Rn[BT + lane];
             if (a.g_cumsum && lane < len) a.g_cumsum[(t0 + lane) * H + head] = x;
         }
     } else {
@@ -503,11 +548,16 @@ constexpr int PLS = 20;               // row stride (floats) of the 16 x 16 LDS 
 constexpr int PBL = 16 * PLS + 4;     // L blocks: successive blocks 4 banks apart
 constexpr int PBT = 16 * PLS + 16;    // T blocks: successive blocks 16 banks apart
 
+// XF: the input transforms or their slots are asked for (a separate
+// instantiation, so that the plain preparation keeps its registers)
+template <bool XF>
 __global__ __launch_bounds__(64) void prep_kernel_h(PrepArgs a) {
     __shared__ __attribute__((aligned(16))) float Ld[4 * PBL];
     __shared__ __attribute__((aligned(16))) float Td[4 * PBT];
     __shared__ __attribute__((aligned(16))) float Gs[BT];
     __shared__ __attribute__((aligned(16))) float Bs[BT];
+    __shared__ __attribute__((aligned(16))) float Rk[BT];
+    __shared__ __attribute__((aligned(16))) float Rq[BT];
 
     // heads vary fastest across the grid, so that waves dispatched together
     // read the same token rows (all heads of a row are contiguous)
@@ -548,6 +598,62 @@ __global__ __launch_bounds__(64) void prep_kernel_h(PrepArgs a) {
         for (int kk = 0; kk < 4; ++kk)
             qf[b][kk] = __builtin_amdgcn_raw_buffer_load_b128(rq, (16 * b + n) * rowb + (32 * kk + 8 * G) * 2, 0, 0);
 
+    // ---- input transforms: the reciprocal norms r of the k and q rows (the
+    // four lanes of a row, G = 0..3, sum their 32 keys and exchange by xor)
+    // and beta through a sigmoid; optional slots of the transformed inputs
+    float rkb[4] = {1.f, 1.f, 1.f, 1.f}, rqb[4] = {1.f, 1.f, 1.f, 1.f};
+    if (XF && a.qk_norm) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            float sk = 0.0f, sq = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float k0 = __builtin_bit_cast(float, kf[b][kk][i] << 16), k1 = __builtin_bit_cast(float, kf[b][kk][i] & 0xffff0000u);
+                    const float q0 = __builtin_bit_cast(float, qf[b][kk][i] << 16), q1 = __builtin_bit_cast(float, qf[b][kk][i] & 0xffff0000u);
+                    sk += k0 * k0 + k1 * k1;
+                    sq += q0 * q0 + q1 * q1;
+                }
+            sk += __shfl_xor(sk, 16, 64);
+            sk += __shfl_xor(sk, 32, 64);
+            sq += __shfl_xor(sq, 16, 64);
+            sq += __shfl_xor(sq, 32, 64);
+            // rows past the chunk end (zero) keep r = 1
+            rkb[b] = 16 * b + n < len ? rnorm_f(sk) : 1.0f;
+            rqb[b] = 16 * b + n < len ? rnorm_f(sq) : 1.0f;
+        }
+    }
+    if (G == 0)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            Rk[16 * b + n] = rkb[b];
+            Rq[16 * b + n] = rqb[b];
+        }
+    if (XF && (a.k_hat || (has_q && a.q_hat))) {
+        // x r rounded to bf16, at the positions the fragments were loaded from
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            if (16 * b + n >= len) continue;
+            const int64_t rowe = (e0 + (int64_t)(16 * b + n) * H) * DK;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                u32x4 wk, wq;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    auto rb = [](uint32_t w, float r) {
+                        const float lo = __builtin_bit_cast(float, w << 16) * r, hi = __builtin_bit_cast(float, w & 0xffff0000u) * r;
+                        return (uint32_t)__builtin_bit_cast(uint16_t, (bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)hi) << 16);
+                    };
+                    wk[i] = rb(kf[b][kk][i], rkb[b]);
+                    wq[i] = rb(qf[b][kk][i], rqb[b]);
+                }
+                if (a.k_hat) *reinterpret_cast<u32x4*>(reinterpret_cast<bf16*>(a.k_hat) + rowe + 32 * kk + 8 * G) = wk;
+                if (has_q && a.q_hat) *reinterpret_cast<u32x4*>(reinterpret_cast<bf16*>(a.q_hat) + rowe + 32 * kk + 8 * G) = wq;
+            }
+        }
+    }
+
     // ---- inclusive scan of the gate (lane = token; zero past the chunk end)
     float x = gv;
 #pragma unroll
@@ -556,16 +662,26 @@ __global__ __launch_bounds__(64) void prep_kernel_h(PrepArgs a) {
         if (lane >= off) x += y;
     }
     const float xl = __shfl(x, len > 0 ? len - 1 : 0, 64);
-    const float bt = __builtin_bit_cast(float, braw << 16);
+    float bt = __builtin_bit_cast(float, braw << 16);
+    if (XF && a.beta_sig) bt = lane < len ? sigmoid_f(bt) : 0.0f;
     Gs[lane] = x;
     Bs[lane] = bt;
+    __syncthreads();   // Rk, Rq
     {
         const float bG = fpow(x, a.use_exp2), bLG = fpow(xl - x, a.use_exp2);
+        const float rk = XF ? Rk[lane] : 1.0f, rq = XF ? Rq[lane] : 1.0f;
         float* cf = reinterpret_cast<float*>(a.ws.cfh) + ch * (CFS / 4);
         const int lo = lane_order(lane);
-        cf[CS_CP + lo] = bLG;
-        cf[CS_BG + lo] = bG;
+        cf[CS_CP + lo] = bLG * rk;
+        cf[CS_BG + lo] = bG * rk;
+        cf[CS_BQ + lo] = bG * rq;
+        if (lane == 0) cf[CS_EL] = fpow(xl, a.use_exp2);
         if (a.g_cumsum && lane < len) a.g_cumsum[e0 + (int64_t)lane * H] = x;
+        if (XF && lane < len) {
+            if (a.k_rstd) a.k_rstd[e0 + (int64_t)lane * H] = rk;
+            if (has_q && a.q_rstd) a.q_rstd[e0 + (int64_t)lane * H] = rq;
+            if (a.beta_eff) reinterpret_cast<bf16*>(a.beta_eff)[e0 + (int64_t)lane * H] = (bf16)bt;
+        }
     }
     float Gi[4], Bi[4];
     f32x4 Gj[4];
@@ -606,12 +722,13 @@ __global__ __launch_bounds__(64) void prep_kernel_h(PrepArgs a) {
                 if (has_q) gq = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(f16x8, qf[I][kk]), gq, 0, 0, 0);
             }
             f32x4 pv, lv;
+            const f32x4 rkj = XF ? *reinterpret_cast<const f32x4*>(&Rk[16 * K + 4 * G]) : f32x4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const bool le = K < I || 4 * G + r <= n, lt = K < I || 4 * G + r < n;
-                const float d = le ? fpow(Gi[I] - Gj[K][r], a.use_exp2) : 0.0f;
-                pv[r] = le ? gq[r] * d : 0.0f;
-                lv[r] = lt ? Bi[I] * gk[r] * d : 0.0f;
+                const float d = le ? fpow(Gi[I] - Gj[K][r], a.use_exp2) * rkj[r] : 0.0f;
+                pv[r] = le ? gq[r] * d * rqb[I] : 0.0f;
+                lv[r] = lt ? Bi[I] * gk[r] * d * rkb[I] : 0.0f;
             }
             if (has_q) *reinterpret_cast<u32x2*>(pdst) = f32x4_to_f16x4(pv);
             if (K < I) TL[I][K] = lv;
@@ -763,6 +880,7 @@ __device__ __forceinline__ float lane_sum32(float (&v)[32], int lane) {
     return v[0] + dpp_f<0xb1>(v[0]);
 }
 
+template <bool XF>
 __global__ __launch_bounds__(256) void prep_kernel_pk(PrepArgs a) {
     // ka: the A form of k for L, then that of q for P, then T (fp32 64 x 65);
     // kb: the B form of k, then the partial products of the inverse; Ls: the
@@ -811,7 +929,9 @@ __global__ __launch_bounds__(256) void prep_kernel_pk(PrepArgs a) {
         qr[r] = __builtin_amdgcn_raw_buffer_load_b32(rq, row * rowk + 4 * lane, 0, 0);
     }
     if (tid < BT) {
-        const float bt = tid < len ? (float)reinterpret_cast<const bf16*>(a.beta)[(t0 + tid) * H + head] : 0.0f;
+        float bt = tid < len ? (float)reinterpret_cast<const bf16*>(a.beta)[(t0 + tid) * H + head] : 0.0f;
+        if (XF && a.beta_sig && tid < len) bt = sigmoid_f(bt);
+        if (XF && a.beta_eff && tid < len) reinterpret_cast<bf16*>(a.beta_eff)[(t0 + tid) * H + head] = (bf16)bt;
         bet[tid] = bt;
         f16* cf = reinterpret_cast<f16*>(a.ws.cfh) + ch * (CFB / 2);
         const int lo = lane_order(tid);
@@ -819,6 +939,46 @@ __global__ __launch_bounds__(256) void prep_kernel_pk(PrepArgs a) {
         cf[CF_CP + lo] = (f16)1.0f;
         cf[CF_BG + lo] = (f16)1.0f;
         cf[CF_BETA + lo] = (f16)bt;
+    }
+
+    // ---- q / k normalisation: the reciprocal norm r of each of the wave's
+    // rows (uniform), from one 64-lane reduction of all 32 sums of squares;
+    // optional slots of the transformed rows
+    float nk[16], nq[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { nk[r] = 1.0f; nq[r] = 1.0f; }
+    if (XF && a.qk_norm) {
+        float v[32];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float k0 = __builtin_bit_cast(float, kr[r] << 16), k1 = __builtin_bit_cast(float, kr[r] & 0xffff0000u);
+            const float q0 = __builtin_bit_cast(float, qr[r] << 16), q1 = __builtin_bit_cast(float, qr[r] & 0xffff0000u);
+            v[r] = k0 * k0 + k1 * k1;
+            v[16 + r] = q0 * q0 + q1 * q1;
+        }
+        const float s = lane_sum32(v, lane);   // sum m in lanes 2m, 2m + 1
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (16 * w + r < len) {
+                nk[r] = rnorm_f(u2f(__builtin_amdgcn_readlane(f2u(s), 2 * r)));
+                nq[r] = rnorm_f(u2f(__builtin_amdgcn_readlane(f2u(s), 32 + 2 * r)));
+            }
+    }
+    if (XF && (a.k_hat || a.q_hat || a.k_rstd || a.q_rstd)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = 16 * w + r;
+            if (row >= len) continue;
+            const int64_t re = e0 + (int64_t)row * H;
+            auto rb = [](uint32_t x, float f) {
+                const float lo = __builtin_bit_cast(float, x << 16) * f, hi = __builtin_bit_cast(float, x & 0xffff0000u) * f;
+                return (uint32_t)__builtin_bit_cast(uint16_t, (bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)hi) << 16);
+            };
+            if (a.k_hat) reinterpret_cast<uint32_t*>(reinterpret_cast<bf16*>(a.k_hat) + re * DK)[lane] = rb(kr[r], nk[r]);
+            if (has_q && a.q_hat) reinterpret_cast<uint32_t*>(reinterpret_cast<bf16*>(a.q_hat) + re * DK)[lane] = rb(qr[r], nq[r]);
+            if (lane == 0 && a.k_rstd) a.k_rstd[re] = nk[r];
+            if (lane == 0 && has_q && a.q_rstd) a.q_rstd[re] = nq[r];
+        }
     }
 
     // ---- cumulative gate down each key column
@@ -889,12 +1049,12 @@ __global__ __launch_bounds__(256) void prep_kernel_pk(PrepArgs a) {
             float v[32];
 #pragma unroll
             for (int m = 0; m < 32; ++m) v[m] = 0.0f;
-            const float ki0 = __builtin_bit_cast(float, kr[i] << 16), ki1 = __builtin_bit_cast(float, kr[i] & 0xffff0000u);
-            const float qi0 = __builtin_bit_cast(float, qr[i] << 16), qi1 = __builtin_bit_cast(float, qr[i] & 0xffff0000u);
+            const float ki0 = __builtin_bit_cast(float, kr[i] << 16) * nk[i], ki1 = __builtin_bit_cast(float, kr[i] & 0xffff0000u) * nk[i];
+            const float qi0 = __builtin_bit_cast(float, qr[i] << 16) * nq[i], qi1 = __builtin_bit_cast(float, qr[i] & 0xffff0000u) * nq[i];
 #pragma unroll
             for (int j = 0; j <= i; ++j) {
-                const float kj0 = __builtin_bit_cast(float, kr[j] << 16) * fpow(gc[i][0] - gc[j][0], a.use_exp2);
-                const float kj1 = __builtin_bit_cast(float, kr[j] & 0xffff0000u) * fpow(gc[i][1] - gc[j][1], a.use_exp2);
+                const float kj0 = __builtin_bit_cast(float, kr[j] << 16) * nk[j] * fpow(gc[i][0] - gc[j][0], a.use_exp2);
+                const float kj1 = __builtin_bit_cast(float, kr[j] & 0xffff0000u) * nk[j] * fpow(gc[i][1] - gc[j][1], a.use_exp2);
                 if (j < i) v[j] = ki0 * kj0 + ki1 * kj1;
                 v[16 + j] = qi0 * kj0 + qi1 * kj1;
             }
@@ -914,8 +1074,8 @@ __global__ __launch_bounds__(256) void prep_kernel_pk(PrepArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int row = 16 * w + r;
-            const float k0 = __builtin_bit_cast(float, kr[r] << 16), k1 = __builtin_bit_cast(float, kr[r] & 0xffff0000u);
-            const float q0 = __builtin_bit_cast(float, qr[r] << 16), q1 = __builtin_bit_cast(float, qr[r] & 0xffff0000u);
+            const float k0 = __builtin_bit_cast(float, kr[r] << 16) * nk[r], k1 = __builtin_bit_cast(float, kr[r] & 0xffff0000u) * nk[r];
+            const float q0 = __builtin_bit_cast(float, qr[r] << 16) * nq[r], q1 = __builtin_bit_cast(float, qr[r] & 0xffff0000u) * nq[r];
             const float eA0 = fpow(gc[r][0] - p0, a.use_exp2), eA1 = fpow(gc[r][1] - p1, a.use_exp2);
             const float eB0 = fpow(r0 - gc[r][0], a.use_exp2), eB1 = fpow(r1 - gc[r][1], a.use_exp2);
             const float ka0 = k0 * eA0, ka1 = k1 * eA1, qa0 = q0 * eA0, qa1 = q1 * eA1;
@@ -1100,6 +1260,8 @@ struct StateArgs {
     float* S_ext;
     float* M;
     const int32_t* order;   // units in launch order (longest first), or NULL: natural order
+    float* vnew;            // optional slot: v_new, fp32 [tokens][H][V]
+    int beta_sig;           // beta through a sigmoid (the fp32 pass, which reads beta itself)
 };
 
 // Work split of the 8 waves of a state-pass workgroup (one 32-column value
@@ -1127,7 +1289,7 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
     __shared__ __attribute__((aligned(16))) Op YT[BV * LDY];
     __shared__ __attribute__((aligned(16))) Op vnT[OUT ? BV * LDY : 8];
     __shared__ __attribute__((aligned(16))) Op vpT[BV * LDY];
-    __shared__ __attribute__((aligned(16))) float gam[2][4 * BT];                // G, b^G, b^{G_L-G}, b^{G_L}
+    __shared__ __attribute__((aligned(16))) float gam[2][GAMR * BT];             // G, b^G r_k, b^{G_L-G} r_k, b^{G_L}, b^G r_q
     __shared__ __attribute__((aligned(16))) float bet[2][BT];
     __shared__ __attribute__((aligned(16))) float gl[2][PERKEY ? DK : 4];
 
@@ -1178,7 +1340,7 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
     // T is the identity on padded rows, and padded output rows are not stored.
     constexpr int VPR = 16 / sizeof(In);
     constexpr int NKV = BT * DK / VPR / ST;           // 16-byte vectors per thread of a 64 x 128 tile
-    constexpr int NGW = PERKEY ? DK : 4 * BT;         // gate words per chunk
+    constexpr int NGW = PERKEY ? DK : GAMR * BT;      // gate words per chunk
     constexpr int RQ = 4 * FV;                        // q registers: the wave's rows
     constexpr int RT = 2 * FV;                        // T / P registers: the wave's rows
     auto chunk_len = [&](int c) { int l = ui.len - c * BT; return l < 0 ? 0 : (l > BT ? BT : l); };
@@ -1224,7 +1386,7 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
                 tile_rc(i, r, cv);
                 x.k[i] = *reinterpret_cast<const f32x4*>(kb + (uint32_t)min(r, last) * tokstride + cv);
             }
-            x.gb = tid < NGW ? a.ws.gam[ch * (4 * BT) + tid] : 0.0f;
+            x.gb = tid < NGW ? a.ws.gam[ch * (GAMR * BT) + tid] : 0.0f;
         }
         if (OUT) {
             const Op* qg = reinterpret_cast<const Op*>(a.ws.qg) + ch * (BT * DK);
@@ -1258,7 +1420,7 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
             if (PERKEY) gl[b][tid] = x.gb;
             else gam[b][tid] = x.gb;
         }
-        if (tid < BT) bet[b][tid] = tid < x.len ? P::f(x.bt) : 0.0f;
+        if (tid < BT) bet[b][tid] = tid < x.len ? (a.beta_sig ? sigmoid_f(P::f(x.bt)) : P::f(x.bt)) : 0.0f;
     };
     // the per-key gated k of a chunk (read only after its step's first barrier)
     auto publish_late = [&](const Raw& x) {
@@ -1324,8 +1486,10 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
             P::st4(&YT[(16 * cg + n) * LDY + 16 * rg + 4 * G], y);
         }
         f32x4 oacc;
-        if (OUT)
-            for (int r = 0; r < 4; ++r) oacc[r] = eG[r] * qh[r];
+        if (OUT) {
+            const f32x4 eQ = PERKEY ? f32x4{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const f32x4*>(&gm[4 * BT + 16 * rg + 4 * G]);
+            for (int r = 0; r < 4; ++r) oacc[r] = eQ[r] * qh[r];
+        }
         __syncthreads();
 
         // ---- v_new = T Y for rows 16rg .. 16rg+15
@@ -1334,6 +1498,11 @@ __global__ __launch_bounds__(ST) void state_kernel(StateArgs a) {
             if (kk < nkw) {
                 const F ta = P::frag(&cur.T[FV * kk]);
                 P::mma(vn, ta, P::ld(&YT[(16 * cg + n) * LDY + 32 * kk + 8 * G]));
+            }
+        if (OUT && a.vnew)
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * rg + 4 * G + r;
+                if (i < len) a.vnew[((t0 + i) * H + head) * DV + col] = vn[r];
             }
         {
             float x[4], xp[4];
@@ -1562,7 +1731,7 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
                     cpf[it] = *reinterpret_cast<const f32x4*>(&cf[CS_CP + 16 * G + 4 * it]);
                     bg[it] = *reinterpret_cast<const f32x4*>(&cf[CS_BG + 16 * G + 4 * it]);
                 }
-                eL = cf[CS_BG + lane_order(len > 0 ? len - 1 : 0)];
+                eL = cf[CS_EL];
             } else {
                 const f16* cbh = reinterpret_cast<const f16*>(cf);
                 for (int it = 0; it < 4; ++it) {
@@ -1609,6 +1778,16 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
             }
             const F yb1 = pack(y[2], y[3]);
             for (int it = 2; it < 4; ++it) PolicyH::mma(vn[it], ldA(Tc, offT[1] + it * 16 * 128), yb1);
+            if (OUT && a.vnew) {
+                // v_new of this wave's output rows (the partner stores the other half)
+                for (int j = 0; j < 2; ++j) {
+                    const int it = 2 * kq + j;
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = 16 * it + 4 * G + r;
+                        if (i < len) a.vnew[((t0 + i) * H + head) * DV + col] = vn[it][r];
+                    }
+                }
+            }
             for (int it = 2; it < 4; ++it)
                 for (int r = 0; r < 4; ++r) vp[it][r] = PK ? vn[it][r] : vn[it][r] * cpf[it][r];
             const F vb1 = pack(vp[2], vp[3]);
@@ -1621,7 +1800,12 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
                     f32x4 qh = {0.f, 0.f, 0.f, 0.f};
                     for (int s2 = 0; s2 < 4; ++s2) PolicyH::mma(qh, ldA(Q, offA[s2] + it * 16 * 256), hb[s2]);
                     f32x4 o;
-                    for (int r = 0; r < 4; ++r) o[r] = PK ? qh[r] : bg[it][r] * qh[r];   // per key: q b^G is prepared
+                    if (PK) {
+                        o = qh;                              // per key: q b^G is prepared
+                    } else {
+                        const f32x4 bq = *reinterpret_cast<const f32x4*>(&cf[CS_BQ + 16 * G + 4 * it]);
+                        for (int r = 0; r < 4; ++r) o[r] = bq[r] * qh[r];
+                    }
                     PolicyH::mma(o, ldA(Pc, offT[0] + it * 16 * 128), nb0);
                     if (kq == 1) PolicyH::mma(o, ldA(Pc, offT[1] + it * 16 * 128), nb1);
                     if (OXS) {
@@ -1734,9 +1918,9 @@ __global__ __launch_bounds__(KST) void state_kernel_ks(StateArgs a) {
                 d.x[12] = __builtin_amdgcn_raw_buffer_load_b128(rv, (16 * role + (lane >> 2)) * rowb + 16 * (lane & 3), 0, 0);
                 if (role == 0) {
                     const rsrc_t rc = make_rsrc(reinterpret_cast<const char*>(a.ws.cfh) + ch * CFS, CFS);
-                    // used: scalar gate floats 64..191; per key the beta row
-                    // (bytes 384..511) and the fp32 b^{G_L} (bytes 512..1023)
-                    const bool used = PK ? lane >= 24 : (lane >= 16 && lane < 48);
+                    // used: scalar gate float 0 and floats 64..255; per key the
+                    // beta row (bytes 384..511) and the fp32 b^{G_L} (bytes 512..1023)
+                    const bool used = PK ? lane >= 24 : (lane == 0 || lane >= 16);
                     d.x[13] = __builtin_amdgcn_raw_buffer_load_b128(rc, used ? 16u * lane : 0x40000000u, 0, 0);
                 }
             };
@@ -2016,16 +2200,23 @@ __global__ __launch_bounds__(ORD_T) void unit_order_kernel(UnitMap um, int32_t* 
 
 // ------------------------------------------------------------------ launchers
 hipError_t launch_prep(const Problem& p, const Workspace& ws, const void* k, const void* q,
-                       const float* g, const void* beta, float* g_cumsum_slot, float* A_slot,
-                       hipStream_t s) {
+                       const float* g, const void* beta, const PrepSlots& sl, hipStream_t s) {
     if (p.um.n_chunks == 0) return hipSuccess;
     PrepArgs a;
     a.um = p.um; a.H = p.H; a.k = k; a.q = q; a.g = g; a.beta = beta; a.use_exp2 = p.use_exp2;
-    a.ws = ws; a.g_cumsum = g_cumsum_slot; a.A = A_slot;
+    a.ws = ws; a.g_cumsum = sl.g_cumsum; a.A = sl.A;
+    a.qk_norm = p.qk_norm; a.beta_sig = p.beta_sig;
+    a.q_hat = sl.q_hat; a.k_hat = sl.k_hat; a.q_rstd = sl.q_rstd; a.k_rstd = sl.k_rstd; a.beta_eff = sl.beta_eff;
     dim3 grid(p.um.n_chunks, p.H), block(256);
+    const bool xf = a.qk_norm || a.beta_sig || a.q_hat || a.k_hat || a.q_rstd || a.k_rstd || a.beta_eff;
     if (p.dtype == 1) {
-        if (p.per_key) hipLaunchKernelGGL(prep_kernel_pk, grid, block, 0, s, a);
-        else hipLaunchKernelGGL(prep_kernel_h, dim3(p.H * p.um.n_chunks), dim3(64), 0, s, a);
+        if (p.per_key) {
+            if (xf) hipLaunchKernelGGL(prep_kernel_pk<true>, grid, block, 0, s, a);
+            else hipLaunchKernelGGL(prep_kernel_pk<false>, grid, block, 0, s, a);
+        } else {
+            if (xf) hipLaunchKernelGGL(prep_kernel_h<true>, dim3(p.H * p.um.n_chunks), dim3(64), 0, s, a);
+            else hipLaunchKernelGGL(prep_kernel_h<false>, dim3(p.H * p.um.n_chunks), dim3(64), 0, s, a);
+        }
     } else {
         if (p.per_key) hipLaunchKernelGGL((prep_kernel<PolicyF, true>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((prep_kernel<PolicyF, false>), grid, block, 0, s, a);
@@ -2041,6 +2232,8 @@ hipError_t launch_prep_f32(const Problem& p, const Workspace& ws, const void* k,
     PrepArgs a;
     a.um = p.um; a.H = p.H; a.k = k; a.q = q; a.g = g; a.beta = beta; a.use_exp2 = p.use_exp2;
     a.ws = ws; a.g_cumsum = nullptr; a.A = nullptr;
+    a.qk_norm = 0; a.beta_sig = 0;
+    a.q_hat = nullptr; a.k_hat = nullptr; a.q_rstd = nullptr; a.k_rstd = nullptr; a.beta_eff = nullptr;
     dim3 grid(p.um.n_chunks, p.H), block(256);
     if (p.dtype == 1) hipLaunchKernelGGL((prep_kernel<PolicyFB, false>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((prep_kernel<PolicyF, false>), grid, block, 0, s, a);
@@ -2082,9 +2275,11 @@ static void launch_state_h(bool summary, StateArgs a, int want_ext, int want_M, 
 
 hipError_t launch_state(const Problem& p, const Workspace& ws, const void* q, const void* k,
                         const void* v, const void* beta, const float* h0, void* o, float* hfinal,
-                        float* hslot, int summary, int want_ext, int want_M, float* S_ext,
+                        float* hslot, float* vnew_slot, int summary, int want_ext, int want_M, float* S_ext,
                         float* M, const int32_t* units_sel, int n_sel, hipStream_t s) {
     StateArgs a;
+    a.vnew = summary ? nullptr : vnew_slot;
+    a.beta_sig = p.beta_sig;
     a.um = p.um; a.H = p.H; a.q = q; a.k = k; a.v = v; a.beta = beta; a.ws = ws;
     a.h0 = h0; a.o = o; a.o_bf16 = p.o_dtype == 1; a.hfinal = hfinal; a.hslot = hslot;
     a.scale = p.scale; a.use_exp2 = p.use_exp2;

@@ -62,7 +62,9 @@ def doc_lengths(n_docs: int, total: int, lo: int, hi: int, seed: int) -> list[in
     ``total``, clamped to [lo, hi], the residual spread +-1 cyclically in index
     order (skipping documents at a bound). Redrawn with seed + 1 until at
     least three quarters of the lengths are not multiples of 64."""
-    while True:
+    if n_docs < 1 or n_docs * lo > total or n_docs * hi < total:
+        raise ValueError(f"{n_docs} documents of {lo}..{hi} tokens cannot sum to {total}")
+    for _ in range(1000):
         gen = torch.Generator("cpu").manual_seed(seed)
         raw = torch.randint(lo, hi + 1, (n_docs,), generator=gen).tolist()
         s = sum(raw)
@@ -80,6 +82,7 @@ def doc_lengths(n_docs: int, total: int, lo: int, hi: int, seed: int) -> list[in
         if resid == 0 and sum(x % 64 != 0 for x in lens) * 4 >= 3 * n_docs:
             return lens
         seed += 1
+    raise ValueError(f"no seeded draw of {n_docs} document lengths fits {total} tokens")
 
 
 def cu_from_lengths(lens) -> list[int]:

@@ -80,7 +80,15 @@ enum {
                                     holds it (from gdn_state_summary or a
                                     GDN_FLAG_PREPARE_ONLY call with the same
                                     descriptor and inputs) */
-    GDN_FLAG_PREPARE_ONLY = 2    /* run chunk preparation only */
+    GDN_FLAG_PREPARE_ONLY = 2,   /* run chunk preparation only */
+    /* In-kernel input transforms (use_qk_l2norm_in_kernel and
+     * use_beta_sigmoid_in_kernel of the native prepare on the Diff Coverage
+     * page), also accepted by gdn_state_summary and gdn_chunk_fwd_noalloc.
+     * A call with GDN_FLAG_REUSE_PREPARED must repeat the transform flags of
+     * the preparing call. */
+    GDN_FLAG_QK_L2NORM = 4,      /* q and k replaced by x r, r = 1 / sqrt(sum_i x_i^2 + 1e-6),
+                                    per (token, head), in fp32 */
+    GDN_FLAG_BETA_SIGMOID = 8    /* beta replaced by 1 / (1 + e^{-beta}) */
 };
 
 /*
@@ -116,8 +124,12 @@ typedef struct {
 
 /*
  * Optional extra outputs of gdn_chunk_fwd (any pointer may be NULL; the
- * struct pointer itself may be NULL). These are the saved-for-backward slots
- * of the native forward on the Diff Coverage page (g_cumsum, A, h).
+ * struct pointer itself may be NULL). These are slots of the native forward
+ * on the Diff Coverage page: the saved-for-backward g_cumsum, A and h of its
+ * ten-slot result, the v_new that chunk_fwd_h returns, and the input-transform
+ * slots q_hat, k_hat, q_rstd, k_rstd and beta_eff. The preparation writes
+ * g_cumsum, A and the transform slots (not under GDN_FLAG_REUSE_PREPARED);
+ * the state pass writes h and v_new (not under GDN_FLAG_PREPARE_ONLY).
  *   g_cumsum: device fp32, token-major like g ([tokens][H] or
  *             [tokens][H][K]): the gate's inclusive cumulative sum inside
  *             each 64-token chunk of each unit.
@@ -127,11 +139,28 @@ typedef struct {
  *             the WY inverse that turns the chunk into dense products.
  *   h:        device fp32 [n_chunks][H][K][V]: the state entering every
  *             chunk (chunks ordered by unit, then position in the unit).
+ *   v_new:    device fp32 [tokens][H][V]: the value each token writes into
+ *             the state, v_new = u - w h = T diag(beta) (v - (k * b^G) h) for
+ *             the chunk's entry state h; token by token this is
+ *             beta_t (v_t - h~^T k_t), h~ the decayed state before token t.
+ *   q_hat, k_hat: device [tokens][H][K] in desc->dtype: q and k as the
+ *             recurrence uses them (normalised with GDN_FLAG_QK_L2NORM,
+ *             else copies), rounded to the input precision.
+ *   q_rstd, k_rstd: device fp32 [tokens][H]: the factor r of the
+ *             normalisation (1 without it). q_hat and q_rstd need q.
+ *   beta_eff: device [tokens][H] in desc->dtype: beta as the recurrence
+ *             uses it (after the sigmoid with GDN_FLAG_BETA_SIGMOID).
  */
 typedef struct {
     float* g_cumsum;
     float* A;
     float* h;
+    float* v_new;
+    void* q_hat;
+    void* k_hat;
+    float* q_rstd;
+    float* k_rstd;
+    void* beta_eff;
 } gdn_slots;
 
 /*

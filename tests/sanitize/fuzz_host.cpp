@@ -112,7 +112,7 @@ void fuzz_fwd() {
     void* ws = aligned_alloc(256, (have + 255) / 256 * 256 + 256);
     stub_set_workspace(ws, have);
     size_t nb = have;
-    const int flags = pick({0, 0, 1, 2, 3, 8});
+    const int flags = pick({0, 0, 1, 2, 3, 4, 8, 12, 16});
     void* q = uni(0, 9) ? FAKE : nullptr;
     tally(gdn_chunk_fwd(&d, q, FAKE, FAKE, (const float*)FAKE, FAKE, nullptr, FAKE, nullptr, nullptr, flags,
                         uni(0, 9) ? ws : static_cast<char*>(ws) + 64, &nb, nullptr));

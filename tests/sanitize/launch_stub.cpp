@@ -30,7 +30,7 @@ void check_problem(const gdn::Problem& p, const gdn::Workspace& ws) {
     if (p.H < 1 || p.um.n_units < 0 || p.um.n_chunks < 0) fail("problem");
     region(ws.Tm, nch * 64 * 64 * es, "T region");
     region(ws.P, nch * 64 * 64 * es, "P region");
-    region(ws.gam, nch * 4 * 64 * 4, "gate rows");
+    region(ws.gam, nch * gdn::GAMR * 64 * 4, "gate rows");
     region(ws.qg, nch * 64 * 128 * es, "q b^G region");
     region(ws.kd, nch * 64 * 128 * es, "k b^G region");
     region(ws.kg, nch * 64 * 128 * es, "k b^(G_L - G) region");
@@ -49,14 +49,14 @@ void stub_set_workspace(const void* base, size_t bytes) {
 namespace gdn {
 
 hipError_t launch_prep(const Problem& p, const Workspace& ws, const void* k, const void*, const float* g,
-                       const void* beta, float*, float*, hipStream_t) {
+                       const void* beta, const PrepSlots&, hipStream_t) {
     check_problem(p, ws);
     if (p.um.total_tokens > 0 && (!k || !g || !beta)) fail("prep inputs");
     return hipSuccess;
 }
 
 hipError_t launch_state(const Problem& p, const Workspace& ws, const void*, const void* k, const void*,
-                        const void*, const float*, void*, float*, float*, int summary, int want_ext, int want_M,
+                        const void*, const float*, void*, float*, float*, float*, int summary, int want_ext, int want_M,
                         float* S_ext, float* M, const int32_t* units_sel, int n_sel, hipStream_t) {
     check_problem(p, ws);
     if (p.um.total_tokens > 0 && !k) fail("state inputs");

@@ -172,7 +172,8 @@ def test_missing_tensors(missing):
 
 def test_flag_errors():
     assert fwd(desc(), flags=3)[0] == gb.GDN_ERR_INVALID
-    assert fwd(desc(), flags=8)[0] == gb.GDN_ERR_INVALID
+    assert fwd(desc(), flags=16)[0] == gb.GDN_ERR_INVALID
+    assert fwd(desc(), flags=3 | 4)[0] == gb.GDN_ERR_INVALID
 
 
 def test_summary_and_merge_errors():
@@ -189,7 +190,7 @@ def test_summary_and_merge_errors():
     assert summ(mode=2, m=None) == gb.GDN_ERR_INVALID
     # flags other than REUSE_PREPARED; more units selected than exist; a
     # selection without its list
-    for fl in (2, 3, 8):
+    for fl in (2, 3, 16, 2 | 4):
         assert summ(flags=fl) == gb.GDN_ERR_INVALID
     assert summ(units=FAKE, n_sel=5) == gb.GDN_ERR_INVALID     # 4 units
     assert summ(units=None, n_sel=2) == gb.GDN_ERR_INVALID
@@ -284,11 +285,11 @@ def bwd(d, *, ws=FAKE, nbytes=None, ptrs=None):
 
 def test_backward_host_checks():
     st, need = bwd(desc(), ws=None)
-    # fp32 preparation (T, P, gate rows), dL/dh at each chunk exit and dvn,
+    # fp32 preparation (T, P, five gate rows), dL/dh at each chunk exit and dvn,
     # every region 256-byte aligned
     nch = 2 * 4 * 3
     a256 = lambda x: ((x + 255) // 256) * 256
-    prep = 2 * a256(nch * 64 * 64 * 4) + a256(nch * 4 * 64 * 4)
+    prep = 2 * a256(nch * 64 * 64 * 4) + a256(nch * 5 * 64 * 4)
     assert st == gb.GDN_OK and need == a256(prep + nch * 128 * 128 * 4) + a256(nch * 64 * 128 * 4)
     assert bwd(desc(gate_kind=1), ws=None)[0] == gb.GDN_ERR_UNSUPPORTED
     assert bwd(desc(chunk_size=32), ws=None)[0] == gb.GDN_ERR_INVALID
