@@ -72,6 +72,10 @@ def lib():
         L.gdn_split_meta.restype = ctypes.c_int
         L.gdn_split_meta.argtypes = [_i32p, ctypes.c_int32, _i32p, ctypes.c_int32, ctypes.c_int32, _i32p,
                                      _i32p, _i32p, ctypes.c_int32, _i32p]
+        L.gdn_state_grad_summary.restype = ctypes.c_int
+        L.gdn_state_grad_summary.argtypes = [ctypes.POINTER(GdnDesc)] + [vp] * 8 + [vp, sz, vp]
+        L.gdn_state_merge_adjoint.restype = ctypes.c_int
+        L.gdn_state_merge_adjoint.argtypes = [ctypes.c_int32] * 5 + [vp] * 6
         L.gdn_state_merge_pieces.restype = ctypes.c_int
         L.gdn_state_merge_pieces.argtypes = [ctypes.c_int32] * 5 + [vp, vp, vp, vp, vp, vp]
         L.gdn_state_merge.restype = ctypes.c_int
@@ -504,6 +508,74 @@ def gdn_chunk_bwd(q, k, v, g, beta, h, dout, scale=None, *, meta: UnitMeta | Non
                               _ptr(dout), _ptr(dht), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
                               _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out.get("dh0")), _ptr(ws),
                               ctypes.byref(nbytes), _stream(dev)), "gdn_chunk_bwd")
+    return out
+
+
+def gdn_state_grad_summary(q, k, v, g, beta, h, dout, scale=None, *, meta: UnitMeta, use_exp2=False,
+                           workspace=None):
+    """dS_ext [units,H,K,V]: dL/d(entry state) of every unit through its own
+    outputs only (zero gradient at its exit); arguments as gdn_chunk_bwd."""
+    H, per_key = _check_inputs(q, k, v, g, beta, meta, device_check=False)
+    if per_key:
+        raise NotImplementedError("the gradient summary supports the scalar gate")
+    if scale is None:
+        scale = k.shape[-1] ** -0.5
+    desc = _desc(k, H, k.dtype, k.dtype, False, use_exp2, scale, meta)
+    dev = k.device
+    K, V = k.shape[-1], v.shape[-1]
+    _check_tensor("h", h, torch.float32, (meta.n_chunks, H, K, V), dev)
+    _check_tensor("dout", dout, k.dtype, v.shape, dev)
+    _require_gpu(q, k, v, g, beta, meta)
+    dS = torch.empty((n_units_of(k, meta), H, K, V), dtype=torch.float32, device=dev)
+    nb = ctypes.c_size_t(0)
+    check(lib().gdn_state_grad_summary(ctypes.byref(desc), *([None] * 9), ctypes.byref(nb), None), "workspace query")
+    ws = workspace if workspace is not None else torch.empty(nb.value, dtype=torch.uint8, device=dev)
+    if ws.dtype != torch.uint8 or ws.device != dev or ws.numel() < nb.value:
+        raise ValueError(f"workspace must be a uint8 tensor of at least {nb.value} bytes on {dev}")
+    nbytes = ctypes.c_size_t(ws.numel())
+    check(lib().gdn_state_grad_summary(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h),
+                                       _ptr(dout), _ptr(dS), _ptr(ws), ctypes.byref(nbytes), _stream(dev)),
+          "gdn_state_grad_summary")
+    return dS
+
+
+def gdn_state_merge_adjoint(dS_ext, M, dS_final=None, *, B: int, n_seg: int, want_dS0=True):
+    """dS_ext [B*n_seg,H,K,V], M [B*n_seg,H,K,K] (units row-major) ->
+    dS_exit [B*n_seg,H,K,V] (the gradient arriving at each segment's exit)
+    and dS0 [B,H,K,V] (at the first segment's entry) or None."""
+    if dS_ext.dim() != 4:
+        raise ValueError("dS_ext must be [B*n_seg, H, K, V]")
+    H, K, V = dS_ext.shape[1], dS_ext.shape[2], dS_ext.shape[3]
+    dev = dS_ext.device
+    if dev.type != "cuda":
+        raise ValueError(f"summaries must be GPU tensors, got {dev}")
+    _check_tensor("dS_ext", dS_ext, torch.float32, (B * n_seg, H, K, V), dev)
+    _check_tensor("M", M, torch.float32, (B * n_seg, H, K, K), dev)
+    if dS_final is not None:
+        _check_tensor("dS_final", dS_final, torch.float32, (B, H, K, V), dev)
+    dS_exit = torch.empty_like(dS_ext)
+    dS0 = torch.empty((B, H, K, V), dtype=torch.float32, device=dev) if want_dS0 else None
+    check(lib().gdn_state_merge_adjoint(B, H, n_seg, K, V, _ptr(dS_ext), _ptr(M), _ptr(dS_final), _ptr(dS_exit),
+                                        _ptr(dS0), _stream(dev)), "gdn_state_merge_adjoint")
+    return dS_exit, dS0
+
+
+def split_backward(q, k, v, g, beta, h, dout, scale=None, *, seg, M, use_exp2=False, dht=None):
+    """Backward of a sequence split of BSND rows (seg: in-row offsets) on one
+    GPU, in the order of the reverse wavefront: every segment's gradient
+    summary, the adjoint merge with the transfer maps M [B*n_seg,H,K,K] of
+    the forward's summaries, then every segment's backward from its true
+    exit gradient. h: the correction forward's chunk entry states over the
+    segments. Returns gdn_chunk_bwd's dict, dh0 being dL/d(initial state)
+    per row [B,H,K,V]."""
+    B, T = k.shape[0], k.shape[1]
+    n_seg = len(seg) - 1
+    meta = make_meta(segment_offsets(B, T, seg), B * T, k.device)
+    dS_ext = gdn_state_grad_summary(q, k, v, g, beta, h, dout, scale, meta=meta, use_exp2=use_exp2)
+    dS_exit, dS0 = gdn_state_merge_adjoint(dS_ext, M, dht, B=B, n_seg=n_seg)
+    out = gdn_chunk_bwd(q, k, v, g, beta, h, dout, scale, meta=meta, dht=dS_exit, use_exp2=use_exp2,
+                        want_dh0=False)
+    out["dh0"] = dS0
     return out
 
 

@@ -500,7 +500,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
 hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* dVN, const void* q, const void* k,
                       const void* v, const float* g, const void* beta, const float* h, const void* dout,
                       const float* dht, float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0,
-                      hipStream_t s) {
+                      bool dh_only, hipStream_t s) {
     if (launch_prep_f32(p, ws, k, q, g, beta, s) != hipSuccess) return hipGetLastError();
     BwdArgs a;
     a.um = p.um; a.H = p.H; a.use_exp2 = p.use_exp2; a.scale = p.scale;
@@ -512,7 +512,7 @@ hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* d
         if (p.dtype == 1) hipLaunchKernelGGL(bwd_dh_kernel<bf16>, dim3(4 * a.n_pairs), dim3(256), 0, s, a);
         else hipLaunchKernelGGL(bwd_dh_kernel<float>, dim3(4 * a.n_pairs), dim3(256), 0, s, a);
     }
-    if (p.um.n_chunks > 0) {
+    if (p.um.n_chunks > 0 && !dh_only) {
         dim3 grid(p.um.n_chunks, p.H);
         if (p.dtype == 1) hipLaunchKernelGGL(bwd_grad_kernel<bf16>, grid, dim3(256), 0, s, a);
         else hipLaunchKernelGGL(bwd_grad_kernel<float>, grid, dim3(256), 0, s, a);

@@ -366,8 +366,50 @@ extern "C" gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const v
     gdn::Workspace ws;
     float *dH = nullptr, *dVN = nullptr;
     bwd_workspace(p, &ws, &dH, &dVN, static_cast<char*>(workspace));
-    if (gdn::launch_bwd(p, ws, dH, dVN, q, k, v, g, beta, h, dout, dht, dq, dk, dv, dg, dbeta, dh0, stream) !=
-        hipSuccess)
+    if (gdn::launch_bwd(p, ws, dH, dVN, q, k, v, g, beta, h, dout, dht, dq, dk, dv, dg, dbeta, dh0, false,
+                        stream) != hipSuccess)
+        return GDN_ERR_DEVICE;
+    return GDN_OK;
+}
+
+extern "C" gdn_status gdn_state_grad_summary(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                                             const float* g, const void* beta, const float* h, const void* dout,
+                                             float* dS_ext, void* workspace, size_t* workspace_bytes,
+                                             hipStream_t stream) {
+    gdn::Problem p;
+    gdn_status st = validate(desc, &p);
+    if (st != GDN_OK) return st;
+    if (p.per_key) return GDN_ERR_UNSUPPORTED;
+    if (workspace_bytes == nullptr) return GDN_ERR_INVALID;
+    const size_t need = bwd_workspace(p, nullptr, nullptr, nullptr, nullptr);
+    if (workspace == nullptr) {
+        *workspace_bytes = need;
+        return GDN_OK;
+    }
+    if (*workspace_bytes < need) {
+        *workspace_bytes = need;
+        return GDN_ERR_CAPACITY;
+    }
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return GDN_ERR_INVALID;
+    if (!dS_ext) return GDN_ERR_INVALID;
+    if (p.um.total_tokens > 0 && (!q || !k || !v || !g || !beta || !h || !dout)) return GDN_ERR_INVALID;
+    gdn::Workspace ws;
+    float *dH = nullptr, *dVN = nullptr;
+    bwd_workspace(p, &ws, &dH, &dVN, static_cast<char*>(workspace));
+    if (gdn::launch_bwd(p, ws, dH, dVN, q, k, v, g, beta, h, dout, nullptr, nullptr, nullptr, nullptr, nullptr,
+                        nullptr, dS_ext, true, stream) != hipSuccess)
+        return GDN_ERR_DEVICE;
+    return GDN_OK;
+}
+
+extern "C" gdn_status gdn_state_merge_adjoint(int32_t B, int32_t H, int32_t n_seg, int32_t K, int32_t V,
+                                              const float* dS_ext, const float* M, const float* dS_final,
+                                              float* dS_exit, float* dS0, hipStream_t stream) {
+    if (K != DK || V != DV) return GDN_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || n_seg < 0) return GDN_ERR_INVALID;
+    if (int64_t(B) * H * n_seg * DK * DK > kMaxElems) return GDN_ERR_INVALID;
+    if (n_seg > 0 && (!dS_ext || !M || !dS_exit)) return GDN_ERR_INVALID;
+    if (gdn::launch_merge_adjoint(B, H, n_seg, dS_ext, M, dS_final, dS_exit, dS0, stream) != hipSuccess)
         return GDN_ERR_DEVICE;
     return GDN_OK;
 }

@@ -96,6 +96,9 @@ hipError_t launch_merge_pieces(int n_pieces, int n_docs, int H, const int32_t* p
 hipError_t launch_merge(int B, int H, int n_seg, const float* S_ext, const float* M,
                         const float* S0, float* S_init, float* S_final, hipStream_t s);
 
+hipError_t launch_merge_adjoint(int B, int H, int n_seg, const float* dS_ext, const float* M,
+                                const float* dS_final, float* dS_exit, float* dS0, hipStream_t s);
+
 // The fp32-operand chunk preparation (T, P, gate rows) for bf16 or fp32 inputs.
 hipError_t launch_prep_f32(const Problem& p, const Workspace& ws, const void* k, const void* q,
                            const float* g, const void* beta, hipStream_t s);
@@ -104,7 +107,8 @@ hipError_t launch_prep_f32(const Problem& p, const Workspace& ws, const void* k,
 hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* dVN, const void* q,
                       const void* k, const void* v, const float* g, const void* beta, const float* h,
                       const void* dout, const float* dht, float* dq, float* dk, float* dv, float* dg,
-                      float* dbeta, float* dh0, hipStream_t s);
+                      float* dbeta, float* dh0,
+                      bool dh_only, hipStream_t s);
 
 // Host-only checks of a gdn_chunk_fwd call (descriptor, flags, pointers), and
 // the workspace it needs; no HIP call.

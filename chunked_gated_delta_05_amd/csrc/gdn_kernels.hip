@@ -2085,6 +2085,67 @@ __global__ __launch_bounds__(256) void merge_kernel(int H, int n_seg, const floa
         }
 }
 
+// The adjoint of the merge, over the segments in reverse: with G_n the
+// gradient at the end of the last segment (zero when dS_final is NULL),
+// dS_exit[s] = G_{s+1} and G_s = M_s^T G_{s+1} + dS_ext[s]; dS0 = G_0. One
+// workgroup per (b, head, 8 state columns). While G is known to be zero (no
+// final-state gradient yet) the map is not read; M_0 is read only for dS0.
+__global__ __launch_bounds__(256) void merge_adjoint_kernel(int H, int n_seg, const float* dS_ext, const float* M,
+                                                             const float* dS_final, float* dS_exit, float* dS0) {
+    __shared__ __attribute__((aligned(16))) float Ms[DK * MLD];
+    __shared__ float Sc[DK * MC];
+    const int tid = threadIdx.x, c = tid % MC, rbase = tid / MC;   // rows rbase + 32 i
+    const int col0 = blockIdx.x * MC, bh = blockIdx.y, b = bh / H, head = bh % H;
+    for (int i = 0; i < 4; ++i) {
+        const int r = rbase + 32 * i;
+        Sc[r * MC + c] = dS_final ? dS_final[((int64_t)bh * DK + r) * DV + col0 + c] : 0.0f;
+    }
+    bool zero = dS_final == nullptr;
+    for (int s = n_seg - 1; s >= 0; --s) {
+        const int64_t us = ((int64_t)b * n_seg + s) * H + head;
+        __syncthreads();                          // Sc written, the previous product done with Ms
+        for (int i = 0; i < 4; ++i) {
+            const int r = rbase + 32 * i;
+            dS_exit[(us * DK + r) * DV + col0 + c] = Sc[r * MC + c];
+        }
+        if (s == 0 && !dS0) break;
+        float acc[4];
+        for (int i = 0; i < 4; ++i) acc[i] = dS_ext[(us * DK + rbase + 32 * i) * DV + col0 + c];
+        if (!zero) {
+            const f32x4* src = reinterpret_cast<const f32x4*>(M + us * DK * DK);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int e = 4 * (tid + 256 * j);
+                *reinterpret_cast<f32x4*>(&Ms[(e / DK) * MLD + e % DK]) = src[tid + 256 * j];
+            }
+            __syncthreads();
+            // (M^T G)[i][c] = sum_m M[m][i] G[m][c]
+            for (int m = 0; m < DK; ++m) {
+                const float gv = Sc[m * MC + c];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] += Ms[m * MLD + rbase + 32 * i] * gv;
+            }
+        }
+        __syncthreads();
+        for (int i = 0; i < 4; ++i) Sc[(rbase + 32 * i) * MC + c] = acc[i];
+        zero = false;
+    }
+    __syncthreads();
+    if (dS0)
+        for (int i = 0; i < 4; ++i) {
+            const int r = rbase + 32 * i;
+            dS0[((int64_t)bh * DK + r) * DV + col0 + c] = Sc[r * MC + c];
+        }
+}
+
+hipError_t launch_merge_adjoint(int B, int H, int n_seg, const float* dS_ext, const float* M,
+                                const float* dS_final, float* dS_exit, float* dS0, hipStream_t s) {
+    if (B * H == 0) return hipSuccess;
+    dim3 grid(DV / MC, B * H);
+    hipLaunchKernelGGL(merge_adjoint_kernel, grid, dim3(256), 0, s, H, n_seg, dS_ext, M, dS_final, dS_exit, dS0);
+    return hipGetLastError();
+}
+
 // Pieces of a sequence split over packed documents, in token order: piece p
 // enters with its document's initial state (zero when S0 is NULL) when it
 // starts the document, else with the exit state of piece p - 1,

@@ -339,6 +339,39 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
                          size_t* workspace_bytes, hipStream_t stream);
 
 /*
+ * gdn_state_grad_summary - the gradient summary of every unit for a split
+ * backward (kda_state_grad_ext_kernel on the state_summary.py coverage page):
+ * dS_ext[u] = dL/d(entry state of u) through unit u's own outputs only, i.e.
+ * with a zero gradient at the unit's exit. It is the reverse state pass of
+ * gdn_chunk_bwd without the per-token gradients; the arguments are as there
+ * (h from the forward over the same units, the workspace of gdn_chunk_bwd's
+ * size), dS_ext device fp32 [units][H][K][V]. Scalar gate only.
+ */
+gdn_status gdn_state_grad_summary(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                                  const float* g, const void* beta, const float* h, const void* dout,
+                                  float* dS_ext, void* workspace, size_t* workspace_bytes, hipStream_t stream);
+
+/*
+ * gdn_state_merge_adjoint - the reverse state wavefront of a split backward
+ * (apply_kda_state_gradient_summary on the Diff Coverage page: M^T dS + dS_ext),
+ * over the segments from the last, in fp32:
+ *   G_n = dS_final[b] (zero when NULL)
+ *   dS_exit[b][s] = G_{s+1}             the gradient arriving at segment s's exit
+ *   G_s = M[b][s]^T G_{s+1} + dS_ext[b][s]
+ *   dS0[b] = G_0                        (skipped when dS0 is NULL)
+ *   dS_ext  device fp32 [B][n_seg][H][K][V] (gdn_state_grad_summary)
+ *   M       device fp32 [B][n_seg][H][K][K] (gdn_state_summary); the last
+ *           segment's map is not read when dS_final is NULL, nor the first's
+ *           when dS0 is NULL
+ *   dS_exit device fp32 [B][n_seg][H][K][V]
+ * gdn_chunk_bwd over the segments with dht = dS_exit then gives the unsplit
+ * backward's gradients.
+ */
+gdn_status gdn_state_merge_adjoint(int32_t B, int32_t H, int32_t n_seg, int32_t K, int32_t V,
+                                   const float* dS_ext, const float* M, const float* dS_final, float* dS_exit,
+                                   float* dS0, hipStream_t stream);
+
+/*
  * gdn_chunk_fwd_noalloc - gdn_chunk_fwd for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc). Same arguments, results and errors as gdn_chunk_fwd

@@ -159,6 +159,23 @@ def merge(S_ext, M, S0=None):
     return out
 
 
+def merge_adjoint(dS_ext, M, dS_final=None):
+    """Reverse wavefront of a split backward in fp64 (the adjoint summary of
+    apply_kda_state_gradient_summary on the Diff Coverage page): with
+    G_n = dS_final (zero when None) and G_s = M_s^T G_{s+1} + dS_ext[s],
+    returns (dS_exit [n_seg, n, K, V] = G_{s+1} per segment, G_0).
+    dS_ext: [n_seg, n, K, V]; M: [n_seg, n, K, K]; dS_final: [n, K, V]."""
+    e = np.asarray(dS_ext, dtype=np.float64)
+    m = np.asarray(M, dtype=np.float64)
+    n_seg = e.shape[0]
+    G = np.zeros(e.shape[1:]) if dS_final is None else np.asarray(dS_final, dtype=np.float64).copy()
+    exits = np.zeros_like(e)
+    for s in range(n_seg - 1, -1, -1):
+        exits[s] = G
+        G = np.swapaxes(m[s], -1, -2) @ G + e[s]
+    return exits, G
+
+
 def input_transforms(q, k, beta, eps=L2NORM_EPS):
     """The transformed inputs and their slots, in fp64: q_hat = q r_q and
     k_hat = k r_k with r = 1 / sqrt(sum x^2 + eps) per (token, head), and

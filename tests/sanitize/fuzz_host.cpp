@@ -140,6 +140,10 @@ void fuzz_fwd() {
     tally(gdn_chunk_bwd(&d, p15[0], p15[1], p15[2], (const float*)p15[3], p15[4], (const float*)p15[5], p15[6],
                         (const float*)p15[7], (float*)p15[8], (float*)p15[9], (float*)p15[10], (float*)p15[11],
                         (float*)p15[12], (float*)p15[13], bws, &bnb, nullptr));
+    bnb = bhave;
+    stub_set_workspace(bws, bhave);
+    tally(gdn_state_grad_summary(&d, p15[0], p15[1], p15[2], (const float*)p15[3], p15[4], (const float*)p15[5],
+                                 p15[6], (float*)p15[13], bws, &bnb, nullptr));
     stub_set_workspace(nullptr, 0);
     free(bws);
 }
@@ -166,6 +170,9 @@ void fuzz_split_meta() {
 }
 
 void fuzz_merge() {
+    tally(gdn_state_merge_adjoint(pick({1, 2, 0}), pick({1, 8, 0}), pick({0, 1, 8, -1}), pick({128, 64}), 128,
+                                  (const float*)FAKE, uni(0, 5) ? (const float*)FAKE : nullptr, nullptr, (float*)FAKE,
+                                  nullptr, nullptr));
     tally(gdn_state_merge_pieces(pick({0, 1, 9, -1}), pick({1, 3, 0}), pick({1, 8, 0}), pick({128, 64}), 128,
                                  static_cast<const int32_t*>(uni(0, 5) ? FAKE : nullptr), (const float*)FAKE,
                                  (const float*)FAKE, nullptr, (float*)FAKE, nullptr));

@@ -65,6 +65,13 @@ hipError_t launch_state(const Problem& p, const Workspace& ws, const void*, cons
     return hipSuccess;
 }
 
+hipError_t launch_merge_adjoint(int B, int H, int n_seg, const float* dS_ext, const float* M, const float*,
+                                float* dS_exit, float*, hipStream_t) {
+    if (B < 1 || H < 1 || n_seg < 0) fail("adjoint merge sizes");
+    if (n_seg > 0 && (!dS_ext || !M || !dS_exit)) fail("adjoint merge buffers");
+    return hipSuccess;
+}
+
 hipError_t launch_merge_pieces(int n_pieces, int n_docs, int H, const int32_t* piece_doc, const float* S_ext,
                                const float* M, const float*, float* S_in, hipStream_t) {
     if (n_pieces < 0 || n_docs < 1 || H < 1) fail("piece merge sizes");
@@ -88,7 +95,8 @@ hipError_t launch_prep_f32(const Problem& p, const Workspace& ws, const void* k,
 
 hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* dVN, const void* q, const void* k,
                       const void* v, const float* g, const void* beta, const float* h, const void* dout,
-                      const float*, float* dq, float* dk, float* dv, float* dg, float* dbeta, float*, hipStream_t) {
+                      const float*, float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0, bool dh_only,
+                      hipStream_t) {
     gdn::Problem pf = p;
     pf.dtype = 0;                  // the backward's preparation has fp32 operands
     check_problem(pf, ws);
@@ -97,8 +105,10 @@ hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* d
     region(dVN, nch * 64 * 128 * 4, "dvn region");
     if (static_cast<const char*>(static_cast<void*>(dVN)) < static_cast<const char*>(static_cast<void*>(dH)) + nch * 128 * 128 * 4)
         fail("dH and dvn overlap");
-    if (p.um.total_tokens > 0 && (!q || !k || !v || !g || !beta || !h || !dout || !dq || !dk || !dv || !dg || !dbeta))
-        fail("backward pointers");
+    if (p.um.total_tokens > 0 && (!q || !k || !v || !g || !beta || !h || !dout))
+        fail("backward inputs");
+    if (p.um.total_tokens > 0 && !dh_only && (!dq || !dk || !dv || !dg || !dbeta)) fail("backward pointers");
+    if (dh_only && !dh0) fail("gradient summary output");
     return hipSuccess;
 }
 

@@ -22,7 +22,8 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     names = declared_functions()
     assert names == ["gdn_chunk_bwd", "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_split_meta",
-                     "gdn_state_merge", "gdn_state_merge_pieces", "gdn_state_summary", "gdn_varlen_meta"]
+                     "gdn_state_grad_summary", "gdn_state_merge", "gdn_state_merge_adjoint",
+                     "gdn_state_merge_pieces", "gdn_state_summary", "gdn_varlen_meta"]
     L = gb.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -302,3 +303,27 @@ def test_backward_host_checks():
         if want == gb.GDN_OK:
             continue                                                  # would launch: GPU only
         assert bwd(desc(), ptrs=p)[0] == want, i
+
+
+def test_gradient_summary_and_adjoint_errors():
+    L = gb.lib()
+    nb = ctypes.c_size_t(0)
+    d = desc()
+    # the backward's workspace size, and its checks
+    st = L.gdn_state_grad_summary(ctypes.byref(d), None, None, None, None, None, None, None, None, None,
+                                  ctypes.byref(nb), None)
+    assert st == gb.GDN_OK and nb.value == bwd(desc(), ws=None)[1]
+    assert L.gdn_state_grad_summary(ctypes.byref(desc(gate_kind=1)), None, None, None, None, None, None, None,
+                                    None, None, ctypes.byref(nb), None) == gb.GDN_ERR_UNSUPPORTED
+    big = ctypes.c_size_t(1 << 40)
+    # no output
+    assert L.gdn_state_grad_summary(ctypes.byref(d), *[FAKE] * 7, None, FAKE, ctypes.byref(big),
+                                    None) == gb.GDN_ERR_INVALID
+    assert L.gdn_state_merge_adjoint(2, 3, 4, 64, 128, FAKE, FAKE, None, FAKE, None, None) == gb.GDN_ERR_UNSUPPORTED
+    assert L.gdn_state_merge_adjoint(0, 3, 4, 128, 128, FAKE, FAKE, None, FAKE, None, None) == gb.GDN_ERR_INVALID
+    assert L.gdn_state_merge_adjoint(2, 3, -1, 128, 128, FAKE, FAKE, None, FAKE, None, None) == gb.GDN_ERR_INVALID
+    for i in range(3):
+        ptrs = [FAKE, FAKE, FAKE]
+        ptrs[i] = None
+        assert L.gdn_state_merge_adjoint(2, 3, 4, 128, 128, ptrs[0], ptrs[1], None, ptrs[2], None,
+                                         None) == gb.GDN_ERR_INVALID

@@ -165,3 +165,93 @@ def test_backward_is_deterministic():
     torch.cuda.synchronize()
     for n in r1:
         assert torch.equal(r1[n], r2[n]), n
+
+
+# ------------------------------------------------------------------ split backward
+@pytest.mark.parametrize("dtype,with_dht", [("bf16", False), ("fp32", True), ("bf16", True)])
+def test_split_backward_equals_unsplit(dtype, with_dht):
+    # rows cut at 100 and 190 (inside chunks): gradient summaries of the
+    # segments, the adjoint merge with the forward's transfer maps, then
+    # every segment's backward from its exit gradient give the unsplit
+    # backward, and the oracle's
+    print(f"split backward {dtype} dht={with_dht}", flush=True)
+    B, T, H = 2, 256, 2
+    w = small(B=B, T=T, H=H, dtype=dtype, gate_coef=0.02)
+    d = W.generate(w, 777)
+    dev = {n: d[n].to(DEV) for n in ("q", "k", "v", "g", "beta")}
+    gen = torch.Generator().manual_seed(778)
+    S0 = (torch.randn(B, H, 128, 128, generator=gen) * 0.3).to(DEV)
+    dht = (torch.randn(B, H, 128, 128, generator=gen) * 0.3).to(DEV) if with_dht else None
+    do = torch.randn(dev["v"].shape, generator=gen).to(dev["v"].dtype).to(DEV)
+    seg = [0, 100, 190, T]
+    n_seg = len(seg) - 1
+    meta = gb.make_meta(gb.segment_offsets(B, T, seg), B * T, DEV)
+    args = (dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"])
+    S_ext, M, _ = gb.gdn_state_summary(dev["k"], dev["v"], dev["g"], dev["beta"], meta=meta)
+    S_init, _ = gb.gdn_state_merge(S_ext, M, S0, B=B, n_seg=n_seg, want_final=False)
+    _, _, ex = gb.gdn_chunk_fwd(*args, d["scale"], meta=meta, initial_state=S_init, want_h=True)
+    got = gb.split_backward(*args, ex["h"], do, d["scale"], seg=seg, M=M, dht=dht)
+    _, _, exu = gb.gdn_chunk_fwd(*args, d["scale"], initial_state=S0, want_h=True)
+    ref_gpu = gb.gdn_chunk_bwd(*args, exu["h"], do, d["scale"], dht=dht)
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    for n in NAMES + ("dh0",):
+        assert_close(np32(got[n]), np32(ref_gpu[n]), tol, f"split vs unsplit {n}")
+    q, k, v, g, beta = flat_inputs(d)
+    flat = lambda x: x.reshape(-1, *x.shape[2:])
+    ref = oracle.bwd(q, k, v, g, beta, [0, T, 2 * T], d["scale"], np32(flat(do)),
+                     S0=np32(S0).astype(np.float64), dht=None if dht is None else np32(dht).astype(np.float64))
+    for n in NAMES:
+        assert_close(np32(flat(got[n])), ref[n], tol, f"split vs oracle {n}")
+    assert_close(np32(got["dh0"]), ref["dS0"], tol, "split vs oracle dh0")
+
+
+def test_gradient_summary_against_oracle():
+    # every segment's dL/d(entry state) through its own outputs only
+    print("gradient summary", flush=True)
+    B, T, H = 1, 300, 2
+    w = small(B=B, T=T, H=H, dtype="fp32", gate_coef=0.05)
+    d = W.generate(w, 790)
+    dev = {n: d[n].to(DEV) for n in ("q", "k", "v", "g", "beta")}
+    gen = torch.Generator().manual_seed(791)
+    do = torch.randn(dev["v"].shape, generator=gen).to(DEV)
+    S_in = (torch.randn(3, H, 128, 128, generator=gen) * 0.3).to(DEV)
+    offs = [0, 64, 65, 300]
+    meta = gb.make_meta(offs, T, DEV)
+    args = (dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"])
+    _, _, ex = gb.gdn_chunk_fwd(*args, d["scale"], meta=meta, initial_state=S_in, want_h=True)
+    dS = gb.gdn_state_grad_summary(*args, ex["h"], do, d["scale"], meta=meta)
+    torch.cuda.synchronize()
+    q, k, v, g, beta = flat_inputs(d)
+    ref = oracle.bwd(q, k, v, g, beta, offs, d["scale"], np32(do.reshape(-1, H, 128)),
+                     S0=np32(S_in).astype(np.float64))
+    assert_close(np32(dS), ref["dS0"], TOL["fp32"], "local dS")
+
+
+@pytest.mark.parametrize("with_final,with_dS0", [(False, False), (True, True), (False, True)])
+def test_merge_adjoint_kernel_against_oracle(with_final, with_dS0):
+    # maps that must not be read (the last segment's without a final-state
+    # gradient, the first's without dS0) hold NaN
+    print(f"adjoint merge final={with_final} dS0={with_dS0}", flush=True)
+    B, H, n_seg = 2, 3, 4
+    gen = torch.Generator().manual_seed(17)
+    E = torch.randn(B * n_seg, H, 128, 128, generator=gen)
+    M = torch.randn(B * n_seg, H, 128, 128, generator=gen) * 0.05
+    F = torch.randn(B, H, 128, 128, generator=gen) if with_final else None
+    Mg = M.clone()
+    for b in range(B):
+        if not with_final:
+            Mg[b * n_seg + n_seg - 1] = float("nan")
+        if not with_dS0:
+            Mg[b * n_seg] = float("nan")
+    exits, dS0 = gb.gdn_state_merge_adjoint(E.to(DEV), Mg.to(DEV), None if F is None else F.to(DEV), B=B, n_seg=n_seg,
+                                            want_dS0=with_dS0)
+    torch.cuda.synchronize()
+    for b in range(B):
+        rows = slice(b * n_seg, (b + 1) * n_seg)
+        want_exits, want_G0 = oracle.merge_adjoint(E[rows].numpy(), M[rows].numpy(), None if F is None else F[b].numpy())
+        got = np32(exits[rows])
+        assert np.isfinite(got).all()
+        assert_close(got, want_exits, 1e-5, "dS_exit")
+        if with_dS0:
+            assert_close(np32(dS0[b]), want_G0, 1e-5, "dS0")

@@ -173,3 +173,36 @@ def test_backward_composes_across_a_split():
     for name in ("dq", "dk", "dv", "dbeta", "dg"):
         np.testing.assert_allclose(np.concatenate([first[name], second[name]]), full[name], rtol=1e-11, atol=1e-13)
     np.testing.assert_allclose(first["dS0"], full["dS0"], rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("with_dht", [False, True])
+def test_merge_adjoint_gives_the_unsplit_backward(with_dht):
+    # one unit cut into four segments: local gradient summaries (each
+    # segment's backward with a zero exit gradient, from its true entry
+    # state), the reverse wavefront through oracle.merge_adjoint, then each
+    # segment's backward from its exit gradient reproduce the unsplit
+    # backward and dL/dS0
+    N, H, K, V, scale = 130, 1, 4, 3, 0.6
+    q, k, v, g, beta = rng_inputs(15, N, H, K, V, False, gate_scale=0.05)
+    r = np.random.default_rng(16)
+    do = r.standard_normal((N, H, V))
+    S0 = r.standard_normal((1, H, K, V))
+    dht = r.standard_normal((1, H, K, V)) if with_dht else None
+    full = oracle.bwd(q, k, v, g, beta, [0, N], scale, do, S0=S0, dht=dht)
+    cuts = [0, 20, 64, 65, N]
+    S_in = oracle.merge(oracle.summary(k, v, g, beta, cuts)["S_ext"], oracle.summary(k, v, g, beta, cuts)["M"], S0[0])
+    sl = lambda a, lo, hi: np.ascontiguousarray(a[lo:hi])
+    seg = lambda s: [sl(a, cuts[s], cuts[s + 1]) for a in (q, k, v, g, beta)]
+    local = [oracle.bwd(*seg(s), [0, cuts[s + 1] - cuts[s]], scale, do[cuts[s]:cuts[s + 1]],
+                        S0=S_in[s][None])["dS0"][0] for s in range(4)]
+    M = oracle.summary(k, v, g, beta, cuts)["M"]
+    exits, G0 = oracle.merge_adjoint(np.stack(local), M, None if dht is None else dht[0])
+    np.testing.assert_allclose(G0, full["dS0"][0], rtol=1e-10, atol=1e-12)
+    parts = [oracle.bwd(*seg(s), [0, cuts[s + 1] - cuts[s]], scale, do[cuts[s]:cuts[s + 1]], S0=S_in[s][None],
+                        dht=exits[s][None]) for s in range(4)]
+    for name in ("dq", "dk", "dv", "dbeta", "dg"):
+        np.testing.assert_allclose(np.concatenate([p[name] for p in parts]), full[name], rtol=1e-10, atol=1e-12)
+    # the forward map (not its transpose) fails
+    bad, _ = oracle.merge_adjoint(np.stack(local), np.swapaxes(M, -1, -2), None if dht is None else dht[0])
+    wrong = oracle.bwd(*seg(0), [0, 20], scale, do[:20], S0=S_in[0][None], dht=bad[0][None])
+    assert np.abs(wrong["dk"] - full["dk"][:20]).max() > 1e-4    # dq does not see the exit gradient
