@@ -62,7 +62,7 @@ struct UnitInfo {
 __device__ __forceinline__ UnitInfo unit_info(const UnitMap& um, int u) {
     UnitInfo r;
     if (um.dense) {
-        r.start = (int64_t)u * um.T;
+        r.start = um.t_base + (int64_t)u * um.row_stride;
         r.len = um.T;
         r.nch = um.nt_dense;
         r.cbase = u * um.nt_dense;

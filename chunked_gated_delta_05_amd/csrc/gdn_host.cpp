@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "gdn.h"
@@ -54,6 +55,8 @@ gdn_status validate(const gdn_desc* d, gdn::Problem* p) {
     gdn::UnitMap um;
     memset(&um, 0, sizeof(um));
     um.T = d->T;
+    um.row_stride = d->T;
+    um.t_base = 0;
     um.total_tokens = total;
     if (d->layout == GDN_LAYOUT_TND) {
         // packed documents: physical batch one, offsets required
@@ -212,13 +215,108 @@ gdn_status gdn::fwd_preflight(const gdn_desc* desc, const void* q, const void* k
     return GDN_OK;
 }
 
+// ---- the forward in pieces
+// Dense rows so few that the state pass leaves most of the GPU idle (at most
+// 128 workgroups) and long enough to cut: the forward runs over pieces of
+// consecutive chunks of every row. The preparation of every piece is issued
+// on a helper stream, the state pass of piece i on the caller's stream after
+// the preparation of piece i, from the state piece i - 1 left; so the
+// preparation of later pieces runs beside the state pass of earlier ones.
+// The pieces' preparations and the state between pieces take their own
+// workspace regions.
+namespace {
+
+constexpr int kPipeMaxPieces = 8;
+
+int pipe_pieces(const gdn::Problem& p) {
+    if (!p.um.dense) return 0;
+    if (int64_t(p.um.n_units) * p.H * (DV / 32) > 128) return 0;
+    if (p.um.nt_dense < 128) return 0;
+    const int n = p.um.nt_dense / 64;
+    return n < kPipeMaxPieces ? n : kPipeMaxPieces;
+}
+
+gdn::Problem pipe_piece(const gdn::Problem& p, int i, int n) {
+    const int per = (p.um.nt_dense + n - 1) / n;
+    const int c0 = i * per, c1 = (c0 + per < p.um.nt_dense) ? c0 + per : p.um.nt_dense;
+    gdn::Problem q = p;
+    const int64_t t0 = int64_t(c0) * BT, t1 = int64_t(c1) * BT < p.um.T ? int64_t(c1) * BT : p.um.T;
+    q.um.t_base = p.um.t_base + t0;
+    q.um.T = (int32_t)(t1 - t0);
+    q.um.nt_dense = c1 - c0;
+    q.um.n_chunks = p.um.n_units * (c1 - c0);
+    return q;
+}
+
+// workspace of the pieces, then the state between them (fp32 [units][H][K][V])
+size_t pipe_workspace(const gdn::Problem& p, int n, gdn::Workspace* ws, float** carry, char* base) {
+    size_t off = 0;
+    for (int i = 0; i < n; ++i) {
+        const gdn::Problem q = pipe_piece(p, i, n);
+        const size_t b = gdn::workspace_bytes(q, nullptr, nullptr);
+        if (ws && base) gdn::workspace_bytes(q, &ws[i], base + off);
+        off += (b + 255) & ~size_t(255);
+    }
+    if (carry && base) *carry = reinterpret_cast<float*>(base + off);
+    off += size_t(p.um.n_units) * p.H * DK * DV * 4;
+    return off;
+}
+
+struct PipeStreams {
+    hipStream_t aux = nullptr;
+    hipEvent_t start = nullptr;
+    hipEvent_t prepared[kPipeMaxPieces] = {};
+    bool ready = false;
+};
+PipeStreams g_pipe[64];
+std::mutex g_pipe_mu;
+
+// the helper stream and events of the current device, made on first use
+PipeStreams* pipe_streams() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    PipeStreams& ps = g_pipe[dev];
+    if (!ps.ready) {
+        if (hipStreamCreateWithFlags(&ps.aux, hipStreamNonBlocking) != hipSuccess) return nullptr;
+        if (hipEventCreateWithFlags(&ps.start, hipEventDisableTiming) != hipSuccess) return nullptr;
+        for (auto& e : ps.prepared)
+            if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return nullptr;
+        ps.ready = true;
+    }
+    return &ps;
+}
+
+}  // namespace
+
 extern "C" gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, const void* v,
                                     const float* g, const void* beta, const float* initial_state,
                                     void* o, float* final_state, const gdn_slots* slots, int32_t flags,
                                     void* workspace, size_t* workspace_bytes, hipStream_t stream) {
+    return gdn::fwd_impl(desc, q, k, v, g, beta, initial_state, o, final_state, slots, flags, workspace,
+                         workspace_bytes, stream, true);
+}
+
+gdn_status gdn::fwd_impl(const gdn_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                         const void* beta, const float* initial_state, void* o, float* final_state,
+                         const gdn_slots* slots, int32_t flags, void* workspace, size_t* workspace_bytes,
+                         hipStream_t stream, bool allow_pipeline) {
     gdn::Problem p;
     gdn_status st = validate(desc, &p);
     if (st != GDN_OK) return st;
+    // pipelined problems keep room for their pieces (the single pass fits in it too)
+    const int pieces = allow_pipeline ? pipe_pieces(p) : 0;
+    if (pieces > 0) {
+        if (workspace_bytes == nullptr) return GDN_ERR_INVALID;
+        const size_t need = pipe_workspace(p, pieces, nullptr, nullptr, nullptr);
+        if (workspace == nullptr) {
+            *workspace_bytes = need;
+            return GDN_OK;
+        }
+        if (*workspace_bytes < need) {
+            *workspace_bytes = need;
+            return GDN_ERR_CAPACITY;
+        }
+    }
     gdn::Workspace ws;
     bool query = false;
     st = size_workspace(p, workspace, workspace_bytes, &ws, &query);
@@ -226,6 +324,44 @@ extern "C" gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const v
     st = gdn::fwd_preflight(desc, q, k, v, g, beta, o, flags, &p, nullptr);
     if (st != GDN_OK) return st;
     const bool reuse = flags & GDN_FLAG_REUSE_PREPARED, prep_only = flags & GDN_FLAG_PREPARE_ONLY;
+    if (pieces > 0 && !reuse && !prep_only && !(slots && slots->h) && p.um.total_tokens > 0) {
+        gdn::PrepSlots ps = {};
+        if (slots) {
+            ps.g_cumsum = slots->g_cumsum;
+            ps.A = slots->A;
+            ps.q_hat = slots->q_hat;
+            ps.k_hat = slots->k_hat;
+            ps.q_rstd = slots->q_rstd;
+            ps.k_rstd = slots->k_rstd;
+            ps.beta_eff = slots->beta_eff;
+        }
+        std::lock_guard<std::mutex> lock(g_pipe_mu);
+        PipeStreams* pst = pipe_streams();
+        if (pst) {
+            gdn::Workspace pws[kPipeMaxPieces];
+            float* carry = nullptr;
+            pipe_workspace(p, pieces, pws, &carry, static_cast<char*>(workspace));
+            if (final_state) carry = final_state;   // each workgroup reads its tile before it writes it
+            if (hipEventRecord(pst->start, stream) != hipSuccess) return GDN_ERR_DEVICE;
+            if (hipStreamWaitEvent(pst->aux, pst->start, 0) != hipSuccess) return GDN_ERR_DEVICE;
+            for (int i = 0; i < pieces; ++i) {
+                // the first preparation has the GPU to itself
+                if (gdn::launch_prep(pipe_piece(p, i, pieces), pws[i], k, q, g, beta, ps, pst->aux, i > 0) != hipSuccess)
+                    return GDN_ERR_DEVICE;
+                if (hipEventRecord(pst->prepared[i], pst->aux) != hipSuccess) return GDN_ERR_DEVICE;
+            }
+            for (int i = 0; i < pieces; ++i) {
+                if (hipStreamWaitEvent(stream, pst->prepared[i], 0) != hipSuccess) return GDN_ERR_DEVICE;
+                const float* h0 = i == 0 ? initial_state : carry;
+                float* hf = i + 1 < pieces ? carry : final_state;
+                if (gdn::launch_state(pipe_piece(p, i, pieces), pws[i], q, k, v, beta, h0, o, hf, nullptr,
+                                      slots ? slots->v_new : nullptr, 0, 0, 0, nullptr, nullptr, nullptr, 0,
+                                      stream) != hipSuccess)
+                    return GDN_ERR_DEVICE;
+            }
+            return GDN_OK;
+        }
+    }
     gdn::PrepSlots ps = {};
     if (slots) {
         ps.g_cumsum = slots->g_cumsum;

@@ -23,11 +23,13 @@ constexpr int ORD_MAX = 2048;  // packed units beyond this count keep their natu
 // Where every chunk of every unit lives on the flat token axis.
 struct UnitMap {
     int32_t n_units;             // number of units (B when dense)
-    int32_t dense;               // 1: unit b = tokens [b*T, (b+1)*T), no device metadata
-    int32_t T;                   // dense row length
+    int32_t dense;               // 1: unit b = tokens [t_base + b*row_stride, +T), no device metadata
+    int32_t T;                   // dense unit length
     int32_t n_chunks;            // total chunks over all units
-    int32_t nt_dense;            // chunks per dense row
+    int32_t nt_dense;            // chunks per dense unit
     int64_t total_tokens;
+    int64_t row_stride;          // dense: tokens between unit starts (the row length)
+    int64_t t_base;              // dense: token offset of unit 0 in its row (a piece of the rows)
     const int32_t* offsets;      // device [n_units + 1] (NULL when dense)
     const int32_t* chunk_offsets;// device [n_units + 1]
     const int32_t* chunk_indices;// device [n_chunks][2]
@@ -80,8 +82,18 @@ struct PrepSlots {
 
 size_t workspace_bytes(const Problem& p, Workspace* ws, char* base);
 
+// gdn_chunk_fwd itself; allow_pipeline = false keeps the single-pass
+// workspace (the allocation-free entry point, whose scratch is sized for it)
+gdn_status fwd_impl(const gdn_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                    const void* beta, const float* initial_state, void* o, float* final_state, const gdn_slots* slots,
+                    int32_t flags, void* workspace, size_t* workspace_bytes, hipStream_t stream, bool allow_pipeline);
+
+// off_state_cus: the preparation runs beside a state pass of the same
+// problem (the pieced forward); it then asks for enough LDS that its
+// workgroups cannot share a compute unit with the state pass's
 hipError_t launch_prep(const Problem& p, const Workspace& ws, const void* k, const void* q,
-                       const float* g, const void* beta, const PrepSlots& slots, hipStream_t s);
+                       const float* g, const void* beta, const PrepSlots& slots, hipStream_t s,
+                       bool off_state_cus = false);
 
 // mode: 0 forward; 1 summary (S_ext and/or M), of the units in units_sel
 // (device, n_sel entries) when given, else of all

@@ -2260,8 +2260,27 @@ __global__ __launch_bounds__(ORD_T) void unit_order_kernel(UnitMap um, int32_t* 
 }
 
 // ------------------------------------------------------------------ launchers
+// dynamic LDS that keeps a workgroup of `prep` off a compute unit that holds
+// one of `state` (0 when the two cannot share one anyway)
+static size_t lds_exclusion_pad(const void* prep, const void* state) {
+    int dev = 0, lds_cu = 0;
+    hipFuncAttributes fp, fs;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+        hipFuncGetAttributes(&fp, prep) != hipSuccess || hipFuncGetAttributes(&fs, state) != hipSuccess)
+        return 0;
+    const long free_lds = (long)lds_cu - (long)fs.sharedSizeBytes;
+    const long need = free_lds - (long)fp.sharedSizeBytes + 1024;
+    // at most four workgroups per compute unit, so that the preparation
+    // draws its bandwidth over the state pass's whole run instead of in
+    // bursts that lengthen the state pass's loads
+    const long quarter = (long)lds_cu / 4 - (long)fp.sharedSizeBytes;
+    const long pad = need > quarter ? need : quarter;
+    return pad > 0 ? (size_t)pad : 0;
+}
+
 hipError_t launch_prep(const Problem& p, const Workspace& ws, const void* k, const void* q,
-                       const float* g, const void* beta, const PrepSlots& sl, hipStream_t s) {
+                       const float* g, const void* beta, const PrepSlots& sl, hipStream_t s, bool off_state_cus) {
     if (p.um.n_chunks == 0) return hipSuccess;
     PrepArgs a;
     a.um = p.um; a.H = p.H; a.k = k; a.q = q; a.g = g; a.beta = beta; a.use_exp2 = p.use_exp2;
@@ -2275,8 +2294,13 @@ hipError_t launch_prep(const Problem& p, const Workspace& ws, const void* k, con
             if (xf) hipLaunchKernelGGL(prep_kernel_pk<true>, grid, block, 0, s, a);
             else hipLaunchKernelGGL(prep_kernel_pk<false>, grid, block, 0, s, a);
         } else {
-            if (xf) hipLaunchKernelGGL(prep_kernel_h<true>, dim3(p.H * p.um.n_chunks), dim3(64), 0, s, a);
-            else hipLaunchKernelGGL(prep_kernel_h<false>, dim3(p.H * p.um.n_chunks), dim3(64), 0, s, a);
+            const void* fn = xf ? reinterpret_cast<const void*>(prep_kernel_h<true>)
+                                : reinterpret_cast<const void*>(prep_kernel_h<false>);
+            const size_t pad = off_state_cus
+                                   ? lds_exclusion_pad(fn, reinterpret_cast<const void*>(state_kernel_ks<false, false, false>))
+                                   : 0;
+            if (xf) hipLaunchKernelGGL(prep_kernel_h<true>, dim3(p.H * p.um.n_chunks), dim3(64), pad, s, a);
+            else hipLaunchKernelGGL(prep_kernel_h<false>, dim3(p.H * p.um.n_chunks), dim3(64), pad, s, a);
         }
     } else {
         if (p.per_key) hipLaunchKernelGGL((prep_kernel<PolicyF, true>), grid, block, 0, s, a);

@@ -63,5 +63,6 @@ extern "C" gdn_status gdn_chunk_fwd_noalloc(const gdn_desc* desc, const void* q,
     st = scratch_for(stream, &ws);
     if (st != GDN_OK) return st;
     size_t bytes = GDN_NOALLOC_SCRATCH_BYTES;
-    return gdn_chunk_fwd(desc, q, k, v, g, beta, initial_state, o, final_state, slots, flags, ws, &bytes, stream);
+    return gdn::fwd_impl(desc, q, k, v, g, beta, initial_state, o, final_state, slots, flags, ws, &bytes, stream,
+                         false);
 }

@@ -72,7 +72,7 @@ void fuzz_fwd() {
     gdn_desc d;
     memset(&d, 0, sizeof(d));
     d.B = pick({1, 1, 2, 3, 0, -1});
-    d.T = pick({0, 1, 63, 64, 65, 200, 1000, 4096, -5});
+    d.T = pick({0, 1, 63, 64, 65, 200, 1000, 4096, 16384, 16400, -5});   // long rows: the pieced forward
     d.H = pick({1, 3, 16, 40, 0});
     d.K = pick({128, 128, 128, 64});
     d.V = pick({128, 128, 128, 64});

@@ -41,6 +41,29 @@ void check_problem(const gdn::Problem& p, const gdn::Workspace& ws) {
 }
 }  // namespace
 
+// The stream and event calls of the pieced forward: fake handles, success.
+extern "C" {
+hipError_t hipGetDevice(int* device) {
+    *device = 0;
+    return hipSuccess;
+}
+hipError_t hipStreamCreateWithFlags(hipStream_t* stream, unsigned int) {
+    static int fake_stream;
+    *stream = reinterpret_cast<hipStream_t>(&fake_stream);
+    return hipSuccess;
+}
+hipError_t hipEventCreateWithFlags(hipEvent_t* event, unsigned int) {
+    static int fake_events[16];
+    static int n = 0;
+    *event = reinterpret_cast<hipEvent_t>(&fake_events[n++ % 16]);
+    return hipSuccess;
+}
+hipError_t hipEventRecord(hipEvent_t event, hipStream_t) { return event ? hipSuccess : hipErrorInvalidValue; }
+hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t event, unsigned int) {
+    return event ? hipSuccess : hipErrorInvalidValue;   // the null stream is the default stream
+}
+}
+
 void stub_set_workspace(const void* base, size_t bytes) {
     g_lo = static_cast<const char*>(base);
     g_hi = g_lo + bytes;
@@ -49,7 +72,7 @@ void stub_set_workspace(const void* base, size_t bytes) {
 namespace gdn {
 
 hipError_t launch_prep(const Problem& p, const Workspace& ws, const void* k, const void*, const float* g,
-                       const void* beta, const PrepSlots&, hipStream_t) {
+                       const void* beta, const PrepSlots&, hipStream_t, bool) {
     check_problem(p, ws);
     if (p.um.total_tokens > 0 && (!k || !g || !beta)) fail("prep inputs");
     return hipSuccess;

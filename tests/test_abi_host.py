@@ -327,3 +327,17 @@ def test_gradient_summary_and_adjoint_errors():
         ptrs[i] = None
         assert L.gdn_state_merge_adjoint(2, 3, 4, 128, 128, ptrs[0], ptrs[1], None, ptrs[2], None,
                                          None) == gb.GDN_ERR_INVALID
+
+
+def test_pieced_forward_workspace():
+    # long dense rows with few (row, head) pairs run in pieces: the size query
+    # covers every piece's preparation and the state between pieces, more than
+    # one pass needs; the allocation-free entry keeps the one-pass size
+    L = gb.lib()
+    d = desc(B=1, T=16384 + 37, H=4)              # 257 chunks, 16 state workgroups
+    st, need = fwd(d, ws=None)
+    one_pass = fwd(desc(B=1, T=16384 + 37, H=64), ws=None)[1] // 16   # 64 pairs: not pieced
+    assert st == gb.GDN_OK and need > one_pass
+    assert need - one_pass >= 4 * 128 * 128 * 4   # the state carried between pieces
+    st, got = fwd(d, nbytes=need - 1)
+    assert st == gb.GDN_ERR_CAPACITY and got == need

@@ -679,3 +679,37 @@ def test_values_near_the_fp16_operand_range(per_key):
     r = run_oracle(d, S0=np32(S0).astype(np.float64))
     assert_close(flat_o(o, w), r["o"], TOL["bf16"], "scaled o")
     assert_close(np32(fin), r["final"], TOL["bf16"], "scaled final")
+
+
+@pytest.mark.parametrize("per_key,dtype,with_final", [(False, "bf16", True), (True, "bf16", False), (False, "fp32", False)])
+def test_pieced_forward_equals_one_pass(per_key, dtype, with_final):
+    # a long row with two heads (8 state workgroups) runs in pieces whose
+    # preparations overlap the state pass; bit for bit the one-pass forward
+    # (prepare, then reuse, which never runs in pieces), and the oracle on a
+    # sampled head
+    print(f"pieced forward per_key={per_key} {dtype} final={with_final}", flush=True)
+    T = 16384 + 37
+    w = small(B=1, T=T, H=2, dtype=dtype, per_key=per_key, use_exp2=per_key, gate_coef=0.02 if per_key else 0.1)
+    d = to_dev(W.generate(w, 611))
+    S0 = (torch.randn(1, 2, 128, 128, generator=torch.Generator().manual_seed(612)) * 0.3).to(DEV)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"])
+    o1, f1, ex1 = gb.gdn_chunk_fwd(*args, initial_state=S0, output_final_state=with_final, use_exp2=w.use_exp2,
+                                   slots=("v_new",))
+    nb = gb.workspace_bytes(gb._desc(d["k"], 2, d["k"].dtype, torch.float32, per_key, w.use_exp2, d["scale"], None))
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    gb.gdn_chunk_fwd(d["q"], d["k"], None, d["g"], d["beta"], d["scale"], use_exp2=w.use_exp2,
+                     flags=gb.FLAG_PREPARE_ONLY, workspace=ws)
+    o2, f2, ex2 = gb.gdn_chunk_fwd(*args, initial_state=S0, output_final_state=with_final, use_exp2=w.use_exp2,
+                                   flags=gb.FLAG_REUSE_PREPARED, workspace=ws, slots=("v_new",))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2), "pieced o differs from the one-pass o"
+    assert torch.equal(ex1["v_new"], ex2["v_new"])
+    if with_final:
+        assert torch.equal(f1, f2)
+    q, k, v, g, beta = flat_inputs(d)
+    pick = lambda x: np.ascontiguousarray(x[:, [1]])
+    r = oracle.fwd(pick(q), pick(k), pick(v), pick(g), pick(beta), [0, T], d["scale"], gate_per_key=per_key,
+                   use_exp2=w.use_exp2, S0=np32(S0)[:, [1]].astype(np.float64))
+    assert_close(flat_o(o1, w)[:, [1]], r["o"], TOL[dtype], "pieced o (head 1)")
+    if with_final:
+        assert_close(np32(f1[:, [1]]), r["final"], TOL[dtype], "pieced final (head 1)")
