@@ -469,19 +469,17 @@ def gdn_state_merge(S_ext, M, S0=None, *, B: int, n_seg: int, want_final=True, S
 
 def gdn_chunk_bwd(q, k, v, g, beta, h, dout, scale=None, *, meta: UnitMeta | None = None, dht=None,
                   use_exp2=False, want_dh0=True, workspace=None):
-    """Gradients of the chunked forward (scalar gate) through libgdn.
+    """Gradients of the chunked forward (scalar or per-key gate) through libgdn.
 
     h: the forward's entry states (gdn_chunk_fwd(..., want_h=True) extras
     "h", fp32 [n_chunks, H, K, V]); dout: dL/do in the input dtype, v's
     shape; dht: dL/d(final state) fp32 [units, H, K, V] or None. Returns a
-    dict of fp32 tensors dq, dk, dv, dg, dbeta and dh0 (dL/d initial state,
-    when wanted)."""
+    dict of fp32 tensors dq, dk, dv, dg (g's shape), dbeta and dh0 (dL/d
+    initial state, when wanted)."""
     H, per_key = _check_inputs(q, k, v, g, beta, meta, device_check=False)
-    if per_key:
-        raise NotImplementedError("the backward supports the scalar gate")
     if scale is None:
         scale = k.shape[-1] ** -0.5
-    desc = _desc(k, H, k.dtype, k.dtype, False, use_exp2, scale, meta)
+    desc = _desc(k, H, k.dtype, k.dtype, per_key, use_exp2, scale, meta)
     dev = k.device
     units = n_units_of(k, meta)
     K, V = k.shape[-1], v.shape[-1]
@@ -516,11 +514,9 @@ def gdn_state_grad_summary(q, k, v, g, beta, h, dout, scale=None, *, meta: UnitM
     """dS_ext [units,H,K,V]: dL/d(entry state) of every unit through its own
     outputs only (zero gradient at its exit); arguments as gdn_chunk_bwd."""
     H, per_key = _check_inputs(q, k, v, g, beta, meta, device_check=False)
-    if per_key:
-        raise NotImplementedError("the gradient summary supports the scalar gate")
     if scale is None:
         scale = k.shape[-1] ** -0.5
-    desc = _desc(k, H, k.dtype, k.dtype, False, use_exp2, scale, meta)
+    desc = _desc(k, H, k.dtype, k.dtype, per_key, use_exp2, scale, meta)
     dev = k.device
     K, V = k.shape[-1], v.shape[-1]
     _check_tensor("h", h, torch.float32, (meta.n_chunks, H, K, V), dev)

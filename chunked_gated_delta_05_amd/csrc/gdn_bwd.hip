@@ -1,5 +1,5 @@
-// HIP kernels of the chunked gated delta rule backward (scalar gate) for
-// gfx950.
+// HIP kernels of the chunked gated delta rule backward (scalar and per-key
+// gates) for gfx950.
 //
 // The forward of one chunk (n <= 64 tokens, entry state h in K x V, G the
 // chunk-local inclusive cumulative gate, b the decay base, gamma = b^{G_L}):
@@ -34,6 +34,24 @@
 //                    dq, dk, dv, dbeta and dg.
 // The chunk preparation (T, P and the gate rows, fp32) comes from the
 // forward's fp32-operand preparation kernel.
+//
+// Per-key gate (b^G a 64 x K matrix): Kd, Qd and Kg are the prepared gated
+// tiles and gamma = diag(b^{G_L}), so the reverse state pass and the value-
+// tile products are the same with those tiles in place of the row scalings.
+// The decay inside L and P is per key, D_ijd = b^{G_id - G_jd}; with
+// X = dL (strictly lower) and dP (lower with the diagonal) the finish needs
+//   R[X, Y]_id = sum_j X_ij Y_jd D_ijd      (rows)
+//   C[X, Y]_jd = sum_i X_ij Y_id D_ijd      (columns)
+// for R[dL, K], R[dP, K], C[diag(beta) dL, K] and C[dP, Q]:
+//   dq = R[dP,K] + b^G o dQd
+//   dk = beta o R[dL,K] + C[beta dL,K] + C[dP,Q] + b^G o dKd + b^{G_L-G} o dKg
+//   dG = ln b (beta k o R[dL,K] + q o R[dP,K] - k o (C[beta dL,K] + C[dP,Q])
+//              + Qd o dQd + Kd o dKd - Kg o dKg),   dbeta_i += k_i . R[dL,K]_i
+// and G_L gains ln b (sum_i Kg o dKg + gamma o diag(h dh'^T)). Off the
+// diagonal 16-row blocks each product splits the decay at a reference row r
+// between the two blocks, b^{G_i - G_r} b^{G_r - G_j}, both factors at most 1
+// for any g <= 0 (the forward's preparation does the same for L and P); the
+// diagonal blocks take the exponent differences directly.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -56,6 +74,7 @@ struct BwdArgs {
     const void* k;
     const void* v;
     const void* beta;
+    const float* g;        // per key: the gates (the finish rebuilds G in key slices)
     const void* dout;
     const float* h;        // [n_chunks][H][K][V] entry state of every chunk
     const float* dht;      // [units][H][K][V] or NULL
@@ -141,6 +160,20 @@ __device__ void load_chunk(const BwdArgs& a, int64_t t0, int64_t ch, int head, i
         for (int e = tid; e < BT * BT; e += 256) Ts[(e >> 6) * BTL + (e & 63)] *= bt[e & 63];
 }
 
+// per key: k b^{G_L - G} into Ks, q b^G into Qs (k b^G replaces the first
+// later in the step), T diag(beta), P and beta
+template <class In>
+__device__ void load_chunk_pk(const BwdArgs& a, int64_t t0, int64_t ch, int head, int len, float* Ks, float* Qs,
+                              float* Ts, float* Ps, float* bt, int tid) {
+    load_tile<float, BT, DK>(reinterpret_cast<const float*>(a.ws.kg) + ch * (BT * DK), DK, BT, Ks, BKL, tid);
+    load_tile<float, BT, DK>(reinterpret_cast<const float*>(a.ws.qg) + ch * (BT * DK), DK, BT, Qs, BKL, tid);
+    load_tile<float, BT, BT>(reinterpret_cast<const float*>(a.ws.Tm) + ch * (BT * BT), BT, BT, Ts, BTL, tid);
+    load_tile<float, BT, BT>(reinterpret_cast<const float*>(a.ws.P) + ch * (BT * BT), BT, BT, Ps, BTL, tid);
+    if (tid < BT) bt[tid] = tid < len ? ldf(reinterpret_cast<const In*>(a.beta), (t0 + tid) * a.H + head) : 0.0f;
+    __syncthreads();
+    for (int e = tid; e < BT * BT; e += 256) Ts[(e >> 6) * BTL + (e & 63)] *= bt[e & 63];
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ reverse state pass
@@ -148,8 +181,8 @@ __device__ void load_chunk(const BwdArgs& a, int64_t t0, int64_t ch, int head, i
 // holds dL/dh for keys 32w .. 32w+31 of the 32 columns (four 16 x 16 tiles).
 // Chunks run from the last: store dh', then dvn = Kg dh' + scale P^T dO (wave
 // w: token rows 16w .. +15), Z = Tb^T dvn, and dh = gamma dh' + scale Qd^T dO
-// - Kd^T Z.
-template <class In>
+// - Kd^T Z (per key: the prepared gated tiles, and gamma per key).
+template <class In, bool PK>
 __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) float Ks[BT * BKL];
     __shared__ __attribute__((aligned(16))) float Qs[BT * BKL];
@@ -190,8 +223,14 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
         const int64_t t0 = ui.start + (int64_t)c * BT;
         const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
         __syncthreads();                               // the previous chunk's tiles are consumed
-        load_chunk<In, true>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, gm, bt, tid);
+        if (PK) load_chunk_pk<In>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, bt, tid);
+        else load_chunk<In, true>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, gm, bt, tid);
         load_tile<In, BT, 32>(dout + (t0 * H + head) * DV + c0, (int64_t)H * DV, len, dOs, 33, tid);
+        float gk[2][4];                                // per key: b^{G_L} of keys 32w + 16kt + 4G + r
+        if (PK)
+            for (int kt = 0; kt < 2; ++kt)
+                for (int r = 0; r < 4; ++r)
+                    gk[kt][r] = fpow(a.ws.gamL[ch * DK + 32 * w + 16 * kt + 4 * G + r], a.use_exp2);
         // dh' of this chunk to the workspace
         for (int kt = 0; kt < 2; ++kt)
             for (int ct = 0; ct < 2; ++ct)
@@ -200,7 +239,8 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
                     a.dH[(ch * DK + key) * DV + c0 + 16 * ct + n] = dh[kt][ct][r];
                 }
         __syncthreads();
-        // dvn = b^{G_L - G} (K dh') + scale P^T dO, token rows 16w .. +15
+        // dvn = Kg dh' + scale P^T dO, token rows 16w .. +15 (scalar gate:
+        // Kg = diag(b^{G_L - G}) K)
         for (int ct = 0; ct < 2; ++ct) {
             f32x4 kh = {0.f, 0.f, 0.f, 0.f}, pd = {0.f, 0.f, 0.f, 0.f};
             mmf<DK>(kh, [&](int m, int k) { return Ks[(16 * w + m) * BKL + k]; },
@@ -209,35 +249,39 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
                     [&](int k, int nn) { return dOs[k * 33 + 16 * ct + nn]; }, G, n);
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * w + 4 * G + r;
-                const float x = gm[2 * BT + row] * kh[r] + a.scale * pd[r];
+                const float x = (PK ? kh[r] : gm[2 * BT + row] * kh[r]) + a.scale * pd[r];
                 dvS[row * 33 + 16 * ct + n] = x;
                 a.dVN[(ch * BT + row) * DV + c0 + 16 * ct + n] = x;
             }
         }
         __syncthreads();
-        // Z = Tb^T dvn, kept as b^G Z
+        // per key, k b^G takes the place of k b^{G_L - G}
+        if (PK) load_tile<float, BT, DK>(reinterpret_cast<const float*>(a.ws.kd) + ch * (BT * DK), DK, BT, Ks, BKL, tid);
+        // Z = Tb^T dvn, kept as b^G Z for the scalar gate
         for (int ct = 0; ct < 2; ++ct) {
             f32x4 z = {0.f, 0.f, 0.f, 0.f};
             mmf<BT>(z, [&](int m, int k) { return Ts[k * BTL + 16 * w + m]; },
                     [&](int k, int nn) { return dvS[k * 33 + 16 * ct + nn]; }, G, n);
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * w + 4 * G + r;
-                Zs[row * 33 + 16 * ct + n] = gm[BT + row] * z[r];
+                Zs[row * 33 + 16 * ct + n] = PK ? z[r] : gm[BT + row] * z[r];
             }
         }
         __syncthreads();
-        // dh = b^{G_L} dh' + Q^T (scale b^G dO) - K^T (b^G Z), keys 32w .. +31
-        const float gam = gm[3 * BT];
+        // dh = gamma dh' + Qd^T (scale dO) - Kd^T Z, keys 32w .. +31 (scalar
+        // gate: Q^T (scale b^G dO) - K^T (b^G Z))
+        const float gam = PK ? 0.0f : gm[3 * BT];
         for (int kt = 0; kt < 2; ++kt)
             for (int ct = 0; ct < 2; ++ct) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acz = {0.f, 0.f, 0.f, 0.f};
                 const int key0 = 32 * w + 16 * kt;
                 mmf<BT>(acc, [&](int m, int k) { return Qs[k * BKL + key0 + m]; },
-                        [&](int k, int nn) { return a.scale * gm[BT + k] * dOs[k * 33 + 16 * ct + nn]; }, G, n);
+                        [&](int k, int nn) { return a.scale * (PK ? 1.0f : gm[BT + k]) * dOs[k * 33 + 16 * ct + nn]; },
+                        G, n);
                 mmf<BT>(acz, [&](int m, int k) { return Ks[k * BKL + key0 + m]; },
                         [&](int k, int nn) { return Zs[k * 33 + 16 * ct + nn]; }, G, n);
                 for (int r = 0; r < 4; ++r) {
-                    const float x = gam * dh[kt][ct][r] + acc[r] - acz[r];
+                    const float x = (PK ? gk[kt][r] : gam) * dh[kt][ct][r] + acc[r] - acz[r];
                     dh[kt][ct][r] = x;
                     dhS[(key0 + 4 * G + r) * 33 + 16 * ct + n] = x;
                 }
@@ -262,7 +306,191 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
 constexpr int VT = 16;          // value columns per tile
 constexpr int VTL = VT + 1;
 
+// The per-key finish of bwd_grad_kernel. On entry: dl = dL rows of this wave
+// (negated), X2 = dP (lower with the diagonal), dbT = the column term of
+// dbeta, aQ / aKd / aKg = dQd / dKd / dKg in accumulator layout (rows
+// row0 + 4G + r, key 16j + n), hk = per-thread shares of diag(h dh'^T).
+// Ks and Qs are free: the key slices (k, q, G, dG of 32 keys) live in Qs,
+// the per-key sums in Ks. Wave w owns token block w of both the row and the
+// column products.
 template <class In>
+__device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int head, int len, int row0, int w,
+                                               int G, int n, int lane, int tid, const f32x4* dl, const f32x4* aQ,
+                                               const f32x4* aKd, const f32x4* aKg, float* hk, float* X1,
+                                               const float* X2, float* Ks, float* Qs, const float* bt, float* dbT) {
+    constexpr int SL = 33;                       // row stride of the slice tiles
+    const int H = a.H, ue = a.use_exp2;
+    const float lnb = ue ? 0.6931471805599453f : 1.0f;
+    float* Ksl = Qs;
+    float* Qsl = Qs + BT * SL;
+    float* Gsl = Qs + 2 * BT * SL;
+    float* dGs = Qs + 3 * BT * SL;
+    float* hdK = Ks;                             // [DK] diag(h dh'^T)
+    float* colL = Ks + DK;                       // [4][32] per-wave sums of Kg o dKg
+    const In* kin = reinterpret_cast<const In*>(a.k);
+    const In* qin = reinterpret_cast<const In*>(a.q);
+    const int last = len > 0 ? len - 1 : 0;
+
+    // dL into X1 (strictly lower); diag(h dh'^T) per key over the 16 columns
+    // of each thread group
+    for (int j = 0; j < 4; ++j)
+        for (int r = 0; r < 4; ++r) {
+            const int i = row0 + 4 * G + r, jj = 16 * j + n;
+            X1[i * BTL + jj] = jj < i ? -dl[j][r] : 0.0f;
+        }
+    for (int m = 0; m < 8; ++m) {
+        float x = hk[m];
+        for (int sft = 1; sft < 16; sft <<= 1) x += __shfl_xor(x, sft, 16);
+        if ((tid & 15) == 0) hdK[(tid >> 4) + 16 * m] = x;
+    }
+    float brow[4] = {0.f, 0.f, 0.f, 0.f};        // k_i . R[dL,K]_i over this lane's keys
+
+#pragma unroll
+    for (int s = 0; s < DK / 32; ++s) {
+        const int d0 = 32 * s;
+        __syncthreads();                         // X1 written; the previous slice consumed
+        for (int e = tid; e < BT * 32; e += 256) {
+            const int r = e >> 5, c = e & 31;
+            const bool ok = r < len;
+            const int64_t off = ((t0 + r) * H + head) * DK + d0 + c;
+            Ksl[r * SL + c] = ok ? ldf(kin, off) : 0.0f;
+            Qsl[r * SL + c] = ok ? ldf(qin, off) : 0.0f;
+            Gsl[r * SL + c] = ok ? a.g[off] : 0.0f;
+        }
+        __syncthreads();
+        // G: inclusive sum down each key column, wave w taking columns
+        // 8w .. 8w+7 (rows past the chunk end keep G at its last row)
+        for (int c = 8 * w; c < 8 * w + 8; ++c) {
+            float x = Gsl[lane * SL + c];
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(x, off, 64);
+                if (lane >= off) x += y;
+            }
+            Gsl[lane * SL + c] = x;
+        }
+        __syncthreads();
+        float glp[2] = {0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            const int c = 16 * kt + n;           // slice column of this lane's key
+            const int jt = 2 * s + kt;           // its 16-key tile
+            f32x4 ra = {0.f, 0.f, 0.f, 0.f}, rp = ra, ca = ra, cp = ra;
+            // rows of block w against the earlier blocks: reference row
+            // 16w - 1, the last one before the block
+            if (w > 0) {
+                const int ref = 16 * w - 1;
+                const float gr = Gsl[ref * SL + c];
+                for (int k0 = 0; k0 < 16 * w; k0 += 4) {
+                    const int j = k0 + G;
+                    const float b = Ksl[j * SL + c] * fpow(gr - Gsl[j * SL + c], ue);
+                    ra = __builtin_amdgcn_mfma_f32_16x16x4f32(X1[(row0 + n) * BTL + j], b, ra, 0, 0, 0);
+                    rp = __builtin_amdgcn_mfma_f32_16x16x4f32(X2[(row0 + n) * BTL + j], b, rp, 0, 0, 0);
+                }
+                for (int r = 0; r < 4; ++r) {
+                    const float f = fpow(Gsl[(row0 + 4 * G + r) * SL + c] - gr, ue);
+                    ra[r] *= f;
+                    rp[r] *= f;
+                }
+            }
+            // columns of block w against the later blocks: reference row
+            // 16w + 15, the block's last
+            if (w < 3) {
+                const int ref = 16 * w + 15;
+                const float gr = Gsl[ref * SL + c];
+                for (int k0 = 16 * (w + 1); k0 < BT; k0 += 4) {
+                    const int i = k0 + G;
+                    const float f = fpow(Gsl[i * SL + c] - gr, ue);
+                    ca = __builtin_amdgcn_mfma_f32_16x16x4f32(bt[i] * X1[i * BTL + row0 + n], Ksl[i * SL + c] * f, ca,
+                                                             0, 0, 0);
+                    cp = __builtin_amdgcn_mfma_f32_16x16x4f32(X2[i * BTL + row0 + n], Qsl[i * SL + c] * f, cp, 0, 0, 0);
+                }
+                for (int r = 0; r < 4; ++r) {
+                    const float f = fpow(gr - Gsl[(row0 + 4 * G + r) * SL + c], ue);
+                    ca[r] *= f;
+                    cp[r] *= f;
+                }
+            }
+            // the diagonal block by exponent differences: m <= i feeds the
+            // row products of row i, m >= i the column products of column i
+            for (int r = 0; r < 4; ++r) {
+                const int i = row0 + 4 * G + r;
+                const float gi = Gsl[i * SL + c];
+                float sa = 0.f, sp = 0.f, sc = 0.f, sq = 0.f;
+                for (int m = row0; m < row0 + 16; ++m) {
+                    const float gmv = Gsl[m * SL + c];
+                    const float dd = fpow(m <= i ? gi - gmv : gmv - gi, ue);
+                    const float km = Ksl[m * SL + c] * dd;
+                    if (m <= i) {
+                        sa += X1[i * BTL + m] * km;
+                        sp += X2[i * BTL + m] * km;
+                    }
+                    if (m >= i) {
+                        sc += bt[m] * X1[m * BTL + i] * km;
+                        sq += X2[m * BTL + i] * Qsl[m * SL + c] * dd;
+                    }
+                }
+                ra[r] += sa;
+                rp[r] += sp;
+                ca[r] += sc;
+                cp[r] += sq;
+            }
+            // gradients of this lane's rows and key
+            for (int r = 0; r < 4; ++r) {
+                const int i = row0 + 4 * G + r;
+                const float gi = Gsl[i * SL + c];
+                const float e1 = fpow(gi, ue), e2 = fpow(Gsl[last * SL + c] - gi, ue);
+                const float qv = Qsl[i * SL + c], kv = Ksl[i * SL + c];
+                const float dQd = aQ[jt][r], dKd = aKd[jt][r], dKg = aKg[jt][r];
+                const float cs = ca[r] + cp[r];
+                const float dqv = rp[r] + dQd * e1;
+                const float dkv = bt[i] * ra[r] + cs + dKd * e1 + dKg * e2;
+                dGs[i * SL + c] = lnb * (bt[i] * kv * ra[r] + qv * rp[r] - kv * cs + dQd * qv * e1 + dKd * kv * e1 -
+                                         dKg * kv * e2);
+                brow[r] += kv * ra[r];
+                glp[kt] += lnb * dKg * kv * e2;
+                if (i < len) {
+                    const int64_t o = ((t0 + i) * H + head) * DK + d0 + c;
+                    a.dq[o] = dqv;
+                    a.dk[o] = dkv;
+                }
+            }
+        }
+        for (int kt = 0; kt < 2; ++kt) {
+            float x = glp[kt];
+            x += __shfl_xor(x, 16, 64);
+            x += __shfl_xor(x, 32, 64);
+            if (G == 0) colL[w * 32 + 16 * kt + n] = x;
+        }
+        __syncthreads();
+        // dg: reverse cumulative sum down each key column, G_L's gradient
+        // entering at the last valid row; wave w takes columns 8w .. 8w+7
+        for (int c = 8 * w; c < 8 * w + 8; ++c) {
+            const float gl = ((colL[c] + colL[32 + c]) + colL[64 + c]) + colL[96 + c] +
+                             lnb * fpow(Gsl[last * SL + c], ue) * hdK[d0 + c];
+            float x = lane < len ? dGs[lane * SL + c] + (lane == last ? gl : 0.0f) : 0.0f;
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_down(x, off, 64);
+                if (lane + off < 64) x += y;
+            }
+            dGs[lane * SL + c] = x;
+        }
+        __syncthreads();
+        for (int e = tid; e < BT * 32; e += 256) {
+            const int r = e >> 5, c = e & 31;
+            if (r < len) a.dg[((t0 + r) * H + head) * DK + d0 + c] = dGs[r * SL + c];
+        }
+    }
+    // dbeta: the row term summed over the 16 lanes of each group, added to the
+    // column term of the same row (each row has one writer)
+    for (int r = 0; r < 4; ++r)
+        for (int sft = 1; sft < 16; sft <<= 1) brow[r] += __shfl_xor(brow[r], sft, 16);
+    if (n == 0)
+        for (int r = 0; r < 4; ++r) dbT[row0 + 4 * G + r] += brow[r];
+    __syncthreads();
+    if (tid < len) a.dbeta[(t0 + tid) * H + head] = dbT[tid];
+}
+
+template <class In, bool PK>
 __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) float Ks[BT * BKL];
     __shared__ __attribute__((aligned(16))) float Qs[BT * BKL];
@@ -300,7 +528,16 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
     const In* vin = reinterpret_cast<const In*>(a.v);
     const In* dout = reinterpret_cast<const In*>(a.dout);
 
-    load_chunk<In, false>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, gm, bt, tid);
+    if (PK) {
+        // per key: k b^G (for Y) in Ks, T and beta; q, k and G come in key
+        // slices in the finish
+        load_tile<float, BT, DK>(reinterpret_cast<const float*>(a.ws.kd) + ch * (BT * DK), DK, BT, Ks, BKL, tid);
+        load_tile<float, BT, BT>(reinterpret_cast<const float*>(a.ws.Tm) + ch * (BT * BT), BT, BT, Ts, BTL, tid);
+        if (tid < BT) bt[tid] = tid < len ? ldf(reinterpret_cast<const In*>(a.beta), (t0 + tid) * H + head) : 0.0f;
+        __syncthreads();
+    } else {
+        load_chunk<In, false>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, gm, bt, tid);
+    }
     if (tid < BT) rowG[tid] = 0.0f;
     const int row0 = 16 * w;
     auto bG = [&](int row) { return gm[BT + row]; };
@@ -310,6 +547,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
     for (int j = 0; j < 4; ++j) { aP[j] = f32x4{0.f, 0.f, 0.f, 0.f}; aT[j] = aP[j]; }
     for (int j = 0; j < 8; ++j) { aQ[j] = f32x4{0.f, 0.f, 0.f, 0.f}; aKg[j] = aQ[j]; aKd[j] = aQ[j]; }
     float hdh = 0.0f;     // this thread's share of sum(h o dh')
+    float hk[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // per key: keys (tid >> 4) + 16m, column tid & 15
 
     for (int vt = 0; vt < DV / VT; ++vt) {
         const int vc0 = vt * VT;
@@ -320,18 +558,21 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
         load_tile<In, BT, VT>(dout + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, DOs, VTL, tid);
         load_tile<float, BT, VT>(a.dVN + ch * BT * DV + vc0, DV, BT, DVs, VTL, tid);
         __syncthreads();
-        for (int e = tid; e < DK * VT; e += 256) {
-            const int key = e / VT, cl = e - key * VT;
-            hdh += Hs[key * VTL + cl] * DHs[key * VTL + cl];
+#pragma unroll
+        for (int m = 0; m < DK * VT / 256; ++m) {
+            const int e = tid + 256 * m, key = e / VT, cl = e - key * VT;
+            const float x = Hs[key * VTL + cl] * DHs[key * VTL + cl];
+            if (PK) hk[m] += x;
+            else hdh += x;
         }
-        // Y = V - b^G (K h), rows of this wave
+        // Y = V - Kd h, rows of this wave (scalar gate: Kd h = b^G (K h))
         {
             f32x4 kh = {0.f, 0.f, 0.f, 0.f};
             mmf<DK>(kh, [&](int m, int k) { return Ks[(row0 + m) * BKL + k]; },
                     [&](int k, int nn) { return Hs[k * VTL + nn]; }, G, n);
             for (int r = 0; r < 4; ++r) {
                 const int row = row0 + 4 * G + r;
-                Ys[row * VTL + n] = Vs[row * VTL + n] - bG(row) * kh[r];
+                Ys[row * VTL + n] = Vs[row * VTL + n] - (PK ? kh[r] : bG(row) * kh[r]);
             }
         }
         __syncthreads();
@@ -400,10 +641,15 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
         kk[j] = dl[j];
         mmf<BT>(dl[j], [&](int m, int k) { return Ts[k * BTL + row0 + m]; },
                 [&](int k, int nn) { return X1[k * BTL + 16 * j + nn]; }, G, n);
-        mmf<DK>(kk[j], [&](int m, int k) { return Ks[(row0 + m) * BKL + k]; },
-                [&](int k, int nn) { return Ks[(16 * j + nn) * BKL + k]; }, G, n);
+        if (!PK)
+            mmf<DK>(kk[j], [&](int m, int k) { return Ks[(row0 + m) * BKL + k]; },
+                    [&](int k, int nn) { return Ks[(16 * j + nn) * BKL + k]; }, G, n);
     }
     __syncthreads();
+    if (PK) {
+        finish_per_key<In>(a, t0, head, len, row0, w, G, n, lane, tid, dl, aQ, aKd, aKg, hk, X1, X2, Ks, Qs, bt, dbT);
+        return;
+    }
     // element terms of L and P: dbeta_i += sum_j dL_ij G_ij, dG = beta_i dL,
     // the G_i / G_j parts of the gate gradient, and dG o D, dP o D in place
     float rb[4] = {0.f, 0.f, 0.f, 0.f}, rg[4] = {0.f, 0.f, 0.f, 0.f}, cg[4] = {0.f, 0.f, 0.f, 0.f};
@@ -504,18 +750,29 @@ hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* d
     if (launch_prep_f32(p, ws, k, q, g, beta, s) != hipSuccess) return hipGetLastError();
     BwdArgs a;
     a.um = p.um; a.H = p.H; a.use_exp2 = p.use_exp2; a.scale = p.scale;
-    a.q = q; a.k = k; a.v = v; a.beta = beta; a.dout = dout; a.h = h; a.dht = dht;
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g; a.dout = dout; a.h = h; a.dht = dht;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
     a.ws = ws; a.dH = dH; a.dVN = dVN;
     a.n_pairs = p.um.n_units * p.H;
     if (a.n_pairs > 0) {
-        if (p.dtype == 1) hipLaunchKernelGGL(bwd_dh_kernel<bf16>, dim3(4 * a.n_pairs), dim3(256), 0, s, a);
-        else hipLaunchKernelGGL(bwd_dh_kernel<float>, dim3(4 * a.n_pairs), dim3(256), 0, s, a);
+        const dim3 grid(4 * a.n_pairs);
+        if (p.per_key) {
+            if (p.dtype == 1) hipLaunchKernelGGL((bwd_dh_kernel<bf16, true>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((bwd_dh_kernel<float, true>), grid, dim3(256), 0, s, a);
+        } else {
+            if (p.dtype == 1) hipLaunchKernelGGL((bwd_dh_kernel<bf16, false>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((bwd_dh_kernel<float, false>), grid, dim3(256), 0, s, a);
+        }
     }
     if (p.um.n_chunks > 0 && !dh_only) {
         dim3 grid(p.um.n_chunks, p.H);
-        if (p.dtype == 1) hipLaunchKernelGGL(bwd_grad_kernel<bf16>, grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL(bwd_grad_kernel<float>, grid, dim3(256), 0, s, a);
+        if (p.per_key) {
+            if (p.dtype == 1) hipLaunchKernelGGL((bwd_grad_kernel<bf16, true>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((bwd_grad_kernel<float, true>), grid, dim3(256), 0, s, a);
+        } else {
+            if (p.dtype == 1) hipLaunchKernelGGL((bwd_grad_kernel<bf16, false>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((bwd_grad_kernel<float, false>), grid, dim3(256), 0, s, a);
+        }
     }
     return hipGetLastError();
 }

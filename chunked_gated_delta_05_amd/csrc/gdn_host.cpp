@@ -459,8 +459,8 @@ extern "C" gdn_status gdn_state_merge_pieces(int32_t n_pieces, int32_t n_docs, i
 }
 
 // Workspace of the backward: the fp32-operand preparation (T, P and the gate
-// rows of every chunk-head), then dL/dh at every chunk's exit and dvn of
-// every chunk, fp32.
+// rows of every chunk-head; per key, the gated q and k tiles and G_last),
+// then dL/dh at every chunk's exit and dvn of every chunk, fp32.
 static size_t bwd_workspace(const gdn::Problem& p, gdn::Workspace* ws, float** dH, float** dVN, char* base) {
     gdn::Problem pf = p;
     pf.dtype = 0;
@@ -484,7 +484,6 @@ extern "C" gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const v
     gdn::Problem p;
     gdn_status st = validate(desc, &p);
     if (st != GDN_OK) return st;
-    if (p.per_key) return GDN_ERR_UNSUPPORTED;
     if (workspace_bytes == nullptr) return GDN_ERR_INVALID;
     const size_t need = bwd_workspace(p, nullptr, nullptr, nullptr, nullptr);
     if (workspace == nullptr) {
@@ -515,7 +514,6 @@ extern "C" gdn_status gdn_state_grad_summary(const gdn_desc* desc, const void* q
     gdn::Problem p;
     gdn_status st = validate(desc, &p);
     if (st != GDN_OK) return st;
-    if (p.per_key) return GDN_ERR_UNSUPPORTED;
     if (workspace_bytes == nullptr) return GDN_ERR_INVALID;
     const size_t need = bwd_workspace(p, nullptr, nullptr, nullptr, nullptr);
     if (workspace == nullptr) {

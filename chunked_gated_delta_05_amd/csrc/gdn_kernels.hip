@@ -2309,8 +2309,9 @@ hipError_t launch_prep(const Problem& p, const Workspace& ws, const void* k, con
     return hipGetLastError();
 }
 
-// The fp32-operand preparation (T, P and the gate rows in fp32, natural
-// order) for either input dtype: what the backward reads.
+// The fp32-operand preparation (T, P and, for the scalar gate, the gate
+// rows; per key, the gated q and k tiles and G_last) in fp32, natural order,
+// for either input dtype: what the backward reads.
 hipError_t launch_prep_f32(const Problem& p, const Workspace& ws, const void* k, const void* q, const float* g,
                            const void* beta, hipStream_t s) {
     if (p.um.n_chunks == 0) return hipSuccess;
@@ -2320,8 +2321,13 @@ hipError_t launch_prep_f32(const Problem& p, const Workspace& ws, const void* k,
     a.qk_norm = 0; a.beta_sig = 0;
     a.q_hat = nullptr; a.k_hat = nullptr; a.q_rstd = nullptr; a.k_rstd = nullptr; a.beta_eff = nullptr;
     dim3 grid(p.um.n_chunks, p.H), block(256);
-    if (p.dtype == 1) hipLaunchKernelGGL((prep_kernel<PolicyFB, false>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((prep_kernel<PolicyF, false>), grid, block, 0, s, a);
+    if (p.per_key) {
+        if (p.dtype == 1) hipLaunchKernelGGL((prep_kernel<PolicyFB, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((prep_kernel<PolicyF, true>), grid, block, 0, s, a);
+    } else {
+        if (p.dtype == 1) hipLaunchKernelGGL((prep_kernel<PolicyFB, false>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((prep_kernel<PolicyF, false>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 

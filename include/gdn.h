@@ -311,12 +311,13 @@ gdn_status gdn_state_merge(int32_t B, int32_t H, int32_t n_seg, int32_t K, int32
                            float* S_final, hipStream_t stream);
 
 /*
- * gdn_chunk_bwd - gradients of the chunked forward (scalar gate): the
- * backward slots of the native GDN op on the Diff Coverage page
+ * gdn_chunk_bwd - gradients of the chunked forward (scalar or per-key gate):
+ * the backward slots of the native GDN op on the Diff Coverage page
  * (_AscendCGDN.backward: dq, dk, dv, dbeta and the raw-gate gradient dg), by
  * the staged chunk backward of the same page (_AscendCKDAStages.backward:
  * preparation, the reverse state pass chunk_gated_delta_rule_bwd_dhu,
- * finalisation), for L with dL/do = dout and dL/dh_final = dht.
+ * finalisation; per key, the KDA stages with their per-key gate gradient),
+ * for L with dL/do = dout and dL/dh_final = dht.
  *
  *   q, k, v, g, beta  device, the forward's inputs (desc as for gdn_chunk_fwd)
  *   h                 device fp32 [n_chunks][H][K][V]: the state entering every
@@ -326,12 +327,16 @@ gdn_status gdn_state_merge(int32_t B, int32_t H, int32_t n_seg, int32_t K, int32
  *   dht               device fp32 [units][H][K][V] or NULL (zero)
  *   dq, dk            device fp32 [tokens][H][K]
  *   dv                device fp32 [tokens][H][V]
- *   dg, dbeta         device fp32 [tokens][H]
+ *   dg                device fp32 [tokens][H] (scalar gate) or [tokens][H][K]
+ *                     (per key): dL/dg, the gradient of the raw gate
+ *   dbeta             device fp32 [tokens][H]
  *   dh0               device fp32 [units][H][K][V] (dL/d initial_state) or NULL
  *   workspace         as for gdn_chunk_fwd (query its size with NULL); about
- *                     129 KiB per (chunk, head)
- * A per-key gate returns GDN_ERR_UNSUPPORTED. Gradients are fp32 whatever the
- * input dtype; every product runs on fp32 operands.
+ *                     129 KiB per (chunk, head), 225 KiB with a per-key gate
+ * Gradients are fp32 whatever the input dtype; every product runs on fp32
+ * operands. The per-key decay is taken in factors that are at most 1 for
+ * every g <= 0 (as in the forward), so strong gates down to total forgetting
+ * give finite gradients.
  */
 gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, const void* v, const float* g,
                          const void* beta, const float* h, const void* dout, const float* dht, float* dq,
@@ -345,7 +350,7 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
  * with a zero gradient at the unit's exit. It is the reverse state pass of
  * gdn_chunk_bwd without the per-token gradients; the arguments are as there
  * (h from the forward over the same units, the workspace of gdn_chunk_bwd's
- * size), dS_ext device fp32 [units][H][K][V]. Scalar gate only.
+ * size), dS_ext device fp32 [units][H][K][V]. Scalar or per-key gate.
  */
 gdn_status gdn_state_grad_summary(const gdn_desc* desc, const void* q, const void* k, const void* v,
                                   const float* g, const void* beta, const float* h, const void* dout,

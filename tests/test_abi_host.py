@@ -292,7 +292,11 @@ def test_backward_host_checks():
     a256 = lambda x: ((x + 255) // 256) * 256
     prep = 2 * a256(nch * 64 * 64 * 4) + a256(nch * 5 * 64 * 4)
     assert st == gb.GDN_OK and need == a256(prep + nch * 128 * 128 * 4) + a256(nch * 64 * 128 * 4)
-    assert bwd(desc(gate_kind=1), ws=None)[0] == gb.GDN_ERR_UNSUPPORTED
+    # per key: T, P, the gated q and k tiles (q b^G, k b^G, k b^{G_L - G}) and
+    # G_last in fp32, then the same dL/dh and dvn regions
+    stk, needk = bwd(desc(gate_kind=1), ws=None)
+    prepk = 2 * a256(nch * 64 * 64 * 4) + 3 * a256(nch * 64 * 128 * 4) + a256(nch * 128 * 4)
+    assert stk == gb.GDN_OK and needk == a256(prepk + nch * 128 * 128 * 4) + a256(nch * 64 * 128 * 4)
     assert bwd(desc(chunk_size=32), ws=None)[0] == gb.GDN_ERR_INVALID
     assert bwd(desc(), nbytes=need - 1)[0] == gb.GDN_ERR_CAPACITY
     assert bwd(desc(), ws=FAKE + 128)[0] == gb.GDN_ERR_INVALID
@@ -314,7 +318,8 @@ def test_gradient_summary_and_adjoint_errors():
                                   ctypes.byref(nb), None)
     assert st == gb.GDN_OK and nb.value == bwd(desc(), ws=None)[1]
     assert L.gdn_state_grad_summary(ctypes.byref(desc(gate_kind=1)), None, None, None, None, None, None, None,
-                                    None, None, ctypes.byref(nb), None) == gb.GDN_ERR_UNSUPPORTED
+                                    None, None, ctypes.byref(nb), None) == gb.GDN_OK
+    assert nb.value == bwd(desc(gate_kind=1), ws=None)[1]
     big = ctypes.c_size_t(1 << 40)
     # no output
     assert L.gdn_state_grad_summary(ctypes.byref(d), *[FAKE] * 7, None, FAKE, ctypes.byref(big),

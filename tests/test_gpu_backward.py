@@ -17,17 +17,18 @@ DEV = "cuda"
 NAMES = ("dq", "dk", "dv", "dg", "dbeta")
 
 
-def small(B=1, T=200, H=3, dtype="bf16", use_exp2=False, gate_coef=0.1, layout="BSND", n_docs=0):
+def small(B=1, T=200, H=3, dtype="bf16", use_exp2=False, gate_coef=0.1, layout="BSND", n_docs=0, per_key=False):
     return W.Workload("small", B=B, T=T, H=H, dtype=dtype, layout=layout, use_exp2=use_exp2,
-                      gate_coef=gate_coef, n_docs=n_docs)
+                      gate_coef=gate_coef, n_docs=n_docs, gate_per_key=per_key)
 
 
-def packed(lens, H, dtype, seed):
+def packed(lens, H, dtype, seed, per_key=False):
     cu = W.cu_from_lengths(lens)
-    base = W.generate(small(B=1, T=cu[-1], H=H, dtype=dtype), seed)
+    kw = dict(use_exp2=per_key, gate_coef=0.05 if per_key else 0.1, per_key=per_key)
+    base = W.generate(small(B=1, T=cu[-1], H=H, dtype=dtype, **kw), seed)
     d = {n: base[n][0].contiguous().to(DEV) for n in ("q", "k", "v", "g", "beta")}
     d.update(scale=base["scale"], offsets=cu,
-             workload=small(B=1, T=cu[-1], H=H, dtype=dtype, layout="TND", n_docs=len(lens)))
+             workload=small(B=1, T=cu[-1], H=H, dtype=dtype, layout="TND", n_docs=len(lens), **kw))
     return d
 
 
@@ -54,7 +55,8 @@ def run_both(d, seed, S0=False, dht=False, heads=None):
     sel = slice(None) if heads is None else heads
     pick = lambda x: np.ascontiguousarray(x[:, sel])
     ref = oracle.bwd(pick(q), pick(k), pick(v), pick(g), pick(beta), offs, d["scale"], pick(dof),
-                     use_exp2=w.use_exp2, S0=None if s0 is None else np32(s0)[:, sel].astype(np.float64),
+                     gate_per_key=w.gate_per_key, use_exp2=w.use_exp2,
+                     S0=None if s0 is None else np32(s0)[:, sel].astype(np.float64),
                      dht=None if dh is None else np32(dh)[:, sel].astype(np.float64))
     out = {n: pick(np32(flat(got[n]))) for n in NAMES}
     out["dh0"] = np32(got["dh0"])[:, sel]
@@ -167,16 +169,89 @@ def test_backward_is_deterministic():
         assert torch.equal(r1[n], r2[n]), n
 
 
+# ------------------------------------------------------------------ per-key gate
+@pytest.mark.parametrize("B,T,H,dtype,use_exp2", [(2, 150, 2, "bf16", True), (1, 130, 2, "fp32", True),
+                                                  (1, 64, 1, "fp32", False), (1, 1, 2, "bf16", True),
+                                                  (3, 63, 1, "bf16", False), (1, 200, 3, "fp32", False)])
+def test_backward_per_key(B, T, H, dtype, use_exp2):
+    print(f"per-key backward B={B} T={T} H={H} {dtype} exp2={use_exp2}", flush=True)
+    w = small(B=B, T=T, H=H, dtype=dtype, use_exp2=use_exp2, gate_coef=0.05 if use_exp2 else 0.03, per_key=True)
+    d = W.generate(w, 251 + T)
+    out, ref = run_both(d, 19 + T, S0=True, dht=True)
+    check_all(out, ref, TOL[dtype], "per key")
+
+
+@pytest.mark.parametrize("coef", [0.6, 1.0, 4.0])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_backward_per_key_strong_gates(coef, dtype):
+    # per-key decays far past the half-chunk range a middle-row factoring
+    # could hold (log2 units): every gradient finite and at the oracle
+    print(f"per-key backward strong gate c={coef} {dtype}", flush=True)
+    w = small(B=1, T=200, H=2, dtype=dtype, use_exp2=True, gate_coef=coef, per_key=True)
+    d = W.generate(w, 257)
+    out, ref = run_both(d, 21, S0=True, dht=True)
+    for n in NAMES + ("dh0",):
+        assert np.isfinite(out[n]).all(), n
+    check_all(out, ref, TOL[dtype], f"per key c={coef}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_backward_per_key_total_forgetting(dtype):
+    # g = -1e4 on every key: nothing crosses a token, dg vanishes
+    print(f"per-key backward total forgetting {dtype}", flush=True)
+    d = W.generate(small(B=1, T=140, H=2, dtype=dtype, use_exp2=True, per_key=True), 263)
+    d["g"] = torch.full_like(d["g"], -1e4)
+    out, ref = run_both(d, 23, dht=True)
+    for n in NAMES:
+        assert np.isfinite(out[n]).all(), n
+    check_all({n: out[n] for n in ("dq", "dk", "dv", "dbeta", "dh0")} | {"dg": ref["dg"]}, ref, TOL[dtype],
+              "per-key total forgetting")
+    assert np.abs(out["dg"]).max() <= 1e-6 * max(1.0, np.abs(out["dq"]).max())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_backward_per_key_packed_documents(dtype):
+    print(f"per-key backward packed {dtype}", flush=True)
+    d = packed([1, 63, 64, 65, 200, 7, 128], 2, dtype, 269, per_key=True)
+    out, ref = run_both(d, 25, S0=True, dht=True)
+    check_all(out, ref, TOL[dtype], "per-key packed")
+
+
+def test_backward_per_key_segment_shape_sampled_heads():
+    # one segment of the per-key split workload (B=2, 8192 tokens, 8 heads,
+    # log2 gate c = 0.05, bf16), heads 1 and 6 against the oracle
+    w = small(B=2, T=8192, H=8, dtype="bf16", use_exp2=True, gate_coef=0.05, per_key=True)
+    d = W.generate(w, 271, device=DEV)
+    out, ref = run_both(d, 27, heads=[1, 6])
+    errs = check_all(out, ref, TOL["bf16"], "per-key segment")
+    print("per-key segment backward (heads 1, 6): " + ", ".join(f"{n} {e:.1e}" for n, e in errs.items()))
+
+
+def test_backward_per_key_is_deterministic():
+    w = small(B=2, T=300, H=2, use_exp2=True, gate_coef=0.05, per_key=True)
+    d = W.generate(w, 277)
+    x = {n: d[n].to(DEV) for n in ("q", "k", "v", "g", "beta")}
+    _, _, ex = gb.gdn_chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], d["scale"], want_h=True, use_exp2=True)
+    do = torch.randn(x["v"].shape, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).to(DEV)
+    r1 = gb.gdn_chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], ex["h"], do, d["scale"], use_exp2=True)
+    r2 = gb.gdn_chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], ex["h"], do, d["scale"], use_exp2=True)
+    torch.cuda.synchronize()
+    for n in r1:
+        assert torch.equal(r1[n], r2[n]), n
+
+
 # ------------------------------------------------------------------ split backward
-@pytest.mark.parametrize("dtype,with_dht", [("bf16", False), ("fp32", True), ("bf16", True)])
-def test_split_backward_equals_unsplit(dtype, with_dht):
+@pytest.mark.parametrize("dtype,with_dht,per_key", [("bf16", False, False), ("fp32", True, False),
+                                                    ("bf16", True, False), ("bf16", True, True),
+                                                    ("fp32", False, True)])
+def test_split_backward_equals_unsplit(dtype, with_dht, per_key):
     # rows cut at 100 and 190 (inside chunks): gradient summaries of the
     # segments, the adjoint merge with the forward's transfer maps, then
     # every segment's backward from its exit gradient give the unsplit
     # backward, and the oracle's
-    print(f"split backward {dtype} dht={with_dht}", flush=True)
+    print(f"split backward {dtype} dht={with_dht} per_key={per_key}", flush=True)
     B, T, H = 2, 256, 2
-    w = small(B=B, T=T, H=H, dtype=dtype, gate_coef=0.02)
+    w = small(B=B, T=T, H=H, dtype=dtype, gate_coef=0.01 if per_key else 0.02, per_key=per_key, use_exp2=per_key)
     d = W.generate(w, 777)
     dev = {n: d[n].to(DEV) for n in ("q", "k", "v", "g", "beta")}
     gen = torch.Generator().manual_seed(778)
@@ -187,30 +262,34 @@ def test_split_backward_equals_unsplit(dtype, with_dht):
     n_seg = len(seg) - 1
     meta = gb.make_meta(gb.segment_offsets(B, T, seg), B * T, DEV)
     args = (dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"])
-    S_ext, M, _ = gb.gdn_state_summary(dev["k"], dev["v"], dev["g"], dev["beta"], meta=meta)
+    e2 = w.use_exp2
+    S_ext, M, _ = gb.gdn_state_summary(dev["k"], dev["v"], dev["g"], dev["beta"], meta=meta, use_exp2=e2,
+                                       q=dev["q"])
     S_init, _ = gb.gdn_state_merge(S_ext, M, S0, B=B, n_seg=n_seg, want_final=False)
-    _, _, ex = gb.gdn_chunk_fwd(*args, d["scale"], meta=meta, initial_state=S_init, want_h=True)
-    got = gb.split_backward(*args, ex["h"], do, d["scale"], seg=seg, M=M, dht=dht)
-    _, _, exu = gb.gdn_chunk_fwd(*args, d["scale"], initial_state=S0, want_h=True)
-    ref_gpu = gb.gdn_chunk_bwd(*args, exu["h"], do, d["scale"], dht=dht)
+    _, _, ex = gb.gdn_chunk_fwd(*args, d["scale"], meta=meta, initial_state=S_init, want_h=True, use_exp2=e2)
+    got = gb.split_backward(*args, ex["h"], do, d["scale"], seg=seg, M=M, dht=dht, use_exp2=e2)
+    _, _, exu = gb.gdn_chunk_fwd(*args, d["scale"], initial_state=S0, want_h=True, use_exp2=e2)
+    ref_gpu = gb.gdn_chunk_bwd(*args, exu["h"], do, d["scale"], dht=dht, use_exp2=e2)
     torch.cuda.synchronize()
     tol = TOL[dtype]
     for n in NAMES + ("dh0",):
         assert_close(np32(got[n]), np32(ref_gpu[n]), tol, f"split vs unsplit {n}")
     q, k, v, g, beta = flat_inputs(d)
     flat = lambda x: x.reshape(-1, *x.shape[2:])
-    ref = oracle.bwd(q, k, v, g, beta, [0, T, 2 * T], d["scale"], np32(flat(do)),
-                     S0=np32(S0).astype(np.float64), dht=None if dht is None else np32(dht).astype(np.float64))
+    ref = oracle.bwd(q, k, v, g, beta, [0, T, 2 * T], d["scale"], np32(flat(do)), gate_per_key=per_key,
+                     use_exp2=e2, S0=np32(S0).astype(np.float64),
+                     dht=None if dht is None else np32(dht).astype(np.float64))
     for n in NAMES:
         assert_close(np32(flat(got[n])), ref[n], tol, f"split vs oracle {n}")
     assert_close(np32(got["dh0"]), ref["dS0"], tol, "split vs oracle dh0")
 
 
-def test_gradient_summary_against_oracle():
+@pytest.mark.parametrize("per_key", [False, True])
+def test_gradient_summary_against_oracle(per_key):
     # every segment's dL/d(entry state) through its own outputs only
-    print("gradient summary", flush=True)
+    print(f"gradient summary per_key={per_key}", flush=True)
     B, T, H = 1, 300, 2
-    w = small(B=B, T=T, H=H, dtype="fp32", gate_coef=0.05)
+    w = small(B=B, T=T, H=H, dtype="fp32", gate_coef=0.05, per_key=per_key, use_exp2=per_key)
     d = W.generate(w, 790)
     dev = {n: d[n].to(DEV) for n in ("q", "k", "v", "g", "beta")}
     gen = torch.Generator().manual_seed(791)
@@ -219,12 +298,12 @@ def test_gradient_summary_against_oracle():
     offs = [0, 64, 65, 300]
     meta = gb.make_meta(offs, T, DEV)
     args = (dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"])
-    _, _, ex = gb.gdn_chunk_fwd(*args, d["scale"], meta=meta, initial_state=S_in, want_h=True)
-    dS = gb.gdn_state_grad_summary(*args, ex["h"], do, d["scale"], meta=meta)
+    _, _, ex = gb.gdn_chunk_fwd(*args, d["scale"], meta=meta, initial_state=S_in, want_h=True, use_exp2=per_key)
+    dS = gb.gdn_state_grad_summary(*args, ex["h"], do, d["scale"], meta=meta, use_exp2=per_key)
     torch.cuda.synchronize()
     q, k, v, g, beta = flat_inputs(d)
-    ref = oracle.bwd(q, k, v, g, beta, offs, d["scale"], np32(do.reshape(-1, H, 128)),
-                     S0=np32(S_in).astype(np.float64))
+    ref = oracle.bwd(q, k, v, g, beta, offs, d["scale"], np32(do.reshape(-1, H, 128)), gate_per_key=per_key,
+                     use_exp2=per_key, S0=np32(S_in).astype(np.float64))
     assert_close(np32(dS), ref["dS0"], TOL["fp32"], "local dS")
 
 
