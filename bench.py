@@ -39,6 +39,12 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3
 FLOP_PER_TOKEN_HEAD = 139264   # 2 [3KV + (BT/2)(3K + 2V)], K = V = 128, BT = 64
+# The backward's products per token-head: seven full ones of K x V per token
+# (Kg dh', Qd^T dO, Kd^T Z, the recomputed Kd h, dO h^T, v_new dh'^T, Z h^T)
+# and eleven triangular ones of (BT/2) x 128 per token (P^T dO, Tb^T dvn, the
+# recomputed Tb Y, dP, dTb, K K^T and the four dq / dk products with the
+# decayed dL and dP, and the dL solve through T counted as one)
+BWD_FLOP_PER_TOKEN_HEAD = 2 * (7 * 128 * 128 + 11 * 32 * 128)
 KERNEL_SRC = os.path.join(ROOT, "chunked_gated_delta_05_amd", "csrc", "gdn_kernels.hip")
 
 
@@ -156,6 +162,145 @@ def cpu_baseline(d, w, offsets, budget_s: float = 15.0) -> dict:
             "seconds": t, "_result": r, "_sel": sel}
 
 
+def bwd_io_bytes(w, token_heads: int, chunk_heads: int, n_states: int, with_dht: bool) -> int:
+    """The backward's algorithmic bytes: the forward's inputs q, k, v, beta,
+    g and dL/do read once per token-head, the fp32 chunk entry states h
+    (K x V per chunk-head) and dL/d final state when given, and the fp32
+    gradients dq, dk, dv, dg (g's shape), dbeta and dL/d initial state
+    written once."""
+    es = 2 if w.dtype == "bf16" else 4
+    gk = 128 if w.gate_per_key else 1
+    reads = token_heads * (4 * 128 * es + es + 4 * gk) + chunk_heads * 128 * 128 * 4
+    writes = token_heads * (3 * 128 * 4 + 4 * gk + 4) + n_states * 128 * 128 * 4
+    return reads + writes + (n_states * 128 * 128 * 4 if with_dht else 0)
+
+
+def bench_backward(args, wl, d, gb, W, torch):
+    """Times the backward of the workload's forward as a training step runs
+    it: gdn_chunk_bwd over the rows or documents (the fp32 preparation, the
+    reverse state pass, the per-chunk gradients), or for a sequence split the
+    split backward (gradient summaries, adjoint merge, every segment's
+    backward). The forward that supplies h (and, split, the maps M) runs once,
+    untimed. Prints one JSON line."""
+    dev = torch.device("cuda:0")
+    q, k, v, g, beta = (d[n] for n in ("q", "k", "v", "g", "beta"))
+    H, e2 = wl.H, wl.use_exp2
+    gen = torch.Generator().manual_seed(2000)
+    do = torch.randn(v.shape, generator=gen).to(v.dtype).to(dev)
+    tokens = wl.B * wl.T
+    offsets = list(d["offsets"]) if wl.layout == "TND" else [b * wl.T for b in range(wl.B + 1)]
+    chunks = sum((b - a + 63) // 64 for a, b in zip(offsets[:-1], offsets[1:]))
+    n_states = len(offsets) - 1
+    dht = (torch.randn((n_states, H, 128, 128), generator=gen) * 0.1).to(dev) if wl.final_state else None
+    if wl.n_seg:
+        seg = d["seg_offsets"]
+        meta = gb.make_meta(gb.segment_offsets(wl.B, wl.T, seg), tokens, dev)
+        S_ext, M, _ = gb.gdn_state_summary(k, v, g, beta, meta=meta, use_exp2=e2, q=q)
+        S_init, _ = gb.gdn_state_merge(S_ext, M, None, B=wl.B, n_seg=wl.n_seg, want_final=False)
+        _, _, ex = gb.gdn_chunk_fwd(q, k, v, g, beta, d["scale"], meta=meta, initial_state=S_init, want_h=True,
+                                    use_exp2=e2)
+        chunks_run = meta.n_chunks
+
+        def step():
+            return gb.split_backward(q, k, v, g, beta, ex["h"], do, d["scale"], seg=seg, M=M, use_exp2=e2)
+        path = "gradient summaries + adjoint merge + segment backward"
+    else:
+        meta = gb.make_meta(d["offsets"], wl.T, dev) if wl.layout == "TND" else None
+        _, _, ex = gb.gdn_chunk_fwd(q, k, v, g, beta, d["scale"], meta=meta, want_h=True, use_exp2=e2)
+        chunks_run = chunks
+
+        def step():
+            return gb.gdn_chunk_bwd(q, k, v, g, beta, ex["h"], do, d["scale"], meta=meta, dht=dht, use_exp2=e2,
+                                    want_dh0=False)
+        path = "gdn_chunk_bwd"
+    for _ in range(max(args.warmup, 1)):
+        res = step()
+    torch.cuda.synchronize()
+    steps = max(1, min(args.steps, 20))
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    token_heads, chunk_heads = tokens * H, chunks_run * H
+    flops = BWD_FLOP_PER_TOKEN_HEAD * token_heads
+    io = bwd_io_bytes(wl, token_heads, chunk_heads, n_states, dht is not None)
+    tf = flops / (ms * 1e-3) / 1e12
+    out = {"metric": "backward tokens/s", "value": tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+           "steps": steps, "warmup": max(args.warmup, 1), "ms_per_step": ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic", "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": H,
+                                           "gate": "per_key" if wl.gate_per_key else "scalar",
+                                           "input_dtype": wl.dtype, "path": path},
+           "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                        "frac": tf / PEAK_FP32_TFLOPS, "traffic": None,
+                        "note": "whole backward; every product runs on fp32 operands (fp32 MFMA peak)"},
+           "hbm_frac_io": io / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9), "io_bytes": io,
+           "flop_per_token_head": BWD_FLOP_PER_TOKEN_HEAD, "cpu_baseline": None}
+    print(f"[bench] {wl.name} backward: {ms:.3f} ms/step, {tf:.1f} TFLOP/s fp32", file=sys.stderr, flush=True)
+    if not args.no_cpu:
+        out["cpu_baseline"], out["parity_sample_err_over_rms"] = bwd_cpu_baseline(d, wl, offsets, do, dht, res)
+    print(json.dumps(out), flush=True)
+
+
+def bwd_cpu_baseline(d, w, offsets, do, dht, res, budget_s: float = 15.0):
+    """The fp64 backward oracle on a bounded sample of (unit, head) streams,
+    whole streams in order while a one-thread estimate (from one stream's
+    first tokens) fits the budget; returns the baseline and the largest
+    deviation of the GPU's gradients on those streams over their rms."""
+    import numpy as np
+
+    import oracle
+
+    threads = max(1, len(os.sched_getaffinity(0)))
+    flat = {n: W_flat(x, w.layout) for n, x in (("q", d["q"]), ("k", d["k"]), ("v", d["v"]), ("g", d["g"]),
+                                              ("beta", d["beta"]), ("do", do))}
+    streams = [(a, b, h) for a, b in zip(offsets[:-1], offsets[1:]) for h in range(w.H)]
+
+    def pack(sel, limit=None):
+        cut = [(a, b if limit is None else min(b, a + limit), h) for a, b, h in sel]
+        arrs = {n: np.ascontiguousarray(np.concatenate([flat[n][a:b, h:h + 1].float().cpu().numpy()
+                                                        for a, b, h in cut], axis=0)) for n in flat}
+        offs = [0]
+        for a, b, _ in cut:
+            offs.append(offs[-1] + (b - a))
+        return arrs, offs
+
+    def run(sel, nthr, limit=None, dh=None):
+        x, offs = pack(sel, limit)
+        t0 = time.perf_counter()
+        r = oracle.bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], offs, d["scale"], x["do"],
+                       gate_per_key=w.gate_per_key, use_exp2=w.use_exp2, dht=dh, threads=nthr)
+        return time.perf_counter() - t0, r, offs[-1]
+
+    probe = min(1024, streams[0][1] - streams[0][0])
+    t1, _, n1 = run(streams[:1], 1, probe)
+    per_tok = t1 / max(n1, 1)
+    sel, tok = [], 0
+    for st in streams:
+        L = st[1] - st[0]
+        if sel and per_tok * (tok + L) / min(threads, len(sel) + 1) > budget_s:
+            break
+        sel.append(st)
+        tok += L
+    used = min(threads, len(sel))
+    dh = None
+    if dht is not None:
+        units = [offsets.index(a) for a, _, _ in sel]
+        dh = np.ascontiguousarray(np.stack([dht[u, h:h + 1].cpu().numpy() for u, (_, _, h) in zip(units, sel)]))
+    t, r, token_heads = run(sel, used, dh=dh)
+    worst = 0.0
+    for name in ("dq", "dk", "dv", "dbeta"):
+        got = np.concatenate([W_flat(res[name], w.layout)[a:b, h].float().cpu().numpy() for a, b, h in sel], axis=0)
+        ref = r[name][:, 0]
+        worst = max(worst, float(np.abs(got - ref).max() / np.sqrt((ref ** 2).mean())))
+    cb = {"value": token_heads / w.H / t, "unit": "tokens/s", "cores": used, "kind": "oracle",
+          "sample": f"{len(sel)} of {len(streams)} (unit, head) streams of {w.name}, whole streams "
+                    f"({token_heads} token-heads), fp64 reverse-mode token recurrence, {t:.1f} s wall on {used} threads",
+          "seconds": t}
+    return cb, worst
+
+
 def W_flat(x, layout):
     return x.reshape(-1, *x.shape[2:]) if layout == "BSND" else x
 
@@ -176,6 +321,8 @@ def main():
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="extra steps timed one by one after a 512 MiB write that evicts the "
                          "last-level cache (reported as cold_ms_per_step; 0 skips)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward of the workload instead (its own JSON line; at most 20 steps)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device to device (calibrates the HBM byte counters) and exit")
     args = ap.parse_args()
@@ -206,6 +353,9 @@ def main():
     wl = W.WORKLOADS[names.index(args.workload)]
     dev = torch.device("cuda:0")
     d = W.generate(wl, 1000 + names.index(wl.name), device=dev)
+    if args.backward:
+        bench_backward(args, wl, d, gb, W, torch)
+        return
     q, k, v, g, beta = (d[n] for n in ("q", "k", "v", "g", "beta"))
     H, split = wl.H, bool(wl.n_seg)
     o_dtype = torch.float32 if args.o_dtype == "fp32" else v.dtype

@@ -73,7 +73,7 @@ def lib():
         L.gdn_split_meta.argtypes = [_i32p, ctypes.c_int32, _i32p, ctypes.c_int32, ctypes.c_int32, _i32p,
                                      _i32p, _i32p, ctypes.c_int32, _i32p]
         L.gdn_state_grad_summary.restype = ctypes.c_int
-        L.gdn_state_grad_summary.argtypes = [ctypes.POINTER(GdnDesc)] + [vp] * 8 + [vp, sz, vp]
+        L.gdn_state_grad_summary.argtypes = [ctypes.POINTER(GdnDesc)] + [vp] * 8 + [ctypes.c_int32, vp, sz, vp]
         L.gdn_state_merge_adjoint.restype = ctypes.c_int
         L.gdn_state_merge_adjoint.argtypes = [ctypes.c_int32] * 5 + [vp] * 6
         L.gdn_state_merge_pieces.restype = ctypes.c_int
@@ -81,7 +81,7 @@ def lib():
         L.gdn_state_merge.restype = ctypes.c_int
         L.gdn_state_merge.argtypes = [ctypes.c_int32] * 5 + [vp, vp, vp, vp, vp, vp]
         L.gdn_chunk_bwd.restype = ctypes.c_int
-        L.gdn_chunk_bwd.argtypes = [ctypes.POINTER(GdnDesc)] + [vp] * 14 + [vp, sz, vp]
+        L.gdn_chunk_bwd.argtypes = [ctypes.POINTER(GdnDesc)] + [vp] * 14 + [ctypes.c_int32, vp, sz, vp]
         L.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
         L.gdn_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(GdnDesc), vp, vp, vp, vp, vp, vp, vp, vp,
                                             ctypes.POINTER(GdnSlots), ctypes.c_int32, vp]
@@ -467,15 +467,27 @@ def gdn_state_merge(S_ext, M, S0=None, *, B: int, n_seg: int, want_final=True, S
     return S_init, S_final
 
 
+def workspace_bytes_bwd(k, g, meta: UnitMeta | None = None, *, use_exp2=False) -> int:
+    """Workspace bytes of gdn_chunk_bwd / gdn_state_grad_summary for inputs
+    shaped like k and g (the query form of the call)."""
+    H = k.shape[-2]
+    desc = _desc(k, H, k.dtype, k.dtype, g.dim() == k.dim(), use_exp2, 1.0, meta)
+    nb = ctypes.c_size_t(0)
+    check(lib().gdn_chunk_bwd(ctypes.byref(desc), *([None] * 14), 0, None, ctypes.byref(nb), None), "workspace query")
+    return nb.value
+
+
 def gdn_chunk_bwd(q, k, v, g, beta, h, dout, scale=None, *, meta: UnitMeta | None = None, dht=None,
-                  use_exp2=False, want_dh0=True, workspace=None):
+                  use_exp2=False, want_dh0=True, workspace=None, reuse_prepared=False):
     """Gradients of the chunked forward (scalar or per-key gate) through libgdn.
 
     h: the forward's entry states (gdn_chunk_fwd(..., want_h=True) extras
     "h", fp32 [n_chunks, H, K, V]); dout: dL/do in the input dtype, v's
     shape; dht: dL/d(final state) fp32 [units, H, K, V] or None. Returns a
     dict of fp32 tensors dq, dk, dv, dg (g's shape), dbeta and dh0 (dL/d
-    initial state, when wanted)."""
+    initial state, when wanted). reuse_prepared: the given workspace holds the
+    backward preparation of these inputs (from gdn_state_grad_summary or an
+    earlier call)."""
     H, per_key = _check_inputs(q, k, v, g, beta, meta, device_check=False)
     if scale is None:
         scale = k.shape[-1] ** -0.5
@@ -497,14 +509,17 @@ def gdn_chunk_bwd(q, k, v, g, beta, h, dout, scale=None, *, meta: UnitMeta | Non
     if want_dh0:
         out["dh0"] = torch.empty((units, H, K, V), dtype=torch.float32, device=dev)
     nb = ctypes.c_size_t(0)
-    check(lib().gdn_chunk_bwd(ctypes.byref(desc), *([None] * 14), None, ctypes.byref(nb), None), "workspace query")
+    if reuse_prepared and workspace is None:
+        raise ValueError("reuse_prepared needs the workspace that holds the preparation")
+    flags = FLAG_REUSE_PREPARED if reuse_prepared else 0
+    check(lib().gdn_chunk_bwd(ctypes.byref(desc), *([None] * 14), 0, None, ctypes.byref(nb), None), "workspace query")
     ws = workspace if workspace is not None else torch.empty(nb.value, dtype=torch.uint8, device=dev)
     if ws.dtype != torch.uint8 or ws.device != dev or ws.numel() < nb.value:
         raise ValueError(f"workspace must be a uint8 tensor of at least {nb.value} bytes on {dev}")
     nbytes = ctypes.c_size_t(ws.numel())
     check(lib().gdn_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h),
                               _ptr(dout), _ptr(dht), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
-                              _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out.get("dh0")), _ptr(ws),
+                              _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out.get("dh0")), flags, _ptr(ws),
                               ctypes.byref(nbytes), _stream(dev)), "gdn_chunk_bwd")
     return out
 
@@ -524,13 +539,14 @@ def gdn_state_grad_summary(q, k, v, g, beta, h, dout, scale=None, *, meta: UnitM
     _require_gpu(q, k, v, g, beta, meta)
     dS = torch.empty((n_units_of(k, meta), H, K, V), dtype=torch.float32, device=dev)
     nb = ctypes.c_size_t(0)
-    check(lib().gdn_state_grad_summary(ctypes.byref(desc), *([None] * 9), ctypes.byref(nb), None), "workspace query")
+    check(lib().gdn_state_grad_summary(ctypes.byref(desc), *([None] * 8), 0, None, ctypes.byref(nb), None),
+          "workspace query")
     ws = workspace if workspace is not None else torch.empty(nb.value, dtype=torch.uint8, device=dev)
     if ws.dtype != torch.uint8 or ws.device != dev or ws.numel() < nb.value:
         raise ValueError(f"workspace must be a uint8 tensor of at least {nb.value} bytes on {dev}")
     nbytes = ctypes.c_size_t(ws.numel())
     check(lib().gdn_state_grad_summary(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h),
-                                       _ptr(dout), _ptr(dS), _ptr(ws), ctypes.byref(nbytes), _stream(dev)),
+                                       _ptr(dout), _ptr(dS), 0, _ptr(ws), ctypes.byref(nbytes), _stream(dev)),
           "gdn_state_grad_summary")
     return dS
 
@@ -567,10 +583,12 @@ def split_backward(q, k, v, g, beta, h, dout, scale=None, *, seg, M, use_exp2=Fa
     B, T = k.shape[0], k.shape[1]
     n_seg = len(seg) - 1
     meta = make_meta(segment_offsets(B, T, seg), B * T, k.device)
-    dS_ext = gdn_state_grad_summary(q, k, v, g, beta, h, dout, scale, meta=meta, use_exp2=use_exp2)
+    ws = torch.empty(workspace_bytes_bwd(k, g, meta, use_exp2=use_exp2), dtype=torch.uint8, device=k.device)
+    # the gradient summaries prepare the chunks once; the segment backward reuses it
+    dS_ext = gdn_state_grad_summary(q, k, v, g, beta, h, dout, scale, meta=meta, use_exp2=use_exp2, workspace=ws)
     dS_exit, dS0 = gdn_state_merge_adjoint(dS_ext, M, dht, B=B, n_seg=n_seg)
     out = gdn_chunk_bwd(q, k, v, g, beta, h, dout, scale, meta=meta, dht=dS_exit, use_exp2=use_exp2,
-                        want_dh0=False)
+                        want_dh0=False, workspace=ws, reuse_prepared=True)
     out["dh0"] = dS0
     return out
 

@@ -345,18 +345,25 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
     }
     float brow[4] = {0.f, 0.f, 0.f, 0.f};        // k_i . R[dL,K]_i over this lane's keys
 
-#pragma unroll
+    // the slice loop stays rolled (its body is large); the slice's two key
+    // tiles of dQd / dKd / dKg are picked out of the register arrays first
+#pragma unroll 1
     for (int s = 0; s < DK / 32; ++s) {
         const int d0 = 32 * s;
-        __syncthreads();                         // X1 written; the previous slice consumed
-        for (int e = tid; e < BT * 32; e += 256) {
-            const int r = e >> 5, c = e & 31;
-            const bool ok = r < len;
-            const int64_t off = ((t0 + r) * H + head) * DK + d0 + c;
-            Ksl[r * SL + c] = ok ? ldf(kin, off) : 0.0f;
-            Qsl[r * SL + c] = ok ? ldf(qin, off) : 0.0f;
-            Gsl[r * SL + c] = ok ? a.g[off] : 0.0f;
+        f32x4 sQ[2], sKd[2], sKg[2];
+        switch (s) {
+#define GDN_PICK(S)                                                                      \
+    case S:                                                                              \
+        sQ[0] = aQ[2 * S]; sQ[1] = aQ[2 * S + 1]; sKd[0] = aKd[2 * S]; sKd[1] = aKd[2 * S + 1]; \
+        sKg[0] = aKg[2 * S]; sKg[1] = aKg[2 * S + 1];                                   \
+        break;
+            GDN_PICK(0) GDN_PICK(1) GDN_PICK(2) default: GDN_PICK(3)
+#undef GDN_PICK
         }
+        __syncthreads();                         // X1 written; the previous slice consumed
+        load_tile<In, BT, 32>(kin + (t0 * H + head) * DK + d0, (int64_t)H * DK, len, Ksl, SL, tid);
+        load_tile<In, BT, 32>(qin + (t0 * H + head) * DK + d0, (int64_t)H * DK, len, Qsl, SL, tid);
+        load_tile<float, BT, 32>(a.g + (t0 * H + head) * DK + d0, (int64_t)H * DK, len, Gsl, SL, tid);
         __syncthreads();
         // G: inclusive sum down each key column, wave w taking columns
         // 8w .. 8w+7 (rows past the chunk end keep G at its last row)
@@ -373,7 +380,6 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             const int c = 16 * kt + n;           // slice column of this lane's key
-            const int jt = 2 * s + kt;           // its 16-key tile
             f32x4 ra = {0.f, 0.f, 0.f, 0.f}, rp = ra, ca = ra, cp = ra;
             // rows of block w against the earlier blocks: reference row
             // 16w - 1, the last one before the block
@@ -416,6 +422,7 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
                 const int i = row0 + 4 * G + r;
                 const float gi = Gsl[i * SL + c];
                 float sa = 0.f, sp = 0.f, sc = 0.f, sq = 0.f;
+#pragma unroll 2
                 for (int m = row0; m < row0 + 16; ++m) {
                     const float gmv = Gsl[m * SL + c];
                     const float dd = fpow(m <= i ? gi - gmv : gmv - gi, ue);
@@ -440,7 +447,7 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
                 const float gi = Gsl[i * SL + c];
                 const float e1 = fpow(gi, ue), e2 = fpow(Gsl[last * SL + c] - gi, ue);
                 const float qv = Qsl[i * SL + c], kv = Ksl[i * SL + c];
-                const float dQd = aQ[jt][r], dKd = aKd[jt][r], dKg = aKg[jt][r];
+                const float dQd = sQ[kt][r], dKd = sKd[kt][r], dKg = sKg[kt][r];
                 const float cs = ca[r] + cp[r];
                 const float dqv = rp[r] + dQd * e1;
                 const float dkv = bt[i] * ra[r] + cs + dKd * e1 + dKg * e2;
@@ -746,8 +753,8 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
 hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* dVN, const void* q, const void* k,
                       const void* v, const float* g, const void* beta, const float* h, const void* dout,
                       const float* dht, float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0,
-                      bool dh_only, hipStream_t s) {
-    if (launch_prep_f32(p, ws, k, q, g, beta, s) != hipSuccess) return hipGetLastError();
+                      bool dh_only, bool reuse_prep, hipStream_t s) {
+    if (!reuse_prep && launch_prep_f32(p, ws, k, q, g, beta, s) != hipSuccess) return hipGetLastError();
     BwdArgs a;
     a.um = p.um; a.H = p.H; a.use_exp2 = p.use_exp2; a.scale = p.scale;
     a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g; a.dout = dout; a.h = h; a.dht = dht;

@@ -479,11 +479,12 @@ static size_t bwd_workspace(const gdn::Problem& p, gdn::Workspace* ws, float** d
 extern "C" gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, const void* v,
                                     const float* g, const void* beta, const float* h, const void* dout,
                                     const float* dht, float* dq, float* dk, float* dv, float* dg,
-                                    float* dbeta, float* dh0, void* workspace, size_t* workspace_bytes,
-                                    hipStream_t stream) {
+                                    float* dbeta, float* dh0, int32_t flags, void* workspace,
+                                    size_t* workspace_bytes, hipStream_t stream) {
     gdn::Problem p;
     gdn_status st = validate(desc, &p);
     if (st != GDN_OK) return st;
+    if (flags != 0 && flags != GDN_FLAG_REUSE_PREPARED) return GDN_ERR_INVALID;
     if (workspace_bytes == nullptr) return GDN_ERR_INVALID;
     const size_t need = bwd_workspace(p, nullptr, nullptr, nullptr, nullptr);
     if (workspace == nullptr) {
@@ -502,18 +503,19 @@ extern "C" gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const v
     float *dH = nullptr, *dVN = nullptr;
     bwd_workspace(p, &ws, &dH, &dVN, static_cast<char*>(workspace));
     if (gdn::launch_bwd(p, ws, dH, dVN, q, k, v, g, beta, h, dout, dht, dq, dk, dv, dg, dbeta, dh0, false,
-                        stream) != hipSuccess)
+                        flags == GDN_FLAG_REUSE_PREPARED, stream) != hipSuccess)
         return GDN_ERR_DEVICE;
     return GDN_OK;
 }
 
 extern "C" gdn_status gdn_state_grad_summary(const gdn_desc* desc, const void* q, const void* k, const void* v,
                                              const float* g, const void* beta, const float* h, const void* dout,
-                                             float* dS_ext, void* workspace, size_t* workspace_bytes,
-                                             hipStream_t stream) {
+                                             float* dS_ext, int32_t flags, void* workspace,
+                                             size_t* workspace_bytes, hipStream_t stream) {
     gdn::Problem p;
     gdn_status st = validate(desc, &p);
     if (st != GDN_OK) return st;
+    if (flags != 0 && flags != GDN_FLAG_REUSE_PREPARED) return GDN_ERR_INVALID;
     if (workspace_bytes == nullptr) return GDN_ERR_INVALID;
     const size_t need = bwd_workspace(p, nullptr, nullptr, nullptr, nullptr);
     if (workspace == nullptr) {
@@ -531,7 +533,7 @@ extern "C" gdn_status gdn_state_grad_summary(const gdn_desc* desc, const void* q
     float *dH = nullptr, *dVN = nullptr;
     bwd_workspace(p, &ws, &dH, &dVN, static_cast<char*>(workspace));
     if (gdn::launch_bwd(p, ws, dH, dVN, q, k, v, g, beta, h, dout, nullptr, nullptr, nullptr, nullptr, nullptr,
-                        nullptr, dS_ext, true, stream) != hipSuccess)
+                        nullptr, dS_ext, true, flags == GDN_FLAG_REUSE_PREPARED, stream) != hipSuccess)
         return GDN_ERR_DEVICE;
     return GDN_OK;
 }

@@ -115,12 +115,12 @@ hipError_t launch_merge_adjoint(int B, int H, int n_seg, const float* dS_ext, co
 hipError_t launch_prep_f32(const Problem& p, const Workspace& ws, const void* k, const void* q,
                            const float* g, const void* beta, hipStream_t s);
 
-// The backward: fp32 preparation, reverse state pass, per-chunk gradients.
+// The backward: fp32 preparation (skipped with reuse_prep: the workspace
+// holds it), reverse state pass, per-chunk gradients (skipped with dh_only).
 hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* dVN, const void* q,
                       const void* k, const void* v, const float* g, const void* beta, const float* h,
                       const void* dout, const float* dht, float* dq, float* dk, float* dv, float* dg,
-                      float* dbeta, float* dh0,
-                      bool dh_only, hipStream_t s);
+                      float* dbeta, float* dh0, bool dh_only, bool reuse_prep, hipStream_t s);
 
 // Host-only checks of a gdn_chunk_fwd call (descriptor, flags, pointers), and
 // the workspace it needs; no HIP call.

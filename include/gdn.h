@@ -331,6 +331,11 @@ gdn_status gdn_state_merge(int32_t B, int32_t H, int32_t n_seg, int32_t K, int32
  *                     (per key): dL/dg, the gradient of the raw gate
  *   dbeta             device fp32 [tokens][H]
  *   dh0               device fp32 [units][H][K][V] (dL/d initial_state) or NULL
+ *   flags             0, or GDN_FLAG_REUSE_PREPARED: the workspace already holds
+ *                     the backward's chunk preparation of this descriptor and
+ *                     these inputs (left there by an earlier gdn_chunk_bwd or
+ *                     gdn_state_grad_summary call), which is then not redone;
+ *                     other bits give GDN_ERR_INVALID
  *   workspace         as for gdn_chunk_fwd (query its size with NULL); about
  *                     129 KiB per (chunk, head), 225 KiB with a per-key gate
  * Gradients are fp32 whatever the input dtype; every product runs on fp32
@@ -340,8 +345,8 @@ gdn_status gdn_state_merge(int32_t B, int32_t H, int32_t n_seg, int32_t K, int32
  */
 gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, const void* v, const float* g,
                          const void* beta, const float* h, const void* dout, const float* dht, float* dq,
-                         float* dk, float* dv, float* dg, float* dbeta, float* dh0, void* workspace,
-                         size_t* workspace_bytes, hipStream_t stream);
+                         float* dk, float* dv, float* dg, float* dbeta, float* dh0, int32_t flags,
+                         void* workspace, size_t* workspace_bytes, hipStream_t stream);
 
 /*
  * gdn_state_grad_summary - the gradient summary of every unit for a split
@@ -349,12 +354,15 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
  * dS_ext[u] = dL/d(entry state of u) through unit u's own outputs only, i.e.
  * with a zero gradient at the unit's exit. It is the reverse state pass of
  * gdn_chunk_bwd without the per-token gradients; the arguments are as there
- * (h from the forward over the same units, the workspace of gdn_chunk_bwd's
- * size), dS_ext device fp32 [units][H][K][V]. Scalar or per-key gate.
+ * (h from the forward over the same units, flags, the workspace of
+ * gdn_chunk_bwd's size), dS_ext device fp32 [units][H][K][V]. Scalar or
+ * per-key gate. The preparation it leaves in the workspace serves a following
+ * gdn_chunk_bwd over the same units with GDN_FLAG_REUSE_PREPARED.
  */
 gdn_status gdn_state_grad_summary(const gdn_desc* desc, const void* q, const void* k, const void* v,
                                   const float* g, const void* beta, const float* h, const void* dout,
-                                  float* dS_ext, void* workspace, size_t* workspace_bytes, hipStream_t stream);
+                                  float* dS_ext, int32_t flags, void* workspace, size_t* workspace_bytes,
+                                  hipStream_t stream);
 
 /*
  * gdn_state_merge_adjoint - the reverse state wavefront of a split backward

@@ -128,9 +128,10 @@ void fuzz_fwd() {
     size_t bneed = 0;
     void* p15[15];
     for (int i = 0; i < 15; ++i) p15[i] = uni(0, 19) ? FAKE : nullptr;
+    const int bflags = pick({0, 0, 1, 2});
     s = gdn_chunk_bwd(&d, p15[0], p15[1], p15[2], (const float*)p15[3], p15[4], (const float*)p15[5], p15[6],
                       (const float*)p15[7], (float*)p15[8], (float*)p15[9], (float*)p15[10], (float*)p15[11],
-                      (float*)p15[12], (float*)p15[13], nullptr, &bneed, nullptr);
+                      (float*)p15[12], (float*)p15[13], bflags, nullptr, &bneed, nullptr);
     tally(s);
     if (s != GDN_OK || bneed > (size_t(128) << 20)) return;
     const size_t bhave = uni(0, 4) ? bneed : bneed - 256;
@@ -139,11 +140,11 @@ void fuzz_fwd() {
     size_t bnb = bhave;
     tally(gdn_chunk_bwd(&d, p15[0], p15[1], p15[2], (const float*)p15[3], p15[4], (const float*)p15[5], p15[6],
                         (const float*)p15[7], (float*)p15[8], (float*)p15[9], (float*)p15[10], (float*)p15[11],
-                        (float*)p15[12], (float*)p15[13], bws, &bnb, nullptr));
+                        (float*)p15[12], (float*)p15[13], bflags, bws, &bnb, nullptr));
     bnb = bhave;
     stub_set_workspace(bws, bhave);
     tally(gdn_state_grad_summary(&d, p15[0], p15[1], p15[2], (const float*)p15[3], p15[4], (const float*)p15[5],
-                                 p15[6], (float*)p15[13], bws, &bnb, nullptr));
+                                 p15[6], (float*)p15[13], bflags, bws, &bnb, nullptr));
     stub_set_workspace(nullptr, 0);
     free(bws);
 }

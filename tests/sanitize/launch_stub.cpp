@@ -119,7 +119,7 @@ hipError_t launch_prep_f32(const Problem& p, const Workspace& ws, const void* k,
 hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* dVN, const void* q, const void* k,
                       const void* v, const float* g, const void* beta, const float* h, const void* dout,
                       const float*, float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0, bool dh_only,
-                      hipStream_t) {
+                      bool, hipStream_t) {
     gdn::Problem pf = p;
     pf.dtype = 0;                  // the backward's preparation has fp32 operands
     check_problem(pf, ws);

@@ -277,11 +277,11 @@ def test_noalloc_rejects_before_any_hip_call():
 
 
 # ------------------------------------------------------------------ backward
-def bwd(d, *, ws=FAKE, nbytes=None, ptrs=None):
+def bwd(d, *, ws=FAKE, nbytes=None, ptrs=None, flags=0):
     # q, k, v, g, beta, h, dout, dht, dq, dk, dv, dg, dbeta, dh0
     p = [FAKE] * 14 if ptrs is None else ptrs
     nb = ctypes.c_size_t(nbytes if nbytes is not None else (1 << 40))
-    return gb.lib().gdn_chunk_bwd(ctypes.byref(d), *p, ws, ctypes.byref(nb), None), nb.value
+    return gb.lib().gdn_chunk_bwd(ctypes.byref(d), *p, flags, ws, ctypes.byref(nb), None), nb.value
 
 
 def test_backward_host_checks():
@@ -298,6 +298,8 @@ def test_backward_host_checks():
     prepk = 2 * a256(nch * 64 * 64 * 4) + 3 * a256(nch * 64 * 128 * 4) + a256(nch * 128 * 4)
     assert stk == gb.GDN_OK and needk == a256(prepk + nch * 128 * 128 * 4) + a256(nch * 64 * 128 * 4)
     assert bwd(desc(chunk_size=32), ws=None)[0] == gb.GDN_ERR_INVALID
+    for f in (2, 3, 4, 8, -1):                       # only REUSE_PREPARED is a backward flag
+        assert bwd(desc(), flags=f)[0] == gb.GDN_ERR_INVALID, f
     assert bwd(desc(), nbytes=need - 1)[0] == gb.GDN_ERR_CAPACITY
     assert bwd(desc(), ws=FAKE + 128)[0] == gb.GDN_ERR_INVALID
     for i in range(14):
@@ -314,15 +316,17 @@ def test_gradient_summary_and_adjoint_errors():
     nb = ctypes.c_size_t(0)
     d = desc()
     # the backward's workspace size, and its checks
-    st = L.gdn_state_grad_summary(ctypes.byref(d), None, None, None, None, None, None, None, None, None,
+    st = L.gdn_state_grad_summary(ctypes.byref(d), None, None, None, None, None, None, None, None, 0, None,
                                   ctypes.byref(nb), None)
     assert st == gb.GDN_OK and nb.value == bwd(desc(), ws=None)[1]
     assert L.gdn_state_grad_summary(ctypes.byref(desc(gate_kind=1)), None, None, None, None, None, None, None,
-                                    None, None, ctypes.byref(nb), None) == gb.GDN_OK
+                                    None, 0, None, ctypes.byref(nb), None) == gb.GDN_OK
     assert nb.value == bwd(desc(gate_kind=1), ws=None)[1]
     big = ctypes.c_size_t(1 << 40)
     # no output
-    assert L.gdn_state_grad_summary(ctypes.byref(d), *[FAKE] * 7, None, FAKE, ctypes.byref(big),
+    assert L.gdn_state_grad_summary(ctypes.byref(d), *[FAKE] * 7, None, 0, FAKE, ctypes.byref(big),
+                                    None) == gb.GDN_ERR_INVALID
+    assert L.gdn_state_grad_summary(ctypes.byref(d), *[FAKE] * 8, 2, FAKE, ctypes.byref(big),
                                     None) == gb.GDN_ERR_INVALID
     assert L.gdn_state_merge_adjoint(2, 3, 4, 64, 128, FAKE, FAKE, None, FAKE, None, None) == gb.GDN_ERR_UNSUPPORTED
     assert L.gdn_state_merge_adjoint(0, 3, 4, 128, 128, FAKE, FAKE, None, FAKE, None, None) == gb.GDN_ERR_INVALID

@@ -61,3 +61,18 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert p.returncode == 2
     assert "one GPU" in p.stderr
+
+
+def test_backward_io_bytes_closed_form():
+    # dense bf16 workload: q, k, v, dL/do (bf16), beta (bf16), g (fp32) read and
+    # dq, dk, dv, dg, dbeta (fp32) written per token-head, h (fp32 K x V) per
+    # chunk-head, and the dL/d initial state of every row
+    import bench
+    from chunked_gated_delta_05_amd import workloads as W
+    w = W.WORKLOADS[1]
+    th, ch, ns = 4 * 4096 * 16, 4 * 64 * 16, 4 * 16
+    per_th = 4 * 128 * 2 + 2 + 4 + 3 * 128 * 4 + 4 + 4
+    assert bench.bwd_io_bytes(w, th, ch, ns, False) == th * per_th + ch * 128 * 128 * 4 + ns * 128 * 128 * 4
+    wk = W.WORKLOADS[3]                          # per-key gate: g and dg are K-vectors
+    per_th_k = 4 * 128 * 2 + 2 + 4 * 128 + 3 * 128 * 4 + 4 * 128 + 4
+    assert bench.bwd_io_bytes(wk, 10, 1, 1, True) == 10 * per_th_k + 128 * 128 * 4 + 2 * 128 * 128 * 4

@@ -169,6 +169,28 @@ def test_backward_is_deterministic():
         assert torch.equal(r1[n], r2[n]), n
 
 
+@pytest.mark.parametrize("per_key", [False, True])
+def test_backward_reusing_the_preparation(per_key):
+    # a backward that reuses the preparation a gradient summary left in the
+    # workspace gives the bits of one that prepares itself
+    w = small(B=2, T=200, H=2, use_exp2=per_key, gate_coef=0.05, per_key=per_key)
+    d = W.generate(w, 281)
+    x = [d[n].to(DEV) for n in ("q", "k", "v", "g", "beta")]
+    meta = gb.make_meta([0, 200, 400], 400, DEV)
+    xf = [t.reshape(-1, *t.shape[2:]) for t in x]
+    _, _, ex = gb.gdn_chunk_fwd(*xf, d["scale"], meta=meta, want_h=True, use_exp2=per_key)
+    do = torch.randn(xf[2].shape, generator=torch.Generator().manual_seed(7)).to(xf[2].dtype).to(DEV)
+    r1 = gb.gdn_chunk_bwd(*xf, ex["h"], do, d["scale"], meta=meta, use_exp2=per_key)
+    nb = gb.workspace_bytes_bwd(xf[1], xf[3], meta, use_exp2=per_key)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    gb.gdn_state_grad_summary(*xf, ex["h"], do, d["scale"], meta=meta, use_exp2=per_key, workspace=ws)
+    r2 = gb.gdn_chunk_bwd(*xf, ex["h"], do, d["scale"], meta=meta, use_exp2=per_key, workspace=ws,
+                          reuse_prepared=True)
+    torch.cuda.synchronize()
+    for n in r1:
+        assert torch.equal(r1[n], r2[n]), n
+
+
 # ------------------------------------------------------------------ per-key gate
 @pytest.mark.parametrize("B,T,H,dtype,use_exp2", [(2, 150, 2, "bf16", True), (1, 130, 2, "fp32", True),
                                                   (1, 64, 1, "fp32", False), (1, 1, 2, "bf16", True),
