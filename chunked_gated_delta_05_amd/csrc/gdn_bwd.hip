@@ -24,6 +24,10 @@
 // kda_state_grad_ext_kernel on the state_summary.py page (the state gradient
 // decays by b^{G_L}, then gains Q^T dO scale - W^T (value gradient)).
 //
+// Every barrier is an LDS hand-off (lds_barrier): no thread reads global
+// memory that another thread of the kernel writes, so the per-chunk stores
+// (dh', dvn, dv) stay in flight across barriers.
+//
 // Kernels (fp32 operands on the fp32 16x16x4 MFMA, LDS tiles):
 //   bwd_dh_kernel    one workgroup per (unit, head, 32 value columns): the
 //                    reverse state pass; stores dh' and dvn of every chunk
@@ -155,7 +159,7 @@ __device__ void load_chunk(const BwdArgs& a, int64_t t0, int64_t ch, int head, i
     load_tile<float, BT, BT>(reinterpret_cast<const float*>(a.ws.P) + ch * (BT * BT), BT, BT, Ps, BTL, tid);
     if (tid < BT) bt[tid] = tid < len ? ldf(reinterpret_cast<const In*>(a.beta), (t0 + tid) * a.H + head) : 0.0f;
     gm[tid] = a.ws.gam[ch * (GAMR * BT) + tid];   // rows 0..3 (the backward has no q / k normalisation)
-    __syncthreads();
+    lds_barrier();
     if (TB)
         for (int e = tid; e < BT * BT; e += 256) Ts[(e >> 6) * BTL + (e & 63)] *= bt[e & 63];
 }
@@ -170,51 +174,54 @@ __device__ void load_chunk_pk(const BwdArgs& a, int64_t t0, int64_t ch, int head
     load_tile<float, BT, BT>(reinterpret_cast<const float*>(a.ws.Tm) + ch * (BT * BT), BT, BT, Ts, BTL, tid);
     load_tile<float, BT, BT>(reinterpret_cast<const float*>(a.ws.P) + ch * (BT * BT), BT, BT, Ps, BTL, tid);
     if (tid < BT) bt[tid] = tid < len ? ldf(reinterpret_cast<const In*>(a.beta), (t0 + tid) * a.H + head) : 0.0f;
-    __syncthreads();
+    lds_barrier();
     for (int e = tid; e < BT * BT; e += 256) Ts[(e >> 6) * BTL + (e & 63)] *= bt[e & 63];
 }
 
 }  // namespace
 
 // ------------------------------------------------------------------ reverse state pass
-// One workgroup of four waves per (unit, head, 32 value columns); wave w
-// holds dL/dh for keys 32w .. 32w+31 of the 32 columns (four 16 x 16 tiles).
+// One workgroup of four waves per (unit, head, 16 NCT value columns); wave w
+// holds dL/dh for keys 32w .. 32w+31 of those columns (2 NCT 16 x 16 tiles).
+// NCT = 1 (16-column tiles) doubles the workgroups where 32-column tiles
+// would leave compute units idle.
 // Chunks run from the last: store dh', then dvn = Kg dh' + scale P^T dO (wave
 // w: token rows 16w .. +15), Z = Tb^T dvn, and dh = gamma dh' + scale Qd^T dO
 // - Kd^T Z (per key: the prepared gated tiles, and gamma per key).
-template <class In, bool PK>
+template <class In, bool PK, int NCT>
 __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
+    constexpr int NC = 16 * NCT, CL = NC + 1;   // columns of the tile, LDS row stride
     __shared__ __attribute__((aligned(16))) float Ks[BT * BKL];
     __shared__ __attribute__((aligned(16))) float Qs[BT * BKL];
     __shared__ __attribute__((aligned(16))) float Ts[BT * BTL];     // T diag(beta)
     __shared__ __attribute__((aligned(16))) float Ps[BT * BTL];
     __shared__ __attribute__((aligned(16))) float gm[4 * BT];       // G, b^G, b^{G_L - G}, b^{G_L}
     __shared__ float bt[BT];
-    __shared__ __attribute__((aligned(16))) float dOs[BT * 33];     // dO, 32 columns
-    __shared__ __attribute__((aligned(16))) float dhS[DK * 33];     // dh' [key][column]
-    __shared__ __attribute__((aligned(16))) float dvS[BT * 33];     // dvn
-    __shared__ __attribute__((aligned(16))) float Zs[BT * 33];      // b^G Z
+    __shared__ __attribute__((aligned(16))) float dOs[BT * CL];     // dO of the tile's columns
+    __shared__ __attribute__((aligned(16))) float dhS[DK * CL];     // dh' [key][column]
+    __shared__ __attribute__((aligned(16))) float dvS[BT * CL];     // dvn
+    __shared__ __attribute__((aligned(16))) float Zs[BT * CL];      // b^G Z
 
     const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = a.H;
-    const int tile = blockIdx.x & 3, pair = blockIdx.x >> 2;
+    const int tile = blockIdx.x % (DV / NC), pair = blockIdx.x / (DV / NC);
     if (pair >= a.n_pairs) return;
     const int u = pair / H, head = pair - u * H;
     const UnitInfo ui = uniform(unit_info(a.um, u));
-    const int c0 = tile * 32;
+    const int c0 = tile * NC;
     const int64_t uh = (int64_t)u * H + head;
     const In* dout = reinterpret_cast<const In*>(a.dout);
 
     // dL/dh at the unit's end: keys 32w + 16kt + 4G + r, column c0 + 16ct + n
-    f32x4 dh[2][2];
+    f32x4 dh[2][NCT];
     for (int kt = 0; kt < 2; ++kt)
-        for (int ct = 0; ct < 2; ++ct)
+        for (int ct = 0; ct < NCT; ++ct)
             for (int r = 0; r < 4; ++r) {
                 const int key = 32 * w + 16 * kt + 4 * G + r, col = 16 * ct + n;
                 const float x = a.dht ? a.dht[(uh * DK + key) * DV + c0 + col] : 0.0f;
                 dh[kt][ct][r] = x;
-                dhS[key * 33 + col] = x;
+                dhS[key * CL + col] = x;
             }
 
     for (int c = ui.nch - 1; c >= 0; --c) {
@@ -222,10 +229,10 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
         len = len > BT ? BT : len;
         const int64_t t0 = ui.start + (int64_t)c * BT;
         const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
-        __syncthreads();                               // the previous chunk's tiles are consumed
+        lds_barrier();                               // the previous chunk's tiles are consumed
         if (PK) load_chunk_pk<In>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, bt, tid);
         else load_chunk<In, true>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, gm, bt, tid);
-        load_tile<In, BT, 32>(dout + (t0 * H + head) * DV + c0, (int64_t)H * DV, len, dOs, 33, tid);
+        load_tile<In, BT, NC>(dout + (t0 * H + head) * DV + c0, (int64_t)H * DV, len, dOs, CL, tid);
         float gk[2][4];                                // per key: b^{G_L} of keys 32w + 16kt + 4G + r
         if (PK)
             for (int kt = 0; kt < 2; ++kt)
@@ -233,63 +240,63 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
                     gk[kt][r] = fpow(a.ws.gamL[ch * DK + 32 * w + 16 * kt + 4 * G + r], a.use_exp2);
         // dh' of this chunk to the workspace
         for (int kt = 0; kt < 2; ++kt)
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < NCT; ++ct)
                 for (int r = 0; r < 4; ++r) {
                     const int key = 32 * w + 16 * kt + 4 * G + r;
                     a.dH[(ch * DK + key) * DV + c0 + 16 * ct + n] = dh[kt][ct][r];
                 }
-        __syncthreads();
+        lds_barrier();
         // dvn = Kg dh' + scale P^T dO, token rows 16w .. +15 (scalar gate:
         // Kg = diag(b^{G_L - G}) K)
-        for (int ct = 0; ct < 2; ++ct) {
+        for (int ct = 0; ct < NCT; ++ct) {
             f32x4 kh = {0.f, 0.f, 0.f, 0.f}, pd = {0.f, 0.f, 0.f, 0.f};
             mmf<DK>(kh, [&](int m, int k) { return Ks[(16 * w + m) * BKL + k]; },
-                    [&](int k, int nn) { return dhS[k * 33 + 16 * ct + nn]; }, G, n);
+                    [&](int k, int nn) { return dhS[k * CL + 16 * ct + nn]; }, G, n);
             mmf<BT>(pd, [&](int m, int k) { return Ps[k * BTL + 16 * w + m]; },
-                    [&](int k, int nn) { return dOs[k * 33 + 16 * ct + nn]; }, G, n);
+                    [&](int k, int nn) { return dOs[k * CL + 16 * ct + nn]; }, G, n);
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * w + 4 * G + r;
                 const float x = (PK ? kh[r] : gm[2 * BT + row] * kh[r]) + a.scale * pd[r];
-                dvS[row * 33 + 16 * ct + n] = x;
+                dvS[row * CL + 16 * ct + n] = x;
                 a.dVN[(ch * BT + row) * DV + c0 + 16 * ct + n] = x;
             }
         }
-        __syncthreads();
+        lds_barrier();
         // per key, k b^G takes the place of k b^{G_L - G}
         if (PK) load_tile<float, BT, DK>(reinterpret_cast<const float*>(a.ws.kd) + ch * (BT * DK), DK, BT, Ks, BKL, tid);
         // Z = Tb^T dvn, kept as b^G Z for the scalar gate
-        for (int ct = 0; ct < 2; ++ct) {
+        for (int ct = 0; ct < NCT; ++ct) {
             f32x4 z = {0.f, 0.f, 0.f, 0.f};
             mmf<BT>(z, [&](int m, int k) { return Ts[k * BTL + 16 * w + m]; },
-                    [&](int k, int nn) { return dvS[k * 33 + 16 * ct + nn]; }, G, n);
+                    [&](int k, int nn) { return dvS[k * CL + 16 * ct + nn]; }, G, n);
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * w + 4 * G + r;
-                Zs[row * 33 + 16 * ct + n] = PK ? z[r] : gm[BT + row] * z[r];
+                Zs[row * CL + 16 * ct + n] = PK ? z[r] : gm[BT + row] * z[r];
             }
         }
-        __syncthreads();
+        lds_barrier();
         // dh = gamma dh' + Qd^T (scale dO) - Kd^T Z, keys 32w .. +31 (scalar
         // gate: Q^T (scale b^G dO) - K^T (b^G Z))
         const float gam = PK ? 0.0f : gm[3 * BT];
         for (int kt = 0; kt < 2; ++kt)
-            for (int ct = 0; ct < 2; ++ct) {
+            for (int ct = 0; ct < NCT; ++ct) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acz = {0.f, 0.f, 0.f, 0.f};
                 const int key0 = 32 * w + 16 * kt;
                 mmf<BT>(acc, [&](int m, int k) { return Qs[k * BKL + key0 + m]; },
-                        [&](int k, int nn) { return a.scale * (PK ? 1.0f : gm[BT + k]) * dOs[k * 33 + 16 * ct + nn]; },
+                        [&](int k, int nn) { return a.scale * (PK ? 1.0f : gm[BT + k]) * dOs[k * CL + 16 * ct + nn]; },
                         G, n);
                 mmf<BT>(acz, [&](int m, int k) { return Ks[k * BKL + key0 + m]; },
-                        [&](int k, int nn) { return Zs[k * 33 + 16 * ct + nn]; }, G, n);
+                        [&](int k, int nn) { return Zs[k * CL + 16 * ct + nn]; }, G, n);
                 for (int r = 0; r < 4; ++r) {
                     const float x = (PK ? gk[kt][r] : gam) * dh[kt][ct][r] + acc[r] - acz[r];
                     dh[kt][ct][r] = x;
-                    dhS[(key0 + 4 * G + r) * 33 + 16 * ct + n] = x;
+                    dhS[(key0 + 4 * G + r) * CL + 16 * ct + n] = x;
                 }
             }
     }
     if (a.dh0)
         for (int kt = 0; kt < 2; ++kt)
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < NCT; ++ct)
                 for (int r = 0; r < 4; ++r) {
                     const int key = 32 * w + 16 * kt + 4 * G + r;
                     a.dh0[(uh * DK + key) * DV + c0 + 16 * ct + n] = dh[kt][ct][r];
@@ -360,11 +367,11 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
             GDN_PICK(0) GDN_PICK(1) GDN_PICK(2) default: GDN_PICK(3)
 #undef GDN_PICK
         }
-        __syncthreads();                         // X1 written; the previous slice consumed
+        lds_barrier();                         // X1 written; the previous slice consumed
         load_tile<In, BT, 32>(kin + (t0 * H + head) * DK + d0, (int64_t)H * DK, len, Ksl, SL, tid);
         load_tile<In, BT, 32>(qin + (t0 * H + head) * DK + d0, (int64_t)H * DK, len, Qsl, SL, tid);
         load_tile<float, BT, 32>(a.g + (t0 * H + head) * DK + d0, (int64_t)H * DK, len, Gsl, SL, tid);
-        __syncthreads();
+        lds_barrier();
         // G: inclusive sum down each key column, wave w taking columns
         // 8w .. 8w+7 (rows past the chunk end keep G at its last row)
         for (int c = 8 * w; c < 8 * w + 8; ++c) {
@@ -375,7 +382,7 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
             }
             Gsl[lane * SL + c] = x;
         }
-        __syncthreads();
+        lds_barrier();
         float glp[2] = {0.f, 0.f};
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
@@ -468,7 +475,7 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
             x += __shfl_xor(x, 32, 64);
             if (G == 0) colL[w * 32 + 16 * kt + n] = x;
         }
-        __syncthreads();
+        lds_barrier();
         // dg: reverse cumulative sum down each key column, G_L's gradient
         // entering at the last valid row; wave w takes columns 8w .. 8w+7
         for (int c = 8 * w; c < 8 * w + 8; ++c) {
@@ -481,7 +488,7 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
             }
             dGs[lane * SL + c] = x;
         }
-        __syncthreads();
+        lds_barrier();
         for (int e = tid; e < BT * 32; e += 256) {
             const int r = e >> 5, c = e & 31;
             if (r < len) a.dg[((t0 + r) * H + head) * DK + d0 + c] = dGs[r * SL + c];
@@ -493,7 +500,7 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
         for (int sft = 1; sft < 16; sft <<= 1) brow[r] += __shfl_xor(brow[r], sft, 16);
     if (n == 0)
         for (int r = 0; r < 4; ++r) dbT[row0 + 4 * G + r] += brow[r];
-    __syncthreads();
+    lds_barrier();
     if (tid < len) a.dbeta[(t0 + tid) * H + head] = dbT[tid];
 }
 
@@ -541,7 +548,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
         load_tile<float, BT, DK>(reinterpret_cast<const float*>(a.ws.kd) + ch * (BT * DK), DK, BT, Ks, BKL, tid);
         load_tile<float, BT, BT>(reinterpret_cast<const float*>(a.ws.Tm) + ch * (BT * BT), BT, BT, Ts, BTL, tid);
         if (tid < BT) bt[tid] = tid < len ? ldf(reinterpret_cast<const In*>(a.beta), (t0 + tid) * H + head) : 0.0f;
-        __syncthreads();
+        lds_barrier();
     } else {
         load_chunk<In, false>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, gm, bt, tid);
     }
@@ -558,13 +565,13 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
 
     for (int vt = 0; vt < DV / VT; ++vt) {
         const int vc0 = vt * VT;
-        __syncthreads();                           // the previous tile's buffers are consumed
+        lds_barrier();                           // the previous tile's buffers are consumed
         load_tile<float, DK, VT>(a.h + ch * DK * DV + vc0, DV, DK, Hs, VTL, tid);
         load_tile<float, DK, VT>(a.dH + ch * DK * DV + vc0, DV, DK, DHs, VTL, tid);
         load_tile<In, BT, VT>(vin + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, Vs, VTL, tid);
         load_tile<In, BT, VT>(dout + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, DOs, VTL, tid);
         load_tile<float, BT, VT>(a.dVN + ch * BT * DV + vc0, DV, BT, DVs, VTL, tid);
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int m = 0; m < DK * VT / 256; ++m) {
             const int e = tid + 256 * m, key = e / VT, cl = e - key * VT;
@@ -582,7 +589,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
                 Ys[row * VTL + n] = Vs[row * VTL + n] - (PK ? kh[r] : bG(row) * kh[r]);
             }
         }
-        __syncthreads();
+        lds_barrier();
         // v_new = Tb Y and Z = Tb^T dvn = dV, rows of this wave
         {
             f32x4 vn = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
@@ -597,7 +604,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
                 if (row < len) a.dv[((t0 + row) * H + head) * DV + vc0 + n] = z[r];
             }
         }
-        __syncthreads();
+        lds_barrier();
         // accumulate over this tile's columns
         for (int j = 0; j < 4; ++j) {
             mmf<VT>(aP[j], [&](int m, int k) { return a.scale * DOs[(row0 + m) * VTL + k]; },
@@ -614,7 +621,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
                     [&](int k, int nn) { return Hs[(16 * j + nn) * VTL + k]; }, G, n);
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- finish. dTb (lower incl. diagonal) to X1, dP (lower incl.) to X2
     for (int j = 0; j < 4; ++j)
@@ -623,7 +630,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
             X1[i * BTL + jj] = jj <= i ? aT[j][r] : 0.0f;
             X2[i * BTL + jj] = jj <= i ? aP[j][r] : 0.0f;
         }
-    __syncthreads();
+    lds_barrier();
     // dbeta from Tb = T diag(beta): column sums of dTb o T
     if (tid < BT) {
         float s = 0.0f;
@@ -637,10 +644,10 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
         mmf<BT>(m1[j], [&](int m, int k) { return X1[(row0 + m) * BTL + k] * bt[k]; },
                 [&](int k, int nn) { return Ts[(16 * j + nn) * BTL + k]; }, G, n);
     }
-    __syncthreads();
+    lds_barrier();
     for (int j = 0; j < 4; ++j)
         for (int r = 0; r < 4; ++r) X1[(row0 + 4 * G + r) * BTL + 16 * j + n] = m1[j][r];
-    __syncthreads();
+    lds_barrier();
     // dL = -T^T M1 (strictly lower), and G = (K K^T) o D, rows of this wave
     f32x4 dl[4], kk[4];
     for (int j = 0; j < 4; ++j) {
@@ -652,7 +659,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
             mmf<DK>(kk[j], [&](int m, int k) { return Ks[(row0 + m) * BKL + k]; },
                     [&](int k, int nn) { return Ks[(16 * j + nn) * BKL + k]; }, G, n);
     }
-    __syncthreads();
+    lds_barrier();
     if (PK) {
         finish_per_key<In>(a, t0, head, len, row0, w, G, n, lane, tid, dl, aQ, aKd, aKg, hk, X1, X2, Ks, Qs, bt, dbT);
         return;
@@ -695,7 +702,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
             atomicAdd(&rowG[row0 + 4 * G + r], rg[r]);
             atomicAdd(&dbT[row0 + 4 * G + r], rb[r]);
         }
-    __syncthreads();
+    lds_barrier();
     // dq, dk, rows of this wave: the products with dG o D and dP o D, then
     // b^G dQd, b^G dKd + b^{G_L - G} dKg, and their gate terms
     float rq[4] = {0.f, 0.f, 0.f, 0.f}, rkg = 0.0f;
@@ -731,7 +738,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
     float tl = lnb * gm[3 * BT] * hdh + rkg;
     for (int s = 1; s < 64; s <<= 1) tl += __shfl_xor(tl, s, 64);
     if (lane == 0) red[w] = tl;
-    __syncthreads();
+    lds_barrier();
     // dg: reverse cumulative sum over the chunk's rows of the gate gradient,
     // with G_L's entering at the last valid row
     if (w == 0) {
@@ -762,14 +769,23 @@ hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* d
     a.ws = ws; a.dH = dH; a.dVN = dVN;
     a.n_pairs = p.um.n_units * p.H;
     if (a.n_pairs > 0) {
-        const dim3 grid(4 * a.n_pairs);
+        // 32-column tiles while they fill the compute units, else 16-column
+        // tiles (twice the workgroups, half the products per step)
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return hipGetLastError();
+        const bool narrow = 4 * (int64_t)a.n_pairs < cus;
+        const dim3 grid((narrow ? 8 : 4) * a.n_pairs);
+#define GDN_DH(IN, PKV)                                                                            \
+    if (narrow) hipLaunchKernelGGL((bwd_dh_kernel<IN, PKV, 1>), grid, dim3(256), 0, s, a);          \
+    else hipLaunchKernelGGL((bwd_dh_kernel<IN, PKV, 2>), grid, dim3(256), 0, s, a);
         if (p.per_key) {
-            if (p.dtype == 1) hipLaunchKernelGGL((bwd_dh_kernel<bf16, true>), grid, dim3(256), 0, s, a);
-            else hipLaunchKernelGGL((bwd_dh_kernel<float, true>), grid, dim3(256), 0, s, a);
+            if (p.dtype == 1) { GDN_DH(bf16, true) } else { GDN_DH(float, true) }
         } else {
-            if (p.dtype == 1) hipLaunchKernelGGL((bwd_dh_kernel<bf16, false>), grid, dim3(256), 0, s, a);
-            else hipLaunchKernelGGL((bwd_dh_kernel<float, false>), grid, dim3(256), 0, s, a);
+            if (p.dtype == 1) { GDN_DH(bf16, false) } else { GDN_DH(float, false) }
         }
+#undef GDN_DH
     }
     if (p.um.n_chunks > 0 && !dh_only) {
         dim3 grid(p.um.n_chunks, p.H);
