@@ -373,14 +373,15 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
         load_tile<float, BT, 32>(a.g + (t0 * H + head) * DK + d0, (int64_t)H * DK, len, Gsl, SL, tid);
         lds_barrier();
         // G: inclusive sum down each key column, wave w taking columns
-        // 8w .. 8w+7 (rows past the chunk end keep G at its last row)
+        // 8w .. 8w+7 (rows past the chunk end keep G at its last row), in
+        // fp64 and rounded once, as the preparation does
         for (int c = 8 * w; c < 8 * w + 8; ++c) {
-            float x = Gsl[lane * SL + c];
+            double x = Gsl[lane * SL + c];
             for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off, 64);
+                const double y = __shfl_up(x, off, 64);
                 if (lane >= off) x += y;
             }
-            Gsl[lane * SL + c] = x;
+            Gsl[lane * SL + c] = (float)x;
         }
         lds_barrier();
         float glp[2] = {0.f, 0.f};
@@ -424,29 +425,29 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
                 }
             }
             // the diagonal block by exponent differences: m <= i feeds the
-            // row products of row i, m >= i the column products of column i
-            for (int r = 0; r < 4; ++r) {
-                const int i = row0 + 4 * G + r;
-                const float gi = Gsl[i * SL + c];
-                float sa = 0.f, sp = 0.f, sc = 0.f, sq = 0.f;
-#pragma unroll 2
+            // row products of row i, m >= i the column products of column i;
+            // row m's g, k, q and beta are read once for the lane's four rows
+            {
+                float gi[4];
+                for (int r = 0; r < 4; ++r) gi[r] = Gsl[(row0 + 4 * G + r) * SL + c];
+#pragma unroll 4
                 for (int m = row0; m < row0 + 16; ++m) {
-                    const float gmv = Gsl[m * SL + c];
-                    const float dd = fpow(m <= i ? gi - gmv : gmv - gi, ue);
-                    const float km = Ksl[m * SL + c] * dd;
-                    if (m <= i) {
-                        sa += X1[i * BTL + m] * km;
-                        sp += X2[i * BTL + m] * km;
-                    }
-                    if (m >= i) {
-                        sc += bt[m] * X1[m * BTL + i] * km;
-                        sq += X2[m * BTL + i] * Qsl[m * SL + c] * dd;
+                    const float gmv = Gsl[m * SL + c], kmv = Ksl[m * SL + c], qmv = Qsl[m * SL + c], bmv = bt[m];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = row0 + 4 * G + r;
+                        const float dd = fpow(m <= i ? gi[r] - gmv : gmv - gi[r], ue);
+                        const float km = kmv * dd;
+                        if (m <= i) {
+                            ra[r] += X1[i * BTL + m] * km;
+                            rp[r] += X2[i * BTL + m] * km;
+                        }
+                        if (m >= i) {
+                            ca[r] += bmv * X1[m * BTL + i] * km;
+                            cp[r] += X2[m * BTL + i] * qmv * dd;
+                        }
                     }
                 }
-                ra[r] += sa;
-                rp[r] += sp;
-                ca[r] += sc;
-                cp[r] += sq;
             }
             // gradients of this lane's rows and key
             for (int r = 0; r < 4; ++r) {

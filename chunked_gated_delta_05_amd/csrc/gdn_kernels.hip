@@ -316,15 +316,37 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
             if (a.g_cumsum && lane < len) a.g_cumsum[(t0 + lane) * H + head] = x;
         }
     } else {
-        // per-key gate: running sum down each key column
-        if (tid < DK) {
-            float acc = 0.0f;
-            for (int r = 0; r < BT; ++r) {
-                if (r < len) acc += a.g[((t0 + r) * H + head) * DK + tid];
-                Gs[r * (DK + 4) + tid] = acc;
-                if (a.g_cumsum && r < len) a.g_cumsum[((t0 + r) * H + head) * DK + tid] = acc;
+        // per-key gate: the chunk's gates into LDS with 16-byte loads, all
+        // issued before any store (rows past the chunk end read as zero)
+        {
+            constexpr int GV = BT * DK / 4 / 256;    // vectors per thread
+            f32x4 gv[GV];
+#pragma unroll
+            for (int i = 0; i < GV; ++i) {
+                const int e4 = tid + 256 * i, r = e4 / (DK / 4), c4 = (e4 % (DK / 4)) * 4;
+                gv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (r < len) gv[i] = *reinterpret_cast<const f32x4*>(a.g + ((t0 + r) * H + head) * DK + c4);
             }
-            a.ws.gamL[ch * DK + tid] = acc;
+#pragma unroll
+            for (int i = 0; i < GV; ++i) {
+                const int e4 = tid + 256 * i, r = e4 / (DK / 4), c4 = (e4 % (DK / 4)) * 4;
+                *reinterpret_cast<f32x4*>(&Gs[r * (DK + 4) + c4]) = gv[i];
+            }
+        }
+        __syncthreads();
+        // running sum down each key column: wave w scans keys 32w .. 32w+31
+        // with the rows on its lanes (rows past the end keep the last sum),
+        // in fp64 so that every G is the correctly rounded prefix sum
+        for (int d = 32 * w; d < 32 * w + 32; ++d) {
+            double xs = Gs[lane * (DK + 4) + d];
+            for (int off = 1; off < 64; off <<= 1) {
+                const double y = __shfl_up(xs, off, 64);
+                if (lane >= off) xs += y;
+            }
+            const float x = (float)xs;
+            Gs[lane * (DK + 4) + d] = x;
+            if (a.g_cumsum && lane < len) a.g_cumsum[((t0 + lane) * H + head) * DK + d] = x;
+            if (lane == BT - 1) a.ws.gamL[ch * DK + d] = x;
         }
     }
     __syncthreads();
@@ -333,22 +355,49 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     // Per key, an off-diagonal tile (I > J) factors the decay about the last
     // row of block J, so that both factors are at most 1 for any g <= 0; a
     // diagonal tile takes the exponent differences directly.
-    auto direct = [&](const Op* xi, int i, int j) {          // sum_d x_id k_jd b^{G_id - G_jd}
-        float s = 0.0f;
-        for (int d = 0; d < DK; ++d)
-            s += (float)xi[i * LDQ + d] * (float)kt[j * LDQ + d] *
-                 fpow(Gs[i * (DK + 4) + d] - Gs[j * (DK + 4) + d], a.use_exp2);
-        return s;
+    // four rows i0 .. i0+3 against row j: sum_d x_id k_jd b^{G_id - G_jd},
+    // 16-byte reads of four keys at a time, row j's k and G shared by the rows
+    auto direct4 = [&](const Op* xi, int i0, int j, float* out) {
+        float s[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int d = 0; d < DK; d += 4) {
+            const f32x4 kj = *reinterpret_cast<const f32x4*>(&kt[j * LDQ + d]);
+            const f32x4 gj = *reinterpret_cast<const f32x4*>(&Gs[j * (DK + 4) + d]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const f32x4 xv = *reinterpret_cast<const f32x4*>(&xi[(i0 + r) * LDQ + d]);
+                const f32x4 gi = *reinterpret_cast<const f32x4*>(&Gs[(i0 + r) * (DK + 4) + d]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[r] += xv[e] * kj[e] * fpow(gi[e] - gj[e], a.use_exp2);
+            }
+        }
+        for (int r = 0; r < 4; ++r) out[r] = s[r];
+    };
+    // row i against the four rows j0 .. j0+3: sum_d x_id k_jd b^{G_id - G_jd}
+    auto direct4j = [&](const Op* xi, int i, int j0, float* out) {
+        float s[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int d = 0; d < DK; d += 4) {
+            const f32x4 xv = *reinterpret_cast<const f32x4*>(&xi[i * LDQ + d]);
+            const f32x4 gi = *reinterpret_cast<const f32x4*>(&Gs[i * (DK + 4) + d]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const f32x4 kj = *reinterpret_cast<const f32x4*>(&kt[(j0 + r) * LDQ + d]);
+                const f32x4 gj = *reinterpret_cast<const f32x4*>(&Gs[(j0 + r) * (DK + 4) + d]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[r] += xv[e] * kj[e] * fpow(gi[e] - gj[e], a.use_exp2);
+            }
+        }
+        for (int r = 0; r < 4; ++r) out[r] = s[r];
     };
     for (int t = w; t < 10; t += 4) {
         const int it = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
         const int jt = t - (it * (it + 1)) / 2;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         if (PERKEY && it == jt) {
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * it + 4 * G + r, j = 16 * jt + n;
-                acc[r] = j < i ? direct(kt, i, j) : 0.0f;
-            }
+            // lanes whose column is past all four rows skip the sums
+            float dv[4] = {0.f, 0.f, 0.f, 0.f};
+            const int i0 = 16 * it + 4 * G, j = 16 * jt + n;
+            if (j < i0 + 3) direct4(kt, i0, j, dv);
+            for (int r = 0; r < 4; ++r) acc[r] = j < i0 + r ? dv[r] : 0.0f;
         } else {
             for (int kk = 0; kk < DK / 32; ++kk) {
                 const int col = 32 * kk + 8 * G;
@@ -445,10 +494,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
             const int jt = t >> 2, it = t & 3;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             if (PERKEY && jt == it) {
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * it + n, j = 16 * jt + 4 * G + r;
-                    acc[r] = j <= i ? direct(qt, i, j) : 0.0f;
-                }
+                float dv[4] = {0.f, 0.f, 0.f, 0.f};
+                const int i = 16 * it + n, j0 = 16 * jt + 4 * G;
+                if (j0 <= i) direct4j(qt, i, j0, dv);
+                for (int r = 0; r < 4; ++r) acc[r] = j0 + r <= i ? dv[r] : 0.0f;
             } else if (jt <= it) {
                 for (int kk = 0; kk < DK / 32; ++kk) {
                     const int col = 32 * kk + 8 * G;
