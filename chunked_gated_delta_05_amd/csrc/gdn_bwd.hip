@@ -51,7 +51,13 @@
 //   dk = beta o R[dL,K] + C[beta dL,K] + C[dP,Q] + b^G o dKd + b^{G_L-G} o dKg
 //   dG = ln b (beta k o R[dL,K] + q o R[dP,K] - k o (C[beta dL,K] + C[dP,Q])
 //              + Qd o dQd + Kd o dKd - Kg o dKg),   dbeta_i += k_i . R[dL,K]_i
-// and G_L gains ln b (sum_i Kg o dKg + gamma o diag(h dh'^T)). Off the
+// and G_L gains ln b (sum_i Kg o dKg + gamma o diag(h dh'^T)). Since dg is
+// the reverse sum of dG inside the chunk with G_L's gradient at the last
+// row, the two Kg o dKg parts cancel for every row from i on; both gates
+// therefore compute dg_j = sum_{i >= j} dG_i (without the Kg part) + ln b
+// gamma o diag(h dh'^T) + sum_{i < j} ln b Kg_i o dKg_i, which keeps the
+// cancellation out of the rounding (the scalar gate's rows are the same
+// with one key). Off the
 // diagonal 16-row blocks each product splits the decay at a reference row r
 // between the two blocks, b^{G_i - G_r} b^{G_r - G_j}, both factors at most 1
 // for any g <= 0 (the forward's preparation does the same for L and P); the
@@ -311,7 +317,19 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
 // dQd, dKg, dKd (64 x 128) in registers. The finish turns dTb into dL through
 // T, and assembles dq, dk, dbeta and the gate gradients.
 constexpr int VT = 16;          // value columns per tile
-constexpr int VTL = VT + 1;
+constexpr int VTL = VT + 4;     // row stride: 16-byte aligned rows; rows 80 bytes apart hit distinct granules
+
+// acc += A B^T over the 16 value columns of a tile, both operands stored row
+// by row with the columns contiguous: lane (G, n) reads columns 4G .. 4G+3 of
+// row n of each with one 16-byte load, and MFMA e contracts column 4G' + e
+// of every lane group G' (the order of the terms inside one contraction
+// does not matter)
+__device__ __forceinline__ void mm_rows16(f32x4& acc, const float* A, const float* B, float sa, int G, int n) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(A + n * VTL + 4 * G);
+    const f32x4 y = *reinterpret_cast<const f32x4*>(B + n * VTL + 4 * G);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sa * x[e], y[e], acc, 0, 0, 0);
+}
 
 // The per-key finish of bwd_grad_kernel. On entry: dl = dL rows of this wave
 // (negated), X2 = dP (lower with the diagonal), dbT = the column term of
@@ -333,7 +351,7 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
     float* Gsl = Qs + 2 * BT * SL;
     float* dGs = Qs + 3 * BT * SL;
     float* hdK = Ks;                             // [DK] diag(h dh'^T)
-    float* colL = Ks + DK;                       // [4][32] per-wave sums of Kg o dKg
+    float* KGs = Ks + DK;                        // [BT][SL] ln b Kg o dKg of the slice
     const In* kin = reinterpret_cast<const In*>(a.k);
     const In* qin = reinterpret_cast<const In*>(a.q);
     const int last = len > 0 ? len - 1 : 0;
@@ -384,7 +402,6 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
             Gsl[lane * SL + c] = (float)x;
         }
         lds_barrier();
-        float glp[2] = {0.f, 0.f};
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             const int c = 16 * kt + n;           // slice column of this lane's key
@@ -459,10 +476,12 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
                 const float cs = ca[r] + cp[r];
                 const float dqv = rp[r] + dQd * e1;
                 const float dkv = bt[i] * ra[r] + cs + dKd * e1 + dKg * e2;
-                dGs[i * SL + c] = lnb * (bt[i] * kv * ra[r] + qv * rp[r] - kv * cs + dQd * qv * e1 + dKd * kv * e1 -
-                                         dKg * kv * e2);
+                // the Kg term of dG_i without its - ln b Kg o dKg: that part
+                // cancels G_L's + ln b Kg o dKg for every row from i on and
+                // enters dg as the prefix over the earlier rows (below)
+                dGs[i * SL + c] = lnb * (bt[i] * kv * ra[r] + qv * rp[r] - kv * cs + dQd * qv * e1 + dKd * kv * e1);
+                KGs[i * SL + c] = lnb * dKg * kv * e2;
                 brow[r] += kv * ra[r];
-                glp[kt] += lnb * dKg * kv * e2;
                 if (i < len) {
                     const int64_t o = ((t0 + i) * H + head) * DK + d0 + c;
                     a.dq[o] = dqv;
@@ -470,24 +489,22 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
                 }
             }
         }
-        for (int kt = 0; kt < 2; ++kt) {
-            float x = glp[kt];
-            x += __shfl_xor(x, 16, 64);
-            x += __shfl_xor(x, 32, 64);
-            if (G == 0) colL[w * 32 + 16 * kt + n] = x;
-        }
         lds_barrier();
-        // dg: reverse cumulative sum down each key column, G_L's gradient
-        // entering at the last valid row; wave w takes columns 8w .. 8w+7
+        // dg_j = sum_{i >= j} dG_i + ln b gamma diag(h dh'^T) + sum_{i < j}
+        // ln b Kg o dKg: a reverse sum down each key column, the state
+        // decay's term, and the exclusive prefix of the Kg terms; wave w
+        // takes columns 8w .. 8w+7
         for (int c = 8 * w; c < 8 * w + 8; ++c) {
-            const float gl = ((colL[c] + colL[32 + c]) + colL[64 + c]) + colL[96 + c] +
-                             lnb * fpow(Gsl[last * SL + c], ue) * hdK[d0 + c];
+            const float gl = lnb * fpow(Gsl[last * SL + c], ue) * hdK[d0 + c];
             float x = lane < len ? dGs[lane * SL + c] + (lane == last ? gl : 0.0f) : 0.0f;
+            const float kg = lane < len ? KGs[lane * SL + c] : 0.0f;
+            float y = kg;
             for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_down(x, off, 64);
-                if (lane + off < 64) x += y;
+                const float xd = __shfl_down(x, off, 64), yu = __shfl_up(y, off, 64);
+                if (lane + off < 64) x += xd;
+                if (lane >= off) y += yu;
             }
-            dGs[lane * SL + c] = x;
+            dGs[lane * SL + c] = x + (y - kg);
         }
         lds_barrier();
         for (int e = tid; e < BT * 32; e += 256) {
@@ -515,7 +532,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
     __shared__ float bt[BT];
     // value-tile buffers, reused as two 64 x 64 scratch tiles by the finish
     __shared__ __attribute__((aligned(16))) float tb[2 * DK * VTL + 6 * BT * VTL];
-    __shared__ float rowG[BT], colP[4][BT], dbT[BT], red[8];
+    __shared__ float rowG[BT], rowK[BT], colP[4][BT], dbT[BT], red[8];
     float* Hs = tb;                      // h      [key][col]
     float* DHs = Hs + DK * VTL;          // dh'    [key][col]
     float* Vs = DHs + DK * VTL;          // v      [row][col]
@@ -553,7 +570,10 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
     } else {
         load_chunk<In, false>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, gm, bt, tid);
     }
-    if (tid < BT) rowG[tid] = 0.0f;
+    if (tid < BT) {
+        rowG[tid] = 0.0f;
+        rowK[tid] = 0.0f;
+    }
     const int row0 = 16 * w;
     auto bG = [&](int row) { return gm[BT + row]; };
     auto Tb = [&](int i, int j) { return Ts[i * BTL + j] * bt[j]; };   // T diag(beta)
@@ -606,20 +626,15 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
             }
         }
         lds_barrier();
-        // accumulate over this tile's columns
+        // accumulate over this tile's columns (both operands column-contiguous)
         for (int j = 0; j < 4; ++j) {
-            mmf<VT>(aP[j], [&](int m, int k) { return a.scale * DOs[(row0 + m) * VTL + k]; },
-                    [&](int k, int nn) { return VNs[(16 * j + nn) * VTL + k]; }, G, n);
-            mmf<VT>(aT[j], [&](int m, int k) { return DVs[(row0 + m) * VTL + k]; },
-                    [&](int k, int nn) { return Ys[(16 * j + nn) * VTL + k]; }, G, n);
+            mm_rows16(aP[j], DOs + row0 * VTL, VNs + 16 * j * VTL, a.scale, G, n);
+            mm_rows16(aT[j], DVs + row0 * VTL, Ys + 16 * j * VTL, 1.0f, G, n);
         }
         for (int j = 0; j < 8; ++j) {
-            mmf<VT>(aQ[j], [&](int m, int k) { return a.scale * DOs[(row0 + m) * VTL + k]; },
-                    [&](int k, int nn) { return Hs[(16 * j + nn) * VTL + k]; }, G, n);
-            mmf<VT>(aKg[j], [&](int m, int k) { return VNs[(row0 + m) * VTL + k]; },
-                    [&](int k, int nn) { return DHs[(16 * j + nn) * VTL + k]; }, G, n);
-            mmf<VT>(aKd[j], [&](int m, int k) { return -Zs[(row0 + m) * VTL + k]; },
-                    [&](int k, int nn) { return Hs[(16 * j + nn) * VTL + k]; }, G, n);
+            mm_rows16(aQ[j], DOs + row0 * VTL, Hs + 16 * j * VTL, a.scale, G, n);
+            mm_rows16(aKg[j], VNs + row0 * VTL, DHs + 16 * j * VTL, 1.0f, G, n);
+            mm_rows16(aKd[j], Zs + row0 * VTL, Hs + 16 * j * VTL, -1.0f, G, n);
         }
     }
     lds_barrier();
@@ -706,7 +721,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
     lds_barrier();
     // dq, dk, rows of this wave: the products with dG o D and dP o D, then
     // b^G dQd, b^G dKd + b^{G_L - G} dKg, and their gate terms
-    float rq[4] = {0.f, 0.f, 0.f, 0.f}, rkg = 0.0f;
+    float rq[4] = {0.f, 0.f, 0.f, 0.f}, rk[4] = {0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < 8; ++j) {
         f32x4 q1 = {0.f, 0.f, 0.f, 0.f}, k1 = q1;
         mmf<BT>(q1, [&](int m, int k) { return X2[(row0 + m) * BTL + k]; },
@@ -723,8 +738,11 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
             const float qv = Qs[i * BKL + d], kv = Ks[i * BKL + d];
             const float dqv = q1[r] + bg * aQ[j][r];
             const float dkv = k1[r] + bg * aKd[j][r] + blg * aKg[j][r];
-            rq[r] += lnb * (aQ[j][r] * bg * qv + aKd[j][r] * bg * kv - aKg[j][r] * blg * kv);
-            rkg += lnb * aKg[j][r] * blg * kv;
+            // the Kg term (ln b dKg Kg) goes to dg as a prefix over earlier
+            // rows: its - part here and its + part in G_L's gradient cancel
+            // for every row from i on
+            rq[r] += lnb * (aQ[j][r] * bg * qv + aKd[j][r] * bg * kv);
+            rk[r] += lnb * aKg[j][r] * blg * kv;
             if (i < len) {
                 a.dq[((t0 + i) * H + head) * DK + d] = dqv;
                 a.dk[((t0 + i) * H + head) * DK + d] = dkv;
@@ -732,24 +750,35 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
         }
     }
     for (int r = 0; r < 4; ++r)
-        for (int s = 1; s < 16; s <<= 1) rq[r] += __shfl_xor(rq[r], s, 16);
+        for (int s = 1; s < 16; s <<= 1) {
+            rq[r] += __shfl_xor(rq[r], s, 16);
+            rk[r] += __shfl_xor(rk[r], s, 16);
+        }
     if (n == 0)
-        for (int r = 0; r < 4; ++r) atomicAdd(&rowG[row0 + 4 * G + r], rq[r]);
-    // G_L: lnb (gamma sum(h o dh') + sum_i sum_d dKg Kg), summed over the workgroup
-    float tl = lnb * gm[3 * BT] * hdh + rkg;
+        for (int r = 0; r < 4; ++r) {
+            atomicAdd(&rowG[row0 + 4 * G + r], rq[r]);
+            rowK[row0 + 4 * G + r] = rk[r];
+        }
+    // the state decay's term of G_L: lnb gamma sum(h o dh'), over the workgroup
+    float tl = lnb * gm[3 * BT] * hdh;
     for (int s = 1; s < 64; s <<= 1) tl += __shfl_xor(tl, s, 64);
     if (lane == 0) red[w] = tl;
     lds_barrier();
     // dg: reverse cumulative sum over the chunk's rows of the gate gradient,
-    // with G_L's entering at the last valid row
+    // with the state decay's term entering at the last valid row, plus the
+    // exclusive prefix of the Kg terms
     if (w == 0) {
         const float gl = red[0] + red[1] + red[2] + red[3];
         const float colG = ((colP[0][lane] + colP[1][lane]) + colP[2][lane]) + colP[3][lane];
         float x = lane < len ? rowG[lane] + colG + (lane == len - 1 ? gl : 0.0f) : 0.0f;
+        const float kg = lane < len ? rowK[lane] : 0.0f;
+        float y = kg;
         for (int s = 1; s < 64; s <<= 1) {
-            const float y = __shfl_down(x, s, 64);
-            if (lane + s < 64) x += y;
+            const float xd = __shfl_down(x, s, 64), yu = __shfl_up(y, s, 64);
+            if (lane + s < 64) x += xd;
+            if (lane >= s) y += yu;
         }
+        x += y - kg;
         if (lane < len) {
             a.dg[(t0 + lane) * H + head] = x;
             a.dbeta[(t0 + lane) * H + head] = dbT[lane];
