@@ -65,6 +65,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -129,29 +131,45 @@ template <> struct Vec16<bf16> {
     }
 };
 
-// ROWS x NCOLS elements (row r at src + r * stride, rows at or past `valid`
-// read as zero) into an fp32 LDS tile with row stride ld: 16-byte loads, all
-// issued before any store so that their latencies overlap
+// ROWS x NCOLS elements of a tile (row r at src + r * stride, rows at or
+// past `valid` read as zero) as 16-byte vectors in registers: issue() loads
+// them, commit() converts them to fp32 and stores them into an LDS tile with
+// row stride ld (optionally scaling column c by scale[c % 4], the four
+// columns every vector of a thread covers when NCOLS is 4 VPR * 16). Between
+// the two the vectors may stay in flight.
 template <class In, int ROWS, int NCOLS>
-__device__ __forceinline__ void load_tile(const In* src, int64_t stride, int valid, float* dst, int ld, int tid) {
-    constexpr int VPR = Vec16<In>::N, PER_ROW = NCOLS / VPR, NV = ROWS * PER_ROW;
-    constexpr int PT = (NV + 255) / 256;
+struct TileRegs {
+    static constexpr int VPR = Vec16<In>::N, PER_ROW = NCOLS / VPR, NV = ROWS * PER_ROW;
+    static constexpr int PT = (NV + 255) / 256;
     u32x4 w[PT];
+    __device__ __forceinline__ void issue(const In* src, int64_t stride, int valid, int tid) {
 #pragma unroll
-    for (int i = 0; i < PT; ++i) {
-        const int e = tid + 256 * i, r = e / PER_ROW, c = (e - r * PER_ROW) * VPR;
-        w[i] = u32x4{0u, 0u, 0u, 0u};
-        if (e < NV && r < valid) w[i] = *reinterpret_cast<const u32x4*>(src + r * stride + c);
-    }
-#pragma unroll
-    for (int i = 0; i < PT; ++i) {
-        const int e = tid + 256 * i, r = e / PER_ROW, c = (e - r * PER_ROW) * VPR;
-        if (e < NV) {
-            float x[VPR];
-            Vec16<In>::cvt(w[i], x);
-            for (int j = 0; j < VPR; ++j) dst[r * ld + c + j] = x[j];
+        for (int i = 0; i < PT; ++i) {
+            const int e = tid + 256 * i, r = e / PER_ROW, c = (e - r * PER_ROW) * VPR;
+            w[i] = u32x4{0u, 0u, 0u, 0u};
+            if (e < NV && r < valid) w[i] = *reinterpret_cast<const u32x4*>(src + r * stride + c);
         }
     }
+    __device__ __forceinline__ void commit(float* dst, int ld, int tid, const float* colscale = nullptr) const {
+#pragma unroll
+        for (int i = 0; i < PT; ++i) {
+            const int e = tid + 256 * i, r = e / PER_ROW, c = (e - r * PER_ROW) * VPR;
+            if (e < NV) {
+                float x[VPR];
+                Vec16<In>::cvt(w[i], x);
+                for (int j = 0; j < VPR; ++j) dst[r * ld + c + j] = colscale ? x[j] * colscale[j % 4] : x[j];
+            }
+        }
+    }
+};
+
+// a tile into LDS: all loads issued before any store, so that their
+// latencies overlap
+template <class In, int ROWS, int NCOLS>
+__device__ __forceinline__ void load_tile(const In* src, int64_t stride, int valid, float* dst, int ld, int tid) {
+    TileRegs<In, ROWS, NCOLS> t;
+    t.issue(src, stride, valid, tid);
+    t.commit(dst, ld, tid);
 }
 
 // the chunk's k and q tiles, T (or T diag(beta)), P, the gate rows and beta
@@ -230,15 +248,51 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
                 dhS[key * CL + col] = x;
             }
 
+    // bf16 inputs, scalar gate: the next chunk's tiles are loaded into
+    // registers while this chunk is computed (about 70 VGPRs), and written
+    // to LDS at the top of the next step, T already scaled by beta
+    constexpr bool PF = !PK && std::is_same<In, bf16>::value;
+    TileRegs<In, BT, DK> pk_, pq_;
+    TileRegs<float, BT, BT> pt_, pp_;
+    TileRegs<In, BT, NC> pd_;
+    float pg_ = 0.0f, pb_[4] = {0.f, 0.f, 0.f, 0.f};
+    auto prefetch = [&](int cc) {
+        int l = ui.len - cc * BT;
+        l = l > BT ? BT : l;
+        const int64_t tt = ui.start + (int64_t)cc * BT, chh = (int64_t)(ui.cbase + cc) * H + head;
+        const int64_t rs = (int64_t)H * DK;
+        pk_.issue(reinterpret_cast<const In*>(a.k) + (tt * H + head) * DK, rs, l, tid);
+        pq_.issue(reinterpret_cast<const In*>(a.q) + (tt * H + head) * DK, rs, l, tid);
+        pt_.issue(reinterpret_cast<const float*>(a.ws.Tm) + chh * (BT * BT), BT, BT, tid);
+        pp_.issue(reinterpret_cast<const float*>(a.ws.P) + chh * (BT * BT), BT, BT, tid);
+        pd_.issue(dout + (tt * H + head) * DV + c0, (int64_t)H * DV, l, tid);
+        pg_ = a.ws.gam[chh * (GAMR * BT) + tid];      // rows 0..3 (no q / k normalisation here)
+        const int cb = 4 * (tid & 15);                // the columns of this thread's T vectors
+        for (int j = 0; j < 4; ++j)
+            pb_[j] = cb + j < l ? ldf(reinterpret_cast<const In*>(a.beta), (tt + cb + j) * H + head) : 0.0f;
+    };
+    if (PF && ui.nch > 0) prefetch(ui.nch - 1);
+
     for (int c = ui.nch - 1; c >= 0; --c) {
         int len = ui.len - c * BT;
         len = len > BT ? BT : len;
         const int64_t t0 = ui.start + (int64_t)c * BT;
         const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
         lds_barrier();                               // the previous chunk's tiles are consumed
-        if (PK) load_chunk_pk<In>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, bt, tid);
-        else load_chunk<In, true>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, gm, bt, tid);
-        load_tile<In, BT, NC>(dout + (t0 * H + head) * DV + c0, (int64_t)H * DV, len, dOs, CL, tid);
+        if (PF) {
+            pk_.commit(Ks, BKL, tid);
+            pq_.commit(Qs, BKL, tid);
+            pt_.commit(Ts, BTL, tid, pb_);          // T diag(beta)
+            pp_.commit(Ps, BTL, tid);
+            pd_.commit(dOs, CL, tid);
+            gm[tid] = pg_;
+            lds_barrier();
+            if (c > 0) prefetch(c - 1);
+        } else {
+            if (PK) load_chunk_pk<In>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, bt, tid);
+            else load_chunk<In, true>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, gm, bt, tid);
+            load_tile<In, BT, NC>(dout + (t0 * H + head) * DV + c0, (int64_t)H * DV, len, dOs, CL, tid);
+        }
         float gk[2][4];                                // per key: b^{G_L} of keys 32w + 16kt + 4G + r
         if (PK)
             for (int kt = 0; kt < 2; ++kt)
