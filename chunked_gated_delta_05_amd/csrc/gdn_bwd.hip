@@ -638,15 +638,30 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
     float hdh = 0.0f;     // this thread's share of sum(h o dh')
     float hk[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // per key: keys (tid >> 4) + 16m, column tid & 15
 
+    // the value tiles of tile vt + 1 are loaded into registers while tile vt
+    // is computed (28 VGPRs), and written to LDS at the next tile's top
+    TileRegs<float, DK, VT> ph, pdh;
+    TileRegs<In, BT, VT> pv, pdo;
+    TileRegs<float, BT, VT> pdv;
+    auto prefetch = [&](int vt) {
+        const int vc0 = vt * VT;
+        ph.issue(a.h + ch * DK * DV + vc0, DV, DK, tid);
+        pdh.issue(a.dH + ch * DK * DV + vc0, DV, DK, tid);
+        pv.issue(vin + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, tid);
+        pdo.issue(dout + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, tid);
+        pdv.issue(a.dVN + ch * BT * DV + vc0, DV, BT, tid);
+    };
+    prefetch(0);
     for (int vt = 0; vt < DV / VT; ++vt) {
         const int vc0 = vt * VT;
         lds_barrier();                           // the previous tile's buffers are consumed
-        load_tile<float, DK, VT>(a.h + ch * DK * DV + vc0, DV, DK, Hs, VTL, tid);
-        load_tile<float, DK, VT>(a.dH + ch * DK * DV + vc0, DV, DK, DHs, VTL, tid);
-        load_tile<In, BT, VT>(vin + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, Vs, VTL, tid);
-        load_tile<In, BT, VT>(dout + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, DOs, VTL, tid);
-        load_tile<float, BT, VT>(a.dVN + ch * BT * DV + vc0, DV, BT, DVs, VTL, tid);
+        ph.commit(Hs, VTL, tid);
+        pdh.commit(DHs, VTL, tid);
+        pv.commit(Vs, VTL, tid);
+        pdo.commit(DOs, VTL, tid);
+        pdv.commit(DVs, VTL, tid);
         lds_barrier();
+        if (vt + 1 < DV / VT) prefetch(vt + 1);
 #pragma unroll
         for (int m = 0; m < DK * VT / 256; ++m) {
             const int e = tid + 256 * m, key = e / VT, cl = e - key * VT;
