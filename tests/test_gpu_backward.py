@@ -364,3 +364,69 @@ def test_merge_adjoint_kernel_against_oracle(with_final, with_dS0):
         assert_close(got, want_exits, 1e-5, "dS_exit")
         if with_dS0:
             assert_close(np32(dS0[b]), want_G0, 1e-5, "dS0")
+
+
+# ------------------------------------------------------------------ full workloads, sampled heads
+def _bwd_sampled(d, got, do, heads, offs, dht=None):
+    """The oracle's backward on the given heads only (sliced on the GPU
+    before the copy), against the GPU gradients of those heads."""
+    w = d["workload"]
+    flat = (lambda x: x.reshape(-1, *x.shape[2:])) if w.layout == "BSND" else (lambda x: x)
+    sel = lambda x: np32(flat(x)[:, heads].contiguous())
+    q, k, v, g, beta = (sel(d[n]) for n in ("q", "k", "v", "g", "beta"))
+    ref = oracle.bwd(q, k, v, g, beta, offs, d["scale"], sel(do), gate_per_key=w.gate_per_key,
+                     use_exp2=w.use_exp2, dht=None if dht is None else np32(dht[:, heads]).astype(np.float64))
+    tol = TOL[w.dtype]
+    return {n: assert_close(sel(got[n]), ref[n], tol, f"{w.name} {n}") for n in NAMES}
+
+
+def test_backward_packed_workload_sampled_heads():
+    # 20 packed documents, 32768 tokens, 32 heads: the whole backward on the
+    # GPU, heads 3 and 20 against the oracle
+    w = W.WORKLOADS[2]
+    d = W.generate(w, 1002, device=DEV)
+    meta = gb.make_meta(d["offsets"], w.T, DEV)
+    x = [d[n] for n in ("q", "k", "v", "g", "beta")]
+    do = torch.randn(x[2].shape, generator=torch.Generator().manual_seed(31)).to(x[2].dtype).to(DEV)
+    _, _, ex = gb.gdn_chunk_fwd(*x, d["scale"], meta=meta, want_h=True)
+    got = gb.gdn_chunk_bwd(*x, ex["h"], do, d["scale"], meta=meta, want_dh0=False)
+    torch.cuda.synchronize()
+    errs = _bwd_sampled(d, got, do, [3, 20], list(d["offsets"]))
+    print(f"{w.name} backward (heads 3, 20): " + ", ".join(f"{n} {e:.1e}" for n, e in errs.items()))
+
+
+def test_backward_split_workload_sampled_heads():
+    # the per-key split workload (2 rows of 65536 tokens, 8 segments each, 8
+    # heads, log2 gate c = 0.05) through the split backward, as bench.py
+    # times it: gradient summaries, adjoint merge, segment backward; heads 1
+    # and 6 of both rows against the oracle's unsplit backward
+    w = W.WORKLOADS[3]
+    d = W.generate(w, 1003, device=DEV)
+    x = [d[n] for n in ("q", "k", "v", "g", "beta")]
+    seg = d["seg_offsets"]
+    meta = gb.make_meta(gb.segment_offsets(w.B, w.T, seg), w.B * w.T, DEV)
+    S_ext, M, _ = gb.gdn_state_summary(d["k"], d["v"], d["g"], d["beta"], meta=meta, use_exp2=True, q=d["q"])
+    S_init, _ = gb.gdn_state_merge(S_ext, M, None, B=w.B, n_seg=w.n_seg, want_final=False)
+    _, _, ex = gb.gdn_chunk_fwd(*x, d["scale"], meta=meta, initial_state=S_init, want_h=True, use_exp2=True)
+    do = torch.randn(x[2].shape, generator=torch.Generator().manual_seed(33)).to(x[2].dtype).to(DEV)
+    got = gb.split_backward(*x, ex["h"], do, d["scale"], seg=seg, M=M, use_exp2=True)
+    torch.cuda.synchronize()
+    errs = _bwd_sampled(d, got, do, [1, 6], [0, w.T, 2 * w.T])
+    print(f"{w.name} split backward (heads 1, 6): " + ", ".join(f"{n} {e:.1e}" for n, e in errs.items()))
+
+
+def test_backward_long_workload_sampled_head():
+    # one row of 262144 tokens, 32 heads, with dL/d final state: head 5
+    # against the oracle (the reverse state pass runs 4096 chunk steps)
+    w = W.WORKLOADS[4]
+    d = W.generate(w, 1004, device=DEV)
+    x = [d[n] for n in ("q", "k", "v", "g", "beta")]
+    gen = torch.Generator().manual_seed(35)
+    do = torch.randn(x[2].shape, generator=gen).to(x[2].dtype).to(DEV)
+    dht = (torch.randn((1, w.H, 128, 128), generator=gen) * 0.1).to(DEV)
+    _, _, ex = gb.gdn_chunk_fwd(*x, d["scale"], want_h=True)
+    got = gb.gdn_chunk_bwd(*x, ex["h"], do, d["scale"], dht=dht, want_dh0=False)
+    del ex
+    torch.cuda.synchronize()
+    errs = _bwd_sampled(d, got, do, [5], [0, w.T], dht=dht)
+    print(f"{w.name} backward (head 5): " + ", ".join(f"{n} {e:.1e}" for n, e in errs.items()))
