@@ -271,10 +271,21 @@ struct PipeStreams {
 PipeStreams g_pipe[64];
 std::mutex g_pipe_mu;
 
-// the helper stream and events of the current device, made on first use
-PipeStreams* pipe_streams() {
+// the helper stream and events of the current device, made on first use;
+// NULL (the caller then runs the single pass) when they cannot be made,
+// when the caller's stream belongs to another device (whose helper stream
+// would have to be made with that device current), or when the stream is
+// being captured into a graph (the single pass keeps the graph on the
+// caller's stream, with no stream made during the capture)
+PipeStreams* pipe_streams(hipStream_t stream) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    if (stream) {
+        hipDevice_t sdev = 0;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess || sdev != dev) return nullptr;
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+    }
     PipeStreams& ps = g_pipe[dev];
     if (!ps.ready) {
         if (hipStreamCreateWithFlags(&ps.aux, hipStreamNonBlocking) != hipSuccess) return nullptr;
@@ -336,7 +347,7 @@ gdn_status gdn::fwd_impl(const gdn_desc* desc, const void* q, const void* k, con
             ps.beta_eff = slots->beta_eff;
         }
         std::lock_guard<std::mutex> lock(g_pipe_mu);
-        PipeStreams* pst = pipe_streams();
+        PipeStreams* pst = pipe_streams(stream);
         if (pst) {
             gdn::Workspace pws[kPipeMaxPieces];
             float* carry = nullptr;

@@ -58,6 +58,14 @@ hipError_t hipEventCreateWithFlags(hipEvent_t* event, unsigned int) {
     *event = reinterpret_cast<hipEvent_t>(&fake_events[n++ % 16]);
     return hipSuccess;
 }
+hipError_t hipStreamGetDevice(hipStream_t, hipDevice_t* device) {
+    *device = 0;
+    return hipSuccess;
+}
+hipError_t hipStreamIsCapturing(hipStream_t, hipStreamCaptureStatus* status) {
+    *status = hipStreamCaptureStatusNone;
+    return hipSuccess;
+}
 hipError_t hipEventRecord(hipEvent_t event, hipStream_t) { return event ? hipSuccess : hipErrorInvalidValue; }
 hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t event, unsigned int) {
     return event ? hipSuccess : hipErrorInvalidValue;   // the null stream is the default stream

@@ -713,3 +713,35 @@ def test_pieced_forward_equals_one_pass(per_key, dtype, with_final):
     assert_close(flat_o(o1, w)[:, [1]], r["o"], TOL[dtype], "pieced o (head 1)")
     if with_final:
         assert_close(np32(f1[:, [1]]), r["final"], TOL[dtype], "pieced final (head 1)")
+
+
+def test_long_row_forward_under_graph_capture():
+    # a row long enough for the pieced forward, captured into a graph on a
+    # side stream: under capture the forward runs its single pass on the
+    # capturing stream (no helper stream joins the graph); every replay,
+    # with eager work and synchronisations between them, gives the bits of
+    # the eager (pieced) call
+    print("long-row forward under graph capture", flush=True)
+    T = 16384 + 37
+    w = small(B=1, T=T, H=2, dtype="bf16")
+    d = to_dev(W.generate(w, 613))
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"])
+    nb = gb.workspace_bytes(gb._desc(d["k"], 2, d["k"].dtype, torch.float32, False, False, d["scale"], None))
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    o = torch.empty(d["v"].shape, dtype=torch.float32, device=DEV)
+    fin = torch.empty((1, 2, 128, 128), dtype=torch.float32, device=DEV)
+    o_e, f_e, _ = gb.gdn_chunk_fwd(*args, output_final_state=True)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        gb.gdn_chunk_fwd(*args, output_final_state=True, workspace=ws, out=o, final_out=fin)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        o.fill_(float("nan"))
+        fin.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_e) and torch.equal(fin, f_e), f"replay {rep}"
