@@ -372,6 +372,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         }
         for (int r = 0; r < 4; ++r) out[r] = s[r];
     };
+    // eight consecutive fp32 values of an LDS row (16-byte aligned) into registers
+    auto ld8 = [](const float* p, float* x) {
+        const f32x4 u = *reinterpret_cast<const f32x4*>(p), w2 = *reinterpret_cast<const f32x4*>(p + 4);
+        for (int e = 0; e < 4; ++e) { x[e] = u[e]; x[e + 4] = w2[e]; }
+    };
     // row i against the four rows j0 .. j0+3: sum_d x_id k_jd b^{G_id - G_jd}
     auto direct4j = [&](const Op* xi, int i, int j0, float* out) {
         float s[4] = {0.f, 0.f, 0.f, 0.f};
@@ -405,13 +410,15 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
                     P::mma(acc, P::ld(&kt[(16 * it + n) * LDQ + col]), P::ld(&kt[(16 * jt + n) * LDQ + col]));
                 } else {
                     const int ref = 16 * jt + 15;
-                    float xa[8], xb[8];
+                    float gr[8], gi[8], gj[8], ki[8], kj[8], xa[8], xb[8];
+                    ld8(&Gs[ref * (DK + 4) + col], gr);
+                    ld8(&Gs[(16 * it + n) * (DK + 4) + col], gi);
+                    ld8(&Gs[(16 * jt + n) * (DK + 4) + col], gj);
+                    ld8(&kt[(16 * it + n) * LDQ + col], ki);
+                    ld8(&kt[(16 * jt + n) * LDQ + col], kj);
                     for (int e = 0; e < 8; ++e) {
-                        const float gr = Gs[ref * (DK + 4) + col + e];
-                        xa[e] = (float)kt[(16 * it + n) * LDQ + col + e] *
-                                fpow(Gs[(16 * it + n) * (DK + 4) + col + e] - gr, a.use_exp2);
-                        xb[e] = (float)kt[(16 * jt + n) * LDQ + col + e] *
-                                fpow(gr - Gs[(16 * jt + n) * (DK + 4) + col + e], a.use_exp2);
+                        xa[e] = ki[e] * fpow(gi[e] - gr[e], a.use_exp2);
+                        xb[e] = kj[e] * fpow(gr[e] - gj[e], a.use_exp2);
                     }
                     P::mma(acc, P::from(xa), P::from(xb));
                 }
@@ -505,13 +512,15 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
                         P::mma(acc, P::ld(&kt[(16 * jt + n) * LDQ + col]), P::ld(&qt[(16 * it + n) * LDQ + col]));
                     } else {
                         const int ref = 16 * jt + 15;
-                        float xa[8], xb[8];
+                        float gr[8], gi[8], gj[8], kj[8], qi[8], xa[8], xb[8];
+                        ld8(&Gs[ref * (DK + 4) + col], gr);
+                        ld8(&Gs[(16 * it + n) * (DK + 4) + col], gi);
+                        ld8(&Gs[(16 * jt + n) * (DK + 4) + col], gj);
+                        ld8(&kt[(16 * jt + n) * LDQ + col], kj);
+                        ld8(&qt[(16 * it + n) * LDQ + col], qi);
                         for (int e = 0; e < 8; ++e) {
-                            const float gr = Gs[ref * (DK + 4) + col + e];
-                            xa[e] = (float)kt[(16 * jt + n) * LDQ + col + e] *
-                                    fpow(gr - Gs[(16 * jt + n) * (DK + 4) + col + e], a.use_exp2);
-                            xb[e] = (float)qt[(16 * it + n) * LDQ + col + e] *
-                                    fpow(Gs[(16 * it + n) * (DK + 4) + col + e] - gr, a.use_exp2);
+                            xa[e] = kj[e] * fpow(gr[e] - gj[e], a.use_exp2);
+                            xb[e] = qi[e] * fpow(gi[e] - gr[e], a.use_exp2);
                         }
                         P::mma(acc, P::from(xa), P::from(xb));
                     }
@@ -538,12 +547,15 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         for (int e4 = tid; e4 < BT * DK / 4; e4 += 256) {
             const int r = e4 / (DK / 4), c4 = (e4 % (DK / 4)) * 4;
             float xq[4], xd[4], xg[4];
+            const f32x4 gg = *reinterpret_cast<const f32x4*>(&Gs[r * (DK + 4) + c4]);
+            const f32x4 gl = *reinterpret_cast<const f32x4*>(&Gs[last * (DK + 4) + c4]);
+            const f32x4 kv = *reinterpret_cast<const f32x4*>(&kt[r * LDQ + c4]);
+            const f32x4 qv = *reinterpret_cast<const f32x4*>(&qt[r * LDQ + c4]);
             for (int e = 0; e < 4; ++e) {
-                const float gg = Gs[r * (DK + 4) + c4 + e];
-                const float kv = (float)kt[r * LDQ + c4 + e];
-                xq[e] = (float)qt[r * LDQ + c4 + e] * fpow(gg, a.use_exp2);
-                xd[e] = kv * fpow(gg, a.use_exp2);
-                xg[e] = kv * fpow(Gs[last * (DK + 4) + c4 + e] - gg, a.use_exp2);
+                const float bg = fpow(gg[e], a.use_exp2);
+                xq[e] = qv[e] * bg;
+                xd[e] = kv[e] * bg;
+                xg[e] = kv[e] * fpow(gl[e] - gg[e], a.use_exp2);
             }
             const int cp = c4;
             if (has_q) P::st4(qg + r * DK + cp, xq);
