@@ -378,11 +378,24 @@ constexpr int VTL = VT + 4;     // row stride: 16-byte aligned rows; rows 80 byt
 // row n of each with one 16-byte load, and MFMA e contracts column 4G' + e
 // of every lane group G' (the order of the terms inside one contraction
 // does not matter)
+// With H16 (bf16 inputs) the same four columns go as fp16 operands into one
+// 16x16x16 fp16 MFMA (lane (G, n) supplies A[n][4G..4G+3] and B[4G..4G+3][n]
+// there as well), accumulating in fp32.
+template <bool H16>
 __device__ __forceinline__ void mm_rows16(f32x4& acc, const float* A, const float* B, float sa, int G, int n) {
     const f32x4 x = *reinterpret_cast<const f32x4*>(A + n * VTL + 4 * G);
     const f32x4 y = *reinterpret_cast<const f32x4*>(B + n * VTL + 4 * G);
+    if (H16) {
+        f16x4 xh, yh;
+        for (int e = 0; e < 4; ++e) {
+            xh[e] = (f16)(sa * x[e]);
+            yh[e] = (f16)y[e];
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(xh, yh, acc, 0, 0, 0);
+    } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sa * x[e], y[e], acc, 0, 0, 0);
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sa * x[e], y[e], acc, 0, 0, 0);
+    }
 }
 
 // The per-key finish of bwd_grad_kernel. On entry: dl = dL rows of this wave
@@ -638,6 +651,9 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
     float hdh = 0.0f;     // this thread's share of sum(h o dh')
     float hk[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // per key: keys (tid >> 4) + 16m, column tid & 15
 
+    // fp16 operands for the value-tile products with bf16 inputs and a scalar
+    // gate (per key, dg under strong gates needs the fp32 operands)
+    constexpr bool H16 = std::is_same<In, bf16>::value && !PK;
     // the value tiles of tile vt + 1 are loaded into registers while tile vt
     // is computed (28 VGPRs), and written to LDS at the next tile's top
     TileRegs<float, DK, VT> ph, pdh;
@@ -697,13 +713,13 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
         lds_barrier();
         // accumulate over this tile's columns (both operands column-contiguous)
         for (int j = 0; j < 4; ++j) {
-            mm_rows16(aP[j], DOs + row0 * VTL, VNs + 16 * j * VTL, a.scale, G, n);
-            mm_rows16(aT[j], DVs + row0 * VTL, Ys + 16 * j * VTL, 1.0f, G, n);
+            mm_rows16<H16>(aP[j], DOs + row0 * VTL, VNs + 16 * j * VTL, a.scale, G, n);
+            mm_rows16<H16>(aT[j], DVs + row0 * VTL, Ys + 16 * j * VTL, 1.0f, G, n);
         }
         for (int j = 0; j < 8; ++j) {
-            mm_rows16(aQ[j], DOs + row0 * VTL, Hs + 16 * j * VTL, a.scale, G, n);
-            mm_rows16(aKg[j], VNs + row0 * VTL, DHs + 16 * j * VTL, 1.0f, G, n);
-            mm_rows16(aKd[j], Zs + row0 * VTL, Hs + 16 * j * VTL, -1.0f, G, n);
+            mm_rows16<H16>(aQ[j], DOs + row0 * VTL, Hs + 16 * j * VTL, a.scale, G, n);
+            mm_rows16<H16>(aKg[j], VNs + row0 * VTL, DHs + 16 * j * VTL, 1.0f, G, n);
+            mm_rows16<H16>(aKd[j], Zs + row0 * VTL, Hs + 16 * j * VTL, -1.0f, G, n);
         }
     }
     lds_barrier();
