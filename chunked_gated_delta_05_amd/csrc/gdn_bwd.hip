@@ -204,6 +204,30 @@ __device__ void load_chunk_pk(const BwdArgs& a, int64_t t0, int64_t ch, int head
 
 }  // namespace
 
+// acc += A B^T over k in [0, KLEN), A and B stored row by row with k
+// contiguous (rows lda / ldb floats apart, 16-byte aligned): lane (G, n)
+// reads k = k0 + 4G .. +3 of row n of each with one 16-byte load per 16 k,
+// as four fp32 MFMAs or (H16) one fp16 16x16x16 MFMA
+template <bool H16, int KLEN>
+__device__ __forceinline__ void mm_rowsk(f32x4& acc, const float* A, int lda, const float* B, int ldb, int G, int n) {
+#pragma unroll
+    for (int k0 = 0; k0 < KLEN; k0 += 16) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(A + n * lda + k0 + 4 * G);
+        const f32x4 y = *reinterpret_cast<const f32x4*>(B + n * ldb + k0 + 4 * G);
+        if (H16) {
+            f16x4 xh, yh;
+            for (int e = 0; e < 4; ++e) {
+                xh[e] = (f16)x[e];
+                yh[e] = (f16)y[e];
+            }
+            acc = __builtin_amdgcn_mfma_f32_16x16x16f16(xh, yh, acc, 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e], y[e], acc, 0, 0, 0);
+        }
+    }
+}
+
 // ------------------------------------------------------------------ reverse state pass
 // One workgroup of four waves per (unit, head, 16 NCT value columns); wave w
 // holds dL/dh for keys 32w .. 32w+31 of those columns (2 NCT 16 x 16 tiles).
@@ -222,7 +246,7 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) float gm[4 * BT];       // G, b^G, b^{G_L - G}, b^{G_L}
     __shared__ float bt[BT];
     __shared__ __attribute__((aligned(16))) float dOs[BT * CL];     // dO of the tile's columns
-    __shared__ __attribute__((aligned(16))) float dhS[DK * CL];     // dh' [key][column]
+    __shared__ __attribute__((aligned(16))) float dhT[NC * BKL];    // dh' [column][key]
     __shared__ __attribute__((aligned(16))) float dvS[BT * CL];     // dvn
     __shared__ __attribute__((aligned(16))) float Zs[BT * CL];      // b^G Z
 
@@ -245,13 +269,14 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
                 const int key = 32 * w + 16 * kt + 4 * G + r, col = 16 * ct + n;
                 const float x = a.dht ? a.dht[(uh * DK + key) * DV + c0 + col] : 0.0f;
                 dh[kt][ct][r] = x;
-                dhS[key * CL + col] = x;
+                dhT[col * BKL + key] = x;
             }
 
     // bf16 inputs, scalar gate: the next chunk's tiles are loaded into
     // registers while this chunk is computed (about 70 VGPRs), and written
     // to LDS at the top of the next step, T already scaled by beta
     constexpr bool PF = !PK && std::is_same<In, bf16>::value;
+    constexpr bool H16 = PF;                     // Kg dh' on fp16 MFMA (bf16 inputs, scalar gate)
     TileRegs<In, BT, DK> pk_, pq_;
     TileRegs<float, BT, BT> pt_, pp_;
     TileRegs<In, BT, NC> pd_;
@@ -310,8 +335,7 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
         // Kg = diag(b^{G_L - G}) K)
         for (int ct = 0; ct < NCT; ++ct) {
             f32x4 kh = {0.f, 0.f, 0.f, 0.f}, pd = {0.f, 0.f, 0.f, 0.f};
-            mmf<DK>(kh, [&](int m, int k) { return Ks[(16 * w + m) * BKL + k]; },
-                    [&](int k, int nn) { return dhS[k * CL + 16 * ct + nn]; }, G, n);
+            mm_rowsk<H16, DK>(kh, Ks + 16 * w * BKL, BKL, dhT + 16 * ct * BKL, BKL, G, n);
             mmf<BT>(pd, [&](int m, int k) { return Ps[k * BTL + 16 * w + m]; },
                     [&](int k, int nn) { return dOs[k * CL + 16 * ct + nn]; }, G, n);
             for (int r = 0; r < 4; ++r) {
@@ -347,11 +371,9 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
                         G, n);
                 mmf<BT>(acz, [&](int m, int k) { return Ks[k * BKL + key0 + m]; },
                         [&](int k, int nn) { return Zs[k * CL + 16 * ct + nn]; }, G, n);
-                for (int r = 0; r < 4; ++r) {
-                    const float x = (PK ? gk[kt][r] : gam) * dh[kt][ct][r] + acc[r] - acz[r];
-                    dh[kt][ct][r] = x;
-                    dhS[(key0 + 4 * G + r) * CL + 16 * ct + n] = x;
-                }
+                for (int r = 0; r < 4; ++r) dh[kt][ct][r] = (PK ? gk[kt][r] : gam) * dh[kt][ct][r] + acc[r] - acz[r];
+                // keys key0 + 4G .. +3 of column 16 ct + n: one 16-byte store
+                *reinterpret_cast<f32x4*>(&dhT[(16 * ct + n) * BKL + key0 + 4 * G]) = dh[kt][ct];
             }
     }
     if (a.dh0)
