@@ -161,7 +161,41 @@ struct TileRegs {
             }
         }
     }
+    // the same, as fp16 values (8 bytes per fp32 vector, 16 per bf16 one),
+    // and with column c scaled by colscale[c % 4] into dst2 when given
+    __device__ __forceinline__ void commit_h(f16* dst, int ld, int tid, const float* colscale = nullptr,
+                                             f16* dst2 = nullptr) const {
+#pragma unroll
+        for (int i = 0; i < PT; ++i) {
+            const int e = tid + 256 * i, r = e / PER_ROW, c = (e - r * PER_ROW) * VPR;
+            if (e < NV) {
+                float x[VPR];
+                Vec16<In>::cvt(w[i], x);
+                typedef _Float16 hv __attribute__((ext_vector_type(VPR)));
+                hv h;
+                for (int j = 0; j < VPR; ++j) h[j] = (f16)x[j];
+                *reinterpret_cast<hv*>(dst + r * ld + c) = h;
+                if (dst2) {
+                    for (int j = 0; j < VPR; ++j) h[j] = (f16)(x[j] * colscale[j % 4]);
+                    *reinterpret_cast<hv*>(dst2 + r * ld + c) = h;
+                }
+            }
+        }
+    }
 };
+
+// sum over a tile of the elementwise product of two fp32 tiles held with the
+// same thread mapping
+template <int ROWS, int NCOLS>
+__device__ __forceinline__ float dot_regs(const TileRegs<float, ROWS, NCOLS>& x, const TileRegs<float, ROWS, NCOLS>& y,
+                                          int tid) {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < TileRegs<float, ROWS, NCOLS>::PT; ++i)
+        if (tid + 256 * i < TileRegs<float, ROWS, NCOLS>::NV)
+            for (int j = 0; j < 4; ++j) s += u2f(x.w[i][j]) * u2f(y.w[i][j]);
+    return s;
+}
 
 // a tile into LDS: all loads issued before any store, so that their
 // latencies overlap
@@ -893,6 +927,381 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ per-chunk gradients, bf16 inputs, scalar gate
+// The same gradients as bwd_grad_kernel, with every tile in LDS as fp16 (the
+// bf16 inputs exactly, the fp32 states, T, P and intermediates rounded once)
+// and every product on the fp16 16x16x32 MFMA with fp32 accumulation.
+// Operand fragments: lane (G, n) holds the 8 values of k-slots 8G .. 8G+7 (A:
+// of row n; B: of column n). frag_row reads them from a tile whose rows run
+// along k (one 16-byte read); frag_col from a tile whose columns run along k
+// (two transposed 8-byte reads). Products whose result stays in registers or
+// goes to LDS are formed transposed, with the wave's 16 token rows as the
+// MFMA's n index: lane (G, n) then holds row 16w + n at the 4 consecutive
+// columns 4G .. 4G+3 of each 16-column block, stored with one 8-byte (fp16)
+// or 16-byte (fp32) write. Blocks that the triangular structure makes zero
+// (T, Tb, P, dTb, dP and dL are triangular) are skipped per wave.
+constexpr int HK = DK + 8;      // row stride (halves) of the 64 x 128 k and q tiles
+constexpr int HT = BT + 8;      // row stride of the 64 x 64 tiles
+constexpr int HVT = 32;         // value columns per tile
+constexpr int HV = HVT + 8;     // row stride of the value tiles
+
+__device__ __forceinline__ f16x8 frag_row(const f16* t, int ld, int row, int k0, int G) {
+    return *reinterpret_cast<const f16x8*>(t + row * ld + k0 + 8 * G);
+}
+// lane (G, n): t[k0 + 8G + e][col0 + n], e = 0..7. In a 16-lane group the
+// transposed read hands lane n column n of the 4 rows that lanes 4e .. 4e+3
+// address (each 4 consecutive values of row e).
+__device__ __forceinline__ f16x8 frag_col(const f16* t, int ld, int k0, int col0, int G, int n) {
+    const f16* p = t + (k0 + 8 * G + (n >> 2)) * ld + col0 + 4 * (n & 3);
+    const f16x4 x = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, p)));
+    const f16x4 y = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, p + 4 * ld)));
+    f16x8 f;
+    for (int e = 0; e < 4; ++e) {
+        f[e] = x[e];
+        f[e + 4] = y[e];
+    }
+    return f;
+}
+__device__ __forceinline__ void mma_h(f32x4& c, f16x8 a, f16x8 b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void st4h(f16* p, f32x4 x) {
+    f16x4 h;
+    for (int e = 0; e < 4; ++e) h[e] = (f16)x[e];
+    *reinterpret_cast<f16x4*>(p) = h;
+}
+__device__ __forceinline__ f32x4 ld4h(const f16* p) {
+    const f16x4 h = *reinterpret_cast<const f16x4*>(p);
+    return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+}
+
+__global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a) {
+    __shared__ __attribute__((aligned(16))) f16 Kh[BT * HK];
+    __shared__ __attribute__((aligned(16))) f16 Qh[BT * HK];
+    __shared__ __attribute__((aligned(16))) f16 Th[BT * HT];     // T
+    __shared__ __attribute__((aligned(16))) f16 Tbh[BT * HT];    // T diag(beta)
+    __shared__ __attribute__((aligned(16))) f16 Ph[BT * HT];
+    // value tiles, reused by the finish for three 64 x 64 tiles
+    __shared__ __attribute__((aligned(16))) f16 vb[2 * DK * HV + 6 * BT * HV];
+    __shared__ __attribute__((aligned(16))) float gm[4 * BT];
+    __shared__ float bt[BT], rowG[BT], rowK[BT], rowB[BT], colP[4][BT], colB[4][BT], red[4];
+    f16* Hh = vb;                       // h      [key][col]
+    f16* DHh = Hh + DK * HV;            // dh'    [key][col]
+    f16* Vh = DHh + DK * HV;            // v      [row][col]
+    f16* DOh = Vh + BT * HV;            // dO
+    f16* DVh = DOh + BT * HV;           // dvn
+    f16* Yh = DVh + BT * HV;            // Y
+    f16* VNh = Yh + BT * HV;            // v_new
+    f16* Zh = VNh + BT * HV;            // Z
+    f16* X1h = vb;                      // finish: dTb, then beta dL o D
+    f16* X2h = vb + BT * HT;            // finish: dP o D
+    f16* M1h = vb + 2 * BT * HT;        // finish: dT T^T
+    static_assert(3 * BT * HT <= 2 * DK * HV + 6 * BT * HV, "finish tiles fit the value-tile buffers");
+
+    const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ci = blockIdx.x, head = blockIdx.y, H = a.H;
+    int u, cc;
+    chunk_of(a.um, ci, u, cc);
+    if (u < 0) return;
+    const UnitInfo ui = unit_info(a.um, u);
+    const int64_t t0 = ui.start + (int64_t)cc * BT;
+    int len = ui.len - cc * BT;
+    len = len < 0 ? 0 : (len > BT ? BT : len);
+    const int64_t ch = (int64_t)ci * H + head;
+    const float lnb = a.use_exp2 ? 0.6931471805599453f : 1.0f;
+    const bf16* vin = reinterpret_cast<const bf16*>(a.v);
+    const bf16* dout = reinterpret_cast<const bf16*>(a.dout);
+    const bf16* bin = reinterpret_cast<const bf16*>(a.beta);
+    const int row0 = 16 * w, im = row0 + n;     // this lane's token row in the transposed products
+    const int lo_js = w >= 2 ? 2 : 1;           // 32-row steps j <= i can reach
+    const int hi_js = w >= 2 ? 1 : 0;           // first 32-row step j >= i can reach
+
+    // the value tiles of tile vt + 1 are loaded into registers while tile vt
+    // is computed, and written to LDS at the next tile's top
+    TileRegs<float, DK, HVT> ph, pdh;
+    TileRegs<bf16, BT, HVT> pv, pdo;
+    TileRegs<float, BT, HVT> pdv;
+    auto prefetch = [&](int vt) {
+        const int vc0 = vt * HVT;
+        ph.issue(a.h + ch * DK * DV + vc0, DV, DK, tid);
+        pdh.issue(a.dH + ch * DK * DV + vc0, DV, DK, tid);
+        pv.issue(vin + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, tid);
+        pdo.issue(dout + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, tid);
+        pdv.issue(a.dVN + ch * BT * DV + vc0, DV, BT, tid);
+    };
+    {
+        TileRegs<bf16, BT, DK> tk, tq;
+        TileRegs<float, BT, BT> tt, tp;
+        const int64_t rs = (int64_t)H * DK;
+        tk.issue(reinterpret_cast<const bf16*>(a.k) + (t0 * H + head) * DK, rs, len, tid);
+        tq.issue(reinterpret_cast<const bf16*>(a.q) + (t0 * H + head) * DK, rs, len, tid);
+        tt.issue(reinterpret_cast<const float*>(a.ws.Tm) + ch * (BT * BT), BT, BT, tid);
+        tp.issue(reinterpret_cast<const float*>(a.ws.P) + ch * (BT * BT), BT, BT, tid);
+        float pb[4];                                 // beta of this thread's T columns 4 (tid & 15) + j
+        const int cb = 4 * (tid & 15);
+        for (int j = 0; j < 4; ++j) pb[j] = cb + j < len ? (float)bin[(t0 + cb + j) * H + head] : 0.0f;
+        if (tid < BT) bt[tid] = tid < len ? (float)bin[(t0 + tid) * H + head] : 0.0f;
+        gm[tid] = a.ws.gam[ch * (GAMR * BT) + tid];   // G, b^G, b^{G_L - G}, b^{G_L}
+        prefetch(0);
+        tk.commit_h(Kh, HK, tid);
+        tq.commit_h(Qh, HK, tid);
+        tt.commit_h(Th, HT, tid, pb, Tbh);
+        tp.commit_h(Ph, HT, tid);
+    }
+
+    // accumulators, transposed: lane (G, n) holds row im at columns 16 b + 4G + r
+    f32x4 aP[4], aT[4], aQ[8], aKg[8], aKd[8];
+    for (int j = 0; j < 4; ++j) { aP[j] = f32x4{0.f, 0.f, 0.f, 0.f}; aT[j] = aP[j]; }
+    for (int j = 0; j < 8; ++j) { aQ[j] = f32x4{0.f, 0.f, 0.f, 0.f}; aKg[j] = aQ[j]; aKd[j] = aQ[j]; }
+    float hdh = 0.0f;                                // this thread's share of sum(h o dh')
+
+    for (int vt = 0; vt < DV / HVT; ++vt) {
+        const int vc0 = vt * HVT;
+        lds_barrier();                               // the previous tile's buffers are consumed
+        hdh += dot_regs(ph, pdh, tid);
+        ph.commit_h(Hh, HV, tid);
+        pdh.commit_h(DHh, HV, tid);
+        pv.commit_h(Vh, HV, tid);
+        pdo.commit_h(DOh, HV, tid);
+        pdv.commit_h(DVh, HV, tid);
+        lds_barrier();
+        if (vt + 1 < DV / HVT) prefetch(vt + 1);
+        // Y = V - b^G (K h), rows of this wave
+        {
+            const float bg = gm[BT + im];
+            f16x8 bk[4];
+            for (int ks = 0; ks < 4; ++ks) bk[ks] = frag_row(Kh, HK, im, 32 * ks, G);
+            for (int mb = 0; mb < 2; ++mb) {
+                f32x4 kh = {0.f, 0.f, 0.f, 0.f};
+                for (int ks = 0; ks < 4; ++ks) mma_h(kh, frag_col(Hh, HV, 32 * ks, 16 * mb, G, n), bk[ks]);
+                const f32x4 v4 = ld4h(Vh + im * HV + 16 * mb + 4 * G);
+                f32x4 y;
+                for (int r = 0; r < 4; ++r) y[r] = v4[r] - bg * kh[r];
+                st4h(Yh + im * HV + 16 * mb + 4 * G, y);
+            }
+        }
+        lds_barrier();
+        // v_new = Tb Y and Z = Tb^T dvn = dV, rows of this wave
+        {
+            f16x8 btb[2], btt[2];
+            for (int js = 0; js < 2; ++js) {
+                if (js < lo_js) btb[js] = frag_row(Tbh, HT, im, 32 * js, G);
+                if (js >= hi_js) btt[js] = frag_col(Th, HT, 32 * js, row0, G, n);
+            }
+            const float bi = bt[im];
+            for (int mb = 0; mb < 2; ++mb) {
+                f32x4 vn = {0.f, 0.f, 0.f, 0.f}, z = vn;
+                for (int js = 0; js < 2; ++js) {
+                    if (js < lo_js) mma_h(vn, frag_col(Yh, HV, 32 * js, 16 * mb, G, n), btb[js]);
+                    if (js >= hi_js) mma_h(z, frag_col(DVh, HV, 32 * js, 16 * mb, G, n), btt[js]);
+                }
+                for (int r = 0; r < 4; ++r) z[r] *= bi;
+                st4h(VNh + im * HV + 16 * mb + 4 * G, vn);
+                st4h(Zh + im * HV + 16 * mb + 4 * G, z);
+                if (im < len) *reinterpret_cast<f32x4*>(a.dv + ((t0 + im) * H + head) * DV + vc0 + 16 * mb + 4 * G) = z;
+            }
+        }
+        lds_barrier();
+        // accumulate over this tile's 32 columns: dP / scale, dTb, dQd / scale,
+        // dKg and -dKd, the wave's rows as n
+        {
+            const f16x8 bdo = frag_row(DOh, HV, im, 0, G), bdv = frag_row(DVh, HV, im, 0, G);
+            const f16x8 bvn = frag_row(VNh, HV, im, 0, G), bz = frag_row(Zh, HV, im, 0, G);
+            for (int jb = 0; jb < 4; ++jb)
+                if (jb <= w) {
+                    mma_h(aP[jb], frag_row(VNh, HV, 16 * jb + n, 0, G), bdo);
+                    mma_h(aT[jb], frag_row(Yh, HV, 16 * jb + n, 0, G), bdv);
+                }
+            for (int kb = 0; kb < 8; ++kb) {
+                const f16x8 hk = frag_row(Hh, HV, 16 * kb + n, 0, G);
+                mma_h(aQ[kb], hk, bdo);
+                mma_h(aKd[kb], hk, bz);
+                mma_h(aKg[kb], frag_row(DHh, HV, 16 * kb + n, 0, G), bvn);
+            }
+        }
+    }
+    lds_barrier();
+
+    // ---- finish. X1 = dTb, X2 = dP (lower incl. diagonal) of the wave's rows;
+    // dbeta's column term: sums over i of dTb o T
+    {
+        float cs[4][4];
+        for (int jb = 0; jb < 4; ++jb) {
+            const f32x4 t4 = ld4h(Th + im * HT + 16 * jb + 4 * G);
+            f32x4 x1, x2;
+            for (int r = 0; r < 4; ++r) {
+                const int j = 16 * jb + 4 * G + r;
+                const bool keep = jb <= w && j <= im;
+                x1[r] = keep ? aT[jb][r] : 0.0f;
+                x2[r] = keep ? a.scale * aP[jb][r] : 0.0f;
+                cs[jb][r] = x1[r] * t4[r];
+            }
+            aP[jb] = x2;
+            st4h(X1h + im * HT + 16 * jb + 4 * G, x1);
+            for (int r = 0; r < 4; ++r)
+                for (int sft = 1; sft < 16; sft <<= 1) cs[jb][r] += __shfl_xor(cs[jb][r], sft, 16);
+        }
+        if (n == 0)
+            for (int jb = 0; jb < 4; ++jb)
+                for (int r = 0; r < 4; ++r) colB[w][16 * jb + 4 * G + r] = cs[jb][r];
+    }
+    lds_barrier();
+    // M1 = dT T^T = dTb Tb^T, rows of this wave
+    {
+        f16x8 bx[2];
+        for (int js = 0; js < 2; ++js)
+            if (js < lo_js) bx[js] = frag_row(X1h, HT, im, 32 * js, G);
+        for (int kb = 0; kb < 4; ++kb) {
+            f32x4 m = {0.f, 0.f, 0.f, 0.f};
+            for (int js = 0; js < 2; ++js)
+                if (js < lo_js) mma_h(m, frag_row(Tbh, HT, 16 * kb + n, 32 * js, G), bx[js]);
+            st4h(M1h + im * HT + 16 * kb + 4 * G, m);
+        }
+    }
+    lds_barrier();
+    // dL = -T^T M1 (strictly lower) and the Gram matrix K K^T, rows of this wave
+    f32x4 dl[4], gr[4];
+    {
+        f16x8 btt[2], bk[4];
+        for (int js = 0; js < 2; ++js)
+            if (js >= hi_js) btt[js] = frag_col(Th, HT, 32 * js, row0, G, n);
+        for (int ks = 0; ks < 4; ++ks) bk[ks] = frag_row(Kh, HK, im, 32 * ks, G);
+        for (int jb = 0; jb < 4; ++jb) {
+            dl[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            gr[jb] = dl[jb];
+            if (jb <= w) {
+                for (int js = 0; js < 2; ++js)
+                    if (js >= hi_js) mma_h(dl[jb], frag_col(M1h, HT, 32 * js, 16 * jb, G, n), btt[js]);
+                for (int ks = 0; ks < 4; ++ks) mma_h(gr[jb], frag_row(Kh, HK, 16 * jb + n, 32 * ks, G), bk[ks]);
+            }
+        }
+    }
+    // element terms of L and P: dbeta_i += sum_j dL_ij G_ij, the G_i / G_j
+    // parts of the gate gradient, and dG o D, dP o D into X1, X2
+    float rg = 0.0f;
+    {
+        const float gi = gm[im], bi = bt[im];
+        float rb = 0.0f, cg[4][4];
+        for (int jb = 0; jb < 4; ++jb) {
+            const f32x4 p4 = ld4h(Ph + im * HT + 16 * jb + 4 * G);
+            f32x4 x1, x2;
+            for (int r = 0; r < 4; ++r) {
+                const int j = 16 * jb + 4 * G + r;
+                const float d = jb <= w && j <= im ? fpow(gi - gm[j], a.use_exp2) : 0.0f;
+                const float lij = j < im ? -dl[jb][r] : 0.0f;     // dL
+                const float gij = gr[jb][r] * d;                   // (k_i . k_j) D_ij
+                const float dgg = bi * lij;                        // dG
+                const float dpij = aP[jb][r];
+                rb += lij * gij;
+                const float t = lnb * (dgg * gij + dpij * p4[r]);
+                rg += t;
+                cg[jb][r] = -t;
+                x1[r] = dgg * d;
+                x2[r] = dpij * d;
+            }
+            st4h(X1h + im * HT + 16 * jb + 4 * G, x1);
+            st4h(X2h + im * HT + 16 * jb + 4 * G, x2);
+            for (int r = 0; r < 4; ++r)
+                for (int sft = 1; sft < 16; sft <<= 1) cg[jb][r] += __shfl_xor(cg[jb][r], sft, 16);
+        }
+        // row sums over the four lane groups
+        rb += __shfl_xor(rb, 16, 64);
+        rb += __shfl_xor(rb, 32, 64);
+        rg += __shfl_xor(rg, 16, 64);
+        rg += __shfl_xor(rg, 32, 64);
+        if (G == 0) rowB[im] = rb;
+        // column sums over this wave's rows: one partial per wave, added in a
+        // fixed order below (the same result on every run)
+        if (n == 0)
+            for (int jb = 0; jb < 4; ++jb)
+                for (int r = 0; r < 4; ++r) colP[w][16 * jb + 4 * G + r] = cg[jb][r];
+    }
+    lds_barrier();
+    // dq, dk, rows of this wave: the products with dG o D and dP o D, then
+    // b^G dQd, b^G dKd + b^{G_L - G} dKg, and their gate terms
+    {
+        f16x8 x2r[2], x1r[2], x1c[2], x2c[2];
+        for (int js = 0; js < 2; ++js) {
+            if (js < lo_js) {
+                x2r[js] = frag_row(X2h, HT, im, 32 * js, G);
+                x1r[js] = frag_row(X1h, HT, im, 32 * js, G);
+            }
+            if (js >= hi_js) {
+                x1c[js] = frag_col(X1h, HT, 32 * js, row0, G, n);
+                x2c[js] = frag_col(X2h, HT, 32 * js, row0, G, n);
+            }
+        }
+        const float bgi = gm[BT + im], blgi = gm[2 * BT + im];
+        float rq = 0.0f, rk = 0.0f;
+        for (int kb = 0; kb < 8; ++kb) {
+            f32x4 q1 = {0.f, 0.f, 0.f, 0.f}, k1 = q1;
+            for (int js = 0; js < 2; ++js) {
+                const f16x8 ak = frag_col(Kh, HK, 32 * js, 16 * kb, G, n);
+                if (js < lo_js) {
+                    mma_h(q1, ak, x2r[js]);
+                    mma_h(k1, ak, x1r[js]);
+                }
+                if (js >= hi_js) {
+                    mma_h(k1, ak, x1c[js]);
+                    mma_h(k1, frag_col(Qh, HK, 32 * js, 16 * kb, G, n), x2c[js]);
+                }
+            }
+            const f32x4 q4 = ld4h(Qh + im * HK + 16 * kb + 4 * G), k4 = ld4h(Kh + im * HK + 16 * kb + 4 * G);
+            f32x4 dqv, dkv;
+            for (int r = 0; r < 4; ++r) {
+                const float dQd = a.scale * aQ[kb][r], dKd = -aKd[kb][r], dKg = aKg[kb][r];
+                dqv[r] = q1[r] + bgi * dQd;
+                dkv[r] = k1[r] + bgi * dKd + blgi * dKg;
+                // the Kg term (ln b dKg Kg) goes to dg as a prefix over earlier
+                // rows: its - part here and its + part in G_L's gradient cancel
+                // for every row from i on
+                rq += lnb * (dQd * bgi * q4[r] + dKd * bgi * k4[r]);
+                rk += lnb * dKg * blgi * k4[r];
+            }
+            if (im < len) {
+                const int64_t o = ((t0 + im) * H + head) * DK + 16 * kb + 4 * G;
+                *reinterpret_cast<f32x4*>(a.dq + o) = dqv;
+                *reinterpret_cast<f32x4*>(a.dk + o) = dkv;
+            }
+        }
+        rq += __shfl_xor(rq, 16, 64);
+        rq += __shfl_xor(rq, 32, 64);
+        rk += __shfl_xor(rk, 16, 64);
+        rk += __shfl_xor(rk, 32, 64);
+        if (G == 0) {
+            rowG[im] = rg + rq;
+            rowK[im] = rk;
+        }
+    }
+    // the state decay's term of G_L: lnb gamma sum(h o dh'), over the workgroup
+    float tl = lnb * gm[3 * BT] * hdh;
+    for (int s = 1; s < 64; s <<= 1) tl += __shfl_xor(tl, s, 64);
+    if (lane == 0) red[w] = tl;
+    lds_barrier();
+    // dg: reverse cumulative sum over the chunk's rows of the gate gradient,
+    // with the state decay's term entering at the last valid row, plus the
+    // exclusive prefix of the Kg terms; dbeta: its column and row terms
+    if (w == 0) {
+        const float gl = ((red[0] + red[1]) + red[2]) + red[3];
+        const float colG = ((colP[0][lane] + colP[1][lane]) + colP[2][lane]) + colP[3][lane];
+        const float colBs = ((colB[0][lane] + colB[1][lane]) + colB[2][lane]) + colB[3][lane];
+        float x = lane < len ? rowG[lane] + colG + (lane == len - 1 ? gl : 0.0f) : 0.0f;
+        const float kg = lane < len ? rowK[lane] : 0.0f;
+        float y = kg;
+        for (int s = 1; s < 64; s <<= 1) {
+            const float xd = __shfl_down(x, s, 64), yu = __shfl_up(y, s, 64);
+            if (lane + s < 64) x += xd;
+            if (lane >= s) y += yu;
+        }
+        x += y - kg;
+        if (lane < len) {
+            a.dg[(t0 + lane) * H + head] = x;
+            a.dbeta[(t0 + lane) * H + head] = colBs + rowB[lane];
+        }
+    }
+}
+
 // ------------------------------------------------------------------ launcher
 hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* dVN, const void* q, const void* k,
                       const void* v, const float* g, const void* beta, const float* h, const void* dout,
@@ -930,7 +1339,7 @@ hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* d
             if (p.dtype == 1) hipLaunchKernelGGL((bwd_grad_kernel<bf16, true>), grid, dim3(256), 0, s, a);
             else hipLaunchKernelGGL((bwd_grad_kernel<float, true>), grid, dim3(256), 0, s, a);
         } else {
-            if (p.dtype == 1) hipLaunchKernelGGL((bwd_grad_kernel<bf16, false>), grid, dim3(256), 0, s, a);
+            if (p.dtype == 1) hipLaunchKernelGGL(bwd_grad_kernel_h, grid, dim3(256), 0, s, a);
             else hipLaunchKernelGGL((bwd_grad_kernel<float, false>), grid, dim3(256), 0, s, a);
         }
     }
