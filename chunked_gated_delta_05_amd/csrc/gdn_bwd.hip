@@ -121,6 +121,13 @@ template <> struct Vec16<float> {
     static constexpr int N = 4;
     __device__ static void cvt(u32x4 w, float* x) { for (int i = 0; i < 4; ++i) x[i] = u2f(w[i]); }
 };
+template <> struct Vec16<f16> {
+    static constexpr int N = 8;
+    __device__ static void cvt(u32x4 w, float* x) {
+        const f16x8 h = __builtin_bit_cast(f16x8, w);
+        for (int i = 0; i < 8; ++i) x[i] = (float)h[i];
+    }
+};
 template <> struct Vec16<bf16> {
     static constexpr int N = 8;
     __device__ static void cvt(u32x4 w, float* x) {
@@ -161,8 +168,9 @@ struct TileRegs {
             }
         }
     }
-    // the same, as fp16 values (8 bytes per fp32 vector, 16 per bf16 one),
-    // and with column c scaled by colscale[c % 4] into dst2 when given
+    // the same, as fp16 values (8 bytes per fp32 vector, 16 per bf16 or fp16
+    // one), and with column c + j of a vector scaled by colscale[j] into dst2
+    // when given
     __device__ __forceinline__ void commit_h(f16* dst, int ld, int tid, const float* colscale = nullptr,
                                              f16* dst2 = nullptr) const {
 #pragma unroll
@@ -176,9 +184,37 @@ struct TileRegs {
                 for (int j = 0; j < VPR; ++j) h[j] = (f16)x[j];
                 *reinterpret_cast<hv*>(dst + r * ld + c) = h;
                 if (dst2) {
-                    for (int j = 0; j < VPR; ++j) h[j] = (f16)(x[j] * colscale[j % 4]);
+                    for (int j = 0; j < VPR; ++j) h[j] = (f16)(x[j] * colscale[j]);
                     *reinterpret_cast<hv*>(dst2 + r * ld + c) = h;
                 }
+            }
+        }
+    }
+    // fp16 values scaled by s (one row per thread: PT == 1)
+    __device__ __forceinline__ void commit_h_mul(f16* dst, int ld, int tid, float s) const {
+        static_assert(PT == 1, "one vector per thread");
+        const int e = tid, r = e / PER_ROW, c = (e - r * PER_ROW) * VPR;
+        if (e < NV) {
+            float x[VPR];
+            Vec16<In>::cvt(w[0], x);
+            typedef _Float16 hv __attribute__((ext_vector_type(VPR)));
+            hv h;
+            for (int j = 0; j < VPR; ++j) h[j] = (f16)(x[j] * s);
+            *reinterpret_cast<hv*>(dst + r * ld + c) = h;
+        }
+    }
+    // fp16 values with column c + j of a vector scaled by colscale[j]
+    __device__ __forceinline__ void commit_h_cols(f16* dst, int ld, int tid, const float* colscale) const {
+#pragma unroll
+        for (int i = 0; i < PT; ++i) {
+            const int e = tid + 256 * i, r = e / PER_ROW, c = (e - r * PER_ROW) * VPR;
+            if (e < NV) {
+                float x[VPR];
+                Vec16<In>::cvt(w[i], x);
+                typedef _Float16 hv __attribute__((ext_vector_type(VPR)));
+                hv h;
+                for (int j = 0; j < VPR; ++j) h[j] = (f16)(x[j] * colscale[j]);
+                *reinterpret_cast<hv*>(dst + r * ld + c) = h;
             }
         }
     }
@@ -975,6 +1011,159 @@ __device__ __forceinline__ f32x4 ld4h(const f16* p) {
     return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
 }
 
+// ------------------------------------------------------------------ reverse state pass, bf16 inputs, scalar gate
+// bwd_dh_kernel on fp16 tiles and the fp16 16x16x32 MFMA: one workgroup of
+// four waves per (unit, head, 16 NCT value columns), dL/dh in fp32 registers
+// (wave w: keys 32w .. 32w+31), its fp16 copy in LDS as [column][key] for
+// the next chunk's Kg dh'. dvn and b^G Z are formed transposed (lane (G, n):
+// token row 16w + n, columns 4G .. 4G+3 of each 16-column block), so that
+// dvn reaches the workspace in 16-byte stores. dO is held twice: as given
+// (P^T dO) and scaled by scale b^G per row (Qd^T dO).
+template <int NCT>
+__global__ __launch_bounds__(256) void bwd_dh_kernel_h(BwdArgs a) {
+    constexpr int NC = 16 * NCT, HC = NC + 8;     // columns of the tile, LDS row stride (halves)
+    __shared__ __attribute__((aligned(16))) f16 Kh[BT * HK];
+    __shared__ __attribute__((aligned(16))) f16 Qh[BT * HK];
+    __shared__ __attribute__((aligned(16))) f16 Tbh[BT * HT];   // T diag(beta)
+    __shared__ __attribute__((aligned(16))) f16 Ph[BT * HT];
+    __shared__ __attribute__((aligned(16))) f16 dOh[BT * HC];   // dO
+    __shared__ __attribute__((aligned(16))) f16 dOg[BT * HC];   // scale b^G dO
+    __shared__ __attribute__((aligned(16))) f16 DVh[BT * HC];   // dvn
+    __shared__ __attribute__((aligned(16))) f16 Zh[BT * HC];    // b^G Z
+    __shared__ __attribute__((aligned(16))) f16 dhT[NC * HK];   // dh' [column][key]
+    __shared__ __attribute__((aligned(16))) float gm[4 * BT];   // G, b^G, b^{G_L - G}, b^{G_L}
+
+    const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = a.H;
+    const int tile = blockIdx.x % (DV / NC), pair = blockIdx.x / (DV / NC);
+    if (pair >= a.n_pairs) return;
+    const int u = pair / H, head = pair - u * H;
+    const UnitInfo ui = uniform(unit_info(a.um, u));
+    const int c0 = tile * NC;
+    const int64_t uh = (int64_t)u * H + head;
+    const bf16* dout = reinterpret_cast<const bf16*>(a.dout);
+    const bf16* bin = reinterpret_cast<const bf16*>(a.beta);
+    const int row0 = 16 * w, im = row0 + n;
+    const int hi_js = w >= 2 ? 1 : 0;            // first 32-row step j >= i can reach
+
+    // dL/dh at the unit's end: keys 32w + 16kt + 4G + r, column 16ct + n
+    f32x4 dh[2][NCT];
+    for (int kt = 0; kt < 2; ++kt)
+        for (int ct = 0; ct < NCT; ++ct) {
+            for (int r = 0; r < 4; ++r) {
+                const int key = 32 * w + 16 * kt + 4 * G + r, col = 16 * ct + n;
+                dh[kt][ct][r] = a.dht ? a.dht[(uh * DK + key) * DV + c0 + col] : 0.0f;
+            }
+            st4h(dhT + (16 * ct + n) * HK + 32 * w + 16 * kt + 4 * G, dh[kt][ct]);
+        }
+
+    // the next chunk's tiles are loaded into registers while this chunk is
+    // computed, and written to LDS at the top of the next step
+    TileRegs<bf16, BT, DK> pk, pq;
+    TileRegs<f16, BT, BT> pt, pp;                  // T and P: fp16 from the preparation
+    TileRegs<bf16, BT, NC> pd;
+    float pg = 0.0f, pbg = 0.0f, pb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    auto prefetch = [&](int cc) {
+        int l = ui.len - cc * BT;
+        l = l > BT ? BT : l;
+        const int64_t tt = ui.start + (int64_t)cc * BT, chh = (int64_t)(ui.cbase + cc) * H + head;
+        const int64_t rs = (int64_t)H * DK;
+        pk.issue(reinterpret_cast<const bf16*>(a.k) + (tt * H + head) * DK, rs, l, tid);
+        pq.issue(reinterpret_cast<const bf16*>(a.q) + (tt * H + head) * DK, rs, l, tid);
+        pt.issue(reinterpret_cast<const f16*>(a.ws.Tm) + chh * (BT * BT), BT, BT, tid);
+        pp.issue(reinterpret_cast<const f16*>(a.ws.P) + chh * (BT * BT), BT, BT, tid);
+        pd.issue(dout + (tt * H + head) * DV + c0, (int64_t)H * DV, l, tid);
+        pg = a.ws.gam[chh * (GAMR * BT) + tid];      // rows 0..3 (no q / k normalisation here)
+        const int cb = 8 * (tid & 7);                // the columns of this thread's T vectors
+        for (int j = 0; j < 8; ++j) pb[j] = cb + j < l ? (float)bin[(tt + cb + j) * H + head] : 0.0f;
+        const int dr = tid / TileRegs<bf16, BT, NC>::PER_ROW;   // this thread's dO row
+        pbg = dr < BT ? a.ws.gam[chh * (GAMR * BT) + BT + dr] : 0.0f;
+    };
+    if (ui.nch > 0) prefetch(ui.nch - 1);
+
+    for (int c = ui.nch - 1; c >= 0; --c) {
+        const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
+        lds_barrier();                               // the previous chunk's tiles are consumed
+        pk.commit_h(Kh, HK, tid);
+        pq.commit_h(Qh, HK, tid);
+        pt.commit_h_cols(Tbh, HT, tid, pb);
+        pp.commit_h(Ph, HT, tid);
+        pd.commit_h(dOh, HC, tid);
+        pd.commit_h_mul(dOg, HC, tid, a.scale * pbg);
+        gm[tid] = pg;
+        lds_barrier();
+        if (c > 0) prefetch(c - 1);
+        // dh' of this chunk to the workspace
+        for (int kt = 0; kt < 2; ++kt)
+            for (int ct = 0; ct < NCT; ++ct)
+                for (int r = 0; r < 4; ++r) {
+                    const int key = 32 * w + 16 * kt + 4 * G + r;
+                    a.dH[(ch * DK + key) * DV + c0 + 16 * ct + n] = dh[kt][ct][r];
+                }
+        // dvn = b^{G_L - G} (K dh') + scale P^T dO, rows of this wave
+        {
+            const float blg = gm[2 * BT + im];
+            f16x8 bk[4], bp[2];
+            for (int ks = 0; ks < 4; ++ks) bk[ks] = frag_row(Kh, HK, im, 32 * ks, G);
+            for (int js = 0; js < 2; ++js)
+                if (js >= hi_js) bp[js] = frag_col(Ph, HT, 32 * js, row0, G, n);
+            for (int ct = 0; ct < NCT; ++ct) {
+                f32x4 kh = {0.f, 0.f, 0.f, 0.f}, pdo = kh;
+                for (int ks = 0; ks < 4; ++ks) mma_h(kh, frag_row(dhT, HK, 16 * ct + n, 32 * ks, G), bk[ks]);
+                for (int js = 0; js < 2; ++js)
+                    if (js >= hi_js) mma_h(pdo, frag_col(dOh, HC, 32 * js, 16 * ct, G, n), bp[js]);
+                f32x4 x;
+                for (int r = 0; r < 4; ++r) x[r] = blg * kh[r] + a.scale * pdo[r];
+                st4h(DVh + im * HC + 16 * ct + 4 * G, x);
+                *reinterpret_cast<f32x4*>(a.dVN + (ch * BT + im) * DV + c0 + 16 * ct + 4 * G) = x;
+            }
+        }
+        lds_barrier();
+        // b^G Z = b^G (Tb^T dvn), rows of this wave
+        {
+            const float bg = gm[BT + im];
+            f16x8 btb[2];
+            for (int js = 0; js < 2; ++js)
+                if (js >= hi_js) btb[js] = frag_col(Tbh, HT, 32 * js, row0, G, n);
+            for (int ct = 0; ct < NCT; ++ct) {
+                f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                for (int js = 0; js < 2; ++js)
+                    if (js >= hi_js) mma_h(z, frag_col(DVh, HC, 32 * js, 16 * ct, G, n), btb[js]);
+                for (int r = 0; r < 4; ++r) z[r] *= bg;
+                st4h(Zh + im * HC + 16 * ct + 4 * G, z);
+            }
+        }
+        lds_barrier();
+        // dh = gamma dh' + Q^T (scale b^G dO) - K^T (b^G Z), keys 32w .. +31
+        const float gam = gm[3 * BT];
+        for (int kt = 0; kt < 2; ++kt) {
+            const int key0 = 32 * w + 16 * kt;
+            f16x8 aq[2], ak[2];
+            for (int js = 0; js < 2; ++js) {
+                aq[js] = frag_col(Qh, HK, 32 * js, key0, G, n);
+                ak[js] = frag_col(Kh, HK, 32 * js, key0, G, n);
+            }
+            for (int ct = 0; ct < NCT; ++ct) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acz = acc;
+                for (int js = 0; js < 2; ++js) {
+                    mma_h(acc, aq[js], frag_col(dOg, HC, 32 * js, 16 * ct, G, n));
+                    mma_h(acz, ak[js], frag_col(Zh, HC, 32 * js, 16 * ct, G, n));
+                }
+                for (int r = 0; r < 4; ++r) dh[kt][ct][r] = gam * dh[kt][ct][r] + acc[r] - acz[r];
+                st4h(dhT + (16 * ct + n) * HK + key0 + 4 * G, dh[kt][ct]);
+            }
+        }
+    }
+    if (a.dh0)
+        for (int kt = 0; kt < 2; ++kt)
+            for (int ct = 0; ct < NCT; ++ct)
+                for (int r = 0; r < 4; ++r) {
+                    const int key = 32 * w + 16 * kt + 4 * G + r;
+                    a.dh0[(uh * DK + key) * DV + c0 + 16 * ct + n] = dh[kt][ct][r];
+                }
+}
+
 __global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) f16 Kh[BT * HK];
     __shared__ __attribute__((aligned(16))) f16 Qh[BT * HK];
@@ -1032,15 +1221,15 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a) {
     };
     {
         TileRegs<bf16, BT, DK> tk, tq;
-        TileRegs<float, BT, BT> tt, tp;
+        TileRegs<f16, BT, BT> tt, tp;               // T and P: fp16 from the preparation
         const int64_t rs = (int64_t)H * DK;
         tk.issue(reinterpret_cast<const bf16*>(a.k) + (t0 * H + head) * DK, rs, len, tid);
         tq.issue(reinterpret_cast<const bf16*>(a.q) + (t0 * H + head) * DK, rs, len, tid);
-        tt.issue(reinterpret_cast<const float*>(a.ws.Tm) + ch * (BT * BT), BT, BT, tid);
-        tp.issue(reinterpret_cast<const float*>(a.ws.P) + ch * (BT * BT), BT, BT, tid);
-        float pb[4];                                 // beta of this thread's T columns 4 (tid & 15) + j
-        const int cb = 4 * (tid & 15);
-        for (int j = 0; j < 4; ++j) pb[j] = cb + j < len ? (float)bin[(t0 + cb + j) * H + head] : 0.0f;
+        tt.issue(reinterpret_cast<const f16*>(a.ws.Tm) + ch * (BT * BT), BT, BT, tid);
+        tp.issue(reinterpret_cast<const f16*>(a.ws.P) + ch * (BT * BT), BT, BT, tid);
+        float pb[8];                                 // beta of this thread's T columns 8 (tid & 7) + j
+        const int cb = 8 * (tid & 7);
+        for (int j = 0; j < 8; ++j) pb[j] = cb + j < len ? (float)bin[(t0 + cb + j) * H + head] : 0.0f;
         if (tid < BT) bt[tid] = tid < len ? (float)bin[(t0 + tid) * H + head] : 0.0f;
         gm[tid] = a.ws.gam[ch * (GAMR * BT) + tid];   // G, b^G, b^{G_L - G}, b^{G_L}
         prefetch(0);
@@ -1307,7 +1496,7 @@ hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* d
                       const void* v, const float* g, const void* beta, const float* h, const void* dout,
                       const float* dht, float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0,
                       bool dh_only, bool reuse_prep, hipStream_t s) {
-    if (!reuse_prep && launch_prep_f32(p, ws, k, q, g, beta, s) != hipSuccess) return hipGetLastError();
+    if (!reuse_prep && launch_prep_bwd(p, ws, k, q, g, beta, s) != hipSuccess) return hipGetLastError();
     BwdArgs a;
     a.um = p.um; a.H = p.H; a.use_exp2 = p.use_exp2; a.scale = p.scale;
     a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g; a.dout = dout; a.h = h; a.dht = dht;
@@ -1328,8 +1517,11 @@ hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* d
     else hipLaunchKernelGGL((bwd_dh_kernel<IN, PKV, 2>), grid, dim3(256), 0, s, a);
         if (p.per_key) {
             if (p.dtype == 1) { GDN_DH(bf16, true) } else { GDN_DH(float, true) }
+        } else if (p.dtype == 1) {
+            if (narrow) hipLaunchKernelGGL(bwd_dh_kernel_h<1>, grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL(bwd_dh_kernel_h<2>, grid, dim3(256), 0, s, a);
         } else {
-            if (p.dtype == 1) { GDN_DH(bf16, false) } else { GDN_DH(float, false) }
+            GDN_DH(float, false)
         }
 #undef GDN_DH
     }

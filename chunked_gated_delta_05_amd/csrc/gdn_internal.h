@@ -111,11 +111,13 @@ hipError_t launch_merge(int B, int H, int n_seg, const float* S_ext, const float
 hipError_t launch_merge_adjoint(int B, int H, int n_seg, const float* dS_ext, const float* M,
                                 const float* dS_final, float* dS_exit, float* dS0, hipStream_t s);
 
-// The fp32-operand chunk preparation (T, P, gate rows) for bf16 or fp32 inputs.
-hipError_t launch_prep_f32(const Problem& p, const Workspace& ws, const void* k, const void* q,
+// The chunk preparation the backward reads (T, P, gate rows; per key the
+// gated tiles), natural order: fp32, or fp16 T and P for bf16 inputs with a
+// scalar gate.
+hipError_t launch_prep_bwd(const Problem& p, const Workspace& ws, const void* k, const void* q,
                            const float* g, const void* beta, hipStream_t s);
 
-// The backward: fp32 preparation (skipped with reuse_prep: the workspace
+// The backward: the chunk preparation (skipped with reuse_prep: the workspace
 // holds it), reverse state pass, per-chunk gradients (skipped with dh_only).
 hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* dVN, const void* q,
                       const void* k, const void* v, const float* g, const void* beta, const float* h,

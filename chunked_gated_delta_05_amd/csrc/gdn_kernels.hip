@@ -610,8 +610,11 @@ constexpr int PBL = 16 * PLS + 4;     // L blocks: successive blocks 4 banks apa
 constexpr int PBT = 16 * PLS + 16;    // T blocks: successive blocks 16 banks apart
 
 // XF: the input transforms or their slots are asked for (a separate
-// instantiation, so that the plain preparation keeps its registers)
-template <bool XF>
+// instantiation, so that the plain preparation keeps its registers).
+// BWD: the preparation the backward reads instead: T itself and P as fp16 in
+// natural order (every block, zeros above the diagonal) and the fp32 gate
+// rows G, b^G, b^{G_L - G}, b^{G_L}, b^G (no input transforms).
+template <bool XF, bool BWD = false>
 __global__ __launch_bounds__(64) void prep_kernel_h(PrepArgs a) {
     __shared__ __attribute__((aligned(16))) float Ld[4 * PBL];
     __shared__ __attribute__((aligned(16))) float Td[4 * PBT];
@@ -731,12 +734,21 @@ __global__ __launch_bounds__(64) void prep_kernel_h(PrepArgs a) {
     {
         const float bG = fpow(x, a.use_exp2), bLG = fpow(xl - x, a.use_exp2);
         const float rk = XF ? Rk[lane] : 1.0f, rq = XF ? Rq[lane] : 1.0f;
-        float* cf = reinterpret_cast<float*>(a.ws.cfh) + ch * (CFS / 4);
-        const int lo = lane_order(lane);
-        cf[CS_CP + lo] = bLG * rk;
-        cf[CS_BG + lo] = bG * rk;
-        cf[CS_BQ + lo] = bG * rq;
-        if (lane == 0) cf[CS_EL] = fpow(xl, a.use_exp2);
+        if (BWD) {
+            float* gw = a.ws.gam + ch * (GAMR * BT);
+            gw[lane] = x;
+            gw[BT + lane] = bG;
+            gw[2 * BT + lane] = bLG;
+            gw[3 * BT + lane] = fpow(xl, a.use_exp2);
+            gw[4 * BT + lane] = bG;
+        } else {
+            float* cf = reinterpret_cast<float*>(a.ws.cfh) + ch * (CFS / 4);
+            const int lo = lane_order(lane);
+            cf[CS_CP + lo] = bLG * rk;
+            cf[CS_BG + lo] = bG * rk;
+            cf[CS_BQ + lo] = bG * rq;
+            if (lane == 0) cf[CS_EL] = fpow(xl, a.use_exp2);
+        }
         if (a.g_cumsum && lane < len) a.g_cumsum[e0 + (int64_t)lane * H] = x;
         if (XF && lane < len) {
             if (a.k_rstd) a.k_rstd[e0 + (int64_t)lane * H] = rk;
@@ -769,10 +781,10 @@ __global__ __launch_bounds__(64) void prep_kernel_h(PrepArgs a) {
     for (int I = 0; I < 4; ++I) {
 #pragma unroll
         for (int K = 0; K < 4; ++K) {
-            f16* pdst = Pw + (16 * I + n) * BT + op_pos(16 * K + 4 * G);
+            f16* pdst = Pw + (16 * I + n) * BT + (BWD ? 16 * K + 4 * G : op_pos(16 * K + 4 * G));
             if (K > I) {
                 // zero blocks; rows 0..31 of the state pass read columns 0..31 only
-                if (has_q && (I >= 2 || K < 2)) *reinterpret_cast<u32x2*>(pdst) = u32x2{0u, 0u};
+                if (BWD || (has_q && (I >= 2 || K < 2))) *reinterpret_cast<u32x2*>(pdst) = u32x2{0u, 0u};
                 continue;
             }
             f32x4 gk = {0.f, 0.f, 0.f, 0.f}, gq = gk;
@@ -851,6 +863,10 @@ __global__ __launch_bounds__(64) void prep_kernel_h(PrepArgs a) {
     for (int I = 0; I < 4; ++I)
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
+            if (BWD) {
+                *reinterpret_cast<u32x2*>(Tw + (16 * I + n) * BT + 16 * J + 4 * G) = f32x4_to_f16x4(TB[I][J]);
+                continue;
+            }
             if (I >= 2 || J < 2)   // rows 0..31 of the state pass read columns 0..31 only
                 *reinterpret_cast<u32x2*>(Tw + (16 * I + n) * BT + op_pos(16 * J + 4 * G)) =
                     f32x4_to_f16x4(TB[I][J] * *reinterpret_cast<const f32x4*>(&Bs[16 * J + 4 * G]));
@@ -2370,10 +2386,10 @@ hipError_t launch_prep(const Problem& p, const Workspace& ws, const void* k, con
     return hipGetLastError();
 }
 
-// The fp32-operand preparation (T, P and, for the scalar gate, the gate
-// rows; per key, the gated q and k tiles and G_last) in fp32, natural order,
-// for either input dtype: what the backward reads.
-hipError_t launch_prep_f32(const Problem& p, const Workspace& ws, const void* k, const void* q, const float* g,
+// The preparation the backward reads: T, P and, for the scalar gate, the
+// gate rows; per key, the gated q and k tiles and G_last. Natural order, fp32
+// (T and P fp16 with bf16 inputs and a scalar gate).
+hipError_t launch_prep_bwd(const Problem& p, const Workspace& ws, const void* k, const void* q, const float* g,
                            const void* beta, hipStream_t s) {
     if (p.um.n_chunks == 0) return hipSuccess;
     PrepArgs a;
@@ -2386,7 +2402,7 @@ hipError_t launch_prep_f32(const Problem& p, const Workspace& ws, const void* k,
         if (p.dtype == 1) hipLaunchKernelGGL((prep_kernel<PolicyFB, true>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((prep_kernel<PolicyF, true>), grid, block, 0, s, a);
     } else {
-        if (p.dtype == 1) hipLaunchKernelGGL((prep_kernel<PolicyFB, false>), grid, block, 0, s, a);
+        if (p.dtype == 1) hipLaunchKernelGGL((prep_kernel_h<false, true>), dim3(p.H * p.um.n_chunks), dim3(64), 0, s, a);
         else hipLaunchKernelGGL((prep_kernel<PolicyF, false>), grid, block, 0, s, a);
     }
     return hipGetLastError();

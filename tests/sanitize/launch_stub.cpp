@@ -117,10 +117,10 @@ hipError_t launch_merge(int B, int H, int n_seg, const float* S_ext, const float
     return hipSuccess;
 }
 
-hipError_t launch_prep_f32(const Problem& p, const Workspace& ws, const void* k, const void*, const float* g,
+hipError_t launch_prep_bwd(const Problem& p, const Workspace& ws, const void* k, const void*, const float* g,
                            const void* beta, hipStream_t) {
     check_problem(p, ws);
-    if (p.um.total_tokens > 0 && (!k || !g || !beta)) fail("fp32 prep inputs");
+    if (p.um.total_tokens > 0 && (!k || !g || !beta)) fail("backward prep inputs");
     return hipSuccess;
 }
 
@@ -129,7 +129,7 @@ hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* d
                       const float*, float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0, bool dh_only,
                       bool, hipStream_t) {
     gdn::Problem pf = p;
-    pf.dtype = 0;                  // the backward's preparation has fp32 operands
+    pf.dtype = 0;                  // the backward's preparation: the fp32 workspace layout
     check_problem(pf, ws);
     const int64_t nch = int64_t(p.um.n_chunks) * p.H;
     region(dH, nch * 128 * 128 * 4, "dH region");
