@@ -28,16 +28,19 @@
 // memory that another thread of the kernel writes, so the per-chunk stores
 // (dh', dvn, dv) stay in flight across barriers.
 //
-// Kernels (fp32 operands on the fp32 16x16x4 MFMA, LDS tiles):
-//   bwd_dh_kernel    one workgroup per (unit, head, 32 value columns): the
-//                    reverse state pass; stores dh' and dvn of every chunk
-//                    and dL/dS0.
+// Kernels:
+//   bwd_dh_kernel    one workgroup per (unit, head, 16 or 32 value columns):
+//                    the reverse state pass; stores dh' and dvn of every
+//                    chunk and dL/dS0.
 //   bwd_grad_kernel  one workgroup per (chunk, head): recomputes Y and v_new
 //                    from the stored entry state, accumulates the products
-//                    over the value columns in 16-column tiles, then forms
-//                    dq, dk, dv, dbeta and dg.
-// The chunk preparation (T, P and the gate rows, fp32) comes from the
-// forward's fp32-operand preparation kernel.
+//                    over the value columns in tiles, then forms dq, dk, dv,
+//                    dbeta and dg.
+// fp32 inputs and the per-key gate use fp32 operands (fp32 16x16x4 MFMA,
+// fp32 LDS tiles) and the fp32 preparation (T, P, gate rows or gated tiles).
+// bf16 inputs with a scalar gate use bwd_dh_kernel_h and bwd_grad_kernel_h:
+// fp16 LDS tiles and the fp16 16x16x32 MFMA with fp32 accumulation, fed by
+// the forward's bf16 preparation writing T and P as fp16.
 //
 // Per-key gate (b^G a 64 x K matrix): Kd, Qd and Kg are the prepared gated
 // tiles and gamma = diag(b^{G_L}), so the reverse state pass and the value-
@@ -277,28 +280,20 @@ __device__ void load_chunk_pk(const BwdArgs& a, int64_t t0, int64_t ch, int head
 // acc += A B^T over k in [0, KLEN), A and B stored row by row with k
 // contiguous (rows lda / ldb floats apart, 16-byte aligned): lane (G, n)
 // reads k = k0 + 4G .. +3 of row n of each with one 16-byte load per 16 k,
-// as four fp32 MFMAs or (H16) one fp16 16x16x16 MFMA
-template <bool H16, int KLEN>
+// as four fp32 MFMAs
+template <int KLEN>
 __device__ __forceinline__ void mm_rowsk(f32x4& acc, const float* A, int lda, const float* B, int ldb, int G, int n) {
 #pragma unroll
     for (int k0 = 0; k0 < KLEN; k0 += 16) {
         const f32x4 x = *reinterpret_cast<const f32x4*>(A + n * lda + k0 + 4 * G);
         const f32x4 y = *reinterpret_cast<const f32x4*>(B + n * ldb + k0 + 4 * G);
-        if (H16) {
-            f16x4 xh, yh;
-            for (int e = 0; e < 4; ++e) {
-                xh[e] = (f16)x[e];
-                yh[e] = (f16)y[e];
-            }
-            acc = __builtin_amdgcn_mfma_f32_16x16x16f16(xh, yh, acc, 0, 0, 0);
-        } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e], y[e], acc, 0, 0, 0);
-        }
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e], y[e], acc, 0, 0, 0);
     }
 }
 
 // ------------------------------------------------------------------ reverse state pass
+// fp32 operands: fp32 inputs, and the per-key gate at either input dtype.
 // One workgroup of four waves per (unit, head, 16 NCT value columns); wave w
 // holds dL/dh for keys 32w .. 32w+31 of those columns (2 NCT 16 x 16 tiles).
 // NCT = 1 (16-column tiles) doubles the workgroups where 32-column tiles
@@ -342,31 +337,6 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
                 dhT[col * BKL + key] = x;
             }
 
-    // bf16 inputs, scalar gate: the next chunk's tiles are loaded into
-    // registers while this chunk is computed (about 70 VGPRs), and written
-    // to LDS at the top of the next step, T already scaled by beta
-    constexpr bool PF = !PK && std::is_same<In, bf16>::value;
-    constexpr bool H16 = PF;                     // Kg dh' on fp16 MFMA (bf16 inputs, scalar gate)
-    TileRegs<In, BT, DK> pk_, pq_;
-    TileRegs<float, BT, BT> pt_, pp_;
-    TileRegs<In, BT, NC> pd_;
-    float pg_ = 0.0f, pb_[4] = {0.f, 0.f, 0.f, 0.f};
-    auto prefetch = [&](int cc) {
-        int l = ui.len - cc * BT;
-        l = l > BT ? BT : l;
-        const int64_t tt = ui.start + (int64_t)cc * BT, chh = (int64_t)(ui.cbase + cc) * H + head;
-        const int64_t rs = (int64_t)H * DK;
-        pk_.issue(reinterpret_cast<const In*>(a.k) + (tt * H + head) * DK, rs, l, tid);
-        pq_.issue(reinterpret_cast<const In*>(a.q) + (tt * H + head) * DK, rs, l, tid);
-        pt_.issue(reinterpret_cast<const float*>(a.ws.Tm) + chh * (BT * BT), BT, BT, tid);
-        pp_.issue(reinterpret_cast<const float*>(a.ws.P) + chh * (BT * BT), BT, BT, tid);
-        pd_.issue(dout + (tt * H + head) * DV + c0, (int64_t)H * DV, l, tid);
-        pg_ = a.ws.gam[chh * (GAMR * BT) + tid];      // rows 0..3 (no q / k normalisation here)
-        const int cb = 4 * (tid & 15);                // the columns of this thread's T vectors
-        for (int j = 0; j < 4; ++j)
-            pb_[j] = cb + j < l ? ldf(reinterpret_cast<const In*>(a.beta), (tt + cb + j) * H + head) : 0.0f;
-    };
-    if (PF && ui.nch > 0) prefetch(ui.nch - 1);
 
     for (int c = ui.nch - 1; c >= 0; --c) {
         int len = ui.len - c * BT;
@@ -374,20 +344,9 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
         const int64_t t0 = ui.start + (int64_t)c * BT;
         const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
         lds_barrier();                               // the previous chunk's tiles are consumed
-        if (PF) {
-            pk_.commit(Ks, BKL, tid);
-            pq_.commit(Qs, BKL, tid);
-            pt_.commit(Ts, BTL, tid, pb_);          // T diag(beta)
-            pp_.commit(Ps, BTL, tid);
-            pd_.commit(dOs, CL, tid);
-            gm[tid] = pg_;
-            lds_barrier();
-            if (c > 0) prefetch(c - 1);
-        } else {
-            if (PK) load_chunk_pk<In>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, bt, tid);
-            else load_chunk<In, true>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, gm, bt, tid);
-            load_tile<In, BT, NC>(dout + (t0 * H + head) * DV + c0, (int64_t)H * DV, len, dOs, CL, tid);
-        }
+        if (PK) load_chunk_pk<In>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, bt, tid);
+        else load_chunk<In, true>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, gm, bt, tid);
+        load_tile<In, BT, NC>(dout + (t0 * H + head) * DV + c0, (int64_t)H * DV, len, dOs, CL, tid);
         float gk[2][4];                                // per key: b^{G_L} of keys 32w + 16kt + 4G + r
         if (PK)
             for (int kt = 0; kt < 2; ++kt)
@@ -405,7 +364,7 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
         // Kg = diag(b^{G_L - G}) K)
         for (int ct = 0; ct < NCT; ++ct) {
             f32x4 kh = {0.f, 0.f, 0.f, 0.f}, pd = {0.f, 0.f, 0.f, 0.f};
-            mm_rowsk<H16, DK>(kh, Ks + 16 * w * BKL, BKL, dhT + 16 * ct * BKL, BKL, G, n);
+            mm_rowsk<DK>(kh, Ks + 16 * w * BKL, BKL, dhT + 16 * ct * BKL, BKL, G, n);
             mmf<BT>(pd, [&](int m, int k) { return Ps[k * BTL + 16 * w + m]; },
                     [&](int k, int nn) { return dOs[k * CL + 16 * ct + nn]; }, G, n);
             for (int r = 0; r < 4; ++r) {
@@ -456,6 +415,7 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ per-chunk gradients
+// fp32 operands: fp32 inputs, and the per-key gate at either input dtype.
 // One workgroup of four waves per (chunk, head); wave w owns token rows
 // 16w .. 16w+15 of every row-indexed product. The value columns are visited
 // in 16-column tiles: each recomputes Y = V - Kd h and v_new = Tb Y, writes
@@ -470,24 +430,11 @@ constexpr int VTL = VT + 4;     // row stride: 16-byte aligned rows; rows 80 byt
 // row n of each with one 16-byte load, and MFMA e contracts column 4G' + e
 // of every lane group G' (the order of the terms inside one contraction
 // does not matter)
-// With H16 (bf16 inputs) the same four columns go as fp16 operands into one
-// 16x16x16 fp16 MFMA (lane (G, n) supplies A[n][4G..4G+3] and B[4G..4G+3][n]
-// there as well), accumulating in fp32.
-template <bool H16>
 __device__ __forceinline__ void mm_rows16(f32x4& acc, const float* A, const float* B, float sa, int G, int n) {
     const f32x4 x = *reinterpret_cast<const f32x4*>(A + n * VTL + 4 * G);
     const f32x4 y = *reinterpret_cast<const f32x4*>(B + n * VTL + 4 * G);
-    if (H16) {
-        f16x4 xh, yh;
-        for (int e = 0; e < 4; ++e) {
-            xh[e] = (f16)(sa * x[e]);
-            yh[e] = (f16)y[e];
-        }
-        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(xh, yh, acc, 0, 0, 0);
-    } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sa * x[e], y[e], acc, 0, 0, 0);
-    }
+    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sa * x[e], y[e], acc, 0, 0, 0);
 }
 
 // The per-key finish of bwd_grad_kernel. On entry: dl = dL rows of this wave
@@ -743,9 +690,6 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
     float hdh = 0.0f;     // this thread's share of sum(h o dh')
     float hk[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // per key: keys (tid >> 4) + 16m, column tid & 15
 
-    // fp16 operands for the value-tile products with bf16 inputs and a scalar
-    // gate (per key, dg under strong gates needs the fp32 operands)
-    constexpr bool H16 = std::is_same<In, bf16>::value && !PK;
     // the value tiles of tile vt + 1 are loaded into registers while tile vt
     // is computed (28 VGPRs), and written to LDS at the next tile's top
     TileRegs<float, DK, VT> ph, pdh;
@@ -805,13 +749,13 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
         lds_barrier();
         // accumulate over this tile's columns (both operands column-contiguous)
         for (int j = 0; j < 4; ++j) {
-            mm_rows16<H16>(aP[j], DOs + row0 * VTL, VNs + 16 * j * VTL, a.scale, G, n);
-            mm_rows16<H16>(aT[j], DVs + row0 * VTL, Ys + 16 * j * VTL, 1.0f, G, n);
+            mm_rows16(aP[j], DOs + row0 * VTL, VNs + 16 * j * VTL, a.scale, G, n);
+            mm_rows16(aT[j], DVs + row0 * VTL, Ys + 16 * j * VTL, 1.0f, G, n);
         }
         for (int j = 0; j < 8; ++j) {
-            mm_rows16<H16>(aQ[j], DOs + row0 * VTL, Hs + 16 * j * VTL, a.scale, G, n);
-            mm_rows16<H16>(aKg[j], VNs + row0 * VTL, DHs + 16 * j * VTL, 1.0f, G, n);
-            mm_rows16<H16>(aKd[j], Zs + row0 * VTL, Hs + 16 * j * VTL, -1.0f, G, n);
+            mm_rows16(aQ[j], DOs + row0 * VTL, Hs + 16 * j * VTL, a.scale, G, n);
+            mm_rows16(aKg[j], VNs + row0 * VTL, DHs + 16 * j * VTL, 1.0f, G, n);
+            mm_rows16(aKd[j], Zs + row0 * VTL, Hs + 16 * j * VTL, -1.0f, G, n);
         }
     }
     lds_barrier();
@@ -1063,7 +1007,11 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel_h(BwdArgs a) {
     TileRegs<bf16, BT, DK> pk, pq;
     TileRegs<f16, BT, BT> pt, pp;                  // T and P: fp16 from the preparation
     TileRegs<bf16, BT, NC> pd;
-    float pg = 0.0f, pbg = 0.0f, pb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // the gate row element and the raw bf16 beta of this thread's T columns,
+    // converted only where they are used (a conversion next to its load
+    // would wait for every load issued before it)
+    float pg = 0.0f, pbg = 0.0f;
+    uint32_t pbr[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
     auto prefetch = [&](int cc) {
         int l = ui.len - cc * BT;
         l = l > BT ? BT : l;
@@ -1075,16 +1023,21 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel_h(BwdArgs a) {
         pp.issue(reinterpret_cast<const f16*>(a.ws.P) + chh * (BT * BT), BT, BT, tid);
         pd.issue(dout + (tt * H + head) * DV + c0, (int64_t)H * DV, l, tid);
         pg = a.ws.gam[chh * (GAMR * BT) + tid];      // rows 0..3 (no q / k normalisation here)
-        const int cb = 8 * (tid & 7);                // the columns of this thread's T vectors
-        for (int j = 0; j < 8; ++j) pb[j] = cb + j < l ? (float)bin[(tt + cb + j) * H + head] : 0.0f;
-        const int dr = tid / TileRegs<bf16, BT, NC>::PER_ROW;   // this thread's dO row
-        pbg = dr < BT ? a.ws.gam[chh * (GAMR * BT) + BT + dr] : 0.0f;
+        // beta of this thread's T columns 8 (tid & 7) + j; past the chunk end zero
+        const rsrc_t rb = make_rsrc(bin + tt * H + head, l > 0 ? ((uint32_t)(l - 1) * H + 1) * 2 : 0);
+        const int cb = 8 * (tid & 7);
+        for (int j = 0; j < 8; ++j) pbr[j] = __builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(cb + j) * H * 2, 0, 0);
+        // b^G of this thread's dO row (threads past the tile's rows store nothing)
+        const int dr = min(tid / TileRegs<bf16, BT, NC>::PER_ROW, BT - 1);
+        pbg = a.ws.gam[chh * (GAMR * BT) + BT + dr];
     };
     if (ui.nch > 0) prefetch(ui.nch - 1);
 
     for (int c = ui.nch - 1; c >= 0; --c) {
         const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
         lds_barrier();                               // the previous chunk's tiles are consumed
+        float pb[8];
+        for (int j = 0; j < 8; ++j) pb[j] = u2f(pbr[j] << 16);
         pk.commit_h(Kh, HK, tid);
         pq.commit_h(Qh, HK, tid);
         pt.commit_h_cols(Tbh, HT, tid, pb);
@@ -1227,12 +1180,20 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a) {
         tq.issue(reinterpret_cast<const bf16*>(a.q) + (t0 * H + head) * DK, rs, len, tid);
         tt.issue(reinterpret_cast<const f16*>(a.ws.Tm) + ch * (BT * BT), BT, BT, tid);
         tp.issue(reinterpret_cast<const f16*>(a.ws.P) + ch * (BT * BT), BT, BT, tid);
-        float pb[8];                                 // beta of this thread's T columns 8 (tid & 7) + j
-        const int cb = 8 * (tid & 7);
-        for (int j = 0; j < 8; ++j) pb[j] = cb + j < len ? (float)bin[(t0 + cb + j) * H + head] : 0.0f;
-        if (tid < BT) bt[tid] = tid < len ? (float)bin[(t0 + tid) * H + head] : 0.0f;
-        gm[tid] = a.ws.gam[ch * (GAMR * BT) + tid];   // G, b^G, b^{G_L - G}, b^{G_L}
+        // raw bf16 beta (past the chunk end zero), converted after the value
+        // tile loads are issued: a conversion next to its load would wait
+        // for every load before it
+        const rsrc_t rb = make_rsrc(bin + t0 * H + head, len > 0 ? ((uint32_t)(len - 1) * H + 1) * 2 : 0);
+        const int cb = 8 * (tid & 7);                // this thread's T columns 8 (tid & 7) + j
+        uint32_t pbr[8];
+        for (int j = 0; j < 8; ++j) pbr[j] = __builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(cb + j) * H * 2, 0, 0);
+        const uint32_t btr = __builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(tid & (BT - 1)) * H * 2, 0, 0);
+        const float gmv = a.ws.gam[ch * (GAMR * BT) + tid];   // G, b^G, b^{G_L - G}, b^{G_L}
         prefetch(0);
+        float pb[8];
+        for (int j = 0; j < 8; ++j) pb[j] = u2f(pbr[j] << 16);
+        if (tid < BT) bt[tid] = u2f(btr << 16);
+        gm[tid] = gmv;
         tk.commit_h(Kh, HK, tid);
         tq.commit_h(Qh, HK, tid);
         tt.commit_h(Th, HT, tid, pb, Tbh);
