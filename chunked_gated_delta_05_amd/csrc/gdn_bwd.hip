@@ -966,16 +966,17 @@ __device__ __forceinline__ f32x4 ld4h(const f16* p) {
 template <int NCT>
 __global__ __launch_bounds__(256) void bwd_dh_kernel_h(BwdArgs a) {
     constexpr int NC = 16 * NCT, HC = NC + 8;     // columns of the tile, LDS row stride (halves)
-    __shared__ __attribute__((aligned(16))) f16 Kh[BT * HK];
-    __shared__ __attribute__((aligned(16))) f16 Qh[BT * HK];
-    __shared__ __attribute__((aligned(16))) f16 Tbh[BT * HT];   // T diag(beta)
-    __shared__ __attribute__((aligned(16))) f16 Ph[BT * HT];
-    __shared__ __attribute__((aligned(16))) f16 dOh[BT * HC];   // dO
-    __shared__ __attribute__((aligned(16))) f16 dOg[BT * HC];   // scale b^G dO
-    __shared__ __attribute__((aligned(16))) f16 DVh[BT * HC];   // dvn
-    __shared__ __attribute__((aligned(16))) f16 Zh[BT * HC];    // b^G Z
-    __shared__ __attribute__((aligned(16))) f16 dhT[NC * HK];   // dh' [column][key]
-    __shared__ __attribute__((aligned(16))) float gm[4 * BT];   // G, b^G, b^{G_L - G}, b^{G_L}
+    // the chunk tiles, double-buffered (chunk c in buffer c & 1)
+    __shared__ __attribute__((aligned(16))) f16 Kh[2][BT * HK];
+    __shared__ __attribute__((aligned(16))) f16 Qh[2][BT * HK];
+    __shared__ __attribute__((aligned(16))) f16 Tbh[2][BT * HT];   // T diag(beta)
+    __shared__ __attribute__((aligned(16))) f16 Ph[2][BT * HT];
+    __shared__ __attribute__((aligned(16))) f16 dOh[2][BT * HC];   // dO
+    __shared__ __attribute__((aligned(16))) f16 dOg[2][BT * HC];   // scale b^G dO
+    __shared__ __attribute__((aligned(16))) float gm[2][4 * BT];   // G, b^G, b^{G_L - G}, b^{G_L}
+    __shared__ __attribute__((aligned(16))) f16 DVh[BT * HC];      // dvn
+    __shared__ __attribute__((aligned(16))) f16 Zh[BT * HC];       // b^G Z
+    __shared__ __attribute__((aligned(16))) f16 dhT[NC * HK];      // dh' [column][key]
 
     const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1002,8 +1003,9 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel_h(BwdArgs a) {
             st4h(dhT + (16 * ct + n) * HK + 32 * w + 16 * kt + 4 * G, dh[kt][ct]);
         }
 
-    // the next chunk's tiles are loaded into registers while this chunk is
-    // computed, and written to LDS at the top of the next step
+    // the tiles of chunk c - 1 are loaded into registers while chunk c + 1
+    // is computed, and written to their LDS buffer at the end of chunk c's
+    // step (after its last products, whose buffer is the other one)
     TileRegs<bf16, BT, DK> pk, pq;
     TileRegs<f16, BT, BT> pt, pp;                  // T and P: fp16 from the preparation
     TileRegs<bf16, BT, NC> pd;
@@ -1031,22 +1033,27 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel_h(BwdArgs a) {
         const int dr = min(tid / TileRegs<bf16, BT, NC>::PER_ROW, BT - 1);
         pbg = a.ws.gam[chh * (GAMR * BT) + BT + dr];
     };
-    if (ui.nch > 0) prefetch(ui.nch - 1);
+    auto commit = [&](int b) {
+        float pb[8];
+        for (int j = 0; j < 8; ++j) pb[j] = u2f(pbr[j] << 16);
+        pk.commit_h(Kh[b], HK, tid);
+        pq.commit_h(Qh[b], HK, tid);
+        pt.commit_h_cols(Tbh[b], HT, tid, pb);
+        pp.commit_h(Ph[b], HT, tid);
+        pd.commit_h(dOh[b], HC, tid);
+        pd.commit_h_mul(dOg[b], HC, tid, a.scale * pbg);
+        gm[b][tid] = pg;
+    };
+    if (ui.nch > 0) {
+        prefetch(ui.nch - 1);
+        commit((ui.nch - 1) & 1);
+        if (ui.nch > 1) prefetch(ui.nch - 2);
+    }
+    lds_barrier();                                   // the last chunk's tiles and dh' published
 
     for (int c = ui.nch - 1; c >= 0; --c) {
         const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
-        lds_barrier();                               // the previous chunk's tiles are consumed
-        float pb[8];
-        for (int j = 0; j < 8; ++j) pb[j] = u2f(pbr[j] << 16);
-        pk.commit_h(Kh, HK, tid);
-        pq.commit_h(Qh, HK, tid);
-        pt.commit_h_cols(Tbh, HT, tid, pb);
-        pp.commit_h(Ph, HT, tid);
-        pd.commit_h(dOh, HC, tid);
-        pd.commit_h_mul(dOg, HC, tid, a.scale * pbg);
-        gm[tid] = pg;
-        lds_barrier();
-        if (c > 0) prefetch(c - 1);
+        const int b = c & 1;
         // dh' of this chunk to the workspace
         for (int kt = 0; kt < 2; ++kt)
             for (int ct = 0; ct < NCT; ++ct)
@@ -1056,16 +1063,16 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel_h(BwdArgs a) {
                 }
         // dvn = b^{G_L - G} (K dh') + scale P^T dO, rows of this wave
         {
-            const float blg = gm[2 * BT + im];
+            const float blg = gm[b][2 * BT + im];
             f16x8 bk[4], bp[2];
-            for (int ks = 0; ks < 4; ++ks) bk[ks] = frag_row(Kh, HK, im, 32 * ks, G);
+            for (int ks = 0; ks < 4; ++ks) bk[ks] = frag_row(Kh[b], HK, im, 32 * ks, G);
             for (int js = 0; js < 2; ++js)
-                if (js >= hi_js) bp[js] = frag_col(Ph, HT, 32 * js, row0, G, n);
+                if (js >= hi_js) bp[js] = frag_col(Ph[b], HT, 32 * js, row0, G, n);
             for (int ct = 0; ct < NCT; ++ct) {
                 f32x4 kh = {0.f, 0.f, 0.f, 0.f}, pdo = kh;
                 for (int ks = 0; ks < 4; ++ks) mma_h(kh, frag_row(dhT, HK, 16 * ct + n, 32 * ks, G), bk[ks]);
                 for (int js = 0; js < 2; ++js)
-                    if (js >= hi_js) mma_h(pdo, frag_col(dOh, HC, 32 * js, 16 * ct, G, n), bp[js]);
+                    if (js >= hi_js) mma_h(pdo, frag_col(dOh[b], HC, 32 * js, 16 * ct, G, n), bp[js]);
                 f32x4 x;
                 for (int r = 0; r < 4; ++r) x[r] = blg * kh[r] + a.scale * pdo[r];
                 st4h(DVh + im * HC + 16 * ct + 4 * G, x);
@@ -1075,10 +1082,10 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel_h(BwdArgs a) {
         lds_barrier();
         // b^G Z = b^G (Tb^T dvn), rows of this wave
         {
-            const float bg = gm[BT + im];
+            const float bg = gm[b][BT + im];
             f16x8 btb[2];
             for (int js = 0; js < 2; ++js)
-                if (js >= hi_js) btb[js] = frag_col(Tbh, HT, 32 * js, row0, G, n);
+                if (js >= hi_js) btb[js] = frag_col(Tbh[b], HT, 32 * js, row0, G, n);
             for (int ct = 0; ct < NCT; ++ct) {
                 f32x4 z = {0.f, 0.f, 0.f, 0.f};
                 for (int js = 0; js < 2; ++js)
@@ -1089,24 +1096,31 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel_h(BwdArgs a) {
         }
         lds_barrier();
         // dh = gamma dh' + Q^T (scale b^G dO) - K^T (b^G Z), keys 32w .. +31
-        const float gam = gm[3 * BT];
+        const float gam = gm[b][3 * BT];
         for (int kt = 0; kt < 2; ++kt) {
             const int key0 = 32 * w + 16 * kt;
             f16x8 aq[2], ak[2];
             for (int js = 0; js < 2; ++js) {
-                aq[js] = frag_col(Qh, HK, 32 * js, key0, G, n);
-                ak[js] = frag_col(Kh, HK, 32 * js, key0, G, n);
+                aq[js] = frag_col(Qh[b], HK, 32 * js, key0, G, n);
+                ak[js] = frag_col(Kh[b], HK, 32 * js, key0, G, n);
             }
             for (int ct = 0; ct < NCT; ++ct) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acz = acc;
                 for (int js = 0; js < 2; ++js) {
-                    mma_h(acc, aq[js], frag_col(dOg, HC, 32 * js, 16 * ct, G, n));
+                    mma_h(acc, aq[js], frag_col(dOg[b], HC, 32 * js, 16 * ct, G, n));
                     mma_h(acz, ak[js], frag_col(Zh, HC, 32 * js, 16 * ct, G, n));
                 }
                 for (int r = 0; r < 4; ++r) dh[kt][ct][r] = gam * dh[kt][ct][r] + acc[r] - acz[r];
                 st4h(dhT + (16 * ct + n) * HK + key0 + 4 * G, dh[kt][ct]);
             }
         }
+        // chunk c - 1 into the other buffer (last read by chunk c + 1), then
+        // the loads of chunk c - 2
+        if (c > 0) {
+            commit(b ^ 1);
+            if (c > 1) prefetch(c - 2);
+        }
+        lds_barrier();                               // dh' and chunk c - 1 published
     }
     if (a.dh0)
         for (int kt = 0; kt < 2; ++kt)
