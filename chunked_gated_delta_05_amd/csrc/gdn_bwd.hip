@@ -206,6 +206,30 @@ struct TileRegs {
             *reinterpret_cast<hv*>(dst + r * ld + c) = h;
         }
     }
+    // fp16 values with vector i's row scaled by rowscale[i]
+    __device__ __forceinline__ void commit_h_rows(f16* dst, int ld, int tid, const float* rowscale) const {
+#pragma unroll
+        for (int i = 0; i < PT; ++i) {
+            const int e = tid + 256 * i, r = e / PER_ROW, c = (e - r * PER_ROW) * VPR;
+            if (e < NV) {
+                float x[VPR];
+                Vec16<In>::cvt(w[i], x);
+                typedef _Float16 hv __attribute__((ext_vector_type(VPR)));
+                hv h;
+                for (int j = 0; j < VPR; ++j) h[j] = (f16)(x[j] * rowscale[i]);
+                *reinterpret_cast<hv*>(dst + r * ld + c) = h;
+            }
+        }
+    }
+    // the 16-byte vectors as they are (fp16 tiles)
+    __device__ __forceinline__ void commit_raw(f16* dst, int ld, int tid) const {
+        static_assert(std::is_same<In, f16>::value, "raw copies of fp16 tiles");
+#pragma unroll
+        for (int i = 0; i < PT; ++i) {
+            const int e = tid + 256 * i, r = e / PER_ROW, c = (e - r * PER_ROW) * VPR;
+            if (e < NV) *reinterpret_cast<u32x4*>(dst + r * ld + c) = w[i];
+        }
+    }
     // fp16 values with column c + j of a vector scaled by colscale[j]
     __device__ __forceinline__ void commit_h_cols(f16* dst, int ld, int tid, const float* colscale) const {
 #pragma unroll
@@ -222,19 +246,6 @@ struct TileRegs {
         }
     }
 };
-
-// sum over a tile of the elementwise product of two fp32 tiles held with the
-// same thread mapping
-template <int ROWS, int NCOLS>
-__device__ __forceinline__ float dot_regs(const TileRegs<float, ROWS, NCOLS>& x, const TileRegs<float, ROWS, NCOLS>& y,
-                                          int tid) {
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < TileRegs<float, ROWS, NCOLS>::PT; ++i)
-        if (tid + 256 * i < TileRegs<float, ROWS, NCOLS>::NV)
-            for (int j = 0; j < 4; ++j) s += u2f(x.w[i][j]) * u2f(y.w[i][j]);
-    return s;
-}
 
 // a tile into LDS: all loads issued before any store, so that their
 // latencies overlap
@@ -318,7 +329,11 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = a.H;
-    const int tile = blockIdx.x % (DV / NC), pair = blockIdx.x / (DV / NC);
+    // XCD-aware: workgroups are dealt to the 8 XCDs round-robin, so the
+    // column tiles of one (unit, head), which read the same chunk tiles, are
+    // given grid slots 8 apart and share that XCD's L2
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int tile = slot % (DV / NC), pair = (slot / (DV / NC)) * 8 + xcd;
     if (pair >= a.n_pairs) return;
     const int u = pair / H, head = pair - u * H;
     const UnitInfo ui = uniform(unit_info(a.um, u));
@@ -956,100 +971,183 @@ __device__ __forceinline__ f32x4 ld4h(const f16* p) {
 }
 
 // ------------------------------------------------------------------ reverse state pass, bf16 inputs, scalar gate
-// bwd_dh_kernel on fp16 tiles and the fp16 16x16x32 MFMA: one workgroup of
-// four waves per (unit, head, 16 NCT value columns), dL/dh in fp32 registers
-// (wave w: keys 32w .. 32w+31), its fp16 copy in LDS as [column][key] for
-// the next chunk's Kg dh'. dvn and b^G Z are formed transposed (lane (G, n):
-// token row 16w + n, columns 4G .. 4G+3 of each 16-column block), so that
-// dvn reaches the workspace in 16-byte stores. dO is held twice: as given
-// (P^T dO) and scaled by scale b^G per row (Qd^T dO).
+// Regrouped, the reverse chunk step is an affine map of the state gradient
+// (D = dL/dh at the chunk's exit, D' at its entry):
+//   D' = gamma D + scale Qd^T dO - Kd^T Z,  Z = Tb^T dvn,  dvn = Kg D + scale P^T dO
+//      = A D + scale U^T dO,   A = gamma I - W^T Kg,  U = Qd - P W,  W = Tb Kd
+// (W is the WY form's w; A is the transpose of the chunk's transfer map of
+// the forward, h' = A^T h + ...). A and U depend on the chunk only, so
+// bwd_transfer_kernel_h forms them for every chunk at once, and the
+// sequential pass is one 128 x 128 product and one barrier per chunk.
+
+// A (128 x 128, [key'][key]) and U (64 x 128, [row][key]) of every chunk-head,
+// fp16: one workgroup of four waves per (chunk, head). W = T diag(beta b^G) K
+// first (wave w: rows 16w .. +15), then A (wave w: rows 32w .. +31) and U
+// (rows 16w .. +15), formed transposed so that each lane holds 4 consecutive
+// columns of one row.
+__global__ __launch_bounds__(256) void bwd_transfer_kernel_h(BwdArgs a, f16* Aw, f16* Uw) {
+    __shared__ __attribute__((aligned(16))) f16 Kh[BT * HK];     // K
+    __shared__ __attribute__((aligned(16))) f16 Kgh[BT * HK];    // Kg = diag(b^{G_L - G}) K
+    __shared__ __attribute__((aligned(16))) f16 Tgh[BT * HT];    // T diag(beta b^G)
+    __shared__ __attribute__((aligned(16))) f16 Ph[BT * HT];
+    __shared__ __attribute__((aligned(16))) f16 Wh[BT * HK];     // W
+    __shared__ __attribute__((aligned(16))) float gm[4 * BT];    // G, b^G, b^{G_L - G}, b^{G_L}
+
+    const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ci = blockIdx.x, head = blockIdx.y, H = a.H;
+    int u, cc;
+    chunk_of(a.um, ci, u, cc);
+    if (u < 0) return;
+    const UnitInfo ui = unit_info(a.um, u);
+    const int64_t t0 = ui.start + (int64_t)cc * BT;
+    int len = ui.len - cc * BT;
+    len = len < 0 ? 0 : (len > BT ? BT : len);
+    const int64_t ch = (int64_t)ci * H + head;
+    const bf16* bin = reinterpret_cast<const bf16*>(a.beta);
+    const int row0 = 16 * w, im = row0 + n;
+    const int lo_js = w >= 2 ? 2 : 1;            // 32-row steps i <= j can reach
+    const float* gam = a.ws.gam + ch * (GAMR * BT);
+    {
+        TileRegs<bf16, BT, DK> tk;
+        TileRegs<f16, BT, BT> tt, tp;
+        tk.issue(reinterpret_cast<const bf16*>(a.k) + (t0 * H + head) * DK, (int64_t)H * DK, len, tid);
+        tt.issue(reinterpret_cast<const f16*>(a.ws.Tm) + ch * (BT * BT), BT, BT, tid);
+        tp.issue(reinterpret_cast<const f16*>(a.ws.P) + ch * (BT * BT), BT, BT, tid);
+        // beta (raw, past the chunk end zero) and b^G of this thread's T
+        // columns 8 (tid & 7) + j; b^{G_L - G} of its k rows 16 i + tid / 16
+        const rsrc_t rb = make_rsrc(bin + t0 * H + head, len > 0 ? ((uint32_t)(len - 1) * H + 1) * 2 : 0);
+        const int cb = 8 * (tid & 7);
+        uint32_t pbr[8];
+        for (int j = 0; j < 8; ++j) pbr[j] = __builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(cb + j) * H * 2, 0, 0);
+        const u32x4 g0 = *reinterpret_cast<const u32x4*>(gam + BT + cb), g1 = *reinterpret_cast<const u32x4*>(gam + BT + cb + 4);
+        float rs[4];
+        for (int i = 0; i < 4; ++i) rs[i] = gam[2 * BT + 16 * i + (tid >> 4)];
+        const float gmv = gam[tid];
+        float pb[8];
+        for (int j = 0; j < 8; ++j) pb[j] = u2f(pbr[j] << 16) * u2f(j < 4 ? g0[j] : g1[j - 4]);
+        gm[tid] = gmv;
+        tk.commit_h(Kh, HK, tid);
+        tk.commit_h_rows(Kgh, HK, tid, rs);
+        tt.commit_h_cols(Tgh, HT, tid, pb);
+        tp.commit_h(Ph, HT, tid);
+    }
+    lds_barrier();
+    // W = T diag(beta b^G) K, rows of this wave
+    {
+        f16x8 bt[2];
+        for (int is = 0; is < 2; ++is)
+            if (is < lo_js) bt[is] = frag_row(Tgh, HT, im, 32 * is, G);
+        for (int kb = 0; kb < 8; ++kb) {
+            f32x4 wv = {0.f, 0.f, 0.f, 0.f};
+            for (int is = 0; is < 2; ++is)
+                if (is < lo_js) mma_h(wv, frag_col(Kh, HK, 32 * is, 16 * kb, G, n), bt[is]);
+            st4h(Wh + im * HK + 16 * kb + 4 * G, wv);
+        }
+    }
+    lds_barrier();
+    // A = gamma I - W^T Kg, rows 32w .. 32w+31
+    f16* Ac = Aw + ch * (DK * DK);
+    const float gL = gm[3 * BT];
+    for (int rb2 = 0; rb2 < 2; ++rb2) {
+        const int k1 = 32 * w + 16 * rb2 + n;
+        f16x8 bw[2];
+        for (int js = 0; js < 2; ++js) bw[js] = frag_col(Wh, HK, 32 * js, 32 * w + 16 * rb2, G, n);
+        for (int kb = 0; kb < 8; ++kb) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int js = 0; js < 2; ++js) mma_h(acc, frag_col(Kgh, HK, 32 * js, 16 * kb, G, n), bw[js]);
+            f32x4 x;
+            for (int r = 0; r < 4; ++r) x[r] = (k1 == 16 * kb + 4 * G + r ? gL : 0.0f) - acc[r];
+            st4h(Ac + k1 * DK + 16 * kb + 4 * G, x);
+        }
+    }
+    // U = Qd - P W, rows of this wave (rows past the chunk end: zero q)
+    {
+        f16* Uc = Uw + ch * (BT * DK);
+        const float bg = gm[BT + im];
+        const bf16* qrow = reinterpret_cast<const bf16*>(a.q) + ((t0 + (im < len ? im : 0)) * H + head) * DK;
+        f16x8 bp[2];
+        for (int is = 0; is < 2; ++is)
+            if (is < lo_js) bp[is] = frag_row(Ph, HT, im, 32 * is, G);
+        for (int kb = 0; kb < 8; ++kb) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int is = 0; is < 2; ++is)
+                if (is < lo_js) mma_h(acc, frag_col(Wh, HK, 32 * is, 16 * kb, G, n), bp[is]);
+            const u32x2 qw = im < len ? *reinterpret_cast<const u32x2*>(qrow + 16 * kb + 4 * G) : u32x2{0u, 0u};
+            f32x4 x;
+            for (int r = 0; r < 4; ++r) {
+                const float qv = u2f(r & 1 ? qw[r >> 1] & 0xffff0000u : qw[r >> 1] << 16);
+                x[r] = bg * qv - acc[r];
+            }
+            st4h(Uc + im * DK + 16 * kb + 4 * G, x);
+        }
+    }
+}
+
+// The sequential pass: one workgroup of four waves per (unit, head, 16 NCT
+// value columns); wave w keeps D for keys 32w .. 32w+31 in fp32 registers,
+// and its fp16 copy goes to LDS as [column][key] for the next chunk's
+// product (double-buffered, so each chunk needs one barrier). A, U and dO of
+// chunk c - 1 are loaded into registers while chunk c + 1 is computed and
+// stored to the other LDS buffer at the end of chunk c. dh' (D of every
+// chunk) goes to the workspace as fp16.
 template <int NCT>
-__global__ __launch_bounds__(256) void bwd_dh_kernel_h(BwdArgs a) {
+__global__ __launch_bounds__(256) void bwd_dh_kernel_h(BwdArgs a, const f16* Aw, const f16* Uw, f16* dHw) {
     constexpr int NC = 16 * NCT, HC = NC + 8;     // columns of the tile, LDS row stride (halves)
-    // the chunk tiles, double-buffered (chunk c in buffer c & 1)
-    __shared__ __attribute__((aligned(16))) f16 Kh[2][BT * HK];
-    __shared__ __attribute__((aligned(16))) f16 Qh[2][BT * HK];
-    __shared__ __attribute__((aligned(16))) f16 Tbh[2][BT * HT];   // T diag(beta)
-    __shared__ __attribute__((aligned(16))) f16 Ph[2][BT * HT];
+    __shared__ __attribute__((aligned(16))) f16 Ah[2][DK * HK];    // A [key'][key]
+    __shared__ __attribute__((aligned(16))) f16 Uh[2][BT * HK];    // U [row][key]
     __shared__ __attribute__((aligned(16))) f16 dOh[2][BT * HC];   // dO
-    __shared__ __attribute__((aligned(16))) f16 dOg[2][BT * HC];   // scale b^G dO
-    __shared__ __attribute__((aligned(16))) float gm[2][4 * BT];   // G, b^G, b^{G_L - G}, b^{G_L}
-    __shared__ __attribute__((aligned(16))) f16 DVh[BT * HC];      // dvn
-    __shared__ __attribute__((aligned(16))) f16 Zh[BT * HC];       // b^G Z
-    __shared__ __attribute__((aligned(16))) f16 dhT[NC * HK];      // dh' [column][key]
+    __shared__ __attribute__((aligned(16))) f16 dhT[2][NC * HK];   // D [column][key]
 
     const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = a.H;
-    const int tile = blockIdx.x % (DV / NC), pair = blockIdx.x / (DV / NC);
+    // XCD-aware: workgroups are dealt to the 8 XCDs round-robin, so the
+    // column tiles of one (unit, head), which read the same chunk tiles, are
+    // given grid slots 8 apart and share that XCD's L2
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int tile = slot % (DV / NC), pair = (slot / (DV / NC)) * 8 + xcd;
     if (pair >= a.n_pairs) return;
     const int u = pair / H, head = pair - u * H;
     const UnitInfo ui = uniform(unit_info(a.um, u));
     const int c0 = tile * NC;
     const int64_t uh = (int64_t)u * H + head;
     const bf16* dout = reinterpret_cast<const bf16*>(a.dout);
-    const bf16* bin = reinterpret_cast<const bf16*>(a.beta);
-    const int row0 = 16 * w, im = row0 + n;
-    const int hi_js = w >= 2 ? 1 : 0;            // first 32-row step j >= i can reach
 
-    // dL/dh at the unit's end: keys 32w + 16kt + 4G + r, column 16ct + n
+    // D at the unit's end: keys 32w + 16kt + 4G + r, column 16ct + n
     f32x4 dh[2][NCT];
+    const int b_last = (ui.nch - 1) & 1;
     for (int kt = 0; kt < 2; ++kt)
         for (int ct = 0; ct < NCT; ++ct) {
             for (int r = 0; r < 4; ++r) {
                 const int key = 32 * w + 16 * kt + 4 * G + r, col = 16 * ct + n;
                 dh[kt][ct][r] = a.dht ? a.dht[(uh * DK + key) * DV + c0 + col] : 0.0f;
             }
-            st4h(dhT + (16 * ct + n) * HK + 32 * w + 16 * kt + 4 * G, dh[kt][ct]);
+            st4h(dhT[b_last] + (16 * ct + n) * HK + 32 * w + 16 * kt + 4 * G, dh[kt][ct]);
         }
 
-    // the tiles of chunk c - 1 are loaded into registers while chunk c + 1
-    // is computed, and written to their LDS buffer at the end of chunk c's
-    // step (after its last products, whose buffer is the other one)
-    TileRegs<bf16, BT, DK> pk, pq;
-    TileRegs<f16, BT, BT> pt, pp;                  // T and P: fp16 from the preparation
+    TileRegs<f16, DK, DK> pa;
+    TileRegs<f16, BT, DK> pu;
     TileRegs<bf16, BT, NC> pd;
-    // the gate row element and the raw bf16 beta of this thread's T columns,
-    // converted only where they are used (a conversion next to its load
-    // would wait for every load issued before it)
-    float pg = 0.0f, pbg = 0.0f;
-    uint32_t pbr[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
     auto prefetch = [&](int cc) {
         int l = ui.len - cc * BT;
         l = l > BT ? BT : l;
         const int64_t tt = ui.start + (int64_t)cc * BT, chh = (int64_t)(ui.cbase + cc) * H + head;
-        const int64_t rs = (int64_t)H * DK;
-        pk.issue(reinterpret_cast<const bf16*>(a.k) + (tt * H + head) * DK, rs, l, tid);
-        pq.issue(reinterpret_cast<const bf16*>(a.q) + (tt * H + head) * DK, rs, l, tid);
-        pt.issue(reinterpret_cast<const f16*>(a.ws.Tm) + chh * (BT * BT), BT, BT, tid);
-        pp.issue(reinterpret_cast<const f16*>(a.ws.P) + chh * (BT * BT), BT, BT, tid);
+        pa.issue(Aw + chh * (DK * DK), DK, DK, tid);
+        pu.issue(Uw + chh * (BT * DK), DK, BT, tid);
         pd.issue(dout + (tt * H + head) * DV + c0, (int64_t)H * DV, l, tid);
-        pg = a.ws.gam[chh * (GAMR * BT) + tid];      // rows 0..3 (no q / k normalisation here)
-        // beta of this thread's T columns 8 (tid & 7) + j; past the chunk end zero
-        const rsrc_t rb = make_rsrc(bin + tt * H + head, l > 0 ? ((uint32_t)(l - 1) * H + 1) * 2 : 0);
-        const int cb = 8 * (tid & 7);
-        for (int j = 0; j < 8; ++j) pbr[j] = __builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(cb + j) * H * 2, 0, 0);
-        // b^G of this thread's dO row (threads past the tile's rows store nothing)
-        const int dr = min(tid / TileRegs<bf16, BT, NC>::PER_ROW, BT - 1);
-        pbg = a.ws.gam[chh * (GAMR * BT) + BT + dr];
     };
     auto commit = [&](int b) {
-        float pb[8];
-        for (int j = 0; j < 8; ++j) pb[j] = u2f(pbr[j] << 16);
-        pk.commit_h(Kh[b], HK, tid);
-        pq.commit_h(Qh[b], HK, tid);
-        pt.commit_h_cols(Tbh[b], HT, tid, pb);
-        pp.commit_h(Ph[b], HT, tid);
+        pa.commit_raw(Ah[b], HK, tid);
+        pu.commit_raw(Uh[b], HK, tid);
         pd.commit_h(dOh[b], HC, tid);
-        pd.commit_h_mul(dOg[b], HC, tid, a.scale * pbg);
-        gm[b][tid] = pg;
     };
     if (ui.nch > 0) {
         prefetch(ui.nch - 1);
-        commit((ui.nch - 1) & 1);
+        commit(b_last);
         if (ui.nch > 1) prefetch(ui.nch - 2);
     }
-    lds_barrier();                                   // the last chunk's tiles and dh' published
+    lds_barrier();                                   // the last chunk's tiles and D published
 
     for (int c = ui.nch - 1; c >= 0; --c) {
         const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
@@ -1059,68 +1157,29 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel_h(BwdArgs a) {
             for (int ct = 0; ct < NCT; ++ct)
                 for (int r = 0; r < 4; ++r) {
                     const int key = 32 * w + 16 * kt + 4 * G + r;
-                    a.dH[(ch * DK + key) * DV + c0 + 16 * ct + n] = dh[kt][ct][r];
+                    dHw[(ch * DK + key) * DV + c0 + 16 * ct + n] = (f16)dh[kt][ct][r];
                 }
-        // dvn = b^{G_L - G} (K dh') + scale P^T dO, rows of this wave
-        {
-            const float blg = gm[b][2 * BT + im];
-            f16x8 bk[4], bp[2];
-            for (int ks = 0; ks < 4; ++ks) bk[ks] = frag_row(Kh[b], HK, im, 32 * ks, G);
-            for (int js = 0; js < 2; ++js)
-                if (js >= hi_js) bp[js] = frag_col(Ph[b], HT, 32 * js, row0, G, n);
-            for (int ct = 0; ct < NCT; ++ct) {
-                f32x4 kh = {0.f, 0.f, 0.f, 0.f}, pdo = kh;
-                for (int ks = 0; ks < 4; ++ks) mma_h(kh, frag_row(dhT, HK, 16 * ct + n, 32 * ks, G), bk[ks]);
-                for (int js = 0; js < 2; ++js)
-                    if (js >= hi_js) mma_h(pdo, frag_col(dOh[b], HC, 32 * js, 16 * ct, G, n), bp[js]);
-                f32x4 x;
-                for (int r = 0; r < 4; ++r) x[r] = blg * kh[r] + a.scale * pdo[r];
-                st4h(DVh + im * HC + 16 * ct + 4 * G, x);
-                *reinterpret_cast<f32x4*>(a.dVN + (ch * BT + im) * DV + c0 + 16 * ct + 4 * G) = x;
-            }
-        }
-        lds_barrier();
-        // b^G Z = b^G (Tb^T dvn), rows of this wave
-        {
-            const float bg = gm[b][BT + im];
-            f16x8 btb[2];
-            for (int js = 0; js < 2; ++js)
-                if (js >= hi_js) btb[js] = frag_col(Tbh[b], HT, 32 * js, row0, G, n);
-            for (int ct = 0; ct < NCT; ++ct) {
-                f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                for (int js = 0; js < 2; ++js)
-                    if (js >= hi_js) mma_h(z, frag_col(DVh, HC, 32 * js, 16 * ct, G, n), btb[js]);
-                for (int r = 0; r < 4; ++r) z[r] *= bg;
-                st4h(Zh + im * HC + 16 * ct + 4 * G, z);
-            }
-        }
-        lds_barrier();
-        // dh = gamma dh' + Q^T (scale b^G dO) - K^T (b^G Z), keys 32w .. +31
-        const float gam = gm[b][3 * BT];
+        // D' = A D + scale U^T dO, keys 32w .. +31
         for (int kt = 0; kt < 2; ++kt) {
             const int key0 = 32 * w + 16 * kt;
-            f16x8 aq[2], ak[2];
-            for (int js = 0; js < 2; ++js) {
-                aq[js] = frag_col(Qh[b], HK, 32 * js, key0, G, n);
-                ak[js] = frag_col(Kh[b], HK, 32 * js, key0, G, n);
-            }
+            f16x8 aa[4], au[2];
+            for (int ks = 0; ks < 4; ++ks) aa[ks] = frag_row(Ah[b], HK, key0 + n, 32 * ks, G);
+            for (int js = 0; js < 2; ++js) au[js] = frag_col(Uh[b], HK, 32 * js, key0, G, n);
             for (int ct = 0; ct < NCT; ++ct) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acz = acc;
-                for (int js = 0; js < 2; ++js) {
-                    mma_h(acc, aq[js], frag_col(dOg[b], HC, 32 * js, 16 * ct, G, n));
-                    mma_h(acz, ak[js], frag_col(Zh, HC, 32 * js, 16 * ct, G, n));
-                }
-                for (int r = 0; r < 4; ++r) dh[kt][ct][r] = gam * dh[kt][ct][r] + acc[r] - acz[r];
-                st4h(dhT + (16 * ct + n) * HK + key0 + 4 * G, dh[kt][ct]);
+                f32x4 ad = {0.f, 0.f, 0.f, 0.f}, ae = ad;
+                for (int ks = 0; ks < 4; ++ks) mma_h(ad, aa[ks], frag_row(dhT[b], HK, 16 * ct + n, 32 * ks, G));
+                for (int js = 0; js < 2; ++js) mma_h(ae, au[js], frag_col(dOh[b], HC, 32 * js, 16 * ct, G, n));
+                for (int r = 0; r < 4; ++r) dh[kt][ct][r] = ad[r] + a.scale * ae[r];
+                st4h(dhT[b ^ 1] + (16 * ct + n) * HK + key0 + 4 * G, dh[kt][ct]);
             }
         }
-        // chunk c - 1 into the other buffer (last read by chunk c + 1), then
+        // chunk c - 1 into the other buffers (last read by chunk c + 1), then
         // the loads of chunk c - 2
         if (c > 0) {
             commit(b ^ 1);
             if (c > 1) prefetch(c - 2);
         }
-        lds_barrier();                               // dh' and chunk c - 1 published
+        lds_barrier();                               // D' and chunk c - 1 published
     }
     if (a.dh0)
         for (int kt = 0; kt < 2; ++kt)
@@ -1131,7 +1190,7 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel_h(BwdArgs a) {
                 }
 }
 
-__global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a) {
+__global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a, const f16* dHw) {
     __shared__ __attribute__((aligned(16))) f16 Kh[BT * HK];
     __shared__ __attribute__((aligned(16))) f16 Qh[BT * HK];
     __shared__ __attribute__((aligned(16))) f16 Th[BT * HT];     // T
@@ -1175,16 +1234,15 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a) {
 
     // the value tiles of tile vt + 1 are loaded into registers while tile vt
     // is computed, and written to LDS at the next tile's top
-    TileRegs<float, DK, HVT> ph, pdh;
+    TileRegs<float, DK, HVT> ph;
+    TileRegs<f16, DK, HVT> pdh;
     TileRegs<bf16, BT, HVT> pv, pdo;
-    TileRegs<float, BT, HVT> pdv;
     auto prefetch = [&](int vt) {
         const int vc0 = vt * HVT;
         ph.issue(a.h + ch * DK * DV + vc0, DV, DK, tid);
-        pdh.issue(a.dH + ch * DK * DV + vc0, DV, DK, tid);
+        pdh.issue(dHw + ch * DK * DV + vc0, DV, DK, tid);
         pv.issue(vin + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, tid);
         pdo.issue(dout + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, tid);
-        pdv.issue(a.dVN + ch * BT * DV + vc0, DV, BT, tid);
     };
     {
         TileRegs<bf16, BT, DK> tk, tq;
@@ -1223,26 +1281,42 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a) {
     for (int vt = 0; vt < DV / HVT; ++vt) {
         const int vc0 = vt * HVT;
         lds_barrier();                               // the previous tile's buffers are consumed
-        hdh += dot_regs(ph, pdh, tid);
         ph.commit_h(Hh, HV, tid);
-        pdh.commit_h(DHh, HV, tid);
+        pdh.commit_raw(DHh, HV, tid);
         pv.commit_h(Vh, HV, tid);
         pdo.commit_h(DOh, HV, tid);
-        pdv.commit_h(DVh, HV, tid);
         lds_barrier();
+        // this thread's share of sum(h o dh'): its fp32 h against the fp16 dh'
+#pragma unroll
+        for (int i = 0; i < TileRegs<float, DK, HVT>::PT; ++i) {
+            const int e = tid + 256 * i, r = e / 8, c4 = (e % 8) * 4;
+            const f32x4 d4 = ld4h(DHh + r * HV + c4);
+            for (int j = 0; j < 4; ++j) hdh += u2f(ph.w[i][j]) * d4[j];
+        }
         if (vt + 1 < DV / HVT) prefetch(vt + 1);
-        // Y = V - b^G (K h), rows of this wave
+        // Y = V - b^G (K h) and dvn = b^{G_L - G} (K dh') + scale P^T dO, rows of this wave
         {
-            const float bg = gm[BT + im];
-            f16x8 bk[4];
+            const float bg = gm[BT + im], blg = gm[2 * BT + im];
+            f16x8 bk[4], bp[2];
             for (int ks = 0; ks < 4; ++ks) bk[ks] = frag_row(Kh, HK, im, 32 * ks, G);
+            for (int js = 0; js < 2; ++js)
+                if (js >= hi_js) bp[js] = frag_col(Ph, HT, 32 * js, row0, G, n);
             for (int mb = 0; mb < 2; ++mb) {
-                f32x4 kh = {0.f, 0.f, 0.f, 0.f};
-                for (int ks = 0; ks < 4; ++ks) mma_h(kh, frag_col(Hh, HV, 32 * ks, 16 * mb, G, n), bk[ks]);
+                f32x4 kh = {0.f, 0.f, 0.f, 0.f}, kd = kh, pd = kh;
+                for (int ks = 0; ks < 4; ++ks) {
+                    mma_h(kh, frag_col(Hh, HV, 32 * ks, 16 * mb, G, n), bk[ks]);
+                    mma_h(kd, frag_col(DHh, HV, 32 * ks, 16 * mb, G, n), bk[ks]);
+                }
+                for (int js = 0; js < 2; ++js)
+                    if (js >= hi_js) mma_h(pd, frag_col(DOh, HV, 32 * js, 16 * mb, G, n), bp[js]);
                 const f32x4 v4 = ld4h(Vh + im * HV + 16 * mb + 4 * G);
-                f32x4 y;
-                for (int r = 0; r < 4; ++r) y[r] = v4[r] - bg * kh[r];
+                f32x4 y, dv;
+                for (int r = 0; r < 4; ++r) {
+                    y[r] = v4[r] - bg * kh[r];
+                    dv[r] = blg * kd[r] + a.scale * pd[r];
+                }
                 st4h(Yh + im * HV + 16 * mb + 4 * G, y);
+                st4h(DVh + im * HV + 16 * mb + 4 * G, dv);
             }
         }
         lds_barrier();
@@ -1472,12 +1546,22 @@ hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* d
                       const float* dht, float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0,
                       bool dh_only, bool reuse_prep, hipStream_t s) {
     if (!reuse_prep && launch_prep_bwd(p, ws, k, q, g, beta, s) != hipSuccess) return hipGetLastError();
+    // bf16 inputs, scalar gate: dh' as fp16 in the first half of the dH
+    // region and U in the second, A in the dvn region (the grad kernel forms
+    // dvn itself)
+    const bool h16 = p.dtype == 1 && !p.per_key;
+    const int64_t nchh = (int64_t)p.um.n_chunks * p.H;
+    f16* dHw = reinterpret_cast<f16*>(dH);
+    f16* Uw = dHw + nchh * DK * DV;
+    f16* Aw = reinterpret_cast<f16*>(dVN);
     BwdArgs a;
     a.um = p.um; a.H = p.H; a.use_exp2 = p.use_exp2; a.scale = p.scale;
     a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g; a.dout = dout; a.h = h; a.dht = dht;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
     a.ws = ws; a.dH = dH; a.dVN = dVN;
     a.n_pairs = p.um.n_units * p.H;
+    if (h16 && !reuse_prep && p.um.n_chunks > 0)
+        hipLaunchKernelGGL(bwd_transfer_kernel_h, dim3(p.um.n_chunks, p.H), dim3(256), 0, s, a, Aw, Uw);
     if (a.n_pairs > 0) {
         // 32-column tiles while they fill the compute units, else 16-column
         // tiles (twice the workgroups, half the products per step)
@@ -1486,15 +1570,15 @@ hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* d
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return hipGetLastError();
         const bool narrow = 4 * (int64_t)a.n_pairs < cus;
-        const dim3 grid((narrow ? 8 : 4) * a.n_pairs);
+        const dim3 grid((narrow ? 8 : 4) * 8 * ((a.n_pairs + 7) / 8));
 #define GDN_DH(IN, PKV)                                                                            \
     if (narrow) hipLaunchKernelGGL((bwd_dh_kernel<IN, PKV, 1>), grid, dim3(256), 0, s, a);          \
     else hipLaunchKernelGGL((bwd_dh_kernel<IN, PKV, 2>), grid, dim3(256), 0, s, a);
         if (p.per_key) {
             if (p.dtype == 1) { GDN_DH(bf16, true) } else { GDN_DH(float, true) }
-        } else if (p.dtype == 1) {
-            if (narrow) hipLaunchKernelGGL(bwd_dh_kernel_h<1>, grid, dim3(256), 0, s, a);
-            else hipLaunchKernelGGL(bwd_dh_kernel_h<2>, grid, dim3(256), 0, s, a);
+        } else if (h16) {
+            if (narrow) hipLaunchKernelGGL(bwd_dh_kernel_h<1>, grid, dim3(256), 0, s, a, Aw, Uw, dHw);
+            else hipLaunchKernelGGL(bwd_dh_kernel_h<2>, grid, dim3(256), 0, s, a, Aw, Uw, dHw);
         } else {
             GDN_DH(float, false)
         }
@@ -1506,7 +1590,7 @@ hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* d
             if (p.dtype == 1) hipLaunchKernelGGL((bwd_grad_kernel<bf16, true>), grid, dim3(256), 0, s, a);
             else hipLaunchKernelGGL((bwd_grad_kernel<float, true>), grid, dim3(256), 0, s, a);
         } else {
-            if (p.dtype == 1) hipLaunchKernelGGL(bwd_grad_kernel_h, grid, dim3(256), 0, s, a);
+            if (p.dtype == 1) hipLaunchKernelGGL(bwd_grad_kernel_h, grid, dim3(256), 0, s, a, dHw);
             else hipLaunchKernelGGL((bwd_grad_kernel<float, false>), grid, dim3(256), 0, s, a);
         }
     }
