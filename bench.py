@@ -39,11 +39,13 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3
 FLOP_PER_TOKEN_HEAD = 139264   # 2 [3KV + (BT/2)(3K + 2V)], K = V = 128, BT = 64
-# The backward's products per token-head: seven full ones of K x V per token
-# (Kg dh', Qd^T dO, Kd^T Z, the recomputed Kd h, dO h^T, v_new dh'^T, Z h^T)
-# and eleven triangular ones of (BT/2) x 128 per token (P^T dO, Tb^T dvn, the
-# recomputed Tb Y, dP, dTb, K K^T and the four dq / dk products with the
-# decayed dL and dP, and the dL solve through T counted as one)
+# The backward's products per token-head, as the method states them: seven
+# full ones of K x V per token (Kg dh', Qd^T dO, Kd^T Z, the recomputed Kd h,
+# dO h^T, v_new dh'^T, Z h^T) and eleven triangular ones of (BT/2) x 128 per
+# token (P^T dO, Tb^T dvn, the recomputed Tb Y, dP, dTb, K K^T and the four
+# dq / dk products with the decayed dL and dP, and the dL solve through T
+# counted as one). The work unit of the backward line, whatever regrouping the
+# kernels use.
 BWD_FLOP_PER_TOKEN_HEAD = 2 * (7 * 128 * 128 + 11 * 32 * 128)
 KERNEL_SRC = os.path.join(ROOT, "chunked_gated_delta_05_amd", "csrc", "gdn_kernels.hip")
 
@@ -177,7 +179,7 @@ def bwd_io_bytes(w, token_heads: int, chunk_heads: int, n_states: int, with_dht:
 
 def bench_backward(args, wl, d, gb, W, torch):
     """Times the backward of the workload's forward as a training step runs
-    it: gdn_chunk_bwd over the rows or documents (the fp32 preparation, the
+    it: gdn_chunk_bwd over the rows or documents (the preparation, the
     reverse state pass, the per-chunk gradients), or for a sequence split the
     split backward (gradient summaries, adjoint merge, every segment's
     backward). The forward that supplies h (and, split, the maps M) runs once,
@@ -226,18 +228,25 @@ def bench_backward(args, wl, d, gb, W, torch):
     flops = BWD_FLOP_PER_TOKEN_HEAD * token_heads
     io = bwd_io_bytes(wl, token_heads, chunk_heads, n_states, dht is not None)
     tf = flops / (ms * 1e-3) / 1e12
+    # bf16 inputs with a scalar gate: fp16 operands (the fp16 MFMA peak, that
+    # of bf16); fp32 inputs and the per-key gate: fp32 operands
+    h16 = wl.dtype == "bf16" and not wl.gate_per_key
+    peak = PEAK_BF16_TFLOPS if h16 else PEAK_FP32_TFLOPS
     out = {"metric": "backward tokens/s", "value": tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
            "steps": steps, "warmup": max(args.warmup, 1), "ms_per_step": ms, "higher_is_better": True,
-           "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "scaling": "weak", "vs_baseline": None, "dtype": "f16" if h16 else "f32",
            "data": "synthetic", "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": H,
                                            "gate": "per_key" if wl.gate_per_key else "scalar",
                                            "input_dtype": wl.dtype, "path": path},
-           "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
-                        "frac": tf / PEAK_FP32_TFLOPS, "traffic": None,
-                        "note": "whole backward; every product runs on fp32 operands (fp32 MFMA peak)"},
+           "roofline": {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
+                        "frac": tf / peak, "traffic": None,
+                        "note": "whole backward on the method's flop count; " +
+                                ("fp16 operands, fp32 accumulation (fp16 MFMA peak)" if h16 else
+                                 "fp32 operands (fp32 MFMA peak)")},
            "hbm_frac_io": io / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9), "io_bytes": io,
            "flop_per_token_head": BWD_FLOP_PER_TOKEN_HEAD, "cpu_baseline": None}
-    print(f"[bench] {wl.name} backward: {ms:.3f} ms/step, {tf:.1f} TFLOP/s fp32", file=sys.stderr, flush=True)
+    print(f"[bench] {wl.name} backward: {ms:.3f} ms/step, {tf:.1f} TFLOP/s ({'fp16' if h16 else 'fp32'} operands)",
+          file=sys.stderr, flush=True)
     if not args.no_cpu:
         out["cpu_baseline"], out["parity_sample_err_over_rms"] = bwd_cpu_baseline(d, wl, offsets, do, dht, res)
     print(json.dumps(out), flush=True)
