@@ -965,6 +965,35 @@ __device__ __forceinline__ void st4h(f16* p, f32x4 x) {
     for (int e = 0; e < 4; ++e) h[e] = (f16)x[e];
     *reinterpret_cast<f16x4*>(p) = h;
 }
+// Cross-lane sums without LDS traffic. row_sum16: 16 per-lane values summed
+// over the 16 lanes of each row by recursive halving (partners 8, 4, 2, 1
+// apart: row_ror:8, swizzle xor 4, quad_perm), so that lane n ends with the
+// row's total of value n. pair16 / pair32: a value summed with that of the
+// lane 16 / 32 apart (v_permlane16_swap / v_permlane32_swap of the value
+// with itself); both together give the sum over the four rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_h(float x) {
+    return u2f(__builtin_amdgcn_update_dpp(0u, f2u(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_sum16(float (&v)[16], int n) {
+    const bool up8 = n & 8, up4 = n & 4, up2 = n & 2, up1 = n & 1;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) v[m] = (up8 ? v[8 + m] : v[m]) + dpp_h<0x128>(up8 ? v[m] : v[8 + m]);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        v[m] = (up4 ? v[4 + m] : v[m]) + u2f(__builtin_amdgcn_ds_swizzle((int)f2u(up4 ? v[m] : v[4 + m]), 0x101f));
+#pragma unroll
+    for (int m = 0; m < 2; ++m) v[m] = (up2 ? v[2 + m] : v[m]) + dpp_h<0x4e>(up2 ? v[m] : v[2 + m]);
+    return (up1 ? v[1] : v[0]) + dpp_h<0xb1>(up1 ? v[0] : v[1]);
+}
+__device__ __forceinline__ float pair16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+    return u2f(r[0]) + u2f(r[1]);
+}
+__device__ __forceinline__ float pair32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+    return u2f(r[0]) + u2f(r[1]);
+}
 __device__ __forceinline__ f32x4 ld4h(const f16* p) {
     const f16x4 h = *reinterpret_cast<const f16x4*>(p);
     return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
@@ -1364,7 +1393,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a, const f16* d
     // ---- finish. X1 = dTb, X2 = dP (lower incl. diagonal) of the wave's rows;
     // dbeta's column term: sums over i of dTb o T
     {
-        float cs[4][4];
+        float cs[16];                                // value 4 jb + r: column j = 16 jb + 4G + r
         for (int jb = 0; jb < 4; ++jb) {
             const f32x4 t4 = ld4h(Th + im * HT + 16 * jb + 4 * G);
             f32x4 x1, x2;
@@ -1373,16 +1402,13 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a, const f16* d
                 const bool keep = jb <= w && j <= im;
                 x1[r] = keep ? aT[jb][r] : 0.0f;
                 x2[r] = keep ? a.scale * aP[jb][r] : 0.0f;
-                cs[jb][r] = x1[r] * t4[r];
+                cs[4 * jb + r] = x1[r] * t4[r];
             }
             aP[jb] = x2;
             st4h(X1h + im * HT + 16 * jb + 4 * G, x1);
-            for (int r = 0; r < 4; ++r)
-                for (int sft = 1; sft < 16; sft <<= 1) cs[jb][r] += __shfl_xor(cs[jb][r], sft, 16);
         }
-        if (n == 0)
-            for (int jb = 0; jb < 4; ++jb)
-                for (int r = 0; r < 4; ++r) colB[w][16 * jb + 4 * G + r] = cs[jb][r];
+        // lane n: the column sum over this wave's rows of value n
+        colB[w][16 * (n >> 2) + 4 * G + (n & 3)] = row_sum16(cs, n);
     }
     lds_barrier();
     // M1 = dT T^T = dTb Tb^T, rows of this wave
@@ -1420,7 +1446,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a, const f16* d
     float rg = 0.0f;
     {
         const float gi = gm[im], bi = bt[im];
-        float rb = 0.0f, cg[4][4];
+        float rb = 0.0f, cg[16];
         for (int jb = 0; jb < 4; ++jb) {
             const f32x4 p4 = ld4h(Ph + im * HT + 16 * jb + 4 * G);
             f32x4 x1, x2;
@@ -1434,26 +1460,20 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a, const f16* d
                 rb += lij * gij;
                 const float t = lnb * (dgg * gij + dpij * p4[r]);
                 rg += t;
-                cg[jb][r] = -t;
+                cg[4 * jb + r] = -t;
                 x1[r] = dgg * d;
                 x2[r] = dpij * d;
             }
             st4h(X1h + im * HT + 16 * jb + 4 * G, x1);
             st4h(X2h + im * HT + 16 * jb + 4 * G, x2);
-            for (int r = 0; r < 4; ++r)
-                for (int sft = 1; sft < 16; sft <<= 1) cg[jb][r] += __shfl_xor(cg[jb][r], sft, 16);
         }
         // row sums over the four lane groups
-        rb += __shfl_xor(rb, 16, 64);
-        rb += __shfl_xor(rb, 32, 64);
-        rg += __shfl_xor(rg, 16, 64);
-        rg += __shfl_xor(rg, 32, 64);
+        rb = pair32(pair16(rb));
+        rg = pair32(pair16(rg));
         if (G == 0) rowB[im] = rb;
         // column sums over this wave's rows: one partial per wave, added in a
         // fixed order below (the same result on every run)
-        if (n == 0)
-            for (int jb = 0; jb < 4; ++jb)
-                for (int r = 0; r < 4; ++r) colP[w][16 * jb + 4 * G + r] = cg[jb][r];
+        colP[w][16 * (n >> 2) + 4 * G + (n & 3)] = row_sum16(cg, n);
     }
     lds_barrier();
     // dq, dk, rows of this wave: the products with dG o D and dP o D, then
@@ -1503,10 +1523,8 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a, const f16* d
                 *reinterpret_cast<f32x4*>(a.dk + o) = dkv;
             }
         }
-        rq += __shfl_xor(rq, 16, 64);
-        rq += __shfl_xor(rq, 32, 64);
-        rk += __shfl_xor(rk, 16, 64);
-        rk += __shfl_xor(rk, 32, 64);
+        rq = pair32(pair16(rq));
+        rk = pair32(pair16(rk));
         if (G == 0) {
             rowG[im] = rg + rq;
             rowK[im] = rk;
