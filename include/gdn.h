@@ -338,10 +338,13 @@ gdn_status gdn_state_merge(int32_t B, int32_t H, int32_t n_seg, int32_t K, int32
  *                     other bits give GDN_ERR_INVALID
  *   workspace         as for gdn_chunk_fwd (query its size with NULL); about
  *                     129 KiB per (chunk, head), 225 KiB with a per-key gate
- * Gradients are fp32 whatever the input dtype; every product runs on fp32
- * operands. The per-key decay is taken in factors that are at most 1 for
- * every g <= 0 (as in the forward), so strong gates down to total forgetting
- * give finite gradients.
+ * Gradients are fp32 whatever the input dtype. With bf16 inputs and a scalar
+ * gate the products run on fp16 operands with fp32 accumulation (the
+ * forward's numeric range applies to the states and their gradients), and
+ * the chunk preparation includes each chunk's transfer maps of the state
+ * gradient; fp32 inputs and the per-key gate use fp32 operands. The per-key
+ * decay is taken in factors that are at most 1 for every g <= 0 (as in the
+ * forward), so strong gates down to total forgetting give finite gradients.
  */
 gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, const void* v, const float* g,
                          const void* beta, const float* h, const void* dout, const float* dht, float* dq,
