@@ -527,12 +527,21 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
         for (int kt = 0; kt < 2; ++kt) {
             const int c = 16 * kt + n;           // slice column of this lane's key
             f32x4 ra = {0.f, 0.f, 0.f, 0.f}, rp = ra, ca = ra, cp = ra;
-            // rows of block w against the earlier blocks: reference row
-            // 16w - 1, the last one before the block
-            if (w > 0) {
-                const int ref = 16 * w - 1;
-                const float gr = Gsl[ref * SL + c];
-                for (int k0 = 0; k0 < 16 * w; k0 += 4) {
+            // The diagonal block joins the factored products below when the
+            // gate falls by at most PK_DIAG_RANGE (2^8 of decay) inside the
+            // block on every key of the tile: its factors about the reference
+            // rows then stay within 2^8 (the forward preparation's rule).
+            // The stored zeros of dL (strictly lower) and dP (lower with the
+            // diagonal) mask the terms past the diagonal.
+            const float g_lo = w > 0 ? Gsl[(16 * w - 1) * SL + c] : 0.0f;
+            const bool fdiag = __all(g_lo - Gsl[(16 * w + 15) * SL + c] <= (ue ? 8.0f : 5.545177444479562f));
+            // rows of block w against the earlier blocks (and the diagonal
+            // block when factored): reference row 16w - 1, the last one
+            // before the block (the chunk start, G = 0, for block 0)
+            const int rend = 16 * w + (fdiag ? 16 : 0);
+            if (rend > 0) {
+                const float gr = g_lo;
+                for (int k0 = 0; k0 < rend; k0 += 4) {
                     const int j = k0 + G;
                     const float b = Ksl[j * SL + c] * fpow(gr - Gsl[j * SL + c], ue);
                     ra = __builtin_amdgcn_mfma_f32_16x16x4f32(X1[(row0 + n) * BTL + j], b, ra, 0, 0, 0);
@@ -544,12 +553,13 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
                     rp[r] *= f;
                 }
             }
-            // columns of block w against the later blocks: reference row
-            // 16w + 15, the block's last
-            if (w < 3) {
+            // columns of block w against the later blocks (and the diagonal
+            // block when factored): reference row 16w + 15, the block's last
+            const int cbeg = 16 * w + (fdiag ? 0 : 16);
+            if (cbeg < BT) {
                 const int ref = 16 * w + 15;
                 const float gr = Gsl[ref * SL + c];
-                for (int k0 = 16 * (w + 1); k0 < BT; k0 += 4) {
+                for (int k0 = cbeg; k0 < BT; k0 += 4) {
                     const int i = k0 + G;
                     const float f = fpow(Gsl[i * SL + c] - gr, ue);
                     ca = __builtin_amdgcn_mfma_f32_16x16x4f32(bt[i] * X1[i * BTL + row0 + n], Ksl[i * SL + c] * f, ca,
@@ -562,10 +572,11 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
                     cp[r] *= f;
                 }
             }
-            // the diagonal block by exponent differences: m <= i feeds the
-            // row products of row i, m >= i the column products of column i;
-            // row m's g, k, q and beta are read once for the lane's four rows
-            {
+            // otherwise the diagonal block by exponent differences: m <= i
+            // feeds the row products of row i, m >= i the column products of
+            // column i; row m's g, k, q and beta are read once for the lane's
+            // four rows
+            if (!fdiag) {
                 float gi[4];
                 for (int r = 0; r < 4; ++r) gi[r] = Gsl[(row0 + 4 * G + r) * SL + c];
 #pragma unroll 4
