@@ -354,7 +354,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     // ---- L = strictly lower (beta_i k_i.k_j b^{G_i-G_j}) on MFMA, 10 tiles over 4 waves.
     // Per key, an off-diagonal tile (I > J) factors the decay about the last
     // row of block J, so that both factors are at most 1 for any g <= 0; a
-    // diagonal tile takes the exponent differences directly.
+    // diagonal tile does the same when its block's gate range allows (below),
+    // and takes the exponent differences directly otherwise.
     // four rows i0 .. i0+3 against row j: sum_d x_id k_jd b^{G_id - G_jd},
     // 16-byte reads of four keys at a time, row j's k and G shared by the rows
     auto direct4 = [&](const Op* xi, int i0, int j, float* out) {
@@ -393,11 +394,21 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         }
         for (int r = 0; r < 4; ++r) out[r] = s[r];
     };
+    // A diagonal tile takes the factored form as well when the gate falls by
+    // at most 2^8 of decay inside its block on every key: the factor of its
+    // rows about the block's last row then stays within 2^8 (the bf16
+    // preparation's rule). Wave-uniform.
+    auto diag_factored = [&](int blk) {
+        float rmax = 0.0f;
+        for (int d = lane; d < DK; d += 64)
+            rmax = fmaxf(rmax, Gs[(16 * blk) * (DK + 4) + d] - Gs[(16 * blk + 15) * (DK + 4) + d]);
+        return __all(rmax <= (a.use_exp2 ? 8.0f : 5.545177444479562f)) != 0;
+    };
     for (int t = w; t < 10; t += 4) {
         const int it = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
         const int jt = t - (it * (it + 1)) / 2;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (PERKEY && it == jt) {
+        if (PERKEY && it == jt && !diag_factored(it)) {
             // lanes whose column is past all four rows skip the sums
             float dv[4] = {0.f, 0.f, 0.f, 0.f};
             const int i0 = 16 * it + 4 * G, j = 16 * jt + n;
@@ -500,7 +511,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         for (int t = w; t < 16; t += 4) {
             const int jt = t >> 2, it = t & 3;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (PERKEY && jt == it) {
+            if (PERKEY && jt == it && !diag_factored(jt)) {
                 float dv[4] = {0.f, 0.f, 0.f, 0.f};
                 const int i = 16 * it + n, j0 = 16 * jt + 4 * G;
                 if (j0 <= i) direct4j(qt, i, j0, dv);
