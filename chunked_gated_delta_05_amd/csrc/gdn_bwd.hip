@@ -171,6 +171,18 @@ struct TileRegs {
             }
         }
     }
+    // the same, transposed: element (r, c) to dst[c * ld + r]
+    __device__ __forceinline__ void commit_tr(float* dst, int ld, int tid) const {
+#pragma unroll
+        for (int i = 0; i < PT; ++i) {
+            const int e = tid + 256 * i, r = e / PER_ROW, c = (e - r * PER_ROW) * VPR;
+            if (e < NV) {
+                float x[VPR];
+                Vec16<In>::cvt(w[i], x);
+                for (int j = 0; j < VPR; ++j) dst[(c + j) * ld + r] = x[j];
+            }
+        }
+    }
     // the same, as fp16 values (8 bytes per fp32 vector, 16 per bf16 or fp16
     // one), and with column c + j of a vector scaled by colscale[j] into dst2
     // when given
@@ -933,6 +945,300 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ reverse state pass, per-key gate
+// The per-key reverse chunk step as an affine map of the state gradient, in
+// fp32 (D = dL/dh at the chunk's exit, D' at its entry):
+//   D' = A D + scale U^T dO,  A = diag(b^{G_L}) - W^T Kg,  U = Qd - P W,  W = Tb Kd
+// with Kd, Kg, Qd the prepared gated tiles (k b^G, k b^{G_L - G}, q b^G):
+// the per-key gamma, Qd^T dO and Kd^T Tb^T (Kg D + scale P^T dO) of the
+// three-phase step regrouped. bwd_transfer_kernel_pk forms A and U of every
+// chunk at once, bwd_dh_kernel_pkr runs the sequential pass with one load
+// phase per chunk (the next chunk's A, U and dO prefetched into registers),
+// and bwd_dvn_kernel_pk forms dvn = Kg D + scale P^T dO of every chunk for
+// the per-chunk gradients.
+
+// One workgroup of four waves per (chunk, head), two per compute unit: wave w
+// forms rows 16w .. +15 of W, rows 32w .. +31 of A and rows 16w .. +15 of U.
+// Kd, then Kg, and W sit transposed in LDS ([key][row]), so that every
+// product reads both operands along its contraction with 16-byte loads; the
+// wave's own rows of T and P (lower triangular: only the first w + 1 16-wide
+// column blocks are nonzero) go straight from memory into MFMA operand
+// registers. The next tile's loads are in flight while the current product
+// runs. A comes out of a transposed product, so a lane holds four consecutive
+// columns of one row (16-byte stores). U^T ([key][row]) overwrites the
+// chunk-head's Qd tile, which nothing reads after this kernel.
+constexpr int KTL = BT + 4;     // row stride (floats) of the transposed 128 x 64 tiles
+
+// a 64 x 128 fp32 tile in registers, 16 x 16 blocks per wave and load, for a
+// transposed store into LDS in which the 64 lanes of a store hit 64 banks
+struct TileT {
+    f32x4 v[8];
+    __device__ __forceinline__ void issue(const float* src, int w, int l) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int bi = 4 * i + w, r = 16 * (bi & 3) + (l & 15), c = 16 * (bi >> 2) + 4 * (l >> 4);
+            v[i] = *reinterpret_cast<const f32x4*>(src + r * DK + c);
+        }
+    }
+    __device__ __forceinline__ void commit(float* dst, int w, int l) const {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int bi = 4 * i + w, r = 16 * (bi & 3) + (l & 15), c = 16 * (bi >> 2) + 4 * (l >> 4);
+            for (int j = 0; j < 4; ++j) dst[(c + j) * KTL + r] = v[i][j];
+        }
+    }
+};
+
+template <class In>
+__global__ __launch_bounds__(256, 2) void bwd_transfer_kernel_pk(BwdArgs a, float* Aw) {
+    __shared__ __attribute__((aligned(16))) float Xt[DK * KTL];   // Kd^T, then Kg^T
+    __shared__ __attribute__((aligned(16))) float Wt[DK * KTL];   // W^T
+    __shared__ float bt[BT], gl[DK];
+
+    const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ci = blockIdx.x, head = blockIdx.y, H = a.H;
+    int u, cc;
+    chunk_of(a.um, ci, u, cc);
+    if (u < 0) return;
+    const UnitInfo ui = unit_info(a.um, u);
+    const int64_t t0 = ui.start + (int64_t)cc * BT;
+    int len = ui.len - cc * BT;
+    len = len < 0 ? 0 : (len > BT ? BT : len);
+    const int64_t ch = (int64_t)ci * H + head;
+    const int row0 = 16 * w;
+    float* qg = reinterpret_cast<float*>(a.ws.qg) + ch * (BT * DK);
+    const float* Tm = reinterpret_cast<const float*>(a.ws.Tm) + ch * (BT * BT) + (row0 + n) * BT + 4 * G;
+    const float* Pm = reinterpret_cast<const float*>(a.ws.P) + ch * (BT * BT) + (row0 + n) * BT + 4 * G;
+
+    TileT tx;                                    // Kd, then Kg
+    tx.issue(reinterpret_cast<const float*>(a.ws.kd) + ch * (BT * DK), w, lane);
+    f32x4 tf[4], pf[4];                          // T, P: row row0 + n, columns 16 kk + 4G .. +3
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        tf[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (kk <= w) tf[kk] = *reinterpret_cast<const f32x4*>(Tm + 16 * kk);
+    }
+    if (tid < BT) bt[tid] = tid < len ? ldf(reinterpret_cast<const In*>(a.beta), (t0 + tid) * H + head) : 0.0f;
+    if (tid < DK) gl[tid] = fpow(a.ws.gamL[ch * DK + tid], a.use_exp2);
+    tx.commit(Xt, w, lane);                      // Kd^T
+    lds_barrier();
+    tx.issue(reinterpret_cast<const float*>(a.ws.kg) + ch * (BT * DK), w, lane);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        pf[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (kk <= w) pf[kk] = *reinterpret_cast<const f32x4*>(Pm + 16 * kk);
+        for (int e = 0; e < 4; ++e) tf[kk][e] *= bt[16 * kk + 4 * G + e];   // T diag(beta)
+    }
+    // W = Tb Kd, rows of this wave, stored as W^T
+    for (int ct = 0; ct < DK / 16; ++ct) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            if (kk > w) continue;
+            const f32x4 y = *reinterpret_cast<const f32x4*>(Xt + (16 * ct + n) * KTL + 16 * kk + 4 * G);
+            for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(tf[kk][e], y[e], acc, 0, 0, 0);
+        }
+        *reinterpret_cast<f32x4*>(&Wt[(16 * ct + n) * KTL + row0 + 4 * G]) = acc;
+    }
+    lds_barrier();
+    tx.commit(Xt, w, lane);                      // Kg^T
+    f32x4 qd[DK / 16];                           // Qd[row0 + 4G + r][16 ct + n]
+#pragma unroll
+    for (int ct = 0; ct < DK / 16; ++ct)
+        for (int r = 0; r < 4; ++r) qd[ct][r] = qg[(row0 + 4 * G + r) * DK + 16 * ct + n];
+    lds_barrier();
+    // A = diag(b^{G_L}) - W^T Kg, rows 32w .. 32w+31: lane holds A[k1 + n][16 ct + 4G .. +3]
+    float* Ac = Aw + ch * (DK * DK);
+    for (int rt = 0; rt < 2; ++rt) {
+        const int k1 = 32 * w + 16 * rt;
+        for (int ct = 0; ct < DK / 16; ++ct) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            mm_rowsk<BT>(acc, Xt + 16 * ct * KTL, KTL, Wt + k1 * KTL, KTL, G, n);
+            f32x4 o;
+            for (int r = 0; r < 4; ++r) o[r] = (k1 + n == 16 * ct + 4 * G + r ? gl[k1 + n] : 0.0f) - acc[r];
+            *reinterpret_cast<f32x4*>(Ac + (k1 + n) * DK + 16 * ct + 4 * G) = o;
+        }
+    }
+    // U = Qd - P W, rows of this wave: lane holds U[row0 + 4G + r][16 ct + n]
+    f32x4 uo[DK / 16];
+    for (int ct = 0; ct < DK / 16; ++ct) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            if (kk > w) continue;
+            const f32x4 y = *reinterpret_cast<const f32x4*>(Wt + (16 * ct + n) * KTL + 16 * kk + 4 * G);
+            for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pf[kk][e], y[e], acc, 0, 0, 0);
+        }
+        uo[ct] = qd[ct] - acc;
+    }
+    // U^T ([key][row]) over the tile: every wave has read its Qd rows
+    __syncthreads();
+    for (int ct = 0; ct < DK / 16; ++ct)
+        *reinterpret_cast<f32x4*>(qg + (16 * ct + n) * BT + row0 + 4 * G) = uo[ct];
+}
+
+// The sequential pass: one workgroup of four waves per (unit, head, 16 NCT
+// value columns), one per compute unit (about 400 registers a lane); wave w
+// keeps D for keys 32w .. 32w+31 in fp32 registers and a copy in LDS as
+// [column][key]. Its rows of A and of U^T come straight
+// from memory into MFMA operand registers, one chunk ahead (two register
+// sets, taken in turn); dO goes through LDS as [column][row]. D and dO are
+// double-buffered in LDS, so one barrier per chunk hands both over. dh' of
+// every chunk goes to the workspace.
+constexpr int DTL = BT + 4;     // row stride (floats) of the transposed dO tile
+
+template <class In, int NCT>
+__global__ __launch_bounds__(256, 1) void bwd_dh_kernel_pkr(BwdArgs a, const float* Aw) {
+    constexpr int NC = 16 * NCT;
+    __shared__ __attribute__((aligned(16))) float dhT[2][NC * BKL];  // D [column][key]
+    __shared__ __attribute__((aligned(16))) float dOT[2][NC * DTL];  // dO [column][row]
+
+    const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = a.H;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int tile = slot % (DV / NC), pair = (slot / (DV / NC)) * 8 + xcd;
+    if (pair >= a.n_pairs) return;
+    const int u = pair / H, head = pair - u * H;
+    const UnitInfo ui = uniform(unit_info(a.um, u));
+    const int c0 = tile * NC;
+    const int64_t uh = (int64_t)u * H + head;
+    const float* Uw = reinterpret_cast<const float*>(a.ws.qg);
+
+    f32x4 dh[2][NCT];
+    const int b_last = (ui.nch - 1) & 1;
+    for (int kt = 0; kt < 2; ++kt)
+        for (int ct = 0; ct < NCT; ++ct) {
+            for (int r = 0; r < 4; ++r) {
+                const int key = 32 * w + 16 * kt + 4 * G + r, col = 16 * ct + n;
+                dh[kt][ct][r] = a.dht ? a.dht[(uh * DK + key) * DV + c0 + col] : 0.0f;
+            }
+            *reinterpret_cast<f32x4*>(&dhT[b_last][(16 * ct + n) * BKL + 32 * w + 16 * kt + 4 * G]) = dh[kt][ct];
+        }
+
+    // operand registers: A[32w + 16kt + n][16kb + 4G .. +3], U^T[32w + 16kt + n][16rb + 4G .. +3]
+    f32x4 A0[2][8], U0[2][4], A1[2][8], U1[2][4];
+    TileRegs<In, BT, NC> pd;
+    auto issue = [&](int cc, f32x4 (&Ar)[2][8], f32x4 (&Ur)[2][4]) {
+        int l = ui.len - cc * BT;
+        l = l > BT ? BT : l;
+        const int64_t tt = ui.start + (int64_t)cc * BT, chh = (int64_t)(ui.cbase + cc) * H + head;
+        const float* ap = Aw + chh * (DK * DK) + (32 * w + n) * DK + 4 * G;
+        const float* up = Uw + chh * (DK * BT) + (32 * w + n) * BT + 4 * G;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb) Ar[kt][kb] = *reinterpret_cast<const f32x4*>(ap + 16 * kt * DK + 16 * kb);
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) Ur[kt][rb] = *reinterpret_cast<const f32x4*>(up + 16 * kt * BT + 16 * rb);
+        }
+        pd.issue(reinterpret_cast<const In*>(a.dout) + (tt * H + head) * DV + c0, (int64_t)H * DV, l, tid);
+    };
+    auto step = [&](int c, const f32x4 (&Ar)[2][8], const f32x4 (&Ur)[2][4], f32x4 (&An)[2][8], f32x4 (&Un)[2][4]) {
+        const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
+        const int b = c & 1;
+        pd.commit_tr(dOT[b], DTL, tid);
+        if (c > 0) issue(c - 1, An, Un);
+        for (int kt = 0; kt < 2; ++kt)
+            for (int ct = 0; ct < NCT; ++ct)
+                for (int r = 0; r < 4; ++r) {
+                    const int key = 32 * w + 16 * kt + 4 * G + r;
+                    a.dH[(ch * DK + key) * DV + c0 + 16 * ct + n] = dh[kt][ct][r];
+                }
+        lds_barrier();                           // D and dO of this chunk are in LDS
+        // D' = A D + scale U^T dO, keys 32w .. +31
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            f32x4 ad[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, ae[2] = {ad[0], ad[0]};
+            const float* dcol = dhT[b] + (16 * ct + n) * BKL + 4 * G;
+            const float* ocol = dOT[b] + (16 * ct + n) * DTL + 4 * G;
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb) {
+                const f32x4 y = *reinterpret_cast<const f32x4*>(dcol + 16 * kb);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt)
+                        ad[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(Ar[kt][kb][e], y[e], ad[kt], 0, 0, 0);
+            }
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const f32x4 y = *reinterpret_cast<const f32x4*>(ocol + 16 * rb);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt)
+                        ae[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(Ur[kt][rb][e], y[e], ae[kt], 0, 0, 0);
+            }
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                for (int r = 0; r < 4; ++r) dh[kt][ct][r] = ad[kt][r] + a.scale * ae[kt][r];
+                *reinterpret_cast<f32x4*>(&dhT[b ^ 1][(16 * ct + n) * BKL + 32 * w + 16 * kt + 4 * G]) = dh[kt][ct];
+            }
+        }
+    };
+    if (ui.nch > 0) issue(ui.nch - 1, A0, U0);
+    for (int c = ui.nch - 1; c >= 0; c -= 2) {
+        step(c, A0, U0, A1, U1);
+        if (c >= 1) step(c - 1, A1, U1, A0, U0);
+    }
+    if (a.dh0)
+        for (int kt = 0; kt < 2; ++kt)
+            for (int ct = 0; ct < NCT; ++ct)
+                for (int r = 0; r < 4; ++r) {
+                    const int key = 32 * w + 16 * kt + 4 * G + r;
+                    a.dh0[(uh * DK + key) * DV + c0 + 16 * ct + n] = dh[kt][ct][r];
+                }
+}
+
+// dvn = Kg dh' + scale P^T dO of every chunk (fp32): one workgroup of four
+// waves per (chunk, head), the value columns in 32-column tiles; wave w
+// takes token rows 16w .. +15.
+template <class In>
+__global__ __launch_bounds__(256) void bwd_dvn_kernel_pk(BwdArgs a) {
+    constexpr int VC = 32, VCL = VC + 1;
+    __shared__ __attribute__((aligned(16))) float Kgs[BT * BKL];
+    __shared__ __attribute__((aligned(16))) float Ps[BT * BTL];
+    __shared__ __attribute__((aligned(16))) float Ds[DK * VCL];      // dh' [key][col]
+    __shared__ __attribute__((aligned(16))) float dOs[BT * VCL];
+
+    const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ci = blockIdx.x, head = blockIdx.y, H = a.H;
+    int u, cc;
+    chunk_of(a.um, ci, u, cc);
+    if (u < 0) return;
+    const UnitInfo ui = unit_info(a.um, u);
+    const int64_t t0 = ui.start + (int64_t)cc * BT;
+    int len = ui.len - cc * BT;
+    len = len < 0 ? 0 : (len > BT ? BT : len);
+    const int64_t ch = (int64_t)ci * H + head;
+    const int row0 = 16 * w;
+
+    load_tile<float, BT, DK>(reinterpret_cast<const float*>(a.ws.kg) + ch * (BT * DK), DK, BT, Kgs, BKL, tid);
+    load_tile<float, BT, BT>(reinterpret_cast<const float*>(a.ws.P) + ch * (BT * BT), BT, BT, Ps, BTL, tid);
+    for (int vt = 0; vt < DV / VC; ++vt) {
+        const int vc0 = vt * VC;
+        lds_barrier();
+        load_tile<float, DK, VC>(a.dH + ch * DK * DV + vc0, DV, DK, Ds, VCL, tid);
+        load_tile<In, BT, VC>(reinterpret_cast<const In*>(a.dout) + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, dOs,
+                              VCL, tid);
+        lds_barrier();
+        for (int ct = 0; ct < VC / 16; ++ct) {
+            f32x4 kd = {0.f, 0.f, 0.f, 0.f}, pd = kd;
+            mmf<DK>(kd, [&](int m, int k) { return Kgs[(row0 + m) * BKL + k]; },
+                    [&](int k, int nn) { return Ds[k * VCL + 16 * ct + nn]; }, G, n);
+            // P^T dO: P[j][i] = 0 for j < i
+            for (int k0 = row0; k0 < BT; k0 += 4)
+                pd = __builtin_amdgcn_mfma_f32_16x16x4f32(Ps[(k0 + G) * BTL + row0 + n], dOs[(k0 + G) * VCL + 16 * ct + n], pd,
+                                                         0, 0, 0);
+            for (int r = 0; r < 4; ++r)
+                a.dVN[(ch * BT + row0 + 4 * G + r) * DV + vc0 + 16 * ct + n] = kd[r] + a.scale * pd[r];
+        }
+    }
+}
+
 // ------------------------------------------------------------------ per-chunk gradients, bf16 inputs, scalar gate
 // The same gradients as bwd_grad_kernel, with every tile in LDS as fp16 (the
 // bf16 inputs exactly, the fp32 states, T, P and intermediates rounded once)
@@ -1583,14 +1889,20 @@ hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* d
     f16* dHw = reinterpret_cast<f16*>(dH);
     f16* Uw = dHw + nchh * DK * DV;
     f16* Aw = reinterpret_cast<f16*>(dVN);
+    // per key: A (fp32) in the region after dvn's, U over the Qd tiles
+    float* Ak = dVN + nchh * BT * DV;
     BwdArgs a;
     a.um = p.um; a.H = p.H; a.use_exp2 = p.use_exp2; a.scale = p.scale;
     a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g; a.dout = dout; a.h = h; a.dht = dht;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
     a.ws = ws; a.dH = dH; a.dVN = dVN;
     a.n_pairs = p.um.n_units * p.H;
-    if (h16 && !reuse_prep && p.um.n_chunks > 0)
-        hipLaunchKernelGGL(bwd_transfer_kernel_h, dim3(p.um.n_chunks, p.H), dim3(256), 0, s, a, Aw, Uw);
+    if (!reuse_prep && p.um.n_chunks > 0) {
+        const dim3 grid(p.um.n_chunks, p.H);
+        if (h16) hipLaunchKernelGGL(bwd_transfer_kernel_h, grid, dim3(256), 0, s, a, Aw, Uw);
+        else if (p.per_key && p.dtype == 1) hipLaunchKernelGGL(bwd_transfer_kernel_pk<bf16>, grid, dim3(256), 0, s, a, Ak);
+        else if (p.per_key) hipLaunchKernelGGL(bwd_transfer_kernel_pk<float>, grid, dim3(256), 0, s, a, Ak);
+    }
     if (a.n_pairs > 0) {
         // 32-column tiles while they fill the compute units, else 16-column
         // tiles (twice the workgroups, half the products per step)
@@ -1600,24 +1912,36 @@ hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* d
             return hipGetLastError();
         const bool narrow = 4 * (int64_t)a.n_pairs < cus;
         const dim3 grid((narrow ? 8 : 4) * 8 * ((a.n_pairs + 7) / 8));
-#define GDN_DH(IN, PKV)                                                                            \
-    if (narrow) hipLaunchKernelGGL((bwd_dh_kernel<IN, PKV, 1>), grid, dim3(256), 0, s, a);          \
-    else hipLaunchKernelGGL((bwd_dh_kernel<IN, PKV, 2>), grid, dim3(256), 0, s, a);
+        // per key (one workgroup per compute unit): the narrowest tiles whose
+        // workgroups all run at once, else 64-column tiles
+        const int pk_nct = 8 * (int64_t)a.n_pairs <= cus ? 1 : 4 * (int64_t)a.n_pairs <= cus ? 2 : 4;
+        const dim3 grid_pk((DV / (16 * pk_nct)) * 8 * ((a.n_pairs + 7) / 8));
+#define GDN_DHA(IN)                                                                                   \
+    if (pk_nct == 4) hipLaunchKernelGGL((bwd_dh_kernel_pkr<IN, 4>), grid_pk, dim3(256), 0, s, a, Ak); \
+    else if (pk_nct == 2) hipLaunchKernelGGL((bwd_dh_kernel_pkr<IN, 2>), grid_pk, dim3(256), 0, s, a, Ak); \
+    else hipLaunchKernelGGL((bwd_dh_kernel_pkr<IN, 1>), grid_pk, dim3(256), 0, s, a, Ak);
         if (p.per_key) {
-            if (p.dtype == 1) { GDN_DH(bf16, true) } else { GDN_DH(float, true) }
+            if (p.dtype == 1) { GDN_DHA(bf16) } else { GDN_DHA(float) }
         } else if (h16) {
             if (narrow) hipLaunchKernelGGL(bwd_dh_kernel_h<1>, grid, dim3(256), 0, s, a, Aw, Uw, dHw);
             else hipLaunchKernelGGL(bwd_dh_kernel_h<2>, grid, dim3(256), 0, s, a, Aw, Uw, dHw);
+        } else if (narrow) {
+            hipLaunchKernelGGL((bwd_dh_kernel<float, false, 1>), grid, dim3(256), 0, s, a);
         } else {
-            GDN_DH(float, false)
+            hipLaunchKernelGGL((bwd_dh_kernel<float, false, 2>), grid, dim3(256), 0, s, a);
         }
-#undef GDN_DH
+#undef GDN_DHA
     }
     if (p.um.n_chunks > 0 && !dh_only) {
         dim3 grid(p.um.n_chunks, p.H);
         if (p.per_key) {
-            if (p.dtype == 1) hipLaunchKernelGGL((bwd_grad_kernel<bf16, true>), grid, dim3(256), 0, s, a);
-            else hipLaunchKernelGGL((bwd_grad_kernel<float, true>), grid, dim3(256), 0, s, a);
+            if (p.dtype == 1) {
+                hipLaunchKernelGGL(bwd_dvn_kernel_pk<bf16>, grid, dim3(256), 0, s, a);
+                hipLaunchKernelGGL((bwd_grad_kernel<bf16, true>), grid, dim3(256), 0, s, a);
+            } else {
+                hipLaunchKernelGGL(bwd_dvn_kernel_pk<float>, grid, dim3(256), 0, s, a);
+                hipLaunchKernelGGL((bwd_grad_kernel<float, true>), grid, dim3(256), 0, s, a);
+            }
         } else {
             if (p.dtype == 1) hipLaunchKernelGGL(bwd_grad_kernel_h, grid, dim3(256), 0, s, a, dHw);
             else hipLaunchKernelGGL((bwd_grad_kernel<float, false>), grid, dim3(256), 0, s, a);
