@@ -705,10 +705,12 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
     const In* dout = reinterpret_cast<const In*>(a.dout);
 
     if (PK) {
-        // per key: k b^G (for Y) in Ks, T and beta; q, k and G come in key
-        // slices in the finish
+        // per key: k b^G (for Y) in Ks, T and beta, and for dvn k b^{G_L - G}
+        // in Qs and P in Ps; q, k and G come in key slices in the finish
         load_tile<float, BT, DK>(reinterpret_cast<const float*>(a.ws.kd) + ch * (BT * DK), DK, BT, Ks, BKL, tid);
         load_tile<float, BT, BT>(reinterpret_cast<const float*>(a.ws.Tm) + ch * (BT * BT), BT, BT, Ts, BTL, tid);
+        load_tile<float, BT, DK>(reinterpret_cast<const float*>(a.ws.kg) + ch * (BT * DK), DK, BT, Qs, BKL, tid);
+        load_tile<float, BT, BT>(reinterpret_cast<const float*>(a.ws.P) + ch * (BT * BT), BT, BT, Ps, BTL, tid);
         if (tid < BT) bt[tid] = tid < len ? ldf(reinterpret_cast<const In*>(a.beta), (t0 + tid) * H + head) : 0.0f;
         lds_barrier();
     } else {
@@ -739,7 +741,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
         pdh.issue(a.dH + ch * DK * DV + vc0, DV, DK, tid);
         pv.issue(vin + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, tid);
         pdo.issue(dout + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, tid);
-        pdv.issue(a.dVN + ch * BT * DV + vc0, DV, BT, tid);
+        if (!PK) pdv.issue(a.dVN + ch * BT * DV + vc0, DV, BT, tid);
     };
     prefetch(0);
     for (int vt = 0; vt < DV / VT; ++vt) {
@@ -749,7 +751,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
         pdh.commit(DHs, VTL, tid);
         pv.commit(Vs, VTL, tid);
         pdo.commit(DOs, VTL, tid);
-        pdv.commit(DVs, VTL, tid);
+        if (!PK) pdv.commit(DVs, VTL, tid);
         lds_barrier();
         if (vt + 1 < DV / VT) prefetch(vt + 1);
 #pragma unroll
@@ -768,6 +770,21 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
                 const int row = row0 + 4 * G + r;
                 Ys[row * VTL + n] = Vs[row * VTL + n] - (PK ? kh[r] : bG(row) * kh[r]);
             }
+        }
+        if (PK) {
+            // dvn = Kg dh' + scale P^T dO, rows of this wave (P[j][i] = 0 for j < i)
+            f32x4 kd = {0.f, 0.f, 0.f, 0.f}, pd = kd;
+#pragma unroll
+            for (int k0 = 0; k0 < DK; k0 += 16) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(Qs + (row0 + n) * BKL + k0 + 4 * G);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    kd = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e], DHs[(k0 + 4 * G + e) * VTL + n], kd, 0, 0, 0);
+            }
+            for (int k0 = row0; k0 < BT; k0 += 4)
+                pd = __builtin_amdgcn_mfma_f32_16x16x4f32(Ps[(k0 + G) * BTL + row0 + n], DOs[(k0 + G) * VTL + n], pd, 0, 0,
+                                                         0);
+            for (int r = 0; r < 4; ++r) DVs[(row0 + 4 * G + r) * VTL + n] = kd[r] + a.scale * pd[r];
         }
         lds_barrier();
         // v_new = Tb Y and Z = Tb^T dvn = dV, rows of this wave
@@ -952,10 +969,9 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
 // with Kd, Kg, Qd the prepared gated tiles (k b^G, k b^{G_L - G}, q b^G):
 // the per-key gamma, Qd^T dO and Kd^T Tb^T (Kg D + scale P^T dO) of the
 // three-phase step regrouped. bwd_transfer_kernel_pk forms A and U of every
-// chunk at once, bwd_dh_kernel_pkr runs the sequential pass with one load
-// phase per chunk (the next chunk's A, U and dO prefetched into registers),
-// and bwd_dvn_kernel_pk forms dvn = Kg D + scale P^T dO of every chunk for
-// the per-chunk gradients.
+// chunk at once, and bwd_dh_kernel_pkr runs the sequential pass with one load
+// phase per chunk (the next chunk's A, U and dO prefetched into registers);
+// the per-chunk gradient kernel forms dvn = Kg D + scale P^T dO itself.
 
 // One workgroup of four waves per (chunk, head), two per compute unit: wave w
 // forms rows 16w .. +15 of W, rows 32w .. +31 of A and rows 16w .. +15 of U.
@@ -1190,53 +1206,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dh_kernel_pkr(BwdArgs a, const flo
                     const int key = 32 * w + 16 * kt + 4 * G + r;
                     a.dh0[(uh * DK + key) * DV + c0 + 16 * ct + n] = dh[kt][ct][r];
                 }
-}
-
-// dvn = Kg dh' + scale P^T dO of every chunk (fp32): one workgroup of four
-// waves per (chunk, head), the value columns in 32-column tiles; wave w
-// takes token rows 16w .. +15.
-template <class In>
-__global__ __launch_bounds__(256) void bwd_dvn_kernel_pk(BwdArgs a) {
-    constexpr int VC = 32, VCL = VC + 1;
-    __shared__ __attribute__((aligned(16))) float Kgs[BT * BKL];
-    __shared__ __attribute__((aligned(16))) float Ps[BT * BTL];
-    __shared__ __attribute__((aligned(16))) float Ds[DK * VCL];      // dh' [key][col]
-    __shared__ __attribute__((aligned(16))) float dOs[BT * VCL];
-
-    const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int ci = blockIdx.x, head = blockIdx.y, H = a.H;
-    int u, cc;
-    chunk_of(a.um, ci, u, cc);
-    if (u < 0) return;
-    const UnitInfo ui = unit_info(a.um, u);
-    const int64_t t0 = ui.start + (int64_t)cc * BT;
-    int len = ui.len - cc * BT;
-    len = len < 0 ? 0 : (len > BT ? BT : len);
-    const int64_t ch = (int64_t)ci * H + head;
-    const int row0 = 16 * w;
-
-    load_tile<float, BT, DK>(reinterpret_cast<const float*>(a.ws.kg) + ch * (BT * DK), DK, BT, Kgs, BKL, tid);
-    load_tile<float, BT, BT>(reinterpret_cast<const float*>(a.ws.P) + ch * (BT * BT), BT, BT, Ps, BTL, tid);
-    for (int vt = 0; vt < DV / VC; ++vt) {
-        const int vc0 = vt * VC;
-        lds_barrier();
-        load_tile<float, DK, VC>(a.dH + ch * DK * DV + vc0, DV, DK, Ds, VCL, tid);
-        load_tile<In, BT, VC>(reinterpret_cast<const In*>(a.dout) + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, dOs,
-                              VCL, tid);
-        lds_barrier();
-        for (int ct = 0; ct < VC / 16; ++ct) {
-            f32x4 kd = {0.f, 0.f, 0.f, 0.f}, pd = kd;
-            mmf<DK>(kd, [&](int m, int k) { return Kgs[(row0 + m) * BKL + k]; },
-                    [&](int k, int nn) { return Ds[k * VCL + 16 * ct + nn]; }, G, n);
-            // P^T dO: P[j][i] = 0 for j < i
-            for (int k0 = row0; k0 < BT; k0 += 4)
-                pd = __builtin_amdgcn_mfma_f32_16x16x4f32(Ps[(k0 + G) * BTL + row0 + n], dOs[(k0 + G) * VCL + 16 * ct + n], pd,
-                                                         0, 0, 0);
-            for (int r = 0; r < 4; ++r)
-                a.dVN[(ch * BT + row0 + 4 * G + r) * DV + vc0 + 16 * ct + n] = kd[r] + a.scale * pd[r];
-        }
-    }
 }
 
 // ------------------------------------------------------------------ per-chunk gradients, bf16 inputs, scalar gate
@@ -1889,8 +1858,8 @@ hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* d
     f16* dHw = reinterpret_cast<f16*>(dH);
     f16* Uw = dHw + nchh * DK * DV;
     f16* Aw = reinterpret_cast<f16*>(dVN);
-    // per key: A (fp32) in the region after dvn's, U over the Qd tiles
-    float* Ak = dVN + nchh * BT * DV;
+    // per key: A (fp32) in the dvn region, U^T over the Qd tiles
+    float* Ak = dVN;
     BwdArgs a;
     a.um = p.um; a.H = p.H; a.use_exp2 = p.use_exp2; a.scale = p.scale;
     a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g; a.dout = dout; a.h = h; a.dht = dht;
@@ -1936,10 +1905,8 @@ hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* d
         dim3 grid(p.um.n_chunks, p.H);
         if (p.per_key) {
             if (p.dtype == 1) {
-                hipLaunchKernelGGL(bwd_dvn_kernel_pk<bf16>, grid, dim3(256), 0, s, a);
                 hipLaunchKernelGGL((bwd_grad_kernel<bf16, true>), grid, dim3(256), 0, s, a);
             } else {
-                hipLaunchKernelGGL(bwd_dvn_kernel_pk<float>, grid, dim3(256), 0, s, a);
                 hipLaunchKernelGGL((bwd_grad_kernel<float, true>), grid, dim3(256), 0, s, a);
             }
         } else {

@@ -472,8 +472,8 @@ extern "C" gdn_status gdn_state_merge_pieces(int32_t n_pieces, int32_t n_docs, i
 // Workspace of the backward: the preparation (T, P and the gate rows of every
 // chunk-head; per key, the gated q and k tiles and G_last, fp32), then dL/dh
 // at every chunk's exit and dvn of every chunk (fp32 regions; the bf16
-// scalar-gate path keeps fp16 values and its chunk maps in them), and per
-// key the fp32 chunk maps A of the state gradient.
+// scalar-gate path keeps fp16 values and its chunk maps in them; per key the
+// second region holds the fp32 chunk maps A of the state gradient instead).
 static size_t bwd_workspace(const gdn::Problem& p, gdn::Workspace* ws, float** dH, float** dVN, char* base) {
     gdn::Problem pf = p;
     pf.dtype = 0;
@@ -481,8 +481,9 @@ static size_t bwd_workspace(const gdn::Problem& p, gdn::Workspace* ws, float** d
     const int64_t prep = (int64_t)gdn::workspace_bytes(pf, ws, base);
     const int64_t nch = (int64_t)p.um.n_chunks * p.H;
     const int64_t o1 = align256(prep), o2 = align256(o1 + nch * DK * DV * 4);
-    // per key: the chunk maps A of the state gradient (fp32 K x K) follow
-    const int64_t end = align256(o2 + nch * BT * DV * 4 + (p.per_key ? nch * DK * DK * 4 : 0));
+    // per key: the chunk maps A of the state gradient (fp32 K x K) in place
+    // of dvn, which the per-key gradient kernel forms itself
+    const int64_t end = align256(o2 + (p.per_key ? nch * DK * DK * 4 : nch * BT * DV * 4));
     if (base) {
         *dH = reinterpret_cast<float*>(base + o1);
         *dVN = reinterpret_cast<float*>(base + o2);

@@ -337,7 +337,7 @@ gdn_status gdn_state_merge(int32_t B, int32_t H, int32_t n_seg, int32_t K, int32
  *                     gdn_state_grad_summary call), which is then not redone;
  *                     other bits give GDN_ERR_INVALID
  *   workspace         as for gdn_chunk_fwd (query its size with NULL); about
- *                     129 KiB per (chunk, head), 289 KiB with a per-key gate
+ *                     129 KiB per (chunk, head), 257 KiB with a per-key gate
  * Gradients are fp32 whatever the input dtype. With bf16 inputs and a scalar
  * gate the products run on fp16 operands with fp32 accumulation (the
  * forward's numeric range applies to the states and their gradients), and

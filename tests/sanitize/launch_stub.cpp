@@ -133,8 +133,8 @@ hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* d
     check_problem(pf, ws);
     const int64_t nch = int64_t(p.um.n_chunks) * p.H;
     region(dH, nch * 128 * 128 * 4, "dH region");
-    region(dVN, nch * 64 * 128 * 4, "dvn region");
-    if (p.per_key) region(dVN + nch * 64 * 128, nch * 128 * 128 * 4, "per-key chunk maps A");
+    if (p.per_key) region(dVN, nch * 128 * 128 * 4, "per-key chunk maps A");
+    else region(dVN, nch * 64 * 128 * 4, "dvn region");
     if (static_cast<const char*>(static_cast<void*>(dVN)) < static_cast<const char*>(static_cast<void*>(dH)) + nch * 128 * 128 * 4)
         fail("dH and dvn overlap");
     if (p.um.total_tokens > 0 && (!q || !k || !v || !g || !beta || !h || !dout))

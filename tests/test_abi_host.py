@@ -293,11 +293,11 @@ def test_backward_host_checks():
     prep = 2 * a256(nch * 64 * 64 * 4) + a256(nch * 5 * 64 * 4)
     assert st == gb.GDN_OK and need == a256(prep + nch * 128 * 128 * 4) + a256(nch * 64 * 128 * 4)
     # per key: T, P, the gated q and k tiles (q b^G, k b^G, k b^{G_L - G}) and
-    # G_last in fp32, then the same dL/dh and dvn regions and the fp32 chunk
-    # maps A (K x K) of the state gradient
+    # G_last in fp32, then the same dL/dh region and, in place of dvn, the
+    # fp32 chunk maps A (K x K) of the state gradient
     stk, needk = bwd(desc(gate_kind=1), ws=None)
     prepk = 2 * a256(nch * 64 * 64 * 4) + 3 * a256(nch * 64 * 128 * 4) + a256(nch * 128 * 4)
-    assert stk == gb.GDN_OK and needk == a256(prepk + nch * 128 * 128 * 4) + a256(nch * 64 * 128 * 4 + nch * 128 * 128 * 4)
+    assert stk == gb.GDN_OK and needk == a256(prepk + nch * 128 * 128 * 4) + a256(nch * 128 * 128 * 4)
     assert bwd(desc(chunk_size=32), ws=None)[0] == gb.GDN_ERR_INVALID
     for f in (2, 3, 4, 8, -1):                       # only REUSE_PREPARED is a backward flag
         assert bwd(desc(), flags=f)[0] == gb.GDN_ERR_INVALID, f
