@@ -131,21 +131,6 @@ struct PolicyF {          // fp32 inputs and operands
     }
 };
 
-// bf16 inputs with fp32 operands (the backward's preparation): bf16 widens to
-// fp32 exactly
-struct PolicyFB : PolicyF {
-    using In = bf16;
-    static constexpr int VPR = 8;
-    __device__ static float f(In x) { return (float)x; }
-    __device__ static void load16(const In* p, float* x) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(p);
-        for (int i = 0; i < 4; ++i) {
-            x[2 * i] = __builtin_bit_cast(float, w[i] << 16);
-            x[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
-        }
-    }
-};
-
 // ------------------------------------------------------------------ operand order
 // Order of the 64 x 128 k / q tiles (along keys) and of the 64 x 64 T and P
 // tiles (along tokens) in the fp16 state pass: within each 32-wide slice,
@@ -334,19 +319,28 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
             }
         }
         __syncthreads();
-        // running sum down each key column: wave w scans keys 32w .. 32w+31
-        // with the rows on its lanes (rows past the end keep the last sum),
-        // in fp64 so that every G is the correctly rounded prefix sum
-        for (int d = 32 * w; d < 32 * w + 32; ++d) {
-            double xs = Gs[lane * (DK + 4) + d];
-            for (int off = 1; off < 64; off <<= 1) {
-                const double y = __shfl_up(xs, off, 64);
-                if (lane >= off) xs += y;
+        // running sum down each key column, in fp64 so that every G is the
+        // correctly rounded prefix sum (rows past the end keep the last sum):
+        // lane l of wave w sums key 32w + (l & 31) over rows 32 (l >> 5) ..
+        // +31 in order, the upper half starting from the lower half's total
+        {
+            const int d = 32 * w + (lane & 31), r0 = 32 * (lane >> 5);
+            float gv[32];
+#pragma unroll
+            for (int r = 0; r < 32; ++r) gv[r] = Gs[(r0 + r) * (DK + 4) + d];
+            double half = 0.0;
+#pragma unroll
+            for (int r = 0; r < 32; ++r) half += (double)gv[r];
+            const double lo = __shfl(half, lane & 31, 64);
+            double xs = lane >= 32 ? lo : 0.0;
+#pragma unroll
+            for (int r = 0; r < 32; ++r) {
+                xs += (double)gv[r];
+                const float x = (float)xs;
+                Gs[(r0 + r) * (DK + 4) + d] = x;
+                if (a.g_cumsum && r0 + r < len) a.g_cumsum[((t0 + r0 + r) * H + head) * DK + d] = x;
             }
-            const float x = (float)xs;
-            Gs[lane * (DK + 4) + d] = x;
-            if (a.g_cumsum && lane < len) a.g_cumsum[((t0 + lane) * H + head) * DK + d] = x;
-            if (lane == BT - 1) a.ws.gamL[ch * DK + d] = x;
+            if (lane >= 32) a.ws.gamL[ch * DK + d] = (float)xs;
         }
     }
     __syncthreads();
@@ -573,6 +567,321 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
             P::st4(kd + r * DK + cp, xd);
             P::st4(kg + r * DK + cp, xg);
         }
+    }
+}
+
+// ------------------------------------------------------------------ prep, per-key gate, backward (bf16 in)
+// The backward's fp32 preparation for bf16 inputs with a per-key gate: the
+// same T, P, gated tiles and G_last as prep_kernel<PolicyF, true> would give
+// for the widened inputs, with its steps reordered so that two workgroups
+// share a compute unit (67 KiB of LDS). k and q stay bf16 in LDS (they widen
+// to fp32 exactly at every read); the L tiles wait in registers while P and
+// the gated tiles are formed, and the inverse then runs over the dead k, q
+// and gate tiles. No input transforms (the backward takes the transformed
+// inputs).
+constexpr int KQB = DK + 8;     // bf16 row stride of the k and q tiles (272 bytes)
+constexpr int GSL = DK + 4;     // fp32 row stride of the gate tile
+
+// 8 bf16 (16 bytes) -> fp32
+__device__ __forceinline__ void bf8_to_f32(const bf16* p, float* x) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __builtin_bit_cast(float, v[i] << 16);
+        x[2 * i + 1] = __builtin_bit_cast(float, v[i] & 0xffff0000u);
+    }
+}
+// 4 bf16 (8 bytes) -> fp32
+__device__ __forceinline__ f32x4 bf4_to_f32(const bf16* p) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    return f32x4{__builtin_bit_cast(float, v[0] << 16), __builtin_bit_cast(float, v[0] & 0xffff0000u),
+                 __builtin_bit_cast(float, v[1] << 16), __builtin_bit_cast(float, v[1] & 0xffff0000u)};
+}
+
+__global__ __launch_bounds__(256, 2) void prep_kernel_pkb(PrepArgs a) {
+    constexpr int KQ_BYTES = 2 * BT * KQB * 2, G_BYTES = BT * GSL * 4;
+    __shared__ __attribute__((aligned(16))) char smem[KQ_BYTES + G_BYTES];
+    __shared__ float bet[BT];
+    bf16* kt = reinterpret_cast<bf16*>(smem);
+    bf16* qt = kt + BT * KQB;
+    float* Gs = reinterpret_cast<float*>(smem + KQ_BYTES);
+    // once P and the gated tiles are out: L, T and the inverse's scratch
+    float* Ls = reinterpret_cast<float*>(smem);
+    float* Ts = Ls + BT * LDL;
+    float* Yb = Ts + BT * LDL;
+    static_assert((2 * BT * LDL + 3 * 16 * 17) * 4 <= KQ_BYTES + G_BYTES, "L, T and scratch fit the tiles");
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, G = lane >> 4, n = lane & 15;
+    const int ci = blockIdx.x, head = blockIdx.y, H = a.H;
+    int u, cc;
+    chunk_of(a.um, ci, u, cc);
+    if (u < 0) return;
+    const UnitInfo ui = unit_info(a.um, u);
+    const int64_t t0 = ui.start + (int64_t)cc * BT;
+    int len = ui.len - cc * BT;
+    len = len < 0 ? 0 : (len > BT ? BT : len);
+    const int64_t ch = (int64_t)ci * H + head;
+    const bf16* kin = reinterpret_cast<const bf16*>(a.k);
+    const bf16* qin = reinterpret_cast<const bf16*>(a.q);
+
+    // ---- every load issued before any store (rows past the chunk end are zero)
+    {
+        u32x4 kv[4], qv[4];
+        f32x4 gv[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid + 256 * i, r = e >> 4, c8 = (e & 15) * 8;
+            kv[i] = u32x4{0u, 0u, 0u, 0u};
+            qv[i] = kv[i];
+            if (r < len) {
+                kv[i] = *reinterpret_cast<const u32x4*>(kin + ((t0 + r) * H + head) * DK + c8);
+                qv[i] = *reinterpret_cast<const u32x4*>(qin + ((t0 + r) * H + head) * DK + c8);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e4 = tid + 256 * i, r = e4 >> 5, c4 = (e4 & 31) * 4;
+            gv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (r < len) gv[i] = *reinterpret_cast<const f32x4*>(a.g + ((t0 + r) * H + head) * DK + c4);
+        }
+        const float bt = tid < len ? (float)reinterpret_cast<const bf16*>(a.beta)[(t0 + tid) * H + head] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid + 256 * i, r = e >> 4, c8 = (e & 15) * 8;
+            *reinterpret_cast<u32x4*>(kt + r * KQB + c8) = kv[i];
+            *reinterpret_cast<u32x4*>(qt + r * KQB + c8) = qv[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e4 = tid + 256 * i, r = e4 >> 5, c4 = (e4 & 31) * 4;
+            *reinterpret_cast<f32x4*>(&Gs[r * GSL + c4]) = gv[i];
+        }
+        if (tid < BT) bet[tid] = bt;
+    }
+    __syncthreads();
+    // ---- running sum down each key column in fp64 (the correctly rounded
+    // prefix sums): lane l of wave w sums key 32w + (l & 31) over rows
+    // 32 (l >> 5) .. +31 in order, the upper half from the lower half's total
+    {
+        const int d = 32 * w + (lane & 31), r0 = 32 * (lane >> 5);
+        float gv[32];
+#pragma unroll
+        for (int r = 0; r < 32; ++r) gv[r] = Gs[(r0 + r) * GSL + d];
+        double half = 0.0;
+#pragma unroll
+        for (int r = 0; r < 32; ++r) half += (double)gv[r];
+        const double lo = __shfl(half, lane & 31, 64);
+        double xs = lane >= 32 ? lo : 0.0;
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+            xs += (double)gv[r];
+            Gs[(r0 + r) * GSL + d] = (float)xs;
+        }
+        if (lane >= 32) a.ws.gamL[ch * DK + d] = (float)xs;
+    }
+    __syncthreads();
+
+    // four rows i0 .. i0+3 against row j (i0 + r > j): sum_d x_id k_jd b^{G_id - G_jd}
+    auto direct4 = [&](const bf16* xi, int i0, int j, float* out) {
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int d = 0; d < DK; d += 4) {
+            const f32x4 kj = bf4_to_f32(kt + j * KQB + d);
+            const f32x4 gj = *reinterpret_cast<const f32x4*>(&Gs[j * GSL + d]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const f32x4 xv = bf4_to_f32(xi + (i0 + r) * KQB + d);
+                const f32x4 gi = *reinterpret_cast<const f32x4*>(&Gs[(i0 + r) * GSL + d]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s4[r] += xv[e] * kj[e] * fpow(gi[e] - gj[e], a.use_exp2);
+            }
+        }
+        for (int r = 0; r < 4; ++r) out[r] = s4[r];
+    };
+    // row i against the four rows j0 .. j0+3
+    auto direct4j = [&](const bf16* xi, int i, int j0, float* out) {
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int d = 0; d < DK; d += 4) {
+            const f32x4 xv = bf4_to_f32(xi + i * KQB + d);
+            const f32x4 gi = *reinterpret_cast<const f32x4*>(&Gs[i * GSL + d]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const f32x4 kj = bf4_to_f32(kt + (j0 + r) * KQB + d);
+                const f32x4 gj = *reinterpret_cast<const f32x4*>(&Gs[(j0 + r) * GSL + d]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s4[r] += xv[e] * kj[e] * fpow(gi[e] - gj[e], a.use_exp2);
+            }
+        }
+        for (int r = 0; r < 4; ++r) out[r] = s4[r];
+    };
+    auto ld8 = [](const float* p, float* x) {
+        const f32x4 u0 = *reinterpret_cast<const f32x4*>(p), u1 = *reinterpret_cast<const f32x4*>(p + 4);
+        for (int e = 0; e < 4; ++e) { x[e] = u0[e]; x[e + 4] = u1[e]; }
+    };
+    // the factored form for a diagonal tile too when the gate falls by at
+    // most 2^8 of decay inside its block on every key (wave-uniform)
+    auto diag_factored = [&](int blk) {
+        float rmax = 0.0f;
+        for (int d = lane; d < DK; d += 64) rmax = fmaxf(rmax, Gs[(16 * blk) * GSL + d] - Gs[(16 * blk + 15) * GSL + d]);
+        return __all(rmax <= (a.use_exp2 ? 8.0f : 5.545177444479562f)) != 0;
+    };
+    // the 16 x 16 tile of sum_d x_id k_jd b^{G_id - G_jd} for rows i = 16 it + .
+    // of x and j = 16 jt + . of k, with the decay factored about the last row
+    // of block jt: x b^{G_i - G_ref} and k b^{G_ref - G_j}, both at most |x|,
+    // |k| off the diagonal. Lane holds (i = 16 it + 4G + r, j = 16 jt + n), or
+    // transposed (j = 16 jt + 4G + r, i = 16 it + n).
+    auto factored = [&](const bf16* x_t, int it, int jt, bool transposed) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const int ref = 16 * jt + 15, i = 16 * it + n, j = 16 * jt + n;
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) {
+            const int col = 32 * kk + 8 * G;
+            float gr[8], gi[8], gj[8], xi[8], kj[8];
+            ld8(&Gs[ref * GSL + col], gr);
+            ld8(&Gs[i * GSL + col], gi);
+            ld8(&Gs[j * GSL + col], gj);
+            bf8_to_f32(x_t + i * KQB + col, xi);
+            bf8_to_f32(kt + j * KQB + col, kj);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float fi = xi[e] * fpow(gi[e] - gr[e], a.use_exp2), fj = kj[e] * fpow(gr[e] - gj[e], a.use_exp2);
+                acc = transposed ? __builtin_amdgcn_mfma_f32_16x16x4f32(fj, fi, acc, 0, 0, 0)
+                                 : __builtin_amdgcn_mfma_f32_16x16x4f32(fi, fj, acc, 0, 0, 0);
+            }
+        }
+        return acc;
+    };
+
+    // ---- L = strictly lower (beta_i k_i.k_j b^{G_i - G_j}), 10 tiles over
+    // 4 waves, kept in registers (tile w + 4q; lane holds L[16it + 4G + r][16jt + n])
+    f32x4 lacc[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        lacc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int t = w + 4 * q;
+        if (t >= 10) continue;
+        const int it = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+        const int jt = t - (it * (it + 1)) / 2;
+        f32x4 acc;
+        if (it == jt && !diag_factored(it)) {
+            float dv[4] = {0.f, 0.f, 0.f, 0.f};
+            const int i0 = 16 * it + 4 * G, j = 16 * jt + n;
+            if (j < i0 + 3) direct4(kt, i0, j, dv);
+            for (int r = 0; r < 4; ++r) acc[r] = j < i0 + r ? dv[r] : 0.0f;
+        } else {
+            acc = factored(kt, it, jt, false);
+        }
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * it + 4 * G + r, j = 16 * jt + n;
+            lacc[q][r] = j < i ? bet[i] * acc[r] : 0.0f;
+        }
+    }
+
+    // ---- P = tril_incl(q k^T decayed), computed as P^T tiles (rows j of
+    // block jt, columns i of block it); blocks above the diagonal are zeros
+    {
+        float* Pw = reinterpret_cast<float*>(a.ws.P) + ch * (BT * BT);
+        for (int t = w; t < 16; t += 4) {
+            const int jt = t >> 2, it = t & 3;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (jt == it && !diag_factored(jt)) {
+                float dv[4] = {0.f, 0.f, 0.f, 0.f};
+                const int i = 16 * it + n, j0 = 16 * jt + 4 * G;
+                if (j0 <= i) direct4j(qt, i, j0, dv);
+                for (int r = 0; r < 4; ++r) acc[r] = j0 + r <= i ? dv[r] : 0.0f;
+            } else if (jt <= it) {
+                acc = factored(qt, it, jt, true);
+            }
+            const int i = 16 * it + n;
+            f32x4 x;
+            for (int r = 0; r < 4; ++r) x[r] = 16 * jt + 4 * G + r <= i ? acc[r] : 0.0f;
+            *reinterpret_cast<f32x4*>(Pw + i * BT + 16 * jt + 4 * G) = x;
+        }
+    }
+
+    // ---- gated q and k tiles: q b^G, k b^G, k b^{G_last - G}
+    {
+        float* qg = reinterpret_cast<float*>(a.ws.qg) + ch * (BT * DK);
+        float* kd = reinterpret_cast<float*>(a.ws.kd) + ch * (BT * DK);
+        float* kg = reinterpret_cast<float*>(a.ws.kg) + ch * (BT * DK);
+        const int last = len > 0 ? len - 1 : 0;
+        for (int e4 = tid; e4 < BT * DK / 4; e4 += 256) {
+            const int r = e4 / (DK / 4), c4 = (e4 % (DK / 4)) * 4;
+            const f32x4 gg = *reinterpret_cast<const f32x4*>(&Gs[r * GSL + c4]);
+            const f32x4 gl = *reinterpret_cast<const f32x4*>(&Gs[last * GSL + c4]);
+            const f32x4 kv = bf4_to_f32(kt + r * KQB + c4), qv = bf4_to_f32(qt + r * KQB + c4);
+            f32x4 xq, xd, xg;
+            for (int e = 0; e < 4; ++e) {
+                const float bg = fpow(gg[e], a.use_exp2);
+                xq[e] = qv[e] * bg;
+                xd[e] = kv[e] * bg;
+                xg[e] = kv[e] * fpow(gl[e] - gg[e], a.use_exp2);
+            }
+            *reinterpret_cast<f32x4*>(qg + r * DK + c4) = xq;
+            *reinterpret_cast<f32x4*>(kd + r * DK + c4) = xd;
+            *reinterpret_cast<f32x4*>(kg + r * DK + c4) = xg;
+        }
+    }
+    __syncthreads();                             // k, q and G are dead from here
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        const int t = w + 4 * q;
+        if (t >= 10) continue;
+        const int it = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+        const int jt = t - (it * (it + 1)) / 2;
+        for (int r = 0; r < 4; ++r) Ls[(16 * it + 4 * G + r) * LDL + 16 * jt + n] = lacc[q][r];
+    }
+    __syncthreads();
+
+    // ---- T = (I + L)^{-1}: 16 x 16 diagonal blocks by substitution (wave 0,
+    // lane = block * 16 + column), then the off-diagonal blocks by distance
+    if (w == 0) {
+        const int bk = lane >> 4, c = lane & 15, o = 16 * bk;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float sacc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < i; ++j) sacc += Ls[(o + i) * LDL + o + j] * x[j];
+            x[i] = i == c ? 1.0f : (i > c ? -sacc : 0.0f);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Ts[(o + i) * LDL + o + c] = x[i];
+    } else {
+        for (int e = tid - 64; e < 6 * 256; e += 192) {
+            const int blk = e >> 8, rr = (e >> 4) & 15, cc2 = e & 15;
+            const int I = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+            const int J = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+            Ts[(16 * I + rr) * LDL + 16 * J + cc2] = 0.0f;
+        }
+    }
+    __syncthreads();
+    for (int d = 1; d < 4; ++d) {
+        const int nb = 4 - d;
+        for (int e = tid; e < nb * 256; e += 256) {
+            const int bi = e >> 8, rr = (e >> 4) & 15, cc2 = e & 15;
+            const int I = d + bi, J = bi;
+            float sacc = 0.0f;
+            for (int K2 = J; K2 < I; ++K2)
+                for (int m = 0; m < 16; ++m)
+                    sacc += Ls[(16 * I + rr) * LDL + 16 * K2 + m] * Ts[(16 * K2 + m) * LDL + 16 * J + cc2];
+            Yb[(bi * 16 + rr) * 17 + cc2] = sacc;
+        }
+        __syncthreads();
+        for (int e = tid; e < nb * 256; e += 256) {
+            const int bi = e >> 8, rr = (e >> 4) & 15, cc2 = e & 15;
+            const int I = d + bi, J = bi;
+            float sacc = 0.0f;
+            for (int m = 0; m < 16; ++m) sacc += Ts[(16 * I + rr) * LDL + 16 * I + m] * Yb[(bi * 16 + m) * 17 + cc2];
+            Ts[(16 * I + rr) * LDL + 16 * J + cc2] = -sacc;
+        }
+        __syncthreads();
+    }
+    float* Tw = reinterpret_cast<float*>(a.ws.Tm) + ch * (BT * BT);
+    for (int e = tid; e < BT * BT / 4; e += 256) {
+        const int r = e / (BT / 4), c4 = (e % (BT / 4)) * 4;
+        f32x4 x;
+        for (int q2 = 0; q2 < 4; ++q2) x[q2] = Ts[r * LDL + c4 + q2];
+        *reinterpret_cast<f32x4*>(Tw + r * BT + c4) = x;
     }
 }
 
@@ -2410,7 +2719,7 @@ hipError_t launch_prep_bwd(const Problem& p, const Workspace& ws, const void* k,
     a.q_hat = nullptr; a.k_hat = nullptr; a.q_rstd = nullptr; a.k_rstd = nullptr; a.beta_eff = nullptr;
     dim3 grid(p.um.n_chunks, p.H), block(256);
     if (p.per_key) {
-        if (p.dtype == 1) hipLaunchKernelGGL((prep_kernel<PolicyFB, true>), grid, block, 0, s, a);
+        if (p.dtype == 1) hipLaunchKernelGGL(prep_kernel_pkb, grid, block, 0, s, a);
         else hipLaunchKernelGGL((prep_kernel<PolicyF, true>), grid, block, 0, s, a);
     } else {
         if (p.dtype == 1) hipLaunchKernelGGL((prep_kernel_h<false, true>), dim3(p.H * p.um.n_chunks), dim3(64), 0, s, a);
