@@ -502,6 +502,15 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
         if ((tid & 15) == 0) hdK[(tid >> 4) + 16 * m] = x;
     }
     float brow[4] = {0.f, 0.f, 0.f, 0.f};        // k_i . R[dL,K]_i over this lane's keys
+    // the key slices' k, q and g tiles, one slice ahead
+    TileRegs<In, BT, 32> pk, pq;
+    TileRegs<float, BT, 32> pg;
+    auto issue = [&](int d0) {
+        pk.issue(kin + (t0 * H + head) * DK + d0, (int64_t)H * DK, len, tid);
+        pq.issue(qin + (t0 * H + head) * DK + d0, (int64_t)H * DK, len, tid);
+        pg.issue(a.g + (t0 * H + head) * DK + d0, (int64_t)H * DK, len, tid);
+    };
+    issue(0);
 
     // the slice loop stays rolled (its body is large); the slice's two key
     // tiles of dQd / dKd / dKg are picked out of the register arrays first
@@ -519,20 +528,30 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
 #undef GDN_PICK
         }
         lds_barrier();                         // X1 written; the previous slice consumed
-        load_tile<In, BT, 32>(kin + (t0 * H + head) * DK + d0, (int64_t)H * DK, len, Ksl, SL, tid);
-        load_tile<In, BT, 32>(qin + (t0 * H + head) * DK + d0, (int64_t)H * DK, len, Qsl, SL, tid);
-        load_tile<float, BT, 32>(a.g + (t0 * H + head) * DK + d0, (int64_t)H * DK, len, Gsl, SL, tid);
+        pk.commit(Ksl, SL, tid);
+        pq.commit(Qsl, SL, tid);
+        pg.commit(Gsl, SL, tid);
+        if (s + 1 < DK / 32) issue(d0 + 32);
         lds_barrier();
-        // G: inclusive sum down each key column, wave w taking columns
-        // 8w .. 8w+7 (rows past the chunk end keep G at its last row), in
-        // fp64 and rounded once, as the preparation does
-        for (int c = 8 * w; c < 8 * w + 8; ++c) {
-            double x = Gsl[lane * SL + c];
-            for (int off = 1; off < 64; off <<= 1) {
-                const double y = __shfl_up(x, off, 64);
-                if (lane >= off) x += y;
+        // G: running sum down each key column (rows past the chunk end keep G
+        // at its last row) in fp64, rounded once, as the preparation does:
+        // lane l of wave 0 sums column l & 31 over rows 32 (l >> 5) .. +31,
+        // the upper half from the lower half's total
+        if (w == 0) {
+            const int c = lane & 31, r0 = 32 * (lane >> 5);
+            float gv[32];
+#pragma unroll
+            for (int r = 0; r < 32; ++r) gv[r] = Gsl[(r0 + r) * SL + c];
+            double half = 0.0;
+#pragma unroll
+            for (int r = 0; r < 32; ++r) half += (double)gv[r];
+            const double lo = __shfl(half, c, 64);
+            double x = lane >= 32 ? lo : 0.0;
+#pragma unroll
+            for (int r = 0; r < 32; ++r) {
+                x += (double)gv[r];
+                Gsl[(r0 + r) * SL + c] = (float)x;
             }
-            Gsl[lane * SL + c] = (float)x;
         }
         lds_barrier();
 #pragma unroll
