@@ -723,32 +723,6 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
     const In* vin = reinterpret_cast<const In*>(a.v);
     const In* dout = reinterpret_cast<const In*>(a.dout);
 
-    if (PK) {
-        // per key: k b^G (for Y) in Ks, T and beta, and for dvn k b^{G_L - G}
-        // in Qs and P in Ps; q, k and G come in key slices in the finish
-        load_tile<float, BT, DK>(reinterpret_cast<const float*>(a.ws.kd) + ch * (BT * DK), DK, BT, Ks, BKL, tid);
-        load_tile<float, BT, BT>(reinterpret_cast<const float*>(a.ws.Tm) + ch * (BT * BT), BT, BT, Ts, BTL, tid);
-        load_tile<float, BT, DK>(reinterpret_cast<const float*>(a.ws.kg) + ch * (BT * DK), DK, BT, Qs, BKL, tid);
-        load_tile<float, BT, BT>(reinterpret_cast<const float*>(a.ws.P) + ch * (BT * BT), BT, BT, Ps, BTL, tid);
-        if (tid < BT) bt[tid] = tid < len ? ldf(reinterpret_cast<const In*>(a.beta), (t0 + tid) * H + head) : 0.0f;
-        lds_barrier();
-    } else {
-        load_chunk<In, false>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, gm, bt, tid);
-    }
-    if (tid < BT) {
-        rowG[tid] = 0.0f;
-        rowK[tid] = 0.0f;
-    }
-    const int row0 = 16 * w;
-    auto bG = [&](int row) { return gm[BT + row]; };
-    auto Tb = [&](int i, int j) { return Ts[i * BTL + j] * bt[j]; };   // T diag(beta)
-
-    f32x4 aP[4], aT[4], aQ[8], aKg[8], aKd[8];
-    for (int j = 0; j < 4; ++j) { aP[j] = f32x4{0.f, 0.f, 0.f, 0.f}; aT[j] = aP[j]; }
-    for (int j = 0; j < 8; ++j) { aQ[j] = f32x4{0.f, 0.f, 0.f, 0.f}; aKg[j] = aQ[j]; aKd[j] = aQ[j]; }
-    float hdh = 0.0f;     // this thread's share of sum(h o dh')
-    float hk[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // per key: keys (tid >> 4) + 16m, column tid & 15
-
     // the value tiles of tile vt + 1 are loaded into registers while tile vt
     // is computed (28 VGPRs), and written to LDS at the next tile's top
     TileRegs<float, DK, VT> ph, pdh;
@@ -762,7 +736,58 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
         pdo.issue(dout + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, tid);
         if (!PK) pdv.issue(a.dVN + ch * BT * DV + vc0, DV, BT, tid);
     };
-    prefetch(0);
+    if (PK) {
+        // per key: k b^G (for Y) in Ks, T and beta, and for dvn k b^{G_L - G}
+        // in Qs and P in Ps (all four loads in flight together); q, k and G
+        // come in key slices in the finish
+        TileRegs<float, BT, DK> rkd, rkg;
+        TileRegs<float, BT, BT> rt, rp;
+        prefetch(0);
+        rkd.issue(reinterpret_cast<const float*>(a.ws.kd) + ch * (BT * DK), DK, BT, tid);
+        rt.issue(reinterpret_cast<const float*>(a.ws.Tm) + ch * (BT * BT), BT, BT, tid);
+        rkg.issue(reinterpret_cast<const float*>(a.ws.kg) + ch * (BT * DK), DK, BT, tid);
+        rp.issue(reinterpret_cast<const float*>(a.ws.P) + ch * (BT * BT), BT, BT, tid);
+        if (tid < BT) bt[tid] = tid < len ? ldf(reinterpret_cast<const In*>(a.beta), (t0 + tid) * H + head) : 0.0f;
+        rkd.commit(Ks, BKL, tid);
+        rt.commit(Ts, BTL, tid);
+        rkg.commit(Qs, BKL, tid);
+        rp.commit(Ps, BTL, tid);
+        lds_barrier();
+    } else {
+        load_chunk<In, false>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, gm, bt, tid);
+        prefetch(0);
+    }
+    if (tid < BT) {
+        rowG[tid] = 0.0f;
+        rowK[tid] = 0.0f;
+    }
+    const int row0 = 16 * w;
+    auto bG = [&](int row) { return gm[BT + row]; };
+
+    // MFMA operands of this wave's rows, read once for all value tiles:
+    // Tb[row0 + n][4q + G] (nonzero for 4q <= row0 + 15), Tb[4q + G][row0 + n]
+    // (nonzero for 4q >= row0), the Ks row row0 + n in 16-byte groups, and per
+    // key P[4q + G][row0 + n] (nonzero for 4q >= row0) and the Kg row
+    float tbr[16], tbc[16], pc[16];
+    f32x4 kdr[8], kgr[8];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int k = 4 * q + G;
+        tbr[q] = Ts[(row0 + n) * BTL + k] * bt[k];
+        tbc[q] = Ts[k * BTL + row0 + n] * bt[row0 + n];
+        pc[q] = PK ? Ps[k * BTL + row0 + n] : 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        kdr[q] = *reinterpret_cast<const f32x4*>(Ks + (row0 + n) * BKL + 16 * q + 4 * G);
+        kgr[q] = PK ? *reinterpret_cast<const f32x4*>(Qs + (row0 + n) * BKL + 16 * q + 4 * G) : kdr[q];
+    }
+
+    f32x4 aP[4], aT[4], aQ[8], aKg[8], aKd[8];
+    for (int j = 0; j < 4; ++j) { aP[j] = f32x4{0.f, 0.f, 0.f, 0.f}; aT[j] = aP[j]; }
+    for (int j = 0; j < 8; ++j) { aQ[j] = f32x4{0.f, 0.f, 0.f, 0.f}; aKg[j] = aQ[j]; aKd[j] = aQ[j]; }
+    float hdh = 0.0f;     // this thread's share of sum(h o dh')
+    float hk[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // per key: keys (tid >> 4) + 16m, column tid & 15
     for (int vt = 0; vt < DV / VT; ++vt) {
         const int vc0 = vt * VT;
         lds_barrier();                           // the previous tile's buffers are consumed
@@ -783,8 +808,11 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
         // Y = V - Kd h, rows of this wave (scalar gate: Kd h = b^G (K h))
         {
             f32x4 kh = {0.f, 0.f, 0.f, 0.f};
-            mmf<DK>(kh, [&](int m, int k) { return Ks[(row0 + m) * BKL + k]; },
-                    [&](int k, int nn) { return Hs[k * VTL + nn]; }, G, n);
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    kh = __builtin_amdgcn_mfma_f32_16x16x4f32(kdr[q][e], Hs[(16 * q + 4 * G + e) * VTL + n], kh, 0, 0, 0);
             for (int r = 0; r < 4; ++r) {
                 const int row = row0 + 4 * G + r;
                 Ys[row * VTL + n] = Vs[row * VTL + n] - (PK ? kh[r] : bG(row) * kh[r]);
@@ -794,25 +822,25 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
             // dvn = Kg dh' + scale P^T dO, rows of this wave (P[j][i] = 0 for j < i)
             f32x4 kd = {0.f, 0.f, 0.f, 0.f}, pd = kd;
 #pragma unroll
-            for (int k0 = 0; k0 < DK; k0 += 16) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(Qs + (row0 + n) * BKL + k0 + 4 * G);
+            for (int q = 0; q < 8; ++q)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    kd = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e], DHs[(k0 + 4 * G + e) * VTL + n], kd, 0, 0, 0);
-            }
-            for (int k0 = row0; k0 < BT; k0 += 4)
-                pd = __builtin_amdgcn_mfma_f32_16x16x4f32(Ps[(k0 + G) * BTL + row0 + n], DOs[(k0 + G) * VTL + n], pd, 0, 0,
-                                                         0);
+                    kd = __builtin_amdgcn_mfma_f32_16x16x4f32(kgr[q][e], DHs[(16 * q + 4 * G + e) * VTL + n], kd, 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                if (4 * q >= row0)
+                    pd = __builtin_amdgcn_mfma_f32_16x16x4f32(pc[q], DOs[(4 * q + G) * VTL + n], pd, 0, 0, 0);
             for (int r = 0; r < 4; ++r) DVs[(row0 + 4 * G + r) * VTL + n] = kd[r] + a.scale * pd[r];
         }
         lds_barrier();
         // v_new = Tb Y and Z = Tb^T dvn = dV, rows of this wave
         {
             f32x4 vn = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
-            mmf<BT>(vn, [&](int m, int k) { return Tb(row0 + m, k); }, [&](int k, int nn) { return Ys[k * VTL + nn]; },
-                    G, n);
-            mmf<BT>(z, [&](int m, int k) { return Tb(k, row0 + m); }, [&](int k, int nn) { return DVs[k * VTL + nn]; },
-                    G, n);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                if (4 * q <= row0 + 15) vn = __builtin_amdgcn_mfma_f32_16x16x4f32(tbr[q], Ys[(4 * q + G) * VTL + n], vn, 0, 0, 0);
+                if (4 * q >= row0) z = __builtin_amdgcn_mfma_f32_16x16x4f32(tbc[q], DVs[(4 * q + G) * VTL + n], z, 0, 0, 0);
+            }
             for (int r = 0; r < 4; ++r) {
                 const int row = row0 + 4 * G + r;
                 VNs[row * VTL + n] = vn[r];
