@@ -284,20 +284,6 @@ __device__ void load_chunk(const BwdArgs& a, int64_t t0, int64_t ch, int head, i
         for (int e = tid; e < BT * BT; e += 256) Ts[(e >> 6) * BTL + (e & 63)] *= bt[e & 63];
 }
 
-// per key: k b^{G_L - G} into Ks, q b^G into Qs (k b^G replaces the first
-// later in the step), T diag(beta), P and beta
-template <class In>
-__device__ void load_chunk_pk(const BwdArgs& a, int64_t t0, int64_t ch, int head, int len, float* Ks, float* Qs,
-                              float* Ts, float* Ps, float* bt, int tid) {
-    load_tile<float, BT, DK>(reinterpret_cast<const float*>(a.ws.kg) + ch * (BT * DK), DK, BT, Ks, BKL, tid);
-    load_tile<float, BT, DK>(reinterpret_cast<const float*>(a.ws.qg) + ch * (BT * DK), DK, BT, Qs, BKL, tid);
-    load_tile<float, BT, BT>(reinterpret_cast<const float*>(a.ws.Tm) + ch * (BT * BT), BT, BT, Ts, BTL, tid);
-    load_tile<float, BT, BT>(reinterpret_cast<const float*>(a.ws.P) + ch * (BT * BT), BT, BT, Ps, BTL, tid);
-    if (tid < BT) bt[tid] = tid < len ? ldf(reinterpret_cast<const In*>(a.beta), (t0 + tid) * a.H + head) : 0.0f;
-    lds_barrier();
-    for (int e = tid; e < BT * BT; e += 256) Ts[(e >> 6) * BTL + (e & 63)] *= bt[e & 63];
-}
-
 }  // namespace
 
 // acc += A B^T over k in [0, KLEN), A and B stored row by row with k
@@ -316,16 +302,18 @@ __device__ __forceinline__ void mm_rowsk(f32x4& acc, const float* A, int lda, co
 }
 
 // ------------------------------------------------------------------ reverse state pass
-// fp32 operands: fp32 inputs, and the per-key gate at either input dtype.
-// One workgroup of four waves per (unit, head, 16 NCT value columns); wave w
+// fp32 inputs with a scalar gate (fp32 operands; the per-key gate takes the
+// affine form below). One workgroup of four waves per (unit, head, 16 NCT
+// value columns); wave w
 // holds dL/dh for keys 32w .. 32w+31 of those columns (2 NCT 16 x 16 tiles).
 // NCT = 1 (16-column tiles) doubles the workgroups where 32-column tiles
 // would leave compute units idle.
 // Chunks run from the last: store dh', then dvn = Kg dh' + scale P^T dO (wave
 // w: token rows 16w .. +15), Z = Tb^T dvn, and dh = gamma dh' + scale Qd^T dO
-// - Kd^T Z (per key: the prepared gated tiles, and gamma per key).
-template <class In, bool PK, int NCT>
+// - Kd^T Z.
+template <int NCT>
 __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
+    using In = float;
     constexpr int NC = 16 * NCT, CL = NC + 1;   // columns of the tile, LDS row stride
     __shared__ __attribute__((aligned(16))) float Ks[BT * BKL];
     __shared__ __attribute__((aligned(16))) float Qs[BT * BKL];
@@ -371,14 +359,8 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
         const int64_t t0 = ui.start + (int64_t)c * BT;
         const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
         lds_barrier();                               // the previous chunk's tiles are consumed
-        if (PK) load_chunk_pk<In>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, bt, tid);
-        else load_chunk<In, true>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, gm, bt, tid);
+        load_chunk<In, true>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, gm, bt, tid);
         load_tile<In, BT, NC>(dout + (t0 * H + head) * DV + c0, (int64_t)H * DV, len, dOs, CL, tid);
-        float gk[2][4];                                // per key: b^{G_L} of keys 32w + 16kt + 4G + r
-        if (PK)
-            for (int kt = 0; kt < 2; ++kt)
-                for (int r = 0; r < 4; ++r)
-                    gk[kt][r] = fpow(a.ws.gamL[ch * DK + 32 * w + 16 * kt + 4 * G + r], a.use_exp2);
         // dh' of this chunk to the workspace
         for (int kt = 0; kt < 2; ++kt)
             for (int ct = 0; ct < NCT; ++ct)
@@ -387,8 +369,8 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
                     a.dH[(ch * DK + key) * DV + c0 + 16 * ct + n] = dh[kt][ct][r];
                 }
         lds_barrier();
-        // dvn = Kg dh' + scale P^T dO, token rows 16w .. +15 (scalar gate:
-        // Kg = diag(b^{G_L - G}) K)
+        // dvn = Kg dh' + scale P^T dO, token rows 16w .. +15, with
+        // Kg = diag(b^{G_L - G}) K
         for (int ct = 0; ct < NCT; ++ct) {
             f32x4 kh = {0.f, 0.f, 0.f, 0.f}, pd = {0.f, 0.f, 0.f, 0.f};
             mm_rowsk<DK>(kh, Ks + 16 * w * BKL, BKL, dhT + 16 * ct * BKL, BKL, G, n);
@@ -396,38 +378,36 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
                     [&](int k, int nn) { return dOs[k * CL + 16 * ct + nn]; }, G, n);
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * w + 4 * G + r;
-                const float x = (PK ? kh[r] : gm[2 * BT + row] * kh[r]) + a.scale * pd[r];
+                const float x = gm[2 * BT + row] * kh[r] + a.scale * pd[r];
                 dvS[row * CL + 16 * ct + n] = x;
                 a.dVN[(ch * BT + row) * DV + c0 + 16 * ct + n] = x;
             }
         }
         lds_barrier();
-        // per key, k b^G takes the place of k b^{G_L - G}
-        if (PK) load_tile<float, BT, DK>(reinterpret_cast<const float*>(a.ws.kd) + ch * (BT * DK), DK, BT, Ks, BKL, tid);
-        // Z = Tb^T dvn, kept as b^G Z for the scalar gate
+        // Z = Tb^T dvn, kept as b^G Z
         for (int ct = 0; ct < NCT; ++ct) {
             f32x4 z = {0.f, 0.f, 0.f, 0.f};
             mmf<BT>(z, [&](int m, int k) { return Ts[k * BTL + 16 * w + m]; },
                     [&](int k, int nn) { return dvS[k * CL + 16 * ct + nn]; }, G, n);
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * w + 4 * G + r;
-                Zs[row * CL + 16 * ct + n] = PK ? z[r] : gm[BT + row] * z[r];
+                Zs[row * CL + 16 * ct + n] = gm[BT + row] * z[r];
             }
         }
         lds_barrier();
-        // dh = gamma dh' + Qd^T (scale dO) - Kd^T Z, keys 32w .. +31 (scalar
-        // gate: Q^T (scale b^G dO) - K^T (b^G Z))
-        const float gam = PK ? 0.0f : gm[3 * BT];
+        // dh = gamma dh' + Qd^T (scale dO) - Kd^T Z, keys 32w .. +31, as
+        // Q^T (scale b^G dO) - K^T (b^G Z)
+        const float gam = gm[3 * BT];
         for (int kt = 0; kt < 2; ++kt)
             for (int ct = 0; ct < NCT; ++ct) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acz = {0.f, 0.f, 0.f, 0.f};
                 const int key0 = 32 * w + 16 * kt;
                 mmf<BT>(acc, [&](int m, int k) { return Qs[k * BKL + key0 + m]; },
-                        [&](int k, int nn) { return a.scale * (PK ? 1.0f : gm[BT + k]) * dOs[k * CL + 16 * ct + nn]; },
+                        [&](int k, int nn) { return a.scale * gm[BT + k] * dOs[k * CL + 16 * ct + nn]; },
                         G, n);
                 mmf<BT>(acz, [&](int m, int k) { return Ks[k * BKL + key0 + m]; },
                         [&](int k, int nn) { return Zs[k * CL + 16 * ct + nn]; }, G, n);
-                for (int r = 0; r < 4; ++r) dh[kt][ct][r] = (PK ? gk[kt][r] : gam) * dh[kt][ct][r] + acc[r] - acz[r];
+                for (int r = 0; r < 4; ++r) dh[kt][ct][r] = gam * dh[kt][ct][r] + acc[r] - acz[r];
                 // keys key0 + 4G .. +3 of column 16 ct + n: one 16-byte store
                 *reinterpret_cast<f32x4*>(&dhT[(16 * ct + n) * BKL + key0 + 4 * G]) = dh[kt][ct];
             }
@@ -559,7 +539,7 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
             const int c = 16 * kt + n;           // slice column of this lane's key
             f32x4 ra = {0.f, 0.f, 0.f, 0.f}, rp = ra, ca = ra, cp = ra;
             // The diagonal block joins the factored products below when the
-            // gate falls by at most PK_DIAG_RANGE (2^8 of decay) inside the
+            // gate falls by at most 2^8 of decay (8 log2 units) inside the
             // block on every key of the tile: its factors about the reference
             // rows then stay within 2^8 (the forward preparation's rule).
             // The stored zeros of dL (strictly lower) and dP (lower with the
@@ -1942,9 +1922,9 @@ hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* d
             if (narrow) hipLaunchKernelGGL(bwd_dh_kernel_h<1>, grid, dim3(256), 0, s, a, Aw, Uw, dHw);
             else hipLaunchKernelGGL(bwd_dh_kernel_h<2>, grid, dim3(256), 0, s, a, Aw, Uw, dHw);
         } else if (narrow) {
-            hipLaunchKernelGGL((bwd_dh_kernel<float, false, 1>), grid, dim3(256), 0, s, a);
+            hipLaunchKernelGGL(bwd_dh_kernel<1>, grid, dim3(256), 0, s, a);
         } else {
-            hipLaunchKernelGGL((bwd_dh_kernel<float, false, 2>), grid, dim3(256), 0, s, a);
+            hipLaunchKernelGGL(bwd_dh_kernel<2>, grid, dim3(256), 0, s, a);
         }
 #undef GDN_DHA
     }
