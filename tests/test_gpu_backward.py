@@ -219,6 +219,18 @@ def test_backward_per_key(B, T, H, dtype, use_exp2):
     check_all(out, ref, TOL[dtype], "per key")
 
 
+@pytest.mark.parametrize("H", [12, 24])
+def test_backward_per_key_wide_column_tiles(H):
+    # 4 x H (unit, head) pairs: with 256 compute units the per-key reverse
+    # pass runs 32-column tiles at H = 12 and 64-column tiles at H = 24 (the
+    # small cases above take 16-column tiles); the oracle checks two heads
+    print(f"per-key backward, wide tiles: B=4 T=70 H={H}", flush=True)
+    w = small(B=4, T=70, H=H, dtype="bf16", use_exp2=True, gate_coef=0.05, per_key=True)
+    d = W.generate(w, 977 + H)
+    out, ref = run_both(d, 31 + H, S0=True, dht=True, heads=[0, H - 1])
+    check_all(out, ref, TOL["bf16"], f"per key H={H}")
+
+
 @pytest.mark.parametrize("coef", [0.6, 1.0, 4.0])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_backward_per_key_strong_gates(coef, dtype):
