@@ -465,6 +465,7 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
     float* dGs = Qs + 3 * BT * SL;
     float* hdK = Ks;                             // [DK] diag(h dh'^T)
     float* KGs = Ks + DK;                        // [BT][SL] ln b Kg o dKg of the slice
+    float* blk = KGs + BT * SL;                  // [4][64] the waves' block totals of the dg sums
     const In* kin = reinterpret_cast<const In*>(a.k);
     const In* qin = reinterpret_cast<const In*>(a.q);
     const int last = len > 0 ? len - 1 : 0;
@@ -634,25 +635,48 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
         }
         lds_barrier();
         // dg_j = sum_{i >= j} dG_i + ln b gamma diag(h dh'^T) + sum_{i < j}
-        // ln b Kg o dKg: a reverse sum down each key column, the state
-        // decay's term, and the exclusive prefix of the Kg terms; wave w
-        // takes columns 8w .. 8w+7
-        for (int c = 8 * w; c < 8 * w + 8; ++c) {
-            const float gl = lnb * fpow(Gsl[last * SL + c], ue) * hdK[d0 + c];
-            float x = lane < len ? dGs[lane * SL + c] + (lane == last ? gl : 0.0f) : 0.0f;
-            const float kg = lane < len ? KGs[lane * SL + c] : 0.0f;
-            float y = kg;
-            for (int off = 1; off < 64; off <<= 1) {
-                const float xd = __shfl_down(x, off, 64), yu = __shfl_up(y, off, 64);
-                if (lane + off < 64) x += xd;
-                if (lane >= off) y += yu;
+        // ln b Kg o dKg: a reverse sum down each key column (the state
+        // decay's term at the last valid row) and the exclusive prefix of the
+        // Kg terms. Wave w sums rows 16w .. +15 of every column in order
+        // (lanes 0..31 the reverse sums, lanes 32..63 the prefixes), then
+        // starts from the other waves' block totals.
+        {
+            const int c = lane & 31;
+            const bool rev = lane < 32;
+            const float gl = rev ? lnb * fpow(Gsl[last * SL + c], ue) * hdK[d0 + c] : 0.0f;
+            float v[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 16 * w + r;
+                const float x = rev ? dGs[row * SL + c] + (row == last ? gl : 0.0f) : KGs[row * SL + c];
+                v[r] = row < len ? x : 0.0f;
             }
-            dGs[lane * SL + c] = x + (y - kg);
+            float tot = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tot += v[r];
+            blk[w * 64 + lane] = tot;
+            lds_barrier();
+            float acc = 0.0f;
+            for (int w2 = 0; w2 < 4; ++w2)
+                if (rev ? w2 > w : w2 < w) acc += blk[w2 * 64 + lane];
+            if (rev) {
+#pragma unroll
+                for (int r = 15; r >= 0; --r) {
+                    acc += v[r];
+                    dGs[(16 * w + r) * SL + c] = acc;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    KGs[(16 * w + r) * SL + c] = acc;
+                    acc += v[r];
+                }
+            }
         }
         lds_barrier();
         for (int e = tid; e < BT * 32; e += 256) {
             const int r = e >> 5, c = e & 31;
-            if (r < len) a.dg[((t0 + r) * H + head) * DK + d0 + c] = dGs[r * SL + c];
+            if (r < len) a.dg[((t0 + r) * H + head) * DK + d0 + c] = dGs[r * SL + c] + KGs[r * SL + c];
         }
     }
     // dbeta: the row term summed over the 16 lanes of each group, added to the
