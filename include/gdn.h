@@ -340,9 +340,10 @@ gdn_status gdn_state_merge(int32_t B, int32_t H, int32_t n_seg, int32_t K, int32
  *                     129 KiB per (chunk, head), 257 KiB with a per-key gate
  * Gradients are fp32 whatever the input dtype. With bf16 inputs and a scalar
  * gate the products run on fp16 operands with fp32 accumulation (the
- * forward's numeric range applies to the states and their gradients), and
- * the chunk preparation includes each chunk's transfer maps of the state
- * gradient; fp32 inputs and the per-key gate use fp32 operands. The per-key
+ * forward's numeric range applies to the states and their gradients); fp32
+ * inputs and the per-key gate use fp32 operands. With bf16 inputs and a
+ * scalar gate, and with a per-key gate, the chunk preparation includes each
+ * chunk's transfer maps of the state gradient (fp16, resp. fp32). The per-key
  * decay is taken in factors that are at most 1 for every g <= 0 (as in the
  * forward), so strong gates down to total forgetting give finite gradients.
  */
