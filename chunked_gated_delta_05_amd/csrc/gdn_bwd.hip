@@ -1145,18 +1145,19 @@ __global__ __launch_bounds__(256, 2) void bwd_transfer_kernel_pk(BwdArgs a, floa
         *reinterpret_cast<f32x4*>(qg + (16 * ct + n) * BT + row0 + 4 * G) = uo[ct];
 }
 
-// The sequential pass: one workgroup of four waves per (unit, head, 16 NCT
-// value columns), one per compute unit (about 400 registers a lane); wave w
-// keeps D for keys 32w .. 32w+31 in fp32 registers and a copy in LDS as
-// [column][key]. Its rows of A and of U^T come straight
-// from memory into MFMA operand registers, one chunk ahead (two register
-// sets, taken in turn); dO goes through LDS as [column][row]. D and dO are
-// double-buffered in LDS, so one barrier per chunk hands both over. dh' of
-// every chunk goes to the workspace.
+// The sequential pass: one workgroup of eight waves per (unit, head, 16 NCT
+// value columns), one per compute unit (two waves per SIMD); wave w keeps D
+// for keys 16w .. 16w+15 in fp32 registers and a copy in LDS as
+// [column][key]. Its rows of A and of U^T come straight from memory into
+// MFMA operand registers, one chunk ahead (two register sets, taken in
+// turn); dO goes through LDS as [column][row]. D and dO are double-buffered
+// in LDS, so one barrier per chunk hands both over. dh' of every chunk goes
+// to the workspace.
 constexpr int DTL = BT + 4;     // row stride (floats) of the transposed dO tile
+constexpr int PKR = 512;        // threads of the per-key sequential pass
 
 template <class In, int NCT>
-__global__ __launch_bounds__(256, 1) void bwd_dh_kernel_pkr(BwdArgs a, const float* Aw) {
+__global__ __launch_bounds__(PKR, 1) void bwd_dh_kernel_pkr(BwdArgs a, const float* Aw) {
     constexpr int NC = 16 * NCT;
     __shared__ __attribute__((aligned(16))) float dhT[2][NC * BKL];  // D [column][key]
     __shared__ __attribute__((aligned(16))) float dOT[2][NC * DTL];  // dO [column][row]
@@ -1172,77 +1173,62 @@ __global__ __launch_bounds__(256, 1) void bwd_dh_kernel_pkr(BwdArgs a, const flo
     const int c0 = tile * NC;
     const int64_t uh = (int64_t)u * H + head;
     const float* Uw = reinterpret_cast<const float*>(a.ws.qg);
+    const int key0 = 16 * w;
+    const bool ld = tid < 256;                   // the threads that stage dO
 
-    f32x4 dh[2][NCT];
+    f32x4 dh[NCT];
     const int b_last = (ui.nch - 1) & 1;
-    for (int kt = 0; kt < 2; ++kt)
-        for (int ct = 0; ct < NCT; ++ct) {
-            for (int r = 0; r < 4; ++r) {
-                const int key = 32 * w + 16 * kt + 4 * G + r, col = 16 * ct + n;
-                dh[kt][ct][r] = a.dht ? a.dht[(uh * DK + key) * DV + c0 + col] : 0.0f;
-            }
-            *reinterpret_cast<f32x4*>(&dhT[b_last][(16 * ct + n) * BKL + 32 * w + 16 * kt + 4 * G]) = dh[kt][ct];
+    for (int ct = 0; ct < NCT; ++ct) {
+        for (int r = 0; r < 4; ++r) {
+            const int key = key0 + 4 * G + r, col = 16 * ct + n;
+            dh[ct][r] = a.dht ? a.dht[(uh * DK + key) * DV + c0 + col] : 0.0f;
         }
+        *reinterpret_cast<f32x4*>(&dhT[b_last][(16 * ct + n) * BKL + key0 + 4 * G]) = dh[ct];
+    }
 
-    // operand registers: A[32w + 16kt + n][16kb + 4G .. +3], U^T[32w + 16kt + n][16rb + 4G .. +3]
-    f32x4 A0[2][8], U0[2][4], A1[2][8], U1[2][4];
+    // operand registers: A[key0 + n][16kb + 4G .. +3], U^T[key0 + n][16rb + 4G .. +3]
+    f32x4 A0[8], U0[4], A1[8], U1[4];
     TileRegs<In, BT, NC> pd;
-    auto issue = [&](int cc, f32x4 (&Ar)[2][8], f32x4 (&Ur)[2][4]) {
+    auto issue = [&](int cc, f32x4 (&Ar)[8], f32x4 (&Ur)[4]) {
         int l = ui.len - cc * BT;
         l = l > BT ? BT : l;
         const int64_t tt = ui.start + (int64_t)cc * BT, chh = (int64_t)(ui.cbase + cc) * H + head;
-        const float* ap = Aw + chh * (DK * DK) + (32 * w + n) * DK + 4 * G;
-        const float* up = Uw + chh * (DK * BT) + (32 * w + n) * BT + 4 * G;
+        const float* ap = Aw + chh * (DK * DK) + (key0 + n) * DK + 4 * G;
+        const float* up = Uw + chh * (DK * BT) + (key0 + n) * BT + 4 * G;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kb = 0; kb < 8; ++kb) Ar[kb] = *reinterpret_cast<const f32x4*>(ap + 16 * kb);
 #pragma unroll
-            for (int kb = 0; kb < 8; ++kb) Ar[kt][kb] = *reinterpret_cast<const f32x4*>(ap + 16 * kt * DK + 16 * kb);
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) Ur[kt][rb] = *reinterpret_cast<const f32x4*>(up + 16 * kt * BT + 16 * rb);
-        }
-        pd.issue(reinterpret_cast<const In*>(a.dout) + (tt * H + head) * DV + c0, (int64_t)H * DV, l, tid);
+        for (int rb = 0; rb < 4; ++rb) Ur[rb] = *reinterpret_cast<const f32x4*>(up + 16 * rb);
+        if (ld) pd.issue(reinterpret_cast<const In*>(a.dout) + (tt * H + head) * DV + c0, (int64_t)H * DV, l, tid);
     };
-    auto step = [&](int c, const f32x4 (&Ar)[2][8], const f32x4 (&Ur)[2][4], f32x4 (&An)[2][8], f32x4 (&Un)[2][4]) {
+    auto step = [&](int c, const f32x4 (&Ar)[8], const f32x4 (&Ur)[4], f32x4 (&An)[8], f32x4 (&Un)[4]) {
         const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
         const int b = c & 1;
-        pd.commit_tr(dOT[b], DTL, tid);
+        if (ld) pd.commit_tr(dOT[b], DTL, tid);
         if (c > 0) issue(c - 1, An, Un);
-        for (int kt = 0; kt < 2; ++kt)
-            for (int ct = 0; ct < NCT; ++ct)
-                for (int r = 0; r < 4; ++r) {
-                    const int key = 32 * w + 16 * kt + 4 * G + r;
-                    a.dH[(ch * DK + key) * DV + c0 + 16 * ct + n] = dh[kt][ct][r];
-                }
+        for (int ct = 0; ct < NCT; ++ct)
+            for (int r = 0; r < 4; ++r) a.dH[(ch * DK + key0 + 4 * G + r) * DV + c0 + 16 * ct + n] = dh[ct][r];
         lds_barrier();                           // D and dO of this chunk are in LDS
-        // D' = A D + scale U^T dO, keys 32w .. +31
+        // D' = A D + scale U^T dO, keys key0 .. +15
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-            f32x4 ad[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, ae[2] = {ad[0], ad[0]};
+            f32x4 ad = {0.f, 0.f, 0.f, 0.f}, ae = ad;
             const float* dcol = dhT[b] + (16 * ct + n) * BKL + 4 * G;
             const float* ocol = dOT[b] + (16 * ct + n) * DTL + 4 * G;
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb) {
                 const f32x4 y = *reinterpret_cast<const f32x4*>(dcol + 16 * kb);
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-#pragma unroll
-                    for (int kt = 0; kt < 2; ++kt)
-                        ad[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(Ar[kt][kb][e], y[e], ad[kt], 0, 0, 0);
+                for (int e = 0; e < 4; ++e) ad = __builtin_amdgcn_mfma_f32_16x16x4f32(Ar[kb][e], y[e], ad, 0, 0, 0);
             }
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
                 const f32x4 y = *reinterpret_cast<const f32x4*>(ocol + 16 * rb);
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-#pragma unroll
-                    for (int kt = 0; kt < 2; ++kt)
-                        ae[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(Ur[kt][rb][e], y[e], ae[kt], 0, 0, 0);
+                for (int e = 0; e < 4; ++e) ae = __builtin_amdgcn_mfma_f32_16x16x4f32(Ur[rb][e], y[e], ae, 0, 0, 0);
             }
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                for (int r = 0; r < 4; ++r) dh[kt][ct][r] = ad[kt][r] + a.scale * ae[kt][r];
-                *reinterpret_cast<f32x4*>(&dhT[b ^ 1][(16 * ct + n) * BKL + 32 * w + 16 * kt + 4 * G]) = dh[kt][ct];
-            }
+            for (int r = 0; r < 4; ++r) dh[ct][r] = ad[r] + a.scale * ae[r];
+            *reinterpret_cast<f32x4*>(&dhT[b ^ 1][(16 * ct + n) * BKL + key0 + 4 * G]) = dh[ct];
         }
     };
     if (ui.nch > 0) issue(ui.nch - 1, A0, U0);
@@ -1251,12 +1237,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dh_kernel_pkr(BwdArgs a, const flo
         if (c >= 1) step(c - 1, A1, U1, A0, U0);
     }
     if (a.dh0)
-        for (int kt = 0; kt < 2; ++kt)
-            for (int ct = 0; ct < NCT; ++ct)
-                for (int r = 0; r < 4; ++r) {
-                    const int key = 32 * w + 16 * kt + 4 * G + r;
-                    a.dh0[(uh * DK + key) * DV + c0 + 16 * ct + n] = dh[kt][ct][r];
-                }
+        for (int ct = 0; ct < NCT; ++ct)
+            for (int r = 0; r < 4; ++r) a.dh0[(uh * DK + key0 + 4 * G + r) * DV + c0 + 16 * ct + n] = dh[ct][r];
 }
 
 // ------------------------------------------------------------------ per-chunk gradients, bf16 inputs, scalar gate
@@ -1937,9 +1919,9 @@ hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* d
         const int pk_nct = 8 * (int64_t)a.n_pairs <= cus ? 1 : 4 * (int64_t)a.n_pairs <= cus ? 2 : 4;
         const dim3 grid_pk((DV / (16 * pk_nct)) * 8 * ((a.n_pairs + 7) / 8));
 #define GDN_DHA(IN)                                                                                   \
-    if (pk_nct == 4) hipLaunchKernelGGL((bwd_dh_kernel_pkr<IN, 4>), grid_pk, dim3(256), 0, s, a, Ak); \
-    else if (pk_nct == 2) hipLaunchKernelGGL((bwd_dh_kernel_pkr<IN, 2>), grid_pk, dim3(256), 0, s, a, Ak); \
-    else hipLaunchKernelGGL((bwd_dh_kernel_pkr<IN, 1>), grid_pk, dim3(256), 0, s, a, Ak);
+    if (pk_nct == 4) hipLaunchKernelGGL((bwd_dh_kernel_pkr<IN, 4>), grid_pk, dim3(PKR), 0, s, a, Ak); \
+    else if (pk_nct == 2) hipLaunchKernelGGL((bwd_dh_kernel_pkr<IN, 2>), grid_pk, dim3(PKR), 0, s, a, Ak); \
+    else hipLaunchKernelGGL((bwd_dh_kernel_pkr<IN, 1>), grid_pk, dim3(PKR), 0, s, a, Ak);
         if (p.per_key) {
             if (p.dtype == 1) { GDN_DHA(bf16) } else { GDN_DHA(float) }
         } else if (h16) {
