@@ -1432,15 +1432,18 @@ __global__ __launch_bounds__(256) void bwd_transfer_kernel_h(BwdArgs a, f16* Aw,
     }
 }
 
-// The sequential pass: one workgroup of four waves per (unit, head, 16 NCT
-// value columns); wave w keeps D for keys 32w .. 32w+31 in fp32 registers,
-// and its fp16 copy goes to LDS as [column][key] for the next chunk's
-// product (double-buffered, so each chunk needs one barrier). A, U and dO of
-// chunk c - 1 are loaded into registers while chunk c + 1 is computed and
-// stored to the other LDS buffer at the end of chunk c. dh' (D of every
-// chunk) goes to the workspace as fp16.
+// The sequential pass: one workgroup of eight waves per (unit, head, 16 NCT
+// value columns), two waves per SIMD; wave w keeps D for keys 16w .. 16w+15
+// in fp32 registers, and its fp16 copy goes to LDS as [column][key] for the
+// next chunk's product (double-buffered, so each chunk needs one barrier).
+// Waves 0..3 stage the chunk tiles: A, U and dO of chunk c - 1 are loaded
+// into their registers while chunk c + 1 is computed and stored to the other
+// LDS buffer at the end of chunk c. dh' (D of every chunk) goes to the
+// workspace as fp16.
+constexpr int DHH = 512;        // threads of the fp16 sequential pass
+
 template <int NCT>
-__global__ __launch_bounds__(256) void bwd_dh_kernel_h(BwdArgs a, const f16* Aw, const f16* Uw, f16* dHw) {
+__global__ __launch_bounds__(DHH, 1) void bwd_dh_kernel_h(BwdArgs a, const f16* Aw, const f16* Uw, f16* dHw) {
     constexpr int NC = 16 * NCT, HC = NC + 8;     // columns of the tile, LDS row stride (halves)
     __shared__ __attribute__((aligned(16))) f16 Ah[2][DK * HK];    // A [key'][key]
     __shared__ __attribute__((aligned(16))) f16 Uh[2][BT * HK];    // U [row][key]
@@ -1461,23 +1464,25 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel_h(BwdArgs a, const f16* Aw,
     const int c0 = tile * NC;
     const int64_t uh = (int64_t)u * H + head;
     const bf16* dout = reinterpret_cast<const bf16*>(a.dout);
+    const int key0 = 16 * w;
+    const bool ld = tid < 256;                   // the threads that stage the chunk tiles
 
-    // D at the unit's end: keys 32w + 16kt + 4G + r, column 16ct + n
-    f32x4 dh[2][NCT];
+    // D at the unit's end: keys key0 + 4G + r, column 16ct + n
+    f32x4 dh[NCT];
     const int b_last = (ui.nch - 1) & 1;
-    for (int kt = 0; kt < 2; ++kt)
-        for (int ct = 0; ct < NCT; ++ct) {
-            for (int r = 0; r < 4; ++r) {
-                const int key = 32 * w + 16 * kt + 4 * G + r, col = 16 * ct + n;
-                dh[kt][ct][r] = a.dht ? a.dht[(uh * DK + key) * DV + c0 + col] : 0.0f;
-            }
-            st4h(dhT[b_last] + (16 * ct + n) * HK + 32 * w + 16 * kt + 4 * G, dh[kt][ct]);
+    for (int ct = 0; ct < NCT; ++ct) {
+        for (int r = 0; r < 4; ++r) {
+            const int key = key0 + 4 * G + r, col = 16 * ct + n;
+            dh[ct][r] = a.dht ? a.dht[(uh * DK + key) * DV + c0 + col] : 0.0f;
         }
+        st4h(dhT[b_last] + (16 * ct + n) * HK + key0 + 4 * G, dh[ct]);
+    }
 
     TileRegs<f16, DK, DK> pa;
     TileRegs<f16, BT, DK> pu;
     TileRegs<bf16, BT, NC> pd;
     auto prefetch = [&](int cc) {
+        if (!ld) return;
         int l = ui.len - cc * BT;
         l = l > BT ? BT : l;
         const int64_t tt = ui.start + (int64_t)cc * BT, chh = (int64_t)(ui.cbase + cc) * H + head;
@@ -1486,6 +1491,7 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel_h(BwdArgs a, const f16* Aw,
         pd.issue(dout + (tt * H + head) * DV + c0, (int64_t)H * DV, l, tid);
     };
     auto commit = [&](int b) {
+        if (!ld) return;
         pa.commit_raw(Ah[b], HK, tid);
         pu.commit_raw(Uh[b], HK, tid);
         pd.commit_h(dOh[b], HC, tid);
@@ -1501,15 +1507,10 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel_h(BwdArgs a, const f16* Aw,
         const int64_t ch = (int64_t)(ui.cbase + c) * H + head;
         const int b = c & 1;
         // dh' of this chunk to the workspace
-        for (int kt = 0; kt < 2; ++kt)
-            for (int ct = 0; ct < NCT; ++ct)
-                for (int r = 0; r < 4; ++r) {
-                    const int key = 32 * w + 16 * kt + 4 * G + r;
-                    dHw[(ch * DK + key) * DV + c0 + 16 * ct + n] = (f16)dh[kt][ct][r];
-                }
-        // D' = A D + scale U^T dO, keys 32w .. +31
-        for (int kt = 0; kt < 2; ++kt) {
-            const int key0 = 32 * w + 16 * kt;
+        for (int ct = 0; ct < NCT; ++ct)
+            for (int r = 0; r < 4; ++r) dHw[(ch * DK + key0 + 4 * G + r) * DV + c0 + 16 * ct + n] = (f16)dh[ct][r];
+        // D' = A D + scale U^T dO, keys key0 .. +15
+        {
             f16x8 aa[4], au[2];
             for (int ks = 0; ks < 4; ++ks) aa[ks] = frag_row(Ah[b], HK, key0 + n, 32 * ks, G);
             for (int js = 0; js < 2; ++js) au[js] = frag_col(Uh[b], HK, 32 * js, key0, G, n);
@@ -1517,8 +1518,8 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel_h(BwdArgs a, const f16* Aw,
                 f32x4 ad = {0.f, 0.f, 0.f, 0.f}, ae = ad;
                 for (int ks = 0; ks < 4; ++ks) mma_h(ad, aa[ks], frag_row(dhT[b], HK, 16 * ct + n, 32 * ks, G));
                 for (int js = 0; js < 2; ++js) mma_h(ae, au[js], frag_col(dOh[b], HC, 32 * js, 16 * ct, G, n));
-                for (int r = 0; r < 4; ++r) dh[kt][ct][r] = ad[r] + a.scale * ae[r];
-                st4h(dhT[b ^ 1] + (16 * ct + n) * HK + key0 + 4 * G, dh[kt][ct]);
+                for (int r = 0; r < 4; ++r) dh[ct][r] = ad[r] + a.scale * ae[r];
+                st4h(dhT[b ^ 1] + (16 * ct + n) * HK + key0 + 4 * G, dh[ct]);
             }
         }
         // chunk c - 1 into the other buffers (last read by chunk c + 1), then
@@ -1530,12 +1531,8 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel_h(BwdArgs a, const f16* Aw,
         lds_barrier();                               // D' and chunk c - 1 published
     }
     if (a.dh0)
-        for (int kt = 0; kt < 2; ++kt)
-            for (int ct = 0; ct < NCT; ++ct)
-                for (int r = 0; r < 4; ++r) {
-                    const int key = 32 * w + 16 * kt + 4 * G + r;
-                    a.dh0[(uh * DK + key) * DV + c0 + 16 * ct + n] = dh[kt][ct][r];
-                }
+        for (int ct = 0; ct < NCT; ++ct)
+            for (int r = 0; r < 4; ++r) a.dh0[(uh * DK + key0 + 4 * G + r) * DV + c0 + 16 * ct + n] = dh[ct][r];
 }
 
 __global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a, const f16* dHw) {
@@ -1925,8 +1922,8 @@ hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* d
         if (p.per_key) {
             if (p.dtype == 1) { GDN_DHA(bf16) } else { GDN_DHA(float) }
         } else if (h16) {
-            if (narrow) hipLaunchKernelGGL(bwd_dh_kernel_h<1>, grid, dim3(256), 0, s, a, Aw, Uw, dHw);
-            else hipLaunchKernelGGL(bwd_dh_kernel_h<2>, grid, dim3(256), 0, s, a, Aw, Uw, dHw);
+            if (narrow) hipLaunchKernelGGL(bwd_dh_kernel_h<1>, grid, dim3(DHH), 0, s, a, Aw, Uw, dHw);
+            else hipLaunchKernelGGL(bwd_dh_kernel_h<2>, grid, dim3(DHH), 0, s, a, Aw, Uw, dHw);
         } else if (narrow) {
             hipLaunchKernelGGL(bwd_dh_kernel<1>, grid, dim3(256), 0, s, a);
         } else {
