@@ -689,6 +689,251 @@ __device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int
     if (tid < len) a.dbeta[(t0 + tid) * H + head] = dbT[tid];
 }
 
+// The per-key finish at eight waves: wave w8 takes token block w = w8 & 3 and
+// the key tile grp = w8 >> 2 of every 32-key slice (the half of the slice's
+// dQd / dKd / dKg tiles its group accumulated); dl holds its rows of dL for
+// column blocks 2 grp, 2 grp + 1. The two groups' dbeta row terms meet in
+// brs.
+template <class In>
+__device__ __forceinline__ void finish_per_key8(const BwdArgs& a, int64_t t0, int head, int len, int row0, int w,
+                                                int w8, int grp, int G, int n, int lane, int tid, const f32x4* dl,
+                                                const f32x4* aQ, const f32x4* aKd, const f32x4* aKg, float* hk,
+                                                float* X1, const float* X2, float* Ks, float* Qs, const float* bt,
+                                                const float* dbT, float* brs) {
+    constexpr int SL = 33;                       // row stride of the slice tiles
+    const int H = a.H, ue = a.use_exp2;
+    const float lnb = ue ? 0.6931471805599453f : 1.0f;
+    float* Ksl = Qs;
+    float* Qsl = Qs + BT * SL;
+    float* Gsl = Qs + 2 * BT * SL;
+    float* dGs = Qs + 3 * BT * SL;
+    float* hdK = Ks;                             // [DK] diag(h dh'^T)
+    float* KGs = Ks + DK;                        // [BT][SL] ln b Kg o dKg of the slice
+    float* blk = KGs + BT * SL;                  // [4][64] the waves' block totals of the dg sums
+    const In* kin = reinterpret_cast<const In*>(a.k);
+    const In* qin = reinterpret_cast<const In*>(a.q);
+    const int last = len > 0 ? len - 1 : 0;
+
+    // dL into X1 (strictly lower); diag(h dh'^T) per key over the 16 columns
+    // of each thread group
+    for (int jh = 0; jh < 2; ++jh)
+        for (int r = 0; r < 4; ++r) {
+            const int i = row0 + 4 * G + r, jj = 16 * (2 * grp + jh) + n;
+            X1[i * BTL + jj] = jj < i ? -dl[jh][r] : 0.0f;
+        }
+    for (int m = 0; m < 4; ++m) {
+        float x = hk[m];
+        for (int sft = 1; sft < 16; sft <<= 1) x += __shfl_xor(x, sft, 16);
+        if ((tid & 15) == 0) hdK[(tid >> 4) + 32 * m] = x;
+    }
+    float brow[4] = {0.f, 0.f, 0.f, 0.f};        // k_i . R[dL,K]_i over this lane's keys
+    // the key slices' k, q and g tiles, one slice ahead
+    TileRegs<In, BT, 32> pk, pq;
+    TileRegs<float, BT, 32> pg;
+    auto issue = [&](int d0) {
+        if (tid >= 256) return;
+        pk.issue(kin + (t0 * H + head) * DK + d0, (int64_t)H * DK, len, tid);
+        pq.issue(qin + (t0 * H + head) * DK + d0, (int64_t)H * DK, len, tid);
+        pg.issue(a.g + (t0 * H + head) * DK + d0, (int64_t)H * DK, len, tid);
+    };
+    issue(0);
+
+    // the slice loop stays rolled (its body is large); the slice's two key
+    // tiles of dQd / dKd / dKg are picked out of the register arrays first
+#pragma unroll 1
+    for (int s = 0; s < DK / 32; ++s) {
+        const int d0 = 32 * s;
+        f32x4 sQ, sKd, sKg;                      // this group's key tile of the slice
+        switch (s) {
+#define GDN_PICK(S)                                                \
+    case S:                                                        \
+        sQ = aQ[S]; sKd = aKd[S]; sKg = aKg[S];                    \
+        break;
+            GDN_PICK(0) GDN_PICK(1) GDN_PICK(2) default: GDN_PICK(3)
+#undef GDN_PICK
+        }
+        lds_barrier();                         // X1 written; the previous slice consumed
+        if (tid < 256) {
+            pk.commit(Ksl, SL, tid);
+            pq.commit(Qsl, SL, tid);
+            pg.commit(Gsl, SL, tid);
+        }
+        if (s + 1 < DK / 32) issue(d0 + 32);
+        lds_barrier();
+        // G: running sum down each key column (rows past the chunk end keep G
+        // at its last row) in fp64, rounded once, as the preparation does:
+        // lane l of wave 0 sums column l & 31 over rows 32 (l >> 5) .. +31,
+        // the upper half from the lower half's total
+        if (w8 == 0) {
+            const int c = lane & 31, r0 = 32 * (lane >> 5);
+            float gv[32];
+#pragma unroll
+            for (int r = 0; r < 32; ++r) gv[r] = Gsl[(r0 + r) * SL + c];
+            double half = 0.0;
+#pragma unroll
+            for (int r = 0; r < 32; ++r) half += (double)gv[r];
+            const double lo = __shfl(half, c, 64);
+            double x = lane >= 32 ? lo : 0.0;
+#pragma unroll
+            for (int r = 0; r < 32; ++r) {
+                x += (double)gv[r];
+                Gsl[(r0 + r) * SL + c] = (float)x;
+            }
+        }
+        lds_barrier();
+        {
+            const int c = 16 * grp + n;          // slice column of this lane's key (the group's key tile)
+            f32x4 ra = {0.f, 0.f, 0.f, 0.f}, rp = ra, ca = ra, cp = ra;
+            // The diagonal block joins the factored products below when the
+            // gate falls by at most 2^8 of decay (8 log2 units) inside the
+            // block on every key of the tile: its factors about the reference
+            // rows then stay within 2^8 (the forward preparation's rule).
+            // The stored zeros of dL (strictly lower) and dP (lower with the
+            // diagonal) mask the terms past the diagonal.
+            const float g_lo = w > 0 ? Gsl[(16 * w - 1) * SL + c] : 0.0f;
+            const bool fdiag = __all(g_lo - Gsl[(16 * w + 15) * SL + c] <= (ue ? 8.0f : 5.545177444479562f));
+            // rows of block w against the earlier blocks (and the diagonal
+            // block when factored): reference row 16w - 1, the last one
+            // before the block (the chunk start, G = 0, for block 0)
+            const int rend = 16 * w + (fdiag ? 16 : 0);
+            if (rend > 0) {
+                const float gr = g_lo;
+                for (int k0 = 0; k0 < rend; k0 += 4) {
+                    const int j = k0 + G;
+                    const float b = Ksl[j * SL + c] * fpow(gr - Gsl[j * SL + c], ue);
+                    ra = __builtin_amdgcn_mfma_f32_16x16x4f32(X1[(row0 + n) * BTL + j], b, ra, 0, 0, 0);
+                    rp = __builtin_amdgcn_mfma_f32_16x16x4f32(X2[(row0 + n) * BTL + j], b, rp, 0, 0, 0);
+                }
+                for (int r = 0; r < 4; ++r) {
+                    const float f = fpow(Gsl[(row0 + 4 * G + r) * SL + c] - gr, ue);
+                    ra[r] *= f;
+                    rp[r] *= f;
+                }
+            }
+            // columns of block w against the later blocks (and the diagonal
+            // block when factored): reference row 16w + 15, the block's last
+            const int cbeg = 16 * w + (fdiag ? 0 : 16);
+            if (cbeg < BT) {
+                const int ref = 16 * w + 15;
+                const float gr = Gsl[ref * SL + c];
+                for (int k0 = cbeg; k0 < BT; k0 += 4) {
+                    const int i = k0 + G;
+                    const float f = fpow(Gsl[i * SL + c] - gr, ue);
+                    ca = __builtin_amdgcn_mfma_f32_16x16x4f32(bt[i] * X1[i * BTL + row0 + n], Ksl[i * SL + c] * f, ca,
+                                                             0, 0, 0);
+                    cp = __builtin_amdgcn_mfma_f32_16x16x4f32(X2[i * BTL + row0 + n], Qsl[i * SL + c] * f, cp, 0, 0, 0);
+                }
+                for (int r = 0; r < 4; ++r) {
+                    const float f = fpow(gr - Gsl[(row0 + 4 * G + r) * SL + c], ue);
+                    ca[r] *= f;
+                    cp[r] *= f;
+                }
+            }
+            // otherwise the diagonal block by exponent differences: m <= i
+            // feeds the row products of row i, m >= i the column products of
+            // column i; row m's g, k, q and beta are read once for the lane's
+            // four rows
+            if (!fdiag) {
+                float gi[4];
+                for (int r = 0; r < 4; ++r) gi[r] = Gsl[(row0 + 4 * G + r) * SL + c];
+#pragma unroll 4
+                for (int m = row0; m < row0 + 16; ++m) {
+                    const float gmv = Gsl[m * SL + c], kmv = Ksl[m * SL + c], qmv = Qsl[m * SL + c], bmv = bt[m];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = row0 + 4 * G + r;
+                        const float dd = fpow(m <= i ? gi[r] - gmv : gmv - gi[r], ue);
+                        const float km = kmv * dd;
+                        if (m <= i) {
+                            ra[r] += X1[i * BTL + m] * km;
+                            rp[r] += X2[i * BTL + m] * km;
+                        }
+                        if (m >= i) {
+                            ca[r] += bmv * X1[m * BTL + i] * km;
+                            cp[r] += X2[m * BTL + i] * qmv * dd;
+                        }
+                    }
+                }
+            }
+            // gradients of this lane's rows and key
+            for (int r = 0; r < 4; ++r) {
+                const int i = row0 + 4 * G + r;
+                const float gi = Gsl[i * SL + c];
+                const float e1 = fpow(gi, ue), e2 = fpow(Gsl[last * SL + c] - gi, ue);
+                const float qv = Qsl[i * SL + c], kv = Ksl[i * SL + c];
+                const float dQd = sQ[r], dKd = sKd[r], dKg = sKg[r];
+                const float cs = ca[r] + cp[r];
+                const float dqv = rp[r] + dQd * e1;
+                const float dkv = bt[i] * ra[r] + cs + dKd * e1 + dKg * e2;
+                // the Kg term of dG_i without its - ln b Kg o dKg: that part
+                // cancels G_L's + ln b Kg o dKg for every row from i on and
+                // enters dg as the prefix over the earlier rows (below)
+                dGs[i * SL + c] = lnb * (bt[i] * kv * ra[r] + qv * rp[r] - kv * cs + dQd * qv * e1 + dKd * kv * e1);
+                KGs[i * SL + c] = lnb * dKg * kv * e2;
+                brow[r] += kv * ra[r];
+                if (i < len) {
+                    const int64_t o = ((t0 + i) * H + head) * DK + d0 + c;
+                    a.dq[o] = dqv;
+                    a.dk[o] = dkv;
+                }
+            }
+        }
+        lds_barrier();
+        // dg_j = sum_{i >= j} dG_i + ln b gamma diag(h dh'^T) + sum_{i < j}
+        // ln b Kg o dKg: a reverse sum down each key column (the state
+        // decay's term at the last valid row) and the exclusive prefix of the
+        // Kg terms. Waves w (reverse sums) and w + 4 (prefixes) sum rows
+        // 16w .. +15 of every column in order on lanes 0..31, then start from
+        // the other row blocks' totals.
+        {
+            const int c = lane & 31;
+            const bool rev = grp == 0, act = lane < 32;
+            const float gl = rev ? lnb * fpow(Gsl[last * SL + c], ue) * hdK[d0 + c] : 0.0f;
+            float v[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 16 * w + r;
+                const float x = rev ? dGs[row * SL + c] + (row == last ? gl : 0.0f) : KGs[row * SL + c];
+                v[r] = row < len ? x : 0.0f;
+            }
+            float tot = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tot += v[r];
+            if (act) blk[(4 * grp + w) * 32 + c] = tot;
+            lds_barrier();
+            float acc = 0.0f;
+            for (int w2 = 0; w2 < 4; ++w2)
+                if (rev ? w2 > w : w2 < w) acc += blk[(4 * grp + w2) * 32 + c];
+            if (act && rev) {
+#pragma unroll
+                for (int r = 15; r >= 0; --r) {
+                    acc += v[r];
+                    dGs[(16 * w + r) * SL + c] = acc;
+                }
+            } else if (act) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    KGs[(16 * w + r) * SL + c] = acc;
+                    acc += v[r];
+                }
+            }
+        }
+        lds_barrier();
+        for (int e = tid; e < BT * 32; e += 512) {
+            const int r = e >> 5, c = e & 31;
+            if (r < len) a.dg[((t0 + r) * H + head) * DK + d0 + c] = dGs[r * SL + c] + KGs[r * SL + c];
+        }
+    }
+    // dbeta: the row term summed over the 16 lanes of each group, added to the
+    // column term of the same row (each row has one writer)
+    for (int r = 0; r < 4; ++r)
+        for (int sft = 1; sft < 16; sft <<= 1) brow[r] += __shfl_xor(brow[r], sft, 16);
+    if (n == 0)
+        for (int r = 0; r < 4; ++r) brs[grp * BT + row0 + 4 * G + r] = brow[r];
+    lds_barrier();
+    if (tid < len) a.dbeta[(t0 + tid) * H + head] = dbT[tid] + brs[tid] + brs[BT + tid];
+}
+
 template <class In, bool PK>
 __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) float Ks[BT * BKL];
@@ -1011,6 +1256,224 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
             a.dbeta[(t0 + lane) * H + head] = dbT[lane];
         }
     }
+}
+
+// Per-key per-chunk gradients at eight waves, two per SIMD. Waves w and
+// w + 4 share token rows 16w .. +15: group 0 (waves 0..3) forms Y and v_new
+// and accumulates dP, group 1 forms dvn and Z (= dV) and accumulates dTb,
+// and each accumulates dQd, dKg and dKd for key tiles 2jj + group (jj =
+// 0..3), the tiles its waves take in the finish. Waves 0..3 stage the value
+// tiles.
+template <class In>
+__global__ __launch_bounds__(512, 1) void bwd_grad_kernel_pk(BwdArgs a) {
+    __shared__ __attribute__((aligned(16))) float Ks[BT * BKL];
+    __shared__ __attribute__((aligned(16))) float Qs[BT * BKL];
+    __shared__ __attribute__((aligned(16))) float Ts[BT * BTL];     // T
+    __shared__ __attribute__((aligned(16))) float Ps[BT * BTL];
+    __shared__ float bt[BT];
+    // value-tile buffers, reused as two 64 x 64 scratch tiles by the finish
+    __shared__ __attribute__((aligned(16))) float tb[2 * DK * VTL + 6 * BT * VTL];
+    __shared__ float dbT[BT], brs[2 * BT];
+    float* Hs = tb;                      // h      [key][col]
+    float* DHs = Hs + DK * VTL;          // dh'    [key][col]
+    float* Vs = DHs + DK * VTL;          // v      [row][col]
+    float* DOs = Vs + BT * VTL;          // dO
+    float* DVs = DOs + BT * VTL;         // dvn
+    float* Ys = DVs + BT * VTL;          // Y
+    float* VNs = Ys + BT * VTL;          // v_new
+    float* Zs = VNs + BT * VTL;          // Z
+    float* X1 = tb;                      // finish: 64 x 64 scratch
+    float* X2 = tb + BT * BTL;
+
+    const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
+    const int w8 = __builtin_amdgcn_readfirstlane(tid >> 6), w = w8 & 3, grp = w8 >> 2;
+    const bool ld = tid < 256;                   // the threads that stage tiles
+    const int ci = blockIdx.x, head = blockIdx.y, H = a.H;
+    int u, cc;
+    chunk_of(a.um, ci, u, cc);
+    if (u < 0) return;
+    const UnitInfo ui = unit_info(a.um, u);
+    const int64_t t0 = ui.start + (int64_t)cc * BT;
+    int len = ui.len - cc * BT;
+    len = len < 0 ? 0 : (len > BT ? BT : len);
+    const int64_t ch = (int64_t)ci * H + head;
+    const In* vin = reinterpret_cast<const In*>(a.v);
+    const In* dout = reinterpret_cast<const In*>(a.dout);
+
+    TileRegs<float, DK, VT> ph, pdh;
+    TileRegs<In, BT, VT> pv, pdo;
+    auto prefetch = [&](int vt) {
+        if (!ld) return;
+        const int vc0 = vt * VT;
+        ph.issue(a.h + ch * DK * DV + vc0, DV, DK, tid);
+        pdh.issue(a.dH + ch * DK * DV + vc0, DV, DK, tid);
+        pv.issue(vin + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, tid);
+        pdo.issue(dout + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, tid);
+    };
+    {
+        // k b^G (for Y) in Ks, T, k b^{G_L - G} (for dvn) in Qs and P, all
+        // four loads in flight together; q, k and G come in key slices in
+        // the finish
+        TileRegs<float, BT, DK> rkd, rkg;
+        TileRegs<float, BT, BT> rt, rp;
+        prefetch(0);
+        if (ld) {
+            rkd.issue(reinterpret_cast<const float*>(a.ws.kd) + ch * (BT * DK), DK, BT, tid);
+            rt.issue(reinterpret_cast<const float*>(a.ws.Tm) + ch * (BT * BT), BT, BT, tid);
+            rkg.issue(reinterpret_cast<const float*>(a.ws.kg) + ch * (BT * DK), DK, BT, tid);
+            rp.issue(reinterpret_cast<const float*>(a.ws.P) + ch * (BT * BT), BT, BT, tid);
+        }
+        if (tid < BT) bt[tid] = tid < len ? ldf(reinterpret_cast<const In*>(a.beta), (t0 + tid) * H + head) : 0.0f;
+        if (ld) {
+            rkd.commit(Ks, BKL, tid);
+            rt.commit(Ts, BTL, tid);
+            rkg.commit(Qs, BKL, tid);
+            rp.commit(Ps, BTL, tid);
+        }
+        lds_barrier();
+    }
+    const int row0 = 16 * w;
+
+    // MFMA operands of this wave's rows, read once for all value tiles.
+    // Group 0: Tb[row0 + n][4q + G] (nonzero for 4q <= row0 + 15) and the Kd
+    // row; group 1: Tb[4q + G][row0 + n] and P[4q + G][row0 + n] (nonzero for
+    // 4q >= row0) and the Kg row.
+    float t1[16], pc[16];
+    f32x4 kx[8];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int k = 4 * q + G;
+        t1[q] = grp == 0 ? Ts[(row0 + n) * BTL + k] * bt[k] : Ts[k * BTL + row0 + n] * bt[row0 + n];
+        pc[q] = grp == 0 ? 0.0f : Ps[k * BTL + row0 + n];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        kx[q] = *reinterpret_cast<const f32x4*>((grp == 0 ? Ks : Qs) + (row0 + n) * BKL + 16 * q + 4 * G);
+
+    f32x4 aPT[4], aQ[4], aKg[4], aKd[4];         // dP (group 0) or dTb (group 1); key tiles 2jj + grp
+    for (int j = 0; j < 4; ++j) {
+        aPT[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        aQ[j] = aPT[j];
+        aKg[j] = aPT[j];
+        aKd[j] = aPT[j];
+    }
+    float hk[4] = {0.f, 0.f, 0.f, 0.f};         // per key: keys (tid >> 4) + 32m, column tid & 15
+    for (int vt = 0; vt < DV / VT; ++vt) {
+        const int vc0 = vt * VT;
+        lds_barrier();                           // the previous tile's buffers are consumed
+        if (ld) {
+            ph.commit(Hs, VTL, tid);
+            pdh.commit(DHs, VTL, tid);
+            pv.commit(Vs, VTL, tid);
+            pdo.commit(DOs, VTL, tid);
+        }
+        lds_barrier();
+        if (vt + 1 < DV / VT) prefetch(vt + 1);
+#pragma unroll
+        for (int m = 0; m < DK * VT / 512; ++m) {
+            const int e = tid + 512 * m, key = e / VT, cl = e - key * VT;
+            hk[m] += Hs[key * VTL + cl] * DHs[key * VTL + cl];
+        }
+        if (grp == 0) {
+            // Y = V - Kd h, rows of this wave
+            f32x4 kh = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    kh = __builtin_amdgcn_mfma_f32_16x16x4f32(kx[q][e], Hs[(16 * q + 4 * G + e) * VTL + n], kh, 0, 0, 0);
+            for (int r = 0; r < 4; ++r) {
+                const int row = row0 + 4 * G + r;
+                Ys[row * VTL + n] = Vs[row * VTL + n] - kh[r];
+            }
+        } else {
+            // dvn = Kg dh' + scale P^T dO, rows of this wave (P[j][i] = 0 for j < i)
+            f32x4 kd = {0.f, 0.f, 0.f, 0.f}, pd = kd;
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    kd = __builtin_amdgcn_mfma_f32_16x16x4f32(kx[q][e], DHs[(16 * q + 4 * G + e) * VTL + n], kd, 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                if (4 * q >= row0)
+                    pd = __builtin_amdgcn_mfma_f32_16x16x4f32(pc[q], DOs[(4 * q + G) * VTL + n], pd, 0, 0, 0);
+            for (int r = 0; r < 4; ++r) DVs[(row0 + 4 * G + r) * VTL + n] = kd[r] + a.scale * pd[r];
+        }
+        lds_barrier();
+        if (grp == 0) {
+            // v_new = Tb Y, rows of this wave
+            f32x4 vn = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                if (4 * q <= row0 + 15) vn = __builtin_amdgcn_mfma_f32_16x16x4f32(t1[q], Ys[(4 * q + G) * VTL + n], vn, 0, 0, 0);
+            for (int r = 0; r < 4; ++r) VNs[(row0 + 4 * G + r) * VTL + n] = vn[r];
+        } else {
+            // Z = Tb^T dvn = dV, rows of this wave
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                if (4 * q >= row0) z = __builtin_amdgcn_mfma_f32_16x16x4f32(t1[q], DVs[(4 * q + G) * VTL + n], z, 0, 0, 0);
+            for (int r = 0; r < 4; ++r) {
+                const int row = row0 + 4 * G + r;
+                Zs[row * VTL + n] = z[r];
+                if (row < len) a.dv[((t0 + row) * H + head) * DV + vc0 + n] = z[r];
+            }
+        }
+        lds_barrier();
+        // accumulate over this tile's columns (both operands column-contiguous)
+        for (int j = 0; j < 4; ++j) {
+            if (grp == 0) mm_rows16(aPT[j], DOs + row0 * VTL, VNs + 16 * j * VTL, a.scale, G, n);
+            else mm_rows16(aPT[j], DVs + row0 * VTL, Ys + 16 * j * VTL, 1.0f, G, n);
+        }
+        for (int jj = 0; jj < 4; ++jj) {
+            const int j = 2 * jj + grp;
+            mm_rows16(aQ[jj], DOs + row0 * VTL, Hs + 16 * j * VTL, a.scale, G, n);
+            mm_rows16(aKg[jj], VNs + row0 * VTL, DHs + 16 * j * VTL, 1.0f, G, n);
+            mm_rows16(aKd[jj], Zs + row0 * VTL, Hs + 16 * j * VTL, -1.0f, G, n);
+        }
+    }
+    lds_barrier();
+
+    // ---- finish. dTb (group 1) to X1, dP (group 0) to X2, lower incl. diagonal
+    {
+        float* X = grp == 0 ? X2 : X1;
+        for (int j = 0; j < 4; ++j)
+            for (int r = 0; r < 4; ++r) {
+                const int i = row0 + 4 * G + r, jj = 16 * j + n;
+                X[i * BTL + jj] = jj <= i ? aPT[j][r] : 0.0f;
+            }
+    }
+    lds_barrier();
+    // dbeta from Tb = T diag(beta): column sums of dTb o T
+    if (tid < BT) {
+        float sc = 0.0f;
+        for (int i = tid; i < BT; ++i) sc += X1[i * BTL + tid] * Ts[i * BTL + tid];
+        dbT[tid] = sc;
+    }
+    // M1 = dT T^T with dT = dTb diag(beta), rows of this wave, column blocks 2 grp, 2 grp + 1
+    f32x4 m1[2];
+    for (int jh = 0; jh < 2; ++jh) {
+        const int j = 2 * grp + jh;
+        m1[jh] = f32x4{0.f, 0.f, 0.f, 0.f};
+        mmf<BT>(m1[jh], [&](int m, int k) { return X1[(row0 + m) * BTL + k] * bt[k]; },
+                [&](int k, int nn) { return Ts[(16 * j + nn) * BTL + k]; }, G, n);
+    }
+    lds_barrier();
+    for (int jh = 0; jh < 2; ++jh)
+        for (int r = 0; r < 4; ++r) X1[(row0 + 4 * G + r) * BTL + 16 * (2 * grp + jh) + n] = m1[jh][r];
+    lds_barrier();
+    // dL = -T^T M1 (strictly lower), rows of this wave, the same column blocks
+    f32x4 dl[2];
+    for (int jh = 0; jh < 2; ++jh) {
+        const int j = 2 * grp + jh;
+        dl[jh] = f32x4{0.f, 0.f, 0.f, 0.f};
+        mmf<BT>(dl[jh], [&](int m, int k) { return Ts[k * BTL + row0 + m]; },
+                [&](int k, int nn) { return X1[k * BTL + 16 * j + nn]; }, G, n);
+    }
+    lds_barrier();
+    finish_per_key8<In>(a, t0, head, len, row0, w, w8, grp, G, n, lane, tid, dl, aQ, aKd, aKg, hk, X1, X2, Ks, Qs,
+                        bt, dbT, brs);
 }
 
 // ------------------------------------------------------------------ reverse state pass, per-key gate
@@ -1935,9 +2398,9 @@ hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* d
         dim3 grid(p.um.n_chunks, p.H);
         if (p.per_key) {
             if (p.dtype == 1) {
-                hipLaunchKernelGGL((bwd_grad_kernel<bf16, true>), grid, dim3(256), 0, s, a);
+                hipLaunchKernelGGL(bwd_grad_kernel_pk<bf16>, grid, dim3(512), 0, s, a);
             } else {
-                hipLaunchKernelGGL((bwd_grad_kernel<float, true>), grid, dim3(256), 0, s, a);
+                hipLaunchKernelGGL(bwd_grad_kernel_pk<float>, grid, dim3(512), 0, s, a);
             }
         } else {
             if (p.dtype == 1) hipLaunchKernelGGL(bwd_grad_kernel_h, grid, dim3(256), 0, s, a, dHw);
