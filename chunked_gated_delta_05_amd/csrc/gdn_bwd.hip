@@ -422,13 +422,15 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ per-chunk gradients
-// fp32 operands: fp32 inputs, and the per-key gate at either input dtype.
-// One workgroup of four waves per (chunk, head); wave w owns token rows
-// 16w .. 16w+15 of every row-indexed product. The value columns are visited
-// in 16-column tiles: each recomputes Y = V - Kd h and v_new = Tb Y, writes
-// dV = Z = Tb^T dvn, and accumulates over its columns dP, dTb (64 x 64) and
-// dQd, dKg, dKd (64 x 128) in registers. The finish turns dTb into dL through
-// T, and assembles dq, dk, dbeta and the gate gradients.
+// fp32 operands: fp32 inputs with a scalar gate (bwd_grad_kernel), and the
+// per-key gate at either input dtype (bwd_grad_kernel_pk, eight waves). The
+// value columns are visited in 16-column tiles: each recomputes
+// Y = V - Kd h and v_new = Tb Y, writes dV = Z = Tb^T dvn, and accumulates
+// over its columns dP, dTb (64 x 64) and dQd, dKg, dKd (64 x 128) in
+// registers. The finish turns dTb into dL through T, and assembles dq, dk,
+// dbeta and the gate gradients. In bwd_grad_kernel one workgroup of four
+// waves per (chunk, head); wave w owns token rows 16w .. 16w+15 of every
+// row-indexed product.
 constexpr int VT = 16;          // value columns per tile
 constexpr int VTL = VT + 4;     // row stride: 16-byte aligned rows; rows 80 bytes apart hit distinct granules
 
@@ -444,256 +446,15 @@ __device__ __forceinline__ void mm_rows16(f32x4& acc, const float* A, const floa
     for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sa * x[e], y[e], acc, 0, 0, 0);
 }
 
-// The per-key finish of bwd_grad_kernel. On entry: dl = dL rows of this wave
-// (negated), X2 = dP (lower with the diagonal), dbT = the column term of
-// dbeta, aQ / aKd / aKg = dQd / dKd / dKg in accumulator layout (rows
-// row0 + 4G + r, key 16j + n), hk = per-thread shares of diag(h dh'^T).
-// Ks and Qs are free: the key slices (k, q, G, dG of 32 keys) live in Qs,
-// the per-key sums in Ks. Wave w owns token block w of both the row and the
-// column products.
-template <class In>
-__device__ __forceinline__ void finish_per_key(const BwdArgs& a, int64_t t0, int head, int len, int row0, int w,
-                                               int G, int n, int lane, int tid, const f32x4* dl, const f32x4* aQ,
-                                               const f32x4* aKd, const f32x4* aKg, float* hk, float* X1,
-                                               const float* X2, float* Ks, float* Qs, const float* bt, float* dbT) {
-    constexpr int SL = 33;                       // row stride of the slice tiles
-    const int H = a.H, ue = a.use_exp2;
-    const float lnb = ue ? 0.6931471805599453f : 1.0f;
-    float* Ksl = Qs;
-    float* Qsl = Qs + BT * SL;
-    float* Gsl = Qs + 2 * BT * SL;
-    float* dGs = Qs + 3 * BT * SL;
-    float* hdK = Ks;                             // [DK] diag(h dh'^T)
-    float* KGs = Ks + DK;                        // [BT][SL] ln b Kg o dKg of the slice
-    float* blk = KGs + BT * SL;                  // [4][64] the waves' block totals of the dg sums
-    const In* kin = reinterpret_cast<const In*>(a.k);
-    const In* qin = reinterpret_cast<const In*>(a.q);
-    const int last = len > 0 ? len - 1 : 0;
-
-    // dL into X1 (strictly lower); diag(h dh'^T) per key over the 16 columns
-    // of each thread group
-    for (int j = 0; j < 4; ++j)
-        for (int r = 0; r < 4; ++r) {
-            const int i = row0 + 4 * G + r, jj = 16 * j + n;
-            X1[i * BTL + jj] = jj < i ? -dl[j][r] : 0.0f;
-        }
-    for (int m = 0; m < 8; ++m) {
-        float x = hk[m];
-        for (int sft = 1; sft < 16; sft <<= 1) x += __shfl_xor(x, sft, 16);
-        if ((tid & 15) == 0) hdK[(tid >> 4) + 16 * m] = x;
-    }
-    float brow[4] = {0.f, 0.f, 0.f, 0.f};        // k_i . R[dL,K]_i over this lane's keys
-    // the key slices' k, q and g tiles, one slice ahead
-    TileRegs<In, BT, 32> pk, pq;
-    TileRegs<float, BT, 32> pg;
-    auto issue = [&](int d0) {
-        pk.issue(kin + (t0 * H + head) * DK + d0, (int64_t)H * DK, len, tid);
-        pq.issue(qin + (t0 * H + head) * DK + d0, (int64_t)H * DK, len, tid);
-        pg.issue(a.g + (t0 * H + head) * DK + d0, (int64_t)H * DK, len, tid);
-    };
-    issue(0);
-
-    // the slice loop stays rolled (its body is large); the slice's two key
-    // tiles of dQd / dKd / dKg are picked out of the register arrays first
-#pragma unroll 1
-    for (int s = 0; s < DK / 32; ++s) {
-        const int d0 = 32 * s;
-        f32x4 sQ[2], sKd[2], sKg[2];
-        switch (s) {
-#define GDN_PICK(S)                                                                      \
-    case S:                                                                              \
-        sQ[0] = aQ[2 * S]; sQ[1] = aQ[2 * S + 1]; sKd[0] = aKd[2 * S]; sKd[1] = aKd[2 * S + 1]; \
-        sKg[0] = aKg[2 * S]; sKg[1] = aKg[2 * S + 1];                                   \
-        break;
-            GDN_PICK(0) GDN_PICK(1) GDN_PICK(2) default: GDN_PICK(3)
-#undef GDN_PICK
-        }
-        lds_barrier();                         // X1 written; the previous slice consumed
-        pk.commit(Ksl, SL, tid);
-        pq.commit(Qsl, SL, tid);
-        pg.commit(Gsl, SL, tid);
-        if (s + 1 < DK / 32) issue(d0 + 32);
-        lds_barrier();
-        // G: running sum down each key column (rows past the chunk end keep G
-        // at its last row) in fp64, rounded once, as the preparation does:
-        // lane l of wave 0 sums column l & 31 over rows 32 (l >> 5) .. +31,
-        // the upper half from the lower half's total
-        if (w == 0) {
-            const int c = lane & 31, r0 = 32 * (lane >> 5);
-            float gv[32];
-#pragma unroll
-            for (int r = 0; r < 32; ++r) gv[r] = Gsl[(r0 + r) * SL + c];
-            double half = 0.0;
-#pragma unroll
-            for (int r = 0; r < 32; ++r) half += (double)gv[r];
-            const double lo = __shfl(half, c, 64);
-            double x = lane >= 32 ? lo : 0.0;
-#pragma unroll
-            for (int r = 0; r < 32; ++r) {
-                x += (double)gv[r];
-                Gsl[(r0 + r) * SL + c] = (float)x;
-            }
-        }
-        lds_barrier();
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            const int c = 16 * kt + n;           // slice column of this lane's key
-            f32x4 ra = {0.f, 0.f, 0.f, 0.f}, rp = ra, ca = ra, cp = ra;
-            // The diagonal block joins the factored products below when the
-            // gate falls by at most 2^8 of decay (8 log2 units) inside the
-            // block on every key of the tile: its factors about the reference
-            // rows then stay within 2^8 (the forward preparation's rule).
-            // The stored zeros of dL (strictly lower) and dP (lower with the
-            // diagonal) mask the terms past the diagonal.
-            const float g_lo = w > 0 ? Gsl[(16 * w - 1) * SL + c] : 0.0f;
-            const bool fdiag = __all(g_lo - Gsl[(16 * w + 15) * SL + c] <= (ue ? 8.0f : 5.545177444479562f));
-            // rows of block w against the earlier blocks (and the diagonal
-            // block when factored): reference row 16w - 1, the last one
-            // before the block (the chunk start, G = 0, for block 0)
-            const int rend = 16 * w + (fdiag ? 16 : 0);
-            if (rend > 0) {
-                const float gr = g_lo;
-                for (int k0 = 0; k0 < rend; k0 += 4) {
-                    const int j = k0 + G;
-                    const float b = Ksl[j * SL + c] * fpow(gr - Gsl[j * SL + c], ue);
-                    ra = __builtin_amdgcn_mfma_f32_16x16x4f32(X1[(row0 + n) * BTL + j], b, ra, 0, 0, 0);
-                    rp = __builtin_amdgcn_mfma_f32_16x16x4f32(X2[(row0 + n) * BTL + j], b, rp, 0, 0, 0);
-                }
-                for (int r = 0; r < 4; ++r) {
-                    const float f = fpow(Gsl[(row0 + 4 * G + r) * SL + c] - gr, ue);
-                    ra[r] *= f;
-                    rp[r] *= f;
-                }
-            }
-            // columns of block w against the later blocks (and the diagonal
-            // block when factored): reference row 16w + 15, the block's last
-            const int cbeg = 16 * w + (fdiag ? 0 : 16);
-            if (cbeg < BT) {
-                const int ref = 16 * w + 15;
-                const float gr = Gsl[ref * SL + c];
-                for (int k0 = cbeg; k0 < BT; k0 += 4) {
-                    const int i = k0 + G;
-                    const float f = fpow(Gsl[i * SL + c] - gr, ue);
-                    ca = __builtin_amdgcn_mfma_f32_16x16x4f32(bt[i] * X1[i * BTL + row0 + n], Ksl[i * SL + c] * f, ca,
-                                                             0, 0, 0);
-                    cp = __builtin_amdgcn_mfma_f32_16x16x4f32(X2[i * BTL + row0 + n], Qsl[i * SL + c] * f, cp, 0, 0, 0);
-                }
-                for (int r = 0; r < 4; ++r) {
-                    const float f = fpow(gr - Gsl[(row0 + 4 * G + r) * SL + c], ue);
-                    ca[r] *= f;
-                    cp[r] *= f;
-                }
-            }
-            // otherwise the diagonal block by exponent differences: m <= i
-            // feeds the row products of row i, m >= i the column products of
-            // column i; row m's g, k, q and beta are read once for the lane's
-            // four rows
-            if (!fdiag) {
-                float gi[4];
-                for (int r = 0; r < 4; ++r) gi[r] = Gsl[(row0 + 4 * G + r) * SL + c];
-#pragma unroll 4
-                for (int m = row0; m < row0 + 16; ++m) {
-                    const float gmv = Gsl[m * SL + c], kmv = Ksl[m * SL + c], qmv = Qsl[m * SL + c], bmv = bt[m];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int i = row0 + 4 * G + r;
-                        const float dd = fpow(m <= i ? gi[r] - gmv : gmv - gi[r], ue);
-                        const float km = kmv * dd;
-                        if (m <= i) {
-                            ra[r] += X1[i * BTL + m] * km;
-                            rp[r] += X2[i * BTL + m] * km;
-                        }
-                        if (m >= i) {
-                            ca[r] += bmv * X1[m * BTL + i] * km;
-                            cp[r] += X2[m * BTL + i] * qmv * dd;
-                        }
-                    }
-                }
-            }
-            // gradients of this lane's rows and key
-            for (int r = 0; r < 4; ++r) {
-                const int i = row0 + 4 * G + r;
-                const float gi = Gsl[i * SL + c];
-                const float e1 = fpow(gi, ue), e2 = fpow(Gsl[last * SL + c] - gi, ue);
-                const float qv = Qsl[i * SL + c], kv = Ksl[i * SL + c];
-                const float dQd = sQ[kt][r], dKd = sKd[kt][r], dKg = sKg[kt][r];
-                const float cs = ca[r] + cp[r];
-                const float dqv = rp[r] + dQd * e1;
-                const float dkv = bt[i] * ra[r] + cs + dKd * e1 + dKg * e2;
-                // the Kg term of dG_i without its - ln b Kg o dKg: that part
-                // cancels G_L's + ln b Kg o dKg for every row from i on and
-                // enters dg as the prefix over the earlier rows (below)
-                dGs[i * SL + c] = lnb * (bt[i] * kv * ra[r] + qv * rp[r] - kv * cs + dQd * qv * e1 + dKd * kv * e1);
-                KGs[i * SL + c] = lnb * dKg * kv * e2;
-                brow[r] += kv * ra[r];
-                if (i < len) {
-                    const int64_t o = ((t0 + i) * H + head) * DK + d0 + c;
-                    a.dq[o] = dqv;
-                    a.dk[o] = dkv;
-                }
-            }
-        }
-        lds_barrier();
-        // dg_j = sum_{i >= j} dG_i + ln b gamma diag(h dh'^T) + sum_{i < j}
-        // ln b Kg o dKg: a reverse sum down each key column (the state
-        // decay's term at the last valid row) and the exclusive prefix of the
-        // Kg terms. Wave w sums rows 16w .. +15 of every column in order
-        // (lanes 0..31 the reverse sums, lanes 32..63 the prefixes), then
-        // starts from the other waves' block totals.
-        {
-            const int c = lane & 31;
-            const bool rev = lane < 32;
-            const float gl = rev ? lnb * fpow(Gsl[last * SL + c], ue) * hdK[d0 + c] : 0.0f;
-            float v[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = 16 * w + r;
-                const float x = rev ? dGs[row * SL + c] + (row == last ? gl : 0.0f) : KGs[row * SL + c];
-                v[r] = row < len ? x : 0.0f;
-            }
-            float tot = 0.0f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) tot += v[r];
-            blk[w * 64 + lane] = tot;
-            lds_barrier();
-            float acc = 0.0f;
-            for (int w2 = 0; w2 < 4; ++w2)
-                if (rev ? w2 > w : w2 < w) acc += blk[w2 * 64 + lane];
-            if (rev) {
-#pragma unroll
-                for (int r = 15; r >= 0; --r) {
-                    acc += v[r];
-                    dGs[(16 * w + r) * SL + c] = acc;
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    KGs[(16 * w + r) * SL + c] = acc;
-                    acc += v[r];
-                }
-            }
-        }
-        lds_barrier();
-        for (int e = tid; e < BT * 32; e += 256) {
-            const int r = e >> 5, c = e & 31;
-            if (r < len) a.dg[((t0 + r) * H + head) * DK + d0 + c] = dGs[r * SL + c] + KGs[r * SL + c];
-        }
-    }
-    // dbeta: the row term summed over the 16 lanes of each group, added to the
-    // column term of the same row (each row has one writer)
-    for (int r = 0; r < 4; ++r)
-        for (int sft = 1; sft < 16; sft <<= 1) brow[r] += __shfl_xor(brow[r], sft, 16);
-    if (n == 0)
-        for (int r = 0; r < 4; ++r) dbT[row0 + 4 * G + r] += brow[r];
-    lds_barrier();
-    if (tid < len) a.dbeta[(t0 + tid) * H + head] = dbT[tid];
-}
-
-// The per-key finish at eight waves: wave w8 takes token block w = w8 & 3 and
-// the key tile grp = w8 >> 2 of every 32-key slice (the half of the slice's
-// dQd / dKd / dKg tiles its group accumulated); dl holds its rows of dL for
-// column blocks 2 grp, 2 grp + 1. The two groups' dbeta row terms meet in
-// brs.
+// The per-key finish of bwd_grad_kernel_pk. On entry: dl = dL of this wave's
+// rows (negated) for column blocks 2 grp, 2 grp + 1, X2 = dP (lower with the
+// diagonal), dbT = the column term of dbeta, aQ / aKd / aKg = the wave's
+// dQd / dKd / dKg tiles in accumulator layout (rows row0 + 4G + r, key tile
+// 2s + grp of slice s), hk = per-thread shares of diag(h dh'^T). Ks and Qs
+// are free: the key slices (k, q, G, dG of 32 keys) live in Qs, the per-key
+// sums in Ks. Wave w8 takes token block w = w8 & 3 and the key tile
+// grp = w8 >> 2 of every slice, for both the row and the column products;
+// the two groups' dbeta row terms meet in brs.
 template <class In>
 __device__ __forceinline__ void finish_per_key8(const BwdArgs& a, int64_t t0, int head, int len, int row0, int w,
                                                 int w8, int grp, int G, int n, int lane, int tid, const f32x4* dl,
@@ -934,8 +695,8 @@ __device__ __forceinline__ void finish_per_key8(const BwdArgs& a, int64_t t0, in
     if (tid < len) a.dbeta[(t0 + tid) * H + head] = dbT[tid] + brs[tid] + brs[BT + tid];
 }
 
-template <class In, bool PK>
 __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
+    using In = float;
     __shared__ __attribute__((aligned(16))) float Ks[BT * BKL];
     __shared__ __attribute__((aligned(16))) float Qs[BT * BKL];
     __shared__ __attribute__((aligned(16))) float Ts[BT * BTL];     // T
@@ -983,29 +744,10 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
         pdh.issue(a.dH + ch * DK * DV + vc0, DV, DK, tid);
         pv.issue(vin + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, tid);
         pdo.issue(dout + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, tid);
-        if (!PK) pdv.issue(a.dVN + ch * BT * DV + vc0, DV, BT, tid);
+        pdv.issue(a.dVN + ch * BT * DV + vc0, DV, BT, tid);
     };
-    if (PK) {
-        // per key: k b^G (for Y) in Ks, T and beta, and for dvn k b^{G_L - G}
-        // in Qs and P in Ps (all four loads in flight together); q, k and G
-        // come in key slices in the finish
-        TileRegs<float, BT, DK> rkd, rkg;
-        TileRegs<float, BT, BT> rt, rp;
-        prefetch(0);
-        rkd.issue(reinterpret_cast<const float*>(a.ws.kd) + ch * (BT * DK), DK, BT, tid);
-        rt.issue(reinterpret_cast<const float*>(a.ws.Tm) + ch * (BT * BT), BT, BT, tid);
-        rkg.issue(reinterpret_cast<const float*>(a.ws.kg) + ch * (BT * DK), DK, BT, tid);
-        rp.issue(reinterpret_cast<const float*>(a.ws.P) + ch * (BT * BT), BT, BT, tid);
-        if (tid < BT) bt[tid] = tid < len ? ldf(reinterpret_cast<const In*>(a.beta), (t0 + tid) * H + head) : 0.0f;
-        rkd.commit(Ks, BKL, tid);
-        rt.commit(Ts, BTL, tid);
-        rkg.commit(Qs, BKL, tid);
-        rp.commit(Ps, BTL, tid);
-        lds_barrier();
-    } else {
-        load_chunk<In, false>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, gm, bt, tid);
-        prefetch(0);
-    }
+    load_chunk<In, false>(a, t0, ch, head, len, Ks, Qs, Ts, Ps, gm, bt, tid);
+    prefetch(0);
     if (tid < BT) {
         rowG[tid] = 0.0f;
         rowK[tid] = 0.0f;
@@ -1015,28 +757,22 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
 
     // MFMA operands of this wave's rows, read once for all value tiles:
     // Tb[row0 + n][4q + G] (nonzero for 4q <= row0 + 15), Tb[4q + G][row0 + n]
-    // (nonzero for 4q >= row0), the Ks row row0 + n in 16-byte groups, and per
-    // key P[4q + G][row0 + n] (nonzero for 4q >= row0) and the Kg row
-    float tbr[16], tbc[16], pc[16];
-    f32x4 kdr[8], kgr[8];
+    // (nonzero for 4q >= row0) and the Ks row row0 + n in 16-byte groups
+    float tbr[16], tbc[16];
+    f32x4 kdr[8];
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         const int k = 4 * q + G;
         tbr[q] = Ts[(row0 + n) * BTL + k] * bt[k];
         tbc[q] = Ts[k * BTL + row0 + n] * bt[row0 + n];
-        pc[q] = PK ? Ps[k * BTL + row0 + n] : 0.0f;
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        kdr[q] = *reinterpret_cast<const f32x4*>(Ks + (row0 + n) * BKL + 16 * q + 4 * G);
-        kgr[q] = PK ? *reinterpret_cast<const f32x4*>(Qs + (row0 + n) * BKL + 16 * q + 4 * G) : kdr[q];
-    }
+    for (int q = 0; q < 8; ++q) kdr[q] = *reinterpret_cast<const f32x4*>(Ks + (row0 + n) * BKL + 16 * q + 4 * G);
 
     f32x4 aP[4], aT[4], aQ[8], aKg[8], aKd[8];
     for (int j = 0; j < 4; ++j) { aP[j] = f32x4{0.f, 0.f, 0.f, 0.f}; aT[j] = aP[j]; }
     for (int j = 0; j < 8; ++j) { aQ[j] = f32x4{0.f, 0.f, 0.f, 0.f}; aKg[j] = aQ[j]; aKd[j] = aQ[j]; }
     float hdh = 0.0f;     // this thread's share of sum(h o dh')
-    float hk[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // per key: keys (tid >> 4) + 16m, column tid & 15
     for (int vt = 0; vt < DV / VT; ++vt) {
         const int vc0 = vt * VT;
         lds_barrier();                           // the previous tile's buffers are consumed
@@ -1044,17 +780,15 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
         pdh.commit(DHs, VTL, tid);
         pv.commit(Vs, VTL, tid);
         pdo.commit(DOs, VTL, tid);
-        if (!PK) pdv.commit(DVs, VTL, tid);
+        pdv.commit(DVs, VTL, tid);
         lds_barrier();
         if (vt + 1 < DV / VT) prefetch(vt + 1);
 #pragma unroll
         for (int m = 0; m < DK * VT / 256; ++m) {
             const int e = tid + 256 * m, key = e / VT, cl = e - key * VT;
-            const float x = Hs[key * VTL + cl] * DHs[key * VTL + cl];
-            if (PK) hk[m] += x;
-            else hdh += x;
+            hdh += Hs[key * VTL + cl] * DHs[key * VTL + cl];
         }
-        // Y = V - Kd h, rows of this wave (scalar gate: Kd h = b^G (K h))
+        // Y = V - Kd h, rows of this wave (Kd h = b^G (K h))
         {
             f32x4 kh = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1064,22 +798,8 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
                     kh = __builtin_amdgcn_mfma_f32_16x16x4f32(kdr[q][e], Hs[(16 * q + 4 * G + e) * VTL + n], kh, 0, 0, 0);
             for (int r = 0; r < 4; ++r) {
                 const int row = row0 + 4 * G + r;
-                Ys[row * VTL + n] = Vs[row * VTL + n] - (PK ? kh[r] : bG(row) * kh[r]);
+                Ys[row * VTL + n] = Vs[row * VTL + n] - bG(row) * kh[r];
             }
-        }
-        if (PK) {
-            // dvn = Kg dh' + scale P^T dO, rows of this wave (P[j][i] = 0 for j < i)
-            f32x4 kd = {0.f, 0.f, 0.f, 0.f}, pd = kd;
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    kd = __builtin_amdgcn_mfma_f32_16x16x4f32(kgr[q][e], DHs[(16 * q + 4 * G + e) * VTL + n], kd, 0, 0, 0);
-#pragma unroll
-            for (int q = 0; q < 16; ++q)
-                if (4 * q >= row0)
-                    pd = __builtin_amdgcn_mfma_f32_16x16x4f32(pc[q], DOs[(4 * q + G) * VTL + n], pd, 0, 0, 0);
-            for (int r = 0; r < 4; ++r) DVs[(row0 + 4 * G + r) * VTL + n] = kd[r] + a.scale * pd[r];
         }
         lds_barrier();
         // v_new = Tb Y and Z = Tb^T dvn = dV, rows of this wave
@@ -1143,15 +863,10 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs a) {
         kk[j] = dl[j];
         mmf<BT>(dl[j], [&](int m, int k) { return Ts[k * BTL + row0 + m]; },
                 [&](int k, int nn) { return X1[k * BTL + 16 * j + nn]; }, G, n);
-        if (!PK)
-            mmf<DK>(kk[j], [&](int m, int k) { return Ks[(row0 + m) * BKL + k]; },
-                    [&](int k, int nn) { return Ks[(16 * j + nn) * BKL + k]; }, G, n);
+        mmf<DK>(kk[j], [&](int m, int k) { return Ks[(row0 + m) * BKL + k]; },
+                [&](int k, int nn) { return Ks[(16 * j + nn) * BKL + k]; }, G, n);
     }
     lds_barrier();
-    if (PK) {
-        finish_per_key<In>(a, t0, head, len, row0, w, G, n, lane, tid, dl, aQ, aKd, aKg, hk, X1, X2, Ks, Qs, bt, dbT);
-        return;
-    }
     // element terms of L and P: dbeta_i += sum_j dL_ij G_ij, dG = beta_i dL,
     // the G_i / G_j parts of the gate gradient, and dG o D, dP o D in place
     float rb[4] = {0.f, 0.f, 0.f, 0.f}, rg[4] = {0.f, 0.f, 0.f, 0.f}, cg[4] = {0.f, 0.f, 0.f, 0.f};
@@ -2404,7 +2119,7 @@ hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* d
             }
         } else {
             if (p.dtype == 1) hipLaunchKernelGGL(bwd_grad_kernel_h, grid, dim3(256), 0, s, a, dHw);
-            else hipLaunchKernelGGL((bwd_grad_kernel<float, false>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL(bwd_grad_kernel, grid, dim3(256), 0, s, a);
         }
     }
     return hipGetLastError();
