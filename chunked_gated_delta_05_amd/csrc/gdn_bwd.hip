@@ -1434,6 +1434,7 @@ __global__ __launch_bounds__(PKR, 1) void bwd_dh_kernel_pkr(BwdArgs a, const flo
 // (T, Tb, P, dTb, dP and dL are triangular) are skipped per wave.
 constexpr int HK = DK + 8;      // row stride (halves) of the 64 x 128 k and q tiles
 constexpr int HT = BT + 8;      // row stride of the 64 x 64 tiles
+constexpr int BTL4 = BT + 4;    // row stride (floats) of a 64 x 64 fp32 tile read 16 bytes at a time
 constexpr int HVT = 32;         // value columns per tile
 constexpr int HV = HVT + 8;     // row stride of the value tiles
 
@@ -1713,7 +1714,13 @@ __global__ __launch_bounds__(DHH, 1) void bwd_dh_kernel_h(BwdArgs a, const f16* 
             for (int r = 0; r < 4; ++r) a.dh0[(uh * DK + key0 + 4 * G + r) * DV + c0 + 16 * ct + n] = dh[ct][r];
 }
 
-__global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a, const f16* dHw) {
+// Eight waves, two per SIMD: waves w and w + 4 share token rows 16w .. +15.
+// Group 0 (waves 0..3) forms Y and v_new and accumulates dP, group 1 forms
+// dvn and Z (= dV) and accumulates dTb; each accumulates dQd, dKd and dKg for
+// the key tiles kb = 2jj + group and forms their dq, dk columns, and the
+// finish's M1, dL and element terms are split between the groups by column
+// block. Waves 0..3 stage the tiles.
+__global__ __launch_bounds__(512, 1) void bwd_grad_kernel_h(BwdArgs a, const f16* dHw) {
     __shared__ __attribute__((aligned(16))) f16 Kh[BT * HK];
     __shared__ __attribute__((aligned(16))) f16 Qh[BT * HK];
     __shared__ __attribute__((aligned(16))) f16 Th[BT * HT];     // T
@@ -1722,7 +1729,8 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a, const f16* d
     // value tiles, reused by the finish for three 64 x 64 tiles
     __shared__ __attribute__((aligned(16))) f16 vb[2 * DK * HV + 6 * BT * HV];
     __shared__ __attribute__((aligned(16))) float gm[4 * BT];
-    __shared__ float bt[BT], rowG[BT], rowK[BT], rowB[BT], colP[4][BT], colB[4][BT], red[4];
+    __shared__ float bt[BT], rowG[2][BT], rowK[2][BT], rowB[2][BT], colP[8][BT], colB[4][BT], red[8];
+    __shared__ __attribute__((aligned(16))) float dPf[BT * BTL4];   // finish: dP (fp32), from group 0 to both
     f16* Hh = vb;                       // h      [key][col]
     f16* DHh = Hh + DK * HV;            // dh'    [key][col]
     f16* Vh = DHh + DK * HV;            // v      [row][col]
@@ -1737,7 +1745,8 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a, const f16* d
     static_assert(3 * BT * HT <= 2 * DK * HV + 6 * BT * HV, "finish tiles fit the value-tile buffers");
 
     const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, n = lane & 15;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w8 = __builtin_amdgcn_readfirstlane(tid >> 6), w = w8 & 3, grp = w8 >> 2;
+    const bool ld = tid < 256;                  // the threads that stage tiles
     const int ci = blockIdx.x, head = blockIdx.y, H = a.H;
     int u, cc;
     chunk_of(a.um, ci, u, cc);
@@ -1761,13 +1770,14 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a, const f16* d
     TileRegs<f16, DK, HVT> pdh;
     TileRegs<bf16, BT, HVT> pv, pdo;
     auto prefetch = [&](int vt) {
+        if (!ld) return;
         const int vc0 = vt * HVT;
         ph.issue(a.h + ch * DK * DV + vc0, DV, DK, tid);
         pdh.issue(dHw + ch * DK * DV + vc0, DV, DK, tid);
         pv.issue(vin + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, tid);
         pdo.issue(dout + (t0 * H + head) * DV + vc0, (int64_t)H * DV, len, tid);
     };
-    {
+    if (ld) {
         TileRegs<bf16, BT, DK> tk, tq;
         TileRegs<f16, BT, BT> tt, tp;               // T and P: fp16 from the preparation
         const int64_t rs = (int64_t)H * DK;
@@ -1795,122 +1805,142 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a, const f16* d
         tp.commit_h(Ph, HT, tid);
     }
 
-    // accumulators, transposed: lane (G, n) holds row im at columns 16 b + 4G + r
-    f32x4 aP[4], aT[4], aQ[8], aKg[8], aKd[8];
-    for (int j = 0; j < 4; ++j) { aP[j] = f32x4{0.f, 0.f, 0.f, 0.f}; aT[j] = aP[j]; }
-    for (int j = 0; j < 8; ++j) { aQ[j] = f32x4{0.f, 0.f, 0.f, 0.f}; aKg[j] = aQ[j]; aKd[j] = aQ[j]; }
+    // accumulators, transposed: lane (G, n) holds row im at columns 16 b + 4G + r;
+    // aPT is dP (group 0) or dTb (group 1), the others key tile 2jj + grp
+    f32x4 aPT[4], aQ[4], aKg[4], aKd[4];
+    for (int j = 0; j < 4; ++j) {
+        aPT[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        aQ[j] = aPT[j];
+        aKg[j] = aPT[j];
+        aKd[j] = aPT[j];
+    }
     float hdh = 0.0f;                                // this thread's share of sum(h o dh')
 
     for (int vt = 0; vt < DV / HVT; ++vt) {
         const int vc0 = vt * HVT;
         lds_barrier();                               // the previous tile's buffers are consumed
-        ph.commit_h(Hh, HV, tid);
-        pdh.commit_raw(DHh, HV, tid);
-        pv.commit_h(Vh, HV, tid);
-        pdo.commit_h(DOh, HV, tid);
+        if (ld) {
+            ph.commit_h(Hh, HV, tid);
+            pdh.commit_raw(DHh, HV, tid);
+            pv.commit_h(Vh, HV, tid);
+            pdo.commit_h(DOh, HV, tid);
+        }
         lds_barrier();
-        // this thread's share of sum(h o dh'): its fp32 h against the fp16 dh'
+        if (ld) {
+            // this thread's share of sum(h o dh'): its fp32 h against the fp16 dh'
 #pragma unroll
-        for (int i = 0; i < TileRegs<float, DK, HVT>::PT; ++i) {
-            const int e = tid + 256 * i, r = e / 8, c4 = (e % 8) * 4;
-            const f32x4 d4 = ld4h(DHh + r * HV + c4);
-            for (int j = 0; j < 4; ++j) hdh += u2f(ph.w[i][j]) * d4[j];
+            for (int i = 0; i < TileRegs<float, DK, HVT>::PT; ++i) {
+                const int e = tid + 256 * i, r = e / 8, c4 = (e % 8) * 4;
+                const f32x4 d4 = ld4h(DHh + r * HV + c4);
+                for (int j = 0; j < 4; ++j) hdh += u2f(ph.w[i][j]) * d4[j];
+            }
         }
         if (vt + 1 < DV / HVT) prefetch(vt + 1);
-        // Y = V - b^G (K h) and dvn = b^{G_L - G} (K dh') + scale P^T dO, rows of this wave
+        // group 0: Y = V - b^G (K h); group 1: dvn = b^{G_L - G} (K dh') + scale P^T dO; rows of this wave
         {
-            const float bg = gm[BT + im], blg = gm[2 * BT + im];
             f16x8 bk[4], bp[2];
             for (int ks = 0; ks < 4; ++ks) bk[ks] = frag_row(Kh, HK, im, 32 * ks, G);
-            for (int js = 0; js < 2; ++js)
-                if (js >= hi_js) bp[js] = frag_col(Ph, HT, 32 * js, row0, G, n);
-            for (int mb = 0; mb < 2; ++mb) {
-                f32x4 kh = {0.f, 0.f, 0.f, 0.f}, kd = kh, pd = kh;
-                for (int ks = 0; ks < 4; ++ks) {
-                    mma_h(kh, frag_col(Hh, HV, 32 * ks, 16 * mb, G, n), bk[ks]);
-                    mma_h(kd, frag_col(DHh, HV, 32 * ks, 16 * mb, G, n), bk[ks]);
-                }
+            if (grp == 1)
                 for (int js = 0; js < 2; ++js)
-                    if (js >= hi_js) mma_h(pd, frag_col(DOh, HV, 32 * js, 16 * mb, G, n), bp[js]);
-                const f32x4 v4 = ld4h(Vh + im * HV + 16 * mb + 4 * G);
-                f32x4 y, dv;
-                for (int r = 0; r < 4; ++r) {
-                    y[r] = v4[r] - bg * kh[r];
-                    dv[r] = blg * kd[r] + a.scale * pd[r];
+                    if (js >= hi_js) bp[js] = frag_col(Ph, HT, 32 * js, row0, G, n);
+            for (int mb = 0; mb < 2; ++mb) {
+                if (grp == 0) {
+                    const float bg = gm[BT + im];
+                    f32x4 kh = {0.f, 0.f, 0.f, 0.f};
+                    for (int ks = 0; ks < 4; ++ks) mma_h(kh, frag_col(Hh, HV, 32 * ks, 16 * mb, G, n), bk[ks]);
+                    const f32x4 v4 = ld4h(Vh + im * HV + 16 * mb + 4 * G);
+                    f32x4 y;
+                    for (int r = 0; r < 4; ++r) y[r] = v4[r] - bg * kh[r];
+                    st4h(Yh + im * HV + 16 * mb + 4 * G, y);
+                } else {
+                    const float blg = gm[2 * BT + im];
+                    f32x4 kd = {0.f, 0.f, 0.f, 0.f}, pd = kd;
+                    for (int ks = 0; ks < 4; ++ks) mma_h(kd, frag_col(DHh, HV, 32 * ks, 16 * mb, G, n), bk[ks]);
+                    for (int js = 0; js < 2; ++js)
+                        if (js >= hi_js) mma_h(pd, frag_col(DOh, HV, 32 * js, 16 * mb, G, n), bp[js]);
+                    f32x4 dv;
+                    for (int r = 0; r < 4; ++r) dv[r] = blg * kd[r] + a.scale * pd[r];
+                    st4h(DVh + im * HV + 16 * mb + 4 * G, dv);
                 }
-                st4h(Yh + im * HV + 16 * mb + 4 * G, y);
-                st4h(DVh + im * HV + 16 * mb + 4 * G, dv);
             }
         }
         lds_barrier();
-        // v_new = Tb Y and Z = Tb^T dvn = dV, rows of this wave
-        {
-            f16x8 btb[2], btt[2];
-            for (int js = 0; js < 2; ++js) {
+        // group 0: v_new = Tb Y; group 1: Z = Tb^T dvn = dV; rows of this wave
+        if (grp == 0) {
+            f16x8 btb[2];
+            for (int js = 0; js < 2; ++js)
                 if (js < lo_js) btb[js] = frag_row(Tbh, HT, im, 32 * js, G);
-                if (js >= hi_js) btt[js] = frag_col(Th, HT, 32 * js, row0, G, n);
+            for (int mb = 0; mb < 2; ++mb) {
+                f32x4 vn = {0.f, 0.f, 0.f, 0.f};
+                for (int js = 0; js < 2; ++js)
+                    if (js < lo_js) mma_h(vn, frag_col(Yh, HV, 32 * js, 16 * mb, G, n), btb[js]);
+                st4h(VNh + im * HV + 16 * mb + 4 * G, vn);
             }
+        } else {
+            f16x8 btt[2];
+            for (int js = 0; js < 2; ++js)
+                if (js >= hi_js) btt[js] = frag_col(Th, HT, 32 * js, row0, G, n);
             const float bi = bt[im];
             for (int mb = 0; mb < 2; ++mb) {
-                f32x4 vn = {0.f, 0.f, 0.f, 0.f}, z = vn;
-                for (int js = 0; js < 2; ++js) {
-                    if (js < lo_js) mma_h(vn, frag_col(Yh, HV, 32 * js, 16 * mb, G, n), btb[js]);
+                f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                for (int js = 0; js < 2; ++js)
                     if (js >= hi_js) mma_h(z, frag_col(DVh, HV, 32 * js, 16 * mb, G, n), btt[js]);
-                }
                 for (int r = 0; r < 4; ++r) z[r] *= bi;
-                st4h(VNh + im * HV + 16 * mb + 4 * G, vn);
                 st4h(Zh + im * HV + 16 * mb + 4 * G, z);
                 if (im < len) *reinterpret_cast<f32x4*>(a.dv + ((t0 + im) * H + head) * DV + vc0 + 16 * mb + 4 * G) = z;
             }
         }
         lds_barrier();
-        // accumulate over this tile's 32 columns: dP / scale, dTb, dQd / scale,
-        // dKg and -dKd, the wave's rows as n
+        // accumulate over this tile's 32 columns: dP / scale (group 0) or dTb
+        // (group 1), and dQd / scale, dKg and -dKd of key tiles 2jj + grp;
+        // the wave's rows as n
         {
-            const f16x8 bdo = frag_row(DOh, HV, im, 0, G), bdv = frag_row(DVh, HV, im, 0, G);
-            const f16x8 bvn = frag_row(VNh, HV, im, 0, G), bz = frag_row(Zh, HV, im, 0, G);
+            const f16x8 bdo = frag_row(DOh, HV, im, 0, G), bvn = frag_row(VNh, HV, im, 0, G);
+            const f16x8 bz = frag_row(Zh, HV, im, 0, G);
+            const f16x8 bpt = grp == 0 ? bdo : frag_row(DVh, HV, im, 0, G);
+            const f16* xpt = grp == 0 ? VNh : Yh;
             for (int jb = 0; jb < 4; ++jb)
-                if (jb <= w) {
-                    mma_h(aP[jb], frag_row(VNh, HV, 16 * jb + n, 0, G), bdo);
-                    mma_h(aT[jb], frag_row(Yh, HV, 16 * jb + n, 0, G), bdv);
-                }
-            for (int kb = 0; kb < 8; ++kb) {
+                if (jb <= w) mma_h(aPT[jb], frag_row(xpt, HV, 16 * jb + n, 0, G), bpt);
+            for (int jj = 0; jj < 4; ++jj) {
+                const int kb = 2 * jj + grp;
                 const f16x8 hk = frag_row(Hh, HV, 16 * kb + n, 0, G);
-                mma_h(aQ[kb], hk, bdo);
-                mma_h(aKd[kb], hk, bz);
-                mma_h(aKg[kb], frag_row(DHh, HV, 16 * kb + n, 0, G), bvn);
+                mma_h(aQ[jj], hk, bdo);
+                mma_h(aKd[jj], hk, bz);
+                mma_h(aKg[jj], frag_row(DHh, HV, 16 * kb + n, 0, G), bvn);
             }
         }
     }
     lds_barrier();
 
-    // ---- finish. X1 = dTb, X2 = dP (lower incl. diagonal) of the wave's rows;
-    // dbeta's column term: sums over i of dTb o T
+    // ---- finish. X1 = dTb (group 1, fp16), dPf = dP (group 0, fp32), lower
+    // incl. diagonal, of the wave's rows; dbeta's column term: sums over i of
+    // dTb o T
     {
         float cs[16];                                // value 4 jb + r: column j = 16 jb + 4G + r
         for (int jb = 0; jb < 4; ++jb) {
             const f32x4 t4 = ld4h(Th + im * HT + 16 * jb + 4 * G);
-            f32x4 x1, x2;
+            f32x4 x;
             for (int r = 0; r < 4; ++r) {
                 const int j = 16 * jb + 4 * G + r;
                 const bool keep = jb <= w && j <= im;
-                x1[r] = keep ? aT[jb][r] : 0.0f;
-                x2[r] = keep ? a.scale * aP[jb][r] : 0.0f;
-                cs[4 * jb + r] = x1[r] * t4[r];
+                x[r] = keep ? (grp == 0 ? a.scale : 1.0f) * aPT[jb][r] : 0.0f;
+                cs[4 * jb + r] = x[r] * t4[r];
             }
-            aP[jb] = x2;
-            st4h(X1h + im * HT + 16 * jb + 4 * G, x1);
+            if (grp == 0) *reinterpret_cast<f32x4*>(&dPf[im * BTL4 + 16 * jb + 4 * G]) = x;
+            else st4h(X1h + im * HT + 16 * jb + 4 * G, x);
         }
         // lane n: the column sum over this wave's rows of value n
-        colB[w][16 * (n >> 2) + 4 * G + (n & 3)] = row_sum16(cs, n);
+        const float csum = row_sum16(cs, n);
+        if (grp == 1) colB[w][16 * (n >> 2) + 4 * G + (n & 3)] = csum;
     }
     lds_barrier();
-    // M1 = dT T^T = dTb Tb^T, rows of this wave
+    // M1 = dT T^T = dTb Tb^T, rows of this wave, column blocks 2 grp, 2 grp + 1
     {
         f16x8 bx[2];
         for (int js = 0; js < 2; ++js)
             if (js < lo_js) bx[js] = frag_row(X1h, HT, im, 32 * js, G);
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kh2 = 0; kh2 < 2; ++kh2) {
+            const int kb = 2 * grp + kh2;
             f32x4 m = {0.f, 0.f, 0.f, 0.f};
             for (int js = 0; js < 2; ++js)
                 if (js < lo_js) mma_h(m, frag_row(Tbh, HT, 16 * kb + n, 32 * js, G), bx[js]);
@@ -1918,39 +1948,47 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a, const f16* d
         }
     }
     lds_barrier();
-    // dL = -T^T M1 (strictly lower) and the Gram matrix K K^T, rows of this wave
-    f32x4 dl[4], gr[4];
+    // dL = -T^T M1 (strictly lower) and the Gram matrix K K^T, rows of this
+    // wave, column blocks 2 grp, 2 grp + 1
+    f32x4 dl[2], gr[2];
     {
         f16x8 btt[2], bk[4];
         for (int js = 0; js < 2; ++js)
             if (js >= hi_js) btt[js] = frag_col(Th, HT, 32 * js, row0, G, n);
         for (int ks = 0; ks < 4; ++ks) bk[ks] = frag_row(Kh, HK, im, 32 * ks, G);
-        for (int jb = 0; jb < 4; ++jb) {
-            dl[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            gr[jb] = dl[jb];
+        for (int jh = 0; jh < 2; ++jh) {
+            const int jb = 2 * grp + jh;
+            dl[jh] = f32x4{0.f, 0.f, 0.f, 0.f};
+            gr[jh] = dl[jh];
             if (jb <= w) {
                 for (int js = 0; js < 2; ++js)
-                    if (js >= hi_js) mma_h(dl[jb], frag_col(M1h, HT, 32 * js, 16 * jb, G, n), btt[js]);
-                for (int ks = 0; ks < 4; ++ks) mma_h(gr[jb], frag_row(Kh, HK, 16 * jb + n, 32 * ks, G), bk[ks]);
+                    if (js >= hi_js) mma_h(dl[jh], frag_col(M1h, HT, 32 * js, 16 * jb, G, n), btt[js]);
+                for (int ks = 0; ks < 4; ++ks) mma_h(gr[jh], frag_row(Kh, HK, 16 * jb + n, 32 * ks, G), bk[ks]);
             }
         }
     }
-    // element terms of L and P: dbeta_i += sum_j dL_ij G_ij, the G_i / G_j
-    // parts of the gate gradient, and dG o D, dP o D into X1, X2
+    // element terms of L and P in column blocks 2 grp, 2 grp + 1: dbeta_i +=
+    // sum_j dL_ij G_ij, the G_i / G_j parts of the gate gradient, and dG o D,
+    // dP o D into X1, X2
     float rg = 0.0f;
     {
         const float gi = gm[im], bi = bt[im];
         float rb = 0.0f, cg[16];
+        for (int e = 0; e < 16; ++e) cg[e] = 0.0f;
+#pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
+            if ((jb >> 1) != grp) continue;          // (jb static, so cg stays in registers)
+            const int jh = jb & 1;
             const f32x4 p4 = ld4h(Ph + im * HT + 16 * jb + 4 * G);
+            const f32x4 dp4 = *reinterpret_cast<const f32x4*>(&dPf[im * BTL4 + 16 * jb + 4 * G]);
             f32x4 x1, x2;
             for (int r = 0; r < 4; ++r) {
                 const int j = 16 * jb + 4 * G + r;
                 const float d = jb <= w && j <= im ? fpow(gi - gm[j], a.use_exp2) : 0.0f;
-                const float lij = j < im ? -dl[jb][r] : 0.0f;     // dL
-                const float gij = gr[jb][r] * d;                   // (k_i . k_j) D_ij
+                const float lij = j < im ? -dl[jh][r] : 0.0f;     // dL
+                const float gij = gr[jh][r] * d;                   // (k_i . k_j) D_ij
                 const float dgg = bi * lij;                        // dG
-                const float dpij = aP[jb][r];
+                const float dpij = dp4[r];
                 rb += lij * gij;
                 const float t = lnb * (dgg * gij + dpij * p4[r]);
                 rg += t;
@@ -1964,14 +2002,15 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a, const f16* d
         // row sums over the four lane groups
         rb = pair32(pair16(rb));
         rg = pair32(pair16(rg));
-        if (G == 0) rowB[im] = rb;
+        if (G == 0) rowB[grp][im] = rb;
         // column sums over this wave's rows: one partial per wave, added in a
         // fixed order below (the same result on every run)
-        colP[w][16 * (n >> 2) + 4 * G + (n & 3)] = row_sum16(cg, n);
+        colP[w8][16 * (n >> 2) + 4 * G + (n & 3)] = row_sum16(cg, n);
     }
     lds_barrier();
-    // dq, dk, rows of this wave: the products with dG o D and dP o D, then
-    // b^G dQd, b^G dKd + b^{G_L - G} dKg, and their gate terms
+    // dq, dk, rows of this wave and key tiles 2jj + grp: the products with
+    // dG o D and dP o D, then b^G dQd, b^G dKd + b^{G_L - G} dKg, and their
+    // gate terms
     {
         f16x8 x2r[2], x1r[2], x1c[2], x2c[2];
         for (int js = 0; js < 2; ++js) {
@@ -1986,7 +2025,8 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a, const f16* d
         }
         const float bgi = gm[BT + im], blgi = gm[2 * BT + im];
         float rq = 0.0f, rk = 0.0f;
-        for (int kb = 0; kb < 8; ++kb) {
+        for (int jj = 0; jj < 4; ++jj) {
+            const int kb = 2 * jj + grp;
             f32x4 q1 = {0.f, 0.f, 0.f, 0.f}, k1 = q1;
             for (int js = 0; js < 2; ++js) {
                 const f16x8 ak = frag_col(Kh, HK, 32 * js, 16 * kb, G, n);
@@ -2002,7 +2042,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a, const f16* d
             const f32x4 q4 = ld4h(Qh + im * HK + 16 * kb + 4 * G), k4 = ld4h(Kh + im * HK + 16 * kb + 4 * G);
             f32x4 dqv, dkv;
             for (int r = 0; r < 4; ++r) {
-                const float dQd = a.scale * aQ[kb][r], dKd = -aKd[kb][r], dKg = aKg[kb][r];
+                const float dQd = a.scale * aQ[jj][r], dKd = -aKd[jj][r], dKg = aKg[jj][r];
                 dqv[r] = q1[r] + bgi * dQd;
                 dkv[r] = k1[r] + bgi * dKd + blgi * dKg;
                 // the Kg term (ln b dKg Kg) goes to dg as a prefix over earlier
@@ -2020,34 +2060,37 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel_h(BwdArgs a, const f16* d
         rq = pair32(pair16(rq));
         rk = pair32(pair16(rk));
         if (G == 0) {
-            rowG[im] = rg + rq;
-            rowK[im] = rk;
+            rowG[grp][im] = rg + rq;
+            rowK[grp][im] = rk;
         }
     }
     // the state decay's term of G_L: lnb gamma sum(h o dh'), over the workgroup
     float tl = lnb * gm[3 * BT] * hdh;
-    for (int s = 1; s < 64; s <<= 1) tl += __shfl_xor(tl, s, 64);
-    if (lane == 0) red[w] = tl;
+    for (int sft = 1; sft < 64; sft <<= 1) tl += __shfl_xor(tl, sft, 64);
+    if (lane == 0) red[w8] = tl;
     lds_barrier();
     // dg: reverse cumulative sum over the chunk's rows of the gate gradient,
     // with the state decay's term entering at the last valid row, plus the
     // exclusive prefix of the Kg terms; dbeta: its column and row terms
-    if (w == 0) {
-        const float gl = ((red[0] + red[1]) + red[2]) + red[3];
-        const float colG = ((colP[0][lane] + colP[1][lane]) + colP[2][lane]) + colP[3][lane];
-        const float colBs = ((colB[0][lane] + colB[1][lane]) + colB[2][lane]) + colB[3][lane];
-        float x = lane < len ? rowG[lane] + colG + (lane == len - 1 ? gl : 0.0f) : 0.0f;
-        const float kg = lane < len ? rowK[lane] : 0.0f;
+    if (w8 == 0) {
+        float gl = 0.0f, colG = 0.0f, colBs = 0.0f;
+        for (int i = 0; i < 8; ++i) {
+            gl += red[i];
+            colG += colP[i][lane];
+        }
+        for (int i = 0; i < 4; ++i) colBs += colB[i][lane];
+        float x = lane < len ? (rowG[0][lane] + rowG[1][lane]) + colG + (lane == len - 1 ? gl : 0.0f) : 0.0f;
+        const float kg = lane < len ? rowK[0][lane] + rowK[1][lane] : 0.0f;
         float y = kg;
-        for (int s = 1; s < 64; s <<= 1) {
-            const float xd = __shfl_down(x, s, 64), yu = __shfl_up(y, s, 64);
-            if (lane + s < 64) x += xd;
-            if (lane >= s) y += yu;
+        for (int sft = 1; sft < 64; sft <<= 1) {
+            const float xd = __shfl_down(x, sft, 64), yu = __shfl_up(y, sft, 64);
+            if (lane + sft < 64) x += xd;
+            if (lane >= sft) y += yu;
         }
         x += y - kg;
         if (lane < len) {
             a.dg[(t0 + lane) * H + head] = x;
-            a.dbeta[(t0 + lane) * H + head] = colBs + rowB[lane];
+            a.dbeta[(t0 + lane) * H + head] = colBs + rowB[0][lane] + rowB[1][lane];
         }
     }
 }
@@ -2118,7 +2161,7 @@ hipError_t launch_bwd(const Problem& p, const Workspace& ws, float* dH, float* d
                 hipLaunchKernelGGL(bwd_grad_kernel_pk<float>, grid, dim3(512), 0, s, a);
             }
         } else {
-            if (p.dtype == 1) hipLaunchKernelGGL(bwd_grad_kernel_h, grid, dim3(256), 0, s, a, dHw);
+            if (p.dtype == 1) hipLaunchKernelGGL(bwd_grad_kernel_h, grid, dim3(512), 0, s, a, dHw);
             else hipLaunchKernelGGL(bwd_grad_kernel, grid, dim3(256), 0, s, a);
         }
     }
