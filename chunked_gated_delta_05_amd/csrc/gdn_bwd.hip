@@ -1535,6 +1535,14 @@ __global__ __launch_bounds__(256) void bwd_transfer_kernel_h(BwdArgs a, f16* Aw,
     const int row0 = 16 * w, im = row0 + n;
     const int lo_js = w >= 2 ? 2 : 1;            // 32-row steps i <= j can reach
     const float* gam = a.ws.gam + ch * (GAMR * BT);
+    // q of this lane's row im for U, loaded with the tiles (rows past the
+    // chunk end: zero)
+    u32x2 qv[8];
+    {
+        const bf16* qrow = reinterpret_cast<const bf16*>(a.q) + ((t0 + (im < len ? im : 0)) * H + head) * DK;
+        for (int kb = 0; kb < 8; ++kb)
+            qv[kb] = im < len ? *reinterpret_cast<const u32x2*>(qrow + 16 * kb + 4 * G) : u32x2{0u, 0u};
+    }
     {
         TileRegs<bf16, BT, DK> tk;
         TileRegs<f16, BT, BT> tt, tp;
@@ -1592,7 +1600,6 @@ __global__ __launch_bounds__(256) void bwd_transfer_kernel_h(BwdArgs a, f16* Aw,
     {
         f16* Uc = Uw + ch * (BT * DK);
         const float bg = gm[BT + im];
-        const bf16* qrow = reinterpret_cast<const bf16*>(a.q) + ((t0 + (im < len ? im : 0)) * H + head) * DK;
         f16x8 bp[2];
         for (int is = 0; is < 2; ++is)
             if (is < lo_js) bp[is] = frag_row(Ph, HT, im, 32 * is, G);
@@ -1600,7 +1607,7 @@ __global__ __launch_bounds__(256) void bwd_transfer_kernel_h(BwdArgs a, f16* Aw,
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             for (int is = 0; is < 2; ++is)
                 if (is < lo_js) mma_h(acc, frag_col(Wh, HK, 32 * is, 16 * kb, G, n), bp[is]);
-            const u32x2 qw = im < len ? *reinterpret_cast<const u32x2*>(qrow + 16 * kb + 4 * G) : u32x2{0u, 0u};
+            const u32x2 qw = qv[kb];
             f32x4 x;
             for (int r = 0; r < 4; ++r) {
                 const float qv = u2f(r & 1 ? qw[r >> 1] & 0xffff0000u : qw[r >> 1] << 16);
